@@ -1,0 +1,379 @@
+// C-ABI entry points of the kvx library: argument validation, workspace
+// layout and kernel launch order.  Every computation runs in the HIP kernels
+// of the other translation units; this file only checks shapes and wires
+// buffers.
+
+#include <mutex>
+
+#include "kvx_internal.hpp"
+
+namespace kvx {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+static bool desc_ok(const kvx_cache_desc* d) {
+  if (!d) return false;
+  if (d->layers < 1 || d->layers > MAX_LAYERS || d->tokens < 0 || d->kv_heads < 1 || d->head_dim < 1) return false;
+  if (d->dtype != KVX_F32 && d->dtype != KVX_BF16) return false;
+  if (!(d->rope_base >= 0.0)) return false;
+  if (d->rope_base > 0.0 && (d->head_dim % 2) != 0) return false;
+  return true;
+}
+
+// Workspace layout of kvx_translate.  Returned sizes and the slices used by
+// the launch come from this single function.
+struct TranslateWs {
+  Runs runs{};
+  void* runs_scratch = nullptr;
+  float2* tab_send = nullptr;
+  float2* tab_recv = nullptr;
+  uint16_t* krows = nullptr;   // rotated-back unique key rows (fp16)
+  int32_t rows_cap = 0;
+  size_t bytes = 0;
+};
+
+static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t per_head,
+                                    bool key_role, void* base) {
+  TranslateWs w;
+  Carve c(base);
+  const int32_t nr = recv->tokens;
+  const bool f32 = send->dtype == KVX_F32;
+  const bool srope = send->rope_base > 0.0 && key_role;
+  const bool rrope = recv->rope_base > 0.0 && key_role;
+  if (!f32 && !per_head) {
+    w.runs.uniq = c.take<int32_t>(nr > 0 ? nr : 1);
+    w.runs.run_begin = c.take<int32_t>(static_cast<size_t>(nr) + 1);
+    w.runs.recv_to_uniq = c.take<int32_t>(nr > 0 ? nr : 1);
+    w.runs.n_uniq = c.take<int32_t>(64);
+    w.runs_scratch = c.take<char>(runs_ws_bytes(nr));
+  }
+  if (srope) w.tab_send = c.take<float2>(static_cast<size_t>(send->tokens) * (send->head_dim / 2));
+  if (rrope) w.tab_recv = c.take<float2>(static_cast<size_t>(nr) * (recv->head_dim / 2));
+  if (!f32 && !per_head && srope) {
+    // U <= N_R always (U <= N_S only for non-decreasing maps)
+    w.rows_cap = nr;
+    w.krows = c.take<uint16_t>(static_cast<size_t>(send->layers) * w.rows_cap * send->kv_heads * send->head_dim);
+  }
+  w.bytes = c.used + 256;
+  return w;
+}
+
+}  // namespace kvx
+
+using namespace kvx;
+
+extern "C" {
+
+const char* kvx_status_string(int status) {
+  switch (status) {
+    case KVX_OK: return "ok";
+    case KVX_ERR_INVALID: return "invalid argument";
+    case KVX_ERR_SHAPE: return "inconsistent shapes";
+    case KVX_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVX_ERR_NOT_SPD: return "regularised Gram matrix is not positive definite";
+    case KVX_ERR_HIP: return "HIP runtime error";
+    case KVX_ERR_UNSUPPORTED: return "unsupported combination";
+    default: return "unknown status";
+  }
+}
+
+size_t kvx_align_workspace_size(int32_t n_recv) { return align_ws_bytes(n_recv) + 256; }
+
+int kvx_align_tokens(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                     int32_t* recv_to_send, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_send < 0 || n_recv < 0) return KVX_ERR_INVALID;
+  if (n_recv == 0) return KVX_OK;
+  if (n_send == 0) return KVX_ERR_SHAPE;
+  if (!send_end || !recv_end || !recv_to_send) return KVX_ERR_INVALID;
+  if (!workspace || ws_bytes < kvx_align_workspace_size(n_recv)) return KVX_ERR_WORKSPACE;
+  return launch_align(send_end, n_send, recv_end, n_recv, recv_to_send, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps, int32_t tap_stride, int32_t* taps_out) {
+  if (send_layers < 1 || recv_layers < 1 || !taps_out) return KVX_ERR_INVALID;
+  if (n_taps < 1 || n_taps > MAX_TAPS || (n_taps % 2) == 0 || tap_stride < 0) return KVX_ERR_INVALID;
+  for (int32_t l = 0; l < recv_layers; ++l) {
+    int64_t m = 0;
+    if (recv_layers > 1) {
+      // round(l (L_S-1) / (L_R-1)), halves up, in integers
+      const int64_t num = 2LL * l * (send_layers - 1) + (recv_layers - 1);
+      m = num / (2LL * (recv_layers - 1));
+    }
+    for (int32_t t = 0; t < n_taps; ++t) {
+      int64_t v = m + static_cast<int64_t>(t - (n_taps - 1) / 2) * tap_stride;
+      v = v < 0 ? 0 : (v > send_layers - 1 ? send_layers - 1 : v);
+      taps_out[l * n_taps + t] = static_cast<int32_t>(v);
+    }
+  }
+  return KVX_OK;
+}
+
+size_t kvx_translate_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
+                                    int32_t per_head) {
+  (void)n_taps;
+  if (!desc_ok(send) || !desc_ok(recv)) return 0;
+  return layout_translate(send, recv, per_head, true, nullptr).bytes;
+}
+
+}  // extern "C"
+
+namespace kvx {
+
+// Records ev[0] before the preparation kernels, ev[1] before the main
+// translation kernel and ev[2] after it, when ev is not null.
+static int translate_impl(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                          const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
+                          const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
+                          const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                          void* stream, hipEvent_t* ev) {
+  if (!desc_ok(send) || !desc_ok(recv)) return KVX_ERR_INVALID;
+  if (w_dtype != KVX_F32 && w_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  if (n_taps < 1 || n_taps > MAX_TAPS || !taps) return KVX_ERR_INVALID;
+  const bool do_k = k_recv != nullptr, do_v = v_recv != nullptr;
+  if (do_k && (!k_send || !wt_k)) return KVX_ERR_INVALID;
+  if (do_v && (!v_send || !wt_v)) return KVX_ERR_INVALID;
+  if (recv->tokens > 0 && !recv_to_send) return KVX_ERR_INVALID;
+  for (int32_t i = 0; i < recv->layers * n_taps; ++i)
+    if (taps[i] < 0 || taps[i] >= send->layers) return KVX_ERR_INVALID;
+  if (per_head) {
+    if (n_taps != 1) return KVX_ERR_SHAPE;
+    if (send->kv_heads != recv->kv_heads || send->head_dim != recv->head_dim) return KVX_ERR_SHAPE;
+  }
+  if (send->dtype != recv->dtype) return KVX_ERR_UNSUPPORTED;
+  if (recv->tokens == 0 || (!do_k && !do_v)) return KVX_OK;
+  if (send->tokens == 0) return KVX_ERR_SHAPE;
+  const TranslateWs need = layout_translate(send, recv, per_head, true, nullptr);
+  if (!workspace || ws_bytes < need.bytes) return KVX_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const TranslateWs w = layout_translate(send, recv, per_head, do_k, workspace);
+  auto mark = [&](int i) -> int {
+    if (ev && hipEventRecord(ev[i], s) != hipSuccess) return KVX_ERR_HIP;
+    return KVX_OK;
+  };
+  auto main_kernel = [&](auto&& launch) -> int {
+    if (int st = mark(1)) return st;
+    if (int st = launch()) return st;
+    return mark(2);
+  };
+  if (int st = mark(0)) return st;
+  const int32_t f_in = n_taps * send->kv_heads * send->head_dim;
+  const int32_t f_out = recv->kv_heads * recv->head_dim;
+
+  if (send->dtype == KVX_F32) {
+    if (w.tab_send) {
+      if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
+    }
+    if (w.tab_recv) {
+      if (int st = launch_rope_table(w.tab_recv, recv->tokens, recv->head_dim, recv->rope_base, s)) return st;
+    }
+    F32Problem p{};
+    p.send_layers = send->layers;
+    p.send_tokens = send->tokens;
+    p.send_heads = send->kv_heads;
+    p.send_dim = send->head_dim;
+    p.recv_layers = recv->layers;
+    p.recv_tokens = recv->tokens;
+    p.recv_heads = recv->kv_heads;
+    p.recv_dim = recv->head_dim;
+    p.n_taps = n_taps;
+    p.per_head = per_head ? 1 : 0;
+    p.w_f32 = w_dtype == KVX_F32;
+    p.taps = taps;
+    p.recv_to_send = recv_to_send;
+    p.tab_send = w.tab_send;
+    p.tab_recv = w.tab_recv;
+    F32Role roles[2];
+    int n = 0;
+    if (do_k)
+      roles[n++] = F32Role{static_cast<const float*>(k_send), wt_k, b_k, static_cast<float*>(k_recv),
+                           w.tab_send ? 1 : 0, w.tab_recv ? 1 : 0};
+    if (do_v) roles[n++] = F32Role{static_cast<const float*>(v_send), wt_v, b_v, static_cast<float*>(v_recv), 0, 0};
+    return main_kernel([&] { return launch_f32(p, roles, n, s); });
+  }
+
+  // bf16 caches: matrix-core paths, head_dim 128
+  if (send->head_dim != 128 || recv->head_dim != 128) return KVX_ERR_UNSUPPORTED;
+  if (per_head) {
+    if (send->rope_base > 0.0 || recv->rope_base > 0.0) return KVX_ERR_UNSUPPORTED;
+    HeadProblem p{};
+    p.send_layers = send->layers;
+    p.send_tokens = send->tokens;
+    p.recv_layers = recv->layers;
+    p.recv_tokens = recv->tokens;
+    p.heads = send->kv_heads;
+    p.w_f32 = w_dtype == KVX_F32;
+    p.taps = taps;
+    p.recv_to_send = recv_to_send;
+    HeadRole roles[2];
+    int n = 0;
+    if (do_k)
+      roles[n++] = HeadRole{static_cast<const uint16_t*>(k_send), wt_k, b_k, static_cast<uint16_t*>(k_recv)};
+    if (do_v)
+      roles[n++] = HeadRole{static_cast<const uint16_t*>(v_send), wt_v, b_v, static_cast<uint16_t*>(v_recv)};
+    return main_kernel([&] { return launch_perhead(p, roles, n, s); });
+  }
+
+  if (f_out % 256 != 0) return KVX_ERR_UNSUPPORTED;
+  if (int st = launch_runs(recv_to_send, recv->tokens, send->tokens, w.runs, w.runs_scratch, s)) return st;
+  const int64_t send_layer_elems = static_cast<int64_t>(send->tokens) * send->kv_heads * send->head_dim;
+  FlatRole roles[2];
+  int n = 0;
+  if (do_k) {
+    FlatRole r{};
+    if (w.tab_send) {
+      if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
+      uint8_t used[MAX_LAYERS] = {0};
+      for (int32_t i = 0; i < recv->layers * n_taps; ++i) used[taps[i]] = 1;
+      if (int st = launch_derotate_rows(static_cast<const uint16_t*>(k_send), send->layers, send->tokens,
+                                        send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, w.krows, s))
+        return st;
+      r.a_src = w.krows;
+      r.a_layer_stride = static_cast<int64_t>(w.rows_cap) * send->kv_heads * send->head_dim;
+      r.a_compact = 1;
+      r.a_f16 = 1;
+    } else {
+      r.a_src = k_send;
+      r.a_layer_stride = send_layer_elems;
+      r.a_compact = 0;
+      r.a_f16 = 0;
+    }
+    if (w.tab_recv) {
+      if (int st = launch_rope_table(w.tab_recv, recv->tokens, recv->head_dim, recv->rope_base, s)) return st;
+    }
+    r.wt = wt_k;
+    r.bias = b_k;
+    r.out = static_cast<uint16_t*>(k_recv);
+    r.rotate = w.tab_recv ? 1 : 0;
+    roles[n++] = r;
+  }
+  if (do_v) {
+    FlatRole r{};
+    r.a_src = v_send;
+    r.a_layer_stride = send_layer_elems;
+    r.a_compact = 0;
+    r.a_f16 = 0;
+    r.wt = wt_v;
+    r.bias = b_v;
+    r.out = static_cast<uint16_t*>(v_recv);
+    r.rotate = 0;
+    roles[n++] = r;
+  }
+  FlatProblem p{};
+  p.send_layers = send->layers;
+  p.send_tokens = send->tokens;
+  p.recv_layers = recv->layers;
+  p.recv_tokens = recv->tokens;
+  p.f_in = f_in;
+  p.f_out = f_out;
+  p.n_taps = n_taps;
+  p.send_row = send->kv_heads * send->head_dim;
+  p.w_f32 = w_dtype == KVX_F32;
+  p.taps = taps;
+  p.tab_recv = w.tab_recv;
+  p.runs = w.runs;
+  return main_kernel([&] { return launch_flat(p, roles, n, s); });
+}
+
+}  // namespace kvx
+
+extern "C" {
+
+int kvx_translate(const kvx_cache_desc* send, const void* k_send, const void* v_send, const kvx_cache_desc* recv,
+                  void* k_recv, void* v_recv, const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                  int32_t per_head, int32_t w_dtype, const void* wt_k, const void* wt_v, const float* b_k,
+                  const float* b_v, void* workspace, size_t ws_bytes, void* stream) {
+  return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr);
+}
+
+int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                        const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
+                        const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
+                        const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                        void* stream, float* stage_ms) {
+  if (!stage_ms) return KVX_ERR_INVALID;
+  stage_ms[0] = stage_ms[1] = 0.0f;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  for (auto& e : ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto& f : ev)
+        if (f) (void)hipEventDestroy(f);
+      return KVX_ERR_HIP;
+    }
+  int st = translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
+                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev);
+  if (st == KVX_OK) {
+    // events exist only when work was launched (empty problems return early)
+    if (hipEventSynchronize(ev[2]) != hipSuccess ||
+        hipEventElapsedTime(&stage_ms[0], ev[0], ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&stage_ms[1], ev[1], ev[2]) != hipSuccess) {
+      stage_ms[0] = stage_ms[1] = 0.0f;
+      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) st = KVX_ERR_HIP;
+    }
+  }
+  for (auto& e : ev) (void)hipEventDestroy(e);
+  return st;
+}
+
+int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t derotate,
+                        const int32_t* recv_to_send, int32_t n_rows, const int32_t* taps_of_layer, int32_t n_taps,
+                        void* x_out, void* stream) {
+  if (!desc_ok(send) || n_rows < 0 || n_taps < 1 || n_taps > MAX_TAPS || !taps_of_layer) return KVX_ERR_INVALID;
+  if (n_rows == 0) return KVX_OK;
+  if (!kv_send || !recv_to_send || !x_out) return KVX_ERR_INVALID;
+  if (send->tokens == 0) return KVX_ERR_SHAPE;
+  if (derotate && !(send->rope_base > 0.0)) return KVX_ERR_INVALID;
+  for (int32_t t = 0; t < n_taps; ++t)
+    if (taps_of_layer[t] < 0 || taps_of_layer[t] >= send->layers) return KVX_ERR_INVALID;
+  const int32_t row = send->kv_heads * send->head_dim;
+  if (!derotate && (row % 2) != 0) return KVX_ERR_UNSUPPORTED;
+  const int64_t stride = static_cast<int64_t>(send->tokens) * row;
+  return launch_gather(kv_send, send->dtype == KVX_F32, send->tokens, row, stride, taps_of_layer, n_taps,
+                       recv_to_send, n_rows, derotate ? send->rope_base : 0.0, send->head_dim, x_out,
+                       static_cast<hipStream_t>(stream));
+}
+
+size_t kvx_fit_ridge_workspace_size(int32_t f_in, int32_t f_out) {
+  if (f_in < 1 || f_out < 1) return 0;
+  return fit_ws_bytes(f_in, f_out);
+}
+
+int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_dtype, int64_t n_rows,
+                  int32_t f_in, int32_t f_out, double lambda_abs, double lambda_rel, int32_t fit_intercept,
+                  float* w_out, float* b_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (f_in < 1 || f_out < 1 || n_rows < 0) return KVX_ERR_INVALID;
+  if (in_dtype != KVX_F32 && in_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  if (!(lambda_abs >= 0.0) || !(lambda_rel >= 0.0)) return KVX_ERR_INVALID;
+  if (!w_out || (fit_intercept && !b_out)) return KVX_ERR_INVALID;
+  if (n_rows > 0 && (!x || !y)) return KVX_ERR_INVALID;
+  if (ldx < f_in || ldy < f_out) return KVX_ERR_SHAPE;
+  if (in_dtype == KVX_BF16 && ((f_in % 8) || (f_out % 8) || (ldx % 8) || (ldy % 8))) return KVX_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < kvx_fit_ridge_workspace_size(f_in, f_out)) return KVX_ERR_WORKSPACE;
+  return launch_fit(x, ldx, y, ldy, in_dtype == KVX_F32, n_rows, f_in, f_out, lambda_abs, lambda_rel,
+                    fit_intercept, w_out, b_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+int kvx_fold_lowrank(const float* wt, const float* a, const float* b, int32_t count, int32_t f_in, int32_t f_out,
+                     int32_t rank, void* w_out, int32_t out_dtype, void* stream) {
+  if (count < 0 || f_in < 1 || f_out < 1 || rank < 0) return KVX_ERR_INVALID;
+  if (out_dtype != KVX_F32 && out_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  if (count == 0) return KVX_OK;
+  if (!wt || !w_out || (rank > 0 && (!a || !b))) return KVX_ERR_INVALID;
+  return launch_fold(wt, a, b, count, f_in, f_out, rank, w_out, out_dtype == KVX_BF16,
+                     static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,572 @@
+// Closed-form ridge fit.
+//
+// "Cross-Model KV Cache Transfer in Production" (pipeline stage 2) fits each
+// map in closed form, W = (X^T X + lambda I)^-1 X^T Y, and "Implementation
+// Guidelines" puts lambda in [1e-4, 1e-2].  Here:
+//   1. G = X^T X (upper triangle) and C = X^T Y are accumulated over the
+//      calibration rows on matrix cores (bf16 inputs, fp32 accumulation), the
+//      rows split into S ranges whose fp32 partial sums are added in fp64
+//      (fp32 inputs use an fp64-accumulated vector kernel instead);
+//   2. optional centring for an unpenalised intercept, lambda from the trace,
+//      lambda added to the diagonal (fp64, on the device);
+//   3. blocked Cholesky G + lambda I = L L^T in fp64 (64-wide blocks: diagonal
+//      factor in LDS, panel triangular solve, trailing update by an fp64
+//      tiled GEMM), then L Z = C and L^T W = Z by blocks;
+//   4. W written output-major in fp32, b = mean_y - mean_x W.
+// A non-positive pivot sets a device flag that the host reads once.
+
+#include "kvx_internal.hpp"
+
+namespace kvx {
+
+constexpr int GR_T = 256;     // Gram tile (features x features)
+constexpr int GR_BK = 64;     // rows per K step
+constexpr int GR_LDR = GR_BK + 8;
+constexpr int GR_MAX_SPLIT = 8;
+constexpr int CH_NB = 64;     // Cholesky block
+
+struct GramArgs {
+  const uint16_t* x;
+  const uint16_t* y;
+  int64_t ldx, ldy, n_rows, rows_per_split;
+  int32_t f_in, f_out, nbi, nbc, n_g, n_c, split;
+  float* part;  // [split][f_in][f_in + f_out]
+};
+
+// 8 rows x 8 features of bf16 (one u32x4 per row) -> 8 features x 8 rows.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = in[2 * w][c >> 1], b = in[2 * w + 1][c >> 1];
+      out[c][w] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void gram_kernel(const GramArgs g) {
+  constexpr int STAGE = 2 * GR_T * GR_LDR;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int32_t per = g.n_g + g.n_c;
+  const int32_t sidx = blockIdx.x / per;
+  int32_t t = blockIdx.x % per;
+  int32_t bi, bj;
+  bool is_c;
+  if (t < g.n_g) {  // upper-triangle tile index -> (bi, bj), bi <= bj
+    is_c = false;
+    bi = 0;
+    int32_t rowlen = g.nbi;
+    while (t >= rowlen) {
+      t -= rowlen;
+      ++bi;
+      --rowlen;
+    }
+    bj = bi + t;
+  } else {
+    is_c = true;
+    t -= g.n_g;
+    bi = t / g.nbc;
+    bj = t % g.nbc;
+  }
+  const int64_t k_begin = static_cast<int64_t>(sidx) * g.rows_per_split;
+  int64_t k_end = k_begin + g.rows_per_split;
+  if (k_end > g.n_rows) k_end = g.n_rows;
+  const int32_t i0 = bi * GR_T, j0 = bj * GR_T;
+  const uint16_t* q = is_c ? g.y : g.x;
+  const int64_t ldq = is_c ? g.ldy : g.ldx;
+  const int32_t fq = is_c ? g.f_out : g.f_in;
+
+  const int fi = tid & 31;  // feature group (8 features)
+  const int kb = tid >> 5;  // row group (8 rows)
+  u32x4 rp[8], rq[8];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t k = k0 + kb * 8 + e;
+      const int32_t fa = i0 + fi * 8, fb = j0 + fi * 8;
+      rp[e] = (k < k_end && fa < g.f_in) ? *reinterpret_cast<const u32x4*>(g.x + k * g.ldx + fa) : u32x4{0, 0, 0, 0};
+      rq[e] = (k < k_end && fb < fq) ? *reinterpret_cast<const u32x4*>(q + k * ldq + fb) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store = [&](int stage) {
+    uint16_t* Ps = smem + stage * STAGE;
+    uint16_t* Qs = Ps + GR_T * GR_LDR;
+    u32x4 tp[8], tq[8];
+    transpose8x8(rp, tp);
+    transpose8x8(rq, tq);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      *reinterpret_cast<u32x4*>(Ps + (fi * 8 + c) * GR_LDR + kb * 8) = tp[c];
+      *reinterpret_cast<u32x4*>(Qs + (fi * 8 + c) * GR_LDR + kb * 8) = tq[c];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int64_t nk = (k_end > k_begin) ? (k_end - k_begin + GR_BK - 1) / GR_BK : 0;
+  if (nk > 0) {
+    load(k_begin);
+    store(0);
+    __syncthreads();
+  }
+  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
+  for (int64_t ks = 0; ks < nk; ++ks) {
+    const int stage = static_cast<int>(ks & 1);
+    if (ks + 1 < nk) load(k_begin + (ks + 1) * GR_BK);
+    const uint16_t* Ps = smem + stage * STAGE;
+    const uint16_t* Qs = Ps + GR_T * GR_LDR;
+#pragma unroll
+    for (int kk = 0; kk < GR_BK / 16; ++kk) {
+      u32x4 af[4], bfr[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4*>(Ps + (wm * 128 + mi * 32 + frag_row) * GR_LDR + kk * 16 + frag_k);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        bfr[ni] = *reinterpret_cast<const u32x4*>(Qs + (wn * 128 + ni * 32 + frag_row) * GR_LDR + kk * 16 + frag_k);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[mi]),
+                                                                __builtin_bit_cast(bf16x8, bfr[ni]), acc[mi][ni], 0, 0, 0);
+    }
+    if (ks + 1 < nk) store(stage ^ 1);
+    __syncthreads();
+  }
+
+  const int64_t ldp = static_cast<int64_t>(g.f_in) + g.f_out;
+  float* part = g.part + static_cast<int64_t>(sidx) * g.f_in * ldp + (is_c ? g.f_in : 0);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t i = i0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int32_t j = j0 + wn * 128 + ni * 32 + (lane & 31);
+        if (i < g.f_in && j < fq) part[static_cast<int64_t>(i) * ldp + j] = acc[mi][ni][r];
+      }
+}
+
+// fp32 inputs: G, C and column sums in fp64 by plain loops (small fits).
+__global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ x, int64_t ldx,
+                                                       const float* __restrict__ y, int64_t ldy,
+                                                       int64_t n_rows, int32_t f_in, int32_t f_out,
+                                                       double* __restrict__ G, double* __restrict__ C) {
+  const int64_t total = static_cast<int64_t>(f_in) * (f_in + f_out);
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t i = static_cast<int32_t>(e / (f_in + f_out));
+    const int32_t j = static_cast<int32_t>(e % (f_in + f_out));
+    double s = 0.0;
+    if (j < f_in) {
+      for (int64_t k = 0; k < n_rows; ++k) s += static_cast<double>(x[k * ldx + i]) * x[k * ldx + j];
+      G[static_cast<int64_t>(i) * f_in + j] = s;
+    } else {
+      const int32_t jj = j - f_in;
+      for (int64_t k = 0; k < n_rows; ++k) s += static_cast<double>(x[k * ldx + i]) * y[k * ldy + jj];
+      C[static_cast<int64_t>(i) * f_out + jj] = s;
+    }
+  }
+}
+
+// Column sums of X and Y in fp64 (for the intercept).
+template <bool F32>
+__global__ __launch_bounds__(256) void colsum_kernel(const void* __restrict__ m, int64_t ld, int64_t n_rows,
+                                                     int32_t cols, double* __restrict__ out) {
+  const int32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  double s = 0.0;
+  for (int64_t k = 0; k < n_rows; ++k)
+    s += F32 ? static_cast<double>(static_cast<const float*>(m)[k * ld + c])
+             : static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(m)[k * ld + c]));
+  out[c] = s;
+}
+
+// Sum of the split partials in fp64; G mirrored from its upper triangle.
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int32_t split,
+                                                          int32_t f_in, int32_t f_out, double* __restrict__ G,
+                                                          double* __restrict__ C) {
+  const int64_t ldp = static_cast<int64_t>(f_in) + f_out;
+  const int64_t total = static_cast<int64_t>(f_in) * ldp;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t i = static_cast<int32_t>(e / ldp);
+    const int32_t j = static_cast<int32_t>(e % ldp);
+    int64_t src;
+    if (j < f_in) src = (i <= j) ? (static_cast<int64_t>(i) * ldp + j) : (static_cast<int64_t>(j) * ldp + i);
+    else src = static_cast<int64_t>(i) * ldp + j;
+    double s = 0.0;
+    for (int32_t q = 0; q < split; ++q) s += static_cast<double>(part[static_cast<int64_t>(q) * total + src]);
+    if (j < f_in) G[static_cast<int64_t>(i) * f_in + j] = s;
+    else C[static_cast<int64_t>(i) * f_out + (j - f_in)] = s;
+  }
+}
+
+// Centring: G -= sx sx^T / n, C -= sx sy^T / n.
+__global__ __launch_bounds__(256) void center_kernel(double* __restrict__ G, double* __restrict__ C,
+                                                     const double* __restrict__ sx, const double* __restrict__ sy,
+                                                     int32_t f_in, int32_t f_out, double inv_n) {
+  const int64_t ld = static_cast<int64_t>(f_in) + f_out;
+  const int64_t total = static_cast<int64_t>(f_in) * ld;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t i = static_cast<int32_t>(e / ld);
+    const int32_t j = static_cast<int32_t>(e % ld);
+    if (j < f_in) G[static_cast<int64_t>(i) * f_in + j] -= sx[i] * sx[j] * inv_n;
+    else C[static_cast<int64_t>(i) * f_out + (j - f_in)] -= sx[i] * sy[j - f_in] * inv_n;
+  }
+}
+
+// lambda = abs + rel * trace(G) / f_in, added to the diagonal (one block,
+// fixed summation order).
+__global__ __launch_bounds__(256) void lambda_kernel(double* __restrict__ G, int32_t f_in, double lam_abs,
+                                                     double lam_rel, double* __restrict__ lam_out) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int32_t i = threadIdx.x; i < f_in; i += 256) s += G[static_cast<int64_t>(i) * f_in + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double lam = lam_abs + lam_rel * red[0] / static_cast<double>(f_in);
+  for (int32_t i = threadIdx.x; i < f_in; i += 256) G[static_cast<int64_t>(i) * f_in + i] += lam;
+  if (threadIdx.x == 0) *lam_out = lam;
+}
+
+// ---------------------------------------------------------------- fp64 Cholesky pieces
+
+// Factor the diagonal block [k0, k0+nb) in LDS (lower), flag non-positive pivots.
+__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int32_t n, int32_t k0, int32_t nb,
+                                                         int32_t* __restrict__ flag) {
+  __shared__ double L[CH_NB][CH_NB + 1];
+  for (int e = threadIdx.x; e < nb * nb; e += 256) {
+    const int i = e / nb, j = e % nb;
+    L[i][j] = A[static_cast<int64_t>(k0 + i) * n + k0 + j];
+  }
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    if (threadIdx.x == 0) {
+      double d = L[j][j];
+      if (!(d > 0.0)) {
+        *flag = 1;
+        d = 1.0;
+      }
+      L[j][j] = sqrt(d);
+    }
+    __syncthreads();
+    const double piv = L[j][j];
+    for (int i = j + 1 + threadIdx.x; i < nb; i += 256) L[i][j] /= piv;
+    __syncthreads();
+    const int m = nb - j - 1;
+    for (int e = threadIdx.x; e < m * m; e += 256) {
+      const int i = j + 1 + e / m, c = j + 1 + e % m;
+      if (c <= i) L[i][c] -= L[i][j] * L[c][j];
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < nb * nb; e += 256) {
+    const int i = e / nb, j = e % nb;
+    if (j <= i) A[static_cast<int64_t>(k0 + i) * n + k0 + j] = L[i][j];
+  }
+}
+
+// Panel: rows r >= k0+nb, A[r][k0..k0+nb) <- A[r][k0..] L_kk^-T.  One thread per row.
+__global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ A, int32_t n, int32_t k0, int32_t nb) {
+  __shared__ double L[CH_NB][CH_NB + 1];
+  for (int e = threadIdx.x; e < nb * nb; e += 64) {
+    const int i = e / nb, j = e % nb;
+    L[i][j] = (j <= i) ? A[static_cast<int64_t>(k0 + i) * n + k0 + j] : 0.0;
+  }
+  __syncthreads();
+  const int32_t r = k0 + nb + blockIdx.x * 64 + threadIdx.x;
+  if (r >= n) return;
+  double x[CH_NB];
+  double* row = A + static_cast<int64_t>(r) * n + k0;
+#pragma unroll
+  for (int c = 0; c < CH_NB; ++c) x[c] = (c < nb) ? row[c] : 0.0;
+#pragma unroll
+  for (int c = 0; c < CH_NB; ++c) {
+    if (c < nb) {
+      double s = x[c];
+#pragma unroll
+      for (int t = 0; t < c; ++t) s -= x[t] * L[c][t];
+      x[c] = s / L[c][c];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CH_NB; ++c)
+    if (c < nb) row[c] = x[c];
+}
+
+// Left solves on a block of right-hand sides: Z = L_kk^-1 Z (forward) or
+// Z = L_kk^-T Z (backward).  One thread per column.
+template <bool TRANS>
+__global__ __launch_bounds__(256) void trsm_left_kernel(const double* __restrict__ A, int32_t n, int32_t k0,
+                                                        int32_t nb, double* __restrict__ Z, int32_t ldz, int32_t ncols) {
+  __shared__ double L[CH_NB][CH_NB + 1];
+  for (int e = threadIdx.x; e < nb * nb; e += 256) {
+    const int i = e / nb, j = e % nb;
+    L[i][j] = (j <= i) ? A[static_cast<int64_t>(k0 + i) * n + k0 + j] : 0.0;
+  }
+  __syncthreads();
+  const int32_t c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncols) return;
+  double z[CH_NB];
+#pragma unroll
+  for (int i = 0; i < CH_NB; ++i) z[i] = (i < nb) ? Z[static_cast<int64_t>(k0 + i) * ldz + c] : 0.0;
+  if (!TRANS) {
+#pragma unroll
+    for (int i = 0; i < CH_NB; ++i) {
+      if (i < nb) {
+        double s = z[i];
+#pragma unroll
+        for (int t = 0; t < i; ++t) s -= L[i][t] * z[t];
+        z[i] = s / L[i][i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = CH_NB - 1; i >= 0; --i) {
+      if (i < nb) {
+        double s = z[i];
+#pragma unroll
+        for (int t = i + 1; t < CH_NB; ++t)
+          if (t < nb) s -= L[t][i] * z[t];
+        z[i] = s / L[i][i];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CH_NB; ++i)
+    if (i < nb) Z[static_cast<int64_t>(k0 + i) * ldz + c] = z[i];
+}
+
+// C[M x N] -= A * B with A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].
+// 64 x 64 tiles, 16 x 16 threads with 4 x 4 outputs each.  lower_only skips
+// tiles strictly above the diagonal (tile row < tile column).
+__global__ __launch_bounds__(256) void gemm64_kernel(int32_t M, int32_t N, int32_t K, const double* __restrict__ A,
+                                                     int64_t sam, int64_t sak, const double* __restrict__ B,
+                                                     int64_t sbk, int64_t sbn, double* __restrict__ C, int64_t ldc,
+                                                     int32_t lower_only) {
+  const int32_t bm = blockIdx.y, bn = blockIdx.x;
+  if (lower_only && bm < bn) return;
+  __shared__ double As[16][65];
+  __shared__ double Bs[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int32_t m0 = bm * 64, n0 = bn * 64;
+  double acc[4][4] = {};
+  for (int32_t k0 = 0; k0 < K; k0 += 16) {
+    for (int e = threadIdx.x; e < 1024; e += 256) {
+      const int mm = e & 63, kk = e >> 6;
+      const int32_t m = m0 + mm, k = k0 + kk;
+      As[kk][mm] = (m < M && k < K) ? A[m * sam + k * sak] : 0.0;
+      const int32_t nn = n0 + mm;
+      Bs[kk][mm] = (nn < N && k < K) ? B[k * sbk + nn * sbn] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t m = m0 + ty + 16 * i, nn = n0 + tx + 16 * j;
+      if (m < M && nn < N) C[m * ldc + nn] -= acc[i][j];
+    }
+}
+
+// w_out[o][f] = W[f][o] (fp32); b_out[o] = mean_y[o] - sum_f mean_x[f] W[f][o].
+__global__ __launch_bounds__(256) void fit_output_kernel(const double* __restrict__ W, int32_t f_in, int32_t f_out,
+                                                         float* __restrict__ w_out, float* __restrict__ b_out,
+                                                         const double* __restrict__ sx, const double* __restrict__ sy,
+                                                         double inv_n) {
+  const int64_t total = static_cast<int64_t>(f_in) * f_out;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t o = static_cast<int32_t>(e / f_in), f = static_cast<int32_t>(e % f_in);
+    w_out[e] = static_cast<float>(W[static_cast<int64_t>(f) * f_out + o]);
+  }
+  if (b_out) {
+    for (int32_t o = blockIdx.x * blockDim.x + threadIdx.x; o < f_out; o += gridDim.x * blockDim.x) {
+      double s = sy[o] * inv_n;
+      for (int32_t f = 0; f < f_in; ++f) s -= sx[f] * inv_n * W[static_cast<int64_t>(f) * f_out + o];
+      b_out[o] = static_cast<float>(s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+size_t fit_ws_bytes(int32_t f_in, int32_t f_out) {
+  Carve c(nullptr);
+  c.take<double>(static_cast<size_t>(f_in) * f_in);
+  c.take<double>(static_cast<size_t>(f_in) * f_out);
+  c.take<double>(f_in);
+  c.take<double>(f_out);
+  c.take<double>(4);
+  c.take<int32_t>(64);
+  c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  return c.used + 256;
+}
+
+static unsigned grid_for(int64_t n) {
+  int64_t b = ceil_div(n, 256);
+  if (b > 16384) b = 16384;
+  return static_cast<unsigned>(b < 1 ? 1 : b);
+}
+
+int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32, int64_t n_rows,
+               int32_t f_in, int32_t f_out, double lam_abs, double lam_rel, int32_t fit_intercept,
+               float* w_out, float* b_out, void* ws, hipStream_t s) {
+  Carve cv(ws);
+  double* G = cv.take<double>(static_cast<size_t>(f_in) * f_in);
+  double* C = cv.take<double>(static_cast<size_t>(f_in) * f_out);
+  double* sx = cv.take<double>(f_in);
+  double* sy = cv.take<double>(f_out);
+  double* lam = cv.take<double>(4);
+  int32_t* flag = cv.take<int32_t>(64);
+  float* part = cv.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  if (int st = launch_fill_i32(flag, 1, 0, s)) return st;
+
+  // 1. Gram and cross products
+  if (in_f32) {
+    gram_f32_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(
+        static_cast<const float*>(x), ldx, static_cast<const float*>(y), ldy, n_rows, f_in, f_out, G, C);
+    KVX_LAUNCH_CHECK();
+  } else {
+    GramArgs g{};
+    g.x = static_cast<const uint16_t*>(x);
+    g.y = static_cast<const uint16_t*>(y);
+    g.ldx = ldx;
+    g.ldy = ldy;
+    g.n_rows = n_rows;
+    g.f_in = f_in;
+    g.f_out = f_out;
+    g.nbi = static_cast<int32_t>(ceil_div(f_in, GR_T));
+    g.nbc = static_cast<int32_t>(ceil_div(f_out, GR_T));
+    g.n_g = g.nbi * (g.nbi + 1) / 2;
+    g.n_c = g.nbi * g.nbc;
+    const int cus = device_cu_count();
+    int split = static_cast<int>(ceil_div(2 * cus, g.n_g + g.n_c));
+    if (split > GR_MAX_SPLIT) split = GR_MAX_SPLIT;
+    const int64_t max_split = ceil_div(n_rows, GR_BK);
+    if (split > max_split) split = static_cast<int>(max_split > 0 ? max_split : 1);
+    if (split < 1) split = 1;
+    g.split = split;
+    g.rows_per_split = ceil_div(ceil_div(n_rows, split), GR_BK) * GR_BK;
+    g.part = part;
+    gram_kernel<<<static_cast<unsigned>(split * (g.n_g + g.n_c)), 256, 0, s>>>(g);
+    KVX_LAUNCH_CHECK();
+    gram_reduce_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(part, split, f_in,
+                                                                                            f_out, G, C);
+    KVX_LAUNCH_CHECK();
+  }
+
+  // 2. centring and lambda
+  const double inv_n = n_rows > 0 ? 1.0 / static_cast<double>(n_rows) : 0.0;
+  if (fit_intercept) {
+    if (in_f32) {
+      colsum_kernel<true><<<grid_for(f_in), 256, 0, s>>>(x, ldx, n_rows, f_in, sx);
+      colsum_kernel<true><<<grid_for(f_out), 256, 0, s>>>(y, ldy, n_rows, f_out, sy);
+    } else {
+      colsum_kernel<false><<<grid_for(f_in), 256, 0, s>>>(x, ldx, n_rows, f_in, sx);
+      colsum_kernel<false><<<grid_for(f_out), 256, 0, s>>>(y, ldy, n_rows, f_out, sy);
+    }
+    KVX_LAUNCH_CHECK();
+    center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
+                                                                                        inv_n);
+    KVX_LAUNCH_CHECK();
+  }
+  lambda_kernel<<<1, 256, 0, s>>>(G, f_in, lam_abs, lam_rel, lam);
+  KVX_LAUNCH_CHECK();
+
+  // 3. Cholesky and the two block triangular solves
+  const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
+  for (int32_t kb = 0; kb < nb_total; ++kb) {
+    const int32_t k0 = kb * CH_NB;
+    const int32_t nb = min(CH_NB, f_in - k0);
+    potrf_diag_kernel<<<1, 256, 0, s>>>(G, f_in, k0, nb, flag);
+    KVX_LAUNCH_CHECK();
+    const int32_t rest = f_in - k0 - nb;
+    if (rest > 0) {
+      trsm_panel_kernel<<<static_cast<unsigned>(ceil_div(rest, 64)), 64, 0, s>>>(G, f_in, k0, nb);
+      KVX_LAUNCH_CHECK();
+      // trailing lower update: G[r][c] -= P[r] . P[c] for r, c >= k0+nb
+      const int32_t t = static_cast<int32_t>(ceil_div(rest, 64));
+      const double* P = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
+      double* Ct = G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
+      gemm64_kernel<<<dim3(t, t), 256, 0, s>>>(rest, rest, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, 1);
+      KVX_LAUNCH_CHECK();
+    }
+  }
+  // forward: L Z = C
+  const unsigned col_blocks = static_cast<unsigned>(ceil_div(f_out, 256));
+  for (int32_t kb = 0; kb < nb_total; ++kb) {
+    const int32_t k0 = kb * CH_NB;
+    const int32_t nb = min(CH_NB, f_in - k0);
+    trsm_left_kernel<false><<<col_blocks, 256, 0, s>>>(G, f_in, k0, nb, C, f_out, f_out);
+    KVX_LAUNCH_CHECK();
+    const int32_t rest = f_in - k0 - nb;
+    if (rest > 0) {
+      const double* Lb = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
+      const double* Zk = C + static_cast<int64_t>(k0) * f_out;
+      double* Cr = C + static_cast<int64_t>(k0 + nb) * f_out;
+      gemm64_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 64)), static_cast<unsigned>(ceil_div(rest, 64))), 256, 0,
+                      s>>>(rest, f_out, nb, Lb, f_in, 1, Zk, f_out, 1, Cr, f_out, 0);
+      KVX_LAUNCH_CHECK();
+    }
+  }
+  // backward: L^T W = Z
+  for (int32_t kb = nb_total - 1; kb >= 0; --kb) {
+    const int32_t k0 = kb * CH_NB;
+    const int32_t nb = min(CH_NB, f_in - k0);
+    trsm_left_kernel<true><<<col_blocks, 256, 0, s>>>(G, f_in, k0, nb, C, f_out, f_out);
+    KVX_LAUNCH_CHECK();
+    if (k0 > 0) {
+      // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_k
+      const double* Lr = G + static_cast<int64_t>(k0) * f_in;
+      const double* Wk = C + static_cast<int64_t>(k0) * f_out;
+      gemm64_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 64)), static_cast<unsigned>(ceil_div(k0, 64))), 256, 0,
+                      s>>>(k0, f_out, nb, Lr, 1, f_in, Wk, f_out, 1, C, f_out, 0);
+      KVX_LAUNCH_CHECK();
+    }
+  }
+
+  // 4. outputs
+  fit_output_kernel<<<grid_for(static_cast<int64_t>(f_in) * f_out), 256, 0, s>>>(
+      C, f_in, f_out, w_out, fit_intercept ? b_out : nullptr, sx, sy, inv_n);
+  KVX_LAUNCH_CHECK();
+
+  int32_t host_flag = 0;
+  KVX_HIP_TRY(hipMemcpyAsync(&host_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  KVX_HIP_TRY(hipStreamSynchronize(s));
+  return host_flag ? KVX_ERR_NOT_SPD : KVX_OK;
+}
+
+}  // namespace kvx

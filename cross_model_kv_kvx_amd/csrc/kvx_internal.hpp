@@ -1,0 +1,117 @@
+// Launchers shared between the translation units of the kvx library.
+#pragma once
+
+#include "kvx_common.hpp"
+
+namespace kvx {
+
+// Largest layer count a cache may have (layer indices travel as uint8).
+constexpr int MAX_LAYERS = 255;
+constexpr int MAX_TAPS = 7;
+
+// Zero-fill of int32 words by a kernel (no runtime memset, so the launches of
+// a call can be captured into a graph).
+int launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// ---------------------------------------------------------------- alignment / runs
+size_t align_ws_bytes(int32_t n_recv);
+int launch_align(const int32_t* send_end, int32_t n_send, const int32_t* recv_end,
+                 int32_t n_recv, int32_t* out, void* ws, hipStream_t s);
+
+struct Runs {
+  int32_t* uniq;          // [N]   value of each run (clamped into [0, n_send))
+  int32_t* run_begin;     // [N+1] first row of each run, run_begin[U] = N
+  int32_t* recv_to_uniq;  // [N]   run index of each row
+  int32_t* n_uniq;        // [1]   U
+};
+size_t runs_ws_bytes(int32_t n);
+int launch_runs(const int32_t* map, int32_t n, int32_t n_send, Runs r, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- rotation
+// tab[p][j] = (cos, sin)(p * base^(-2j/head_dim)), p < n_pos, j < head_dim/2,
+// evaluated in fp64 and rounded to fp32.
+int launch_rope_table(float2* tab, int32_t n_pos, int32_t head_dim, double base, hipStream_t s);
+
+// Rotated-back sender keys of the unique rows as fp16:
+// out[s][u][h][c] for u < U (device count), every sender layer s with
+// layer_used[s] != 0.  Requires head_dim == 128, bf16 cache.
+int launch_derotate_rows(const uint16_t* k_send, int32_t send_layers, int32_t send_tokens,
+                         int32_t heads, const uint8_t* layer_used, const Runs& r,
+                         int32_t rows_cap, const float2* tab_send, uint16_t* out, hipStream_t s);
+
+// ---------------------------------------------------------------- flattened translation
+struct FlatRole {
+  const void* a_src;       // sender cache (bf16) or rotated-back rows (fp16)
+  int64_t a_layer_stride;  // elements between consecutive sender layers of a_src
+  int32_t a_compact;       // 1: rows of a_src are run indices u; 0: sender tokens uniq[u]
+  int32_t a_f16;           // 1: a_src holds fp16, 0: bf16
+  const void* wt;          // [L_R][F_out][F_in]
+  const float* bias;       // [L_R][F_out] or null
+  uint16_t* out;           // [L_R][N_R][F_out] bf16
+  int32_t rotate;          // rotate outputs at the receiver position
+};
+
+struct FlatProblem {
+  int32_t send_layers, send_tokens, recv_layers, recv_tokens;
+  int32_t f_in, f_out, n_taps, send_row;  // send_row = H_S * d_S
+  int32_t w_f32;
+  const int32_t* taps;  // host [L_R][n_taps]
+  const float2* tab_recv;
+  Runs runs;
+};
+
+int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s);
+
+// ---------------------------------------------------------------- per-head translation (bf16)
+struct HeadProblem {
+  int32_t send_layers, send_tokens, recv_layers, recv_tokens, heads;
+  int32_t w_f32;
+  const int32_t* taps;         // host [L_R][1]
+  const int32_t* recv_to_send;
+};
+struct HeadRole {
+  const uint16_t* x;   // [L_S][N_S][H][128]
+  const void* wt;      // [L_R][H][128][128]
+  const float* bias;   // [L_R][H*128] or null
+  uint16_t* out;       // [L_R][N_R][H][128]
+};
+int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hipStream_t s);
+
+// ---------------------------------------------------------------- fp32 caches (any shape)
+struct F32Problem {
+  int32_t send_layers, send_tokens, send_heads, send_dim;
+  int32_t recv_layers, recv_tokens, recv_heads, recv_dim;
+  int32_t n_taps, per_head, w_f32;
+  const int32_t* taps;  // host [L_R][n_taps]
+  const int32_t* recv_to_send;
+  const float2* tab_send;  // null when the sender keys are unrotated
+  const float2* tab_recv;  // null when the receiver keys are unrotated
+};
+struct F32Role {
+  const float* x;
+  const void* wt;
+  const float* bias;
+  float* out;
+  int32_t derotate, rotate;
+};
+int launch_f32(const F32Problem& p, const F32Role* roles, int n_roles, hipStream_t s);
+
+// ---------------------------------------------------------------- fold
+int launch_fold(const float* wt, const float* a, const float* b, int64_t count, int32_t f_in,
+                int32_t f_out, int32_t rank, void* out, int32_t out_bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- features / fit
+int launch_gather(const void* cache, int32_t cache_f32, int32_t send_tokens, int32_t row,
+                  int64_t layer_stride, const int32_t* taps, int32_t n_taps,
+                  const int32_t* recv_to_send, int32_t n_rows, double rope_base, int32_t head_dim,
+                  void* out, hipStream_t s);
+
+size_t fit_ws_bytes(int32_t f_in, int32_t f_out);
+int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32,
+               int64_t n_rows, int32_t f_in, int32_t f_out, double lam_abs, double lam_rel,
+               int32_t fit_intercept, float* w_out, float* b_out, void* ws, hipStream_t s);
+
+// Compute-unit count of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace kvx

@@ -1,0 +1,282 @@
+"""Python binding of ``libkvx.so`` (argument marshalling only).
+
+Every function here converts torch tensors to raw pointers and sizes, picks
+the current HIP stream and calls the C entry point of the same name; all
+computation runs in the library's HIP kernels.  Device workspaces are
+allocated with torch when the caller does not pass one.
+
+Raises ``KvxError`` with the library's status when a call fails, and
+``RuntimeError`` at import of a call when the library has not been built
+(there is no other implementation to fall back on).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvx.so")
+
+F32, BF16 = 0, 1
+OK, ERR_INVALID, ERR_SHAPE, ERR_WORKSPACE, ERR_NOT_SPD, ERR_HIP, ERR_UNSUPPORTED = range(7)
+
+EXPORTS = (
+    "kvx_status_string", "kvx_align_workspace_size", "kvx_align_tokens", "kvx_layer_map",
+    "kvx_translate_workspace_size", "kvx_translate", "kvx_translate_timed", "kvx_gather_features",
+    "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fold_lowrank",
+)
+
+
+class KvxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("tokens", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built beforehand by ``cross_model_kv_kvx_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m cross_model_kv_kvx_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+        dp = ctypes.POINTER(CacheDesc)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        sig = {
+            "kvx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "kvx_align_workspace_size": (sz, [i32]),
+            "kvx_align_tokens": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, sz, vp]),
+            "kvx_layer_map": (ctypes.c_int, [i32, i32, i32, i32, ip]),
+            "kvx_translate_workspace_size": (sz, [dp, dp, i32, i32]),
+            "kvx_translate": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp, vp,
+                                             vp, sz, vp]),
+            "kvx_translate_timed": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp, vp,
+                                                   vp, sz, vp, ctypes.POINTER(ctypes.c_float)]),
+            "kvx_gather_features": (ctypes.c_int, [dp, vp, i32, vp, i32, ip, i32, vp, vp]),
+            "kvx_fit_ridge_workspace_size": (sz, [i32, i32]),
+            "kvx_fit_ridge": (ctypes.c_int, [vp, i64, vp, i64, i32, i64, i32, i32, dbl, dbl, i32, vp, vp, vp, sz,
+                                             vp]),
+            "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kvx_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise KvxError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def cache_desc(cache: torch.Tensor, rope_base: float = 0.0, tokens: Optional[int] = None) -> CacheDesc:
+    """Descriptor of a [layers][tokens][heads][head_dim] cache tensor."""
+    L, N, H, d = cache.shape
+    return CacheDesc(int(L), int(N if tokens is None else tokens), int(H), int(d), _dtype_code(cache),
+                     float(rope_base))
+
+
+# ---------------------------------------------------------------- entry points
+
+
+def align_tokens(send_end: torch.Tensor, recv_end: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvx_align_tokens: receiver->sender token map (device int32)."""
+    _need(send_end, "send_end", torch.int32)
+    _need(recv_end, "recv_end", torch.int32)
+    n_r = recv_end.numel()
+    if out is None:
+        out = torch.empty(n_r, dtype=torch.int32, device=recv_end.device)
+    _need(out, "out", torch.int32)
+    ws = _workspace(lib().kvx_align_workspace_size(n_r), recv_end.device, workspace)
+    st = lib().kvx_align_tokens(_ptr(send_end), send_end.numel(), _ptr(recv_end), n_r, _ptr(out), _ptr(ws),
+                                ws.numel(), _stream(stream))
+    _check(st, "kvx_align_tokens")
+    return out
+
+
+def layer_map(send_layers: int, recv_layers: int, n_taps: int = 3, tap_stride: int = 4) -> np.ndarray:
+    """kvx_layer_map: host int32 [recv_layers][n_taps]."""
+    out = np.zeros((recv_layers, n_taps), dtype=np.int32)
+    st = lib().kvx_layer_map(int(send_layers), int(recv_layers), int(n_taps), int(tap_stride),
+                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    _check(st, "kvx_layer_map")
+    return out
+
+
+def translate_workspace_size(send: CacheDesc, recv: CacheDesc, n_taps: int, per_head: bool) -> int:
+    return int(lib().kvx_translate_workspace_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps),
+                                                   int(bool(per_head))))
+
+
+def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], recv_to_send: torch.Tensor,
+              taps, wt_k: Optional[torch.Tensor], wt_v: Optional[torch.Tensor],
+              b_k: Optional[torch.Tensor] = None, b_v: Optional[torch.Tensor] = None, *,
+              recv_layers: Optional[int] = None, recv_heads: Optional[int] = None,
+              recv_head_dim: Optional[int] = None, per_head: bool = False,
+              send_rope_base: float = 0.0, recv_rope_base: float = 0.0,
+              k_recv: Optional[torch.Tensor] = None, v_recv: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None, stage_ms: Optional[list] = None):
+    """kvx_translate.  Returns (k_recv, v_recv) (either None when its role is
+    skipped).  ``taps``: host int32 [L_R][n_taps] (numpy).  With a list
+    ``stage_ms``, calls kvx_translate_timed instead (synchronous) and appends
+    the [preparation, translation kernel] device times in ms."""
+    ref = k_send if k_send is not None else v_send
+    if ref is None:
+        raise ValueError("at least one role is needed")
+    taps = np.ascontiguousarray(taps, dtype=np.int32)
+    L_R, n_taps = taps.shape
+    if recv_layers is not None and recv_layers != L_R:
+        raise ValueError("taps rows must equal recv_layers")
+    _need(recv_to_send, "recv_to_send", torch.int32)
+    for name, t in (("k_send", k_send), ("v_send", v_send)):
+        if t is not None:
+            _need(t, name, ref.dtype)
+    w_ref = wt_k if wt_k is not None else wt_v
+    H_R = recv_heads if recv_heads is not None else ref.shape[2]
+    d_R = recv_head_dim if recv_head_dim is not None else ref.shape[3]
+    N_R = recv_to_send.numel()
+    send = cache_desc(ref, send_rope_base)
+    recv = CacheDesc(int(L_R), int(N_R), int(H_R), int(d_R), _dtype_code(ref), float(recv_rope_base))
+    for name, t in (("wt_k", wt_k), ("wt_v", wt_v)):
+        if t is not None:
+            _need(t, name, w_ref.dtype)
+    for name, t in (("b_k", b_k), ("b_v", b_v)):
+        if t is not None:
+            _need(t, name, torch.float32)
+    if k_send is not None and k_recv is None:
+        k_recv = torch.empty((L_R, N_R, H_R, d_R), dtype=ref.dtype, device=ref.device)
+    if v_send is not None and v_recv is None:
+        v_recv = torch.empty((L_R, N_R, H_R, d_R), dtype=ref.dtype, device=ref.device)
+    ws = _workspace(translate_workspace_size(send, recv, n_taps, per_head), ref.device, workspace)
+    args = [ctypes.byref(send), _ptr(k_send), _ptr(v_send), ctypes.byref(recv),
+            _ptr(k_recv) if k_send is not None else None, _ptr(v_recv) if v_send is not None else None,
+            _ptr(recv_to_send), taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_taps),
+            int(bool(per_head)), _dtype_code(w_ref), _ptr(wt_k), _ptr(wt_v), _ptr(b_k), _ptr(b_v),
+            _ptr(ws), ws.numel(), _stream(stream)]
+    if stage_ms is None:
+        _check(lib().kvx_translate(*args), "kvx_translate")
+    else:
+        ms = (ctypes.c_float * 2)()
+        _check(lib().kvx_translate_timed(*args, ms), "kvx_translate_timed")
+        stage_ms.extend([float(ms[0]), float(ms[1])])
+    return (k_recv if k_send is not None else None), (v_recv if v_send is not None else None)
+
+
+def gather_features(kv_send: torch.Tensor, recv_to_send: torch.Tensor, taps_of_layer: Sequence[int], *,
+                    derotate: bool = False, rope_base: float = 0.0, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """kvx_gather_features: [n_rows][n_taps*H*d] in the cache dtype."""
+    _need(kv_send, "kv_send")
+    _need(recv_to_send, "recv_to_send", torch.int32)
+    taps = np.ascontiguousarray(taps_of_layer, dtype=np.int32).ravel()
+    n = recv_to_send.numel()
+    L, N, H, d = kv_send.shape
+    if out is None:
+        out = torch.empty((n, taps.size * H * d), dtype=kv_send.dtype, device=kv_send.device)
+    _need(out, "out", kv_send.dtype)
+    send = cache_desc(kv_send, rope_base)
+    st = lib().kvx_gather_features(ctypes.byref(send), _ptr(kv_send), int(bool(derotate)), _ptr(recv_to_send), n,
+                                   taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), taps.size, _ptr(out),
+                                   _stream(stream))
+    _check(st, "kvx_gather_features")
+    return out
+
+
+def fit_ridge(x: torch.Tensor, y: torch.Tensor, *, lambda_abs: float = 0.0, lambda_rel: float = 0.0,
+              fit_intercept: bool = False, w_out: Optional[torch.Tensor] = None,
+              b_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvx_fit_ridge on row-major 2-D x [n][f_in], y [n][f_out].  Returns
+    (wt fp32 [f_out][f_in], b fp32 [f_out] or None)."""
+    if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
+        raise ValueError("x and y must be 2-D with equal row counts")
+    if x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("rows of x and y must be contiguous")
+    if x.dtype != y.dtype:
+        raise TypeError("x and y must share a dtype")
+    n, f_in = x.shape
+    f_out = y.shape[1]
+    if w_out is None:
+        w_out = torch.empty((f_out, f_in), dtype=torch.float32, device=x.device)
+    if fit_intercept and b_out is None:
+        b_out = torch.empty(f_out, dtype=torch.float32, device=x.device)
+    ws = _workspace(lib().kvx_fit_ridge_workspace_size(f_in, f_out), x.device, workspace)
+    st = lib().kvx_fit_ridge(_ptr(x), x.stride(0), _ptr(y), y.stride(0), _dtype_code(x), n, f_in, f_out,
+                             float(lambda_abs), float(lambda_rel), int(bool(fit_intercept)), _ptr(w_out),
+                             _ptr(b_out) if fit_intercept else None, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kvx_fit_ridge")
+    return w_out, (b_out if fit_intercept else None)
+
+
+def fold_lowrank(wt: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvx_fold_lowrank on [count][f_out][f_in] maps with a [count][f_in][r],
+    b [count][f_out][r] (a single map may drop the leading dimension)."""
+    squeeze = wt.dim() == 2
+    if squeeze:
+        wt, a, b = wt[None], a[None], b[None]
+    for name, t in (("wt", wt), ("a", a), ("b", b)):
+        _need(t, name, torch.float32)
+    count, f_out, f_in = wt.shape
+    rank = a.shape[-1]
+    if out is None:
+        out = torch.empty((count, f_out, f_in), dtype=out_dtype, device=wt.device)
+    code = BF16 if out.dtype == torch.bfloat16 else F32
+    st = lib().kvx_fold_lowrank(_ptr(wt), _ptr(a), _ptr(b), count, f_in, f_out, rank, _ptr(out), code,
+                                _stream(stream))
+    _check(st, "kvx_fold_lowrank")
+    return out[0] if squeeze else out

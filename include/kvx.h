@@ -1,0 +1,244 @@
+/*
+ * kvx: translation of a sender model's per-layer KV cache into a receiver
+ * model's KV space without re-running the receiver's prefill, on MI355X
+ * (gfx950).
+ *
+ * The operation is the translator of the interface KV_B(C) = T_{A->B}(KV_A(C))
+ * ("A Universal Context-Reuse Layer for Cross-Model KV Sharing", section 2.2),
+ * built from:
+ *   - token alignment on shared character-end boundaries, forward fill, no
+ *     averaging ("Prefill-Free Cross-Family KV Cache Transfer for
+ *     Heterogeneous Multi-Agent LLMs", Key Contributions item 1 and
+ *     Methodology step 1);
+ *   - proportional layer matching with sender taps at -4, 0, +4 and
+ *     flattened cross-head affine maps for K and V (same page, Methodology
+ *     step 2), rank-16 corrections folded into one fixed affine map per layer
+ *     and role (Methodology step 3);
+ *   - RoPE stripping of cached keys, per-head d x d maps, the proportional
+ *     layer formula and RoPE re-application at the receiver, and the closed
+ *     form ridge fit W = (X^T X + lambda I)^-1 X^T Y ("Cross-Model KV Cache
+ *     Transfer in Production: ... Closed-Form Ridge Projections ...",
+ *     section "The Closed-Form Ridge Mapping Pipeline", stages 1-4).
+ *
+ * Conventions shared by every call:
+ *   - Buffers are owned by the caller.  Pointers documented as "device" must
+ *     point to memory of the device that is current on the calling thread;
+ *     pointers documented as "host" are ordinary host memory.
+ *   - Caches are dense [layers][tokens][kv_heads][head_dim] arrays, K and V
+ *     separate, element type given by kvx_dtype.
+ *   - Token offsets and maps are int32.
+ *   - Streams are hipStream_t passed as void* (NULL = the default stream).
+ *   - Argument and shape errors are reported before anything is launched.
+ *     HIP runtime failures return KVX_ERR_HIP.  No C++ exception crosses
+ *     this interface.
+ *   - The library keeps no per-call state; calls on different streams with
+ *     disjoint buffers may run concurrently.
+ */
+#ifndef KVX_H
+#define KVX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVX_OK = 0,
+  KVX_ERR_INVALID = 1,     /* bad argument value (null pointer, bad offsets, tap out of range) */
+  KVX_ERR_SHAPE = 2,       /* inconsistent shapes between arguments */
+  KVX_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
+  KVX_ERR_NOT_SPD = 4,     /* regularised Gram matrix not positive definite */
+  KVX_ERR_HIP = 5,         /* a HIP runtime call failed */
+  KVX_ERR_UNSUPPORTED = 6  /* a valid combination this build does not implement */
+} kvx_status;
+
+typedef enum { KVX_F32 = 0, KVX_BF16 = 1 } kvx_dtype;
+
+/* Shape of one role (K or V) of one model's cache. */
+typedef struct {
+  int32_t layers;     /* >= 1, <= 255 */
+  int32_t tokens;     /* >= 0 */
+  int32_t kv_heads;   /* >= 1 */
+  int32_t head_dim;   /* >= 1; even when rope_base > 0 */
+  int32_t dtype;      /* kvx_dtype of the cache elements */
+  double rope_base;   /* > 0: keys are stored rotated (RoPE, half-split pairs
+                         (c, c + head_dim/2), angle pos * base^(-2j/head_dim));
+                         0: keys are stored unrotated.  Values are never rotated. */
+} kvx_cache_desc;
+
+/* Human-readable name of a status code (static string). */
+const char* kvx_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Token alignment ("Prefill-Free Cross-Family KV Cache Transfer ...",
+ * Key Contributions 1, Methodology 1).
+ *
+ * send_end, recv_end: device int32 exclusive character-end offsets of the
+ *   sender's n_send and the receiver's n_recv tokens over one shared string;
+ *   each strictly increasing and > 0.
+ * recv_to_send: device int32 [n_recv] output.  For receiver token i, let b be
+ *   the largest offset that ends both a sender and a receiver token and is
+ *   <= recv_end[i]; recv_to_send[i] is the sender token ending at b (so a
+ *   receiver token whose end is shared takes the sender token ending at the
+ *   same character, and an unshared one is forward-filled).  Receiver tokens
+ *   before the first shared boundary map to sender token 0.  The result is
+ *   non-decreasing.
+ * workspace: device scratch of at least kvx_align_workspace_size(n_recv)
+ *   bytes.
+ * Synchronises `stream` once to read a device-side validity flag: offsets
+ *   that are not strictly increasing and positive give KVX_ERR_INVALID (the
+ *   output is then unspecified).  n_recv == 0 is a no-op; n_send == 0 with
+ *   n_recv > 0 is KVX_ERR_SHAPE.
+ * ---------------------------------------------------------------------- */
+size_t kvx_align_workspace_size(int32_t n_recv);
+int kvx_align_tokens(const int32_t* send_end, int32_t n_send,
+                     const int32_t* recv_end, int32_t n_recv,
+                     int32_t* recv_to_send, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Layer matching ("Prefill-Free ...", Methodology 2: proportional depth and
+ * taps at -4, 0, +4; "Cross-Model KV Cache Transfer in Production", stage 3).
+ *
+ * Host only.  taps_out: host int32 [recv_layers][n_taps].  Receiver layer l
+ * matches m = round(l * (send_layers-1) / (recv_layers-1)) (halves rounded
+ * up, exact integer arithmetic; m = 0 when recv_layers == 1) and reads sender
+ * layers m + (t - (n_taps-1)/2) * tap_stride for t = 0..n_taps-1, clamped to
+ * [0, send_layers-1], duplicates kept.  n_taps must be odd, 1..7.
+ * ---------------------------------------------------------------------- */
+int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps,
+                  int32_t tap_stride, int32_t* taps_out);
+
+/* ------------------------------------------------------------------------
+ * Translation ("Cross-Model KV Cache Transfer in Production", pipeline
+ * stages 1, 2 and 4; "Prefill-Free ...", Methodology 2).
+ *
+ * For every receiver layer l, receiver token i and role (K, V):
+ *   j = recv_to_send[i];
+ *   x = concat over t of the sender row cache[taps[l][t]][j][:][:]
+ *       (feature f = t*H_S*d_S + h*d_S + c); keys of a sender with
+ *       rope_base > 0 are first rotated back by position j;
+ *   y = x W_l + b_l                  (flattened, per_head = 0), or
+ *   y_h = x_h W_{l,h} + b_{l,h}      (per_head = 1: one tap, H and d equal on
+ *                                     both sides, one d x d map per head);
+ *   keys of a receiver with rope_base > 0 are then rotated to position i.
+ *   The result is rounded to the receiver's dtype (nearest even).
+ *
+ * send, recv: host descriptors.  Layers, heads and head_dim must agree
+ *   between K and V of one side; send->tokens is the sender token count,
+ *   recv->tokens the receiver token count.
+ * k_send, v_send: device caches of the sender (send->dtype).
+ * k_recv, v_recv: device output caches of the receiver (recv->dtype; must
+ *   equal send->dtype).  Either role may be NULL together with its maps to
+ *   skip that role.
+ * recv_to_send: device int32 [recv->tokens]; values must lie in
+ *   [0, send->tokens) (values outside are clamped on the device, never read
+ *   out of bounds).
+ * taps: host int32 [recv->layers][n_taps], values in [0, send->layers).
+ * w_dtype: element type of the maps (KVX_F32 or KVX_BF16).
+ * wt_k, wt_v: device maps stored output-major:
+ *   flattened: [L_R][H_R*d_R][n_taps*H_S*d_S], wt[l][o][f] multiplies
+ *              feature f into output o;
+ *   per_head:  [L_R][H][d][d], wt[l][h][o][c].
+ * b_k, b_v: device fp32 bias [L_R][H_R*d_R], or NULL for none.  The bias is
+ *   added before the receiver rotation.
+ * workspace: device scratch of kvx_translate_workspace_size(...) bytes.
+ * Asynchronous on `stream`.
+ *
+ * Arithmetic: bf16 caches with bf16 maps use bf16 matrix cores; fp32 maps are
+ * applied as a bf16 high part plus a bf16 low part; keys rotated back from a
+ * rotated sender are fed as fp16 (with the map converted to fp16); fp32
+ * caches use fp32 arithmetic.  Accumulation is fp32 everywhere.
+ * Supported: recv->dtype == send->dtype; bf16 caches need head_dim == 128
+ * on both sides and, for per_head, no rotation on either side.
+ * ---------------------------------------------------------------------- */
+size_t kvx_translate_workspace_size(const kvx_cache_desc* send,
+                                    const kvx_cache_desc* recv,
+                                    int32_t n_taps, int32_t per_head);
+int kvx_translate(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                  const kvx_cache_desc* recv, void* k_recv, void* v_recv,
+                  const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                  int32_t per_head, int32_t w_dtype, const void* wt_k, const void* wt_v,
+                  const float* b_k, const float* b_v,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Same translation as kvx_translate, synchronous, reporting elapsed device
+ * time of its two phases measured with HIP events on `stream`:
+ * stage_ms[0] = preparation (run compaction, rotation tables, rotated-back
+ * key rows), stage_ms[1] = the translation kernel itself.  stage_ms: host
+ * float[2] (both 0 when nothing was launched).  For benchmarks and
+ * profiling; the results are bit-identical to kvx_translate. */
+int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                        const kvx_cache_desc* recv, void* k_recv, void* v_recv,
+                        const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                        int32_t per_head, int32_t w_dtype, const void* wt_k, const void* wt_v,
+                        const float* b_k, const float* b_v,
+                        void* workspace, size_t ws_bytes, void* stream, float* stage_ms);
+
+/* ------------------------------------------------------------------------
+ * Feature gather: the flattened sender features that the translation feeds
+ * to the map, written out for a fit ("Prefill-Free ...", Methodology 2).
+ *
+ * send: host descriptor; kv_send: device cache of one role.
+ * derotate: nonzero rotates keys back by the sender position (send->rope_base
+ *   must be > 0).
+ * recv_to_send: device int32 [n_rows]; taps_of_layer: host int32 [n_taps].
+ * x_out: device [n_rows][n_taps*H*d] in send->dtype (rotated-back keys are
+ *   rounded to that dtype).  Asynchronous.
+ * ---------------------------------------------------------------------- */
+int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t derotate,
+                        const int32_t* recv_to_send, int32_t n_rows,
+                        const int32_t* taps_of_layer, int32_t n_taps,
+                        void* x_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Closed-form ridge fit ("Cross-Model KV Cache Transfer in Production",
+ * stage 2: W = (X^T X + lambda I)^-1 X^T Y; section "Implementation
+ * Guidelines": lambda in [1e-4, 1e-2]).
+ *
+ * x: device [n_rows][f_in] with row stride ldx elements; y: device
+ *   [n_rows][f_out] with row stride ldy; both of in_dtype.
+ * lambda = lambda_abs + lambda_rel * trace(G) / f_in, where G = X^T X (or the
+ *   centred Gram when fit_intercept != 0).
+ * fit_intercept != 0: the bias is unpenalised; X and Y are centred by their
+ *   column means, W solves the centred system and b = mean_y - mean_x W.
+ * w_out: device fp32 [f_out][f_in] (output-major, the layout kvx_translate
+ *   takes); b_out: device fp32 [f_out] (written only with fit_intercept; may
+ *   be NULL otherwise).
+ * workspace: device scratch of kvx_fit_ridge_workspace_size(f_in, f_out).
+ * G and X^T Y are accumulated in fp32 on matrix cores; the solve (Cholesky
+ * factorisation and two triangular solves) runs in fp64.
+ * Synchronises `stream` once to read the factorisation flag:
+ *   KVX_ERR_NOT_SPD when G + lambda I is not positive definite.
+ * ---------------------------------------------------------------------- */
+size_t kvx_fit_ridge_workspace_size(int32_t f_in, int32_t f_out);
+int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_dtype,
+                  int64_t n_rows, int32_t f_in, int32_t f_out,
+                  double lambda_abs, double lambda_rel, int32_t fit_intercept,
+                  float* w_out, float* b_out, void* workspace, size_t ws_bytes,
+                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rank-r fold ("Prefill-Free ...", Methodology 3: low-rank corrections folded
+ * into one fixed affine map per layer and role).
+ *
+ * For each of `count` maps: wt: device fp32 [f_out][f_in] (output-major);
+ * a: device fp32 [f_in][rank]; b: device fp32 [f_out][rank];
+ * w_out[o][f] = wt[o][f] + sum_r b[o][r] * a[f][r], each product rounded to
+ * fp32, the products summed in rank order r = 0, 1, ... in fp32 and the sum
+ * added to wt[o][f] in fp32 (no fused multiply-add anywhere), then stored as
+ * out_dtype (bf16: nearest even).  The maps are consecutive in memory.
+ * w_out: device, count*f_out*f_in elements; must not overlap the inputs.
+ * Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+int kvx_fold_lowrank(const float* wt, const float* a, const float* b, int32_t count,
+                     int32_t f_in, int32_t f_out, int32_t rank, void* w_out,
+                     int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVX_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and its host-only logic (layer map, argument validation,
+workspace sizes) behaves as documented.  No kernel is launched here: every
+call below returns before the first HIP runtime call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from cross_model_kv_kvx_amd import kvx
+from oracle import kvx_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvx.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = kvx.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(kvx.EXPORTS)
+    out = os.popen(f"nm -D --defined-only {kvx.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_status_strings():
+    assert kvx.status_string(0) == "ok"
+    assert "positive definite" in kvx.status_string(4)
+    assert kvx.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("ls,lr,nt,stride", [(36, 32, 3, 4), (32, 80, 1, 4), (7, 3, 3, 2), (1, 4, 3, 4),
+                                             (10, 1, 1, 4), (3, 5, 5, 1)])
+def test_layer_map_matches_oracle(ls, lr, nt, stride):
+    got = kvx.layer_map(ls, lr, nt, stride)
+    assert np.array_equal(got, O.layer_taps(ls, lr, nt, stride))
+
+
+def test_layer_map_rejects_bad_arguments():
+    out = (ctypes.c_int32 * 64)()
+    L = kvx.lib()
+    assert L.kvx_layer_map(36, 32, 2, 4, out) == kvx.ERR_INVALID   # even tap count
+    assert L.kvx_layer_map(0, 32, 3, 4, out) == kvx.ERR_INVALID
+    assert L.kvx_layer_map(36, 32, 9, 4, out) == kvx.ERR_INVALID
+    assert L.kvx_layer_map(36, 32, 3, 4, None) == kvx.ERR_INVALID
+
+
+def desc(L, N, H, d, dt=kvx.BF16, rope=0.0):
+    return kvx.CacheDesc(L, N, H, d, dt, rope)
+
+
+def test_translate_validation_before_launch():
+    L = kvx.lib()
+    s, r = desc(36, 100, 8, 128), desc(32, 120, 8, 128)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tp = taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    fake = ctypes.c_void_p(0x1000)
+    args = dict(k_send=fake, v_send=fake, k_recv=fake, v_recv=fake, map=fake, wk=fake, wv=fake)
+
+    def call(sd=s, rd=r, taps_p=tp, n_taps=3, per_head=0, w_dtype=kvx.BF16, ws=fake, ws_bytes=1 << 40, **kw):
+        a = dict(args, **kw)
+        return L.kvx_translate(ctypes.byref(sd), a["k_send"], a["v_send"], ctypes.byref(rd), a["k_recv"],
+                               a["v_recv"], a["map"], taps_p, n_taps, per_head, w_dtype, a["wk"], a["wv"], None,
+                               None, ws, ws_bytes, None)
+
+    assert call(w_dtype=7) == kvx.ERR_INVALID
+    assert call(n_taps=0) == kvx.ERR_INVALID
+    assert call(taps_p=None) == kvx.ERR_INVALID
+    assert call(k_send=None) == kvx.ERR_INVALID                  # K output without K input
+    assert call(wv=None) == kvx.ERR_INVALID
+    assert call(map=None) == kvx.ERR_INVALID
+    bad = taps.copy()
+    bad[3, 1] = 36                                               # tap past the last sender layer
+    assert call(taps_p=bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == kvx.ERR_INVALID
+    assert call(per_head=1) == kvx.ERR_SHAPE                     # per head needs one tap
+    assert call(rd=desc(32, 120, 8, 128, kvx.F32)) == kvx.ERR_UNSUPPORTED
+    assert call(ws=None) == kvx.ERR_WORKSPACE
+    assert call(ws_bytes=16) == kvx.ERR_WORKSPACE
+    assert call(sd=desc(0, 100, 8, 128)) == kvx.ERR_INVALID
+    assert call(sd=desc(36, 100, 8, 127, rope=1e4)) == kvx.ERR_INVALID  # odd head dim with rotation
+    assert call(rd=desc(32, 0, 8, 128)) == kvx.OK                # nothing to translate
+    assert call(k_recv=None, v_recv=None) == kvx.OK              # no role requested
+
+
+def test_workspace_sizes_are_monotone_and_cover_the_key_rows():
+    s, r = desc(36, 25000, 8, 128, rope=5e5), desc(32, 32768, 8, 128, rope=1e6)
+    big = kvx.translate_workspace_size(s, r, 3, False)
+    # rotated-back unique key rows: sender layers x min(N_R, N_S) rows x 2 KB
+    assert big >= 36 * 25000 * 1024 * 2
+    plain = kvx.translate_workspace_size(desc(36, 25000, 8, 128), desc(32, 32768, 8, 128), 3, False)
+    assert plain < big
+    assert kvx.translate_workspace_size(desc(32, 4096, 8, 128), desc(80, 4096, 8, 128), 1, True) >= 0
+    L = kvx.lib()
+    assert L.kvx_fit_ridge_workspace_size(3072, 1024) > 3072 * 3072 * 8
+    assert L.kvx_fit_ridge_workspace_size(0, 1024) == 0
+    assert L.kvx_align_workspace_size(1 << 20) > L.kvx_align_workspace_size(1000)
+
+
+def test_other_entry_points_validate_before_launch():
+    L = kvx.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.kvx_align_tokens(fake, 5, fake, 0, fake, None, 0, None) == kvx.OK   # empty receiver
+    assert L.kvx_align_tokens(fake, 0, fake, 5, fake, fake, 1 << 30, None) == kvx.ERR_SHAPE
+    assert L.kvx_align_tokens(fake, 5, fake, 5, fake, None, 0, None) == kvx.ERR_WORKSPACE
+    assert L.kvx_align_tokens(None, 5, fake, 5, fake, fake, 1 << 30, None) == kvx.ERR_INVALID
+    assert L.kvx_fit_ridge(fake, 64, fake, 64, kvx.BF16, 10, 64, 64, -1.0, 0.0, 0, fake, None, fake,
+                           1 << 40, None) == kvx.ERR_INVALID
+    assert L.kvx_fit_ridge(fake, 32, fake, 64, kvx.BF16, 10, 64, 64, 0.0, 0.0, 0, fake, None, fake,
+                           1 << 40, None) == kvx.ERR_SHAPE
+    assert L.kvx_fit_ridge(fake, 64, fake, 64, kvx.BF16, 10, 60, 64, 0.0, 0.0, 0, fake, None, fake,
+                           1 << 40, None) == kvx.ERR_UNSUPPORTED
+    assert L.kvx_fit_ridge(fake, 64, fake, 64, kvx.BF16, 10, 64, 64, 0.0, 0.0, 1, fake, None, fake,
+                           1 << 40, None) == kvx.ERR_INVALID                     # intercept needs b_out
+    assert L.kvx_fit_ridge(fake, 64, fake, 64, kvx.BF16, 10, 64, 64, 0.0, 0.0, 0, fake, None, fake,
+                           16, None) == kvx.ERR_WORKSPACE
+    assert L.kvx_fold_lowrank(fake, fake, fake, 0, 8, 8, 2, fake, kvx.BF16, None) == kvx.OK
+    assert L.kvx_fold_lowrank(fake, None, fake, 1, 8, 8, 2, fake, kvx.BF16, None) == kvx.ERR_INVALID
+    assert L.kvx_fold_lowrank(fake, fake, fake, 1, 8, 8, 2, fake, 5, None) == kvx.ERR_INVALID
+    s = desc(4, 10, 2, 8)
+    tp = np.array([0, 1], np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.kvx_gather_features(ctypes.byref(s), fake, 1, fake, 3, tp, 2, fake, None) == kvx.ERR_INVALID
+    bad = np.array([0, 4], np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert L.kvx_gather_features(ctypes.byref(s), fake, 0, fake, 3, bad, 2, fake, None) == kvx.ERR_INVALID
+    assert L.kvx_gather_features(ctypes.byref(s), fake, 0, fake, 0, tp, 2, fake, None) == kvx.OK

@@ -1,0 +1,432 @@
+"""HIP path vs the CPU oracle, element by element, through the C-ABI.
+
+Token maps are compared bit for bit; translated K/V by max|err|/RMS per role
+against the oracle's unrounded fp64 result (1e-4 for fp32 caches, 2e-2 for
+bf16 caches).  Small cases compare every element over several tiles with a
+ragged tail; the full workload sizes compare sampled receiver rows (all
+layers, heads and channels of each row) or properties that hold at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from cross_model_kv_kvx_amd import kvx, synth
+from oracle import kvx_oracle as O
+from tests.kvx_cases import TOL_BF16, TOL_F32, bf16_floor, host, rows_of, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def dev_i32(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.int32), device=DEV)
+
+
+# ---------------------------------------------------------------- alignment
+
+
+@pytest.mark.parametrize("n,seed", [(8192, 3), (32768, 4), (65536, 5), (16384, 6), (1, 0), (777, 9), (1025, 2)])
+def test_align_bit_exact(n, seed):
+    say(f"align n={n} seed={seed}")
+    s, r = synth.token_ends(n, seed)
+    got = kvx.align_tokens(dev_i32(s), dev_i32(r)).cpu().numpy()
+    want = O.token_align(s, r)
+    assert np.array_equal(got, want)
+
+
+def test_align_special_cases():
+    rng = np.random.default_rng(0)
+    e = np.cumsum(rng.integers(1, 7, size=3000)).astype(np.int32)
+    cases = [
+        (e, e),                                                     # identical tokenizations
+        (np.arange(1, e[-1] + 1, dtype=np.int32), e),               # single-character sender
+        (e, np.arange(1, e[-1] + 1, dtype=np.int32)),               # single-character receiver
+        (np.array([e[-1]], np.int32), e),                           # one sender token
+        (np.array([2, 4, 9], np.int32), np.array([1, 3, 5, 7, 9, 11, 12], np.int32)),  # leading/trailing
+    ]
+    for s, r in cases:
+        say(f"align special n_send={s.size} n_recv={r.size}")
+        got = kvx.align_tokens(dev_i32(s), dev_i32(r)).cpu().numpy()
+        assert np.array_equal(got, O.token_align(s, r))
+
+
+def test_align_rejects_non_increasing_offsets():
+    for s, r in (([1, 3, 3], [1, 2, 3]), ([1, 2, 3], [2, 1, 3]), ([0, 2], [2]), ([1, 2], [-1, 2])):
+        say(f"align invalid {s} {r}")
+        with pytest.raises(kvx.KvxError) as ei:
+            kvx.align_tokens(dev_i32(s), dev_i32(r))
+        assert ei.value.status == kvx.ERR_INVALID
+
+
+# ---------------------------------------------------------------- fold
+
+
+def test_fold_bit_exact():
+    say("fold 3 maps 1024x3072 rank 16")
+    wt, u, v, _ = synth.flat_maps(3, 3072, 1024, 31, "cpu")
+    got = kvx.fold_lowrank(wt.to(DEV), u.to(DEV), v.to(DEV), torch.bfloat16)
+    got32 = kvx.fold_lowrank(wt.to(DEV), u.to(DEV), v.to(DEV), torch.float32)
+    for l in range(3):
+        tot, bits = O.fold_lowrank(wt[l].numpy(), u[l].numpy(), v[l].numpy())
+        assert np.array_equal(got[l].cpu().view(torch.int16).numpy().view(np.uint16), bits)
+        assert np.array_equal(got32[l].cpu().numpy(), tot)
+
+
+# ---------------------------------------------------------------- cfg1: fp32 per-head fit + translate
+
+
+def cfg1_receiver(x, wt, b, noise):
+    """The matched receiver of the fp32 single-layer setting, built on the
+    host: y_h = x_h W_true,h^T + b_h + noise (W stored output-major)."""
+    xs = x.double()
+    y = torch.einsum("lnhc,hoc->lnho", xs, wt[0].double()) + b.double().reshape(1, 1, wt.shape[1], -1)
+    return (y + noise.double()).float()
+
+
+def test_cfg1_fit_and_translate_fp32():
+    say("cfg1 fp32 fit + per-head translate")
+    c = synth.config(1, "cpu")
+    H, d = c["heads"], c["head_dim"]
+    taps = kvx.layer_map(1, 1, 1)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    tmap = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    assert np.array_equal(tmap.cpu().numpy(), tmap_o)
+    maps_g, maps_o = {}, {}
+    for role in ("k", "v"):
+        y_cal = cfg1_receiver(c[f"x_cal_{role}"], c[f"w_true_{role}"], c[f"b_true_{role}"], c[f"noise_cal_{role}"])
+        xg, yg = c[f"x_cal_{role}"].to(DEV), y_cal.to(DEV)
+        wts, bs, wto, bo = [], [], [], []
+        for h in range(H):
+            w, b = kvx.fit_ridge(xg[0, :, h, :], yg[0, :, h, :], lambda_abs=1e-2, fit_intercept=True)
+            wo, bo_h, lam = O.ridge_fit(O.as_f64(c[f"x_cal_{role}"][0, :, h, :]), O.as_f64(y_cal[0, :, h, :]),
+                                        lam_abs=1e-2, fit_intercept=True)
+            assert O.rel_err(w.cpu().numpy(), wo.T) <= TOL_F32
+            assert O.rel_err(b.cpu().numpy(), bo_h) <= TOL_F32
+            wts.append(w)
+            bs.append(b)
+            wto.append(wo.T)
+            bo.append(bo_h)
+        maps_g[role] = (torch.stack(wts)[None].contiguous(), torch.cat(bs)[None].contiguous())
+        maps_o[role] = (np.stack(wto)[None], np.concatenate(bo)[None])
+    k, v = kvx.translate(c["x_k"].to(DEV), c["x_v"].to(DEV), tmap, taps, maps_g["k"][0], maps_g["v"][0],
+                         maps_g["k"][1], maps_g["v"][1], per_head=True)
+    for role, out in (("k", k), ("v", v)):
+        want = O.translate_rows(c[f"x_{role}"], tmap_o, taps, maps_o[role][0], maps_o[role][1], np.arange(128),
+                                per_head=True, recv_heads=H, recv_head_dim=d)
+        got = O.as_f64(out).reshape(1, 128, H * d)
+        err = O.rel_err(got, want)
+        say(f"  cfg1 {role}: max|err|/RMS = {err:.3e}")
+        assert err <= TOL_F32
+
+
+# ---------------------------------------------------------------- cfg2: per-head bf16, 32 -> 80 layers
+
+
+def run_cfg2(n_tokens, rows=None, seed=2):
+    c = synth.config(2, DEV, small=True) if n_tokens == 256 else None
+    if c is None:
+        cc = dict(synth.CONFIGS[2])
+        shp = synth.CacheShape(32, n_tokens, 8, 128)
+        c = dict(send_shape=shp)
+        c["send_end"], c["recv_end"] = synth.identical_ends(n_tokens, seed)
+        for r, role in enumerate(("k", "v")):
+            c[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, DEV, channel_scale="loguniform")
+            c[f"wt_{role}"], c[f"b_{role}"] = synth.perhead_maps(80, 8, 128, seed * 100 + 20 + r, DEV)
+    taps = kvx.layer_map(32, 80, 1)
+    tmap = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    assert np.array_equal(tmap.cpu().numpy(), tmap_o)
+    k, v = kvx.translate(c["k_send"], c["v_send"], tmap, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"],
+                         per_head=True)
+    n = tmap_o.size
+    rows = np.arange(n) if rows is None else rows
+    for role, out in (("k", k), ("v", v)):
+        want = O.translate_rows(c[f"{role}_send"], tmap_o, taps, host(c[f"wt_{role}"]), host(c[f"b_{role}"]), rows,
+                                per_head=True, recv_heads=8, recv_head_dim=128)
+        got = rows_of(out, rows)
+        err = O.rel_err(got, want)
+        say(f"  cfg2 n={n} {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+    return k, v
+
+
+def test_cfg2_perhead_small_all_elements():
+    say("cfg2 per-head 256 tokens")
+    run_cfg2(256)
+
+
+def test_cfg2_perhead_ragged_all_elements():
+    say("cfg2 per-head 300 tokens (ragged chunk)")
+    run_cfg2(300, seed=12)
+
+
+def test_cfg2_perhead_full_sampled_rows():
+    say("cfg2 per-head 4096 tokens, sampled rows")
+    rows = sample_rows(np.arange(4096), 128, 0)
+    run_cfg2(4096, rows)
+
+
+# ---------------------------------------------------------------- cfg3/4: flattened maps
+
+
+class Bf16Maps:
+    """Oracle-folded maps kept as bf16 bit patterns; indexing a layer gives
+    its float64 values (the oracle reads one layer at a time)."""
+
+    def __init__(self, bits):
+        self.bits = bits
+
+    def __len__(self):
+        return len(self.bits)
+
+    def __getitem__(self, l):
+        return O.bf16_bits_to_f64(self.bits[l])
+
+
+_MAPS = {}
+
+
+def flat_maps(k):
+    """Maps of a flattened setting, folded by the library (bf16, device) and
+    by the oracle (bf16 bits, host); the two folds must agree bit for bit."""
+    if k not in _MAPS:
+        seed = synth.CONFIGS[k]["seed"]
+        out = {}
+        for r, role in enumerate(("k", "v")):
+            say(f"  folding maps of setting {k} role {role}")
+            wt, u, v, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, DEV, 16)
+            g = kvx.fold_lowrank(wt, u, v, torch.bfloat16)
+            wh, uh, vh = host(wt).numpy(), host(u).numpy(), host(v).numpy()
+            bits = np.stack([O.fold_lowrank(wh[l], uh[l], vh[l])[1] for l in range(32)])
+            assert np.array_equal(host(g).view(torch.int16).numpy().view(np.uint16), bits)
+            out[role] = (g, b, Bf16Maps(bits), host(b).numpy().astype(np.float64))
+            del wt, u, v
+        _MAPS[k] = out
+    return _MAPS[k]
+
+
+def flat_case(k, n_recv=None, seed=None):
+    """Inputs of the flattened settings on the device: token ends and caches
+    seeded by ``seed``, maps of setting ``k``."""
+    cfg = dict(synth.CONFIGS[k])
+    seed = cfg["seed"] if seed is None else seed
+    nr = cfg["recv_tokens"] if n_recv is None else n_recv
+    send_end, recv_end = synth.token_ends(nr, seed)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    c = dict(send_end=send_end, recv_end=recv_end, shp=shp, n_recv=nr)
+    rope = "send_rope" in cfg
+    maps = flat_maps(k)
+    for r, role in enumerate(("k", "v")):
+        c[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, DEV, outlier_frac=cfg.get("outlier_frac", 0.0),
+                                               outlier_scale=cfg.get("outlier_scale", 1.0),
+                                               outlier_pairs=(role == "k" and rope))
+        c[f"wt_{role}"], c[f"b_{role}"], c[f"wt_o_{role}"], c[f"b_o_{role}"] = maps[role]
+    c["send_rope"] = cfg.get("send_rope", 0.0)
+    c["recv_rope"] = cfg.get("recv_rope", 0.0)
+    return c
+
+
+def check_flat(c, rows=None):
+    taps = kvx.layer_map(36, 32, 3, 4)
+    assert np.array_equal(taps, O.layer_taps(36, 32, 3, 4))
+    tmap = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    assert np.array_equal(tmap.cpu().numpy(), tmap_o)
+    k, v = kvx.translate(c["k_send"], c["v_send"], tmap, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"],
+                         send_rope_base=c["send_rope"], recv_rope_base=c["recv_rope"])
+    torch.cuda.synchronize()
+    n = tmap_o.size
+    rows = np.arange(n) if rows is None else rows
+    errs = {}
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(c[f"{role}_send"], tmap_o, taps, c[f"wt_o_{role}"], c[f"b_o_{role}"], rows,
+                                per_head=False, recv_heads=8, recv_head_dim=128,
+                                send_rope_base=c["send_rope"] if rk else 0.0,
+                                recv_rope_base=c["recv_rope"] if rk else 0.0)
+        got = rows_of(out, rows)
+        err = O.rel_err(got, want)
+        errs[role] = err
+        say(f"  flat n={n} {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+    return k, v, tmap, errs
+
+
+def test_cfg3_flat_small_all_elements():
+    say("cfg3 flattened, 600 receiver tokens")
+    c = flat_case(3, 600, seed=13)
+    check_flat(c)
+
+
+def test_cfg4_flat_rope_small_all_elements():
+    say("cfg4 flattened + RoPE, 700 receiver tokens")
+    c = flat_case(4, 700, seed=14)
+    check_flat(c)
+
+
+def test_cfg3_flat_full_sampled_rows():
+    say("cfg3 flattened, 8192 receiver tokens, sampled rows")
+    c = flat_case(3)
+    s, r = c["send_end"], c["recv_end"]
+    rows = sample_rows(O.token_align(s, r), 256, 3)
+    k, v, tmap, _ = check_flat(c, rows)
+    # V rows of one run are bitwise equal (one product written to the run)
+    m = tmap.cpu().numpy()
+    starts = np.flatnonzero(np.diff(m) == 0)[:50]
+    for i in starts:
+        assert torch.equal(v[:, int(i)], v[:, int(i) + 1])
+
+
+def test_cfg4_flat_rope_full_sampled_rows():
+    say("cfg4 flattened + RoPE, 32768 receiver tokens, sampled rows")
+    c = flat_case(4)
+    rows = sample_rows(O.token_align(c["send_end"], c["recv_end"]), 256, 4)
+    check_flat(c, rows)
+
+
+def test_translate_deterministic_and_identity_maps():
+    say("determinism + identity maps")
+    c = flat_case(3, 520, seed=23)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    k1, v1 = kvx.translate(c["k_send"], c["v_send"], tmap, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"])
+    k2, v2 = kvx.translate(c["k_send"], c["v_send"], tmap, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"])
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    # flattened [0; I; 0] selects the centre tap exactly (bf16 in, bf16 out)
+    L, N, F = 6, 300, 1024
+    x = synth.sender_cache(synth.CacheShape(L, N, 8, 128), 77, DEV)
+    sel = torch.zeros((L, F, 3 * F), dtype=torch.bfloat16, device=DEV)
+    sel[:, :, F:2 * F] = torch.eye(F, dtype=torch.bfloat16, device=DEV)
+    ident = dev_i32(np.arange(N))
+    taps6 = kvx.layer_map(L, L, 3, 1)
+    ky, _ = kvx.translate(x, None, ident, taps6, sel, None)
+    assert torch.equal(ky, x)
+    # per head W = I (fp32 map, hi/lo split) reproduces the input exactly
+    eye = torch.eye(128, device=DEV).expand(L, 8, 128, 128).contiguous()
+    kp, _ = kvx.translate(x, None, ident, kvx.layer_map(L, L, 1), eye, None, per_head=True)
+    assert torch.equal(kp, x)
+
+
+def test_translate_edge_cases():
+    say("edge cases: one receiver token, one run, leading unmatched")
+    c = flat_case(3, 64, seed=33)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    Ns = c["shp"].tokens
+    for name, m in (("one row", np.array([5])), ("single run", np.zeros(300, np.int64) + 7),
+                    ("long final run", np.minimum(np.arange(257), Ns - 1))):
+        say(f"  {name}")
+        tm = dev_i32(m)
+        k, v = kvx.translate(c["k_send"], c["v_send"], tm, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"])
+        for role, out in (("k", k), ("v", v)):
+            want = O.translate_rows(c[f"{role}_send"], m, taps, c[f"wt_o_{role}"], c[f"b_o_{role}"], np.arange(m.size),
+                                    per_head=False, recv_heads=8, recv_head_dim=128)
+            assert O.rel_err(rows_of(out, np.arange(m.size)), want) <= TOL_BF16
+
+
+# ---------------------------------------------------------------- features and fit (cfg5)
+
+
+def test_gather_features():
+    say("gather features")
+    c = flat_case(3, 200, seed=43)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    tm = dev_i32(tmap_o)
+    for l in (0, 17, 31):
+        x = kvx.gather_features(c["k_send"], tm, taps[l])
+        want = O.features(c["k_send"], tmap_o, taps[l])
+        assert np.array_equal(O.as_f64(x), want)
+    # fp32 cache with rotation undone at the sender position
+    kf = synth.sender_cache(synth.CacheShape(5, 300, 2, 64), 9, DEV, torch.float32)
+    m = np.sort(np.random.default_rng(1).integers(0, 300, size=150))
+    xf = kvx.gather_features(kf, dev_i32(m), [4, 1], derotate=True, rope_base=1e4)
+    want = O.features(kf, m, [4, 1], derotate_base=1e4)
+    assert O.rel_err(O.as_f64(xf), want) <= 1e-6
+
+
+def fit_case(n_cal, seed=5):
+    send_end, recv_end = synth.token_ends(n_cal, seed)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    c = dict(send_end=send_end, recv_end=recv_end)
+    c["k_send"] = synth.sender_cache(shp, seed * 100, DEV)
+    c["recv_k"] = synth.receiver_cache(synth.CacheShape(32, n_cal, 8, 128), seed * 100 + 50, DEV)
+    return c
+
+
+@pytest.mark.parametrize("layer", [0, 15, 31])
+def test_fit_ridge_vs_oracle(layer):
+    say(f"ridge fit layer {layer}, 4096 calibration rows")
+    c = fit_case(4096)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    tm = dev_i32(tmap_o)
+    x = kvx.gather_features(c["k_send"], tm, taps[layer])
+    y = c["recv_k"][layer].reshape(4096, 1024)
+    w, _ = kvx.fit_ridge(x, y, lambda_rel=1e-3)
+    xo = O.features(c["k_send"], tmap_o, taps[layer])
+    yo = O.as_f64(c["recv_k"][layer]).reshape(4096, 1024)
+    wo, _, lam = O.ridge_fit(xo, yo, lam_rel=1e-3)
+    err = O.rel_err(w.cpu().numpy(), wo.T)
+    say(f"  W max|err|/RMS = {err:.3e} (lambda {lam:.4g})")
+    assert err <= TOL_BF16
+    if layer in (0, 31):  # duplicated taps -> equal weight blocks
+        t = taps[layer]
+        dup = [(i, j) for i in range(3) for j in range(i + 1, 3) if t[i] == t[j]][0]
+        wn = w.cpu().numpy()
+        a, b = dup
+        assert np.array_equal(wn[:, a * 1024:(a + 1) * 1024], wn[:, b * 1024:(b + 1) * 1024])
+
+
+def test_fit_rejects_singular_gram():
+    say("ridge fit lambda 0 on duplicated taps -> not SPD")
+    c = fit_case(512, seed=8)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tm = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    x = kvx.gather_features(c["k_send"], tm, taps[0])   # taps (0, 0, 4): two equal blocks, 512 < 3072 rows
+    y = c["recv_k"][0].reshape(512, 1024)
+    with pytest.raises(kvx.KvxError) as ei:
+        kvx.fit_ridge(x, y)
+    assert ei.value.status == kvx.ERR_NOT_SPD
+
+
+def test_fit_full_size_normal_equations():
+    """65536 calibration rows, one layer: the fitted W satisfies the normal
+    equations (G + lambda I) W = X^T Y, checked on random probe vectors with
+    products the oracle's data forms directly (Freivalds)."""
+    say("ridge fit 65536 rows: normal-equation residual on probes")
+    c = fit_case(65536)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tm = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    layer = 20
+    x = kvx.gather_features(c["k_send"], tm, taps[layer])
+    y = c["recv_k"][layer].reshape(65536, 1024)
+    w, _ = kvx.fit_ridge(x, y, lambda_rel=1e-3)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    X = O.features(c["k_send"], tmap_o, taps[layer])
+    Y = O.as_f64(c["recv_k"][layer]).reshape(65536, 1024)
+    W = w.cpu().numpy().astype(np.float64).T
+    lam = 1e-3 * float(np.einsum("ij,ij->", X, X)) / 3072
+    rng = np.random.default_rng(0)
+    for _ in range(3):
+        r = rng.standard_normal(1024)
+        wr = W @ r
+        lhs = X.T @ (X @ wr) + lam * wr
+        rhs = X.T @ (Y @ r)
+        res = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
+        say(f"  residual {res:.3e}")
+        assert res <= 1e-3
