@@ -202,10 +202,10 @@ __global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ wt,
     const float* br = b + (m * f_out + o) * rank;
     float acc = 0.0f;
     for (int32_t r = 0; r < rank; ++r) {
-      const float p = __fmul_rn(br[r], ar[r]);
-      acc = (r == 0) ? p : __fadd_rn(acc, p);
+      const float p = br[r] * ar[r];
+      acc = (r == 0) ? p : acc + p;
     }
-    const float tot = (rank > 0) ? __fadd_rn(wt[i], acc) : wt[i];
+    const float tot = (rank > 0) ? wt[i] + acc : wt[i];
     if (out_bf16)
       static_cast<uint16_t*>(out)[i] = f32_to_bf16_rne(tot);
     else

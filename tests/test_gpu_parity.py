@@ -384,12 +384,16 @@ def test_fit_ridge_vs_oracle(layer):
     err = O.rel_err(w.cpu().numpy(), wo.T)
     say(f"  W max|err|/RMS = {err:.3e} (lambda {lam:.4g})")
     assert err <= TOL_BF16
-    if layer in (0, 31):  # duplicated taps -> equal weight blocks
+    if layer in (0, 31):
+        # duplicated taps -> equal weight blocks (exact for the exact solution;
+        # the blocked factorisation eliminates the two copies at different
+        # steps, so they agree to fp64 rounding amplified by the condition)
         t = taps[layer]
-        dup = [(i, j) for i in range(3) for j in range(i + 1, 3) if t[i] == t[j]][0]
-        wn = w.cpu().numpy()
-        a, b = dup
-        assert np.array_equal(wn[:, a * 1024:(a + 1) * 1024], wn[:, b * 1024:(b + 1) * 1024])
+        a, b = [(i, j) for i in range(3) for j in range(i + 1, 3) if t[i] == t[j]][0]
+        wn = w.cpu().numpy().astype(np.float64)
+        gap = np.max(np.abs(wn[:, a * 1024:(a + 1) * 1024] - wn[:, b * 1024:(b + 1) * 1024]))
+        say(f"  duplicated-block gap / RMS = {gap / np.sqrt(np.mean(wn * wn)):.3e}")
+        assert gap <= 1e-6 * np.sqrt(np.mean(wn * wn))
 
 
 def test_fit_rejects_singular_gram():
