@@ -40,12 +40,15 @@ struct TranslateWs {
   float2* tab_send = nullptr;
   float2* tab_recv = nullptr;
   uint16_t* krows = nullptr;   // rotated-back unique key rows (fp16)
+  uint16_t* wk16 = nullptr;    // key map as 16-bit operands (fp16 copy or hi|lo split)
+  uint16_t* wv16 = nullptr;    // value map hi|lo split (fp32 maps only)
   int32_t rows_cap = 0;
   size_t bytes = 0;
 };
 
-static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t per_head,
-                                    bool key_role, void* base) {
+static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
+                                    int32_t per_head, int32_t w_dtype, bool key_role, bool value_role,
+                                    void* base) {
   TranslateWs w;
   Carve c(base);
   const int32_t nr = recv->tokens;
@@ -65,6 +68,16 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
     // U <= N_R always (U <= N_S only for non-decreasing maps)
     w.rows_cap = nr;
     w.krows = c.take<uint16_t>(static_cast<size_t>(send->layers) * w.rows_cap * send->kv_heads * send->head_dim);
+  }
+  if (!f32 && !per_head) {
+    const size_t map_elems = static_cast<size_t>(recv->layers) * recv->kv_heads * recv->head_dim *
+                             (static_cast<size_t>(n_taps) * send->kv_heads * send->head_dim);
+    if (w_dtype == KVX_F32) {
+      if (key_role) w.wk16 = c.take<uint16_t>(2 * map_elems);
+      if (value_role) w.wv16 = c.take<uint16_t>(2 * map_elems);
+    } else if (srope) {
+      w.wk16 = c.take<uint16_t>(map_elems);
+    }
   }
   w.bytes = c.used + 256;
   return w;
@@ -123,9 +136,9 @@ int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps, int3
 
 size_t kvx_translate_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
                                     int32_t per_head) {
-  (void)n_taps;
-  if (!desc_ok(send) || !desc_ok(recv)) return 0;
-  return layout_translate(send, recv, per_head, true, nullptr).bytes;
+  if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS) return 0;
+  // sized for fp32 maps (the larger case) and both roles
+  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, nullptr).bytes;
 }
 
 }  // extern "C"
@@ -155,10 +168,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   if (send->dtype != recv->dtype) return KVX_ERR_UNSUPPORTED;
   if (recv->tokens == 0 || (!do_k && !do_v)) return KVX_OK;
   if (send->tokens == 0) return KVX_ERR_SHAPE;
-  const TranslateWs need = layout_translate(send, recv, per_head, true, nullptr);
+  const TranslateWs need = layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, nullptr);
   if (!workspace || ws_bytes < need.bytes) return KVX_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const TranslateWs w = layout_translate(send, recv, per_head, do_k, workspace);
+  const TranslateWs w = layout_translate(send, recv, n_taps, per_head, w_dtype, do_k, do_v, workspace);
   auto mark = [&](int i) -> int {
     if (ev && hipEventRecord(ev[i], s) != hipSuccess) return KVX_ERR_HIP;
     return KVX_OK;
@@ -227,8 +240,15 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   }
 
   if (f_out % 256 != 0) return KVX_ERR_UNSUPPORTED;
+  const int32_t send_row = send->kv_heads * send->head_dim;
+  // row offsets inside one sender layer travel as int32
+  if (static_cast<int64_t>(send->tokens) * send_row >= (1LL << 31) ||
+      static_cast<int64_t>(recv->tokens) * send_row >= (1LL << 31))
+    return KVX_ERR_UNSUPPORTED;
   if (int st = launch_runs(recv_to_send, recv->tokens, send->tokens, w.runs, w.runs_scratch, s)) return st;
-  const int64_t send_layer_elems = static_cast<int64_t>(send->tokens) * send->kv_heads * send->head_dim;
+  const int64_t send_layer_elems = static_cast<int64_t>(send->tokens) * send_row;
+  const int64_t map_rows = static_cast<int64_t>(recv->layers) * f_out;
+  const bool split = w_dtype == KVX_F32;
   FlatRole roles[2];
   int n = 0;
   if (do_k) {
@@ -241,7 +261,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
                                         send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, w.krows, s))
         return st;
       r.a_src = w.krows;
-      r.a_layer_stride = static_cast<int64_t>(w.rows_cap) * send->kv_heads * send->head_dim;
+      r.a_layer_stride = static_cast<int64_t>(w.rows_cap) * send_row;
       r.a_compact = 1;
       r.a_f16 = 1;
     } else {
@@ -253,7 +273,15 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     if (w.tab_recv) {
       if (int st = launch_rope_table(w.tab_recv, recv->tokens, recv->head_dim, recv->rope_base, s)) return st;
     }
-    r.wt = wt_k;
+    if (split) {
+      if (int st = launch_prepare_maps(wt_k, w.wk16, map_rows, f_in, r.a_f16 ? 2 : 1, s)) return st;
+      r.wt = w.wk16;
+    } else if (r.a_f16) {
+      if (int st = launch_prepare_maps(wt_k, w.wk16, map_rows, f_in, 0, s)) return st;
+      r.wt = w.wk16;
+    } else {
+      r.wt = wt_k;
+    }
     r.bias = b_k;
     r.out = static_cast<uint16_t*>(k_recv);
     r.rotate = w.tab_recv ? 1 : 0;
@@ -265,7 +293,12 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     r.a_layer_stride = send_layer_elems;
     r.a_compact = 0;
     r.a_f16 = 0;
-    r.wt = wt_v;
+    if (split) {
+      if (int st = launch_prepare_maps(wt_v, w.wv16, map_rows, f_in, 1, s)) return st;
+      r.wt = w.wv16;
+    } else {
+      r.wt = wt_v;
+    }
     r.bias = b_v;
     r.out = static_cast<uint16_t*>(v_recv);
     r.rotate = 0;
@@ -276,11 +309,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   p.send_tokens = send->tokens;
   p.recv_layers = recv->layers;
   p.recv_tokens = recv->tokens;
-  p.f_in = f_in;
+  p.k_dim = split ? 2 * f_in : f_in;
   p.f_out = f_out;
   p.n_taps = n_taps;
-  p.send_row = send->kv_heads * send->head_dim;
-  p.w_f32 = w_dtype == KVX_F32;
+  p.send_row = send_row;
   p.taps = taps;
   p.tab_recv = w.tab_recv;
   p.runs = w.runs;

@@ -44,8 +44,8 @@ struct FlatRole {
   const void* a_src;       // sender cache (bf16) or rotated-back rows (fp16)
   int64_t a_layer_stride;  // elements between consecutive sender layers of a_src
   int32_t a_compact;       // 1: rows of a_src are run indices u; 0: sender tokens uniq[u]
-  int32_t a_f16;           // 1: a_src holds fp16, 0: bf16
-  const void* wt;          // [L_R][F_out][F_in]
+  int32_t a_f16;           // 1: operands are fp16, 0: bf16
+  const void* wt;          // 16-bit map of the operand type, [L_R][F_out][k_dim]
   const float* bias;       // [L_R][F_out] or null
   uint16_t* out;           // [L_R][N_R][F_out] bf16
   int32_t rotate;          // rotate outputs at the receiver position
@@ -53,14 +53,19 @@ struct FlatRole {
 
 struct FlatProblem {
   int32_t send_layers, send_tokens, recv_layers, recv_tokens;
-  int32_t f_in, f_out, n_taps, send_row;  // send_row = H_S * d_S
-  int32_t w_f32;
-  const int32_t* taps;  // host [L_R][n_taps]
+  int32_t k_dim;           // n_taps * send_row, doubled for split fp32 maps
+  int32_t f_out, n_taps, send_row;  // send_row = H_S * d_S
+  const int32_t* taps;     // host [L_R][n_taps]
   const float2* tab_recv;
   Runs runs;
 };
 
 int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s);
+
+// 16-bit operand maps from the caller's maps: mode 0 bf16 -> fp16; mode 1
+// fp32 -> [bf16 hi | bf16 lo]; mode 2 fp32 -> [fp16 hi | fp16 lo] (rows of
+// f_in become rows of 2 f_in).
+int launch_prepare_maps(const void* in, uint16_t* out, int64_t rows, int32_t f_in, int32_t mode, hipStream_t s);
 
 // ---------------------------------------------------------------- per-head translation (bf16)
 struct HeadProblem {

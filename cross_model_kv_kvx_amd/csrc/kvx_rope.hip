@@ -39,17 +39,21 @@ int launch_rope_table(float2* tab, int32_t n_pos, int32_t head_dim, double base,
 
 // ---------------------------------------------------------------- rotated-back unique rows
 // One thread: 8 pairs (j .. j+7 and j+64 .. j+71) of one head of one row.
-// Block: 256 threads = 4 rows x 8 heads x 8 pair groups; 4 passes = 16 rows.
+// Block: 16 rows of one sender layer (blockIdx.y indexes the used layers).
 constexpr int DR_ROWS = 16;
 
+struct LayerList {
+  uint8_t l[MAX_LAYERS];
+};
+
 __global__ __launch_bounds__(256) void derotate_rows_kernel(
-    const uint16_t* __restrict__ k_send, int32_t send_tokens, int32_t heads,
-    const int32_t* __restrict__ uniq,
+    const uint16_t* __restrict__ k_send, int32_t send_tokens, int32_t heads, const int32_t* __restrict__ uniq,
     const int32_t* __restrict__ n_uniq, int32_t rows_cap, const float2* __restrict__ tab,
-    uint16_t* __restrict__ out, int32_t layer) {
+    uint16_t* __restrict__ out, const LayerList layers) {
   const int32_t U = min(*n_uniq, rows_cap);
   const int32_t row0 = blockIdx.x * DR_ROWS;
   if (row0 >= U) return;
+  const int32_t layer = layers.l[blockIdx.y];
   const int32_t row_elems = heads * 128;
   const int32_t per_row = heads * 8;  // threads per row
   for (int32_t it = threadIdx.x; it < DR_ROWS * per_row; it += 256) {
@@ -80,17 +84,19 @@ __global__ __launch_bounds__(256) void derotate_rows_kernel(
   }
 }
 
-int launch_derotate_rows(const uint16_t* k_send, int32_t send_layers, int32_t send_tokens,
-                         int32_t heads, const uint8_t* layer_used, const Runs& r, int32_t rows_cap,
-                         const float2* tab_send, uint16_t* out, hipStream_t s) {
+int launch_derotate_rows(const uint16_t* k_send, int32_t send_layers, int32_t send_tokens, int32_t heads,
+                         const uint8_t* layer_used, const Runs& r, int32_t rows_cap, const float2* tab_send,
+                         uint16_t* out, hipStream_t s) {
   if (rows_cap <= 0) return KVX_OK;
-  const unsigned blocks = static_cast<unsigned>(ceil_div(rows_cap, DR_ROWS));
-  for (int32_t l = 0; l < send_layers; ++l) {
-    if (!layer_used[l]) continue;
-    derotate_rows_kernel<<<blocks, 256, 0, s>>>(k_send, send_tokens, heads, r.uniq,
-                                                r.n_uniq, rows_cap, tab_send, out, l);
-    KVX_LAUNCH_CHECK();
-  }
+  LayerList ll{};
+  int n = 0;
+  for (int32_t l = 0; l < send_layers; ++l)
+    if (layer_used[l]) ll.l[n++] = static_cast<uint8_t>(l);
+  if (n == 0) return KVX_OK;
+  const dim3 grid(static_cast<unsigned>(ceil_div(rows_cap, DR_ROWS)), static_cast<unsigned>(n));
+  derotate_rows_kernel<<<grid, 256, 0, s>>>(k_send, send_tokens, heads, r.uniq, r.n_uniq, rows_cap, tab_send, out,
+                                            ll);
+  KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
 
