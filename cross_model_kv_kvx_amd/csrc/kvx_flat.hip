@@ -13,25 +13,34 @@
 // problems, each T[U x F_out] = A[U x K] * W^T + b, with 16-bit operands of
 // one type per role (bf16, or fp16 for rotated-back keys) and fp32
 // accumulation:
-//   * block tile 256 (rows) x 256 (outputs = two 128-wide heads), 4 waves of
-//     128 x 128, each built from 4 x 4 MFMA 32x32x16 accumulators;
-//   * K advances 32 elements per step through a ring of 4 LDS stages (32 KB
-//     each) filled by direct global->LDS 16-byte loads: A rows are gathered
-//     per lane (sender token of each run, or a compact rotated-back row) and
-//     W rows are read output-major, so no staging registers are needed and
-//     three steps stay in flight while one is multiplied;
-//   * 16-byte chunks are XOR-swizzled inside each 64-byte LDS row so the
-//     fragment reads of 16 consecutive rows hit distinct banks;
-//   * each stage is a separate LDS array so the compiler can keep counted
-//     vmcnt waits (a single array would force a full drain before every LDS
-//     read), and the only synchronisation per step is one s_barrier;
-//   * tiles of one problem are grouped 8 (rows) x F_out/256 (outputs) and one
-//     group goes to the 32 blocks of one XCD (blocks are dispatched round
-//     robin over the 8 XCDs), so A and W slices are shared in that XCD's L2;
-//   * epilogue: each wave stages 64 rows x 128 outputs (bias added) in its
-//     own ring slot, then walks the receiver rows of those runs 8 at a time,
-//     rotating key pairs (c, c+64) at the receiver position by a recurrence
-//     and storing 2 x 16 bytes of bf16 (nearest even) per lane.
+//   * one workgroup of 8 waves per CU (two waves per SIMD, so one wave's
+//     barrier wait or fragment-read latency is covered by the other's
+//     matrix instructions); block tile 256 (rows) x 256 (outputs = two
+//     128-wide heads), wave tile 64 x 128 (one head) built from 2 x 4 MFMA
+//     32x32x16 accumulators;
+//   * K advances 64 elements per step; the A part (256 rows x 64) and the W
+//     part (256 outputs x 64) of a step are 32 KB each and go through a ring
+//     of five 32 KB LDS parts (all 160 KB of LDS), filled by direct
+//     global->LDS 16-byte loads: A rows are gathered per lane (sender token
+//     of each run, or a compact rotated-back row) and W rows are read
+//     output-major.  64 elements are one whole 128-byte line of each row, so
+//     every L2 request is a full line (half-line requests halve the L2
+//     throughput).  While step k is multiplied, W of step k+1 and A of steps
+//     k+1 and k+2 are in flight;
+//   * inside each 128-byte LDS row the 16-byte chunks are XOR-swizzled by
+//     (row / 2) mod 8 so fragment reads of consecutive rows hit distinct
+//     banks;
+//   * each part is a separate LDS array so the compiler can keep counted
+//     vmcnt waits, and the only synchronisation per step is one s_barrier;
+//   * tiles of one problem are grouped 8 (rows) x F_out/256 (outputs) and
+//     consecutive groups go to the workgroups of one XCD (workgroups are
+//     dispatched round robin over the 8 XCDs), so A and W slices are shared
+//     in that XCD's L2;
+//   * epilogue: each wave stages 32 rows x 128 outputs (bias added, fp32) in
+//     its 16 KB share of parts 1..4, then walks the receiver rows of those
+//     runs 8 at a time, rotating key pairs (c, c+64) at the receiver position
+//     by a recurrence and storing 2 x 16 bytes of bf16 (nearest even) per
+//     lane.
 
 #include "kvx_internal.hpp"
 
@@ -39,10 +48,16 @@ namespace kvx {
 
 constexpr int FT_M = 256;
 constexpr int FT_N = 256;
-constexpr int FT_BK = 32;
-constexpr int FT_THREADS = 256;
-constexpr int FT_SLOT_ELEMS = (FT_M + FT_N) * FT_BK;  // 16-bit elements per stage (32 KB)
-constexpr int FT_B_OFF = FT_M * FT_BK;                // B tile offset inside a stage
+constexpr int FT_BK = 64;
+constexpr int FT_WAVES = 8;
+constexpr int FT_THREADS = 64 * FT_WAVES;
+constexpr int FT_GM = 8;                              // row tiles per L2 group
+constexpr int FT_PART_ELEMS = FT_M * FT_BK;          // 16-bit elements of one ring part (32 KB)
+static_assert(FT_M == FT_N, "A and W parts share one size");
+constexpr int FT_ROWS_PER_LD = 8;                     // rows of one direct load (8 x 128 B)
+constexpr int FT_A_LD = FT_M / FT_ROWS_PER_LD / FT_WAVES;  // A loads per wave per step
+constexpr int FT_B_LD = FT_N / FT_ROWS_PER_LD / FT_WAVES;  // B loads per wave per step
+constexpr int FT_EP_FLOATS = 32 * 128;                // staging of one wave (16 KB)
 
 struct FlatKArgs {
   const uint16_t* a_src[2];
@@ -68,7 +83,8 @@ struct FlatKArgs {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Buffer resource over [base, base + bytes) for raw 32-bit loads (word 3 as
-// for gfx9 raw buffers); loads past the end return zero.
+// for gfx9 raw buffers); loads past the end return zero without a memory
+// access.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ft_rsrc(const char* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
@@ -101,118 +117,133 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                    0, 0, 0);
 }
 
-// Per-tile addressing of this thread's direct loads.  Load instruction i of
-// wave w covers tile rows (4w + i) * 16 .. +16; lane j lands at row +j/4,
-// physical chunk j%4, and fetches logical chunk (j%4) ^ ((j/16)%4).
+// Physical 16-byte chunk of logical chunk c in tile row r.
+__device__ __forceinline__ int ft_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Per-tile addressing of this thread's direct loads.  A load instruction
+// covers 8 tile rows (1 KB of the stage); lane j lands at row +j/8, physical
+// chunk j%8.  Wave w loads row groups FT_A_LD*w .. +FT_A_LD of A and
+// FT_B_LD*w .. +FT_B_LD of B.
 struct TileAddr {
   const char* a_src;            // A source, layer 0
   int64_t a_ls;                 // bytes between A source layers (< 2^31)
   uint32_t taps0, taps1;        // sender layer of taps 0..3 and 4..6, one byte each
-  __amdgpu_buffer_rsrc_t w_r;   // map rows n0 .. n0+255 of this layer
-  uint32_t a_off[4];            // byte offsets of the A rows (row * send_row + chunk)
-  uint32_t b_off[4];            // byte offsets of the W rows
-  int32_t spt;                  // K steps per tap (send_row / 32)
+  const char* w_base;           // map rows n0 .. n0+255 of this layer
+  uint32_t w_bytes;
+  uint32_t a_off[FT_A_LD];      // byte offsets of the A rows (row * send_row + chunk)
+  uint32_t b_off[FT_B_LD];      // byte offsets of the W rows
+  int32_t spt;                  // K steps per tap (send_row / 64)
   int32_t n_taps;
+  int32_t nk;                   // K steps of the problem
 };
 
 // Wave index as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-__device__ __forceinline__ void ft_issue(const TileAddr& ta, int k, uint16_t* slot) {
-  const int wave = wave_id();
-  const int32_t tap_i = k / ta.spt;
-  const int32_t w0 = (k - tap_i * ta.spt) * FT_BK;
-  const int32_t tap = tap_i % ta.n_taps;  // fp32 maps split in two repeat the taps
-  const uint32_t layer = ((tap < 4 ? ta.taps0 : ta.taps1) >> (8 * (tap & 3))) & 0xffu;
-  const __amdgpu_buffer_rsrc_t a_r = ft_rsrc(ta.a_src + static_cast<int64_t>(layer) * ta.a_ls,
-                                             static_cast<uint32_t>(ta.a_ls));
-  const uint32_t a_soff = 2u * static_cast<uint32_t>(w0);
-  const uint32_t b_soff = 2u * static_cast<uint32_t>(k * FT_BK);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(a_r, ta.a_off[i], a_soff, slot + (wave * 4 + i) * 512);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(ta.w_r, ta.b_off[i], b_soff, slot + FT_B_OFF + (wave * 4 + i) * 512);
+// Layer source of step k (fp32 maps split in two repeat the taps).
+__device__ __forceinline__ uint32_t ft_layer(const TileAddr& ta, int k) {
+  const int32_t tap = (k / ta.spt) % ta.n_taps;
+  return ((tap < 4 ? ta.taps0 : ta.taps1) >> (8 * (tap & 3))) & 0xffu;
 }
 
-// One K step from a stage: 2 x (4 A + 4 B fragment reads, 16 MFMAs).
+// A part of step k into `part` (steps past the end read an empty range).
+__device__ __forceinline__ void ft_issue_a(const TileAddr& ta, int k, uint16_t* part) {
+  const int wave = wave_id();
+  const bool live = k < ta.nk;
+  const __amdgpu_buffer_rsrc_t a_r = ft_rsrc(ta.a_src + static_cast<int64_t>(ft_layer(ta, k)) * ta.a_ls,
+                                             live ? static_cast<uint32_t>(ta.a_ls) : 0u);
+  const uint32_t a_soff = 2u * static_cast<uint32_t>((k % ta.spt) * FT_BK);
+#pragma unroll
+  for (int i = 0; i < FT_A_LD; ++i) dma16(a_r, ta.a_off[i], a_soff, part + (wave * FT_A_LD + i) * 512);
+}
+
+// W part of step k into `part`.
+__device__ __forceinline__ void ft_issue_b(const TileAddr& ta, int k, uint16_t* part) {
+  const int wave = wave_id();
+  const __amdgpu_buffer_rsrc_t w_r = ft_rsrc(ta.w_base, k < ta.nk ? ta.w_bytes : 0u);
+  const uint32_t b_soff = 2u * static_cast<uint32_t>(k * FT_BK);
+#pragma unroll
+  for (int i = 0; i < FT_B_LD; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * FT_B_LD + i) * 512);
+}
+
+// One K step from an A part and a W part: 4 x (2 A + 4 B fragment reads,
+// 8 MFMAs).
 template <bool F16>
-__device__ __forceinline__ void ft_compute(const uint16_t* slot, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4]) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int wm = wave & 1, wn = wave >> 1;
-  const char* sb = reinterpret_cast<const char*>(slot);
+  const int wm = wave & 3, wn = wave >> 2;
+  const char* sa = reinterpret_cast<const char*>(pa);
+  const char* sb = reinterpret_cast<const char*>(pb);
   const int fr = lane & 31;
-  const int sw = (lane >> 2) & 3;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int pc = ((2 * kk + (lane >> 5)) ^ sw) << 4;
-    u32x4 af[4], bfr[4];
+  for (int kk = 0; kk < 4; ++kk) {
+    const int pc = ft_chunk(fr, 2 * kk + (lane >> 5)) << 4;
+    u32x4 af[2], bfr[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[mi] = *reinterpret_cast<const u32x4*>(sb + (wm * 128 + mi * 32 + fr) * 64 + pc);
+    for (int mi = 0; mi < 2; ++mi) af[mi] = *reinterpret_cast<const u32x4*>(sa + (wm * 64 + mi * 32 + fr) * 128 + pc);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
-      bfr[ni] = *reinterpret_cast<const u32x4*>(sb + FT_B_OFF * 2 + (wn * 128 + ni * 32 + fr) * 64 + pc);
+      bfr[ni] = *reinterpret_cast<const u32x4*>(sb + (wn * 128 + ni * 32 + fr) * 128 + pc);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma32<F16>(af[mi], bfr[ni], acc[mi][ni]);
   }
 }
 
-// Wait until step k's loads have landed with `after` younger steps still in
-// flight, then one barrier.
-template <int AFTER>
+// Wait until all but the last A part issued by this wave have landed, then
+// one barrier: the parts of the current step are complete and every wave
+// has finished the previous step, whose two parts are now free.
 __device__ __forceinline__ void ft_sync() {
-  FT_WAIT_VM(8 * AFTER);
+  FT_WAIT_VM(FT_A_LD);
   FT_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
   FT_COMPILER_FENCE();
 }
 
-// K loop over nk steps (nk a multiple of 4, >= 4) with steps 0..2 already
-// issued into slots 0..2.  The main loop issues unconditionally (a
-// conditional issue makes the compiler drain every load before LDS reads);
-// the last four steps are peeled.
+// One step of the ring: A of step k is in part 2k mod 5, W in part
+// 2k+1 mod 5; the step issues W of k+1 and A of k+2 into the two parts of
+// step k-1.
+#define FT_STEP(K, PA, PB, NB, NA, LIVE)        \
+  ft_sync();                                    \
+  ft_issue_b(ta, (K) + 1, NB);                  \
+  ft_issue_a(ta, (K) + 2, NA);                  \
+  if (LIVE) ft_compute<F16>(PA, PB, acc);
+
+// K loop over nk >= 1 steps with A0, W0 and A1 already issued into parts 0,
+// 1 and 2.  The part pattern repeats every five steps.  Issues are
+// unconditional (steps past the end read an empty buffer range and are not
+// multiplied); the loads still in flight at the end are drained before the
+// parts are reused.
 template <bool F16>
-__device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* s0, uint16_t* s1, uint16_t* s2,
-                                         uint16_t* s3, f32x16 (&acc)[4][4]) {
-  for (int k = 0; k < nk - 4; k += 4) {
-    ft_sync<2>();
-    ft_issue(ta, k + 3, s3);
-    ft_compute<F16>(s0, acc);
-    ft_sync<2>();
-    ft_issue(ta, k + 4, s0);
-    ft_compute<F16>(s1, acc);
-    ft_sync<2>();
-    ft_issue(ta, k + 5, s1);
-    ft_compute<F16>(s2, acc);
-    ft_sync<2>();
-    ft_issue(ta, k + 6, s2);
-    ft_compute<F16>(s3, acc);
+__device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
+                                         uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
+  for (int k = 0; k < nk; k += 5) {
+    FT_STEP(k, p0, p1, p3, p4, true)
+    FT_STEP(k + 1, p2, p3, p0, p1, k + 1 < nk)
+    FT_STEP(k + 2, p4, p0, p2, p3, k + 2 < nk)
+    FT_STEP(k + 3, p1, p2, p4, p0, k + 3 < nk)
+    FT_STEP(k + 4, p3, p4, p1, p2, k + 4 < nk)
   }
-  ft_sync<2>();
-  ft_issue(ta, nk - 1, s3);
-  ft_compute<F16>(s0, acc);
-  ft_sync<2>();
-  ft_compute<F16>(s1, acc);
-  ft_sync<1>();
-  ft_compute<F16>(s2, acc);
-  ft_sync<0>();
-  ft_compute<F16>(s3, acc);
+  FT_WAIT_VM(0);
 }
+#undef FT_STEP
 
 // F16: operand type of every role of this launch (fp16 or bf16).
 template <bool F16>
-__global__ __launch_bounds__(FT_THREADS, 1) void flat_gemm_kernel(const FlatKArgs args) {
-  __shared__ __attribute__((aligned(1024))) uint16_t s0[FT_SLOT_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t s1[FT_SLOT_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t s2[FT_SLOT_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t s3[FT_SLOT_ELEMS];
+__global__ __attribute__((amdgpu_flat_work_group_size(FT_THREADS, FT_THREADS), amdgpu_waves_per_eu(2, 2))) void
+flat_gemm_kernel(const FlatKArgs args) {
+  __shared__ __attribute__((aligned(1024))) uint16_t p0[FT_PART_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t p1[FT_PART_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t p2[FT_PART_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t p3[FT_PART_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t p4[FT_PART_ELEMS];
 
   const int32_t U = *args.n_uniq;
   if (U <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int32_t mt = (U + FT_M - 1) / FT_M;
   const int32_t nt = args.f_out / FT_N;
   const int64_t per_p = static_cast<int64_t>(mt) * nt;
@@ -220,17 +251,19 @@ __global__ __launch_bounds__(FT_THREADS, 1) void flat_gemm_kernel(const FlatKArg
   const int32_t G = gridDim.x;
   const int32_t slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int32_t nk = args.k_dim / FT_BK;
-  const int lrow = lane >> 2;                               // row inside a 16-row load group
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);        // logical chunk fetched by this lane
+  const int lrow = lane >> 3;  // row inside an 8-row load group
+  // staging of this wave: half of part 1 + wave / 2
+  uint16_t* const ep_part = wave < 2 ? p1 : (wave < 4 ? p2 : (wave < 6 ? p3 : p4));
+  float* const ep = reinterpret_cast<float*>(ep_part) + (wave & 1) * FT_EP_FLOATS;
 
   for (int64_t t = slot; t < T; t += G) {
     const int32_t p = static_cast<int32_t>(t / per_p);
     const int32_t rr = static_cast<int32_t>(t % per_p);
-    const int32_t mg = rr / (8 * nt);
-    const int32_t r2 = rr % (8 * nt);
-    const int32_t gm = min(8, mt - mg * 8);
+    const int32_t mg = rr / (FT_GM * nt);
+    const int32_t r2 = rr % (FT_GM * nt);
+    const int32_t gm = min(FT_GM, mt - mg * FT_GM);
     const int32_t n0 = (r2 / gm) * FT_N;
-    const int32_t m0 = (mg * 8 + r2 % gm) * FT_M;
+    const int32_t m0 = (mg * FT_GM + r2 % gm) * FT_M;
     const int role = p / args.recv_layers;
     const int l = p % args.recv_layers;
 
@@ -241,37 +274,43 @@ __global__ __launch_bounds__(FT_THREADS, 1) void flat_gemm_kernel(const FlatKArg
     ta.taps1 = args.taps[l][1];
     ta.spt = args.send_row / FT_BK;
     ta.n_taps = args.n_taps;
-    ta.w_r = ft_rsrc(reinterpret_cast<const char*>(args.wt[role] + (static_cast<int64_t>(l) * args.f_out + n0) * args.k_dim),
-                     static_cast<uint32_t>(2 * FT_N * args.k_dim));
+    ta.w_base = reinterpret_cast<const char*>(args.wt[role] + (static_cast<int64_t>(l) * args.f_out + n0) * args.k_dim);
+    ta.w_bytes = static_cast<uint32_t>(2 * FT_N * args.k_dim);
+    ta.nk = nk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (wave * 4 + i) * 16 + lrow;
+    for (int i = 0; i < FT_A_LD; ++i) {
+      const int r = (wave * FT_A_LD + i) * FT_ROWS_PER_LD + lrow;
       int32_t u = m0 + r;
       u = u < U ? u : U - 1;
       const int32_t srow = args.a_compact[role] ? u : args.uniq[u];
-      ta.a_off[i] = 2u * static_cast<uint32_t>(srow * args.send_row + lchunk * 8);
-      ta.b_off[i] = 2u * static_cast<uint32_t>(r * args.k_dim + lchunk * 8);
+      ta.a_off[i] = 2u * static_cast<uint32_t>(srow * args.send_row + ft_chunk(r, lane & 7) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < FT_B_LD; ++i) {
+      const int r = (wave * FT_B_LD + i) * FT_ROWS_PER_LD + lrow;
+      ta.b_off[i] = 2u * static_cast<uint32_t>(r * args.k_dim + ft_chunk(r, lane & 7) * 8);
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // prologue: steps 0..2 in flight.  Slots 0..2 were last read before the
-    // final barrier of the previous tile, so they are free.
-    ft_issue(ta, 0, s0);
-    ft_issue(ta, 1, s1);
-    ft_issue(ta, 2, s2);
-    ft_kloop<F16>(ta, nk, s0, s1, s2, s3, acc);
+    // prologue: A0, W0 and A1 in flight.  The parts were last used as
+    // staging before the final barrier of the previous tile, so they are
+    // free.
+    ft_issue_a(ta, 0, p0);
+    ft_issue_b(ta, 0, p1);
+    ft_issue_a(ta, 1, p2);
+    ft_kloop<F16>(ta, nk, p0, p1, p2, p3, p4, acc);
 
     // ------------------------------------------------------------ epilogue
-    // Each wave owns 128 unique rows x one 128-wide head, written in two
-    // phases of 64 unique rows staged (bias added, fp32) in the wave's own
-    // ring slot.  The phase's receiver rows P0 .. P1-1 are walked by 8 lane
+    // Each wave owns 64 unique rows x one 128-wide head, written in two
+    // phases of 32 unique rows (one accumulator row block) staged with bias
+    // in fp32.  The phase's receiver rows P0 .. P1-1 are walked by 8 lane
     // groups, group g taking rows P0 + g + 8i (balanced, no divergence); lane
     // q of a group owns pairs 8q .. 8q+7.  The unique row of a receiver row
     // comes from the run index array (coalesced loads one round of 64 rows
@@ -288,34 +327,31 @@ __global__ __launch_bounds__(FT_THREADS, 1) void flat_gemm_kernel(const FlatKArg
       bcol[ni] = bias ? bias[static_cast<int64_t>(l) * args.f_out + n0 + wn * 128 + ni * 32 + (lane & 31)] : 0.0f;
     const bool rot = args.rotate[role] != 0;
     uint16_t* outp = args.out[role] + static_cast<int64_t>(l) * args.recv_tokens * args.f_out + n0 + col;
-    float* ep = reinterpret_cast<float*>(wave == 0 ? s0 : (wave == 1 ? s1 : (wave == 2 ? s2 : s3)));
-    // every wave has finished reading the ring (the last step read slot 3)
+    // every wave has finished reading the parts
     FT_COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
     FT_COMPILER_FENCE();
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
-      const int32_t u0 = m0 + wm * 128 + 64 * ph;
-      // stage rows 64*ph .. +64 (columns XOR 32 on rows with bit 2 set so the
-      // two half-waves hit different banks); the scheduling barrier keeps the
-      // accumulator reads of a phase here
+      const int32_t u0 = m0 + wm * 64 + 32 * ph;
+      // stage the phase's 32 rows (columns XOR 32 on rows with bit 2 set so
+      // the two half-waves hit different banks); the scheduling barrier keeps
+      // the accumulator reads of a phase here
       __builtin_amdgcn_sched_barrier(0);
       FT_COMPILER_FENCE();
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2)
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 32 * m2 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int cc = (ni * 32 + (lane & 31)) ^ (((row >> 2) & 1) << 5);
-            ep[row * 128 + cc] = acc[2 * ph + m2][ni][r] + bcol[ni];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int cc = (ni * 32 + (lane & 31)) ^ (((row >> 2) & 1) << 5);
+          ep[row * 128 + cc] = acc[ph][ni][r] + bcol[ni];
+        }
       FT_COMPILER_FENCE();  // LDS operations of one wave execute in order
       __builtin_amdgcn_sched_barrier(0);
       if (u0 >= U) continue;
       const int32_t p0 = args.run_begin[u0];
-      const int32_t n = args.run_begin[min(u0 + 64, U)] - p0;
+      const int32_t n = args.run_begin[min(u0 + 32, U)] - p0;
       float cs[8], sn[8], c8[8], s8[8];
       if (rot) {
         const float4* t8 = reinterpret_cast<const float4*>(args.tab_recv + 8 * 64 + 8 * q);
@@ -376,7 +412,7 @@ __global__ __launch_bounds__(FT_THREADS, 1) void flat_gemm_kernel(const FlatKArg
         rv = rv_next;
       }
     }
-    // the next tile's first loads overwrite slots 0..2 (staging of waves 0..2)
+    // the next tile's first loads overwrite parts 1 and 2 (staging)
     FT_COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
     FT_COMPILER_FENCE();
@@ -436,7 +472,8 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
   a.run_begin = p.runs.run_begin;
   a.r2u = p.runs.recv_to_uniq;
   a.n_uniq = p.runs.n_uniq;
-  if (p.k_dim % (4 * FT_BK) != 0 || p.send_row % FT_BK != 0) return KVX_ERR_UNSUPPORTED;
+  if (p.k_dim % FT_BK != 0 || p.k_dim < FT_BK || p.send_row % FT_BK != 0 || p.f_out % FT_N != 0)
+    return KVX_ERR_UNSUPPORTED;
   for (int l = 0; l < p.recv_layers; ++l)
     for (int t = 0; t < p.n_taps; ++t)
       a.taps[l][t / 4] |= static_cast<uint32_t>(p.taps[l * p.n_taps + t] & 0xff) << (8 * (t % 4));
