@@ -9,6 +9,9 @@
 
 namespace kvx {
 
+constexpr int32_t RECV_TAB_MIN = 16;
+static int32_t recv_tab_rows(int32_t n) { return n > RECV_TAB_MIN ? n : RECV_TAB_MIN; }
+
 int device_cu_count() {
   static std::mutex mu;
   static int cached[64] = {0};
@@ -63,7 +66,10 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
     w.runs_scratch = c.take<char>(runs_ws_bytes(nr));
   }
   if (srope) w.tab_send = c.take<float2>(static_cast<size_t>(send->tokens) * (send->head_dim / 2));
-  if (rrope) w.tab_recv = c.take<float2>(static_cast<size_t>(nr) * (recv->head_dim / 2));
+  // the receiver table holds at least RECV_TAB_MIN positions: the flattened
+  // epilogue reads the (cos, sin) step of its rotation recurrence from the
+  // table row of position 8, also for caches of fewer tokens
+  if (rrope) w.tab_recv = c.take<float2>(static_cast<size_t>(recv_tab_rows(nr)) * (recv->head_dim / 2));
   if (!f32 && !per_head && srope) {
     // U <= N_R always (U <= N_S only for non-decreasing maps)
     w.rows_cap = nr;
@@ -190,7 +196,8 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
       if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
     }
     if (w.tab_recv) {
-      if (int st = launch_rope_table(w.tab_recv, recv->tokens, recv->head_dim, recv->rope_base, s)) return st;
+      if (int st = launch_rope_table(w.tab_recv, recv_tab_rows(recv->tokens), recv->head_dim, recv->rope_base, s))
+        return st;
     }
     F32Problem p{};
     p.send_layers = send->layers;
@@ -271,7 +278,8 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
       r.a_f16 = 0;
     }
     if (w.tab_recv) {
-      if (int st = launch_rope_table(w.tab_recv, recv->tokens, recv->head_dim, recv->rope_base, s)) return st;
+      if (int st = launch_rope_table(w.tab_recv, recv_tab_rows(recv->tokens), recv->head_dim, recv->rope_base, s))
+        return st;
     }
     if (split) {
       if (int st = launch_prepare_maps(wt_k, w.wk16, map_rows, f_in, r.a_f16 ? 2 : 1, s)) return st;
