@@ -48,6 +48,41 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return static_cast<uint32_t>(f32_to_f16_bits(a)) | (static_cast<uint32_t>(f32_to_f16_bits(b)) << 16);
 }
 
+// ---------------------------------------------------------------- direct loads, waits
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Buffer resource over [base, base + bytes) for raw 32-bit loads (word 3 as
+// for gfx9 raw buffers); loads past the end return zero without a memory
+// access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from the buffer at voffset + soffset (per-lane and
+// uniform byte offsets) straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding:
+// vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
+#define KVX_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
+#define KVX_COMPILER_FENCE() asm volatile("" ::: "memory")
+// s_waitcnt lgkmcnt(0): this wave's LDS writes are complete (a barrier alone
+// does not wait for them).
+#define KVX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// Two fp32 -> packed bf16 (hardware convert, round to nearest even).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
+// Wave index inside the workgroup as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ---------------------------------------------------------------- launch check
 
 #define KVX_HIP_TRY(expr)                                        \

@@ -80,33 +80,6 @@ struct FlatKArgs {
   uint32_t taps[MAX_LAYERS][2];
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Buffer resource over [base, base + bytes) for raw 32-bit loads (word 3 as
-// for gfx9 raw buffers); loads past the end return zero without a memory
-// access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ft_rsrc(const char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-
-// 16 bytes per lane from the buffer at voffset + soffset (per-lane and
-// uniform byte offsets) into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, voff, soff, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding:
-// vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
-#define FT_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x70 | 0xF00)
-#define FT_COMPILER_FENCE() asm volatile("" ::: "memory")
-
-// Two fp32 -> packed bf16 (hardware convert, round to nearest even).
-__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
-}
-
 template <bool F16>
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   if constexpr (F16)
@@ -137,9 +110,6 @@ struct TileAddr {
   int32_t nk;                   // K steps of the problem
 };
 
-// Wave index as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
 // Layer source of step k (fp32 maps split in two repeat the taps).
 __device__ __forceinline__ uint32_t ft_layer(const TileAddr& ta, int k) {
   const int32_t tap = (k / ta.spt) % ta.n_taps;
@@ -150,7 +120,7 @@ __device__ __forceinline__ uint32_t ft_layer(const TileAddr& ta, int k) {
 __device__ __forceinline__ void ft_issue_a(const TileAddr& ta, int k, uint16_t* part) {
   const int wave = wave_id();
   const bool live = k < ta.nk;
-  const __amdgpu_buffer_rsrc_t a_r = ft_rsrc(ta.a_src + static_cast<int64_t>(ft_layer(ta, k)) * ta.a_ls,
+  const __amdgpu_buffer_rsrc_t a_r = buf_rsrc(ta.a_src + static_cast<int64_t>(ft_layer(ta, k)) * ta.a_ls,
                                              live ? static_cast<uint32_t>(ta.a_ls) : 0u);
   const uint32_t a_soff = 2u * static_cast<uint32_t>((k % ta.spt) * FT_BK);
 #pragma unroll
@@ -160,7 +130,7 @@ __device__ __forceinline__ void ft_issue_a(const TileAddr& ta, int k, uint16_t* 
 // W part of step k into `part`.
 __device__ __forceinline__ void ft_issue_b(const TileAddr& ta, int k, uint16_t* part) {
   const int wave = wave_id();
-  const __amdgpu_buffer_rsrc_t w_r = ft_rsrc(ta.w_base, k < ta.nk ? ta.w_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t w_r = buf_rsrc(ta.w_base, k < ta.nk ? ta.w_bytes : 0u);
   const uint32_t b_soff = 2u * static_cast<uint32_t>(k * FT_BK);
 #pragma unroll
   for (int i = 0; i < FT_B_LD; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * FT_B_LD + i) * 512);
@@ -196,10 +166,10 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
 // one barrier: the parts of the current step are complete and every wave
 // has finished the previous step, whose two parts are now free.
 __device__ __forceinline__ void ft_sync() {
-  FT_WAIT_VM(FT_A_LD);
-  FT_COMPILER_FENCE();
+  KVX_WAIT_VM(FT_A_LD);
+  KVX_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
-  FT_COMPILER_FENCE();
+  KVX_COMPILER_FENCE();
 }
 
 // One step of the ring: A of step k is in part 2k mod 5, W in part
@@ -226,7 +196,7 @@ __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p
     FT_STEP(k + 3, p1, p2, p4, p0, k + 3 < nk)
     FT_STEP(k + 4, p3, p4, p1, p2, k + 4 < nk)
   }
-  FT_WAIT_VM(0);
+  KVX_WAIT_VM(0);
 }
 #undef FT_STEP
 
@@ -328,9 +298,9 @@ flat_gemm_kernel(const FlatKArgs args) {
     const bool rot = args.rotate[role] != 0;
     uint16_t* outp = args.out[role] + static_cast<int64_t>(l) * args.recv_tokens * args.f_out + n0 + col;
     // every wave has finished reading the parts
-    FT_COMPILER_FENCE();
+    KVX_COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
-    FT_COMPILER_FENCE();
+    KVX_COMPILER_FENCE();
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
       const int32_t u0 = m0 + wm * 64 + 32 * ph;
@@ -338,7 +308,7 @@ flat_gemm_kernel(const FlatKArgs args) {
       // the two half-waves hit different banks); the scheduling barrier keeps
       // the accumulator reads of a phase here
       __builtin_amdgcn_sched_barrier(0);
-      FT_COMPILER_FENCE();
+      KVX_COMPILER_FENCE();
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -347,7 +317,7 @@ flat_gemm_kernel(const FlatKArgs args) {
           const int cc = (ni * 32 + (lane & 31)) ^ (((row >> 2) & 1) << 5);
           ep[row * 128 + cc] = acc[ph][ni][r] + bcol[ni];
         }
-      FT_COMPILER_FENCE();  // LDS operations of one wave execute in order
+      KVX_COMPILER_FENCE();  // LDS operations of one wave execute in order
       __builtin_amdgcn_sched_barrier(0);
       if (u0 >= U) continue;
       const int32_t p0 = args.run_begin[u0];
@@ -413,9 +383,9 @@ flat_gemm_kernel(const FlatKArgs args) {
       }
     }
     // the next tile's first loads overwrite parts 1 and 2 (staging)
-    FT_COMPILER_FENCE();
+    KVX_COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
-    FT_COMPILER_FENCE();
+    KVX_COMPILER_FENCE();
   }
 }
 

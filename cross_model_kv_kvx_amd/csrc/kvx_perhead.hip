@@ -4,20 +4,40 @@
 // KV head with its own d x d matrix when sender and receiver share head count
 // and head dimension; stage 3 assigns each receiver layer one sender layer by
 // proportional depth.  Several receiver layers may read the same sender layer
-// (a deeper receiver), so one block reads a sender tile once and applies the
-// maps of every receiver layer assigned to that sender layer.  The work per
-// byte is low (a 128 x 128 map per 256-byte row), so this path is bound by
-// HBM: X is read once, Y written once, and the fp32 maps are split into a
-// bf16 high and low half on the fly (two matrix-core passes keep fp32-level
-// accuracy of the map while the bf16 inputs stay exact).
+// (a deeper receiver); their workgroups run side by side on one XCD so the
+// sender rows come from HBM once.  The work per byte is low (a 128 x 128 map
+// per 256-byte row), so this path is bound by HBM.
 
 #include "kvx_internal.hpp"
 
 namespace kvx {
 
 // ---------------------------------------------------------------- bf16 caches, d = 128
-constexpr int PH_TOK = 256;      // receiver tokens per block (64 per wave)
-constexpr int PH_LDW = 136;      // LDS row stride of a staged map (128 + 8)
+// One workgroup per (role, receiver layer l, head h, span of up to 2048
+// receiver tokens) with two kinds of waves:
+//   * compute waves 0..3, wave w owning outputs 32w .. 32w+31 of the head.
+//     The wave's 32 rows of W_{l,h} stay in registers for the whole span as
+//     MFMA A fragments (fp32 maps split once into bf16 high and low halves:
+//     y = x W_hi + x W_lo keeps fp32-level accuracy of the map while the bf16
+//     inputs stay exact).  The sender rows of 64-token tiles stream through a
+//     ring of six 16 KB LDS stages by direct global->LDS 16-byte loads (whole
+//     256-byte rows, 16-byte chunks XOR-swizzled by row so fragment reads of
+//     16 consecutive rows hit distinct banks); the span's token map is
+//     copied to LDS once at the start.  Each tile's 64 x 128 bf16 outputs
+//     are staged in one of two 16 KB LDS buffers;
+//   * store waves 4..7 write the staged tile one step later, 16 bytes per
+//     lane and four whole 256-byte rows per instruction.
+// The vector-memory counter is per wave: compute waves only load, so their
+// waits name exactly the tile they need, and store waves never wait, so no
+// load ever waits for stores to complete.  One barrier per tile orders the
+// stages and staging buffers between the two kinds.  Workgroups are numbered
+// receiver layer innermost and consecutive numbers go to one XCD, so the
+// receiver layers that share a sender layer read its rows through one L2.
+constexpr int PH_TILE = 64;                      // tokens per tile
+constexpr int PH_SPAN = 4096;                    // tokens per workgroup
+constexpr int PH_TILE_ELEMS = PH_TILE * 128;     // 16-bit elements of a tile (16 KB)
+constexpr int PH_RING = 6;                       // LDS stages of sender tiles
+constexpr int PH_THREADS = 512;                  // 4 compute + 4 store waves
 
 struct HeadKArgs {
   const uint16_t* x[2];
@@ -25,120 +45,238 @@ struct HeadKArgs {
   const float* bias[2];
   uint16_t* out[2];
   const int32_t* map;
-  int32_t send_layers, send_tokens, recv_layers, recv_tokens, heads, n_chunks;
-  int32_t n_blocks, xcd_remap;
-  uint8_t first[MAX_LAYERS + 1];   // receiver layers of sender layer s: list[first[s] .. first[s+1])
-  uint8_t list[MAX_LAYERS];
+  int32_t send_tokens, recv_layers, recv_tokens, heads, n_span, n_blocks, xcd_remap;
+  uint8_t tap[MAX_LAYERS];  // sender layer of each receiver layer
 };
 
-template <bool WF32>
-__global__ __launch_bounds__(256, 2) void perhead_kernel(const HeadKArgs a) {
-  constexpr int SPLIT = WF32 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t wsm[SPLIT * 128 * PH_LDW];
+// Physical 16-byte chunk of logical chunk c in tile row r.
+__device__ __forceinline__ int ph_chunk(int r, int c) { return c ^ (r & 15); }
 
-  int32_t b = blockIdx.x;
-  if (a.xcd_remap) b = (b & 7) * (a.n_blocks >> 3) + (b >> 3);
-  const int32_t chunk = b % a.n_chunks;
-  int32_t rest = b / a.n_chunks;
-  const int32_t h = rest % a.heads;
-  rest /= a.heads;
-  const int32_t s = rest % a.send_layers;
-  const int role = rest / a.send_layers;
-  const int32_t l_begin = a.first[s], l_end = a.first[s + 1];
-  if (l_begin == l_end) return;
+struct PhTile {
+  __amdgpu_buffer_rsrc_t xr;  // sender rows of layer s, head h
+  const int32_t* msm;         // LDS: sender row of each token of the span
+  int32_t t0, n_tok, n_tiles;
+  uint32_t row_bytes;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t tok0 = chunk * PH_TOK + wave * 64;
-  const int64_t row_elems = static_cast<int64_t>(a.heads) * 128;
-
-  // X fragments (B operand): token tok0 + 32*ti + lane%32, channels
-  // 16*ks + 8*(lane/32) .. +8.
-  u32x4 xf[2][8];
+// Direct loads of tile k (64 rows) into `slot` by compute wave w: rows
+// 16w .. 16w+15 with 4 instructions of 4 rows; lane j of instruction i takes
+// row 16w + 4i + j/16, physical chunk j%16.  Tiles past the end read nothing.
+__device__ __forceinline__ void ph_issue(const PhTile& pt, int k, uint16_t* slot) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const bool live = k < pt.n_tiles;
+  const __amdgpu_buffer_rsrc_t xr = live ? pt.xr : buf_rsrc(nullptr, 0);
+  const int q = lane >> 4;
+  const int32_t r0 = k * PH_TILE + 16 * wave + q;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
-    int32_t tok = tok0 + 32 * ti + (lane & 31);
-    tok = tok < a.recv_tokens ? tok : a.recv_tokens - 1;
-    int32_t src = a.map[tok];
-    src = src < 0 ? 0 : (src >= a.send_tokens ? a.send_tokens - 1 : src);
-    const uint16_t* xp = a.x[role] + (static_cast<int64_t>(s) * a.send_tokens + src) * row_elems + h * 128 + (lane >> 5) * 8;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) xf[ti][ks] = *reinterpret_cast<const u32x4*>(xp + ks * 16);
+  for (int i = 0; i < 4; ++i) {
+    // tiles past the end (not multiplied) read an in-range map entry
+    const int32_t sv = pt.msm[min(r0 + 4 * i, PH_SPAN - 1)];
+    const int row = 16 * wave + 4 * i + q;
+    const uint32_t voff = static_cast<uint32_t>(sv) * pt.row_bytes + 16u * ph_chunk(row, lane & 15);
+    dma16(xr, voff, 0, slot + (4 * wave + i) * 512);
   }
+}
 
-  for (int32_t li = l_begin; li < l_end; ++li) {
-    const int32_t l = a.list[li];
-    __syncthreads();
-    // stage W_{l,h} (output-major [o][c]) into LDS as bf16 (hi[, lo])
-    if constexpr (WF32) {
-      const float* wp = static_cast<const float*>(a.wt[role]) + (static_cast<int64_t>(l) * a.heads + h) * 128 * 128;
-#pragma unroll 4
-      for (int i = tid; i < 128 * 32; i += 256) {
-        const int o = i >> 5, c4 = (i & 31) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(wp + o * 128 + c4);
-        const uint32_t h0 = pack_bf16(v.x, v.y), h1 = pack_bf16(v.z, v.w);
-        const uint32_t l0 = pack_bf16(v.x - bf16lo(h0), v.y - bf16hi(h0));
-        const uint32_t l1 = pack_bf16(v.z - bf16lo(h1), v.w - bf16hi(h1));
-        *reinterpret_cast<u32x2*>(wsm + o * PH_LDW + c4) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(wsm + 128 * PH_LDW + o * PH_LDW + c4) = u32x2{l0, l1};
-      }
-    } else {
-      const uint16_t* wp = static_cast<const uint16_t*>(a.wt[role]) + (static_cast<int64_t>(l) * a.heads + h) * 128 * 128;
-#pragma unroll 4
-      for (int i = tid; i < 128 * 16; i += 256) {
-        const int o = i >> 4, c8 = (i & 15) * 8;
-        *reinterpret_cast<u32x4*>(wsm + o * PH_LDW + c8) = *reinterpret_cast<const u32x4*>(wp + o * 128 + c8);
-      }
-    }
-    __syncthreads();
-
-    f32x16 acc[2][4];
+// Fragments of one tile, MFMA D[n][tok] += W[n][k] X[tok][k]; stage outputs
+// (bias added, bf16 nearest even) into `ys` as [tok][n] with swizzled chunks.
+template <bool WF32>
+__device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, const u32x4 (&wh)[8],
+                                           const u32x4 (&wl)[8], const float (&bn)[16]) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const char* xb = reinterpret_cast<const char*>(xs);
+  f32x16 acc[2];
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+  for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+    for (int e = 0; e < 16; ++e) acc[ti][e] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[ti][ni][e] = 0.0f;
-
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-#pragma unroll
-        for (int sp = 0; sp < SPLIT; ++sp) {
-          const u32x4 wf = *reinterpret_cast<const u32x4*>(
-              wsm + sp * 128 * PH_LDW + (ni * 32 + (lane & 31)) * PH_LDW + ks * 16 + (lane >> 5) * 8);
-#pragma unroll
-          for (int ti = 0; ti < 2; ++ti)
-            acc[ti][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, wf), __builtin_bit_cast(bf16x8, xf[ti][ks]), acc[ti][ni], 0, 0, 0);
-        }
-      }
-    }
-
-    // D[n][tok]: lane holds token 32*ti + lane%32 and outputs
-    // n = 32*ni + 8*(r/4) + 4*(lane/32) + r%4.
-    const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 xf[2];
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
-      const int32_t tok = tok0 + 32 * ti + (lane & 31);
-      if (tok >= a.recv_tokens) continue;
-      uint16_t* op = a.out[role] + (static_cast<int64_t>(l) * a.recv_tokens + tok) * row_elems + h * 128;
+      const int row = 32 * ti + (lane & 31);
+      xf[ti] = *reinterpret_cast<const u32x4*>(xb + row * 256 + 16 * ph_chunk(row, 2 * ks + (lane >> 5)));
+    }
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+    for (int ti = 0; ti < 2; ++ti) {
+      acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wh[ks]),
+                                                        __builtin_bit_cast(bf16x8, xf[ti]), acc[ti], 0, 0, 0);
+      if constexpr (WF32)
+        acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wl[ks]),
+                                                          __builtin_bit_cast(bf16x8, xf[ti]), acc[ti], 0, 0, 0);
+    }
+  }
+  // lane: token 32 ti + lane % 32, outputs n = 32 wave + 8 g + 4 (lane / 32) + e
+  char* yb = reinterpret_cast<char*>(ys);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = ni * 32 + 8 * g + 4 * (lane >> 5);
-          float v[4];
+  for (int ti = 0; ti < 2; ++ti) {
+    const int tok = 32 * ti + (lane & 31);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[ti][ni][4 * g + e] + (bias ? bias[n + e] : 0.0f);
-          *reinterpret_cast<u32x2*>(op + n) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int c = 4 * wave + g;  // 16-byte chunk of outputs 8c .. 8c+7
+      const u32x2 v = u32x2{cvt_bf16x2(acc[ti][4 * g] + bn[4 * g], acc[ti][4 * g + 1] + bn[4 * g + 1]),
+                            cvt_bf16x2(acc[ti][4 * g + 2] + bn[4 * g + 2], acc[ti][4 * g + 3] + bn[4 * g + 3])};
+      *reinterpret_cast<u32x2*>(yb + tok * 256 + 16 * ph_chunk(tok, c) + 8 * (lane >> 5)) = v;
     }
   }
 }
 
+// Store a staged tile by the 256 threads of the store waves: thread t writes
+// 16 bytes of row 16 q + t / 16 for q = 0..3 (rows past the span end are
+// skipped).
+__device__ __forceinline__ void ph_store(const uint16_t* ys, uint16_t* out_tile, int32_t rows, int64_t row_elems) {
+  const int t = threadIdx.x - 256;
+  const char* yb = reinterpret_cast<const char*>(ys);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 16 * q + (t >> 4);
+    const int c = t & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(yb + row * 256 + 16 * ph_chunk(row, c));
+    if (row < rows) *reinterpret_cast<u32x4*>(out_tile + row * row_elems + 8 * c) = v;
+  }
+}
+
+__device__ __forceinline__ void ph_barrier() {
+  KVX_COMPILER_FENCE();
+  __builtin_amdgcn_s_barrier();
+  KVX_COMPILER_FENCE();
+}
+
+template <bool WF32>
+__global__ __attribute__((amdgpu_flat_work_group_size(PH_THREADS, PH_THREADS), amdgpu_waves_per_eu(2, 2))) void
+perhead_kernel(const HeadKArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t x0[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t x1[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t x2[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t x3[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t x4[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t x5[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t y0[PH_TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t y1[PH_TILE_ELEMS];
+  __shared__ int32_t msm[PH_SPAN];
+
+  int32_t b = blockIdx.x;
+  if (a.xcd_remap) b = (b & 7) * (a.n_blocks >> 3) + (b >> 3);
+  const int32_t l = b % a.recv_layers;
+  int32_t rest = b / a.recv_layers;
+  const int32_t span = rest % a.n_span;
+  rest /= a.n_span;
+  const int32_t h = rest % a.heads;
+  const int role = rest / a.heads;
+  const int32_t s = a.tap[l];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int64_t row_elems = static_cast<int64_t>(a.heads) * 128;
+
+  PhTile pt;
+  pt.t0 = span * PH_SPAN;
+  pt.n_tok = min(PH_SPAN, a.recv_tokens - pt.t0);
+  pt.n_tiles = (pt.n_tok + PH_TILE - 1) / PH_TILE;
+  pt.msm = msm;
+  pt.row_bytes = static_cast<uint32_t>(2 * row_elems);
+  const uint16_t* xs = a.x[role] + static_cast<int64_t>(s) * a.send_tokens * row_elems + h * 128;
+  pt.xr = buf_rsrc(xs, static_cast<uint32_t>(static_cast<int64_t>(a.send_tokens) * 2 * row_elems - 256 * h));
+  uint16_t* out = a.out[role] + (static_cast<int64_t>(l) * a.recv_tokens + pt.t0) * row_elems + h * 128;
+
+  // the span's token map, clamped to valid sender rows (entries past the
+  // span repeat its last token)
+  for (int i = threadIdx.x; i < PH_SPAN; i += PH_THREADS) {
+    int32_t v = a.map[pt.t0 + min(i, pt.n_tok - 1)];
+    msm[i] = v < 0 ? 0 : (v >= a.send_tokens ? a.send_tokens - 1 : v);
+  }
+  __syncthreads();
+
+  // Every wave passes the barriers B_0 .. B_n (n = n_tiles) once each: at
+  // B_k tile k is in LDS and the staged tile k-1 is complete.
+  if (wave >= 4) {
+    ph_barrier();  // B_0
+    for (int32_t k = 1; k <= pt.n_tiles; ++k) {
+      ph_barrier();  // B_k: store tile k-1
+      ph_store(((k - 1) & 1) ? y1 : y0, out + static_cast<int64_t>(k - 1) * PH_TILE * row_elems,
+               pt.n_tok - (k - 1) * PH_TILE, row_elems);
+    }
+    return;
+  }
+
+  // compute waves: tiles 0 .. 4 in flight while the map fragments are prepared
+  ph_issue(pt, 0, x0);
+  ph_issue(pt, 1, x1);
+  ph_issue(pt, 2, x2);
+  ph_issue(pt, 3, x3);
+  ph_issue(pt, 4, x4);
+
+  // A fragments: rows n = 32 wave + lane % 32 of W_{l,h} ([n][c], output
+  // major), k = 16 ks + 8 (lane / 32) .. +8
+  u32x4 wh[8], wl[8];
+  const int n_row = 32 * wave + (lane & 31);
+  if constexpr (WF32) {
+    const float* wp = static_cast<const float*>(a.wt[role]) +
+                      ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float4 u = *reinterpret_cast<const float4*>(wp + 16 * ks);
+      const float4 v = *reinterpret_cast<const float4*>(wp + 16 * ks + 4);
+      const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
+        lo[e] = pack_bf16(f[2 * e] - bf16lo(hi[e]), f[2 * e + 1] - bf16hi(hi[e]));
+      }
+      wh[ks] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      wl[ks] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+  } else {
+    const uint16_t* wp = static_cast<const uint16_t*>(a.wt[role]) +
+                         ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      wh[ks] = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
+      wl[ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  float bn[16];
+  const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bn[r] = bias ? bias[32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] : 0.0f;
+
+  // Step k (tile k in stage k % 6, staging k % 2): the wait leaves the four
+  // younger tiles in flight and completes this wave's staging writes, then
+  // B_k; tile k+5 is issued into the stage of tile k-1 and tile k is
+  // multiplied into its staging buffer.  Steps past n_tiles (the unrolled
+  // loop runs a multiple of 6) pass no barrier.
+#define PH_STEP(K, XS, YS, XNEXT)                                            \
+  {                                                                          \
+    if ((K) <= pt.n_tiles) {                                                 \
+      KVX_WAIT_VM(4 * (PH_RING - 2));                                        \
+      KVX_WAIT_LGKM0();                                                      \
+      ph_barrier();                                                          \
+    }                                                                        \
+    ph_issue(pt, (K) + PH_RING - 1, XNEXT);                                  \
+    if ((K) < pt.n_tiles) ph_compute<WF32>(XS, YS, wh, wl, bn);              \
+  }
+  for (int32_t k = 0; k < pt.n_tiles; k += 6) {
+    PH_STEP(k, x0, y0, x5)
+    PH_STEP(k + 1, x1, y1, x0)
+    PH_STEP(k + 2, x2, y0, x1)
+    PH_STEP(k + 3, x3, y1, x2)
+    PH_STEP(k + 4, x4, y0, x3)
+    PH_STEP(k + 5, x5, y1, x4)
+  }
+#undef PH_STEP
+  // B_n when the loop ended exactly at step n - 1; then drain the loads of
+  // tiles past the end before the workgroup's LDS is released
+  if (pt.n_tiles % 6 == 0) {
+    KVX_WAIT_LGKM0();
+    ph_barrier();
+  }
+  KVX_WAIT_VM(0);
+}
+
 int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hipStream_t s) {
   if (p.recv_tokens <= 0 || n_roles <= 0) return KVX_OK;
+  // sender rows of one layer are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(p.send_tokens) * p.heads * 256 >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
   HeadKArgs a{};
   for (int i = 0; i < n_roles; ++i) {
     a.x[i] = roles[i].x;
@@ -147,29 +285,20 @@ int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hip
     a.out[i] = roles[i].out;
   }
   a.map = p.recv_to_send;
-  a.send_layers = p.send_layers;
   a.send_tokens = p.send_tokens;
   a.recv_layers = p.recv_layers;
   a.recv_tokens = p.recv_tokens;
   a.heads = p.heads;
-  a.n_chunks = static_cast<int32_t>(ceil_div(p.recv_tokens, PH_TOK));
-  // receiver layers grouped by their sender layer (counting sort, ascending l)
-  int cnt[MAX_LAYERS + 1] = {0};
-  for (int l = 0; l < p.recv_layers; ++l) cnt[p.taps[l] + 1]++;
-  for (int q = 0; q < p.send_layers; ++q) cnt[q + 1] += cnt[q];
-  for (int q = 0; q <= p.send_layers; ++q) a.first[q] = static_cast<uint8_t>(cnt[q]);
-  int fill[MAX_LAYERS] = {0};
-  for (int l = 0; l < p.recv_layers; ++l) {
-    const int q = p.taps[l];
-    a.list[cnt[q] + fill[q]++] = static_cast<uint8_t>(l);
-  }
-  const int64_t nb = static_cast<int64_t>(n_roles) * p.send_layers * p.heads * a.n_chunks;
+  a.n_span = static_cast<int32_t>(ceil_div(p.recv_tokens, PH_SPAN));
+  for (int l = 0; l < p.recv_layers; ++l) a.tap[l] = static_cast<uint8_t>(p.taps[l]);
+  const int64_t nb = static_cast<int64_t>(n_roles) * p.heads * a.n_span * p.recv_layers;
+  if (nb >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
   a.n_blocks = static_cast<int32_t>(nb);
   a.xcd_remap = (nb % 8 == 0) ? 1 : 0;
   if (p.w_f32)
-    perhead_kernel<true><<<static_cast<unsigned>(nb), 256, 0, s>>>(a);
+    perhead_kernel<true><<<static_cast<unsigned>(nb), PH_THREADS, 0, s>>>(a);
   else
-    perhead_kernel<false><<<static_cast<unsigned>(nb), 256, 0, s>>>(a);
+    perhead_kernel<false><<<static_cast<unsigned>(nb), PH_THREADS, 0, s>>>(a);
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
