@@ -12,17 +12,29 @@ synthetic tensors resident in HBM before timing.
 
 Prints one JSON line.  ``value`` = receiver tokens translated per second
 (all layers, K+V).  ``roofline`` reports the dominant kernel (the grouped
-GEMM with its fused epilogue) against the bf16/fp16 dense matrix-core peak,
-timed with HIP events on the launch stream inside each timed step.
+GEMM with its fused epilogue, launched once per operand type: fp16 for the
+rotated-back keys, bf16 for the values) against the bf16/fp16 dense
+matrix-core peak, timed with HIP events on the launch stream inside each
+timed step.  ``traffic`` is the HBM bytes per launch read from the committed
+rocprofv3 counter summary when the kernel sources still match it, else null.
 ``cpu_baseline`` times the CPU oracle on a bounded row sample of the same
 workload.  ``also`` reports the per-head workload (32 -> 80 layers, 4096
 tokens, fp32 128 x 128 maps) against the HBM peak.
+
+Profiling helpers: ``--calibration-copy`` first runs a plain 1 GiB device
+copy (1 GiB read + 1 GiB written) so a rocprofv3 counter run of the same
+command sees a kernel of known traffic; ``--pmc-summary FETCH.csv WRITE.csv``
+turns the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run into the
+per-launch traffic summary kept under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,10 +48,106 @@ from cross_model_kv_kvx_amd import kvx, synth  # noqa: E402
 
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+CALIB_BYTES = 1 << 30            # bytes read (and written) by the calibration copy
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "flat_gemm_kernel": ["kvx_flat.hip", "kvx_common.hpp", "kvx_internal.hpp"],
+    "perhead_kernel": ["kvx_perhead.hip", "kvx_common.hpp", "kvx_internal.hpp"],
+}
+TRAFFIC_FILES = {
+    "flat_gemm_kernel": "flat_gemm_kernel__crossfamily_rope_32k__traffic.md",
+    "perhead_kernel": "perhead_kernel__32to80_4k__traffic.md",
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "cross_model_kv_kvx_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, TRAFFIC_FILES[kernel])
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"source hash: `([0-9a-f]+)`", text)
+    m_b = re.search(r"HBM bytes per launch \(mean\): `([0-9.]+)`", text)
+    if not m_h or not m_b or m_h.group(1) != source_hash(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+def calibration_copy(dev):
+    """A plain device copy of known size: CALIB_BYTES read, CALIB_BYTES written
+    per dispatch (an elementwise multiply by one, run twice)."""
+    src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """Markdown traffic summaries from a FETCH_SIZE and a WRITE_SIZE counter run
+    (rocprofv3 --pmc ... --output-format csv) of a --calibration-copy command."""
+    def per_kernel(path, counter):
+        rows = sorted((r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        vals = {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            key = None
+            if "flat_gemm_kernel" in name:
+                key = "flat_gemm_kernel"
+            elif "perhead_kernel" in name:
+                key = "perhead_kernel"
+            elif "MulFunctor" in name and len(vals.get("copy", [])) < 2:
+                key = "copy"  # the calibration copy runs first, twice
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+        return vals
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    if "copy" not in f or "copy" not in w:
+        raise SystemExit("no calibration copy in the counter files (run the command with --calibration-copy)")
+    kf = CALIB_BYTES / float(np.median(f["copy"]))
+    kw = CALIB_BYTES / float(np.median(w["copy"]))
+    out = {}
+    for kernel in ("flat_gemm_kernel", "perhead_kernel"):
+        if kernel not in f or kernel not in w:
+            continue
+        fb = np.array(f[kernel]) * kf
+        wb = np.array(w[kernel]) * kw
+        n = min(fb.size, wb.size)
+        tot = fb[:n] + wb[:n]
+        out[kernel] = (f"# HBM traffic: {kernel}\n\n"
+                       f"source hash: `{source_hash(kernel)}`\n\n"
+                       "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths "
+                       "relative to the repository), then this summary:\n\n```\n"
+                       "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch -o fetch --output-format csv -- "
+                       "python3 bench.py --calibration-copy --steps 2 --warmup 1 --no-cpu-baseline\n"
+                       "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write -o write --output-format csv -- "
+                       "python3 bench.py --calibration-copy --steps 2 --warmup 1 --no-cpu-baseline\n"
+                       "python3 bench.py --pmc-summary gpurun_out/prof/fetch/fetch_counter_collection.csv "
+                       "gpurun_out/prof/write/write_counter_collection.csv\n```\n\n"
+                       f"Counters: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one rocprofv3 run each.\n"
+                       f"Calibration: a plain copy of {CALIB_BYTES} bytes read and written reads "
+                       f"FETCH_SIZE {np.median(f['copy']):.0f} B and WRITE_SIZE {np.median(w['copy']):.0f} B, "
+                       f"so the factors are {kf:.4f} (fetch) and {kw:.4f} (write).\n\n"
+                       f"| dispatches | fetch bytes (mean) | write bytes (mean) |\n|---|---|---|\n"
+                       f"| {n} | {fb[:n].mean():.4g} | {wb[:n].mean():.4g} |\n\n"
+                       f"HBM bytes per launch (mean): `{tot.mean():.6g}`\n")
+    return out
 
 
 def flat_inputs(dev):
@@ -136,7 +244,8 @@ def perhead_measure(dev, steps=10):
     return {"workload": "per-head 32->80 layers, 4096 tokens, 8x128 heads, fp32 maps, bf16 caches",
             "tokens_per_s": 4096 / t, "kernel_ms": t * 1e3,
             "roofline": {"bound": "hbm", "achieved": bytes_alg / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": bytes_alg / t / 1e9 / PEAK_HBM_GBS, "traffic": None}}
+                         "frac": bytes_alg / t / 1e9 / PEAK_HBM_GBS, "traffic": committed_traffic("perhead_kernel"),
+                         "kernel": "perhead_kernel", "launch_ms": t * 1e3, "algorithmic_bytes_per_launch": bytes_alg}}
 
 
 def main():
@@ -146,13 +255,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.pmc_summary:
+        for kernel, text in pmc_summary(*args.pmc_summary).items():
+            path = os.path.join(PROFILES, TRAFFIC_FILES[kernel])
+            with open(path, "w") as fh:
+                fh.write(text)
+            print(f"wrote {path}")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the translation runs on a single device with no collectives; "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        log("bench: calibration copy")
+        calibration_copy(dev)
     log("bench: building inputs")
     x = flat_inputs(dev)
     taps = kvx.layer_map(36, 32, 3, 4)
@@ -183,8 +304,15 @@ def main():
     U = int(1 + np.count_nonzero(np.diff(m)))
     gemm_ms = float(np.mean([s[1] for s in stages]))
     prep_ms = float(np.mean([s[0] for s in stages]))
-    flops = 2.0 * U * 3072 * 1024 * 32 * 2
-    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    # one launch per role (K: fp16 operands, V: bf16); algorithmic work of a
+    # launch: U distinct sender rows x 3072 features x 1024 outputs x 32 layers
+    launches = 2
+    launch_ms = gemm_ms / launches
+    flops = 2.0 * U * 3072 * 1024 * 32
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    # algorithmic bytes of a launch: unique sender rows of the 3 taps, maps,
+    # bias, and every receiver row written once
+    bytes_alg = 32 * (3 * U * 2048 + 3072 * 1024 * 2 + 1024 * 4 + N_R * 2048)
     res = {
         "metric": "translated KV tokens/sec (all layers, K+V) at 32k ctx; % of MFMA/HBM roofline",
         "value": N_R / (ms_step * 1e-3),
@@ -203,9 +331,9 @@ def main():
                    "recv_tokens": N_R, "send_tokens": int(x["send_end_h"].size), "distinct_sender_rows": U,
                    "global_batch": 1, "seq_len": N_R, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": None,
-                     "kernel": "flat_gemm_kernel", "kernel_ms": gemm_ms, "prep_ms": prep_ms,
-                     "flops_per_launch": flops},
+                     "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": committed_traffic("flat_gemm_kernel"),
+                     "kernel": "flat_gemm_kernel", "launches_per_step": launches, "launch_ms": launch_ms,
+                     "flops_per_launch": flops, "algorithmic_bytes_per_launch": bytes_alg, "prep_ms": prep_ms},
     }
     if not args.no_also:
         log("bench: per-head workload")
