@@ -80,7 +80,7 @@ def committed_traffic(kernel):
         return None
     text = open(path).read()
     m_h = re.search(r"source hash: `([0-9a-f]+)`", text)
-    m_b = re.search(r"HBM bytes per launch \(mean\): `([0-9.]+)`", text)
+    m_b = re.search(r"HBM bytes per launch \(mean\): `([0-9.eE+-]+)`", text)
     if not m_h or not m_b or m_h.group(1) != source_hash(kernel):
         return None
     return float(m_b.group(1))
