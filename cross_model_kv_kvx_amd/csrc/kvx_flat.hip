@@ -392,36 +392,62 @@ flat_gemm_kernel(const FlatKArgs args) {
 // ---------------------------------------------------------------- map preparation
 // mode 0: bf16 -> fp16 (same layout); mode 1: fp32 -> [bf16 hi | bf16 lo];
 // mode 2: fp32 -> [fp16 hi | fp16 lo].  Split maps double the K extent:
-// out[l][o][f] = hi, out[l][o][F_in + f] = lo.
+// out[l][o][f] = hi, out[l][o][F_in + f] = lo.  Each thread converts 8
+// (mode 0) or 4 (modes 1, 2) consecutive elements of a row per step with
+// 16-byte loads; every conversion rounds to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
+}
+
 __global__ __launch_bounds__(256) void prepare_maps_kernel(const void* __restrict__ in, uint16_t* __restrict__ out,
                                                            int64_t rows, int32_t f_in, int32_t mode) {
-  const int64_t total = rows * f_in;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    if (mode == 0) {
-      out[i] = f32_to_f16_bits(bf16_to_f32(static_cast<const uint16_t*>(in)[i]));
-    } else {
-      const float x = static_cast<const float*>(in)[i];
-      const int64_t r = i / f_in, f = i % f_in;
-      uint16_t hi, lo;
-      if (mode == 1) {
-        hi = f32_to_bf16_rne(x);
-        lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
-      } else {
-        hi = f32_to_f16_bits(x);
-        lo = f32_to_f16_bits(x - static_cast<float>(__builtin_bit_cast(_Float16, hi)));
-      }
-      out[r * 2 * f_in + f] = hi;
-      out[r * 2 * f_in + f_in + f] = lo;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (mode == 0) {
+    const int64_t n8 = rows * f_in / 8;
+    const u32x4* src = static_cast<const u32x4*>(in);
+    u32x4* dst = reinterpret_cast<u32x4*>(out);
+    for (int64_t i = t0; i < n8; i += stride) {
+      const u32x4 v = src[i];
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_f16x2(bf16lo(v[e]), bf16hi(v[e]));
+      dst[i] = o;
     }
+    return;
+  }
+  const int32_t q = f_in / 4;  // 4-element groups per row
+  const int64_t n4 = rows * q;
+  for (int64_t i = t0; i < n4; i += stride) {
+    const int64_t r = i / q, f = (i % q) * 4;
+    const float4 x = static_cast<const float4*>(in)[i];
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (mode == 1) {
+        hi[e] = pack_bf16(xs[2 * e], xs[2 * e + 1]);
+        lo[e] = pack_bf16(xs[2 * e] - bf16lo(hi[e]), xs[2 * e + 1] - bf16hi(hi[e]));
+      } else {
+        hi[e] = pack_f16x2(xs[2 * e], xs[2 * e + 1]);
+        const float h0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] & 0xffffu)));
+        const float h1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] >> 16)));
+        lo[e] = pack_f16x2(xs[2 * e] - h0, xs[2 * e + 1] - h1);
+      }
+    }
+    *reinterpret_cast<u32x2*>(out + r * 2 * f_in + f) = u32x2{hi[0], hi[1]};
+    *reinterpret_cast<u32x2*>(out + r * 2 * f_in + f_in + f) = u32x2{lo[0], lo[1]};
   }
 }
 
 int launch_prepare_maps(const void* in, uint16_t* out, int64_t rows, int32_t f_in, int32_t mode, hipStream_t s) {
   const int64_t total = rows * f_in;
   if (total <= 0) return KVX_OK;
-  int64_t blocks = ceil_div(total, 256);
-  if (blocks > 32768) blocks = 32768;
+  if (f_in % 8 != 0) return KVX_ERR_UNSUPPORTED;
+  int64_t blocks = ceil_div(total / (mode == 0 ? 8 : 4), 256);
+  if (blocks > 16384) blocks = 16384;
   prepare_maps_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, rows, f_in, mode);
   KVX_LAUNCH_CHECK();
   return KVX_OK;

@@ -299,6 +299,49 @@ def test_cfg4_flat_rope_full_sampled_rows():
     check_flat(c, rows)
 
 
+class F32Maps:
+    """fp32 maps [L][F_out][F_in] (host), handed to the oracle one layer at a
+    time as fp64."""
+
+    def __init__(self, a):
+        self.a = a
+
+    def __getitem__(self, l):
+        return self.a[l].astype(np.float64)
+
+
+def test_flat_fp32_maps_all_elements():
+    """Flattened translation with fp32 maps (the fitted-map path): the kernel
+    splits each map into a 16-bit high and low half (fp16 for the
+    rotated-back keys, bf16 for the values) and doubles the K extent."""
+    say("flattened + RoPE with fp32 maps, 400 receiver tokens")
+    cfg = synth.CONFIGS[4]
+    send_end, recv_end = synth.token_ends(400, 61)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(send_end, recv_end)
+    tm = dev_i32(tmap_o)
+    caches, maps, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, 6100 + r, DEV, outlier_frac=0.01, outlier_scale=20.0,
+                                          outlier_pairs=(role == "k"))
+        wt, _, _, b = synth.flat_maps(32, 3072, 1024, 6200 + r, DEV, 16)
+        maps[role], bias[role] = wt, b
+    k, v = kvx.translate(caches["k"], caches["v"], tm, taps, maps["k"], maps["v"], bias["k"], bias["v"],
+                         send_rope_base=cfg["send_rope"], recv_rope_base=cfg["recv_rope"])
+    torch.cuda.synchronize()
+    rows = np.arange(tmap_o.size)
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], tmap_o, taps, F32Maps(host(maps[role]).numpy()),
+                                host(bias[role]).numpy().astype(np.float64), rows, per_head=False, recv_heads=8,
+                                recv_head_dim=128, send_rope_base=cfg["send_rope"] if rk else 0.0,
+                                recv_rope_base=cfg["recv_rope"] if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  fp32 maps {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+
+
 def test_translate_deterministic_and_identity_maps():
     say("determinism + identity maps")
     c = flat_case(3, 520, seed=23)
