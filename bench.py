@@ -12,9 +12,9 @@ synthetic tensors resident in HBM before timing.
 
 Prints one JSON line.  ``value`` = receiver tokens translated per second
 (all layers, K+V).  ``roofline`` reports the dominant kernel (the grouped
-GEMM with its fused epilogue, launched once per operand type: fp16 for the
-rotated-back keys, bf16 for the values) against the bf16/fp16 dense
-matrix-core peak, timed with HIP events on the launch stream inside each
+GEMM with its fused epilogue, one launch per step covering both roles: fp16
+operands for the rotated-back keys, bf16 for the values) against the
+bf16/fp16 dense matrix-core peak, timed with HIP events on the launch stream inside each
 timed step.  ``traffic`` is the HBM bytes per launch read from the committed
 rocprofv3 counter summary when the kernel sources still match it, else null.
 ``cpu_baseline`` times the CPU oracle on a bounded row sample of the same
@@ -304,15 +304,15 @@ def main():
     U = int(1 + np.count_nonzero(np.diff(m)))
     gemm_ms = float(np.mean([s[1] for s in stages]))
     prep_ms = float(np.mean([s[0] for s in stages]))
-    # one launch per role (K: fp16 operands, V: bf16); algorithmic work of a
-    # launch: U distinct sender rows x 3072 features x 1024 outputs x 32 layers
-    launches = 2
+    # one launch per step covers both roles; its algorithmic work: U distinct
+    # sender rows x 3072 features x 1024 outputs x 32 layers x 2 roles
+    launches = 1
     launch_ms = gemm_ms / launches
-    flops = 2.0 * U * 3072 * 1024 * 32
+    flops = 2.0 * U * 3072 * 1024 * 32 * 2
     achieved = flops / (launch_ms * 1e-3) / 1e12
     # algorithmic bytes of a launch: unique sender rows of the 3 taps, maps,
-    # bias, and every receiver row written once
-    bytes_alg = 32 * (3 * U * 2048 + 3072 * 1024 * 2 + 1024 * 4 + N_R * 2048)
+    # bias, and every receiver row written once, both roles
+    bytes_alg = 2 * 32 * (3 * U * 2048 + 3072 * 1024 * 2 + 1024 * 4 + N_R * 2048)
     res = {
         "metric": "translated KV tokens/sec (all layers, K+V) at 32k ctx; % of MFMA/HBM roofline",
         "value": N_R / (ms_step * 1e-3),

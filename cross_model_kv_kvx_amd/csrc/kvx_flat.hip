@@ -200,8 +200,7 @@ __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p
 }
 #undef FT_STEP
 
-// F16: operand type of every role of this launch (fp16 or bf16).
-template <bool F16>
+// Both operand types in one launch: the K loop is chosen per tile.
 __global__ __attribute__((amdgpu_flat_work_group_size(FT_THREADS, FT_THREADS), amdgpu_waves_per_eu(2, 2))) void
 flat_gemm_kernel(const FlatKArgs args) {
   __shared__ __attribute__((aligned(1024))) uint16_t p0[FT_PART_ELEMS];
@@ -275,7 +274,10 @@ flat_gemm_kernel(const FlatKArgs args) {
     ft_issue_a(ta, 0, p0);
     ft_issue_b(ta, 0, p1);
     ft_issue_a(ta, 1, p2);
-    ft_kloop<F16>(ta, nk, p0, p1, p2, p3, p4, acc);
+    if (args.a_f16[role])
+      ft_kloop<true>(ta, nk, p0, p1, p2, p3, p4, acc);
+    else
+      ft_kloop<false>(ta, nk, p0, p1, p2, p3, p4, acc);
 
     // ------------------------------------------------------------ epilogue
     // Each wave owns 64 unique rows x one 128-wide head, written in two
@@ -475,29 +477,18 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
       a.taps[l][t / 4] |= static_cast<uint32_t>(p.taps[l * p.n_taps + t] & 0xff) << (8 * (t % 4));
   int G = device_cu_count();
   G = G >= 8 ? (G / 8) * 8 : 8;
-  // one launch per operand type (fp16 for rotated-back keys, bf16 otherwise)
-  for (int f16 = 1; f16 >= 0; --f16) {
-    FlatKArgs b = a;
-    b.n_roles = 0;
-    for (int j = 0; j < n_roles; ++j) {
-      if (roles[j].a_f16 != f16) continue;
-      const int k = b.n_roles++;
-      b.a_src[k] = static_cast<const uint16_t*>(roles[j].a_src);
-      b.a_layer_stride[k] = roles[j].a_layer_stride;
-      b.a_compact[k] = roles[j].a_compact;
-      b.a_f16[k] = roles[j].a_f16;
-      b.wt[k] = static_cast<const uint16_t*>(roles[j].wt);
-      b.bias[k] = roles[j].bias;
-      b.out[k] = roles[j].out;
-      b.rotate[k] = roles[j].rotate;
-    }
-    if (b.n_roles == 0) continue;
-    if (f16)
-      flat_gemm_kernel<true><<<G, FT_THREADS, 0, s>>>(b);
-    else
-      flat_gemm_kernel<false><<<G, FT_THREADS, 0, s>>>(b);
-    KVX_LAUNCH_CHECK();
+  for (int j = 0; j < n_roles; ++j) {
+    a.a_src[j] = static_cast<const uint16_t*>(roles[j].a_src);
+    a.a_layer_stride[j] = roles[j].a_layer_stride;
+    a.a_compact[j] = roles[j].a_compact;
+    a.a_f16[j] = roles[j].a_f16;
+    a.wt[j] = static_cast<const uint16_t*>(roles[j].wt);
+    a.bias[j] = roles[j].bias;
+    a.out[j] = roles[j].out;
+    a.rotate[j] = roles[j].rotate;
   }
+  flat_gemm_kernel<<<G, FT_THREADS, 0, s>>>(a);
+  KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
 
