@@ -248,6 +248,79 @@ def perhead_measure(dev, steps=10):
                          "kernel": "perhead_kernel", "launch_ms": t * 1e3, "algorithmic_bytes_per_launch": bytes_alg}}
 
 
+def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8):
+    """A flattened setting other than the headline one: translation of all
+    32 receiver layers, K and V, from 36 sender layers with three taps."""
+    send_end, recv_end = synth.token_ends(n_recv, seed)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    x = {}
+    for r, role in enumerate(("k", "v")):
+        x[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, dev, outlier_frac=0.01 if rope else 0.0,
+                                               outlier_scale=20.0 if rope else 1.0, outlier_pairs=(rope and role == "k"))
+        wt, u, v, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, dev, 16)
+        x[f"wt_{role}"] = wt if fp32_maps else kvx.fold_lowrank(wt, u, v, torch.bfloat16)
+        x[f"b_{role}"] = b
+        del u, v
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap = kvx.align_tokens(torch.as_tensor(send_end, device=dev), torch.as_tensor(recv_end, device=dev))
+    m = tmap.cpu().numpy()
+    U = int(1 + np.count_nonzero(np.diff(m)))
+    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
+    outs = {"k_recv": torch.empty((32, n_recv, 8, 128), dtype=torch.bfloat16, device=dev)}
+    outs["v_recv"] = torch.empty_like(outs["k_recv"])
+    ms, gm = [], []
+    for i in range(steps + 2):
+        st = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kvx.translate(x["k_send"], x["v_send"], tmap, taps, x["wt_k"], x["wt_v"], x["b_k"], x["b_v"], stage_ms=st,
+                      **kw, **outs)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append((time.perf_counter() - t0) * 1e3)
+            gm.append(st[1])
+    t_gemm = float(np.mean(gm))
+    flops = 2.0 * U * 3072 * 1024 * 32 * 2  # algorithmic (fp32 maps execute twice: high and low halves)
+    return {"workload": f"flattened{' + RoPE' if rope else ''}, {n_recv} receiver tokens, "
+                        f"{'fp32' if fp32_maps else 'bf16'} maps", "distinct_sender_rows": U,
+            "tokens_per_s": n_recv / (float(np.mean(ms)) * 1e-3), "translate_ms": float(np.mean(ms)),
+            "roofline": {"bound": "mfma", "achieved": flops / (t_gemm * 1e-3) / 1e12, "peak": PEAK_MFMA_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / (t_gemm * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                         "kernel": "flat_gemm_kernel", "launch_ms": t_gemm, "flops_per_launch": flops,
+                         "executed_flops_per_launch": flops * (2 if fp32_maps else 1), "traffic": None}}
+
+
+def fit_measure(dev, reps=3):
+    """Closed-form ridge fit of one (layer, role) of the calibration setting:
+    65536 rows of 3072 gathered features -> 1024 outputs, lambda = 1e-3 tr/3072."""
+    n, layer = 65536, 20
+    send_end, recv_end = synth.token_ends(n, 5)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    k_send = synth.sender_cache(shp, 500, dev)
+    y = synth.receiver_cache(synth.CacheShape(1, n, 8, 128), 550, dev)[0].reshape(n, 1024)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tm = kvx.align_tokens(torch.as_tensor(send_end, device=dev), torch.as_tensor(recv_end, device=dev))
+    x = kvx.gather_features(k_send, tm, taps[layer])
+    del k_send
+    ws = torch.empty(kvx.lib().kvx_fit_ridge_workspace_size(3072, 1024), dtype=torch.uint8, device=dev)
+    ms = []
+    for i in range(reps + 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kvx.fit_ridge(x, y, lambda_rel=1e-3, workspace=ws)   # synchronous (reads the SPD flag)
+        if i >= 1:
+            ms.append((time.perf_counter() - t0) * 1e3)
+    t = float(np.mean(ms))
+    gram = 2.0 * n * (3072 * 3073 / 2 + 3072 * 1024)      # G (one triangle) and X^T Y
+    solve = 3072.0 ** 3 / 3 + 2 * 3072.0 ** 2 * 1024      # Cholesky + two triangular solves (fp64)
+    return {"workload": "ridge fit, one layer and role: 65536 x 3072 bf16 features -> 1024 outputs, "
+                        "lambda = 1e-3 tr(G)/3072", "fit_ms": t, "problems_per_full_fit": 64,
+            "gram_flops": gram, "solve_flops_fp64": solve,
+            "roofline": {"bound": "mfma", "achieved": gram / (t * 1e-3) / 1e12, "peak": PEAK_MFMA_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": gram / (t * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                         "note": "Gram FLOPs over the whole fit time (Gram + fp64 solve)", "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,12 +408,21 @@ def main():
                      "kernel": "flat_gemm_kernel", "launches_per_step": launches, "launch_ms": launch_ms,
                      "flops_per_launch": flops, "algorithmic_bytes_per_launch": bytes_alg, "prep_ms": prep_ms},
     }
-    if not args.no_also:
-        log("bench: per-head workload")
-        res["also"] = perhead_measure(dev)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(x)
+    if not args.no_also:
+        log("bench: per-head workload")
+        res["also"] = perhead_measure(dev)
+        del x, outs, ws
+        torch.cuda.empty_cache()
+        log("bench: flattened, 8192 tokens, no RoPE")
+        res["also_cfg3"] = flat_setting_measure(dev, 8192, 3, rope=False, fp32_maps=False)
+        log("bench: flattened with fp32 maps, 16384 tokens")
+        res["also_fp32_maps"] = flat_setting_measure(dev, 16384, 6, rope=False, fp32_maps=True)
+        torch.cuda.empty_cache()
+        log("bench: ridge fit")
+        res["also_fit"] = fit_measure(dev)
     print(json.dumps(res), flush=True)
 
 

@@ -249,119 +249,74 @@ __global__ __launch_bounds__(256) void lambda_kernel(double* __restrict__ G, int
 
 // ---------------------------------------------------------------- fp64 Cholesky pieces
 
-// Factor the diagonal block [k0, k0+nb) in LDS (lower), flag non-positive pivots.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int32_t n, int32_t k0, int32_t nb,
-                                                         int32_t* __restrict__ flag) {
+// Factor the diagonal block [k0, k0+nb) (lower), flag non-positive pivots,
+// and write the inverse of the factor (lower, nb x nb, zero above the
+// diagonal, row stride CH_NB) to `linv`: the panel and the block triangular
+// solves then become products with it.  One wave, no barrier: lane i keeps
+// row i in registers; at column j every lane takes the pivot from lane j
+// (the square root is recomputed per lane), lane i scales its entry and
+// publishes it in LDS, and each lane updates its row with the published
+// column (LDS operations of one wave execute in order).  Rows past nb are
+// the identity.  The inverse is formed one column per lane by forward
+// substitution against the factor in LDS.
+__global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, int32_t n, int32_t k0, int32_t nb,
+                                                        int32_t* __restrict__ flag, double* __restrict__ linv) {
   __shared__ double L[CH_NB][CH_NB + 1];
-  for (int e = threadIdx.x; e < nb * nb; e += 256) {
-    const int i = e / nb, j = e % nb;
-    L[i][j] = A[static_cast<int64_t>(k0 + i) * n + k0 + j];
-  }
-  __syncthreads();
-  for (int j = 0; j < nb; ++j) {
-    if (threadIdx.x == 0) {
-      double d = L[j][j];
-      if (!(d > 0.0)) {
-        *flag = 1;
-        d = 1.0;
-      }
-      L[j][j] = sqrt(d);
-    }
-    __syncthreads();
-    const double piv = L[j][j];
-    for (int i = j + 1 + threadIdx.x; i < nb; i += 256) L[i][j] /= piv;
-    __syncthreads();
-    const int m = nb - j - 1;
-    for (int e = threadIdx.x; e < m * m; e += 256) {
-      const int i = j + 1 + e / m, c = j + 1 + e % m;
-      if (c <= i) L[i][c] -= L[i][j] * L[c][j];
-    }
-    __syncthreads();
-  }
-  for (int e = threadIdx.x; e < nb * nb; e += 256) {
-    const int i = e / nb, j = e % nb;
-    if (j <= i) A[static_cast<int64_t>(k0 + i) * n + k0 + j] = L[i][j];
-  }
-}
-
-// Panel: rows r >= k0+nb, A[r][k0..k0+nb) <- A[r][k0..] L_kk^-T.  One thread per row.
-__global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ A, int32_t n, int32_t k0, int32_t nb) {
-  __shared__ double L[CH_NB][CH_NB + 1];
-  for (int e = threadIdx.x; e < nb * nb; e += 64) {
-    const int i = e / nb, j = e % nb;
-    L[i][j] = (j <= i) ? A[static_cast<int64_t>(k0 + i) * n + k0 + j] : 0.0;
-  }
-  __syncthreads();
-  const int32_t r = k0 + nb + blockIdx.x * 64 + threadIdx.x;
-  if (r >= n) return;
-  double x[CH_NB];
-  double* row = A + static_cast<int64_t>(r) * n + k0;
-#pragma unroll
-  for (int c = 0; c < CH_NB; ++c) x[c] = (c < nb) ? row[c] : 0.0;
-#pragma unroll
-  for (int c = 0; c < CH_NB; ++c) {
-    if (c < nb) {
-      double s = x[c];
-#pragma unroll
-      for (int t = 0; t < c; ++t) s -= x[t] * L[c][t];
-      x[c] = s / L[c][c];
-    }
-  }
+  __shared__ double col[CH_NB];
+  const int i = threadIdx.x;
+  double row[CH_NB];
 #pragma unroll
   for (int c = 0; c < CH_NB; ++c)
-    if (c < nb) row[c] = x[c];
-}
-
-// Left solves on a block of right-hand sides: Z = L_kk^-1 Z (forward) or
-// Z = L_kk^-T Z (backward).  One thread per column.
-template <bool TRANS>
-__global__ __launch_bounds__(256) void trsm_left_kernel(const double* __restrict__ A, int32_t n, int32_t k0,
-                                                        int32_t nb, double* __restrict__ Z, int32_t ldz, int32_t ncols) {
-  __shared__ double L[CH_NB][CH_NB + 1];
-  for (int e = threadIdx.x; e < nb * nb; e += 256) {
-    const int i = e / nb, j = e % nb;
-    L[i][j] = (j <= i) ? A[static_cast<int64_t>(k0 + i) * n + k0 + j] : 0.0;
+    row[c] = (i < nb && c < nb) ? A[static_cast<int64_t>(k0 + i) * n + k0 + c] : (i == c ? 1.0 : 0.0);
+  int bad = 0;
+#pragma unroll
+  for (int j = 0; j < CH_NB; ++j) {
+    // pivot of column j, from lane j
+    const double d = __shfl(row[j], j, 64);
+    const bool ok = d > 0.0;
+    if (j < nb && !ok) bad = 1;
+    const double piv = sqrt(ok ? d : 1.0);
+    const double rp = 1.0 / piv;
+    if (i == j) row[j] = piv;
+    if (i > j) row[j] *= rp;
+    col[i] = row[j];
+    KVX_COMPILER_FENCE();
+#pragma unroll
+    for (int c = j + 1; c < CH_NB; ++c) {
+      const double lc = col[c];
+      if (i >= c) row[c] -= row[j] * lc;
+    }
+    KVX_COMPILER_FENCE();
   }
-  __syncthreads();
-  const int32_t c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= ncols) return;
-  double z[CH_NB];
+  if (bad && i == 0) *flag = 1;
 #pragma unroll
-  for (int i = 0; i < CH_NB; ++i) z[i] = (i < nb) ? Z[static_cast<int64_t>(k0 + i) * ldz + c] : 0.0;
-  if (!TRANS) {
+  for (int c = 0; c < CH_NB; ++c) L[i][c] = (c <= i) ? row[c] : 0.0;
+  KVX_COMPILER_FENCE();
+  // inverse: lane c forms column c
+  double x[CH_NB];
+  const int c = i;
 #pragma unroll
-    for (int i = 0; i < CH_NB; ++i) {
-      if (i < nb) {
-        double s = z[i];
+  for (int r = 0; r < CH_NB; ++r) {
+    double v = (r == c) ? 1.0 : 0.0;
 #pragma unroll
-        for (int t = 0; t < i; ++t) s -= L[i][t] * z[t];
-        z[i] = s / L[i][i];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = CH_NB - 1; i >= 0; --i) {
-      if (i < nb) {
-        double s = z[i];
-#pragma unroll
-        for (int t = i + 1; t < CH_NB; ++t)
-          if (t < nb) s -= L[t][i] * z[t];
-        z[i] = s / L[i][i];
-      }
-    }
+    for (int q = 0; q < r; ++q) v -= L[r][q] * x[q];
+    x[r] = (r >= c) ? v / L[r][r] : 0.0;
   }
 #pragma unroll
-  for (int i = 0; i < CH_NB; ++i)
-    if (i < nb) Z[static_cast<int64_t>(k0 + i) * ldz + c] = z[i];
+  for (int r = 0; r < CH_NB; ++r) {
+    if (i < nb && r < nb && r >= i) A[static_cast<int64_t>(k0 + r) * n + k0 + i] = L[r][i];
+    linv[r * CH_NB + c] = (r < nb && c < nb) ? x[r] : 0.0;
+  }
 }
 
-// C[M x N] -= A * B with A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].
-// 64 x 64 tiles, 16 x 16 threads with 4 x 4 outputs each.  lower_only skips
-// tiles strictly above the diagonal (tile row < tile column).
-__global__ __launch_bounds__(256) void gemm64_kernel(int32_t M, int32_t N, int32_t K, const double* __restrict__ A,
-                                                     int64_t sam, int64_t sak, const double* __restrict__ B,
-                                                     int64_t sbk, int64_t sbn, double* __restrict__ C, int64_t ldc,
-                                                     int32_t lower_only) {
+// C[M x N] -= A * B (overwrite = 0) or C = A * B (overwrite = 1), with
+// A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].  64 x 64 tiles, 16 x 16
+// threads with 4 x 4 outputs each; a workgroup reads all of its A rows and B
+// columns before it writes its tile, so C may alias A when N <= 64 or B when
+// M <= 64.  lower_only skips tiles strictly above the diagonal.
+__global__ __launch_bounds__(256) void gemm64_kernel(int32_t M, int32_t N, int32_t K, const double* A, int64_t sam,
+                                                     int64_t sak, const double* B, int64_t sbk, int64_t sbn, double* C,
+                                                     int64_t ldc, int32_t lower_only, int32_t overwrite) {
   const int32_t bm = blockIdx.y, bn = blockIdx.x;
   if (lower_only && bm < bn) return;
   __shared__ double As[16][65];
@@ -397,7 +352,12 @@ __global__ __launch_bounds__(256) void gemm64_kernel(int32_t M, int32_t N, int32
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int32_t m = m0 + ty + 16 * i, nn = n0 + tx + 16 * j;
-      if (m < M && nn < N) C[m * ldc + nn] -= acc[i][j];
+      if (m < M && nn < N) {
+        if (overwrite)
+          C[m * ldc + nn] = acc[i][j];
+        else
+          C[m * ldc + nn] -= acc[i][j];
+      }
     }
 }
 
@@ -432,6 +392,7 @@ size_t fit_ws_bytes(int32_t f_in, int32_t f_out) {
   c.take<double>(4);
   c.take<int32_t>(64);
   c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  c.take<double>(static_cast<size_t>(ceil_div(f_in, CH_NB)) * CH_NB * CH_NB);
   return c.used + 256;
 }
 
@@ -452,6 +413,8 @@ int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t i
   double* lam = cv.take<double>(4);
   int32_t* flag = cv.take<int32_t>(64);
   float* part = cv.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
+  double* linv = cv.take<double>(static_cast<size_t>(nb_total) * CH_NB * CH_NB);  // inverse diagonal factors
   if (int st = launch_fill_i32(flag, 1, 0, s)) return st;
 
   // 1. Gram and cross products
@@ -506,39 +469,44 @@ int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t i
   lambda_kernel<<<1, 256, 0, s>>>(G, f_in, lam_abs, lam_rel, lam);
   KVX_LAUNCH_CHECK();
 
-  // 3. Cholesky and the two block triangular solves
-  const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
+  // 3. Cholesky and the two block triangular solves; the diagonal kernel
+  // leaves the inverse factor of its block, so each panel and each block
+  // solve is an in-place product with it.
   for (int32_t kb = 0; kb < nb_total; ++kb) {
     const int32_t k0 = kb * CH_NB;
     const int32_t nb = min(CH_NB, f_in - k0);
-    potrf_diag_kernel<<<1, 256, 0, s>>>(G, f_in, k0, nb, flag);
+    double* li = linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+    potrf_diag_kernel<<<1, 64, 0, s>>>(G, f_in, k0, nb, flag, li);
     KVX_LAUNCH_CHECK();
     const int32_t rest = f_in - k0 - nb;
     if (rest > 0) {
-      trsm_panel_kernel<<<static_cast<unsigned>(ceil_div(rest, 64)), 64, 0, s>>>(G, f_in, k0, nb);
+      const int32_t t = static_cast<int32_t>(ceil_div(rest, 64));
+      // panel: P = P L_kk^-T (in place, one 64-column tile)
+      double* P = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
+      gemm64_kernel<<<dim3(1, t), 256, 0, s>>>(rest, nb, nb, P, f_in, 1, li, 1, CH_NB, P, f_in, 0, 1);
       KVX_LAUNCH_CHECK();
       // trailing lower update: G[r][c] -= P[r] . P[c] for r, c >= k0+nb
-      const int32_t t = static_cast<int32_t>(ceil_div(rest, 64));
-      const double* P = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
       double* Ct = G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
-      gemm64_kernel<<<dim3(t, t), 256, 0, s>>>(rest, rest, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, 1);
+      gemm64_kernel<<<dim3(t, t), 256, 0, s>>>(rest, rest, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, 1, 0);
       KVX_LAUNCH_CHECK();
     }
   }
+  const unsigned col_tiles = static_cast<unsigned>(ceil_div(f_out, 64));
   // forward: L Z = C
-  const unsigned col_blocks = static_cast<unsigned>(ceil_div(f_out, 256));
   for (int32_t kb = 0; kb < nb_total; ++kb) {
     const int32_t k0 = kb * CH_NB;
     const int32_t nb = min(CH_NB, f_in - k0);
-    trsm_left_kernel<false><<<col_blocks, 256, 0, s>>>(G, f_in, k0, nb, C, f_out, f_out);
+    const double* li = linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+    double* Zk = C + static_cast<int64_t>(k0) * f_out;
+    // Z_k = L_kk^-1 Z_k (in place, one 64-row tile)
+    gemm64_kernel<<<dim3(col_tiles, 1), 256, 0, s>>>(nb, f_out, nb, li, CH_NB, 1, Zk, f_out, 1, Zk, f_out, 0, 1);
     KVX_LAUNCH_CHECK();
     const int32_t rest = f_in - k0 - nb;
     if (rest > 0) {
       const double* Lb = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
-      const double* Zk = C + static_cast<int64_t>(k0) * f_out;
       double* Cr = C + static_cast<int64_t>(k0 + nb) * f_out;
-      gemm64_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 64)), static_cast<unsigned>(ceil_div(rest, 64))), 256, 0,
-                      s>>>(rest, f_out, nb, Lb, f_in, 1, Zk, f_out, 1, Cr, f_out, 0);
+      gemm64_kernel<<<dim3(col_tiles, static_cast<unsigned>(ceil_div(rest, 64))), 256, 0, s>>>(
+          rest, f_out, nb, Lb, f_in, 1, Zk, f_out, 1, Cr, f_out, 0, 0);
       KVX_LAUNCH_CHECK();
     }
   }
@@ -546,14 +514,16 @@ int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t i
   for (int32_t kb = nb_total - 1; kb >= 0; --kb) {
     const int32_t k0 = kb * CH_NB;
     const int32_t nb = min(CH_NB, f_in - k0);
-    trsm_left_kernel<true><<<col_blocks, 256, 0, s>>>(G, f_in, k0, nb, C, f_out, f_out);
+    const double* li = linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+    double* Wk = C + static_cast<int64_t>(k0) * f_out;
+    // W_k = L_kk^-T W_k (in place)
+    gemm64_kernel<<<dim3(col_tiles, 1), 256, 0, s>>>(nb, f_out, nb, li, 1, CH_NB, Wk, f_out, 1, Wk, f_out, 0, 1);
     KVX_LAUNCH_CHECK();
     if (k0 > 0) {
       // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_k
       const double* Lr = G + static_cast<int64_t>(k0) * f_in;
-      const double* Wk = C + static_cast<int64_t>(k0) * f_out;
-      gemm64_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 64)), static_cast<unsigned>(ceil_div(k0, 64))), 256, 0,
-                      s>>>(k0, f_out, nb, Lr, 1, f_in, Wk, f_out, 1, C, f_out, 0);
+      gemm64_kernel<<<dim3(col_tiles, static_cast<unsigned>(ceil_div(k0, 64))), 256, 0, s>>>(
+          k0, f_out, nb, Lr, 1, f_in, Wk, f_out, 1, C, f_out, 0, 0);
       KVX_LAUNCH_CHECK();
     }
   }
