@@ -19,7 +19,10 @@ timed step.  ``traffic`` is the HBM bytes per launch read from the committed
 rocprofv3 counter summary when the kernel sources still match it, else null.
 ``cpu_baseline`` times the CPU oracle on a bounded row sample of the same
 workload.  ``also`` reports the per-head workload (32 -> 80 layers, 4096
-tokens, fp32 128 x 128 maps) against the HBM peak.
+tokens, fp32 128 x 128 maps) against the HBM peak, ``also_perhead_rope`` the
+same with keys stored rotated on both sides; ``also_cfg3``,
+``also_fp32_maps`` and ``also_fit`` other flattened settings and the ridge
+fit.
 
 Profiling helpers: ``--calibration-copy`` first runs a plain 1 GiB device
 copy (1 GiB read + 1 GiB written) so a rocprofv3 counter run of the same
@@ -218,9 +221,11 @@ def cpu_baseline(x, target_s=15.0):
                       f"{n_recv} rows"}
 
 
-def perhead_measure(dev, steps=10):
+def perhead_measure(dev, steps=10, rope=False):
     """Per-head workload: sender 32 layers, receiver 80, 4096 tokens,
-    8 x 128 heads, fp32 128 x 128 maps, identity token map."""
+    8 x 128 heads, fp32 128 x 128 maps, identity token map.  With ``rope``
+    the keys are stored rotated on both sides (bases 5e5 and 1e6): the
+    preparation rotates the sender keys back into fp16 rows first."""
     shp = synth.CacheShape(32, 4096, 8, 128)
     x = {}
     for r, role in enumerate(("k", "v")):
@@ -230,19 +235,22 @@ def perhead_measure(dev, steps=10):
     ident = torch.arange(4096, dtype=torch.int32, device=dev)
     k = torch.empty((80, 4096, 8, 128), dtype=torch.bfloat16, device=dev)
     v = torch.empty_like(k)
-    ms = []
+    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
+    ms, prep = [], []
     for i in range(steps + 2):
         st = []
         kvx.translate(x["k_send"], x["v_send"], ident, taps, x["wt_k"], x["wt_v"], x["b_k"], x["b_v"],
-                      per_head=True, k_recv=k, v_recv=v, stage_ms=st)
+                      per_head=True, k_recv=k, v_recv=v, stage_ms=st, **kw)
         if i >= 2:
+            prep.append(st[0])
             ms.append(st[1])
     t = float(np.mean(ms)) * 1e-3
     # algorithmic bytes: each sender row read once, each receiver row written
     # once, maps (fp32) and bias read once
     bytes_alg = 2 * (32 * 4096 * 1024 * 2 + 80 * 4096 * 1024 * 2 + 80 * 8 * 128 * 128 * 4 + 80 * 1024 * 4)
-    return {"workload": "per-head 32->80 layers, 4096 tokens, 8x128 heads, fp32 maps, bf16 caches",
-            "tokens_per_s": 4096 / t, "kernel_ms": t * 1e3,
+    return {"workload": "per-head 32->80 layers, 4096 tokens, 8x128 heads, fp32 maps, bf16 caches"
+                        + (", keys rotated (RoPE 5e5 -> 1e6)" if rope else ""),
+            "tokens_per_s": 4096 / t, "kernel_ms": t * 1e3, "prep_ms": float(np.mean(prep)),
             "roofline": {"bound": "hbm", "achieved": bytes_alg / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": bytes_alg / t / 1e9 / PEAK_HBM_GBS, "traffic": committed_traffic("perhead_kernel"),
                          "kernel": "perhead_kernel", "launch_ms": t * 1e3, "algorithmic_bytes_per_launch": bytes_alg}}
@@ -414,6 +422,8 @@ def main():
     if not args.no_also:
         log("bench: per-head workload")
         res["also"] = perhead_measure(dev)
+        log("bench: per-head workload, rotated keys")
+        res["also_perhead_rope"] = perhead_measure(dev, rope=True)
         del x, outs, ws
         torch.cuda.empty_cache()
         log("bench: flattened, 8192 tokens, no RoPE")

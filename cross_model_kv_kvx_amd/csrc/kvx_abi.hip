@@ -58,7 +58,9 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
   const bool f32 = send->dtype == KVX_F32;
   const bool srope = send->rope_base > 0.0 && key_role;
   const bool rrope = recv->rope_base > 0.0 && key_role;
-  if (!f32 && !per_head) {
+  // runs of equal sender tokens: the flattened path's row index, and the
+  // index of rotated-back key rows on both paths
+  if (!f32 && (!per_head || srope)) {
     w.runs.uniq = c.take<int32_t>(nr > 0 ? nr : 1);
     w.runs.run_begin = c.take<int32_t>(static_cast<size_t>(nr) + 1);
     w.runs.recv_to_uniq = c.take<int32_t>(nr > 0 ? nr : 1);
@@ -70,7 +72,7 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
   // epilogue reads the (cos, sin) step of its rotation recurrence from the
   // table row of position 8, also for caches of fewer tokens
   if (rrope) w.tab_recv = c.take<float2>(static_cast<size_t>(recv_tab_rows(nr)) * (recv->head_dim / 2));
-  if (!f32 && !per_head && srope) {
+  if (!f32 && srope) {
     // U <= N_R always (U <= N_S only for non-decreasing maps)
     w.rows_cap = nr;
     w.krows = c.take<uint16_t>(static_cast<size_t>(send->layers) * w.rows_cap * send->kv_heads * send->head_dim);
@@ -227,7 +229,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   // bf16 caches: matrix-core paths, head_dim 128
   if (send->head_dim != 128 || recv->head_dim != 128) return KVX_ERR_UNSUPPORTED;
   if (per_head) {
-    if (send->rope_base > 0.0 || recv->rope_base > 0.0) return KVX_ERR_UNSUPPORTED;
+    const int64_t row_elems = static_cast<int64_t>(send->kv_heads) * 128;
     HeadProblem p{};
     p.send_layers = send->layers;
     p.send_tokens = send->tokens;
@@ -237,12 +239,55 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     p.w_f32 = w_dtype == KVX_F32;
     p.taps = taps;
     p.recv_to_send = recv_to_send;
+    p.tab_recv = w.tab_recv;
     HeadRole roles[2];
     int n = 0;
-    if (do_k)
-      roles[n++] = HeadRole{static_cast<const uint16_t*>(k_send), wt_k, b_k, static_cast<uint16_t*>(k_recv)};
-    if (do_v)
-      roles[n++] = HeadRole{static_cast<const uint16_t*>(v_send), wt_v, b_v, static_cast<uint16_t*>(v_recv)};
+    if (do_k) {
+      HeadRole r{};
+      if (w.tab_send) {
+        // keys rotated back at their sender positions, one fp16 row per run
+        if (int st = launch_runs(recv_to_send, recv->tokens, send->tokens, w.runs, w.runs_scratch, s)) return st;
+        if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
+        uint8_t used[MAX_LAYERS] = {0};
+        for (int32_t i = 0; i < recv->layers; ++i) used[taps[i]] = 1;
+        if (int st = launch_derotate_rows(static_cast<const uint16_t*>(k_send), send->layers, send->tokens,
+                                          send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, w.krows, s))
+          return st;
+        r.x = w.krows;
+        r.x_layer_stride = static_cast<int64_t>(w.rows_cap) * row_elems;
+        r.x_rows = w.rows_cap;
+        r.row_of = w.runs.recv_to_uniq;
+        r.x_f16 = 1;
+      } else {
+        r.x = static_cast<const uint16_t*>(k_send);
+        r.x_layer_stride = static_cast<int64_t>(send->tokens) * row_elems;
+        r.x_rows = send->tokens;
+        r.row_of = recv_to_send;
+        r.x_f16 = 0;
+      }
+      if (w.tab_recv) {
+        if (int st = launch_rope_table(w.tab_recv, recv_tab_rows(recv->tokens), recv->head_dim, recv->rope_base, s))
+          return st;
+      }
+      r.rotate = w.tab_recv ? 1 : 0;
+      r.wt = wt_k;
+      r.bias = b_k;
+      r.out = static_cast<uint16_t*>(k_recv);
+      roles[n++] = r;
+    }
+    if (do_v) {
+      HeadRole r{};
+      r.x = static_cast<const uint16_t*>(v_send);
+      r.x_layer_stride = static_cast<int64_t>(send->tokens) * row_elems;
+      r.x_rows = send->tokens;
+      r.row_of = recv_to_send;
+      r.x_f16 = 0;
+      r.rotate = 0;
+      r.wt = wt_v;
+      r.bias = b_v;
+      r.out = static_cast<uint16_t*>(v_recv);
+      roles[n++] = r;
+    }
     return main_kernel([&] { return launch_perhead(p, roles, n, s); });
   }
 

@@ -80,6 +80,13 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
+// Two fp32 -> packed fp16 (hardware convert, round to nearest even).
+__device__ __forceinline__ uint32_t cvt_f16x2(float a, float b) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
+}
+
 // Wave index inside the workgroup as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

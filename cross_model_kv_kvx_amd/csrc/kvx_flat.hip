@@ -397,12 +397,6 @@ flat_gemm_kernel(const FlatKArgs args) {
 // out[l][o][f] = hi, out[l][o][F_in + f] = lo.  Each thread converts 8
 // (mode 0) or 4 (modes 1, 2) consecutive elements of a row per step with
 // 16-byte loads; every conversion rounds to nearest even.
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
-}
-
 __global__ __launch_bounds__(256) void prepare_maps_kernel(const void* __restrict__ in, uint16_t* __restrict__ out,
                                                            int64_t rows, int32_t f_in, int32_t mode) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -415,7 +409,7 @@ __global__ __launch_bounds__(256) void prepare_maps_kernel(const void* __restric
       const u32x4 v = src[i];
       u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_f16x2(bf16lo(v[e]), bf16hi(v[e]));
+      for (int e = 0; e < 4; ++e) o[e] = cvt_f16x2(bf16lo(v[e]), bf16hi(v[e]));
       dst[i] = o;
     }
     return;
@@ -433,10 +427,10 @@ __global__ __launch_bounds__(256) void prepare_maps_kernel(const void* __restric
         hi[e] = pack_bf16(xs[2 * e], xs[2 * e + 1]);
         lo[e] = pack_bf16(xs[2 * e] - bf16lo(hi[e]), xs[2 * e + 1] - bf16hi(hi[e]));
       } else {
-        hi[e] = pack_f16x2(xs[2 * e], xs[2 * e + 1]);
+        hi[e] = cvt_f16x2(xs[2 * e], xs[2 * e + 1]);
         const float h0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] & 0xffffu)));
         const float h1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] >> 16)));
-        lo[e] = pack_f16x2(xs[2 * e] - h0, xs[2 * e + 1] - h1);
+        lo[e] = cvt_f16x2(xs[2 * e] - h0, xs[2 * e + 1] - h1);
       }
     }
     *reinterpret_cast<u32x2*>(out + r * 2 * f_in + f) = u32x2{hi[0], hi[1]};

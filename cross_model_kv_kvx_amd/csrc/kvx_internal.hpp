@@ -73,12 +73,18 @@ struct HeadProblem {
   int32_t w_f32;
   const int32_t* taps;         // host [L_R][1]
   const int32_t* recv_to_send;
+  const float2* tab_recv;      // receiver RoPE table (rotated roles)
 };
 struct HeadRole {
-  const uint16_t* x;   // [L_S][N_S][H][128]
-  const void* wt;      // [L_R][H][128][128]
-  const float* bias;   // [L_R][H*128] or null
-  uint16_t* out;       // [L_R][N_R][H][128]
+  const uint16_t* x;       // sender rows: [L_S][N_S][H][128] bf16, or compact [L_S][rows][H][128] fp16
+  int64_t x_layer_stride;  // elements between sender layers of x
+  int32_t x_rows;          // rows of one sender layer of x
+  const int32_t* row_of;   // [N_R] row of x for each receiver token (the token map, or the run index)
+  int32_t x_f16;           // x holds fp16 rows rotated back at the sender position
+  int32_t rotate;          // rotate outputs at the receiver position
+  const void* wt;          // [L_R][H][128][128]
+  const float* bias;       // [L_R][H*128] or null
+  uint16_t* out;           // [L_R][N_R][H][128]
 };
 int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hipStream_t s);
 

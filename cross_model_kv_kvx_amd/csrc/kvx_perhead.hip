@@ -13,26 +13,34 @@
 namespace kvx {
 
 // ---------------------------------------------------------------- bf16 caches, d = 128
-// One workgroup per (role, receiver layer l, head h, span of up to 2048
+// One workgroup per (role, receiver layer l, head h, span of up to 4096
 // receiver tokens) with two kinds of waves:
-//   * compute waves 0..3, wave w owning outputs 32w .. 32w+31 of the head.
-//     The wave's 32 rows of W_{l,h} stay in registers for the whole span as
-//     MFMA A fragments (fp32 maps split once into bf16 high and low halves:
-//     y = x W_hi + x W_lo keeps fp32-level accuracy of the map while the bf16
-//     inputs stay exact).  The sender rows of 64-token tiles stream through a
-//     ring of six 16 KB LDS stages by direct global->LDS 16-byte loads (whole
-//     256-byte rows, 16-byte chunks XOR-swizzled by row so fragment reads of
-//     16 consecutive rows hit distinct banks); the span's token map is
-//     copied to LDS once at the start.  Each tile's 64 x 128 bf16 outputs
-//     are staged in one of two 16 KB LDS buffers;
+//   * compute waves 0..3.  Wave w owns the 32 outputs 16w .. 16w+15 and
+//     64+16w .. 64+16w+15 of the head, so the two members (c, c+64) of every
+//     rotary pair sit in one lane (accumulator elements r and r+8).  The
+//     wave's 32 rows of W_{l,h} stay in registers for the whole span as MFMA
+//     A fragments (fp32 maps split once into a high and a low 16-bit half:
+//     y = x W_hi + x W_lo keeps fp32-level accuracy of the map while the
+//     16-bit inputs stay exact).  Sender rows of 64-token tiles stream
+//     through a ring of six 16 KB LDS stages by direct global->LDS 16-byte
+//     loads (whole 256-byte rows, 16-byte chunks XOR-swizzled by row so
+//     fragment reads of 16 consecutive rows hit distinct banks); the span's
+//     row indices are copied to LDS once.  Keys of a rotated receiver are
+//     rotated at the receiver position before rounding, with a recurrence
+//     that steps each lane's (cos, sin) by 64 positions per tile from table
+//     values read once.  Each tile's 64 x 128 bf16 outputs are staged in one
+//     of two 16 KB LDS buffers;
 //   * store waves 4..7 write the staged tile one step later, 16 bytes per
 //     lane and four whole 256-byte rows per instruction.
-// The vector-memory counter is per wave: compute waves only load, so their
-// waits name exactly the tile they need, and store waves never wait, so no
-// load ever waits for stores to complete.  One barrier per tile orders the
-// stages and staging buffers between the two kinds.  Workgroups are numbered
-// receiver layer innermost and consecutive numbers go to one XCD, so the
-// receiver layers that share a sender layer read its rows through one L2.
+// Sender rows are bf16 cache rows (token map as row index), or, for keys
+// stored rotated, fp16 rows rotated back at the sender position (run index
+// as row index; the map is then split into fp16 halves).  The vector-memory
+// counter is per wave: compute waves only load and store waves never wait,
+// so no load ever waits for stores to complete.  One barrier per tile orders
+// the stages and staging buffers between the two kinds.  Workgroups are
+// numbered receiver layer innermost and consecutive numbers go to one XCD,
+// so the receiver layers that share a sender layer read its rows through one
+// L2.
 constexpr int PH_TILE = 64;                      // tokens per tile
 constexpr int PH_SPAN = 4096;                    // tokens per workgroup
 constexpr int PH_TILE_ELEMS = PH_TILE * 128;     // 16-bit elements of a tile (16 KB)
@@ -41,16 +49,23 @@ constexpr int PH_THREADS = 512;                  // 4 compute + 4 store waves
 
 struct HeadKArgs {
   const uint16_t* x[2];
+  int64_t x_layer_stride[2];
+  int32_t x_rows[2];
+  const int32_t* row_of[2];
+  int32_t rotate[2];
   const void* wt[2];
   const float* bias[2];
   uint16_t* out[2];
-  const int32_t* map;
-  int32_t send_tokens, recv_layers, recv_tokens, heads, n_span, n_blocks, xcd_remap;
+  const float2* tab_recv;
+  int32_t recv_layers, recv_tokens, heads, n_span, n_blocks, xcd_remap;
   uint8_t tap[MAX_LAYERS];  // sender layer of each receiver layer
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r.
 __device__ __forceinline__ int ph_chunk(int r, int c) { return c ^ (r & 15); }
+
+// Output of local row j (0..31) of compute wave w: pairs (16w + j, 64 + 16w + j).
+__device__ __forceinline__ int ph_out(int w, int j) { return j < 16 ? 16 * w + j : 48 + 16 * w + j; }
 
 struct PhTile {
   __amdgpu_buffer_rsrc_t xr;  // sender rows of layer s, head h
@@ -70,7 +85,7 @@ __device__ __forceinline__ void ph_issue(const PhTile& pt, int k, uint16_t* slot
   const int32_t r0 = k * PH_TILE + 16 * wave + q;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // tiles past the end (not multiplied) read an in-range map entry
+    // tiles past the end (not multiplied) read an in-range entry
     const int32_t sv = pt.msm[min(r0 + 4 * i, PH_SPAN - 1)];
     const int row = 16 * wave + 4 * i + q;
     const uint32_t voff = static_cast<uint32_t>(sv) * pt.row_bytes + 16u * ph_chunk(row, lane & 15);
@@ -78,11 +93,28 @@ __device__ __forceinline__ void ph_issue(const PhTile& pt, int k, uint16_t* slot
   }
 }
 
-// Fragments of one tile, MFMA D[n][tok] += W[n][k] X[tok][k]; stage outputs
-// (bias added, bf16 nearest even) into `ys` as [tok][n] with swizzled chunks.
-template <bool WF32>
+template <bool F16>
+__device__ __forceinline__ f32x16 ph_mfma(const u32x4& w, const u32x4& x, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, w), __builtin_bit_cast(f16x8, x), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x), c, 0,
+                                                   0, 0);
+}
+
+// Rotation state of a lane: (cos, sin) at its two tokens of the current tile
+// for its 8 pairs, and the step (cos, sin)(64 t) per tile.
+struct PhRot {
+  float cs[2][8], sn[2][8], c64[8], s64[8];
+};
+
+// Fragments of one tile, MFMA D[n][tok] += W[n][k] X[tok][k]; add the bias,
+// rotate pairs when `rot`, stage (bf16 nearest even) into `ys` as [tok][n]
+// with swizzled chunks.
+template <bool WF32, bool F16>
 __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, const u32x4 (&wh)[8],
-                                           const u32x4 (&wl)[8], const float (&bn)[16]) {
+                                           const u32x4 (&wl)[8], const float (&bn)[16], bool rot, PhRot& rs) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const char* xb = reinterpret_cast<const char*>(xs);
   f32x16 acc[2];
@@ -100,24 +132,34 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
     }
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
-      acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wh[ks]),
-                                                        __builtin_bit_cast(bf16x8, xf[ti]), acc[ti], 0, 0, 0);
-      if constexpr (WF32)
-        acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wl[ks]),
-                                                          __builtin_bit_cast(bf16x8, xf[ti]), acc[ti], 0, 0, 0);
+      acc[ti] = ph_mfma<F16>(wh[ks], xf[ti], acc[ti]);
+      if constexpr (WF32) acc[ti] = ph_mfma<F16>(wl[ks], xf[ti], acc[ti]);
     }
   }
-  // lane: token 32 ti + lane % 32, outputs n = 32 wave + 8 g + 4 (lane / 32) + e
+  // lane: token 32 ti + lane % 32, local rows j = 8 g + 4 (lane / 32) + e
   char* yb = reinterpret_cast<char*>(ys);
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = acc[ti][r] + bn[r];
+    if (rot) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float a = v[r], b = v[r + 8];
+        v[r] = a * rs.cs[ti][r] - b * rs.sn[ti][r];
+        v[r + 8] = a * rs.sn[ti][r] + b * rs.cs[ti][r];
+        const float cn = rs.cs[ti][r] * rs.c64[r] - rs.sn[ti][r] * rs.s64[r];
+        rs.sn[ti][r] = rs.sn[ti][r] * rs.c64[r] + rs.cs[ti][r] * rs.s64[r];
+        rs.cs[ti][r] = cn;
+      }
+    }
     const int tok = 32 * ti + (lane & 31);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int c = 4 * wave + g;  // 16-byte chunk of outputs 8c .. 8c+7
-      const u32x2 v = u32x2{cvt_bf16x2(acc[ti][4 * g] + bn[4 * g], acc[ti][4 * g + 1] + bn[4 * g + 1]),
-                            cvt_bf16x2(acc[ti][4 * g + 2] + bn[4 * g + 2], acc[ti][4 * g + 3] + bn[4 * g + 3])};
-      *reinterpret_cast<u32x2*>(yb + tok * 256 + 16 * ph_chunk(tok, c) + 8 * (lane >> 5)) = v;
+      const int c = ph_out(wave, 8 * g) >> 3;  // 16-byte chunk of outputs ph_out(w, 8g) .. +7
+      const u32x2 o = u32x2{cvt_bf16x2(v[4 * g], v[4 * g + 1]), cvt_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+      *reinterpret_cast<u32x2*>(yb + tok * 256 + 16 * ph_chunk(tok, c) + 8 * (lane >> 5)) = o;
     }
   }
 }
@@ -143,7 +185,9 @@ __device__ __forceinline__ void ph_barrier() {
   KVX_COMPILER_FENCE();
 }
 
-template <bool WF32>
+// WF32: fp32 maps (split in two halves); F16: fp16 sender rows (rotated back)
+// and fp16 map halves, else bf16.
+template <bool WF32, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(PH_THREADS, PH_THREADS), amdgpu_waves_per_eu(2, 2))) void
 perhead_kernel(const HeadKArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t x0[PH_TILE_ELEMS];
@@ -167,6 +211,7 @@ perhead_kernel(const HeadKArgs a) {
   const int32_t s = a.tap[l];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int64_t row_elems = static_cast<int64_t>(a.heads) * 128;
+  const int32_t x_rows = a.x_rows[role];
 
   PhTile pt;
   pt.t0 = span * PH_SPAN;
@@ -174,15 +219,16 @@ perhead_kernel(const HeadKArgs a) {
   pt.n_tiles = (pt.n_tok + PH_TILE - 1) / PH_TILE;
   pt.msm = msm;
   pt.row_bytes = static_cast<uint32_t>(2 * row_elems);
-  const uint16_t* xs = a.x[role] + static_cast<int64_t>(s) * a.send_tokens * row_elems + h * 128;
-  pt.xr = buf_rsrc(xs, static_cast<uint32_t>(static_cast<int64_t>(a.send_tokens) * 2 * row_elems - 256 * h));
+  const uint16_t* xs = a.x[role] + static_cast<int64_t>(s) * a.x_layer_stride[role] + h * 128;
+  pt.xr = buf_rsrc(xs, static_cast<uint32_t>(static_cast<int64_t>(x_rows) * 2 * row_elems - 256 * h));
   uint16_t* out = a.out[role] + (static_cast<int64_t>(l) * a.recv_tokens + pt.t0) * row_elems + h * 128;
 
-  // the span's token map, clamped to valid sender rows (entries past the
-  // span repeat its last token)
+  // the span's sender rows, clamped to valid rows (entries past the span
+  // repeat its last token)
+  const int32_t* row_of = a.row_of[role];
   for (int i = threadIdx.x; i < PH_SPAN; i += PH_THREADS) {
-    int32_t v = a.map[pt.t0 + min(i, pt.n_tok - 1)];
-    msm[i] = v < 0 ? 0 : (v >= a.send_tokens ? a.send_tokens - 1 : v);
+    int32_t v = row_of[pt.t0 + min(i, pt.n_tok - 1)];
+    msm[i] = v < 0 ? 0 : (v >= x_rows ? x_rows - 1 : v);
   }
   __syncthreads();
 
@@ -198,17 +244,40 @@ perhead_kernel(const HeadKArgs a) {
     return;
   }
 
-  // compute waves: tiles 0 .. 4 in flight while the map fragments are prepared
+  // compute waves.  Rotation state first (its loads precede the tile loads,
+  // so waiting for them never waits for a tile): the lane's tokens of tile 0
+  // and the step by one tile.
+  const bool rot = a.rotate[role] != 0;
+  PhRot rs;
+  if (rot) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int pr = ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));  // pair index (< 64)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int32_t tok = min(pt.t0 + 32 * ti + (lane & 31), a.recv_tokens - 1);
+        const float2 t = a.tab_recv[static_cast<int64_t>(tok) * 64 + pr];
+        rs.cs[ti][r] = t.x;
+        rs.sn[ti][r] = t.y;
+      }
+      // the table holds position 64 whenever a span has more than one tile
+      const float2 t64 = pt.n_tiles > 1 ? a.tab_recv[64 * 64 + pr] : float2{1.0f, 0.0f};
+      rs.c64[r] = t64.x;
+      rs.s64[r] = t64.y;
+    }
+  }
+
+  // tiles 0 .. 4 in flight while the map fragments are prepared
   ph_issue(pt, 0, x0);
   ph_issue(pt, 1, x1);
   ph_issue(pt, 2, x2);
   ph_issue(pt, 3, x3);
   ph_issue(pt, 4, x4);
 
-  // A fragments: rows n = 32 wave + lane % 32 of W_{l,h} ([n][c], output
-  // major), k = 16 ks + 8 (lane / 32) .. +8
+  // A fragments: rows n = ph_out(wave, lane % 32) of W_{l,h} ([n][c], output
+  // major), k = 16 ks + 8 (lane / 32) .. +8; halves rounded to nearest even
   u32x4 wh[8], wl[8];
-  const int n_row = 32 * wave + (lane & 31);
+  const int n_row = ph_out(wave, lane & 31);
   if constexpr (WF32) {
     const float* wp = static_cast<const float*>(a.wt[role]) +
                       ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
@@ -220,8 +289,15 @@ perhead_kernel(const HeadKArgs a) {
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hi[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
-        lo[e] = pack_bf16(f[2 * e] - bf16lo(hi[e]), f[2 * e + 1] - bf16hi(hi[e]));
+        if constexpr (F16) {
+          hi[e] = cvt_f16x2(f[2 * e], f[2 * e + 1]);
+          const float h0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] & 0xffffu)));
+          const float h1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] >> 16)));
+          lo[e] = cvt_f16x2(f[2 * e] - h0, f[2 * e + 1] - h1);
+        } else {
+          hi[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
+          lo[e] = pack_bf16(f[2 * e] - bf16lo(hi[e]), f[2 * e + 1] - bf16hi(hi[e]));
+        }
       }
       wh[ks] = u32x4{hi[0], hi[1], hi[2], hi[3]};
       wl[ks] = u32x4{lo[0], lo[1], lo[2], lo[3]};
@@ -231,29 +307,35 @@ perhead_kernel(const HeadKArgs a) {
                          ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      wh[ks] = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
+      u32x4 w = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
+      if constexpr (F16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = cvt_f16x2(bf16lo(w[e]), bf16hi(w[e]));
+      }
+      wh[ks] = w;
       wl[ks] = u32x4{0u, 0u, 0u, 0u};
     }
   }
   float bn[16];
   const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) bn[r] = bias ? bias[32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] : 0.0f;
+  for (int r = 0; r < 16; ++r)
+    bn[r] = bias ? bias[ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
 
   // Step k (tile k in stage k % 6, staging k % 2): the wait leaves the four
   // younger tiles in flight and completes this wave's staging writes, then
   // B_k; tile k+5 is issued into the stage of tile k-1 and tile k is
   // multiplied into its staging buffer.  Steps past n_tiles (the unrolled
   // loop runs a multiple of 6) pass no barrier.
-#define PH_STEP(K, XS, YS, XNEXT)                                            \
-  {                                                                          \
-    if ((K) <= pt.n_tiles) {                                                 \
-      KVX_WAIT_VM(4 * (PH_RING - 2));                                        \
-      KVX_WAIT_LGKM0();                                                      \
-      ph_barrier();                                                          \
-    }                                                                        \
-    ph_issue(pt, (K) + PH_RING - 1, XNEXT);                                  \
-    if ((K) < pt.n_tiles) ph_compute<WF32>(XS, YS, wh, wl, bn);              \
+#define PH_STEP(K, XS, YS, XNEXT)                                              \
+  {                                                                            \
+    if ((K) <= pt.n_tiles) {                                                   \
+      KVX_WAIT_VM(4 * (PH_RING - 2));                                          \
+      KVX_WAIT_LGKM0();                                                        \
+      ph_barrier();                                                            \
+    }                                                                          \
+    ph_issue(pt, (K) + PH_RING - 1, XNEXT);                                    \
+    if ((K) < pt.n_tiles) ph_compute<WF32, F16>(XS, YS, wh, wl, bn, rot, rs);  \
   }
   for (int32_t k = 0; k < pt.n_tiles; k += 6) {
     PH_STEP(k, x0, y0, x5)
@@ -275,31 +357,49 @@ perhead_kernel(const HeadKArgs a) {
 
 int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hipStream_t s) {
   if (p.recv_tokens <= 0 || n_roles <= 0) return KVX_OK;
-  // sender rows of one layer are addressed with 32-bit byte offsets
-  if (static_cast<int64_t>(p.send_tokens) * p.heads * 256 >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
-  HeadKArgs a{};
-  for (int i = 0; i < n_roles; ++i) {
-    a.x[i] = roles[i].x;
-    a.wt[i] = roles[i].wt;
-    a.bias[i] = roles[i].bias;
-    a.out[i] = roles[i].out;
+  // one launch per operand type (fp16 rotated-back key rows, bf16 otherwise)
+  for (int f16 = 1; f16 >= 0; --f16) {
+    HeadKArgs a{};
+    int n = 0;
+    for (int i = 0; i < n_roles; ++i) {
+      if (roles[i].x_f16 != f16) continue;
+      // sender rows of one layer are addressed with 32-bit byte offsets
+      if (static_cast<int64_t>(roles[i].x_rows) * p.heads * 256 >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
+      a.x[n] = roles[i].x;
+      a.x_layer_stride[n] = roles[i].x_layer_stride;
+      a.x_rows[n] = roles[i].x_rows;
+      a.row_of[n] = roles[i].row_of;
+      a.rotate[n] = roles[i].rotate;
+      a.wt[n] = roles[i].wt;
+      a.bias[n] = roles[i].bias;
+      a.out[n] = roles[i].out;
+      ++n;
+    }
+    if (n == 0) continue;
+    a.tab_recv = p.tab_recv;
+    a.recv_layers = p.recv_layers;
+    a.recv_tokens = p.recv_tokens;
+    a.heads = p.heads;
+    a.n_span = static_cast<int32_t>(ceil_div(p.recv_tokens, PH_SPAN));
+    for (int l = 0; l < p.recv_layers; ++l) a.tap[l] = static_cast<uint8_t>(p.taps[l]);
+    const int64_t nb = static_cast<int64_t>(n) * p.heads * a.n_span * p.recv_layers;
+    if (nb >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
+    a.n_blocks = static_cast<int32_t>(nb);
+    a.xcd_remap = (nb % 8 == 0) ? 1 : 0;
+    const unsigned g = static_cast<unsigned>(nb);
+    if (p.w_f32) {
+      if (f16)
+        perhead_kernel<true, true><<<g, PH_THREADS, 0, s>>>(a);
+      else
+        perhead_kernel<true, false><<<g, PH_THREADS, 0, s>>>(a);
+    } else {
+      if (f16)
+        perhead_kernel<false, true><<<g, PH_THREADS, 0, s>>>(a);
+      else
+        perhead_kernel<false, false><<<g, PH_THREADS, 0, s>>>(a);
+    }
+    KVX_LAUNCH_CHECK();
   }
-  a.map = p.recv_to_send;
-  a.send_tokens = p.send_tokens;
-  a.recv_layers = p.recv_layers;
-  a.recv_tokens = p.recv_tokens;
-  a.heads = p.heads;
-  a.n_span = static_cast<int32_t>(ceil_div(p.recv_tokens, PH_SPAN));
-  for (int l = 0; l < p.recv_layers; ++l) a.tap[l] = static_cast<uint8_t>(p.taps[l]);
-  const int64_t nb = static_cast<int64_t>(n_roles) * p.heads * a.n_span * p.recv_layers;
-  if (nb >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
-  a.n_blocks = static_cast<int32_t>(nb);
-  a.xcd_remap = (nb % 8 == 0) ? 1 : 0;
-  if (p.w_f32)
-    perhead_kernel<true><<<static_cast<unsigned>(nb), PH_THREADS, 0, s>>>(a);
-  else
-    perhead_kernel<false><<<static_cast<unsigned>(nb), PH_THREADS, 0, s>>>(a);
-  KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
 

@@ -148,11 +148,12 @@ int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps,
  * Asynchronous on `stream`.
  *
  * Arithmetic: bf16 caches with bf16 maps use bf16 matrix cores; fp32 maps are
- * applied as a bf16 high part plus a bf16 low part; keys rotated back from a
- * rotated sender are fed as fp16 (with the map converted to fp16); fp32
- * caches use fp32 arithmetic.  Accumulation is fp32 everywhere.
+ * applied as a 16-bit high part plus a 16-bit low part; keys rotated back
+ * from a rotated sender are fed as fp16 (the map converted to, or split
+ * into, fp16), other bf16 rows as bf16; fp32 caches use fp32 arithmetic.
+ * Accumulation is fp32 everywhere.
  * Supported: recv->dtype == send->dtype; bf16 caches need head_dim == 128
- * on both sides and, for per_head, no rotation on either side.
+ * on both sides.
  * ---------------------------------------------------------------------- */
 size_t kvx_translate_workspace_size(const kvx_cache_desc* send,
                                     const kvx_cache_desc* recv,

@@ -181,6 +181,56 @@ def test_cfg2_perhead_full_sampled_rows():
     run_cfg2(4096, rows)
 
 
+def perhead_rope_case(n_recv, seed, send_rope, recv_rope, map_dtype, rows=None, L_S=8, L_R=20):
+    """Per-head translation of rotated keys: sender keys rotated back at their
+    sender positions (fp16 rows), mapped per head, rotated at the receiver
+    positions; values mapped without rotation."""
+    send_end, recv_end = synth.token_ends(n_recv, seed)
+    shp = synth.CacheShape(L_S, len(send_end), 8, 128)
+    taps = kvx.layer_map(L_S, L_R, 1)
+    tmap_o = O.token_align(send_end, recv_end)
+    tm = dev_i32(tmap_o)
+    caches, maps, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        # channel scales of the per-head workload (a head's outlier channel
+        # would spread over all its outputs and put the bf16 rounding of the
+        # result itself above the max|err|/RMS tolerance)
+        caches[role] = synth.sender_cache(shp, seed * 10 + r, DEV, channel_scale="loguniform")
+        wt, b = synth.perhead_maps(L_R, 8, 128, seed * 10 + 5 + r, DEV)
+        maps[role], bias[role] = wt.to(map_dtype), b
+    k, v = kvx.translate(caches["k"], caches["v"], tm, taps, maps["k"], maps["v"], bias["k"], bias["v"],
+                         per_head=True, send_rope_base=send_rope, recv_rope_base=recv_rope)
+    torch.cuda.synchronize()
+    rows = np.arange(tmap_o.size) if rows is None else rows
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], tmap_o, taps, host(maps[role]).float().numpy().astype(np.float64),
+                                host(bias[role]).numpy().astype(np.float64), rows, per_head=True, recv_heads=8,
+                                recv_head_dim=128, send_rope_base=send_rope if rk else 0.0,
+                                recv_rope_base=recv_rope if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  per-head rope n={tmap_o.size} {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("send_rope,recv_rope", [(5e5, 1e6), (0.0, 1e6), (1e4, 0.0)])
+@pytest.mark.parametrize("map_dtype", [torch.float32, torch.bfloat16])
+def test_perhead_rope_all_elements(send_rope, recv_rope, map_dtype):
+    say(f"per-head + RoPE {send_rope:g}->{recv_rope:g} maps {map_dtype}, 300 receiver tokens")
+    perhead_rope_case(300, 71, send_rope, recv_rope, map_dtype)
+
+
+def test_perhead_rope_long_span_sampled_rows():
+    """Two spans of receiver tokens (4096 + a ragged rest): the rotation
+    recurrence runs over 64 tiles; rows sampled at the start and end of each
+    span and in between."""
+    say("per-head + RoPE, 4500 receiver tokens, sampled rows")
+    n = 4500
+    rows = np.unique(np.concatenate([np.arange(0, 70), np.arange(4030, 4160), np.arange(n - 70, n),
+                                     sample_rows(np.arange(n), 64, 3)]))
+    perhead_rope_case(n, 72, 5e5, 1e6, torch.float32, rows=rows, L_S=4, L_R=6)
+
+
 # ---------------------------------------------------------------- cfg3/4: flattened maps
 
 
