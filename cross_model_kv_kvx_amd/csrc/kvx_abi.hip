@@ -431,24 +431,38 @@ int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t
                        static_cast<hipStream_t>(stream));
 }
 
-size_t kvx_fit_ridge_workspace_size(int32_t f_in, int32_t f_out) {
-  if (f_in < 1 || f_out < 1) return 0;
-  return fit_ws_bytes(f_in, f_out);
+size_t kvx_fit_ridge_workspace_size(int32_t f_in, int32_t f_out) { return kvx_fit_ridge_batched_workspace_size(1, f_in, f_out); }
+
+size_t kvx_fit_ridge_batched_workspace_size(int32_t count, int32_t f_in, int32_t f_out) {
+  if (count < 1 || f_in < 1 || f_out < 1) return 0;
+  return fit_ws_bytes(count, f_in, f_out);
+}
+
+int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy,
+                          int32_t in_dtype, int64_t n_rows, int32_t f_in, int32_t f_out, double lambda_abs,
+                          double lambda_rel, int32_t fit_intercept, float* const* w_out, float* const* b_out,
+                          int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+  if (count < 0 || f_in < 1 || f_out < 1 || n_rows < 0) return KVX_ERR_INVALID;
+  if (count == 0) return KVX_OK;
+  if (in_dtype != KVX_F32 && in_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  if (!(lambda_abs >= 0.0) || !(lambda_rel >= 0.0)) return KVX_ERR_INVALID;
+  if (!x || !y || !w_out || (fit_intercept && !b_out)) return KVX_ERR_INVALID;
+  for (int32_t z = 0; z < count; ++z) {
+    if (!w_out[z] || (fit_intercept && !b_out[z])) return KVX_ERR_INVALID;
+    if (n_rows > 0 && (!x[z] || !y[z])) return KVX_ERR_INVALID;
+  }
+  if (ldx < f_in || ldy < f_out) return KVX_ERR_SHAPE;
+  if (in_dtype == KVX_BF16 && ((f_in % 8) || (f_out % 8) || (ldx % 8) || (ldy % 8))) return KVX_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < kvx_fit_ridge_batched_workspace_size(count, f_in, f_out)) return KVX_ERR_WORKSPACE;
+  return launch_fit(count, x, ldx, y, ldy, in_dtype == KVX_F32, n_rows, f_in, f_out, lambda_abs, lambda_rel,
+                    fit_intercept, w_out, b_out, status, workspace, static_cast<hipStream_t>(stream));
 }
 
 int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_dtype, int64_t n_rows,
                   int32_t f_in, int32_t f_out, double lambda_abs, double lambda_rel, int32_t fit_intercept,
                   float* w_out, float* b_out, void* workspace, size_t ws_bytes, void* stream) {
-  if (f_in < 1 || f_out < 1 || n_rows < 0) return KVX_ERR_INVALID;
-  if (in_dtype != KVX_F32 && in_dtype != KVX_BF16) return KVX_ERR_INVALID;
-  if (!(lambda_abs >= 0.0) || !(lambda_rel >= 0.0)) return KVX_ERR_INVALID;
-  if (!w_out || (fit_intercept && !b_out)) return KVX_ERR_INVALID;
-  if (n_rows > 0 && (!x || !y)) return KVX_ERR_INVALID;
-  if (ldx < f_in || ldy < f_out) return KVX_ERR_SHAPE;
-  if (in_dtype == KVX_BF16 && ((f_in % 8) || (f_out % 8) || (ldx % 8) || (ldy % 8))) return KVX_ERR_UNSUPPORTED;
-  if (!workspace || ws_bytes < kvx_fit_ridge_workspace_size(f_in, f_out)) return KVX_ERR_WORKSPACE;
-  return launch_fit(x, ldx, y, ldy, in_dtype == KVX_F32, n_rows, f_in, f_out, lambda_abs, lambda_rel,
-                    fit_intercept, w_out, b_out, workspace, static_cast<hipStream_t>(stream));
+  return kvx_fit_ridge_batched(1, &x, ldx, &y, ldy, in_dtype, n_rows, f_in, f_out, lambda_abs, lambda_rel,
+                               fit_intercept, &w_out, &b_out, nullptr, workspace, ws_bytes, stream);
 }
 
 int kvx_fold_lowrank(const float* wt, const float* a, const float* b, int32_t count, int32_t f_in, int32_t f_out,

@@ -10,10 +10,17 @@
 //   2. optional centring for an unpenalised intercept, lambda from the trace,
 //      lambda added to the diagonal (fp64, on the device);
 //   3. blocked Cholesky G + lambda I = L L^T in fp64 (64-wide blocks: diagonal
-//      factor in LDS, panel triangular solve, trailing update by an fp64
-//      tiled GEMM), then L Z = C and L^T W = Z by blocks;
+//      factor and its inverse by one wave, panel triangular solve and
+//      trailing update as fp64 matrix-core products), then L Z = C and
+//      L^T W = Z by blocks;
 //   4. W written output-major in fp32, b = mean_y - mean_x W.
-// A non-positive pivot sets a device flag that the host reads once.
+// Several problems of one shape (the maps of every layer and role) are
+// fitted by one call: steps 1, 2 and 4 run problem by problem (each fills
+// the GPU), step 3 runs every launch of its serial chain over all problems
+// at once, so the chain's latency is paid once per call.  A non-positive
+// pivot sets the problem's device flag; the host reads the flags once.
+
+#include <vector>
 
 #include "kvx_internal.hpp"
 
@@ -249,7 +256,8 @@ __global__ __launch_bounds__(256) void lambda_kernel(double* __restrict__ G, int
 
 // ---------------------------------------------------------------- fp64 Cholesky pieces
 
-// Factor the diagonal block [k0, k0+nb) (lower), flag non-positive pivots,
+// Factor the diagonal block [k0, k0+nb) (lower) of one problem of a batch
+// (one workgroup per problem), flag non-positive pivots,
 // and write the inverse of the factor (lower, nb x nb, zero above the
 // diagonal, row stride CH_NB) to `linv`: the panel and the block triangular
 // solves then become products with it.  One wave, no barrier: lane i keeps
@@ -259,8 +267,13 @@ __global__ __launch_bounds__(256) void lambda_kernel(double* __restrict__ G, int
 // column (LDS operations of one wave execute in order).  Rows past nb are
 // the identity.  The inverse is formed one column per lane by forward
 // substitution against the factor in LDS.
-__global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, int32_t n, int32_t k0, int32_t nb,
-                                                        int32_t* __restrict__ flag, double* __restrict__ linv) {
+__global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, int64_t bsa, int32_t n, int32_t k0,
+                                                        int32_t nb, int32_t* __restrict__ flag,
+                                                        double* __restrict__ linv, int64_t bsl) {
+  // problem blockIdx.x of a batch
+  A += blockIdx.x * bsa;
+  flag += blockIdx.x;
+  linv += blockIdx.x * bsl;
   __shared__ double L[CH_NB][CH_NB + 1];
   __shared__ double col[CH_NB];
   const int i = threadIdx.x;
@@ -309,56 +322,99 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
   }
 }
 
-// C[M x N] -= A * B (overwrite = 0) or C = A * B (overwrite = 1), with
-// A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].  64 x 64 tiles, 16 x 16
-// threads with 4 x 4 outputs each; a workgroup reads all of its A rows and B
-// columns before it writes its tile, so C may alias A when N <= 64 or B when
-// M <= 64.  lower_only skips tiles strictly above the diagonal.
-__global__ __launch_bounds__(256) void gemm64_kernel(int32_t M, int32_t N, int32_t K, const double* A, int64_t sam,
-                                                     int64_t sak, const double* B, int64_t sbk, int64_t sbn, double* C,
-                                                     int64_t ldc, int32_t lower_only, int32_t overwrite) {
+// C[M x N] -= A * B (overwrite = 0) or C = A * B (overwrite = 1) in fp64 on
+// matrix cores, for a batch of problems (blockIdx.z; the operands of problem
+// z start bsa, bsb, bsc elements after those of problem z-1), with
+// A(m,k) = A[m*sam + k*sak] and B(k,n) = B[k*sbk + n*sbn].  64 x 64 tiles;
+// four waves of 32 x 32, each from 2 x 2 MFMA 16x16x4 fp64 blocks; K in steps
+// of 16 through LDS as [k][m] and [k][n] (global elements are read along the
+// operand's unit-stride index; rows padded so the 16-lane row pieces of a
+// fragment read fall in distinct banks).  A workgroup reads all of its A rows
+// and B columns before it writes its tile, so C may alias A when N <= 64 or B
+// when M <= 64.  lower_only skips tiles strictly above the diagonal.
+struct DgArgs {
+  int32_t M, N, K;
+  const double* A;
+  int64_t sam, sak, bsa;
+  const double* B;
+  int64_t sbk, sbn, bsb;
+  double* C;
+  int64_t ldc, bsc;
+  int32_t lower_only, overwrite;
+};
+constexpr int DG_T = 64;
+constexpr int DG_BK = 16;
+constexpr int DG_LD = DG_T + 16;
+
+__global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
   const int32_t bm = blockIdx.y, bn = blockIdx.x;
-  if (lower_only && bm < bn) return;
-  __shared__ double As[16][65];
-  __shared__ double Bs[16][65];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int32_t m0 = bm * 64, n0 = bn * 64;
-  double acc[4][4] = {};
-  for (int32_t k0 = 0; k0 < K; k0 += 16) {
-    for (int e = threadIdx.x; e < 1024; e += 256) {
-      const int mm = e & 63, kk = e >> 6;
-      const int32_t m = m0 + mm, k = k0 + kk;
-      As[kk][mm] = (m < M && k < K) ? A[m * sam + k * sak] : 0.0;
-      const int32_t nn = n0 + mm;
-      Bs[kk][mm] = (nn < N && k < K) ? B[k * sbk + nn * sbn] : 0.0;
+  if (g.lower_only && bm < bn) return;
+  __shared__ double As[DG_BK][DG_LD];
+  __shared__ double Bs[DG_BK][DG_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int32_t m0 = bm * DG_T, n0 = bn * DG_T;
+  const double* A = g.A + blockIdx.z * g.bsa;
+  const double* B = g.B + blockIdx.z * g.bsb;
+  double* C = g.C + blockIdx.z * g.bsc;
+  const bool a_k = g.sak == 1 && g.sam != 1;  // A read along k
+  const bool b_k = g.sbk == 1 && g.sbn != 1;  // B read along k
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int32_t k0 = 0; k0 < g.K; k0 += DG_BK) {
+    double av[4], bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      const int ma = a_k ? (e >> 4) : (e & 63), ka = a_k ? (e & 15) : (e >> 6);
+      const int32_t m = m0 + ma, k = k0 + ka;
+      av[q] = (m < g.M && k < g.K) ? A[m * g.sam + k * g.sak] : 0.0;
+      const int nb_ = b_k ? (e >> 4) : (e & 63), kb = b_k ? (e & 15) : (e >> 6);
+      const int32_t n = n0 + nb_, kq = k0 + kb;
+      bv[q] = (n < g.N && kq < g.K) ? B[kq * g.sbk + n * g.sbn] : 0.0;
+    }
+    __syncthreads();  // the previous step's fragment reads are done
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      As[a_k ? (e & 15) : (e >> 6)][a_k ? (e >> 4) : (e & 63)] = av[q];
+      Bs[b_k ? (e & 15) : (e >> 6)][b_k ? (e >> 4) : (e & 63)] = bv[q];
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      double a[4], b[4];
+    for (int k4 = 0; k4 < DG_BK; k4 += 4) {
+      // operands of MFMA 16x16x4: lane l holds A[l%16][l/16] and B[l/16][l%16]
+      const int kr = k4 + (lane >> 4);
+      double a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+      for (int i = 0; i < 2; ++i) a[i] = As[kr][wm * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+      for (int j = 0; j < 2; ++j) b[j] = Bs[kr][wn * 32 + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
+  // element r of lane l: row l/16 + 4r, column l%16 of its 16 x 16 block
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int32_t m = m0 + ty + 16 * i, nn = n0 + tx + 16 * j;
-      if (m < M && nn < N) {
-        if (overwrite)
-          C[m * ldc + nn] = acc[i][j];
-        else
-          C[m * ldc + nn] -= acc[i][j];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t m = m0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r;
+        const int32_t n = n0 + wn * 32 + j * 16 + (lane & 15);
+        if (m < g.M && n < g.N) {
+          if (g.overwrite)
+            C[m * g.ldc + n] = acc[i][j][r];
+          else
+            C[m * g.ldc + n] -= acc[i][j][r];
+        }
       }
-    }
 }
 
 // w_out[o][f] = W[f][o] (fp32); b_out[o] = mean_y[o] - sum_f mean_x[f] W[f][o].
@@ -383,18 +439,46 @@ __global__ __launch_bounds__(256) void fit_output_kernel(const double* __restric
 
 // ---------------------------------------------------------------- host side
 
-size_t fit_ws_bytes(int32_t f_in, int32_t f_out) {
-  Carve c(nullptr);
-  c.take<double>(static_cast<size_t>(f_in) * f_in);
-  c.take<double>(static_cast<size_t>(f_in) * f_out);
-  c.take<double>(f_in);
-  c.take<double>(f_out);
-  c.take<double>(4);
-  c.take<int32_t>(64);
-  c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
-  c.take<double>(static_cast<size_t>(ceil_div(f_in, CH_NB)) * CH_NB * CH_NB);
-  return c.used + 256;
+// Workspace: the Gram partials (shared by the problems, which are
+// accumulated one after the other), then per problem G, C, column sums,
+// lambda and the inverse diagonal factors, then one flag per problem.
+struct FitWs {
+  float* part;
+  double *G, *C, *sx, *sy, *lam, *linv;
+  int64_t bs;  // doubles between the per-problem areas
+  int64_t oG, oC, oSx, oSy, oLam, oLinv;
+  int32_t* flags;
+  size_t bytes;
+};
+
+static FitWs fit_layout(int32_t count, int32_t f_in, int32_t f_out, void* base) {
+  FitWs w{};
+  Carve c(base);
+  w.part = c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  const int64_t nb_total = ceil_div(f_in, CH_NB);
+  auto up = [](int64_t v) { return (v + 31) / 32 * 32; };  // 256-byte sub-areas
+  w.oG = 0;
+  w.oC = w.oG + up(static_cast<int64_t>(f_in) * f_in);
+  w.oSx = w.oC + up(static_cast<int64_t>(f_in) * f_out);
+  w.oSy = w.oSx + up(f_in);
+  w.oLam = w.oSy + up(f_out);
+  w.oLinv = w.oLam + up(4);
+  w.bs = w.oLinv + up(nb_total * CH_NB * CH_NB);
+  double* area = c.take<double>(static_cast<size_t>(count) * w.bs);
+  if (area) {
+    w.G = area + w.oG;
+    w.C = area + w.oC;
+    w.sx = area + w.oSx;
+    w.sy = area + w.oSy;
+    w.lam = area + w.oLam;
+    w.linv = area + w.oLinv;
+  }
+  w.flags = c.take<int32_t>(static_cast<size_t>(count) + 64);
+  w.bytes = c.used + 256;
+  return w;
 }
+
+size_t fit_ws_bytes(int32_t count, int32_t f_in, int32_t f_out) { return fit_layout(count, f_in, f_out, nullptr).bytes; }
 
 static unsigned grid_for(int64_t n) {
   int64_t b = ceil_div(n, 256);
@@ -402,141 +486,154 @@ static unsigned grid_for(int64_t n) {
   return static_cast<unsigned>(b < 1 ? 1 : b);
 }
 
-int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32, int64_t n_rows,
-               int32_t f_in, int32_t f_out, double lam_abs, double lam_rel, int32_t fit_intercept,
-               float* w_out, float* b_out, void* ws, hipStream_t s) {
-  Carve cv(ws);
-  double* G = cv.take<double>(static_cast<size_t>(f_in) * f_in);
-  double* C = cv.take<double>(static_cast<size_t>(f_in) * f_out);
-  double* sx = cv.take<double>(f_in);
-  double* sy = cv.take<double>(f_out);
-  double* lam = cv.take<double>(4);
-  int32_t* flag = cv.take<int32_t>(64);
-  float* part = cv.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
-  const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
-  double* linv = cv.take<double>(static_cast<size_t>(nb_total) * CH_NB * CH_NB);  // inverse diagonal factors
-  if (int st = launch_fill_i32(flag, 1, 0, s)) return st;
+static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, const double* A, int64_t sam,
+                 int64_t sak, const double* B, int64_t sbk, int64_t sbn, double* C, int64_t ldc, int64_t bs,
+                 int32_t lower_only, int32_t overwrite, int64_t bsb = -1) {
+  DgArgs g{M, N, K, A, sam, sak, bs, B, sbk, sbn, bsb < 0 ? bs : bsb, C, ldc, bs, lower_only, overwrite};
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, DG_T)), static_cast<unsigned>(ceil_div(M, DG_T)),
+                  static_cast<unsigned>(count));
+  dgemm_kernel<<<grid, 256, 0, s>>>(g);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
+}
 
-  // 1. Gram and cross products
+// Gram and cross products of one problem into its G and C.
+static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32, int64_t n_rows,
+                    int32_t f_in, int32_t f_out, float* part, double* G, double* C, hipStream_t s) {
   if (in_f32) {
     gram_f32_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(
         static_cast<const float*>(x), ldx, static_cast<const float*>(y), ldy, n_rows, f_in, f_out, G, C);
     KVX_LAUNCH_CHECK();
-  } else {
-    GramArgs g{};
-    g.x = static_cast<const uint16_t*>(x);
-    g.y = static_cast<const uint16_t*>(y);
-    g.ldx = ldx;
-    g.ldy = ldy;
-    g.n_rows = n_rows;
-    g.f_in = f_in;
-    g.f_out = f_out;
-    g.nbi = static_cast<int32_t>(ceil_div(f_in, GR_T));
-    g.nbc = static_cast<int32_t>(ceil_div(f_out, GR_T));
-    g.n_g = g.nbi * (g.nbi + 1) / 2;
-    g.n_c = g.nbi * g.nbc;
-    const int cus = device_cu_count();
-    int split = static_cast<int>(ceil_div(2 * cus, g.n_g + g.n_c));
-    if (split > GR_MAX_SPLIT) split = GR_MAX_SPLIT;
-    const int64_t max_split = ceil_div(n_rows, GR_BK);
-    if (split > max_split) split = static_cast<int>(max_split > 0 ? max_split : 1);
-    if (split < 1) split = 1;
-    g.split = split;
-    g.rows_per_split = ceil_div(ceil_div(n_rows, split), GR_BK) * GR_BK;
-    g.part = part;
-    gram_kernel<<<static_cast<unsigned>(split * (g.n_g + g.n_c)), 256, 0, s>>>(g);
-    KVX_LAUNCH_CHECK();
-    gram_reduce_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(part, split, f_in,
-                                                                                            f_out, G, C);
-    KVX_LAUNCH_CHECK();
+    return KVX_OK;
   }
-
-  // 2. centring and lambda
-  const double inv_n = n_rows > 0 ? 1.0 / static_cast<double>(n_rows) : 0.0;
-  if (fit_intercept) {
-    if (in_f32) {
-      colsum_kernel<true><<<grid_for(f_in), 256, 0, s>>>(x, ldx, n_rows, f_in, sx);
-      colsum_kernel<true><<<grid_for(f_out), 256, 0, s>>>(y, ldy, n_rows, f_out, sy);
-    } else {
-      colsum_kernel<false><<<grid_for(f_in), 256, 0, s>>>(x, ldx, n_rows, f_in, sx);
-      colsum_kernel<false><<<grid_for(f_out), 256, 0, s>>>(y, ldy, n_rows, f_out, sy);
-    }
-    KVX_LAUNCH_CHECK();
-    center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
-                                                                                        inv_n);
-    KVX_LAUNCH_CHECK();
-  }
-  lambda_kernel<<<1, 256, 0, s>>>(G, f_in, lam_abs, lam_rel, lam);
+  GramArgs g{};
+  g.x = static_cast<const uint16_t*>(x);
+  g.y = static_cast<const uint16_t*>(y);
+  g.ldx = ldx;
+  g.ldy = ldy;
+  g.n_rows = n_rows;
+  g.f_in = f_in;
+  g.f_out = f_out;
+  g.nbi = static_cast<int32_t>(ceil_div(f_in, GR_T));
+  g.nbc = static_cast<int32_t>(ceil_div(f_out, GR_T));
+  g.n_g = g.nbi * (g.nbi + 1) / 2;
+  g.n_c = g.nbi * g.nbc;
+  const int cus = device_cu_count();
+  int split = static_cast<int>(ceil_div(2 * cus, g.n_g + g.n_c));
+  if (split > GR_MAX_SPLIT) split = GR_MAX_SPLIT;
+  const int64_t max_split = ceil_div(n_rows, GR_BK);
+  if (split > max_split) split = static_cast<int>(max_split > 0 ? max_split : 1);
+  if (split < 1) split = 1;
+  g.split = split;
+  g.rows_per_split = ceil_div(ceil_div(n_rows, split), GR_BK) * GR_BK;
+  g.part = part;
+  gram_kernel<<<static_cast<unsigned>(split * (g.n_g + g.n_c)), 256, 0, s>>>(g);
   KVX_LAUNCH_CHECK();
+  gram_reduce_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(part, split, f_in, f_out,
+                                                                                          G, C);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
+}
 
-  // 3. Cholesky and the two block triangular solves; the diagonal kernel
-  // leaves the inverse factor of its block, so each panel and each block
-  // solve is an in-place product with it.
+int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy, int32_t in_f32,
+               int64_t n_rows, int32_t f_in, int32_t f_out, double lam_abs, double lam_rel, int32_t fit_intercept,
+               float* const* w_out, float* const* b_out, int32_t* status, void* ws, hipStream_t s) {
+  const FitWs w = fit_layout(count, f_in, f_out, ws);
+  const int64_t bs = w.bs;
+  if (int st = launch_fill_i32(w.flags, count, 0, s)) return st;
+  const double inv_n = n_rows > 0 ? 1.0 / static_cast<double>(n_rows) : 0.0;
+
+  // 1. Gram and cross products, centring and lambda, problem by problem
+  for (int32_t z = 0; z < count; ++z) {
+    double* G = w.G + z * bs;
+    double* C = w.C + z * bs;
+    double* sx = w.sx + z * bs;
+    double* sy = w.sy + z * bs;
+    if (int st = gram_one(x[z], ldx, y[z], ldy, in_f32, n_rows, f_in, f_out, w.part, G, C, s)) return st;
+    if (fit_intercept) {
+      if (in_f32) {
+        colsum_kernel<true><<<grid_for(f_in), 256, 0, s>>>(x[z], ldx, n_rows, f_in, sx);
+        colsum_kernel<true><<<grid_for(f_out), 256, 0, s>>>(y[z], ldy, n_rows, f_out, sy);
+      } else {
+        colsum_kernel<false><<<grid_for(f_in), 256, 0, s>>>(x[z], ldx, n_rows, f_in, sx);
+        colsum_kernel<false><<<grid_for(f_out), 256, 0, s>>>(y[z], ldy, n_rows, f_out, sy);
+      }
+      KVX_LAUNCH_CHECK();
+      center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
+                                                                                          inv_n);
+      KVX_LAUNCH_CHECK();
+    }
+    lambda_kernel<<<1, 256, 0, s>>>(G, f_in, lam_abs, lam_rel, w.lam + z * bs);
+    KVX_LAUNCH_CHECK();
+  }
+
+  // 2. Cholesky and the two block triangular solves of all problems at once;
+  // the diagonal kernel leaves the inverse factor of its block, so each panel
+  // and each block solve is an in-place product with it.
+  const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
   for (int32_t kb = 0; kb < nb_total; ++kb) {
     const int32_t k0 = kb * CH_NB;
     const int32_t nb = min(CH_NB, f_in - k0);
-    double* li = linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
-    potrf_diag_kernel<<<1, 64, 0, s>>>(G, f_in, k0, nb, flag, li);
+    double* li = w.linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+    potrf_diag_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(w.G, bs, f_in, k0, nb, w.flags, li, bs);
     KVX_LAUNCH_CHECK();
     const int32_t rest = f_in - k0 - nb;
     if (rest > 0) {
-      const int32_t t = static_cast<int32_t>(ceil_div(rest, 64));
       // panel: P = P L_kk^-T (in place, one 64-column tile)
-      double* P = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
-      gemm64_kernel<<<dim3(1, t), 256, 0, s>>>(rest, nb, nb, P, f_in, 1, li, 1, CH_NB, P, f_in, 0, 1);
-      KVX_LAUNCH_CHECK();
+      double* P = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0;
+      if (int st = dgemm(s, count, rest, nb, nb, P, f_in, 1, li, 1, CH_NB, P, f_in, bs, 0, 1)) return st;
       // trailing lower update: G[r][c] -= P[r] . P[c] for r, c >= k0+nb
-      double* Ct = G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
-      gemm64_kernel<<<dim3(t, t), 256, 0, s>>>(rest, rest, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, 1, 0);
-      KVX_LAUNCH_CHECK();
+      double* Ct = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
+      if (int st = dgemm(s, count, rest, rest, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, bs, 1, 0)) return st;
     }
   }
-  const unsigned col_tiles = static_cast<unsigned>(ceil_div(f_out, 64));
   // forward: L Z = C
   for (int32_t kb = 0; kb < nb_total; ++kb) {
     const int32_t k0 = kb * CH_NB;
     const int32_t nb = min(CH_NB, f_in - k0);
-    const double* li = linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
-    double* Zk = C + static_cast<int64_t>(k0) * f_out;
+    const double* li = w.linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+    double* Zk = w.C + static_cast<int64_t>(k0) * f_out;
     // Z_k = L_kk^-1 Z_k (in place, one 64-row tile)
-    gemm64_kernel<<<dim3(col_tiles, 1), 256, 0, s>>>(nb, f_out, nb, li, CH_NB, 1, Zk, f_out, 1, Zk, f_out, 0, 1);
-    KVX_LAUNCH_CHECK();
+    if (int st = dgemm(s, count, nb, f_out, nb, li, CH_NB, 1, Zk, f_out, 1, Zk, f_out, bs, 0, 1)) return st;
     const int32_t rest = f_in - k0 - nb;
     if (rest > 0) {
-      const double* Lb = G + static_cast<int64_t>(k0 + nb) * f_in + k0;
-      double* Cr = C + static_cast<int64_t>(k0 + nb) * f_out;
-      gemm64_kernel<<<dim3(col_tiles, static_cast<unsigned>(ceil_div(rest, 64))), 256, 0, s>>>(
-          rest, f_out, nb, Lb, f_in, 1, Zk, f_out, 1, Cr, f_out, 0, 0);
-      KVX_LAUNCH_CHECK();
+      const double* Lb = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0;
+      double* Cr = w.C + static_cast<int64_t>(k0 + nb) * f_out;
+      if (int st = dgemm(s, count, rest, f_out, nb, Lb, f_in, 1, Zk, f_out, 1, Cr, f_out, bs, 0, 0)) return st;
     }
   }
   // backward: L^T W = Z
   for (int32_t kb = nb_total - 1; kb >= 0; --kb) {
     const int32_t k0 = kb * CH_NB;
     const int32_t nb = min(CH_NB, f_in - k0);
-    const double* li = linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
-    double* Wk = C + static_cast<int64_t>(k0) * f_out;
+    const double* li = w.linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+    double* Wk = w.C + static_cast<int64_t>(k0) * f_out;
     // W_k = L_kk^-T W_k (in place)
-    gemm64_kernel<<<dim3(col_tiles, 1), 256, 0, s>>>(nb, f_out, nb, li, 1, CH_NB, Wk, f_out, 1, Wk, f_out, 0, 1);
-    KVX_LAUNCH_CHECK();
+    if (int st = dgemm(s, count, nb, f_out, nb, li, 1, CH_NB, Wk, f_out, 1, Wk, f_out, bs, 0, 1)) return st;
     if (k0 > 0) {
       // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_k
-      const double* Lr = G + static_cast<int64_t>(k0) * f_in;
-      gemm64_kernel<<<dim3(col_tiles, static_cast<unsigned>(ceil_div(k0, 64))), 256, 0, s>>>(
-          k0, f_out, nb, Lr, 1, f_in, Wk, f_out, 1, C, f_out, 0, 0);
-      KVX_LAUNCH_CHECK();
+      const double* Lr = w.G + static_cast<int64_t>(k0) * f_in;
+      if (int st = dgemm(s, count, k0, f_out, nb, Lr, 1, f_in, Wk, f_out, 1, w.C, f_out, bs, 0, 0)) return st;
     }
   }
 
-  // 4. outputs
-  fit_output_kernel<<<grid_for(static_cast<int64_t>(f_in) * f_out), 256, 0, s>>>(
-      C, f_in, f_out, w_out, fit_intercept ? b_out : nullptr, sx, sy, inv_n);
-  KVX_LAUNCH_CHECK();
+  // 3. outputs
+  for (int32_t z = 0; z < count; ++z) {
+    fit_output_kernel<<<grid_for(static_cast<int64_t>(f_in) * f_out), 256, 0, s>>>(
+        w.C + z * bs, f_in, f_out, w_out[z], fit_intercept ? b_out[z] : nullptr, w.sx + z * bs, w.sy + z * bs,
+        inv_n);
+    KVX_LAUNCH_CHECK();
+  }
 
-  int32_t host_flag = 0;
-  KVX_HIP_TRY(hipMemcpyAsync(&host_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  std::vector<int32_t> host_flags(static_cast<size_t>(count), 0);
+  KVX_HIP_TRY(hipMemcpyAsync(host_flags.data(), w.flags, sizeof(int32_t) * count, hipMemcpyDeviceToHost, s));
   KVX_HIP_TRY(hipStreamSynchronize(s));
-  return host_flag ? KVX_ERR_NOT_SPD : KVX_OK;
+  int result = KVX_OK;
+  for (int32_t z = 0; z < count; ++z) {
+    if (status) status[z] = host_flags[z] ? KVX_ERR_NOT_SPD : KVX_OK;
+    if (host_flags[z]) result = KVX_ERR_NOT_SPD;
+  }
+  return result;
 }
 
 }  // namespace kvx

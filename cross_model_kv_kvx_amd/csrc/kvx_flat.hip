@@ -32,10 +32,13 @@
 //     banks;
 //   * each part is a separate LDS array so the compiler can keep counted
 //     vmcnt waits, and the only synchronisation per step is one s_barrier;
-//   * tiles of one problem are grouped 8 (rows) x F_out/256 (outputs) and
-//     consecutive groups go to the workgroups of one XCD (workgroups are
-//     dispatched round robin over the 8 XCDs), so A and W slices are shared
-//     in that XCD's L2;
+//   * the row tiles of all problems, in problem order, are grouped 8 at a
+//     time (a group may hold the last row tiles of one problem and the first
+//     of the next) x F_out/256 output tiles, and each group goes to
+//     consecutive workgroups of one XCD (workgroups are dispatched round
+//     robin over the 8 XCDs): the XCD's 32 concurrent tiles read 8 A slices
+//     and 4 (or 8) W slices through its L2, and every A slice is read by one
+//     group only;
 //   * epilogue: each wave stages 32 rows x 128 outputs (bias added, fp32) in
 //     its 16 KB share of parts 1..4, then walks the receiver rows of those
 //     runs 8 at a time, rotating key pairs (c, c+64) at the receiver position
@@ -225,14 +228,17 @@ flat_gemm_kernel(const FlatKArgs args) {
   uint16_t* const ep_part = wave < 2 ? p1 : (wave < 4 ? p2 : (wave < 6 ? p3 : p4));
   float* const ep = reinterpret_cast<float*>(ep_part) + (wave & 1) * FT_EP_FLOATS;
 
+  const int64_t R = static_cast<int64_t>(args.n_roles) * args.recv_layers * mt;  // row tiles of all problems
   for (int64_t t = slot; t < T; t += G) {
-    const int32_t p = static_cast<int32_t>(t / per_p);
-    const int32_t rr = static_cast<int32_t>(t % per_p);
-    const int32_t mg = rr / (FT_GM * nt);
-    const int32_t r2 = rr % (FT_GM * nt);
-    const int32_t gm = min(FT_GM, mt - mg * FT_GM);
+    // group of FT_GM consecutive row tiles (of one problem or the end of one
+    // and the start of the next) x all output tiles
+    const int64_t g = t / (FT_GM * nt);
+    const int32_t r2 = static_cast<int32_t>(t % (FT_GM * nt));
+    const int32_t gm = static_cast<int32_t>(min(static_cast<int64_t>(FT_GM), R - g * FT_GM));
     const int32_t n0 = (r2 / gm) * FT_N;
-    const int32_t m0 = (mg * FT_GM + r2 % gm) * FT_M;
+    const int64_t mrow = g * FT_GM + r2 % gm;
+    const int32_t p = static_cast<int32_t>(mrow / mt);
+    const int32_t m0 = static_cast<int32_t>(mrow % mt) * FT_M;
     const int role = p / args.recv_layers;
     const int l = p % args.recv_layers;
 

@@ -117,10 +117,13 @@ int launch_gather(const void* cache, int32_t cache_f32, int32_t send_tokens, int
                   const int32_t* recv_to_send, int32_t n_rows, double rope_base, int32_t head_dim,
                   void* out, hipStream_t s);
 
-size_t fit_ws_bytes(int32_t f_in, int32_t f_out);
-int launch_fit(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32,
-               int64_t n_rows, int32_t f_in, int32_t f_out, double lam_abs, double lam_rel,
-               int32_t fit_intercept, float* w_out, float* b_out, void* ws, hipStream_t s);
+size_t fit_ws_bytes(int32_t count, int32_t f_in, int32_t f_out);
+// `count` problems of one shape; x, y, w_out, b_out are host arrays of device
+// pointers; status (host, may be null) receives each problem's status.
+int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy,
+               int32_t in_f32, int64_t n_rows, int32_t f_in, int32_t f_out, double lam_abs,
+               double lam_rel, int32_t fit_intercept, float* const* w_out, float* const* b_out,
+               int32_t* status, void* ws, hipStream_t s);
 
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();

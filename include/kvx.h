@@ -222,6 +222,31 @@ int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_
                   void* stream);
 
 /* ------------------------------------------------------------------------
+ * The same fit for `count` problems of one shape (the maps of every receiver
+ * layer and role of one model pair, same source), with the results of
+ * `count` calls of kvx_fit_ridge.  The serial chain of the fp64 solve (one
+ * diagonal factor after another) then runs once for all problems, each of
+ * its launches covering every problem.
+ *
+ * x, y, w_out, b_out: HOST arrays of `count` device pointers, each as in
+ *   kvx_fit_ridge (b_out may be NULL without fit_intercept).
+ * status: host int32 [count] or NULL; receives KVX_OK or KVX_ERR_NOT_SPD
+ *   per problem.
+ * workspace: device scratch of kvx_fit_ridge_batched_workspace_size(count,
+ *   f_in, f_out) bytes (the Gram partials, shared, plus about
+ *   8 (f_in + 1)(f_in + f_out) bytes per problem).
+ * Returns KVX_ERR_NOT_SPD when any problem is not positive definite (the
+ * others are still solved), otherwise as kvx_fit_ridge.  Synchronises
+ * `stream` once.
+ * ---------------------------------------------------------------------- */
+size_t kvx_fit_ridge_batched_workspace_size(int32_t count, int32_t f_in, int32_t f_out);
+int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, const void* const* y,
+                          int64_t ldy, int32_t in_dtype, int64_t n_rows, int32_t f_in,
+                          int32_t f_out, double lambda_abs, double lambda_rel,
+                          int32_t fit_intercept, float* const* w_out, float* const* b_out,
+                          int32_t* status, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Rank-r fold ("Prefill-Free ...", Methodology 3: low-rank corrections folded
  * into one fixed affine map per layer and role).
  *

@@ -501,6 +501,59 @@ def test_fit_rejects_singular_gram():
     assert ei.value.status == kvx.ERR_NOT_SPD
 
 
+def test_fit_batched_matches_single_and_oracle():
+    """Three layers fitted by one batched call: each result equals the
+    single-problem call bit for bit (the same kernels, tile by tile) and the
+    oracle's fit within the tolerance."""
+    say("batched ridge fit, layers 0 / 15 / 31, 4096 calibration rows")
+    c = fit_case(4096)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    tm = dev_i32(tmap_o)
+    layers = (0, 15, 31)
+    xs = [kvx.gather_features(c["k_send"], tm, taps[l]) for l in layers]
+    ys = [c["recv_k"][l].reshape(4096, 1024) for l in layers]
+    st = []
+    ws, _ = kvx.fit_ridge_batched(xs, ys, lambda_rel=1e-3, status=st)
+    assert st == [kvx.OK] * 3
+    for l, x, y, w in zip(layers, xs, ys, ws):
+        w1, _ = kvx.fit_ridge(x, y, lambda_rel=1e-3)
+        assert torch.equal(w, w1), f"layer {l}: batched and single fits differ"
+        wo, _, _ = O.ridge_fit(O.features(c["k_send"], tmap_o, taps[l]),
+                               O.as_f64(c["recv_k"][l]).reshape(4096, 1024), lam_rel=1e-3)
+        err = O.rel_err(w.cpu().numpy(), wo.T)
+        say(f"  layer {l}: W max|err|/RMS = {err:.3e}")
+        assert err <= TOL_BF16
+
+
+def test_fit_batched_flags_each_problem():
+    """lambda = 0 with one rank-deficient problem (half its feature columns
+    zero: exact zero pivots) next to a well-posed one: the status of each is
+    reported, the well-posed one is still solved (vs the oracle and the
+    single-problem call), with the bias of the centred fit."""
+    say("batched ridge fit with one singular problem, intercept")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(91)
+    n, f_in, f_out = 1024, 128, 64
+    x0 = torch.randn((n, f_in), generator=g, device=DEV).to(torch.bfloat16)
+    x1 = torch.randn((n, f_in), generator=g, device=DEV).to(torch.bfloat16)
+    x1[:, 64:] = 0
+    ys = [torch.randn((n, f_out), generator=g, device=DEV).to(torch.bfloat16) for _ in range(2)]
+    st = []
+    ws, bs = kvx.fit_ridge_batched([x0, x1], ys, fit_intercept=True, status=st)
+    assert st == [kvx.OK, kvx.ERR_NOT_SPD]
+    w1, b1 = kvx.fit_ridge(x0, ys[0], fit_intercept=True)
+    assert torch.equal(ws[0], w1) and torch.equal(bs[0], b1)
+    wo, bo, _ = O.ridge_fit(O.as_f64(x0), O.as_f64(ys[0]), fit_intercept=True)
+    err_w = O.rel_err(ws[0].cpu().numpy(), wo.T)
+    err_b = O.rel_err(bs[0].cpu().numpy(), bo)
+    say(f"  W max|err|/RMS = {err_w:.3e}, b {err_b:.3e}")
+    assert err_w <= TOL_F32 and err_b <= TOL_F32
+    with pytest.raises(kvx.KvxError) as ei:
+        kvx.fit_ridge_batched([x0, x1], ys, fit_intercept=True)
+    assert ei.value.status == kvx.ERR_NOT_SPD
+
+
 def test_fit_full_size_normal_equations():
     """65536 calibration rows, one layer: the fitted W satisfies the normal
     equations (G + lambda I) W = X^T Y, checked on random probe vectors with
