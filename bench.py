@@ -24,11 +24,15 @@ same with keys stored rotated on both sides; ``also_cfg3``,
 ``also_fp32_maps`` and ``also_fit`` other flattened settings and the ridge
 fit.
 
-Profiling helpers: ``--calibration-copy`` first runs a plain 1 GiB device
-copy (1 GiB read + 1 GiB written) so a rocprofv3 counter run of the same
-command sees a kernel of known traffic; ``--pmc-summary FETCH.csv WRITE.csv``
-turns the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run into the
-per-launch traffic summary kept under profiles/.
+Profiling helpers: ``--no-also`` runs the headline step alone and
+``--perhead-only`` the per-head workload alone, so each kernel is profiled on
+one workload; ``--calibration-copy`` first runs a plain 1 GiB device copy
+(1 GiB read + 1 GiB written) so a rocprofv3 counter run of the same command
+sees a kernel of known traffic; ``--pmc-summary FETCH.csv WRITE.csv`` turns
+the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run into the per-launch
+traffic summary kept under profiles/, ``--trace-summary STATS.csv LOG`` a
+kernel-trace statistics file and the bench output of the same run into the
+trace summary.
 """
 from __future__ import annotations
 
@@ -51,6 +55,7 @@ from cross_model_kv_kvx_amd import kvx, synth  # noqa: E402
 
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_FP64_TFLOPS = 78.6          # MI355X dense fp64 (matrix and vector)
 CALIB_BYTES = 1 << 30            # bytes read (and written) by the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -60,6 +65,17 @@ KERNEL_SOURCES = {
 TRAFFIC_FILES = {
     "flat_gemm_kernel": "flat_gemm_kernel__crossfamily_rope_32k__traffic.md",
     "perhead_kernel": "perhead_kernel__32to80_4k__traffic.md",
+}
+TRACE_FILES = {
+    "flat_gemm_kernel": "flat_gemm_kernel__crossfamily_rope_32k__trace.md",
+    "perhead_kernel": "perhead_kernel__32to80_4k__trace.md",
+}
+# bench.py arguments of the profiled runs of each kernel: the headline step
+# alone, or the per-head workload alone, so every dispatch of the kernel in
+# the profile belongs to the workload the summary names
+PROFILE_ARGS = {
+    "flat_gemm_kernel": ("flat", "--steps 5 --warmup 1 --no-cpu-baseline --no-also"),
+    "perhead_kernel": ("ph", "--perhead-only"),
 }
 
 
@@ -133,16 +149,17 @@ def pmc_summary(fetch_csv, write_csv):
         wb = np.array(w[kernel]) * kw
         n = min(fb.size, wb.size)
         tot = fb[:n] + wb[:n]
+        tag, bargs = PROFILE_ARGS[kernel]
         out[kernel] = (f"# HBM traffic: {kernel}\n\n"
                        f"source hash: `{source_hash(kernel)}`\n\n"
                        "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths "
                        "relative to the repository), then this summary:\n\n```\n"
-                       "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch -o fetch --output-format csv -- "
-                       "python3 bench.py --calibration-copy --steps 2 --warmup 1 --no-cpu-baseline\n"
-                       "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write -o write --output-format csv -- "
-                       "python3 bench.py --calibration-copy --steps 2 --warmup 1 --no-cpu-baseline\n"
-                       "python3 bench.py --pmc-summary gpurun_out/prof/fetch/fetch_counter_collection.csv "
-                       "gpurun_out/prof/write/write_counter_collection.csv\n```\n\n"
+                       f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/{tag}_fetch -o fetch --output-format csv -- "
+                       f"python3 bench.py --calibration-copy {bargs}\n"
+                       f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/{tag}_write -o write --output-format csv -- "
+                       f"python3 bench.py --calibration-copy {bargs}\n"
+                       f"python3 bench.py --pmc-summary gpurun_out/prof/{tag}_fetch/fetch_counter_collection.csv "
+                       f"gpurun_out/prof/{tag}_write/write_counter_collection.csv\n```\n\n"
                        f"Counters: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one rocprofv3 run each.\n"
                        f"Calibration: a plain copy of {CALIB_BYTES} bytes read and written reads "
                        f"FETCH_SIZE {np.median(f['copy']):.0f} B and WRITE_SIZE {np.median(w['copy']):.0f} B, "
@@ -150,6 +167,43 @@ def pmc_summary(fetch_csv, write_csv):
                        f"| dispatches | fetch bytes (mean) | write bytes (mean) |\n|---|---|---|\n"
                        f"| {n} | {fb[:n].mean():.4g} | {wb[:n].mean():.4g} |\n\n"
                        f"HBM bytes per launch (mean): `{tot.mean():.6g}`\n")
+    return out
+
+
+def trace_summary(stats_csv, bench_log):
+    """Markdown summaries of a rocprofv3 --kernel-trace --stats run of one of
+    the profiled commands: the kernel statistics as rocprofv3 wrote them and
+    the live HIP-event launch time that bench.py printed in the same run."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    line = next(l for l in open(bench_log) if l.startswith("{"))
+    res = json.loads(line)
+    out = {}
+    for kernel in ("flat_gemm_kernel", "perhead_kernel"):
+        mine = [r for r in rows if f"kvx::{kernel}" in r["Name"]]
+        if not mine:
+            continue
+        tag, bargs = PROFILE_ARGS[kernel]
+        calls = sum(int(r["Calls"]) for r in mine)
+        total = sum(float(r["TotalDurationNs"]) for r in mine)
+        roof = res["roofline"] if kernel == "flat_gemm_kernel" else res["also"]["roofline"]
+        tab = "\n".join(f"| {r['Name'].removeprefix('void ')[:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                        f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} |"
+                        for r in rows[:14])
+        out[kernel] = (f"# Kernel trace: {kernel}\n\n"
+                       f"source hash: `{source_hash(kernel)}`\n\n"
+                       "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths "
+                       "relative to the repository), then this summary:\n\n```\n"
+                       f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof/{tag}_trace -o trace --output-format csv "
+                       f"-- python3 bench.py {bargs} > gpurun_out/prof/{tag}_trace.log\n"
+                       f"python3 bench.py --trace-summary gpurun_out/prof/{tag}_trace/trace_kernel_stats.csv "
+                       f"gpurun_out/prof/{tag}_trace.log\n```\n\n"
+                       "Kernel statistics of the run (all dispatches, input generation and warm-up included; "
+                       "top 14):\n\n| kernel | calls | avg us | min us | max us | % time |\n|---|---|---|---|---|---|\n"
+                       f"{tab}\n\n"
+                       f"{kernel}: {calls} dispatches, mean {total / calls / 1e3:.1f} us per dispatch.\n\n"
+                       f"Same run, live HIP-event timing in bench.py: {roof['launch_ms'] * 1e3:.1f} us per launch "
+                       f"({roof['achieved']:.1f} {roof['unit']} algorithmic, {100 * roof['frac']:.1f}% of "
+                       f"{roof['peak']:.0f}).\n")
     return out
 
 
@@ -298,35 +352,56 @@ def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8):
                          "executed_flops_per_launch": flops * (2 if fp32_maps else 1), "traffic": None}}
 
 
-def fit_measure(dev, reps=3):
-    """Closed-form ridge fit of one (layer, role) of the calibration setting:
-    65536 rows of 3072 gathered features -> 1024 outputs, lambda = 1e-3 tr/3072."""
-    n, layer = 65536, 20
+def fit_measure(dev, reps=2):
+    """Closed-form ridge fit of the whole calibration setting in one batched
+    call: 32 receiver layers x K, V = 64 problems, each 65536 rows of 3072
+    gathered features (taps -4/0/+4 of the 36 sender layers) -> 1024 outputs,
+    lambda = 1e-3 tr(G)/3072; and one problem alone for comparison."""
+    n = 65536
     send_end, recv_end = synth.token_ends(n, 5)
     shp = synth.CacheShape(36, len(send_end), 8, 128)
-    k_send = synth.sender_cache(shp, 500, dev)
-    y = synth.receiver_cache(synth.CacheShape(1, n, 8, 128), 550, dev)[0].reshape(n, 1024)
     taps = kvx.layer_map(36, 32, 3, 4)
     tm = kvx.align_tokens(torch.as_tensor(send_end, device=dev), torch.as_tensor(recv_end, device=dev))
-    x = kvx.gather_features(k_send, tm, taps[layer])
-    del k_send
-    ws = torch.empty(kvx.lib().kvx_fit_ridge_workspace_size(3072, 1024), dtype=torch.uint8, device=dev)
-    ms = []
-    for i in range(reps + 1):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        kvx.fit_ridge(x, y, lambda_rel=1e-3, workspace=ws)   # synchronous (reads the SPD flag)
-        if i >= 1:
-            ms.append((time.perf_counter() - t0) * 1e3)
-    t = float(np.mean(ms))
-    gram = 2.0 * n * (3072 * 3073 / 2 + 3072 * 1024)      # G (one triangle) and X^T Y
-    solve = 3072.0 ** 3 / 3 + 2 * 3072.0 ** 2 * 1024      # Cholesky + two triangular solves (fp64)
-    return {"workload": "ridge fit, one layer and role: 65536 x 3072 bf16 features -> 1024 outputs, "
-                        "lambda = 1e-3 tr(G)/3072", "fit_ms": t, "problems_per_full_fit": 64,
-            "gram_flops": gram, "solve_flops_fp64": solve,
+    xs, ys = [], []
+    for r in range(2):
+        send = synth.sender_cache(shp, 500 + r, dev)
+        recv = synth.receiver_cache(synth.CacheShape(32, n, 8, 128), 550 + r, dev)
+        for l in range(32):
+            xs.append(kvx.gather_features(send, tm, taps[l]))
+            ys.append(recv[l].reshape(n, 1024))
+        del send, recv
+    count = len(xs)
+    w_outs = [torch.empty((1024, 3072), dtype=torch.float32, device=dev) for _ in range(count)]
+
+    def timed(c):
+        ws = torch.empty(kvx.lib().kvx_fit_ridge_batched_workspace_size(c, 3072, 1024), dtype=torch.uint8,
+                         device=dev)
+        ms = []
+        for i in range(reps + 1):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            kvx.fit_ridge_batched(xs[:c], ys[:c], lambda_rel=1e-3, w_outs=w_outs[:c], workspace=ws)  # synchronous
+            if i >= 1:
+                ms.append((time.perf_counter() - t0) * 1e3)
+        del ws
+        torch.cuda.empty_cache()
+        return float(np.mean(ms))
+
+    t_one = timed(1)
+    t = timed(count)
+    gram = count * 2.0 * n * (3072 * 3073 / 2 + 3072 * 1024)      # G (one triangle) and X^T Y, bf16 MFMA
+    solve = count * (3072.0 ** 3 / 3 + 2 * 3072.0 ** 2 * 1024)    # Cholesky + two triangular solves, fp64
+    t_roof = gram / (PEAK_MFMA_BF16_TFLOPS * 1e12) + solve / (PEAK_FP64_TFLOPS * 1e12)
+    return {"workload": f"ridge fit of all {count} maps (32 layers x K,V) in one call: 65536 x 3072 bf16 "
+                        "features -> 1024 outputs each, lambda = 1e-3 tr(G)/3072",
+            "fit_ms": t, "problems": count, "ms_per_problem": t / count, "one_problem_alone_ms": t_one,
+            "calibration_tokens_per_s": count * n / (t * 1e-3),
+            "gram_flops": gram, "solve_flops_fp64": solve, "roofline_ms": t_roof * 1e3,
             "roofline": {"bound": "mfma", "achieved": gram / (t * 1e-3) / 1e12, "peak": PEAK_MFMA_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": gram / (t * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
-                         "note": "Gram FLOPs over the whole fit time (Gram + fp64 solve)", "traffic": None}}
+                         "unit": "TFLOP/s", "frac": t_roof / (t * 1e-3),
+                         "note": "frac = (Gram FLOPs at the bf16 peak + solve FLOPs at the fp64 peak) / "
+                                 "measured time; achieved = Gram FLOPs over the whole fit time",
+                         "traffic": None}}
 
 
 def main():
@@ -338,10 +413,15 @@ def main():
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"))
+    ap.add_argument("--perhead-only", action="store_true",
+                    help="measure the per-head workload alone (profiling runs of the per-head kernel)")
     args = ap.parse_args()
-    if args.pmc_summary:
-        for kernel, text in pmc_summary(*args.pmc_summary).items():
-            path = os.path.join(PROFILES, TRAFFIC_FILES[kernel])
+    if args.pmc_summary or args.trace_summary:
+        made = pmc_summary(*args.pmc_summary) if args.pmc_summary else trace_summary(*args.trace_summary)
+        files = TRAFFIC_FILES if args.pmc_summary else TRACE_FILES
+        for kernel, text in made.items():
+            path = os.path.join(PROFILES, files[kernel])
             with open(path, "w") as fh:
                 fh.write(text)
             print(f"wrote {path}")
@@ -355,6 +435,10 @@ def main():
     if args.calibration_copy:
         log("bench: calibration copy")
         calibration_copy(dev)
+    if args.perhead_only:
+        log("bench: per-head workload")
+        print(json.dumps({"also": perhead_measure(dev)}), flush=True)
+        return
     log("bench: building inputs")
     x = flat_inputs(dev)
     taps = kvx.layer_map(36, 32, 3, 4)
