@@ -452,7 +452,12 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
     if (n_rows > 0 && (!x[z] || !y[z])) return KVX_ERR_INVALID;
   }
   if (ldx < f_in || ldy < f_out) return KVX_ERR_SHAPE;
-  if (in_dtype == KVX_BF16 && ((f_in % 8) || (f_out % 8) || (ldx % 8) || (ldy % 8))) return KVX_ERR_UNSUPPORTED;
+  if (in_dtype == KVX_BF16) {
+    // bf16 rows are read in 16-byte pieces
+    if ((f_in % 8) || (f_out % 8) || (ldx % 8) || (ldy % 8)) return KVX_ERR_UNSUPPORTED;
+    for (int32_t z = 0; z < count; ++z)
+      if ((reinterpret_cast<uintptr_t>(x[z]) | reinterpret_cast<uintptr_t>(y[z])) % 16) return KVX_ERR_UNSUPPORTED;
+  }
   if (!workspace || ws_bytes < kvx_fit_ridge_batched_workspace_size(count, f_in, f_out)) return KVX_ERR_WORKSPACE;
   return launch_fit(count, x, ldx, y, ldy, in_dtype == KVX_F32, n_rows, f_in, f_out, lambda_abs, lambda_rel,
                     fit_intercept, w_out, b_out, status, workspace, static_cast<hipStream_t>(stream));

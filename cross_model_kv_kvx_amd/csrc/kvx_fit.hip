@@ -26,11 +26,13 @@
 
 namespace kvx {
 
-constexpr int GR_T = 256;     // Gram tile (features x features)
-constexpr int GR_BK = 64;     // rows per K step
-constexpr int GR_LDR = GR_BK + 8;
+constexpr int GR_T = 256;          // Gram tile (features x features)
+constexpr int GR_BK = 64;          // rows per K step
 constexpr int GR_MAX_SPLIT = 8;
-constexpr int CH_NB = 64;     // Cholesky block
+constexpr int GR_THREADS = 512;    // 8 waves, two per SIMD
+constexpr int GR_PART = GR_BK * GR_T;  // 16-bit elements of one ring part (32 KB)
+constexpr int GR_LD = 4;           // direct loads (1 KB each) per wave per part and step
+constexpr int CH_NB = 64;          // Cholesky block
 
 struct GramArgs {
   const uint16_t* x;
@@ -40,131 +42,204 @@ struct GramArgs {
   float* part;  // [split][f_in][f_in + f_out]
 };
 
-// 8 rows x 8 features of bf16 (one u32x4 per row) -> 8 features x 8 rows.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a = in[2 * w][c >> 1], b = in[2 * w + 1][c >> 1];
-      out[c][w] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
+// G = X^T X (tiles on and above the diagonal) and C = X^T Y over row splits,
+// fp32 partial sums per split (added in fp64 afterwards).  Persistent
+// workgroups of 8 waves, one per CU, take (split, tile) items; the block tile
+// is 256 x 256 features, the wave tile 64 x 128 from MFMA 32x32x16 bf16.
+// The K loop runs over the split's rows, 64 per step: the P part (64 rows x
+// the tile's 256 row features of X) and the Q part (64 rows x its 256 column
+// features of X or Y) are 32 KB each and go through a ring of five 32 KB LDS
+// parts (all 160 KB), Q one step and P two steps ahead of the matrix
+// instructions, filled by direct global->LDS 16-byte loads of whole 512-byte
+// row pieces kept row-major; 16-byte chunks are XOR-swizzled by 4 (row mod 4)
+// inside each row.  The operands want 8 consecutive rows of one feature per
+// lane: the transposing LDS read of gfx950 (ds_read_b64_tr_b16) gives a lane
+// 4 of them per instruction (in each group of 16 lanes, element e of lane t
+// is element t mod 4 of the 8 bytes that lane 4e + t/4 addressed; so lane s
+// addresses row s/4 at feature 4 (s mod 4) of a 4-row x 16-feature block and
+// lane t receives rows 0..3 of feature t), and the swizzle puts the 8 rows x
+// 64 bytes of one such read (two passes) in distinct banks.
+__device__ __forceinline__ int gr_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// Rows `row`..+3 and `row`+4..+7 of feature `feat` (transposed reads by the
+// lane addressing pattern above) as one 8 x bf16 operand, rows ascending.
+__device__ __forceinline__ u32x4 gr_frag(const uint16_t* part, int row, int feat) {
+  const char* b = reinterpret_cast<const char*>(part);
+  const char* a0 = b + row * 512 + 16 * gr_chunk(row, feat >> 3) + 2 * (feat & 7);
+  const char* a1 = b + (row + 4) * 512 + 16 * gr_chunk(row + 4, feat >> 3) + 2 * (feat & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
-__global__ __launch_bounds__(256, 1) void gram_kernel(const GramArgs g) {
-  constexpr int STAGE = 2 * GR_T * GR_LDR;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+struct GrItem {
+  __amdgpu_buffer_rsrc_t pr, qr;  // split rows x tile features of P and Q
+  uint32_t p_pitch, q_pitch;      // row pitch (bytes)
+  uint32_t p_off[GR_LD], q_off[GR_LD];  // this lane's row * pitch + chunk * 16 inside a step
+  int32_t nk;                     // steps of the split
+};
 
-  const int32_t per = g.n_g + g.n_c;
-  const int32_t sidx = blockIdx.x / per;
-  int32_t t = blockIdx.x % per;
-  int32_t bi, bj;
-  bool is_c;
-  if (t < g.n_g) {  // upper-triangle tile index -> (bi, bj), bi <= bj
-    is_c = false;
-    bi = 0;
-    int32_t rowlen = g.nbi;
-    while (t >= rowlen) {
-      t -= rowlen;
-      ++bi;
-      --rowlen;
-    }
-    bj = bi + t;
-  } else {
-    is_c = true;
-    t -= g.n_g;
-    bi = t / g.nbc;
-    bj = t % g.nbc;
-  }
-  const int64_t k_begin = static_cast<int64_t>(sidx) * g.rows_per_split;
-  int64_t k_end = k_begin + g.rows_per_split;
-  if (k_end > g.n_rows) k_end = g.n_rows;
-  const int32_t i0 = bi * GR_T, j0 = bj * GR_T;
-  const uint16_t* q = is_c ? g.y : g.x;
-  const int64_t ldq = is_c ? g.ldy : g.ldx;
-  const int32_t fq = is_c ? g.f_out : g.f_in;
+// Part of step k (64 rows) into `part`: load i of wave w covers part rows
+// 2 (4w + i) and +1, lane j -> row + j/32, physical chunk j mod 32.  Steps
+// past the end read nothing.
+__device__ __forceinline__ void gr_issue(__amdgpu_buffer_rsrc_t r, uint32_t pitch, const uint32_t (&off)[GR_LD], int k,
+                                         int nk, uint16_t* part) {
+  const int wave = wave_id();
+  const __amdgpu_buffer_rsrc_t rr = k < nk ? r : buf_rsrc(nullptr, 0);
+  const uint32_t base = static_cast<uint32_t>(k) * GR_BK * pitch;
+#pragma unroll
+  for (int i = 0; i < GR_LD; ++i) dma16(rr, base + off[i], 0, part + (wave * GR_LD + i) * 512);
+}
 
-  const int fi = tid & 31;  // feature group (8 features)
-  const int kb = tid >> 5;  // row group (8 rows)
-  u32x4 rp[8], rq[8];
-  auto load = [&](int64_t k0) {
+// One step: 4 x (2 P + 4 Q fragments, 8 MFMAs).
+__device__ __forceinline__ void gr_compute(const uint16_t* pp, const uint16_t* pq, f32x16 (&acc)[2][4]) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave & 3, wn = wave >> 2;
+  // lane of a 16-lane group g: the MFMA operand of lane l covers features
+  // l mod 32 and rows 8 (l / 32) .. +7
+  const int g = lane >> 4, s = lane & 15;
+  const int r0 = 8 * (g >> 1) + (s >> 2);
+  const int f0 = 16 * (g & 1) + 4 * (s & 3);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t k = k0 + kb * 8 + e;
-      const int32_t fa = i0 + fi * 8, fb = j0 + fi * 8;
-      rp[e] = (k < k_end && fa < g.f_in) ? *reinterpret_cast<const u32x4*>(g.x + k * g.ldx + fa) : u32x4{0, 0, 0, 0};
-      rq[e] = (k < k_end && fb < fq) ? *reinterpret_cast<const u32x4*>(q + k * ldq + fb) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store = [&](int stage) {
-    uint16_t* Ps = smem + stage * STAGE;
-    uint16_t* Qs = Ps + GR_T * GR_LDR;
-    u32x4 tp[8], tq[8];
-    transpose8x8(rp, tp);
-    transpose8x8(rq, tq);
+  for (int kk = 0; kk < GR_BK / 16; ++kk) {
+    u32x4 af[2], bf[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      *reinterpret_cast<u32x4*>(Ps + (fi * 8 + c) * GR_LDR + kb * 8) = tp[c];
-      *reinterpret_cast<u32x4*>(Qs + (fi * 8 + c) * GR_LDR + kb * 8) = tq[c];
-    }
-  };
-
-  f32x16 acc[4][4];
+    for (int mi = 0; mi < 2; ++mi) af[mi] = gr_frag(pp, 16 * kk + r0, wm * 64 + mi * 32 + f0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int ni = 0; ni < 4; ++ni) bf[ni] = gr_frag(pq, 16 * kk + r0, wn * 128 + ni * 32 + f0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int64_t nk = (k_end > k_begin) ? (k_end - k_begin + GR_BK - 1) / GR_BK : 0;
-  if (nk > 0) {
-    load(k_begin);
-    store(0);
-    __syncthreads();
-  }
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int stage = static_cast<int>(ks & 1);
-    if (ks + 1 < nk) load(k_begin + (ks + 1) * GR_BK);
-    const uint16_t* Ps = smem + stage * STAGE;
-    const uint16_t* Qs = Ps + GR_T * GR_LDR;
-#pragma unroll
-    for (int kk = 0; kk < GR_BK / 16; ++kk) {
-      u32x4 af[4], bfr[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const u32x4*>(Ps + (wm * 128 + mi * 32 + frag_row) * GR_LDR + kk * 16 + frag_k);
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        bfr[ni] = *reinterpret_cast<const u32x4*>(Qs + (wn * 128 + ni * 32 + frag_row) * GR_LDR + kk * 16 + frag_k);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[mi]),
-                                                                __builtin_bit_cast(bf16x8, bfr[ni]), acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[mi]),
+                                                              __builtin_bit_cast(bf16x8, bf[ni]), acc[mi][ni], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void gr_sync() {
+  KVX_WAIT_VM(GR_LD);
+  KVX_COMPILER_FENCE();
+  __builtin_amdgcn_s_barrier();
+  KVX_COMPILER_FENCE();
+}
+
+// P of step k in part 2k mod 5, Q in part 2k+1 mod 5; the step issues Q of
+// k+1 and P of k+2 into the two parts of step k-1.
+#define GR_STEP(K, PA, PB, NB, NA, LIVE)                   \
+  gr_sync();                                               \
+  gr_issue(it.qr, it.q_pitch, it.q_off, (K) + 1, it.nk, NB); \
+  gr_issue(it.pr, it.p_pitch, it.p_off, (K) + 2, it.nk, NA); \
+  if (LIVE) gr_compute(PA, PB, acc);
+
+__global__ __attribute__((amdgpu_flat_work_group_size(GR_THREADS, GR_THREADS), amdgpu_waves_per_eu(2, 2))) void
+gram_kernel(const GramArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint16_t p0[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p1[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p2[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p3[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p4[GR_PART];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave & 3, wn = wave >> 2;
+  const int32_t per = g.n_g + g.n_c;
+  const int64_t T = static_cast<int64_t>(g.split) * per;
+  const int32_t G = gridDim.x;
+  // consecutive items go to the workgroups of one XCD (dispatch is round
+  // robin over the 8 XCDs)
+  const int32_t slot = (G % 8 == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int64_t ldp = static_cast<int64_t>(g.f_in) + g.f_out;
+
+  for (int64_t t = slot; t < T; t += G) {
+    const int32_t sidx = static_cast<int32_t>(t / per);
+    int32_t tt = static_cast<int32_t>(t % per);
+    int32_t bi, bj;
+    bool is_c;
+    if (tt < g.n_g) {  // upper-triangle tile index -> (bi, bj), bi <= bj
+      is_c = false;
+      bi = 0;
+      int32_t rowlen = g.nbi;
+      while (tt >= rowlen) {
+        tt -= rowlen;
+        ++bi;
+        --rowlen;
+      }
+      bj = bi + tt;
+    } else {
+      is_c = true;
+      tt -= g.n_g;
+      bi = tt / g.nbc;
+      bj = tt % g.nbc;
     }
-    if (ks + 1 < nk) store(stage ^ 1);
+    const int64_t k_begin = static_cast<int64_t>(sidx) * g.rows_per_split;
+    int64_t rows = g.n_rows - k_begin;
+    if (rows > g.rows_per_split) rows = g.rows_per_split;
+    if (rows < 0) rows = 0;
+    const int32_t i0 = bi * GR_T, j0 = bj * GR_T;
+    const uint16_t* q = is_c ? g.y : g.x;
+    const int64_t ldq = is_c ? g.ldy : g.ldx;
+    const int32_t fq = is_c ? g.f_out : g.f_in;
+
+    GrItem it;
+    it.p_pitch = static_cast<uint32_t>(2 * g.ldx);
+    it.q_pitch = static_cast<uint32_t>(2 * ldq);
+    // the range ends with the split's last row (features past the row's end
+    // come from the next row and only reach outputs that are not written)
+    it.pr = buf_rsrc(g.x + k_begin * g.ldx + i0, static_cast<uint32_t>(rows * 2 * g.ldx - 2 * i0));
+    it.qr = buf_rsrc(q + k_begin * ldq + j0, static_cast<uint32_t>(rows * 2 * ldq - 2 * j0));
+    if (rows == 0) {
+      it.pr = buf_rsrc(nullptr, 0);
+      it.qr = buf_rsrc(nullptr, 0);
+    }
+    it.nk = static_cast<int32_t>((rows + GR_BK - 1) / GR_BK);
+#pragma unroll
+    for (int i = 0; i < GR_LD; ++i) {
+      const int row = 2 * (wave * GR_LD + i) + (lane >> 5);
+      const int pc = gr_chunk(row, lane & 31);  // logical chunk of physical position lane % 32
+      it.p_off[i] = static_cast<uint32_t>(row) * it.p_pitch + 16u * pc;
+      it.q_off[i] = static_cast<uint32_t>(row) * it.q_pitch + 16u * pc;
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    if (it.nk > 0) {
+      gr_issue(it.pr, it.p_pitch, it.p_off, 0, it.nk, p0);
+      gr_issue(it.qr, it.q_pitch, it.q_off, 0, it.nk, p1);
+      gr_issue(it.pr, it.p_pitch, it.p_off, 1, it.nk, p2);
+      for (int k = 0; k < it.nk; k += 5) {
+        GR_STEP(k, p0, p1, p3, p4, true)
+        GR_STEP(k + 1, p2, p3, p0, p1, k + 1 < it.nk)
+        GR_STEP(k + 2, p4, p0, p2, p3, k + 2 < it.nk)
+        GR_STEP(k + 3, p1, p2, p4, p0, k + 3 < it.nk)
+        GR_STEP(k + 4, p3, p4, p1, p2, k + 4 < it.nk)
+      }
+      KVX_WAIT_VM(0);
+    }
+
+    float* part = g.part + static_cast<int64_t>(sidx) * g.f_in * ldp + (is_c ? g.f_in : 0);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t i = i0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int32_t j = j0 + wn * 128 + ni * 32 + (lane & 31);
+          if (i < g.f_in && j < fq) part[static_cast<int64_t>(i) * ldp + j] = acc[mi][ni][r];
+        }
+    // every wave is past its last step before the next item's loads land
     __syncthreads();
   }
-
-  const int64_t ldp = static_cast<int64_t>(g.f_in) + g.f_out;
-  float* part = g.part + static_cast<int64_t>(sidx) * g.f_in * ldp + (is_c ? g.f_in : 0);
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t i = i0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int32_t j = j0 + wn * 128 + ni * 32 + (lane & 31);
-        if (i < g.f_in && j < fq) part[static_cast<int64_t>(i) * ldp + j] = acc[mi][ni][r];
-      }
 }
+#undef GR_STEP
 
 // fp32 inputs: G, C and column sums in fp64 by plain loops (small fits).
 __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ x, int64_t ldx,
@@ -201,23 +276,65 @@ __global__ __launch_bounds__(256) void colsum_kernel(const void* __restrict__ m,
   out[c] = s;
 }
 
-// Sum of the split partials in fp64; G mirrored from its upper triangle.
+// Sum of the split partials in fp64 by 64 x 64 blocks of [G | C]: blocks of
+// G on and above the diagonal and every block of C are read row by row
+// (256-byte rows of each split); a block of G above the diagonal is also
+// written to its mirror through an LDS transpose, so every global access
+// walks rows.
+constexpr int RD_T = 64;
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int32_t split,
                                                           int32_t f_in, int32_t f_out, double* __restrict__ G,
                                                           double* __restrict__ C) {
+  __shared__ double tr[RD_T][RD_T + 1];
+  const int32_t nbi = (f_in + RD_T - 1) / RD_T;
+  const int32_t nbc = (f_out + RD_T - 1) / RD_T;
+  const int32_t n_g = nbi * (nbi + 1) / 2;
+  int32_t t = blockIdx.x;
+  int32_t bi, bj;
+  bool is_c;
+  if (t < n_g) {
+    is_c = false;
+    bi = 0;
+    int32_t rowlen = nbi;
+    while (t >= rowlen) {
+      t -= rowlen;
+      ++bi;
+      --rowlen;
+    }
+    bj = bi + t;
+  } else {
+    is_c = true;
+    t -= n_g;
+    bi = t / nbc;
+    bj = t % nbc;
+  }
   const int64_t ldp = static_cast<int64_t>(f_in) + f_out;
   const int64_t total = static_cast<int64_t>(f_in) * ldp;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int32_t i = static_cast<int32_t>(e / ldp);
-    const int32_t j = static_cast<int32_t>(e % ldp);
-    int64_t src;
-    if (j < f_in) src = (i <= j) ? (static_cast<int64_t>(i) * ldp + j) : (static_cast<int64_t>(j) * ldp + i);
-    else src = static_cast<int64_t>(i) * ldp + j;
-    double s = 0.0;
-    for (int32_t q = 0; q < split; ++q) s += static_cast<double>(part[static_cast<int64_t>(q) * total + src]);
-    if (j < f_in) G[static_cast<int64_t>(i) * f_in + j] = s;
-    else C[static_cast<int64_t>(i) * f_out + (j - f_in)] = s;
+  const int32_t fq = is_c ? f_out : f_in;
+  const int c = threadIdx.x & 63, r4 = threadIdx.x >> 6;
+  const int32_t j = bj * RD_T + c;
+#pragma unroll 4
+  for (int rr = 0; rr < RD_T; rr += 4) {
+    const int32_t i = bi * RD_T + rr + r4;
+    if (i < f_in && j < fq) {
+      const int64_t src = static_cast<int64_t>(i) * ldp + (is_c ? f_in : 0) + j;
+      double v = 0.0;
+      for (int32_t q = 0; q < split; ++q) v += static_cast<double>(part[static_cast<int64_t>(q) * total + src]);
+      if (is_c)
+        C[static_cast<int64_t>(i) * f_out + j] = v;
+      else
+        G[static_cast<int64_t>(i) * f_in + j] = v;
+      tr[rr + r4][c] = v;
+    }
+  }
+  if (is_c || bi == bj) return;
+  __syncthreads();
+  // mirror: G[j][i] for the block's columns j as rows
+#pragma unroll 4
+  for (int rr = 0; rr < RD_T; rr += 4) {
+    const int32_t jj = bj * RD_T + rr + r4;  // row of the mirror
+    const int32_t ii = bi * RD_T + c;        // column of the mirror
+    if (jj < f_in && ii < f_in) G[static_cast<int64_t>(jj) * f_in + ii] = tr[c][rr + r4];
   }
 }
 
@@ -346,6 +463,9 @@ constexpr int DG_T = 64;
 constexpr int DG_BK = 16;
 constexpr int DG_LD = DG_T + 16;
 
+// The next K chunk is read into registers while the current one is
+// multiplied, and an updated C tile is read before the K loop, so both
+// latencies overlap the matrix instructions.
 __global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
   const int32_t bm = blockIdx.y, bn = blockIdx.x;
   if (g.lower_only && bm < bn) return;
@@ -359,13 +479,9 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
   double* C = g.C + blockIdx.z * g.bsc;
   const bool a_k = g.sak == 1 && g.sam != 1;  // A read along k
   const bool b_k = g.sbk == 1 && g.sbn != 1;  // B read along k
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int32_t k0 = 0; k0 < g.K; k0 += DG_BK) {
-    double av[4], bv[4];
+
+  double av[4], bv[4];
+  auto load = [&](int32_t k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
@@ -376,7 +492,33 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
       const int32_t n = n0 + nb_, kq = k0 + kb;
       bv[q] = (n < g.N && kq < g.K) ? B[kq * g.sbk + n * g.sbn] : 0.0;
     }
-    __syncthreads();  // the previous step's fragment reads are done
+  };
+  // element r of lane l: row l/16 + 4r, column l%16 of its 16 x 16 block
+  auto row_of = [&](int i, int r) { return m0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r; };
+  auto col_of = [&](int j) { return n0 + wn * 32 + j * 16 + (lane & 15); };
+
+  f64x4 acc[2][2], cv[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+      cv[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    }
+  load(0);
+  if (!g.overwrite) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t m = row_of(i, r), n = col_of(j);
+          if (m < g.M && n < g.N) cv[i][j][r] = C[m * g.ldc + n];
+        }
+  }
+  for (int32_t k0 = 0; k0 < g.K; k0 += DG_BK) {
+    __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
@@ -384,6 +526,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
       Bs[b_k ? (e & 15) : (e >> 6)][b_k ? (e >> 4) : (e & 63)] = bv[q];
     }
     __syncthreads();
+    if (k0 + DG_BK < g.K) load(k0 + DG_BK);
 #pragma unroll
     for (int k4 = 0; k4 < DG_BK; k4 += 4) {
       // operands of MFMA 16x16x4: lane l holds A[l%16][l/16] and B[l/16][l%16]
@@ -399,21 +542,14 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
-  // element r of lane l: row l/16 + 4r, column l%16 of its 16 x 16 block
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int32_t m = m0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r;
-        const int32_t n = n0 + wn * 32 + j * 16 + (lane & 15);
-        if (m < g.M && n < g.N) {
-          if (g.overwrite)
-            C[m * g.ldc + n] = acc[i][j][r];
-          else
-            C[m * g.ldc + n] -= acc[i][j][r];
-        }
+        const int32_t m = row_of(i, r), n = col_of(j);
+        if (m < g.M && n < g.N) C[m * g.ldc + n] = g.overwrite ? acc[i][j][r] : cv[i][j][r] - acc[i][j][r];
       }
 }
 
@@ -518,19 +654,37 @@ static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int3
   g.nbc = static_cast<int32_t>(ceil_div(f_out, GR_T));
   g.n_g = g.nbi * (g.nbi + 1) / 2;
   g.n_c = g.nbi * g.nbc;
+  // row splits: the fewest that fill the persistent grid best (fewer
+  // partials to add up, longer K loops), each at least one step long
   const int cus = device_cu_count();
-  int split = static_cast<int>(ceil_div(2 * cus, g.n_g + g.n_c));
-  if (split > GR_MAX_SPLIT) split = GR_MAX_SPLIT;
+  const int64_t tiles = g.n_g + g.n_c;
+  int64_t split = 1;
+  double best = 0.0;
+  for (int64_t sp = 1; sp <= GR_MAX_SPLIT; ++sp) {
+    const int64_t items = sp * tiles;
+    const double eff = static_cast<double>(items) / static_cast<double>(ceil_div(items, cus) * cus);
+    if (eff > best + 1e-9) {
+      best = eff;
+      split = sp;
+    }
+  }
   const int64_t max_split = ceil_div(n_rows, GR_BK);
-  if (split > max_split) split = static_cast<int>(max_split > 0 ? max_split : 1);
-  if (split < 1) split = 1;
-  g.split = split;
+  if (split > max_split) split = max_split > 0 ? max_split : 1;
   g.rows_per_split = ceil_div(ceil_div(n_rows, split), GR_BK) * GR_BK;
+  if (g.rows_per_split > 0) split = ceil_div(n_rows, g.rows_per_split);
+  g.split = static_cast<int32_t>(split);
+  // a split's rows are addressed with 32-bit byte offsets
+  if (g.rows_per_split * 2 * (ldx > ldy ? ldx : ldy) >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
   g.part = part;
-  gram_kernel<<<static_cast<unsigned>(split * (g.n_g + g.n_c)), 256, 0, s>>>(g);
+  const int64_t items = split * tiles;
+  const unsigned grid = static_cast<unsigned>(items < cus ? items : cus);
+  gram_kernel<<<grid, GR_THREADS, 0, s>>>(g);
   KVX_LAUNCH_CHECK();
-  gram_reduce_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(part, split, f_in, f_out,
-                                                                                          G, C);
+  {
+    const int64_t nbi = ceil_div(f_in, RD_T), nbc = ceil_div(f_out, RD_T);
+    gram_reduce_kernel<<<static_cast<unsigned>(nbi * (nbi + 1) / 2 + nbi * nbc), 256, 0, s>>>(part, g.split, f_in,
+                                                                                               f_out, G, C);
+  }
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }

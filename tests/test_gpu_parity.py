@@ -554,6 +554,24 @@ def test_fit_batched_flags_each_problem():
     assert ei.value.status == kvx.ERR_NOT_SPD
 
 
+@pytest.mark.parametrize("n,f_in,ld_pad,f_out", [(1000, 264, 16, 72), (77, 64, 0, 8), (4160, 512, 8, 256)])
+def test_fit_ragged_shapes(n, f_in, ld_pad, f_out):
+    """bf16 fits whose sizes leave partial tiles: rows not a multiple of the
+    64-row step (and fewer rows than one split per CU), features not a
+    multiple of the 256-wide tile, padded row strides."""
+    say(f"ridge fit n={n} f_in={f_in} (row stride {f_in + ld_pad}) f_out={f_out}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(n + f_in)
+    xb = torch.randn((n, f_in + ld_pad), generator=g, device=DEV).to(torch.bfloat16)
+    x = xb[:, :f_in]
+    y = torch.randn((n, f_out), generator=g, device=DEV).to(torch.bfloat16)
+    w, _ = kvx.fit_ridge(x, y, lambda_rel=1e-3)
+    wo, _, _ = O.ridge_fit(O.as_f64(x), O.as_f64(y), lam_rel=1e-3)
+    err = O.rel_err(w.cpu().numpy(), wo.T)
+    say(f"  W max|err|/RMS = {err:.3e}")
+    assert err <= TOL_F32
+
+
 def test_fit_full_size_normal_equations():
     """65536 calibration rows, one layer: the fitted W satisfies the normal
     equations (G + lambda I) W = X^T Y, checked on random probe vectors with
