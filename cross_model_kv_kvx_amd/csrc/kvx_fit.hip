@@ -12,7 +12,10 @@
 //   3. blocked Cholesky G + lambda I = L L^T in fp64 (64-wide blocks: diagonal
 //      factor and its inverse by one wave, panel triangular solve and
 //      trailing update as fp64 matrix-core products), then L Z = C and
-//      L^T W = Z by blocks;
+//      L^T W = Z by 256-row blocks with the inverses of the 256-wide
+//      diagonal blocks (assembled from the 64-wide ones by block
+//      substitution), so the right-hand sides are read and written 12
+//      rather than 48 times;
 //   4. W written output-major in fp32, b = mean_y - mean_x W.
 // Several problems of one shape (the maps of every layer and role) are
 // fitted by one call: steps 1, 2 and 4 run problem by problem (each fills
@@ -442,13 +445,15 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
 // C[M x N] -= A * B (overwrite = 0) or C = A * B (overwrite = 1) in fp64 on
 // matrix cores, for a batch of problems (blockIdx.z; the operands of problem
 // z start bsa, bsb, bsc elements after those of problem z-1), with
-// A(m,k) = A[m*sam + k*sak] and B(k,n) = B[k*sbk + n*sbn].  64 x 64 tiles;
-// four waves of 32 x 32, each from 2 x 2 MFMA 16x16x4 fp64 blocks; K in steps
-// of 16 through LDS as [k][m] and [k][n] (global elements are read along the
-// operand's unit-stride index; rows padded so the 16-lane row pieces of a
-// fragment read fall in distinct banks).  A workgroup reads all of its A rows
-// and B columns before it writes its tile, so C may alias A when N <= 64 or B
-// when M <= 64.  lower_only skips tiles strictly above the diagonal.
+// A(m,k) = A[m*sam + k*sak] and B(k,n) = B[k*sbk + n*sbn].  Block tiles of
+// 2 WT x 2 WT; four waves of WT x WT, each from MFMA 16x16x4 fp64 blocks; K in
+// chunks of 16 through LDS as [k][m] and [k][n] (global elements are read
+// along the operand's unit-stride index; rows padded so the 16-lane row
+// pieces of a fragment read fall in distinct banks); the next chunk is read
+// into registers while the current one is multiplied.  A workgroup reads all
+// of its A rows and B columns before it writes its tile, so C may alias A when
+// N <= 2 WT or B when M <= 2 WT.  lower_only skips tiles strictly above the
+// diagonal.
 struct DgArgs {
   int32_t M, N, K;
   const double* A;
@@ -459,71 +464,82 @@ struct DgArgs {
   int64_t ldc, bsc;
   int32_t lower_only, overwrite;
 };
-constexpr int DG_T = 64;
 constexpr int DG_BK = 16;
-constexpr int DG_LD = DG_T + 16;
 
-// The next K chunk is read into registers while the current one is
-// multiplied, and an updated C tile is read before the K loop, so both
-// latencies overlap the matrix instructions.
-__global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
+// WT = 32: 64 x 64 block tiles (small products), the updated C tile read
+// before the K loop; WT = 64: 128 x 128 block tiles (large products, long K).
+// AK / BK: A / B read along k (unit stride in k), else along m / n.
+template <int WT, bool AK, bool BK>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WT == 32 ? 4 : 2, 8))) void
+dgemm_kernel(const DgArgs g) {
+  constexpr int BT = 2 * WT;           // block tile
+  constexpr int LD = BT + 16;          // LDS row (doubles): 16-lane row pieces in distinct banks
+  constexpr int NQ = BT * DG_BK / 256; // elements of A (and of B) per thread and chunk
+  constexpr int NF = WT / 16;          // MFMA blocks per wave and dimension
+  constexpr bool PRE_C = WT == 32;
   const int32_t bm = blockIdx.y, bn = blockIdx.x;
   if (g.lower_only && bm < bn) return;
-  __shared__ double As[DG_BK][DG_LD];
-  __shared__ double Bs[DG_BK][DG_LD];
+  __shared__ double As[DG_BK][LD];
+  __shared__ double Bs[DG_BK][LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int32_t m0 = bm * DG_T, n0 = bn * DG_T;
+  const int32_t m0 = bm * BT, n0 = bn * BT;
   const double* A = g.A + blockIdx.z * g.bsa;
   const double* B = g.B + blockIdx.z * g.bsb;
   double* C = g.C + blockIdx.z * g.bsc;
-  const bool a_k = g.sak == 1 && g.sam != 1;  // A read along k
-  const bool b_k = g.sbk == 1 && g.sbn != 1;  // B read along k
-
-  double av[4], bv[4];
+  constexpr bool a_k = AK, b_k = BK;
+  // this thread's elements of a chunk: fixed row / column, k offset 0..15;
+  // offsets inside one problem's operands are below 2^31 elements
+  int32_t oa[NQ], ob[NQ];
+  uint32_t va = 0, vb = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = tid + 256 * q;
+    const int ma = a_k ? (e >> 4) : (e % BT), ka = a_k ? (e & 15) : (e / BT);
+    if (m0 + ma < g.M) va |= 1u << q;
+    oa[q] = static_cast<int32_t>((m0 + ma) * g.sam + ka * g.sak);
+    const int nb_ = b_k ? (e >> 4) : (e % BT), kb = b_k ? (e & 15) : (e / BT);
+    if (n0 + nb_ < g.N) vb |= 1u << q;
+    ob[q] = static_cast<int32_t>((n0 + nb_) * g.sbn + kb * g.sbk);
+  }
+  double av[NQ], bv[NQ];
   auto load = [&](int32_t k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
-      const int ma = a_k ? (e >> 4) : (e & 63), ka = a_k ? (e & 15) : (e >> 6);
-      const int32_t m = m0 + ma, k = k0 + ka;
-      av[q] = (m < g.M && k < g.K) ? A[m * g.sam + k * g.sak] : 0.0;
-      const int nb_ = b_k ? (e >> 4) : (e & 63), kb = b_k ? (e & 15) : (e >> 6);
-      const int32_t n = n0 + nb_, kq = k0 + kb;
-      bv[q] = (n < g.N && kq < g.K) ? B[kq * g.sbk + n * g.sbn] : 0.0;
+      const int ka = a_k ? (e & 15) : (e / BT), kb = b_k ? (e & 15) : (e / BT);
+      av[q] = ((va >> q) & 1u) && k0 + ka < g.K ? A[oa[q] + static_cast<int64_t>(k0) * g.sak] : 0.0;
+      bv[q] = ((vb >> q) & 1u) && k0 + kb < g.K ? B[ob[q] + static_cast<int64_t>(k0) * g.sbk] : 0.0;
     }
   };
   // element r of lane l: row l/16 + 4r, column l%16 of its 16 x 16 block
-  auto row_of = [&](int i, int r) { return m0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r; };
-  auto col_of = [&](int j) { return n0 + wn * 32 + j * 16 + (lane & 15); };
+  auto row_of = [&](int i, int r) { return m0 + wm * WT + i * 16 + (lane >> 4) + 4 * r; };
+  auto col_of = [&](int j) { return n0 + wn * WT + j * 16 + (lane & 15); };
 
-  f64x4 acc[2][2], cv[2][2];
+  f64x4 acc[NF][NF], cv[PRE_C ? NF : 1][PRE_C ? NF : 1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NF; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-      cv[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-    }
+    for (int j = 0; j < NF; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
   load(0);
-  if (!g.overwrite) {
+  if constexpr (PRE_C) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NF; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t m = row_of(i, r), n = col_of(j);
-          if (m < g.M && n < g.N) cv[i][j][r] = C[m * g.ldc + n];
+          cv[i][j][r] = (!g.overwrite && m < g.M && n < g.N) ? C[m * g.ldc + n] : 0.0;
         }
   }
   for (int32_t k0 = 0; k0 < g.K; k0 += DG_BK) {
     __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
-      As[a_k ? (e & 15) : (e >> 6)][a_k ? (e >> 4) : (e & 63)] = av[q];
-      Bs[b_k ? (e & 15) : (e >> 6)][b_k ? (e >> 4) : (e & 63)] = bv[q];
+      As[a_k ? (e & 15) : (e / BT)][a_k ? (e >> 4) : (e % BT)] = av[q];
+      Bs[b_k ? (e & 15) : (e / BT)][b_k ? (e >> 4) : (e % BT)] = bv[q];
     }
     __syncthreads();
     if (k0 + DG_BK < g.K) load(k0 + DG_BK);
@@ -531,25 +547,32 @@ __global__ __launch_bounds__(256) void dgemm_kernel(const DgArgs g) {
     for (int k4 = 0; k4 < DG_BK; k4 += 4) {
       // operands of MFMA 16x16x4: lane l holds A[l%16][l/16] and B[l/16][l%16]
       const int kr = k4 + (lane >> 4);
-      double a[2], b[2];
+      double a[NF], b[NF];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[kr][wm * 32 + i * 16 + (lane & 15)];
+      for (int i = 0; i < NF; ++i) a[i] = As[kr][wm * WT + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = Bs[kr][wn * 32 + j * 16 + (lane & 15)];
+      for (int j = 0; j < NF; ++j) b[j] = Bs[kr][wn * WT + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NF; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NF; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NF; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int32_t m = row_of(i, r), n = col_of(j);
-        if (m < g.M && n < g.N) C[m * g.ldc + n] = g.overwrite ? acc[i][j][r] : cv[i][j][r] - acc[i][j][r];
+        if (m < g.M && n < g.N) {
+          double c_old;
+          if constexpr (PRE_C)
+            c_old = cv[i][j][r];
+          else
+            c_old = g.overwrite ? 0.0 : C[m * g.ldc + n];
+          C[m * g.ldc + n] = g.overwrite ? acc[i][j][r] : c_old - acc[i][j][r];
+        }
       }
 }
 
@@ -573,6 +596,33 @@ __global__ __launch_bounds__(256) void fit_output_kernel(const double* __restric
   }
 }
 
+// Inverse of each 256-wide diagonal block of the factor (for the block
+// triangular solves), assembled per problem (blockIdx.y) from the 64-wide
+// inverse factors: first the diagonal 64 x 64 pieces are placed.
+constexpr int SV_NB = 256;  // block of the triangular solves
+__global__ __launch_bounds__(256) void place_linv_kernel(const double* __restrict__ linv, double* __restrict__ xinv,
+                                                         int64_t bs) {
+  const int32_t kb = blockIdx.x;
+  const double* src = linv + blockIdx.y * bs + static_cast<int64_t>(kb) * CH_NB * CH_NB;
+  double* dst = xinv + blockIdx.y * bs + static_cast<int64_t>(kb / 4) * SV_NB * SV_NB +
+                static_cast<int64_t>(kb % 4) * CH_NB * (SV_NB + 1);
+  for (int e = threadIdx.x; e < CH_NB * CH_NB; e += 256) dst[(e / CH_NB) * SV_NB + e % CH_NB] = src[e];
+}
+
+__global__ __launch_bounds__(256) void fill_f64_kernel(double* __restrict__ p, int64_t n, int64_t bs, double v) {
+  double* q = p + blockIdx.y * bs;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256)
+    q[e] = v;
+}
+
+__global__ __launch_bounds__(256) void copy_f64_kernel(const double* __restrict__ src, double* __restrict__ dst,
+                                                       int64_t n, int64_t bs) {
+  const double* a = src + blockIdx.y * bs;
+  double* b = dst + blockIdx.y * bs;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256)
+    b[e] = a[e];
+}
+
 // ---------------------------------------------------------------- host side
 
 // Workspace: the Gram partials (shared by the problems, which are
@@ -580,9 +630,9 @@ __global__ __launch_bounds__(256) void fit_output_kernel(const double* __restric
 // lambda and the inverse diagonal factors, then one flag per problem.
 struct FitWs {
   float* part;
-  double *G, *C, *sx, *sy, *lam, *linv;
+  double *G, *C, *sx, *sy, *lam, *linv, *xinv, *zbuf;
   int64_t bs;  // doubles between the per-problem areas
-  int64_t oG, oC, oSx, oSy, oLam, oLinv;
+  int64_t oG, oC, oSx, oSy, oLam, oLinv, oXinv, oZbuf;
   int32_t* flags;
   size_t bytes;
 };
@@ -599,7 +649,11 @@ static FitWs fit_layout(int32_t count, int32_t f_in, int32_t f_out, void* base) 
   w.oSy = w.oSx + up(f_in);
   w.oLam = w.oSy + up(f_out);
   w.oLinv = w.oLam + up(4);
-  w.bs = w.oLinv + up(nb_total * CH_NB * CH_NB);
+  w.oXinv = w.oLinv + up(nb_total * CH_NB * CH_NB);
+  const int64_t n_outer = ceil_div(f_in, SV_NB);
+  w.oZbuf = w.oXinv + up(n_outer * SV_NB * SV_NB);
+  const int64_t zb = static_cast<int64_t>(SV_NB) * f_out;
+  w.bs = w.oZbuf + up(zb > CH_NB * 3 * CH_NB ? zb : CH_NB * 3 * CH_NB);
   double* area = c.take<double>(static_cast<size_t>(count) * w.bs);
   if (area) {
     w.G = area + w.oG;
@@ -608,6 +662,8 @@ static FitWs fit_layout(int32_t count, int32_t f_in, int32_t f_out, void* base) 
     w.sy = area + w.oSy;
     w.lam = area + w.oLam;
     w.linv = area + w.oLinv;
+    w.xinv = area + w.oXinv;
+    w.zbuf = area + w.oZbuf;
   }
   w.flags = c.take<int32_t>(static_cast<size_t>(count) + 64);
   w.bytes = c.used + 256;
@@ -626,9 +682,22 @@ static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, 
                  int64_t sak, const double* B, int64_t sbk, int64_t sbn, double* C, int64_t ldc, int64_t bs,
                  int32_t lower_only, int32_t overwrite, int64_t bsb = -1) {
   DgArgs g{M, N, K, A, sam, sak, bs, B, sbk, sbn, bsb < 0 ? bs : bsb, C, ldc, bs, lower_only, overwrite};
-  const dim3 grid(static_cast<unsigned>(ceil_div(N, DG_T)), static_cast<unsigned>(ceil_div(M, DG_T)),
+  // 128-wide tiles for large in-place-free products with a long K (aliasing
+  // of C with A or B is only used with one 64-wide tile along that side)
+  const bool ak = sak == 1 && sam != 1, bk = sbk == 1 && sbn != 1;
+  const bool big = M >= 128 && N >= 128 && K >= 128;
+  const int bt = big ? 128 : 64;
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, bt)), static_cast<unsigned>(ceil_div(M, bt)),
                   static_cast<unsigned>(count));
-  dgemm_kernel<<<grid, 256, 0, s>>>(g);
+#define KVX_DG(WT, A_, B_) dgemm_kernel<WT, A_, B_><<<grid, 256, 0, s>>>(g)
+  if (big) {
+    if (ak) { if (bk) KVX_DG(64, true, true); else KVX_DG(64, true, false); }
+    else { if (bk) KVX_DG(64, false, true); else KVX_DG(64, false, false); }
+  } else {
+    if (ak) { if (bk) KVX_DG(32, true, true); else KVX_DG(32, true, false); }
+    else { if (bk) KVX_DG(32, false, true); else KVX_DG(32, false, false); }
+  }
+#undef KVX_DG
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
@@ -724,50 +793,102 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
   // 2. Cholesky and the two block triangular solves of all problems at once;
   // the diagonal kernel leaves the inverse factor of its block, so each panel
   // and each block solve is an in-place product with it.
+  // Right-looking by 256-column panels: inside a panel, each 64-wide block
+  // is factored, its panel solved and only the panel's remaining columns
+  // updated; the trailing matrix right of the panel is updated once per
+  // panel with K = 256, so it is read and written 12 rather than 48 times.
   const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
-  for (int32_t kb = 0; kb < nb_total; ++kb) {
-    const int32_t k0 = kb * CH_NB;
-    const int32_t nb = min(CH_NB, f_in - k0);
-    double* li = w.linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
-    potrf_diag_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(w.G, bs, f_in, k0, nb, w.flags, li, bs);
-    KVX_LAUNCH_CHECK();
-    const int32_t rest = f_in - k0 - nb;
-    if (rest > 0) {
+  const int32_t n_outer = static_cast<int32_t>(ceil_div(f_in, SV_NB));
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t p0 = I * SV_NB;
+    const int32_t pn = min(SV_NB, f_in - p0);
+    for (int32_t k0 = p0; k0 < p0 + pn; k0 += CH_NB) {
+      const int32_t nb = min(CH_NB, f_in - k0);
+      double* li = w.linv + static_cast<int64_t>(k0 / CH_NB) * CH_NB * CH_NB;
+      potrf_diag_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(w.G, bs, f_in, k0, nb, w.flags, li, bs);
+      KVX_LAUNCH_CHECK();
+      const int32_t rest = f_in - k0 - nb;
+      if (rest <= 0) continue;
       // panel: P = P L_kk^-T (in place, one 64-column tile)
       double* P = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0;
       if (int st = dgemm(s, count, rest, nb, nb, P, f_in, 1, li, 1, CH_NB, P, f_in, bs, 0, 1)) return st;
-      // trailing lower update: G[r][c] -= P[r] . P[c] for r, c >= k0+nb
-      double* Ct = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
-      if (int st = dgemm(s, count, rest, rest, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, bs, 1, 0)) return st;
+      // the panel's remaining columns: G[r][c] -= P[r] . P[c], c < p0 + pn
+      const int32_t pw = p0 + pn - (k0 + nb);
+      if (pw > 0) {
+        double* Ct = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
+        if (int st = dgemm(s, count, rest, pw, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, bs, 1, 0)) return st;
+      }
+    }
+    // trailing lower update right of the panel, K = the panel's width
+    const int32_t rest = f_in - p0 - pn;
+    if (rest > 0) {
+      const double* PI = w.G + static_cast<int64_t>(p0 + pn) * f_in + p0;
+      double* Ct = w.G + static_cast<int64_t>(p0 + pn) * f_in + p0 + pn;
+      if (int st = dgemm(s, count, rest, rest, pn, PI, f_in, 1, PI, 1, f_in, Ct, f_in, bs, 1, 0)) return st;
     }
   }
-  // forward: L Z = C
-  for (int32_t kb = 0; kb < nb_total; ++kb) {
-    const int32_t k0 = kb * CH_NB;
-    const int32_t nb = min(CH_NB, f_in - k0);
-    const double* li = w.linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
-    double* Zk = w.C + static_cast<int64_t>(k0) * f_out;
-    // Z_k = L_kk^-1 Z_k (in place, one 64-row tile)
-    if (int st = dgemm(s, count, nb, f_out, nb, li, CH_NB, 1, Zk, f_out, 1, Zk, f_out, bs, 0, 1)) return st;
+
+  // inverses of the 256-wide diagonal blocks: X_bb = L_bb^-1 (placed), then
+  // for each lower block row b, X[b, 0:b] = -L_bb^-1 (L[b, 0:b] X[0:b, 0:b])
+  const dim3 fill_grid(static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_outer) * SV_NB * SV_NB, 256 * 8)),
+                       static_cast<unsigned>(count));
+  fill_f64_kernel<<<fill_grid, 256, 0, s>>>(w.xinv, static_cast<int64_t>(n_outer) * SV_NB * SV_NB, bs, 0.0);
+  KVX_LAUNCH_CHECK();
+  place_linv_kernel<<<dim3(static_cast<unsigned>(nb_total), static_cast<unsigned>(count)), 256, 0, s>>>(w.linv, w.xinv,
+                                                                                                      bs);
+  KVX_LAUNCH_CHECK();
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, f_in - k0);
+    double* X = w.xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    for (int32_t b = 1; b * CH_NB < nb; ++b) {
+      const int32_t sb = min(CH_NB, nb - b * CH_NB);
+      const int32_t wb = b * CH_NB;
+      // T = L[b, 0:b] X[0:b, 0:b] (in zbuf, row stride 3 * 64)
+      if (int st = dgemm(s, count, sb, wb, wb, w.G + static_cast<int64_t>(k0 + wb) * f_in + k0, f_in, 1, X, SV_NB, 1,
+                         w.zbuf, 3 * CH_NB, bs, 0, 1))
+        return st;
+      // X[b, 0:b] = 0 - L_bb^-1 T
+      const double* li = w.linv + static_cast<int64_t>(I * 4 + b) * CH_NB * CH_NB;
+      if (int st = dgemm(s, count, sb, wb, sb, li, CH_NB, 1, w.zbuf, 3 * CH_NB, 1,
+                         X + static_cast<int64_t>(wb) * SV_NB, SV_NB, bs, 0, 0))
+        return st;
+    }
+  }
+  auto copy_back = [&](double* dst, int64_t n) -> int {
+    copy_f64_kernel<<<dim3(static_cast<unsigned>(ceil_div(n, 256 * 8)), static_cast<unsigned>(count)), 256, 0, s>>>(
+        w.zbuf, dst, n, bs);
+    KVX_LAUNCH_CHECK();
+    return KVX_OK;
+  };
+  // forward: L Z = C by 256-row blocks (Z_I = X_II C_I, then the rows below)
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, f_in - k0);
+    const double* X = w.xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    double* CI = w.C + static_cast<int64_t>(k0) * f_out;
+    if (int st = dgemm(s, count, nb, f_out, nb, X, SV_NB, 1, CI, f_out, 1, w.zbuf, f_out, bs, 0, 1)) return st;
+    if (int st = copy_back(CI, static_cast<int64_t>(nb) * f_out)) return st;
     const int32_t rest = f_in - k0 - nb;
     if (rest > 0) {
       const double* Lb = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0;
-      double* Cr = w.C + static_cast<int64_t>(k0 + nb) * f_out;
-      if (int st = dgemm(s, count, rest, f_out, nb, Lb, f_in, 1, Zk, f_out, 1, Cr, f_out, bs, 0, 0)) return st;
+      if (int st = dgemm(s, count, rest, f_out, nb, Lb, f_in, 1, w.zbuf, f_out, 1, CI + static_cast<int64_t>(nb) * f_out,
+                         f_out, bs, 0, 0))
+        return st;
     }
   }
-  // backward: L^T W = Z
-  for (int32_t kb = nb_total - 1; kb >= 0; --kb) {
-    const int32_t k0 = kb * CH_NB;
-    const int32_t nb = min(CH_NB, f_in - k0);
-    const double* li = w.linv + static_cast<int64_t>(kb) * CH_NB * CH_NB;
-    double* Wk = w.C + static_cast<int64_t>(k0) * f_out;
-    // W_k = L_kk^-T W_k (in place)
-    if (int st = dgemm(s, count, nb, f_out, nb, li, 1, CH_NB, Wk, f_out, 1, Wk, f_out, bs, 0, 1)) return st;
+  // backward: L^T W = Z (W_I = X_II^T Z_I, then the rows above)
+  for (int32_t I = n_outer - 1; I >= 0; --I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, f_in - k0);
+    const double* X = w.xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    double* CI = w.C + static_cast<int64_t>(k0) * f_out;
+    if (int st = dgemm(s, count, nb, f_out, nb, X, 1, SV_NB, CI, f_out, 1, w.zbuf, f_out, bs, 0, 1)) return st;
+    if (int st = copy_back(CI, static_cast<int64_t>(nb) * f_out)) return st;
     if (k0 > 0) {
-      // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_k
+      // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_I
       const double* Lr = w.G + static_cast<int64_t>(k0) * f_in;
-      if (int st = dgemm(s, count, k0, f_out, nb, Lr, 1, f_in, Wk, f_out, 1, w.C, f_out, bs, 0, 0)) return st;
+      if (int st = dgemm(s, count, k0, f_out, nb, Lr, 1, f_in, w.zbuf, f_out, 1, w.C, f_out, bs, 0, 0)) return st;
     }
   }
 
