@@ -202,9 +202,23 @@ def affine(x, wt, b=None) -> np.ndarray:
     return y
 
 
+def key_norm(y, weight, eps: float) -> np.ndarray:
+    """The receiver's own key normalisation, applied to mapped keys before
+    its RoPE ([HF] "Methodology" step 2: keys are mapped before key
+    normalisation and RoPE, then the receiver applies its own).  The pages
+    do not give its form; reading: RMS normalisation of each head vector
+    over head_dim with a per-channel weight shared by the heads of a layer,
+    y / sqrt(mean(y^2) + eps) * weight.  ``y``: [n, H, d]; ``weight``: [d]."""
+    y = np.asarray(y, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    ms = np.mean(y * y, axis=-1, keepdims=True)
+    return y / np.sqrt(ms + eps) * w
+
+
 def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: bool,
                    recv_heads: int, recv_head_dim: int,
-                   send_rope_base: float = 0.0, recv_rope_base: float = 0.0) -> np.ndarray:
+                   send_rope_base: float = 0.0, recv_rope_base: float = 0.0,
+                   recv_key_norm=None, key_norm_eps: float = 1e-6) -> np.ndarray:
     """Translated receiver rows for one role (K or V), all receiver layers.
 
     ``rows``: receiver token indices to produce.  Returns float64
@@ -215,7 +229,8 @@ def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: boo
     Keys: with ``send_rope_base`` the sender keys are de-rotated at the sender
     position; with ``recv_rope_base`` the mapped key of receiver row i is
     rotated at position i (bias added before the rotation; values are never
-    rotated).
+    rotated).  With ``recv_key_norm`` ([L_R][d_R]) the mapped keys are
+    normalised by ``key_norm`` (after the bias, before the receiver rotation).
     """
     rows = np.asarray(rows, dtype=np.int64)
     tm = np.asarray(token_map, dtype=np.int64)
@@ -234,6 +249,9 @@ def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: boo
                                                  None if bl is None else bl[h * d:(h + 1) * d])
         else:
             y = affine(x, as_f64(wt[l]), bl)
+        if recv_key_norm is not None:
+            y = key_norm(y.reshape(rows.size, recv_heads, recv_head_dim), as_f64(recv_key_norm[l]),
+                         key_norm_eps).reshape(rows.size, -1)
         if recv_rope_base:
             y = rope_rotate(y.reshape(rows.size, recv_heads, recv_head_dim), rows,
                             recv_rope_base, +1).reshape(rows.size, -1)

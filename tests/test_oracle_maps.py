@@ -167,6 +167,55 @@ def test_identity_maps_reproduce_input_exactly():
     assert np.max(np.abs(yr - rot.reshape(L, N, F))) < 1e-12
 
 
+def test_key_norm_pins():
+    """Receiver key normalisation: with unit weights and eps = 0 every head
+    vector comes out with RMS exactly 1; a positive scale of the input
+    changes nothing; a hand example; and because a rotation keeps a head
+    vector's RMS, normalising then rotating equals rotating then normalising
+    when the weights are equal across the pair members."""
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((7, 3, 8)) * rng.uniform(0.1, 30.0, size=(7, 3, 1))
+    ones = np.ones(8)
+    z = O.key_norm(y, ones, 0.0)
+    assert np.max(np.abs(np.sqrt(np.mean(z * z, axis=-1)) - 1.0)) < 1e-14
+    assert np.max(np.abs(O.key_norm(4.5 * y, ones, 0.0) - z)) < 1e-14
+    # (3, 4) with weights (1, 2): mean square 12.5 -> (3, 8) / sqrt(12.5)
+    got = O.key_norm(np.array([[[3.0, 4.0]]]), np.array([1.0, 2.0]), 0.0)
+    assert np.max(np.abs(got - np.array([[[0.848528137423857, 2.262741699796952]]]))) < 1e-15
+    # eps enters the denominator only: a zero vector stays zero
+    assert np.array_equal(O.key_norm(np.zeros((1, 1, 4)), ones[:4], 1e-6), np.zeros((1, 1, 4)))
+    w = np.tile(rng.uniform(0.5, 1.5, size=4), 2)  # equal weight on c and c + d/2
+    pos = np.arange(7) * 37
+    a = O.rope_rotate(O.key_norm(y, w, 1e-6), pos, 1e4, +1)
+    b = O.key_norm(O.rope_rotate(y, pos, 1e4, +1), w, 1e-6)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_translate_rows_with_key_norm():
+    """translate_rows with the receiver key norm: per head RMS 1 before the
+    receiver rotation with unit weights (also after it, the rotation keeps
+    the RMS), and the norm is applied after the bias (a bias-only map gives
+    the normalised bias)."""
+    rng = np.random.default_rng(13)
+    L_S, N_S, H, d = 4, 10, 2, 8
+    cache = rng.standard_normal((L_S, N_S, H, d))
+    taps = O.layer_taps(L_S, 3, 3, 1)
+    wt = rng.standard_normal((3, H * d, 3 * H * d))
+    b = rng.standard_normal((3, H * d))
+    tmap = np.array([0, 1, 1, 4, 7, 9])
+    rows = np.arange(tmap.size)
+    kn = np.ones((3, d))
+    y = O.translate_rows(cache, tmap, taps, wt, b, rows, per_head=False, recv_heads=H, recv_head_dim=d,
+                         recv_rope_base=1e4, recv_key_norm=kn, key_norm_eps=0.0)
+    rms = np.sqrt(np.mean(y.reshape(3, rows.size, H, d) ** 2, axis=-1))
+    assert np.max(np.abs(rms - 1.0)) < 1e-13
+    z = O.translate_rows(cache, tmap, taps, np.zeros_like(wt), b, rows, per_head=False, recv_heads=H,
+                         recv_head_dim=d, recv_key_norm=kn, key_norm_eps=0.0)
+    bh = b.reshape(3, 1, H, d)
+    want = bh / np.sqrt(np.mean(bh * bh, axis=-1, keepdims=True))
+    assert np.max(np.abs(z.reshape(3, rows.size, H, d) - want)) < 1e-14
+
+
 def test_features_layout_and_derotation():
     rng = np.random.default_rng(5)
     cache = rng.standard_normal((4, 6, 2, 4))
