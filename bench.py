@@ -21,7 +21,8 @@ rocprofv3 counter summary when the kernel sources still match it, else null.
 workload.  ``also`` reports the per-head workload (32 -> 80 layers, 4096
 tokens, fp32 128 x 128 maps) against the HBM peak, ``also_perhead_rope`` the
 same with keys stored rotated on both sides; ``also_cfg3``,
-``also_fp32_maps`` and ``also_fit`` other flattened settings and the ridge
+``also_fp32_maps``, ``also_key_norm`` (the 32k setting with the receiver's
+key normalisation) and ``also_fit`` other flattened settings and the ridge
 fit.
 
 Profiling helpers: ``--no-also`` runs the headline step alone and
@@ -330,9 +331,10 @@ def perhead_measure(dev, steps=10, rope=False):
                          "kernel": "perhead_kernel", "launch_ms": t * 1e3, "algorithmic_bytes_per_launch": bytes_alg}}
 
 
-def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8):
+def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8, key_norm=False):
     """A flattened setting other than the headline one: translation of all
-    32 receiver layers, K and V, from 36 sender layers with three taps."""
+    32 receiver layers, K and V, from 36 sender layers with three taps
+    (with ``key_norm``, the receiver's key normalisation in the epilogue)."""
     send_end, recv_end = synth.token_ends(n_recv, seed)
     shp = synth.CacheShape(36, len(send_end), 8, 128)
     x = {}
@@ -348,6 +350,8 @@ def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8):
     m = tmap.cpu().numpy()
     U = int(1 + np.count_nonzero(np.diff(m)))
     kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
+    if key_norm:
+        kw["recv_key_norm"] = synth.key_norm_weights(32, 128, seed * 100 + 30, dev)
     outs = {"k_recv": torch.empty((32, n_recv, 8, 128), dtype=torch.bfloat16, device=dev)}
     outs["v_recv"] = torch.empty_like(outs["k_recv"])
     ms, gm = [], []
@@ -363,8 +367,8 @@ def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8):
             gm.append(st[1])
     t_gemm = float(np.mean(gm))
     flops = 2.0 * U * 3072 * 1024 * 32 * 2  # algorithmic (fp32 maps execute twice: high and low halves)
-    return {"workload": f"flattened{' + RoPE' if rope else ''}, {n_recv} receiver tokens, "
-                        f"{'fp32' if fp32_maps else 'bf16'} maps", "distinct_sender_rows": U,
+    return {"workload": f"flattened{' + RoPE' if rope else ''}{' + receiver key norm' if key_norm else ''}, "
+                        f"{n_recv} receiver tokens, {'fp32' if fp32_maps else 'bf16'} maps", "distinct_sender_rows": U,
             "tokens_per_s": n_recv / (float(np.mean(ms)) * 1e-3), "translate_ms": float(np.mean(ms)),
             "roofline": {"bound": "mfma", "achieved": flops / (t_gemm * 1e-3) / 1e12, "peak": PEAK_MFMA_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / (t_gemm * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
@@ -529,6 +533,9 @@ def main():
         log("bench: per-head workload, rotated keys")
         res["also_perhead_rope"] = perhead_measure(dev, rope=True)
         del x, outs, ws
+        torch.cuda.empty_cache()
+        log("bench: flattened + RoPE + receiver key norm, 32768 tokens")
+        res["also_key_norm"] = flat_setting_measure(dev, 32768, 4, rope=True, fp32_maps=False, key_norm=True)
         torch.cuda.empty_cache()
         log("bench: flattened, 8192 tokens, no RoPE")
         res["also_cfg3"] = flat_setting_measure(dev, 8192, 3, rope=False, fp32_maps=False)

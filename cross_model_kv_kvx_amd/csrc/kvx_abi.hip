@@ -32,6 +32,7 @@ static bool desc_ok(const kvx_cache_desc* d) {
   if (d->dtype != KVX_F32 && d->dtype != KVX_BF16) return false;
   if (!(d->rope_base >= 0.0)) return false;
   if (d->rope_base > 0.0 && (d->head_dim % 2) != 0) return false;
+  if (d->k_norm && !(d->k_norm_eps >= 0.0)) return false;
   return true;
 }
 
@@ -174,6 +175,9 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     if (send->kv_heads != recv->kv_heads || send->head_dim != recv->head_dim) return KVX_ERR_SHAPE;
   }
   if (send->dtype != recv->dtype) return KVX_ERR_UNSUPPORTED;
+  // the receiver's key normalisation: flattened bf16 path (one head of
+  // 128 outputs per wave in the epilogue)
+  if (recv->k_norm && do_k && (per_head || send->dtype != KVX_BF16)) return KVX_ERR_UNSUPPORTED;
   if (recv->tokens == 0 || (!do_k && !do_v)) return KVX_OK;
   if (send->tokens == 0) return KVX_ERR_SHAPE;
   const TranslateWs need = layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, nullptr);
@@ -338,6 +342,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     r.bias = b_k;
     r.out = static_cast<uint16_t*>(k_recv);
     r.rotate = w.tab_recv ? 1 : 0;
+    r.knorm = recv->k_norm;
     roles[n++] = r;
   }
   if (do_v) {
@@ -369,6 +374,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   p.taps = taps;
   p.tab_recv = w.tab_recv;
   p.runs = w.runs;
+  p.knorm_eps = static_cast<float>(recv->k_norm_eps);
   return main_kernel([&] { return launch_flat(p, roles, n, s); });
 }
 

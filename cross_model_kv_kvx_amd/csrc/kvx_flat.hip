@@ -43,7 +43,10 @@
 //     its 16 KB share of parts 1..4, then walks the receiver rows of those
 //     runs 8 at a time, rotating key pairs (c, c+64) at the receiver position
 //     by a recurrence and storing 2 x 16 bytes of bf16 (nearest even) per
-//     lane.
+//     lane.  The receiver's own key normalisation ("Prefill-Free ...",
+//     Methodology 2: keys are mapped before it and before RoPE) scales each
+//     staged run row by its 1/RMS over the head and by the channel weights
+//     before the rotation.
 
 #include "kvx_internal.hpp"
 
@@ -71,6 +74,8 @@ struct FlatKArgs {
   const float* bias[2];
   uint16_t* out[2];
   int32_t rotate[2];
+  const float* knorm[2];  // key-normalisation weights [L_R][128] or null
+  float knorm_eps;
   int32_t n_roles;
   int32_t recv_layers, recv_tokens, k_dim, f_out, send_row, n_taps;
   const float2* tab_recv;
@@ -304,6 +309,10 @@ flat_gemm_kernel(const FlatKArgs args) {
     for (int ni = 0; ni < 4; ++ni)
       bcol[ni] = bias ? bias[static_cast<int64_t>(l) * args.f_out + n0 + wn * 128 + ni * 32 + (lane & 31)] : 0.0f;
     const bool rot = args.rotate[role] != 0;
+    // the receiver's key normalisation: weights of this lane's pair members
+    // (channels 8q.. and 64 + 8q.., read where used: L1-resident)
+    const float* kn = args.knorm[role];
+    const float4* g4 = kn ? reinterpret_cast<const float4*>(kn + static_cast<int64_t>(l) * 128 + 8 * q) : nullptr;
     uint16_t* outp = args.out[role] + static_cast<int64_t>(l) * args.recv_tokens * args.f_out + n0 + col;
     // every wave has finished reading the parts
     KVX_COMPILER_FENCE();
@@ -328,6 +337,20 @@ flat_gemm_kernel(const FlatKArgs args) {
       KVX_COMPILER_FENCE();  // LDS operations of one wave execute in order
       __builtin_amdgcn_sched_barrier(0);
       if (u0 >= U) continue;
+      // 1 / RMS of each staged row (lanes 2r and 2r+1 sum the two halves of
+      // row r; the column swizzle only permutes a row)
+      float inv = 1.0f;
+      if (kn) {
+        const float4* h4 = reinterpret_cast<const float4*>(ep + (lane >> 1) * 128 + 64 * (lane & 1));
+        float ss = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+          const float4 v = h4[w];
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+        ss += __shfl_xor(ss, 1, 64);
+        inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + args.knorm_eps);
+      }
       const int32_t p0 = args.run_begin[u0];
       const int32_t n = args.run_begin[min(u0 + 32, U)] - p0;
       float cs[8], sn[8], c8[8], s8[8];
@@ -355,6 +378,7 @@ flat_gemm_kernel(const FlatKArgs args) {
         for (int i = 0; i < 8; ++i) {
           const int32_t off = base + grp + 8 * i;
           const int ul = __shfl(rv, grp + 8 * i, 64) - u0;
+          const float sc = __shfl(inv, 2 * min(max(ul, 0), 31), 64);  // unconditional: all lanes take part
           if (off < n) {
             const int swz = ((ul >> 2) & 1) << 5;
             const float* rowp = ep + ul * 128;
@@ -364,6 +388,16 @@ flat_gemm_kernel(const FlatKArgs args) {
             const float4 y1 = *reinterpret_cast<const float4*>(rowp + ((64 + 8 * q) ^ swz) + 4);
             float a[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
             float b[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            if (kn) {
+              const float4 u0 = g4[0], u1 = g4[1], v0 = g4[16], v1 = g4[17];
+              const float ga[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+              const float gb[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                a[e] *= sc * ga[e];
+                b[e] *= sc * gb[e];
+              }
+            }
             if (rot) {
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
@@ -486,7 +520,9 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
     a.bias[j] = roles[j].bias;
     a.out[j] = roles[j].out;
     a.rotate[j] = roles[j].rotate;
+    a.knorm[j] = roles[j].knorm;
   }
+  a.knorm_eps = p.knorm_eps;
   flat_gemm_kernel<<<G, FT_THREADS, 0, s>>>(a);
   KVX_LAUNCH_CHECK();
   return KVX_OK;

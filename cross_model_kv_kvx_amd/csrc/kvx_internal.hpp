@@ -49,6 +49,7 @@ struct FlatRole {
   const float* bias;       // [L_R][F_out] or null
   uint16_t* out;           // [L_R][N_R][F_out] bf16
   int32_t rotate;          // rotate outputs at the receiver position
+  const float* knorm;      // [L_R][128] key-normalisation weights (before the rotation) or null
 };
 
 struct FlatProblem {
@@ -58,6 +59,7 @@ struct FlatProblem {
   const int32_t* taps;     // host [L_R][n_taps]
   const float2* tab_recv;
   Runs runs;
+  float knorm_eps;
 };
 
 int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s);

@@ -40,7 +40,8 @@ class KvxError(RuntimeError):
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("tokens", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_double)]
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("k_norm", ctypes.c_void_p), ("k_norm_eps", ctypes.c_double)]
 
 
 _lib = None
@@ -175,7 +176,8 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
               recv_head_dim: Optional[int] = None, per_head: bool = False,
               send_rope_base: float = 0.0, recv_rope_base: float = 0.0,
               k_recv: Optional[torch.Tensor] = None, v_recv: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, stream=None, stage_ms: Optional[list] = None):
+              workspace: Optional[torch.Tensor] = None, stream=None, stage_ms: Optional[list] = None,
+              recv_key_norm: Optional[torch.Tensor] = None, key_norm_eps: float = 1e-6):
     """kvx_translate.  Returns (k_recv, v_recv) (either None when its role is
     skipped).  ``taps``: host int32 [L_R][n_taps] (numpy).  With a list
     ``stage_ms``, calls kvx_translate_timed instead (synchronous) and appends
@@ -197,6 +199,12 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
     N_R = recv_to_send.numel()
     send = cache_desc(ref, send_rope_base)
     recv = CacheDesc(int(L_R), int(N_R), int(H_R), int(d_R), _dtype_code(ref), float(recv_rope_base))
+    if recv_key_norm is not None:
+        _need(recv_key_norm, "recv_key_norm", torch.float32)
+        if tuple(recv_key_norm.shape) != (L_R, d_R):
+            raise ValueError("recv_key_norm must be [recv_layers][head_dim]")
+        recv.k_norm = recv_key_norm.data_ptr()
+        recv.k_norm_eps = float(key_norm_eps)
     for name, t in (("wt_k", wt_k), ("wt_v", wt_v)):
         if t is not None:
             _need(t, name, w_ref.dtype)

@@ -198,6 +198,13 @@ def perhead_maps(recv_layers: int, heads: int, head_dim: int, seed: int, device=
     return wt.contiguous(), b.contiguous()
 
 
+def key_norm_weights(recv_layers: int, head_dim: int, seed: int, device="cpu"):
+    """Weights of a receiver's key normalisation, fp32 [L][d], 1 + 0.1 N(0,1)
+    (a trained norm's weights sit near one)."""
+    g = _gen(device, seed)
+    return (1.0 + 0.1 * torch.randn((recv_layers, head_dim), generator=g, device=device)).contiguous()
+
+
 def config(k: int, device="cpu", small: bool = False):
     """Inputs of workload ``k`` as a dict of tensors / arrays.
 

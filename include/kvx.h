@@ -66,6 +66,14 @@ typedef struct {
   double rope_base;   /* > 0: keys are stored rotated (RoPE, half-split pairs
                          (c, c + head_dim/2), angle pos * base^(-2j/head_dim));
                          0: keys are stored unrotated.  Values are never rotated. */
+  const float* k_norm; /* receiver only ("Prefill-Free ...", Methodology 2: keys
+                         are mapped before the receiver's own key normalisation
+                         and RoPE): device fp32 [layers][head_dim] weights w of
+                         an RMS normalisation of each translated key head vector,
+                         y / sqrt(mean_c y_c^2 + k_norm_eps) * w, applied after
+                         the bias and before the rotation; NULL: none.  Ignored
+                         for the sender. */
+  double k_norm_eps;  /* >= 0 */
 } kvx_cache_desc;
 
 /* Human-readable name of a status code (static string). */
@@ -153,7 +161,8 @@ int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps,
  * into, fp16), other bf16 rows as bf16; fp32 caches use fp32 arithmetic.
  * Accumulation is fp32 everywhere.
  * Supported: recv->dtype == send->dtype; bf16 caches need head_dim == 128
- * on both sides.
+ * on both sides; recv->k_norm only on the flattened bf16 path
+ * (KVX_ERR_UNSUPPORTED otherwise).
  * ---------------------------------------------------------------------- */
 size_t kvx_translate_workspace_size(const kvx_cache_desc* send,
                                     const kvx_cache_desc* recv,

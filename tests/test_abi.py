@@ -89,6 +89,16 @@ def test_translate_validation_before_launch():
     assert call(ws_bytes=16) == kvx.ERR_WORKSPACE
     assert call(sd=desc(0, 100, 8, 128)) == kvx.ERR_INVALID
     assert call(sd=desc(36, 100, 8, 127, rope=1e4)) == kvx.ERR_INVALID  # odd head dim with rotation
+    kn = desc(32, 120, 8, 128)
+    kn.k_norm = 0x2000
+    kn.k_norm_eps = -1.0
+    assert call(rd=kn) == kvx.ERR_INVALID                       # negative eps of the key norm
+    kn.k_norm_eps = 1e-6
+    ph = desc(32, 120, 8, 128)
+    assert call(sd=desc(32, 100, 8, 128), rd=kn, taps_p=kvx.layer_map(32, 32, 1).ctypes.data_as(
+        ctypes.POINTER(ctypes.c_int32)), n_taps=1, per_head=1) == kvx.ERR_UNSUPPORTED  # key norm: flattened only
+    assert call(sd=desc(32, 100, 8, 128), rd=ph, taps_p=kvx.layer_map(32, 32, 1).ctypes.data_as(
+        ctypes.POINTER(ctypes.c_int32)), n_taps=1, per_head=1, ws_bytes=16) == kvx.ERR_WORKSPACE
     assert call(rd=desc(32, 0, 8, 128)) == kvx.OK                # nothing to translate
     assert call(k_recv=None, v_recv=None) == kvx.OK              # no role requested
 

@@ -392,6 +392,46 @@ def test_flat_fp32_maps_all_elements():
         assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("rope", [True, False])
+def test_flat_key_norm_all_elements(rope):
+    """The receiver's key normalisation in the flattened epilogue (after the
+    bias, before the receiver rotation), keys vs the oracle with the norm,
+    values vs the oracle without it."""
+    say(f"flattened + receiver key norm, rope={rope}, 400 receiver tokens")
+    send_end, recv_end = synth.token_ends(400, 81)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(send_end, recv_end)
+    tm = dev_i32(tmap_o)
+    caches, maps, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, 8100 + r, DEV, outlier_frac=0.01 if rope else 0.0,
+                                          outlier_scale=20.0 if rope else 1.0, outlier_pairs=(rope and role == "k"))
+        wt, u, v, b = synth.flat_maps(32, 3072, 1024, 8200 + r, DEV, 16)
+        # dense part rounded to bf16 on the host (no fold: the inputs of the
+        # oracle never come from the library)
+        wb = host(wt).to(torch.bfloat16)
+        maps[role] = (wb.to(DEV), Bf16Maps(wb.view(torch.int16).numpy().view(np.uint16)))
+        bias[role] = b
+        del wt, u, v
+    kn = synth.key_norm_weights(32, 128, 8300, DEV)
+    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
+    k, v = kvx.translate(caches["k"], caches["v"], tm, taps, maps["k"][0], maps["v"][0], bias["k"], bias["v"],
+                         recv_key_norm=kn, key_norm_eps=1e-6, **kw)
+    torch.cuda.synchronize()
+    rows = np.arange(tmap_o.size)
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], tmap_o, taps, maps[role][1], host(bias[role]).numpy().astype(np.float64), rows,
+                                per_head=False, recv_heads=8, recv_head_dim=128,
+                                send_rope_base=kw.get("send_rope_base", 0.0) if rk else 0.0,
+                                recv_rope_base=kw.get("recv_rope_base", 0.0) if rk else 0.0,
+                                recv_key_norm=host(kn).numpy() if rk else None, key_norm_eps=1e-6)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  key norm {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+
+
 def test_translate_deterministic_and_identity_maps():
     say("determinism + identity maps")
     c = flat_case(3, 520, seed=23)
