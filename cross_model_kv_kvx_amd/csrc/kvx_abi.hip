@@ -50,9 +50,18 @@ struct TranslateWs {
   size_t bytes = 0;
 };
 
+// Rows of the rotation tables: positions 0 .. rows-1.
+static int32_t send_tab_rows(const kvx_cache_desc* send, int32_t pos_limit) {
+  return send->tokens > pos_limit ? send->tokens : pos_limit;
+}
+static int32_t recv_tab_rows_for(const kvx_cache_desc* recv, int32_t pos_limit) {
+  const int32_t r = recv_tab_rows(recv->tokens);
+  return r > pos_limit ? r : pos_limit;
+}
+
 static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
                                     int32_t per_head, int32_t w_dtype, bool key_role, bool value_role,
-                                    void* base) {
+                                    int32_t pos_limit, void* base) {
   TranslateWs w;
   Carve c(base);
   const int32_t nr = recv->tokens;
@@ -68,11 +77,11 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
     w.runs.n_uniq = c.take<int32_t>(64);
     w.runs_scratch = c.take<char>(runs_ws_bytes(nr));
   }
-  if (srope) w.tab_send = c.take<float2>(static_cast<size_t>(send->tokens) * (send->head_dim / 2));
+  if (srope) w.tab_send = c.take<float2>(static_cast<size_t>(send_tab_rows(send, pos_limit)) * (send->head_dim / 2));
   // the receiver table holds at least RECV_TAB_MIN positions: the flattened
   // epilogue reads the (cos, sin) step of its rotation recurrence from the
   // table row of position 8, also for caches of fewer tokens
-  if (rrope) w.tab_recv = c.take<float2>(static_cast<size_t>(recv_tab_rows(nr)) * (recv->head_dim / 2));
+  if (rrope) w.tab_recv = c.take<float2>(static_cast<size_t>(recv_tab_rows_for(recv, pos_limit)) * (recv->head_dim / 2));
   if (!f32 && srope) {
     // U <= N_R always (U <= N_S only for non-decreasing maps)
     w.rows_cap = nr;
@@ -124,6 +133,27 @@ int kvx_align_tokens(const int32_t* send_end, int32_t n_send, const int32_t* rec
                       static_cast<hipStream_t>(stream));
 }
 
+size_t kvx_align_batched_workspace_size(const int32_t* recv_off, int32_t n_seq) {
+  if (!recv_off || n_seq < 1) return 0;
+  return align_batched_ws_bytes(recv_off, n_seq) + 256;
+}
+
+int kvx_align_tokens_batched(const int32_t* send_end, const int32_t* send_off, const int32_t* recv_end,
+                             const int32_t* recv_off, int32_t n_seq, int32_t* recv_to_send, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  if (n_seq < 1 || !send_off || !recv_off) return KVX_ERR_INVALID;
+  if (send_off[0] != 0 || recv_off[0] != 0) return KVX_ERR_INVALID;
+  for (int32_t q = 0; q < n_seq; ++q) {
+    if (send_off[q + 1] < send_off[q] || recv_off[q + 1] < recv_off[q]) return KVX_ERR_INVALID;
+    if (recv_off[q + 1] > recv_off[q] && send_off[q + 1] == send_off[q]) return KVX_ERR_SHAPE;
+  }
+  if (recv_off[n_seq] == 0) return KVX_OK;
+  if (!send_end || !recv_end || !recv_to_send) return KVX_ERR_INVALID;
+  if (!workspace || ws_bytes < kvx_align_batched_workspace_size(recv_off, n_seq)) return KVX_ERR_WORKSPACE;
+  return launch_align_batched(send_end, send_off, recv_end, recv_off, n_seq, recv_to_send, workspace,
+                              static_cast<hipStream_t>(stream));
+}
+
 int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps, int32_t tap_stride, int32_t* taps_out) {
   if (send_layers < 1 || recv_layers < 1 || !taps_out) return KVX_ERR_INVALID;
   if (n_taps < 1 || n_taps > MAX_TAPS || (n_taps % 2) == 0 || tap_stride < 0) return KVX_ERR_INVALID;
@@ -147,7 +177,7 @@ size_t kvx_translate_workspace_size(const kvx_cache_desc* send, const kvx_cache_
                                     int32_t per_head) {
   if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS) return 0;
   // sized for fp32 maps (the larger case) and both roles
-  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, nullptr).bytes;
+  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, 0, nullptr).bytes;
 }
 
 }  // extern "C"
@@ -160,7 +190,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
                           const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
                           const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
                           const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
-                          void* stream, hipEvent_t* ev) {
+                          void* stream, hipEvent_t* ev, const kvx_placement* pl) {
   if (!desc_ok(send) || !desc_ok(recv)) return KVX_ERR_INVALID;
   if (w_dtype != KVX_F32 && w_dtype != KVX_BF16) return KVX_ERR_INVALID;
   if (n_taps < 1 || n_taps > MAX_TAPS || !taps) return KVX_ERR_INVALID;
@@ -175,15 +205,29 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     if (send->kv_heads != recv->kv_heads || send->head_dim != recv->head_dim) return KVX_ERR_SHAPE;
   }
   if (send->dtype != recv->dtype) return KVX_ERR_UNSUPPORTED;
+  // placement into a pool of rows, per-token rotary positions
+  const int64_t* slot = pl ? pl->slot : nullptr;
+  const int32_t* recv_pos = pl ? pl->recv_pos : nullptr;
+  const int32_t* send_pos = pl ? pl->send_pos : nullptr;
+  const int32_t pos_limit = (recv_pos || send_pos) ? pl->pos_limit : 0;
+  int64_t pool_rows = recv->tokens;
+  if (pl) {
+    if (pl->pool_rows < 0 || (slot && pl->pool_rows < 1)) return KVX_ERR_INVALID;
+    if (!slot && pl->pool_rows != 0 && pl->pool_rows < recv->tokens) return KVX_ERR_SHAPE;
+    if (pl->pool_rows != 0) pool_rows = pl->pool_rows;
+    if ((recv_pos || send_pos) && pl->pos_limit < 1) return KVX_ERR_INVALID;
+    if ((slot || recv_pos || send_pos || pool_rows != recv->tokens) && send->dtype == KVX_F32)
+      return KVX_ERR_UNSUPPORTED;
+  }
   // the receiver's key normalisation: flattened bf16 path (one head of
   // 128 outputs per wave in the epilogue)
   if (recv->k_norm && do_k && (per_head || send->dtype != KVX_BF16)) return KVX_ERR_UNSUPPORTED;
   if (recv->tokens == 0 || (!do_k && !do_v)) return KVX_OK;
   if (send->tokens == 0) return KVX_ERR_SHAPE;
-  const TranslateWs need = layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, nullptr);
+  const TranslateWs need = layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, nullptr);
   if (!workspace || ws_bytes < need.bytes) return KVX_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const TranslateWs w = layout_translate(send, recv, n_taps, per_head, w_dtype, do_k, do_v, workspace);
+  const TranslateWs w = layout_translate(send, recv, n_taps, per_head, w_dtype, do_k, do_v, pos_limit, workspace);
   auto mark = [&](int i) -> int {
     if (ev && hipEventRecord(ev[i], s) != hipSuccess) return KVX_ERR_HIP;
     return KVX_OK;
@@ -199,10 +243,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
 
   if (send->dtype == KVX_F32) {
     if (w.tab_send) {
-      if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
+      if (int st = launch_rope_table(w.tab_send, send_tab_rows(send, pos_limit), send->head_dim, send->rope_base, s)) return st;
     }
     if (w.tab_recv) {
-      if (int st = launch_rope_table(w.tab_recv, recv_tab_rows(recv->tokens), recv->head_dim, recv->rope_base, s))
+      if (int st = launch_rope_table(w.tab_recv, recv_tab_rows_for(recv, pos_limit), recv->head_dim, recv->rope_base, s))
         return st;
     }
     F32Problem p{};
@@ -244,6 +288,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     p.taps = taps;
     p.recv_to_send = recv_to_send;
     p.tab_recv = w.tab_recv;
+    p.slot = slot;
+    p.pool_rows = pool_rows;
+    p.recv_pos = recv_pos;
+    p.pos_limit = pos_limit;
     HeadRole roles[2];
     int n = 0;
     if (do_k) {
@@ -251,11 +299,11 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
       if (w.tab_send) {
         // keys rotated back at their sender positions, one fp16 row per run
         if (int st = launch_runs(recv_to_send, recv->tokens, send->tokens, w.runs, w.runs_scratch, s)) return st;
-        if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
+        if (int st = launch_rope_table(w.tab_send, send_tab_rows(send, pos_limit), send->head_dim, send->rope_base, s)) return st;
         uint8_t used[MAX_LAYERS] = {0};
         for (int32_t i = 0; i < recv->layers; ++i) used[taps[i]] = 1;
         if (int st = launch_derotate_rows(static_cast<const uint16_t*>(k_send), send->layers, send->tokens,
-                                          send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, w.krows, s))
+                                          send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, send_pos, pos_limit, w.krows, s))
           return st;
         r.x = w.krows;
         r.x_layer_stride = static_cast<int64_t>(w.rows_cap) * row_elems;
@@ -270,7 +318,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
         r.x_f16 = 0;
       }
       if (w.tab_recv) {
-        if (int st = launch_rope_table(w.tab_recv, recv_tab_rows(recv->tokens), recv->head_dim, recv->rope_base, s))
+        if (int st = launch_rope_table(w.tab_recv, recv_tab_rows_for(recv, pos_limit), recv->head_dim, recv->rope_base, s))
           return st;
       }
       r.rotate = w.tab_recv ? 1 : 0;
@@ -310,11 +358,11 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   if (do_k) {
     FlatRole r{};
     if (w.tab_send) {
-      if (int st = launch_rope_table(w.tab_send, send->tokens, send->head_dim, send->rope_base, s)) return st;
+      if (int st = launch_rope_table(w.tab_send, send_tab_rows(send, pos_limit), send->head_dim, send->rope_base, s)) return st;
       uint8_t used[MAX_LAYERS] = {0};
       for (int32_t i = 0; i < recv->layers * n_taps; ++i) used[taps[i]] = 1;
       if (int st = launch_derotate_rows(static_cast<const uint16_t*>(k_send), send->layers, send->tokens,
-                                        send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, w.krows, s))
+                                        send->kv_heads, used, w.runs, w.rows_cap, w.tab_send, send_pos, pos_limit, w.krows, s))
         return st;
       r.a_src = w.krows;
       r.a_layer_stride = static_cast<int64_t>(w.rows_cap) * send_row;
@@ -327,7 +375,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
       r.a_f16 = 0;
     }
     if (w.tab_recv) {
-      if (int st = launch_rope_table(w.tab_recv, recv_tab_rows(recv->tokens), recv->head_dim, recv->rope_base, s))
+      if (int st = launch_rope_table(w.tab_recv, recv_tab_rows_for(recv, pos_limit), recv->head_dim, recv->rope_base, s))
         return st;
     }
     if (split) {
@@ -375,6 +423,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   p.tab_recv = w.tab_recv;
   p.runs = w.runs;
   p.knorm_eps = static_cast<float>(recv->k_norm_eps);
+  p.slot = slot;
+  p.pool_rows = pool_rows;
+  p.recv_pos = recv_pos;
+  p.pos_limit = pos_limit;
   return main_kernel([&] { return launch_flat(p, roles, n, s); });
 }
 
@@ -387,7 +439,22 @@ int kvx_translate(const kvx_cache_desc* send, const void* k_send, const void* v_
                   int32_t per_head, int32_t w_dtype, const void* wt_k, const void* wt_v, const float* b_k,
                   const float* b_v, void* workspace, size_t ws_bytes, void* stream) {
   return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr);
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+size_t kvx_translate_placed_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
+                                           int32_t per_head, int32_t pos_limit) {
+  if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS || pos_limit < 0) return 0;
+  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, nullptr).bytes;
+}
+
+int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                         const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
+                         const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
+                         const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                         void* stream, const kvx_placement* place) {
+  return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, place);
 }
 
 int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
@@ -405,7 +472,7 @@ int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const vo
       return KVX_ERR_HIP;
     }
   int st = translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev);
+                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
   if (st == KVX_OK) {
     // events exist only when work was launched (empty problems return early)
     if (hipEventSynchronize(ev[2]) != hipSuccess ||

@@ -19,6 +19,8 @@
 // state): uniq[u] = value of run u, run_begin[u] = first receiver row of run
 // u (run_begin[U] = N), recv_to_uniq[i] = run of row i, and U.
 
+#include <vector>
+
 #include "kvx_internal.hpp"
 
 namespace kvx {
@@ -145,8 +147,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void align_match_scan(
   scan_tile_local<OpMax>(out, n_recv, agg);
 }
 
+// `add`: the sequence's first token in a concatenation of sender sequences.
 __global__ __launch_bounds__(SCAN_THREADS) void align_finish(int32_t* __restrict__ out, int32_t n,
-                                                             const int32_t* __restrict__ carry) {
+                                                             const int32_t* __restrict__ carry, int32_t add) {
   const int64_t base = static_cast<int64_t>(blockIdx.x) * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
   const int32_t c = carry[blockIdx.x];
 #pragma unroll
@@ -154,33 +157,63 @@ __global__ __launch_bounds__(SCAN_THREADS) void align_finish(int32_t* __restrict
     const int64_t i = base + k;
     if (i < n) {
       const int32_t v = OpMax::apply(c, out[i]);
-      out[i] = v < 0 ? 0 : v;
+      out[i] = (v < 0 ? 0 : v) + add;
     }
   }
 }
 
 size_t align_ws_bytes(int32_t n_recv) {
-  const int64_t tiles = ceil_div(n_recv > 0 ? n_recv : 1, SCAN_TILE);
-  return align_up(sizeof(int32_t) * 64, 256) + align_up(sizeof(int32_t) * tiles, 256);
+  const int32_t ro[2] = {0, n_recv > 0 ? n_recv : 1};
+  return align_batched_ws_bytes(ro, 1);
 }
 
-int launch_align(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
-                 int32_t* out, void* ws, hipStream_t s) {
-  Carve c(ws);
-  int32_t* bad = c.take<int32_t>(64);
+// One sequence, no synchronisation: flags invalid offsets in *bad.
+static int align_one(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv, int32_t* out,
+                     int32_t add, int32_t* agg, int32_t* bad, hipStream_t s) {
   const int32_t tiles = static_cast<int32_t>(ceil_div(n_recv, SCAN_TILE));
-  int32_t* agg = c.take<int32_t>(tiles);
-  if (int st = launch_fill_i32(bad, 1, 0, s)) return st;
   align_match_scan<<<tiles, SCAN_THREADS, 0, s>>>(send_end, n_send, recv_end, n_recv, out, agg, bad);
   KVX_LAUNCH_CHECK();
   scan_carries<OpMax><<<1, SCAN_THREADS, 0, s>>>(agg, tiles);
   KVX_LAUNCH_CHECK();
-  align_finish<<<tiles, SCAN_THREADS, 0, s>>>(out, n_recv, agg);
+  align_finish<<<tiles, SCAN_THREADS, 0, s>>>(out, n_recv, agg, add);
   KVX_LAUNCH_CHECK();
-  int32_t host_bad = 0;
-  KVX_HIP_TRY(hipMemcpyAsync(&host_bad, bad, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  return KVX_OK;
+}
+
+int launch_align(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                 int32_t* out, void* ws, hipStream_t s) {
+  const int32_t so[2] = {0, n_send}, ro[2] = {0, n_recv};
+  return launch_align_batched(send_end, so, recv_end, ro, 1, out, ws, s);
+}
+
+size_t align_batched_ws_bytes(const int32_t* recv_off, int32_t n_seq) {
+  int32_t longest = 1;
+  for (int32_t q = 0; q < n_seq; ++q) longest = max(longest, recv_off[q + 1] - recv_off[q]);
+  return align_up(sizeof(int32_t) * (static_cast<size_t>(n_seq) + 64), 256) +
+         align_up(sizeof(int32_t) * ceil_div(longest, SCAN_TILE), 256);
+}
+
+int launch_align_batched(const int32_t* send_end, const int32_t* send_off, const int32_t* recv_end,
+                         const int32_t* recv_off, int32_t n_seq, int32_t* out, void* ws, hipStream_t s) {
+  Carve c(ws);
+  int32_t* bad = c.take<int32_t>(static_cast<size_t>(n_seq) + 64);
+  int32_t longest = 1;
+  for (int32_t q = 0; q < n_seq; ++q) longest = max(longest, recv_off[q + 1] - recv_off[q]);
+  int32_t* agg = c.take<int32_t>(ceil_div(longest, SCAN_TILE));  // reused in stream order
+  if (int st = launch_fill_i32(bad, n_seq, 0, s)) return st;
+  for (int32_t q = 0; q < n_seq; ++q) {
+    const int32_t nr = recv_off[q + 1] - recv_off[q];
+    if (nr == 0) continue;
+    if (int st = align_one(send_end + send_off[q], send_off[q + 1] - send_off[q], recv_end + recv_off[q], nr,
+                           out + recv_off[q], send_off[q], agg, bad + q, s))
+      return st;
+  }
+  std::vector<int32_t> host_bad(static_cast<size_t>(n_seq), 0);
+  KVX_HIP_TRY(hipMemcpyAsync(host_bad.data(), bad, sizeof(int32_t) * n_seq, hipMemcpyDeviceToHost, s));
   KVX_HIP_TRY(hipStreamSynchronize(s));
-  return host_bad ? KVX_ERR_INVALID : KVX_OK;
+  for (int32_t q = 0; q < n_seq; ++q)
+    if (host_bad[q]) return KVX_ERR_INVALID;
+  return KVX_OK;
 }
 
 // ---------------------------------------------------------------- run compaction

@@ -76,6 +76,10 @@ struct FlatKArgs {
   int32_t rotate[2];
   const float* knorm[2];  // key-normalisation weights [L_R][128] or null
   float knorm_eps;
+  const int64_t* slot;     // output row of each receiver token, or null (row i)
+  int64_t pool_rows;       // output rows per layer
+  const int32_t* recv_pos; // rotary position of each receiver token, or null (i)
+  int32_t pos_limit;
   int32_t n_roles;
   int32_t recv_layers, recv_tokens, k_dim, f_out, send_row, n_taps;
   const float2* tab_recv;
@@ -208,7 +212,10 @@ __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p
 }
 #undef FT_STEP
 
-// Both operand types in one launch: the K loop is chosen per tile.
+// Both operand types in one launch: the K loop is chosen per tile.  PLACED:
+// output rows from the slot array and rotary positions per token (else row
+// and position i).
+template <bool PLACED>
 __global__ __attribute__((amdgpu_flat_work_group_size(FT_THREADS, FT_THREADS), amdgpu_waves_per_eu(2, 2))) void
 flat_gemm_kernel(const FlatKArgs args) {
   __shared__ __attribute__((aligned(1024))) uint16_t p0[FT_PART_ELEMS];
@@ -313,7 +320,8 @@ flat_gemm_kernel(const FlatKArgs args) {
     // (channels 8q.. and 64 + 8q.., read where used: L1-resident)
     const float* kn = args.knorm[role];
     const float4* g4 = kn ? reinterpret_cast<const float4*>(kn + static_cast<int64_t>(l) * 128 + 8 * q) : nullptr;
-    uint16_t* outp = args.out[role] + static_cast<int64_t>(l) * args.recv_tokens * args.f_out + n0 + col;
+    uint16_t* outp = args.out[role] + static_cast<int64_t>(l) * args.pool_rows * args.f_out + n0 + col;
+    const int32_t* rpos = (PLACED && rot) ? args.recv_pos : nullptr;  // per-token positions, no recurrence
     // every wave has finished reading the parts
     KVX_COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
@@ -354,7 +362,7 @@ flat_gemm_kernel(const FlatKArgs args) {
       const int32_t p0 = args.run_begin[u0];
       const int32_t n = args.run_begin[min(u0 + 32, U)] - p0;
       float cs[8], sn[8], c8[8], s8[8];
-      if (rot) {
+      if (rot && !rpos) {
         const float4* t8 = reinterpret_cast<const float4*>(args.tab_recv + 8 * 64 + 8 * q);
         const float4* t0 = reinterpret_cast<const float4*>(args.tab_recv + static_cast<int64_t>(p0 + min(grp, n - 1)) * 64 + 8 * q);
 #pragma unroll
@@ -398,7 +406,22 @@ flat_gemm_kernel(const FlatKArgs args) {
                 b[e] *= sc * gb[e];
               }
             }
-            if (rot) {
+            if (rpos) {
+              // position of this receiver token (several sequences): table row
+              int32_t pp = rpos[p0 + off];
+              pp = pp < 0 ? 0 : (pp >= args.pos_limit ? args.pos_limit - 1 : pp);
+              const float4* tp = reinterpret_cast<const float4*>(args.tab_recv + static_cast<int64_t>(pp) * 64 + 8 * q);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const float4 t = tp[w];  // (cos, sin) of pairs 2w and 2w+1
+                const float ra0 = a[2 * w] * t.x - b[2 * w] * t.y;
+                b[2 * w] = a[2 * w] * t.y + b[2 * w] * t.x;
+                a[2 * w] = ra0;
+                const float ra1 = a[2 * w + 1] * t.z - b[2 * w + 1] * t.w;
+                b[2 * w + 1] = a[2 * w + 1] * t.w + b[2 * w + 1] * t.z;
+                a[2 * w + 1] = ra1;
+              }
+            } else if (rot) {
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const float ra = a[e] * cs[e] - b[e] * sn[e];
@@ -406,13 +429,17 @@ flat_gemm_kernel(const FlatKArgs args) {
                 a[e] = ra;
               }
             }
-            uint16_t* o = outp + static_cast<int64_t>(p0 + off) * args.f_out;
-            *reinterpret_cast<u32x4*>(o) = u32x4{cvt_bf16x2(a[0], a[1]), cvt_bf16x2(a[2], a[3]),
-                                                 cvt_bf16x2(a[4], a[5]), cvt_bf16x2(a[6], a[7])};
-            *reinterpret_cast<u32x4*>(o + 64) = u32x4{cvt_bf16x2(b[0], b[1]), cvt_bf16x2(b[2], b[3]),
-                                                      cvt_bf16x2(b[4], b[5]), cvt_bf16x2(b[6], b[7])};
+            int64_t orow = p0 + off;
+            if (PLACED && args.slot) orow = args.slot[p0 + off];
+            if (orow >= 0 && orow < args.pool_rows) {
+              uint16_t* o = outp + orow * args.f_out;
+              *reinterpret_cast<u32x4*>(o) = u32x4{cvt_bf16x2(a[0], a[1]), cvt_bf16x2(a[2], a[3]),
+                                                   cvt_bf16x2(a[4], a[5]), cvt_bf16x2(a[6], a[7])};
+              *reinterpret_cast<u32x4*>(o + 64) = u32x4{cvt_bf16x2(b[0], b[1]), cvt_bf16x2(b[2], b[3]),
+                                                        cvt_bf16x2(b[4], b[5]), cvt_bf16x2(b[6], b[7])};
+            }
           }
-          if (rot) {
+          if (rot && !rpos) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float cn = cs[e] * c8[e] - sn[e] * s8[e];
@@ -523,7 +550,14 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
     a.knorm[j] = roles[j].knorm;
   }
   a.knorm_eps = p.knorm_eps;
-  flat_gemm_kernel<<<G, FT_THREADS, 0, s>>>(a);
+  a.slot = p.slot;
+  a.pool_rows = p.pool_rows;
+  a.recv_pos = p.recv_pos;
+  a.pos_limit = p.pos_limit;
+  if (p.slot || p.recv_pos || p.pool_rows != p.recv_tokens)
+    flat_gemm_kernel<true><<<G, FT_THREADS, 0, s>>>(a);
+  else
+    flat_gemm_kernel<false><<<G, FT_THREADS, 0, s>>>(a);
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }

@@ -15,6 +15,11 @@ int launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ---------------------------------------------------------------- alignment / runs
 size_t align_ws_bytes(int32_t n_recv);
+// Several sequences concatenated (host offset arrays of n_seq + 1 entries);
+// out holds indices into the concatenated sender tokens.
+size_t align_batched_ws_bytes(const int32_t* recv_off, int32_t n_seq);
+int launch_align_batched(const int32_t* send_end, const int32_t* send_off, const int32_t* recv_end,
+                         const int32_t* recv_off, int32_t n_seq, int32_t* out, void* ws, hipStream_t s);
 int launch_align(const int32_t* send_end, int32_t n_send, const int32_t* recv_end,
                  int32_t n_recv, int32_t* out, void* ws, hipStream_t s);
 
@@ -35,9 +40,12 @@ int launch_rope_table(float2* tab, int32_t n_pos, int32_t head_dim, double base,
 // Rotated-back sender keys of the unique rows as fp16:
 // out[s][u][h][c] for u < U (device count), every sender layer s with
 // layer_used[s] != 0.  Requires head_dim == 128, bf16 cache.
+// pos (device [send_tokens], or null = token index): rotary position of each
+// sender token, clamped to [0, pos_limit).
 int launch_derotate_rows(const uint16_t* k_send, int32_t send_layers, int32_t send_tokens,
                          int32_t heads, const uint8_t* layer_used, const Runs& r,
-                         int32_t rows_cap, const float2* tab_send, uint16_t* out, hipStream_t s);
+                         int32_t rows_cap, const float2* tab_send, const int32_t* pos,
+                         int32_t pos_limit, uint16_t* out, hipStream_t s);
 
 // ---------------------------------------------------------------- flattened translation
 struct FlatRole {
@@ -60,6 +68,10 @@ struct FlatProblem {
   const float2* tab_recv;
   Runs runs;
   float knorm_eps;
+  const int64_t* slot;     // [N_R] output row of each receiver token, or null (row i)
+  int64_t pool_rows;       // output rows per layer
+  const int32_t* recv_pos; // [N_R] rotary position of each receiver token, or null (i)
+  int32_t pos_limit;       // positions clamped to [0, pos_limit)
 };
 
 int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s);
@@ -76,6 +88,10 @@ struct HeadProblem {
   const int32_t* taps;         // host [L_R][1]
   const int32_t* recv_to_send;
   const float2* tab_recv;      // receiver RoPE table (rotated roles)
+  const int64_t* slot;         // [N_R] output row of each receiver token, or null (row i)
+  int64_t pool_rows;           // output rows per layer
+  const int32_t* recv_pos;     // [N_R] rotary position of each receiver token, or null (i)
+  int32_t pos_limit;
 };
 struct HeadRole {
   const uint16_t* x;       // sender rows: [L_S][N_S][H][128] bf16, or compact [L_S][rows][H][128] fp16

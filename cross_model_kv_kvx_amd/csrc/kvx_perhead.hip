@@ -57,6 +57,10 @@ struct HeadKArgs {
   const float* bias[2];
   uint16_t* out[2];
   const float2* tab_recv;
+  const int64_t* slot;      // output row of each receiver token, or null (row i)
+  int64_t pool_rows;        // output rows per layer
+  const int32_t* recv_pos;  // rotary position of each receiver token, or null (i)
+  int32_t pos_limit;
   int32_t recv_layers, recv_tokens, heads, n_span, n_blocks, xcd_remap;
   uint8_t tap[MAX_LAYERS];  // sender layer of each receiver layer
 };
@@ -112,9 +116,13 @@ struct PhRot {
 // Fragments of one tile, MFMA D[n][tok] += W[n][k] X[tok][k]; add the bias,
 // rotate pairs when `rot`, stage (bf16 nearest even) into `ys` as [tok][n]
 // with swizzled chunks.
+// With per-token positions (`rpos`), the (cos, sin) of the lane's tokens
+// (tile tokens from `tok0`) are read from the table instead of stepped.
 template <bool WF32, bool F16>
 __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, const u32x4 (&wh)[8],
-                                           const u32x4 (&wl)[8], const float (&bn)[16], bool rot, PhRot& rs) {
+                                           const u32x4 (&wl)[8], const float (&bn)[16], bool rot, PhRot& rs,
+                                           const int32_t* rpos, const float2* tab, int32_t tok0, int32_t n_tok_all,
+                                           int32_t pos_limit) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const char* xb = reinterpret_cast<const char*>(xs);
   f32x16 acc[2];
@@ -143,7 +151,17 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
     float v[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = acc[ti][r] + bn[r];
-    if (rot) {
+    if (rot && rpos) {
+      int32_t pp = rpos[min(tok0 + 32 * ti + (lane & 31), n_tok_all - 1)];
+      pp = pp < 0 ? 0 : (pp >= pos_limit ? pos_limit - 1 : pp);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float2 t = tab[static_cast<int64_t>(pp) * 64 + ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))];
+        const float a = v[r], b = v[r + 8];
+        v[r] = a * t.x - b * t.y;
+        v[r + 8] = a * t.y + b * t.x;
+      }
+    } else if (rot) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const float a = v[r], b = v[r + 8];
@@ -167,7 +185,10 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
 // Store a staged tile by the 256 threads of the store waves: thread t writes
 // 16 bytes of row 16 q + t / 16 for q = 0..3 (rows past the span end are
 // skipped).
-__device__ __forceinline__ void ph_store(const uint16_t* ys, uint16_t* out_tile, int32_t rows, int64_t row_elems) {
+// outb: row 0 of the layer and head in the output pool; tok0: the tile's
+// first receiver token; slot: output row of each token (null: the token).
+__device__ __forceinline__ void ph_store(const uint16_t* ys, uint16_t* outb, int32_t tok0, int32_t rows,
+                                         int64_t row_elems, const int64_t* slot, int64_t pool_rows) {
   const int t = threadIdx.x - 256;
   const char* yb = reinterpret_cast<const char*>(ys);
 #pragma unroll
@@ -175,7 +196,10 @@ __device__ __forceinline__ void ph_store(const uint16_t* ys, uint16_t* out_tile,
     const int row = 16 * q + (t >> 4);
     const int c = t & 15;
     const u32x4 v = *reinterpret_cast<const u32x4*>(yb + row * 256 + 16 * ph_chunk(row, c));
-    if (row < rows) *reinterpret_cast<u32x4*>(out_tile + row * row_elems + 8 * c) = v;
+    if (row < rows) {
+      const int64_t orow = slot ? slot[tok0 + row] : static_cast<int64_t>(tok0 + row);
+      if (orow >= 0 && orow < pool_rows) *reinterpret_cast<u32x4*>(outb + orow * row_elems + 8 * c) = v;
+    }
   }
 }
 
@@ -221,7 +245,7 @@ perhead_kernel(const HeadKArgs a) {
   pt.row_bytes = static_cast<uint32_t>(2 * row_elems);
   const uint16_t* xs = a.x[role] + static_cast<int64_t>(s) * a.x_layer_stride[role] + h * 128;
   pt.xr = buf_rsrc(xs, static_cast<uint32_t>(static_cast<int64_t>(x_rows) * 2 * row_elems - 256 * h));
-  uint16_t* out = a.out[role] + (static_cast<int64_t>(l) * a.recv_tokens + pt.t0) * row_elems + h * 128;
+  uint16_t* outb = a.out[role] + static_cast<int64_t>(l) * a.pool_rows * row_elems + h * 128;
 
   // the span's sender rows, clamped to valid rows (entries past the span
   // repeat its last token)
@@ -238,8 +262,8 @@ perhead_kernel(const HeadKArgs a) {
     ph_barrier();  // B_0
     for (int32_t k = 1; k <= pt.n_tiles; ++k) {
       ph_barrier();  // B_k: store tile k-1
-      ph_store(((k - 1) & 1) ? y1 : y0, out + static_cast<int64_t>(k - 1) * PH_TILE * row_elems,
-               pt.n_tok - (k - 1) * PH_TILE, row_elems);
+      ph_store(((k - 1) & 1) ? y1 : y0, outb, pt.t0 + (k - 1) * PH_TILE, pt.n_tok - (k - 1) * PH_TILE, row_elems,
+               a.slot, a.pool_rows);
     }
     return;
   }
@@ -248,8 +272,9 @@ perhead_kernel(const HeadKArgs a) {
   // so waiting for them never waits for a tile): the lane's tokens of tile 0
   // and the step by one tile.
   const bool rot = a.rotate[role] != 0;
+  const int32_t* rpos = rot ? a.recv_pos : nullptr;
   PhRot rs;
-  if (rot) {
+  if (rot && !rpos) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int pr = ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));  // pair index (< 64)
@@ -335,7 +360,9 @@ perhead_kernel(const HeadKArgs a) {
       ph_barrier();                                                            \
     }                                                                          \
     ph_issue(pt, (K) + PH_RING - 1, XNEXT);                                    \
-    if ((K) < pt.n_tiles) ph_compute<WF32, F16>(XS, YS, wh, wl, bn, rot, rs);  \
+    if ((K) < pt.n_tiles)                                                      \
+      ph_compute<WF32, F16>(XS, YS, wh, wl, bn, rot, rs, rpos, a.tab_recv,      \
+                            pt.t0 + (K) * PH_TILE, a.recv_tokens, a.pos_limit); \
   }
   for (int32_t k = 0; k < pt.n_tiles; k += 6) {
     PH_STEP(k, x0, y0, x5)
@@ -377,6 +404,10 @@ int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hip
     }
     if (n == 0) continue;
     a.tab_recv = p.tab_recv;
+    a.slot = p.slot;
+    a.pool_rows = p.pool_rows;
+    a.recv_pos = p.recv_pos;
+    a.pos_limit = p.pos_limit;
     a.recv_layers = p.recv_layers;
     a.recv_tokens = p.recv_tokens;
     a.heads = p.heads;

@@ -49,7 +49,7 @@ struct LayerList {
 __global__ __launch_bounds__(256) void derotate_rows_kernel(
     const uint16_t* __restrict__ k_send, int32_t send_tokens, int32_t heads, const int32_t* __restrict__ uniq,
     const int32_t* __restrict__ n_uniq, int32_t rows_cap, const float2* __restrict__ tab,
-    uint16_t* __restrict__ out, const LayerList layers) {
+    const int32_t* __restrict__ pos, int32_t pos_limit, uint16_t* __restrict__ out, const LayerList layers) {
   const int32_t U = min(*n_uniq, rows_cap);
   const int32_t row0 = blockIdx.x * DR_ROWS;
   if (row0 >= U) return;
@@ -65,7 +65,12 @@ __global__ __launch_bounds__(256) void derotate_rows_kernel(
     const uint16_t* src = k_send + (static_cast<int64_t>(layer) * send_tokens + p) * row_elems + h * 128;
     const u32x4 a = *reinterpret_cast<const u32x4*>(src + 8 * q);
     const u32x4 b = *reinterpret_cast<const u32x4*>(src + 64 + 8 * q);
-    const float4* t4 = reinterpret_cast<const float4*>(tab + static_cast<int64_t>(p) * 64 + 8 * q);
+    int32_t pp = p;  // rotary position of the sender token
+    if (pos) {
+      pp = pos[p];
+      pp = pp < 0 ? 0 : (pp >= pos_limit ? pos_limit - 1 : pp);
+    }
+    const float4* t4 = reinterpret_cast<const float4*>(tab + static_cast<int64_t>(pp) * 64 + 8 * q);
     uint32_t oa[4], ob[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256) void derotate_rows_kernel(
 
 int launch_derotate_rows(const uint16_t* k_send, int32_t send_layers, int32_t send_tokens, int32_t heads,
                          const uint8_t* layer_used, const Runs& r, int32_t rows_cap, const float2* tab_send,
-                         uint16_t* out, hipStream_t s) {
+                         const int32_t* pos, int32_t pos_limit, uint16_t* out, hipStream_t s) {
   if (rows_cap <= 0) return KVX_OK;
   LayerList ll{};
   int n = 0;
@@ -94,8 +99,8 @@ int launch_derotate_rows(const uint16_t* k_send, int32_t send_layers, int32_t se
     if (layer_used[l]) ll.l[n++] = static_cast<uint8_t>(l);
   if (n == 0) return KVX_OK;
   const dim3 grid(static_cast<unsigned>(ceil_div(rows_cap, DR_ROWS)), static_cast<unsigned>(n));
-  derotate_rows_kernel<<<grid, 256, 0, s>>>(k_send, send_tokens, heads, r.uniq, r.n_uniq, rows_cap, tab_send, out,
-                                            ll);
+  derotate_rows_kernel<<<grid, 256, 0, s>>>(k_send, send_tokens, heads, r.uniq, r.n_uniq, rows_cap, tab_send, pos,
+                                            pos_limit, out, ll);
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }

@@ -25,8 +25,9 @@ F32, BF16 = 0, 1
 OK, ERR_INVALID, ERR_SHAPE, ERR_WORKSPACE, ERR_NOT_SPD, ERR_HIP, ERR_UNSUPPORTED = range(7)
 
 EXPORTS = (
-    "kvx_status_string", "kvx_align_workspace_size", "kvx_align_tokens", "kvx_layer_map",
-    "kvx_translate_workspace_size", "kvx_translate", "kvx_translate_timed", "kvx_gather_features",
+    "kvx_status_string", "kvx_align_workspace_size", "kvx_align_tokens", "kvx_align_batched_workspace_size",
+    "kvx_align_tokens_batched", "kvx_layer_map", "kvx_translate_workspace_size", "kvx_translate",
+    "kvx_translate_timed", "kvx_translate_placed_workspace_size", "kvx_translate_placed", "kvx_gather_features",
     "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fit_ridge_batched_workspace_size",
     "kvx_fit_ridge_batched", "kvx_fold_lowrank",
 )
@@ -42,6 +43,11 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("tokens", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_double),
                 ("k_norm", ctypes.c_void_p), ("k_norm_eps", ctypes.c_double)]
+
+
+class Placement(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_void_p), ("pool_rows", ctypes.c_int64), ("recv_pos", ctypes.c_void_p),
+                ("send_pos", ctypes.c_void_p), ("pos_limit", ctypes.c_int32)]
 
 
 _lib = None
@@ -62,12 +68,17 @@ def lib() -> ctypes.CDLL:
             "kvx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "kvx_align_workspace_size": (sz, [i32]),
             "kvx_align_tokens": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, sz, vp]),
+            "kvx_align_batched_workspace_size": (sz, [ip, i32]),
+            "kvx_align_tokens_batched": (ctypes.c_int, [vp, ip, vp, ip, i32, vp, vp, sz, vp]),
             "kvx_layer_map": (ctypes.c_int, [i32, i32, i32, i32, ip]),
             "kvx_translate_workspace_size": (sz, [dp, dp, i32, i32]),
             "kvx_translate": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp, vp,
                                              vp, sz, vp]),
             "kvx_translate_timed": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp, vp,
                                                    vp, sz, vp, ctypes.POINTER(ctypes.c_float)]),
+            "kvx_translate_placed_workspace_size": (sz, [dp, dp, i32, i32, i32]),
+            "kvx_translate_placed": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp, vp,
+                                                    vp, sz, vp, ctypes.POINTER(Placement)]),
             "kvx_gather_features": (ctypes.c_int, [dp, vp, i32, vp, i32, ip, i32, vp, vp]),
             "kvx_fit_ridge_workspace_size": (sz, [i32, i32]),
             "kvx_fit_ridge": (ctypes.c_int, [vp, i64, vp, i64, i32, i64, i32, i32, dbl, dbl, i32, vp, vp, vp, sz,
@@ -155,6 +166,29 @@ def align_tokens(send_end: torch.Tensor, recv_end: torch.Tensor, out: Optional[t
     return out
 
 
+def align_tokens_batched(send_end: torch.Tensor, send_off, recv_end: torch.Tensor, recv_off,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """kvx_align_tokens_batched: sequences concatenated (host offsets of
+    n_seq + 1 entries); returns the map into the concatenated sender tokens."""
+    _need(send_end, "send_end", torch.int32)
+    _need(recv_end, "recv_end", torch.int32)
+    so = np.ascontiguousarray(send_off, dtype=np.int32)
+    ro = np.ascontiguousarray(recv_off, dtype=np.int32)
+    n_seq = ro.size - 1
+    if so.size != ro.size or n_seq < 1:
+        raise ValueError("send_off and recv_off need n_seq + 1 entries")
+    ip = ctypes.POINTER(ctypes.c_int32)
+    if out is None:
+        out = torch.empty(int(ro[-1]), dtype=torch.int32, device=recv_end.device)
+    _need(out, "out", torch.int32)
+    ws = _workspace(lib().kvx_align_batched_workspace_size(ro.ctypes.data_as(ip), n_seq), recv_end.device, workspace)
+    st = lib().kvx_align_tokens_batched(_ptr(send_end), so.ctypes.data_as(ip), _ptr(recv_end), ro.ctypes.data_as(ip),
+                                        n_seq, _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kvx_align_tokens_batched")
+    return out
+
+
 def layer_map(send_layers: int, recv_layers: int, n_taps: int = 3, tap_stride: int = 4) -> np.ndarray:
     """kvx_layer_map: host int32 [recv_layers][n_taps]."""
     out = np.zeros((recv_layers, n_taps), dtype=np.int32)
@@ -177,7 +211,10 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
               send_rope_base: float = 0.0, recv_rope_base: float = 0.0,
               k_recv: Optional[torch.Tensor] = None, v_recv: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, stream=None, stage_ms: Optional[list] = None,
-              recv_key_norm: Optional[torch.Tensor] = None, key_norm_eps: float = 1e-6):
+              recv_key_norm: Optional[torch.Tensor] = None, key_norm_eps: float = 1e-6,
+              slot: Optional[torch.Tensor] = None, pool_rows: Optional[int] = None,
+              recv_pos: Optional[torch.Tensor] = None, send_pos: Optional[torch.Tensor] = None,
+              pos_limit: Optional[int] = None):
     """kvx_translate.  Returns (k_recv, v_recv) (either None when its role is
     skipped).  ``taps``: host int32 [L_R][n_taps] (numpy).  With a list
     ``stage_ms``, calls kvx_translate_timed instead (synchronous) and appends
@@ -211,17 +248,36 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
     for name, t in (("b_k", b_k), ("b_v", b_v)):
         if t is not None:
             _need(t, name, torch.float32)
+    placed = any(x is not None for x in (slot, pool_rows, recv_pos, send_pos, pos_limit))
+    rows = N_R if pool_rows is None else int(pool_rows)
     if k_send is not None and k_recv is None:
-        k_recv = torch.empty((L_R, N_R, H_R, d_R), dtype=ref.dtype, device=ref.device)
+        k_recv = torch.empty((L_R, rows, H_R, d_R), dtype=ref.dtype, device=ref.device)
     if v_send is not None and v_recv is None:
-        v_recv = torch.empty((L_R, N_R, H_R, d_R), dtype=ref.dtype, device=ref.device)
-    ws = _workspace(translate_workspace_size(send, recv, n_taps, per_head), ref.device, workspace)
+        v_recv = torch.empty((L_R, rows, H_R, d_R), dtype=ref.dtype, device=ref.device)
+    if placed:
+        if stage_ms is not None:
+            raise ValueError("stage timing is not available with a placement")
+        for name, t, dt in (("slot", slot, torch.int64), ("recv_pos", recv_pos, torch.int32),
+                            ("send_pos", send_pos, torch.int32)):
+            if t is not None:
+                _need(t, name, dt)
+        place = Placement(slot.data_ptr() if slot is not None else None, 0 if pool_rows is None else rows,
+                          recv_pos.data_ptr() if recv_pos is not None else None,
+                          send_pos.data_ptr() if send_pos is not None else None,
+                          int(pos_limit) if pos_limit is not None else 0)
+        ws = _workspace(lib().kvx_translate_placed_workspace_size(ctypes.byref(send), ctypes.byref(recv),
+                                                                  int(n_taps), int(bool(per_head)), place.pos_limit),
+                        ref.device, workspace)
+    else:
+        ws = _workspace(translate_workspace_size(send, recv, n_taps, per_head), ref.device, workspace)
     args = [ctypes.byref(send), _ptr(k_send), _ptr(v_send), ctypes.byref(recv),
             _ptr(k_recv) if k_send is not None else None, _ptr(v_recv) if v_send is not None else None,
             _ptr(recv_to_send), taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_taps),
             int(bool(per_head)), _dtype_code(w_ref), _ptr(wt_k), _ptr(wt_v), _ptr(b_k), _ptr(b_v),
             _ptr(ws), ws.numel(), _stream(stream)]
-    if stage_ms is None:
+    if placed:
+        _check(lib().kvx_translate_placed(*args, ctypes.byref(place)), "kvx_translate_placed")
+    elif stage_ms is None:
         _check(lib().kvx_translate(*args), "kvx_translate")
     else:
         ms = (ctypes.c_float * 2)()

@@ -107,6 +107,27 @@ int kvx_align_tokens(const int32_t* send_end, int32_t n_send,
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * Token alignment of n_seq sequences at once (several requests' caches
+ * translated together).  Their tokens are concatenated: sequence q owns
+ * sender tokens send_off[q] .. send_off[q+1]-1 and receiver tokens
+ * recv_off[q] .. recv_off[q+1]-1 (send_off, recv_off: HOST int32 arrays of
+ * n_seq + 1 non-decreasing entries starting at 0).  send_end / recv_end hold
+ * each sequence's own character-end offsets (each sequence's string starts
+ * at 0), with the rules of kvx_align_tokens per sequence.  recv_to_send
+ * (device int32 [recv_off[n_seq]]) receives indices into the concatenated
+ * sender tokens: the per-sequence alignment plus send_off[q].  A sequence
+ * with receiver tokens and no sender tokens is KVX_ERR_SHAPE.
+ * workspace: kvx_align_batched_workspace_size(recv_off, n_seq) bytes.
+ * Synchronises `stream` once (KVX_ERR_INVALID if any sequence's offsets are
+ * invalid).
+ * ---------------------------------------------------------------------- */
+size_t kvx_align_batched_workspace_size(const int32_t* recv_off, int32_t n_seq);
+int kvx_align_tokens_batched(const int32_t* send_end, const int32_t* send_off,
+                             const int32_t* recv_end, const int32_t* recv_off, int32_t n_seq,
+                             int32_t* recv_to_send, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * Layer matching ("Prefill-Free ...", Methodology 2: proportional depth and
  * taps at -4, 0, +4; "Cross-Model KV Cache Transfer in Production", stage 3).
  *
@@ -202,6 +223,55 @@ int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t
                         const int32_t* recv_to_send, int32_t n_rows,
                         const int32_t* taps_of_layer, int32_t n_taps,
                         void* x_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Translation placed into the receiver's paged KV cache, for one or several
+ * sequences at once ("Cross-Model KV Cache Transfer in Production", stage 4:
+ * the translated keys and values go straight into the receiver's
+ * PagedAttention cache slots; "Prefill-Free ...", Main Findings: requests
+ * translated in batches).
+ *
+ * Arguments as kvx_translate, plus `place` (host, may be NULL = plain
+ * kvx_translate):
+ *   slot: device int64 [recv->tokens] or NULL: the row of receiver token i in
+ *     the output pool; k_recv / v_recv are then [recv->layers][pool_rows]
+ *     [H_R][d_R] and layer l of token i is written at row l * pool_rows +
+ *     slot[i] (a slot outside [0, pool_rows) writes nothing).  NULL: row i,
+ *     pool_rows >= recv->tokens (0 means recv->tokens).
+ *   recv_pos: device int32 [recv->tokens] or NULL: rotary position of
+ *     receiver token i (NULL: i).  send_pos: device int32 [send->tokens] or
+ *     NULL: rotary position of sender token j (NULL: j).  Positions are
+ *     clamped to [0, pos_limit).
+ *   pos_limit: > every position given; sizes the rotation tables.
+ * Several sequences: concatenate their sender tokens and their receiver
+ * tokens, take recv_to_send from kvx_align_tokens_batched (indices into the
+ * concatenated sender tokens), positions relative to each sequence's start,
+ * and slots from each sequence's block table (slot = block * block_size +
+ * offset).  Runs of equal sender tokens never cross sequences, so each
+ * sequence's rows are exactly its own translation.
+ * workspace: kvx_translate_placed_workspace_size(send, recv, n_taps,
+ *   per_head, pos_limit) bytes.
+ * Supported on the bf16 paths (flattened and per head); fp32 caches with a
+ * placement give KVX_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const int64_t* slot;
+  int64_t pool_rows;
+  const int32_t* recv_pos;
+  const int32_t* send_pos;
+  int32_t pos_limit;
+} kvx_placement;
+
+size_t kvx_translate_placed_workspace_size(const kvx_cache_desc* send,
+                                           const kvx_cache_desc* recv, int32_t n_taps,
+                                           int32_t per_head, int32_t pos_limit);
+int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                         const kvx_cache_desc* recv, void* k_recv, void* v_recv,
+                         const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                         int32_t per_head, int32_t w_dtype, const void* wt_k,
+                         const void* wt_v, const float* b_k, const float* b_v,
+                         void* workspace, size_t ws_bytes, void* stream,
+                         const kvx_placement* place);
 
 /* ------------------------------------------------------------------------
  * Closed-form ridge fit ("Cross-Model KV Cache Transfer in Production",

@@ -432,6 +432,78 @@ def test_flat_key_norm_all_elements(rope):
         assert err <= TOL_BF16
 
 
+def multi_sequence_case(per_head, lengths=(150, 333, 70), seed=91, block=16):
+    """Sequences of ragged lengths concatenated, aligned by one batched call,
+    translated by one placed call into a shuffled pool of 16-row blocks with
+    positions relative to each sequence; each sequence's rows (gathered
+    through its slots) against the oracle on that sequence alone, rows of the
+    pool no slot names untouched."""
+    rng = np.random.default_rng(seed)
+    ends = [synth.token_ends(n, seed + q) for q, n in enumerate(lengths)]
+    so = np.concatenate([[0], np.cumsum([len(e[0]) for e in ends])]).astype(np.int32)
+    ro = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    send_end = dev_i32(np.concatenate([e[0] for e in ends]))
+    recv_end = dev_i32(np.concatenate([e[1] for e in ends]))
+    tm = kvx.align_tokens_batched(send_end, so, recv_end, ro)
+    maps_o = [O.token_align(*e) for e in ends]
+    assert np.array_equal(tm.cpu().numpy(), np.concatenate([m + so[q] for q, m in enumerate(maps_o)]))
+    L_S, L_R, n_taps = (8, 20, 1) if per_head else (36, 32, 3)
+    shp = synth.CacheShape(L_S, int(so[-1]), 8, 128)
+    taps = kvx.layer_map(L_S, L_R, n_taps, 4)
+    caches, maps, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, seed * 10 + r, DEV, channel_scale="loguniform")
+        if per_head:
+            wt, b = synth.perhead_maps(L_R, 8, 128, seed * 10 + 5 + r, DEV)
+            maps[role] = (wt, host(wt).numpy().astype(np.float64))
+        else:
+            wt, _, _, b = synth.flat_maps(L_R, 3072, 1024, seed * 10 + 5 + r, DEV, 16)
+            wb = host(wt).to(torch.bfloat16)
+            maps[role] = (wb.to(DEV), Bf16Maps(wb.view(torch.int16).numpy().view(np.uint16)))
+            del wt
+        bias[role] = b
+    # block tables: every sequence takes shuffled blocks of a pool with spare blocks
+    nblk = [(n + block - 1) // block for n in lengths]
+    pool_blocks = sum(nblk) + 5
+    perm = rng.permutation(pool_blocks)
+    slot, used, b0 = [], [], 0
+    for q, n in enumerate(lengths):
+        table = perm[b0:b0 + nblk[q]]
+        b0 += nblk[q]
+        j = np.arange(n)
+        slot.append(table[j // block] * block + j % block)
+    slot = np.concatenate(slot).astype(np.int64)
+    pool_rows = pool_blocks * block
+    recv_pos = np.concatenate([np.arange(n) for n in lengths]).astype(np.int32)
+    send_pos = np.concatenate([np.arange(so[q + 1] - so[q]) for q in range(len(lengths))]).astype(np.int32)
+    pos_limit = int(max(max(lengths), int(np.max(np.diff(so)))))
+    outs = {role: torch.full((L_R, pool_rows, 8, 128), 7.0, dtype=torch.bfloat16, device=DEV) for role in "kv"}
+    kvx.translate(caches["k"], caches["v"], tm, taps, maps["k"][0], maps["v"][0], bias["k"], bias["v"],
+                  per_head=per_head, send_rope_base=5e5, recv_rope_base=1e6, k_recv=outs["k"], v_recv=outs["v"],
+                  slot=torch.as_tensor(slot, device=DEV), pool_rows=pool_rows,
+                  recv_pos=torch.as_tensor(recv_pos, device=DEV), send_pos=torch.as_tensor(send_pos, device=DEV),
+                  pos_limit=pos_limit)
+    torch.cuda.synchronize()
+    free = np.setdiff1d(np.arange(pool_rows), slot)
+    for role in ("k", "v"):
+        rk = role == "k"
+        assert torch.all(outs[role][:, torch.as_tensor(free, device=DEV)] == 7.0)
+        for q, n in enumerate(lengths):
+            cache_q = caches[role][:, so[q]:so[q + 1]]
+            want = O.translate_rows(cache_q, maps_o[q], taps, maps[role][1], host(bias[role]).numpy().astype(np.float64),
+                                    np.arange(n), per_head=per_head, recv_heads=8, recv_head_dim=128,
+                                    send_rope_base=5e5 if rk else 0.0, recv_rope_base=1e6 if rk else 0.0)
+            err = O.rel_err(rows_of(outs[role], slot[ro[q]:ro[q + 1]]), want)
+            say(f"  sequence {q} ({n} tokens) {role}: max|err|/RMS = {err:.4e}")
+            assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_multi_sequence_into_paged_pool(per_head):
+    say(f"three sequences, paged pool, {'per-head' if per_head else 'flattened'} + RoPE")
+    multi_sequence_case(per_head)
+
+
 def test_translate_deterministic_and_identity_maps():
     say("determinism + identity maps")
     c = flat_case(3, 520, seed=23)
