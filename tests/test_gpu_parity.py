@@ -392,6 +392,50 @@ def test_flat_fp32_maps_all_elements():
         assert err <= TOL_BF16
 
 
+def test_perhead_rope_full_size_sampled_rows():
+    """The per-head setting with rotated keys at the size the bench times
+    (32 -> 80 layers, 4096 tokens, fp32 maps), sampled rows."""
+    say("per-head + RoPE 32 -> 80 layers, 4096 tokens, sampled rows")
+    shp = synth.CacheShape(32, 4096, 8, 128)
+    taps = kvx.layer_map(32, 80, 1)
+    ident = np.arange(4096)
+    rows = sample_rows(ident, 96, 5)
+    for r, role in enumerate(("k", "v")):
+        x = synth.sender_cache(shp, 200 + r, DEV, channel_scale="loguniform")
+        wt, b = synth.perhead_maps(80, 8, 128, 220 + r, DEV)
+        rk = role == "k"
+        kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rk else {}
+        out, _ = kvx.translate(x, None, dev_i32(ident), taps, wt, None, b, None, per_head=True, **kw)
+        want = O.translate_rows(x, ident, taps, host(wt).numpy().astype(np.float64),
+                                host(b).numpy().astype(np.float64), rows, per_head=True, recv_heads=8,
+                                recv_head_dim=128, send_rope_base=5e5 if rk else 0.0,
+                                recv_rope_base=1e6 if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+        del x, wt, out
+
+
+def test_flat_key_norm_full_size_sampled_rows():
+    """Receiver key normalisation on the 32k cross-family setting (the bench's
+    key-norm line), sampled rows of the key output."""
+    say("flattened + RoPE + key norm, 32768 tokens, sampled rows")
+    c = flat_case(4)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    kn = synth.key_norm_weights(32, 128, 430, DEV)
+    k, _ = kvx.translate(c["k_send"], None, dev_i32(tmap_o), taps, c["wt_k"], None, c["b_k"], None,
+                         send_rope_base=c["send_rope"], recv_rope_base=c["recv_rope"], recv_key_norm=kn,
+                         key_norm_eps=1e-6)
+    rows = sample_rows(tmap_o, 128, 7)
+    want = O.translate_rows(c["k_send"], tmap_o, taps, c["wt_o_k"], c["b_o_k"], rows, per_head=False, recv_heads=8,
+                            recv_head_dim=128, send_rope_base=c["send_rope"], recv_rope_base=c["recv_rope"],
+                            recv_key_norm=host(kn).numpy(), key_norm_eps=1e-6)
+    err = O.rel_err(rows_of(k, rows), want)
+    say(f"  k: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+    assert err <= TOL_BF16
+
+
 @pytest.mark.parametrize("rope", [True, False])
 def test_flat_key_norm_all_elements(rope):
     """The receiver's key normalisation in the flattened epilogue (after the
