@@ -324,6 +324,54 @@ def ridge_fit(x, y, lam_abs: float = 0.0, lam_rel: float = 0.0, fit_intercept: b
 
 
 # ---------------------------------------------------------------------------
+# Recolor: moment-matched affine map   [HF] Key Contributions 2, Methodology 3
+
+
+def spd_power(s, p: float) -> np.ndarray:
+    """S^p of a symmetric positive definite matrix from its eigendecomposition."""
+    e, v = np.linalg.eigh(np.asarray(s, dtype=np.float64))
+    if e.min() <= 0.0:
+        raise np.linalg.LinAlgError("matrix is not positive definite")
+    return (v * e ** p) @ v.T
+
+
+def recolor_fit(x, y, rho_x: float = 0.0, rho_y: float = 0.0):
+    """Recolor: both feature spaces are whitened, the whitened spaces are
+    aligned by an orthogonal Procrustes solution, then the receiver's
+    covariance and mean are put back.  Steps in the pages' order:
+
+    1. moments of the calibration rows: means mu_x, mu_y and covariances
+       S_xx, S_yy, S_xy of the centred rows (divided by n; the scale cancels);
+    2. (reading) whitening needs S_xx and S_yy invertible, and duplicated
+       layer taps make S_xx singular: rho * trace(S) / F is added to each
+       diagonal, relative like the ridge penalty (rho_y = 0 keeps S_yy);
+    3. whitening by the symmetric inverse square roots: a sender row x goes to
+       (x - mu_x) S_xx^-1/2, a receiver row y to (y - mu_y) S_yy^-1/2;
+    4. Procrustes: the map Q with orthonormal columns (rows when F_in < F_out)
+       that best takes whitened x to whitened y maximises tr(Q^T M) for the
+       whitened cross-covariance M = S_xx^-1/2 S_xy S_yy^-1/2, so Q = U V^T
+       from the thin SVD M = U diag(s) V^T;
+    5. recolouring: multiply by S_yy^1/2 and add mu_y, so
+       W = S_xx^-1/2 Q S_yy^1/2 and b = mu_y - mu_x W.
+
+    Returns (W [F_in][F_out], b [F_out]) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    n = x.shape[0]
+    mx, my = x.mean(axis=0), y.mean(axis=0)
+    xc, yc = x - mx, y - my
+    sxx, syy, sxy = xc.T @ xc / n, yc.T @ yc / n, xc.T @ yc / n
+    sxx = sxx + rho_x * np.trace(sxx) / sxx.shape[0] * np.eye(sxx.shape[0])
+    syy = syy + rho_y * np.trace(syy) / syy.shape[0] * np.eye(syy.shape[0])
+    wx = spd_power(sxx, -0.5)
+    wy = spd_power(syy, -0.5)
+    u, _, vt = np.linalg.svd(wx @ sxy @ wy, full_matrices=False)
+    q = u @ vt
+    w = wx @ q @ spd_power(syy, 0.5)
+    return w, my - mx @ w
+
+
+# ---------------------------------------------------------------------------
 # error metric used by the parity tests
 
 
