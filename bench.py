@@ -376,11 +376,10 @@ def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8, key_norm=F
                          "executed_flops_per_launch": flops * (2 if fp32_maps else 1), "traffic": None}}
 
 
-def fit_measure(dev, reps=2):
-    """Closed-form ridge fit of the whole calibration setting in one batched
-    call: 32 receiver layers x K, V = 64 problems, each 65536 rows of 3072
-    gathered features (taps -4/0/+4 of the 36 sender layers) -> 1024 outputs,
-    lambda = 1e-3 tr(G)/3072; and one problem alone for comparison."""
+def fit_inputs(dev):
+    """The calibration setting: 32 receiver layers x K, V = 64 problems, each
+    65536 rows of 3072 gathered bf16 features (taps -4/0/+4 of the 36 sender
+    layers) and 1024 receiver outputs."""
     n = 65536
     send_end, recv_end = synth.token_ends(n, 5)
     shp = synth.CacheShape(36, len(send_end), 8, 128)
@@ -394,6 +393,13 @@ def fit_measure(dev, reps=2):
             xs.append(kvx.gather_features(send, tm, taps[l]))
             ys.append(recv[l].reshape(n, 1024))
         del send, recv
+    return xs, ys
+
+
+def fit_measure(dev, xs, ys, reps=2):
+    """Closed-form ridge fit of the whole calibration setting in one batched
+    call, lambda = 1e-3 tr(G)/3072; and one problem alone for comparison."""
+    n = xs[0].shape[0]
     count = len(xs)
     w_outs = [torch.empty((1024, 3072), dtype=torch.float32, device=dev) for _ in range(count)]
 
@@ -428,6 +434,45 @@ def fit_measure(dev, reps=2):
                          "traffic": None}}
 
 
+def recolor_measure(dev, xs, ys, reps=2):
+    """Moment-matched (Recolor) fit of the whole calibration setting in one
+    call: 64 problems of 65536 rows, 3072 -> 1024, rho_x = 1e-3."""
+    n, count = xs[0].shape[0], len(xs)
+    fi, fo = 3072, 1024
+    w_outs = [torch.empty((fo, fi), dtype=torch.float32, device=dev) for _ in range(count)]
+    b_outs = [torch.empty(fo, dtype=torch.float32, device=dev) for _ in range(count)]
+    ws = torch.empty(kvx.lib().kvx_fit_recolor_workspace_size(count, fi, fo), dtype=torch.uint8, device=dev)
+    ms, info, st = [], {}, []
+    for i in range(reps + 1):
+        st.clear()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kvx.fit_recolor(xs, ys, rho_x=1e-3, w_outs=w_outs, b_outs=b_outs, workspace=ws, info=info, status=st)
+        if i >= 1:
+            ms.append((time.perf_counter() - t0) * 1e3)
+    del ws
+    torch.cuda.empty_cache()
+    t = float(np.mean(ms))
+    it = info["iters"]
+    gram = count * 2.0 * n * (fi * (fi + 1) / 2 + fi * fo + fo * (fo + 1) / 2)   # S_xx, S_xy, S_yy on bf16 MFMA
+    fp64 = count * (fi ** 3 / 3 + fo ** 3 / 3 + fi ** 2 * fo + fo ** 3 / 3       # factors, L_x^-1 S_xy, L_y^-1
+                    + 2 * fi * fo ** 2 + fi * fo ** 2                             # M = Z L_y^-T, S = M^T M
+                    + it * 6 * fo ** 3                                            # polar iterations
+                    + 2 * fi * fo ** 2 + fi * fo ** 2 + fi ** 2 * fo)              # Q, Q L_y^T, L_x^-T
+    t_roof = gram / (PEAK_MFMA_BF16_TFLOPS * 1e12) + fp64 / (PEAK_FP64_TFLOPS * 1e12)
+    return {"workload": f"Recolor fit of all {count} maps (32 layers x K,V) in one call: 65536 x 3072 bf16 "
+                        "features -> 1024 receiver outputs each, rho_x = 1e-3",
+            "fit_ms": t, "problems": count, "ms_per_problem": t / count, "polar_iterations": it,
+            "statuses_ok": int(sum(1 for v in st if v == kvx.OK)),
+            "calibration_tokens_per_s": count * n / (t * 1e-3),
+            "gram_flops": gram, "fp64_flops": fp64, "roofline_ms": t_roof * 1e3,
+            "roofline": {"bound": "fp64", "achieved": fp64 / (t * 1e-3) / 1e12, "peak": PEAK_FP64_TFLOPS,
+                         "unit": "TFLOP/s", "frac": t_roof / (t * 1e-3),
+                         "note": "frac = (moment FLOPs at the bf16 peak + fp64 FLOPs at the fp64 peak) / "
+                                 "measured time; achieved = fp64 FLOPs over the whole fit time",
+                         "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,6 +483,8 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"))
+    ap.add_argument("--fit-only", action="store_true",
+                    help="measure the ridge and Recolor fits of the calibration setting alone")
     ap.add_argument("--perhead-only", action="store_true",
                     help="measure the per-head workload alone (profiling runs of the per-head kernel)")
     args = ap.parse_args()
@@ -459,6 +506,12 @@ def main():
     if args.calibration_copy:
         log("bench: calibration copy")
         calibration_copy(dev)
+    if args.fit_only:
+        log("bench: calibration fits")
+        xs, ys = fit_inputs(dev)
+        print(json.dumps({"also_fit": fit_measure(dev, xs, ys), "also_recolor": recolor_measure(dev, xs, ys)}),
+              flush=True)
+        return
     if args.perhead_only:
         log("bench: per-head workload")
         print(json.dumps({"also": perhead_measure(dev)}), flush=True)
@@ -543,7 +596,11 @@ def main():
         res["also_fp32_maps"] = flat_setting_measure(dev, 16384, 6, rope=False, fp32_maps=True)
         torch.cuda.empty_cache()
         log("bench: ridge fit")
-        res["also_fit"] = fit_measure(dev)
+        xs, ys = fit_inputs(dev)
+        res["also_fit"] = fit_measure(dev, xs, ys)
+        log("bench: Recolor fit")
+        res["also_recolor"] = recolor_measure(dev, xs, ys)
+        del xs, ys
     print(json.dumps(res), flush=True)
 
 

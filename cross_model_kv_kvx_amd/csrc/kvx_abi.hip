@@ -5,7 +5,7 @@
 
 #include <mutex>
 
-#include "kvx_internal.hpp"
+#include "kvx_fit.hpp"
 
 namespace kvx {
 
@@ -116,6 +116,7 @@ const char* kvx_status_string(int status) {
     case KVX_ERR_NOT_SPD: return "regularised Gram matrix is not positive definite";
     case KVX_ERR_HIP: return "HIP runtime error";
     case KVX_ERR_UNSUPPORTED: return "unsupported combination";
+    case KVX_ERR_NOT_CONVERGED: return "iteration did not converge";
     default: return "unknown status";
   }
 }
@@ -534,6 +535,36 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
   if (!workspace || ws_bytes < kvx_fit_ridge_batched_workspace_size(count, f_in, f_out)) return KVX_ERR_WORKSPACE;
   return launch_fit(count, x, ldx, y, ldy, in_dtype == KVX_F32, n_rows, f_in, f_out, lambda_abs, lambda_rel,
                     fit_intercept, w_out, b_out, status, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t kvx_fit_recolor_workspace_size(int32_t count, int32_t f_in, int32_t f_out) {
+  if (count < 1 || f_in < 1 || f_out < 1) return 0;
+  return recolor_ws_bytes(count, f_in, f_out);
+}
+
+int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy,
+                    int32_t in_dtype, int64_t n_rows, int32_t f_in, int32_t f_out, double rho_x, double rho_y,
+                    float* const* w_out, float* const* b_out, int32_t* status, int32_t* iters, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (count < 0 || f_in < 1 || f_out < 1 || n_rows < 0) return KVX_ERR_INVALID;
+  if (count == 0) return KVX_OK;
+  if (in_dtype != KVX_F32 && in_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  if (!(rho_x >= 0.0) || !(rho_y >= 0.0)) return KVX_ERR_INVALID;
+  if (!x || !y || !w_out || !b_out) return KVX_ERR_INVALID;
+  for (int32_t z = 0; z < count; ++z) {
+    if (!w_out[z] || !b_out[z]) return KVX_ERR_INVALID;
+    if (n_rows > 0 && (!x[z] || !y[z])) return KVX_ERR_INVALID;
+  }
+  if (ldx < f_in || ldy < f_out) return KVX_ERR_SHAPE;
+  if (f_in < f_out) return KVX_ERR_UNSUPPORTED;
+  if (in_dtype == KVX_BF16) {
+    if ((f_in % 8) || (f_out % 8) || (ldx % 8) || (ldy % 8)) return KVX_ERR_UNSUPPORTED;
+    for (int32_t z = 0; z < count; ++z)
+      if ((reinterpret_cast<uintptr_t>(x[z]) | reinterpret_cast<uintptr_t>(y[z])) % 16) return KVX_ERR_UNSUPPORTED;
+  }
+  if (!workspace || ws_bytes < kvx_fit_recolor_workspace_size(count, f_in, f_out)) return KVX_ERR_WORKSPACE;
+  return launch_recolor(count, x, ldx, y, ldy, in_dtype == KVX_F32, n_rows, f_in, f_out, rho_x, rho_y, w_out, b_out,
+                        status, iters, workspace, static_cast<hipStream_t>(stream));
 }
 
 int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_dtype, int64_t n_rows,

@@ -25,7 +25,7 @@
 
 #include <vector>
 
-#include "kvx_internal.hpp"
+#include "kvx_fit.hpp"
 
 namespace kvx {
 
@@ -266,17 +266,62 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
   }
 }
 
-// Column sums of X and Y in fp64 (for the intercept).
+// Column sums of X and Y in fp64 (for the intercept and the moments), in
+// two passes with a fixed summation order: workgroup (g, r) adds rows
+// r * rows_per_chunk .. of its 256 V columns (V = 8 bf16 columns per 16-byte
+// load, or 1 fp32 column) into partial[r][col]; then each column's
+// CS_CHUNKS partials are added in chunk order.  bf16 callers guarantee
+// cols % 8 == 0, ld % 8 == 0 and a 16-byte aligned base.
+constexpr int CS_CHUNKS = 128;
 template <bool F32>
-__global__ __launch_bounds__(256) void colsum_kernel(const void* __restrict__ m, int64_t ld, int64_t n_rows,
-                                                     int32_t cols, double* __restrict__ out) {
-  const int32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void colsum_part_kernel(const void* __restrict__ m, int64_t ld, int64_t n_rows,
+                                                          int32_t cols, int64_t rows_per_chunk,
+                                                          double* __restrict__ partial) {
+  constexpr int V = F32 ? 1 : 8;
+  const int32_t c0 = (blockIdx.x * 256 + threadIdx.x) * V;
+  if (c0 >= cols) return;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_chunk;
+  const int64_t r1 = min(n_rows, r0 + rows_per_chunk);
+  double acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.0;
+  for (int64_t r = r0; r < r1; ++r) {
+    if constexpr (F32) {
+      acc[0] += static_cast<double>(static_cast<const float*>(m)[r * ld + c0]);
+    } else {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(m) + r * ld + c0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += static_cast<double>(bf16lo(q[e]));
+        acc[2 * e + 1] += static_cast<double>(bf16hi(q[e]));
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) partial[static_cast<int64_t>(blockIdx.y) * cols + c0 + v] = acc[v];
+}
+
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(const double* __restrict__ partial, int32_t cols,
+                                                            double* __restrict__ out) {
+  const int32_t c = blockIdx.x * 256 + threadIdx.x;
   if (c >= cols) return;
   double s = 0.0;
-  for (int64_t k = 0; k < n_rows; ++k)
-    s += F32 ? static_cast<double>(static_cast<const float*>(m)[k * ld + c])
-             : static_cast<double>(bf16_to_f32(static_cast<const uint16_t*>(m)[k * ld + c]));
+  for (int q = 0; q < CS_CHUNKS; ++q) s += partial[static_cast<int64_t>(q) * cols + c];
   out[c] = s;
+}
+
+static int colsum(const void* m, int64_t ld, int64_t n_rows, int32_t cols, int32_t f32, double* partial, double* out,
+                  hipStream_t s) {
+  const int64_t rpc = (n_rows + CS_CHUNKS - 1) / CS_CHUNKS;
+  const int v = f32 ? 1 : 8;
+  const dim3 grid(static_cast<unsigned>(ceil_div(cols, 256 * v)), CS_CHUNKS);
+  if (f32)
+    colsum_part_kernel<true><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial);
+  else
+    colsum_part_kernel<false><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial);
+  colsum_reduce_kernel<<<static_cast<unsigned>(ceil_div(cols, 256)), 256, 0, s>>>(partial, cols, out);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
 }
 
 // Sum of the split partials in fp64 by 64 x 64 blocks of [G | C]: blocks of
@@ -630,6 +675,7 @@ __global__ __launch_bounds__(256) void copy_f64_kernel(const double* __restrict_
 // lambda and the inverse diagonal factors, then one flag per problem.
 struct FitWs {
   float* part;
+  double* csp;  // column-sum partials [CS_CHUNKS][max(f_in, f_out)]
   double *G, *C, *sx, *sy, *lam, *linv, *xinv, *zbuf;
   int64_t bs;  // doubles between the per-problem areas
   int64_t oG, oC, oSx, oSy, oLam, oLinv, oXinv, oZbuf;
@@ -641,6 +687,7 @@ static FitWs fit_layout(int32_t count, int32_t f_in, int32_t f_out, void* base) 
   FitWs w{};
   Carve c(base);
   w.part = c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  w.csp = c.take<double>(static_cast<size_t>(CS_CHUNKS) * (f_in > f_out ? f_in : f_out));
   const int64_t nb_total = ceil_div(f_in, CH_NB);
   auto up = [](int64_t v) { return (v + 31) / 32 * 32; };  // 256-byte sub-areas
   w.oG = 0;
@@ -699,6 +746,131 @@ static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, 
   }
 #undef KVX_DG
   KVX_LAUNCH_CHECK();
+  return KVX_OK;
+}
+
+// Blocked Cholesky A = L L^T (lower, in place) of `count` problems of order
+// n; problem z's A, linv, xinv and zbuf sit z * bs doubles after problem 0's.
+// The diagonal kernel leaves the inverse of each 64-wide factor in linv, so
+// each panel solve is an in-place product with it.  Right-looking by
+// 256-column panels: inside a panel, each 64-wide block is factored, its
+// panel solved and only the panel's remaining columns updated; the trailing
+// matrix right of the panel is updated once per panel with K = 256, so it is
+// read and written n/256 rather than n/64 times.  Afterwards xinv holds the
+// inverses of the 256-wide diagonal blocks for the triangular solves:
+// X_bb = L_bb^-1 (placed), then for each lower block row b,
+// X[b, 0:b] = -L_bb^-1 (L[b, 0:b] X[0:b, 0:b]).  Entries strictly above the
+// diagonal of A are left with partial updates (only the lower triangle is
+// the factor).  A non-positive pivot sets flags[z].
+static int chol_factor(hipStream_t s, int32_t count, double* A, int32_t n, int64_t bs, double* linv, double* xinv,
+                       double* zbuf, int32_t* flags) {
+  const int32_t nb_total = static_cast<int32_t>(ceil_div(n, CH_NB));
+  const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t p0 = I * SV_NB;
+    const int32_t pn = min(SV_NB, n - p0);
+    for (int32_t k0 = p0; k0 < p0 + pn; k0 += CH_NB) {
+      const int32_t nb = min(CH_NB, n - k0);
+      double* li = linv + static_cast<int64_t>(k0 / CH_NB) * CH_NB * CH_NB;
+      potrf_diag_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(A, bs, n, k0, nb, flags, li, bs);
+      KVX_LAUNCH_CHECK();
+      const int32_t rest = n - k0 - nb;
+      if (rest <= 0) continue;
+      // panel: P = P L_kk^-T (in place, one 64-column tile)
+      double* P = A + static_cast<int64_t>(k0 + nb) * n + k0;
+      if (int st = dgemm(s, count, rest, nb, nb, P, n, 1, li, 1, CH_NB, P, n, bs, 0, 1)) return st;
+      // the panel's remaining columns: A[r][c] -= P[r] . P[c], c < p0 + pn
+      const int32_t pw = p0 + pn - (k0 + nb);
+      if (pw > 0) {
+        double* Ct = A + static_cast<int64_t>(k0 + nb) * n + k0 + nb;
+        if (int st = dgemm(s, count, rest, pw, nb, P, n, 1, P, 1, n, Ct, n, bs, 1, 0)) return st;
+      }
+    }
+    // trailing lower update right of the panel, K = the panel's width
+    const int32_t rest = n - p0 - pn;
+    if (rest > 0) {
+      const double* PI = A + static_cast<int64_t>(p0 + pn) * n + p0;
+      double* Ct = A + static_cast<int64_t>(p0 + pn) * n + p0 + pn;
+      if (int st = dgemm(s, count, rest, rest, pn, PI, n, 1, PI, 1, n, Ct, n, bs, 1, 0)) return st;
+    }
+  }
+  const dim3 fill_grid(static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_outer) * SV_NB * SV_NB, 256 * 8)),
+                       static_cast<unsigned>(count));
+  fill_f64_kernel<<<fill_grid, 256, 0, s>>>(xinv, static_cast<int64_t>(n_outer) * SV_NB * SV_NB, bs, 0.0);
+  KVX_LAUNCH_CHECK();
+  place_linv_kernel<<<dim3(static_cast<unsigned>(nb_total), static_cast<unsigned>(count)), 256, 0, s>>>(linv, xinv,
+                                                                                                      bs);
+  KVX_LAUNCH_CHECK();
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, n - k0);
+    double* X = xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    for (int32_t b = 1; b * CH_NB < nb; ++b) {
+      const int32_t sb = min(CH_NB, nb - b * CH_NB);
+      const int32_t wb = b * CH_NB;
+      // T = L[b, 0:b] X[0:b, 0:b] (in zbuf, row stride 3 * 64)
+      if (int st = dgemm(s, count, sb, wb, wb, A + static_cast<int64_t>(k0 + wb) * n + k0, n, 1, X, SV_NB, 1, zbuf,
+                         3 * CH_NB, bs, 0, 1))
+        return st;
+      // X[b, 0:b] = 0 - L_bb^-1 T
+      const double* li = linv + static_cast<int64_t>(I * 4 + b) * CH_NB * CH_NB;
+      if (int st = dgemm(s, count, sb, wb, sb, li, CH_NB, 1, zbuf, 3 * CH_NB, 1, X + static_cast<int64_t>(wb) * SV_NB,
+                         SV_NB, bs, 0, 0))
+        return st;
+    }
+  }
+  return KVX_OK;
+}
+
+static int copy_back(hipStream_t s, int32_t count, const double* src, double* dst, int64_t n, int64_t bs) {
+  copy_f64_kernel<<<dim3(static_cast<unsigned>(ceil_div(n, 256 * 8)), static_cast<unsigned>(count)), 256, 0, s>>>(
+      src, dst, n, bs);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
+}
+
+// L Z = C in place for the factor of chol_factor (C [n][nrhs], row stride
+// nrhs) by 256-row blocks: Z_I = X_II C_I, then the rows below are updated,
+// so the right-hand sides are read and written n/256 times.  zbuf holds
+// 256 x nrhs doubles.
+static int chol_forward(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+                        double* zbuf, double* C, int32_t nrhs) {
+  const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, n - k0);
+    const double* X = xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    double* CI = C + static_cast<int64_t>(k0) * nrhs;
+    if (int st = dgemm(s, count, nb, nrhs, nb, X, SV_NB, 1, CI, nrhs, 1, zbuf, nrhs, bs, 0, 1)) return st;
+    if (int st = copy_back(s, count, zbuf, CI, static_cast<int64_t>(nb) * nrhs, bs)) return st;
+    const int32_t rest = n - k0 - nb;
+    if (rest > 0) {
+      const double* Lb = A + static_cast<int64_t>(k0 + nb) * n + k0;
+      if (int st = dgemm(s, count, rest, nrhs, nb, Lb, n, 1, zbuf, nrhs, 1, CI + static_cast<int64_t>(nb) * nrhs, nrhs,
+                         bs, 0, 0))
+        return st;
+    }
+  }
+  return KVX_OK;
+}
+
+// L^T W = Z in place (W_I = X_II^T Z_I, then the rows above are updated).
+static int chol_backward(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+                         double* zbuf, double* C, int32_t nrhs) {
+  const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
+  for (int32_t I = n_outer - 1; I >= 0; --I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, n - k0);
+    const double* X = xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    double* CI = C + static_cast<int64_t>(k0) * nrhs;
+    if (int st = dgemm(s, count, nb, nrhs, nb, X, 1, SV_NB, CI, nrhs, 1, zbuf, nrhs, bs, 0, 1)) return st;
+    if (int st = copy_back(s, count, zbuf, CI, static_cast<int64_t>(nb) * nrhs, bs)) return st;
+    if (k0 > 0) {
+      // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_I
+      const double* Lr = A + static_cast<int64_t>(k0) * n;
+      if (int st = dgemm(s, count, k0, nrhs, nb, Lr, 1, n, zbuf, nrhs, 1, C, nrhs, bs, 0, 0)) return st;
+    }
+  }
   return KVX_OK;
 }
 
@@ -774,14 +946,8 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
     double* sy = w.sy + z * bs;
     if (int st = gram_one(x[z], ldx, y[z], ldy, in_f32, n_rows, f_in, f_out, w.part, G, C, s)) return st;
     if (fit_intercept) {
-      if (in_f32) {
-        colsum_kernel<true><<<grid_for(f_in), 256, 0, s>>>(x[z], ldx, n_rows, f_in, sx);
-        colsum_kernel<true><<<grid_for(f_out), 256, 0, s>>>(y[z], ldy, n_rows, f_out, sy);
-      } else {
-        colsum_kernel<false><<<grid_for(f_in), 256, 0, s>>>(x[z], ldx, n_rows, f_in, sx);
-        colsum_kernel<false><<<grid_for(f_out), 256, 0, s>>>(y[z], ldy, n_rows, f_out, sy);
-      }
-      KVX_LAUNCH_CHECK();
+      if (int st = colsum(x[z], ldx, n_rows, f_in, in_f32, w.csp, sx, s)) return st;
+      if (int st = colsum(y[z], ldy, n_rows, f_out, in_f32, w.csp, sy, s)) return st;
       center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
                                                                                           inv_n);
       KVX_LAUNCH_CHECK();
@@ -790,107 +956,10 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
     KVX_LAUNCH_CHECK();
   }
 
-  // 2. Cholesky and the two block triangular solves of all problems at once;
-  // the diagonal kernel leaves the inverse factor of its block, so each panel
-  // and each block solve is an in-place product with it.
-  // Right-looking by 256-column panels: inside a panel, each 64-wide block
-  // is factored, its panel solved and only the panel's remaining columns
-  // updated; the trailing matrix right of the panel is updated once per
-  // panel with K = 256, so it is read and written 12 rather than 48 times.
-  const int32_t nb_total = static_cast<int32_t>(ceil_div(f_in, CH_NB));
-  const int32_t n_outer = static_cast<int32_t>(ceil_div(f_in, SV_NB));
-  for (int32_t I = 0; I < n_outer; ++I) {
-    const int32_t p0 = I * SV_NB;
-    const int32_t pn = min(SV_NB, f_in - p0);
-    for (int32_t k0 = p0; k0 < p0 + pn; k0 += CH_NB) {
-      const int32_t nb = min(CH_NB, f_in - k0);
-      double* li = w.linv + static_cast<int64_t>(k0 / CH_NB) * CH_NB * CH_NB;
-      potrf_diag_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(w.G, bs, f_in, k0, nb, w.flags, li, bs);
-      KVX_LAUNCH_CHECK();
-      const int32_t rest = f_in - k0 - nb;
-      if (rest <= 0) continue;
-      // panel: P = P L_kk^-T (in place, one 64-column tile)
-      double* P = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0;
-      if (int st = dgemm(s, count, rest, nb, nb, P, f_in, 1, li, 1, CH_NB, P, f_in, bs, 0, 1)) return st;
-      // the panel's remaining columns: G[r][c] -= P[r] . P[c], c < p0 + pn
-      const int32_t pw = p0 + pn - (k0 + nb);
-      if (pw > 0) {
-        double* Ct = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0 + nb;
-        if (int st = dgemm(s, count, rest, pw, nb, P, f_in, 1, P, 1, f_in, Ct, f_in, bs, 1, 0)) return st;
-      }
-    }
-    // trailing lower update right of the panel, K = the panel's width
-    const int32_t rest = f_in - p0 - pn;
-    if (rest > 0) {
-      const double* PI = w.G + static_cast<int64_t>(p0 + pn) * f_in + p0;
-      double* Ct = w.G + static_cast<int64_t>(p0 + pn) * f_in + p0 + pn;
-      if (int st = dgemm(s, count, rest, rest, pn, PI, f_in, 1, PI, 1, f_in, Ct, f_in, bs, 1, 0)) return st;
-    }
-  }
-
-  // inverses of the 256-wide diagonal blocks: X_bb = L_bb^-1 (placed), then
-  // for each lower block row b, X[b, 0:b] = -L_bb^-1 (L[b, 0:b] X[0:b, 0:b])
-  const dim3 fill_grid(static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_outer) * SV_NB * SV_NB, 256 * 8)),
-                       static_cast<unsigned>(count));
-  fill_f64_kernel<<<fill_grid, 256, 0, s>>>(w.xinv, static_cast<int64_t>(n_outer) * SV_NB * SV_NB, bs, 0.0);
-  KVX_LAUNCH_CHECK();
-  place_linv_kernel<<<dim3(static_cast<unsigned>(nb_total), static_cast<unsigned>(count)), 256, 0, s>>>(w.linv, w.xinv,
-                                                                                                      bs);
-  KVX_LAUNCH_CHECK();
-  for (int32_t I = 0; I < n_outer; ++I) {
-    const int32_t k0 = I * SV_NB;
-    const int32_t nb = min(SV_NB, f_in - k0);
-    double* X = w.xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
-    for (int32_t b = 1; b * CH_NB < nb; ++b) {
-      const int32_t sb = min(CH_NB, nb - b * CH_NB);
-      const int32_t wb = b * CH_NB;
-      // T = L[b, 0:b] X[0:b, 0:b] (in zbuf, row stride 3 * 64)
-      if (int st = dgemm(s, count, sb, wb, wb, w.G + static_cast<int64_t>(k0 + wb) * f_in + k0, f_in, 1, X, SV_NB, 1,
-                         w.zbuf, 3 * CH_NB, bs, 0, 1))
-        return st;
-      // X[b, 0:b] = 0 - L_bb^-1 T
-      const double* li = w.linv + static_cast<int64_t>(I * 4 + b) * CH_NB * CH_NB;
-      if (int st = dgemm(s, count, sb, wb, sb, li, CH_NB, 1, w.zbuf, 3 * CH_NB, 1,
-                         X + static_cast<int64_t>(wb) * SV_NB, SV_NB, bs, 0, 0))
-        return st;
-    }
-  }
-  auto copy_back = [&](double* dst, int64_t n) -> int {
-    copy_f64_kernel<<<dim3(static_cast<unsigned>(ceil_div(n, 256 * 8)), static_cast<unsigned>(count)), 256, 0, s>>>(
-        w.zbuf, dst, n, bs);
-    KVX_LAUNCH_CHECK();
-    return KVX_OK;
-  };
-  // forward: L Z = C by 256-row blocks (Z_I = X_II C_I, then the rows below)
-  for (int32_t I = 0; I < n_outer; ++I) {
-    const int32_t k0 = I * SV_NB;
-    const int32_t nb = min(SV_NB, f_in - k0);
-    const double* X = w.xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
-    double* CI = w.C + static_cast<int64_t>(k0) * f_out;
-    if (int st = dgemm(s, count, nb, f_out, nb, X, SV_NB, 1, CI, f_out, 1, w.zbuf, f_out, bs, 0, 1)) return st;
-    if (int st = copy_back(CI, static_cast<int64_t>(nb) * f_out)) return st;
-    const int32_t rest = f_in - k0 - nb;
-    if (rest > 0) {
-      const double* Lb = w.G + static_cast<int64_t>(k0 + nb) * f_in + k0;
-      if (int st = dgemm(s, count, rest, f_out, nb, Lb, f_in, 1, w.zbuf, f_out, 1, CI + static_cast<int64_t>(nb) * f_out,
-                         f_out, bs, 0, 0))
-        return st;
-    }
-  }
-  // backward: L^T W = Z (W_I = X_II^T Z_I, then the rows above)
-  for (int32_t I = n_outer - 1; I >= 0; --I) {
-    const int32_t k0 = I * SV_NB;
-    const int32_t nb = min(SV_NB, f_in - k0);
-    const double* X = w.xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
-    double* CI = w.C + static_cast<int64_t>(k0) * f_out;
-    if (int st = dgemm(s, count, nb, f_out, nb, X, 1, SV_NB, CI, f_out, 1, w.zbuf, f_out, bs, 0, 1)) return st;
-    if (int st = copy_back(CI, static_cast<int64_t>(nb) * f_out)) return st;
-    if (k0 > 0) {
-      // Z[0..k0) -= L[k0..k0+nb)[0..k0)^T W_I
-      const double* Lr = w.G + static_cast<int64_t>(k0) * f_in;
-      if (int st = dgemm(s, count, k0, f_out, nb, Lr, 1, f_in, w.zbuf, f_out, 1, w.C, f_out, bs, 0, 0)) return st;
-    }
-  }
+  // 2. Cholesky and the two block triangular solves of all problems at once
+  if (int st = chol_factor(s, count, w.G, f_in, bs, w.linv, w.xinv, w.zbuf, w.flags)) return st;
+  if (int st = chol_forward(s, count, w.G, f_in, bs, w.xinv, w.zbuf, w.C, f_out)) return st;
+  if (int st = chol_backward(s, count, w.G, f_in, bs, w.xinv, w.zbuf, w.C, f_out)) return st;
 
   // 3. outputs
   for (int32_t z = 0; z < count; ++z) {
@@ -907,6 +976,279 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
   for (int32_t z = 0; z < count; ++z) {
     if (status) status[z] = host_flags[z] ? KVX_ERR_NOT_SPD : KVX_OK;
     if (host_flags[z]) result = KVX_ERR_NOT_SPD;
+  }
+  return result;
+}
+
+// ---------------------------------------------------------------- Recolor
+//
+// "Prefill-Free Cross-Family KV Cache Transfer ..." (Key Contributions 2,
+// Methodology 3): the moment-matched map whitens both feature spaces, aligns
+// the whitened spaces by an orthogonal Procrustes solution and restores the
+// receiver's covariance and mean:
+//   W = A_x Q A_y^-1,  b = mean_y - mean_x W,  A^T S A = I,
+//   Q = polar factor of the whitened cross-covariance A_x^T S_xy A_y.
+// W does not depend on which whitening A is used (A R for an orthogonal R
+// gives the same W), so the Cholesky factors S_xx = L_x L_x^T and
+// S_yy = L_y L_y^T serve: A_x = L_x^-T, A_y^-1 = L_y^T, and
+//   M = L_x^-1 S_xy L_y^-T,  Q = M (M^T M)^-1/2,  W = L_x^-T Q L_y^T.
+// Moments are kept as n times the covariances (the factor cancels in W and
+// in the relative regulariser rho * trace / F added to each diagonal).  The
+// inverse square root of S = M^T M comes from the coupled Newton-Schulz
+// iteration Y <- Y T, Z <- T Z, T = (3 I - Z Y) / 2, started at Y = S / c,
+// Z = I with c = ||S||_F (so every eigenvalue of S / c is in (0, 1]):
+// Z -> (S / c)^-1/2.  All products are fp64 on matrix cores, every problem of
+// the call at once; the host reads max |T - I| per problem after each step.
+
+constexpr int NS_BLOCKS = 64;        // workgroups per problem of the middle step
+constexpr int RC_MAX_ITERS = 100;
+constexpr double RC_TOL = 1e-10;     // max |T - I| taken as converged
+constexpr double RC_FLOOR = 1e-6;    // below this, a step that gains < 4x is the rounding floor
+// ||(S / c)^-1/2||_F above this: M is numerically rank-deficient (fewer
+// distinct calibration rows than outputs, or outputs unrelated to the
+// features in some direction), so the polar factor is not determined
+constexpr double RC_ZMAX = 1e6;
+
+__global__ __launch_bounds__(256) void identity_kernel(double* __restrict__ p, int32_t n, int64_t bs) {
+  double* q = p + blockIdx.y * bs;
+  const int64_t total = static_cast<int64_t>(n) * n;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * 256)
+    q[e] = (e / n == e % n) ? 1.0 : 0.0;
+}
+
+// Entries strictly above the diagonal set to zero (the factor is the lower
+// triangle).
+__global__ __launch_bounds__(256) void zero_upper_kernel(double* __restrict__ p, int32_t n, int64_t bs) {
+  double* q = p + blockIdx.y * bs;
+  const int64_t total = static_cast<int64_t>(n) * n;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * 256)
+    if (e % n > e / n) q[e] = 0.0;
+}
+
+// ||S||_F of each problem (one workgroup per problem, fixed summation order).
+__global__ __launch_bounds__(256) void frob_kernel(const double* __restrict__ S, int32_t n, int64_t bs,
+                                                   double* __restrict__ out) {
+  S += blockIdx.x * bs;
+  __shared__ double red[256];
+  const int64_t total = static_cast<int64_t>(n) * n;
+  double a = 0.0;
+  for (int64_t e = threadIdx.x; e < total; e += 256) a += S[e] * S[e];
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x * bs] = sqrt(red[0]);
+}
+
+// p *= c^power with c = scal of the problem.
+__global__ __launch_bounds__(256) void scale_kernel(double* __restrict__ p, int64_t n, int64_t bs,
+                                                    const double* __restrict__ scal, double power) {
+  double* q = p + blockIdx.y * bs;
+  const double f = pow(scal[blockIdx.y * bs], power);
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256)
+    q[e] *= f;
+}
+
+__device__ __forceinline__ double nan_max(double a, double b) { return (b > a || b != b) ? b : a; }
+
+// Middle of a Newton-Schulz step: P = Z Y becomes T = (3 I - P) / 2 in place;
+// each workgroup writes the largest |T - I| of its share (NaN propagates) to
+// dev[problem][workgroup].
+__global__ __launch_bounds__(256) void ns_mid_kernel(double* __restrict__ P, int32_t n, int64_t bs,
+                                                     double* __restrict__ dev) {
+  double* q = P + blockIdx.y * bs;
+  __shared__ double red[256];
+  const int64_t total = static_cast<int64_t>(n) * n;
+  double m = 0.0;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total; e += NS_BLOCKS * 256) {
+    const double id = (e / n == e % n) ? 1.0 : 0.0;
+    const double t = 1.5 * id - 0.5 * q[e];
+    q[e] = t;
+    m = nan_max(m, fabs(t - id));
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = nan_max(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dev[blockIdx.y * NS_BLOCKS + blockIdx.x] = red[0];
+}
+
+struct RcWs {
+  float* part;
+  double* csp;
+  double *G, *C, *sx, *sy, *lam, *linvx, *xinvx, *zbuf, *Gy, *linvy, *xinvy, *E, *M, *ns[4], *scal;
+  int64_t bs;
+  double* dev;
+  int32_t* flags;
+  size_t bytes;
+};
+
+static RcWs recolor_layout(int32_t count, int32_t f_in, int32_t f_out, void* base) {
+  RcWs w{};
+  Carve c(base);
+  w.part = c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  w.csp = c.take<double>(static_cast<size_t>(CS_CHUNKS) * (f_in > f_out ? f_in : f_out));
+  int64_t o = 0;
+  auto take = [&](int64_t n) {
+    const int64_t at = o;
+    o += (n + 31) / 32 * 32;  // 256-byte sub-areas
+    return at;
+  };
+  const int64_t fi = f_in, fo = f_out;
+  const int64_t zb = static_cast<int64_t>(SV_NB) * fo;
+  const int64_t oG = take(fi * fi), oC = take(fi * fo), oSx = take(fi), oSy = take(fo), oLam = take(4);
+  const int64_t oLx = take(ceil_div(fi, CH_NB) * CH_NB * CH_NB), oXx = take(ceil_div(fi, SV_NB) * SV_NB * SV_NB);
+  const int64_t oZ = take(zb > CH_NB * 3 * CH_NB ? zb : CH_NB * 3 * CH_NB);
+  const int64_t oGy = take(fo * fo), oLy = take(ceil_div(fo, CH_NB) * CH_NB * CH_NB);
+  const int64_t oXy = take(ceil_div(fo, SV_NB) * SV_NB * SV_NB), oE = take(fo * fo), oM = take(fi * fo);
+  int64_t oN[4];
+  for (int i = 0; i < 4; ++i) oN[i] = take(fo * fo);
+  const int64_t oS = take(4);
+  w.bs = o;
+  double* area = c.take<double>(static_cast<size_t>(count) * w.bs);
+  if (area) {
+    w.G = area + oG;
+    w.C = area + oC;
+    w.sx = area + oSx;
+    w.sy = area + oSy;
+    w.lam = area + oLam;
+    w.linvx = area + oLx;
+    w.xinvx = area + oXx;
+    w.zbuf = area + oZ;
+    w.Gy = area + oGy;
+    w.linvy = area + oLy;
+    w.xinvy = area + oXy;
+    w.E = area + oE;
+    w.M = area + oM;
+    for (int i = 0; i < 4; ++i) w.ns[i] = area + oN[i];
+    w.scal = area + oS;
+  }
+  w.dev = c.take<double>(static_cast<size_t>(count) * NS_BLOCKS);
+  w.flags = c.take<int32_t>(static_cast<size_t>(count) + 64);
+  w.bytes = c.used + 256;
+  return w;
+}
+
+size_t recolor_ws_bytes(int32_t count, int32_t f_in, int32_t f_out) {
+  return recolor_layout(count, f_in, f_out, nullptr).bytes;
+}
+
+int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy,
+                   int32_t in_f32, int64_t n_rows, int32_t f_in, int32_t f_out, double rho_x, double rho_y,
+                   float* const* w_out, float* const* b_out, int32_t* status, int32_t* iters, void* ws,
+                   hipStream_t s) {
+  RcWs w = recolor_layout(count, f_in, f_out, ws);
+  const int64_t bs = w.bs;
+  if (int st = launch_fill_i32(w.flags, count, 0, s)) return st;
+  const double inv_n = n_rows > 0 ? 1.0 / static_cast<double>(n_rows) : 0.0;
+  const int64_t fo2 = static_cast<int64_t>(f_out) * f_out;
+  const dim3 grid_o2(grid_for(fo2 / 8 + 1), static_cast<unsigned>(count));
+
+  // 1. moments (n times the covariances), regularised
+  for (int32_t z = 0; z < count; ++z) {
+    double* G = w.G + z * bs;
+    double* C = w.C + z * bs;
+    double* Gy = w.Gy + z * bs;
+    double* sx = w.sx + z * bs;
+    double* sy = w.sy + z * bs;
+    if (int st = gram_one(x[z], ldx, y[z], ldy, in_f32, n_rows, f_in, f_out, w.part, G, C, s)) return st;
+    if (int st = gram_one(y[z], ldy, y[z], ldy, in_f32, n_rows, f_out, 0, w.part, Gy, nullptr, s)) return st;
+    if (int st = colsum(x[z], ldx, n_rows, f_in, in_f32, w.csp, sx, s)) return st;
+    if (int st = colsum(y[z], ldy, n_rows, f_out, in_f32, w.csp, sy, s)) return st;
+    center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
+                                                                                        inv_n);
+    center_kernel<<<grid_for(fo2), 256, 0, s>>>(Gy, nullptr, sy, sy, f_out, 0, inv_n);
+    KVX_LAUNCH_CHECK();
+    lambda_kernel<<<1, 256, 0, s>>>(G, f_in, 0.0, rho_x, w.lam + z * bs);
+    lambda_kernel<<<1, 256, 0, s>>>(Gy, f_out, 0.0, rho_y, w.lam + z * bs + 1);
+    KVX_LAUNCH_CHECK();
+  }
+
+  // 2. factors and the whitened cross-covariance M = L_x^-1 C L_y^-T
+  if (int st = chol_factor(s, count, w.G, f_in, bs, w.linvx, w.xinvx, w.zbuf, w.flags)) return st;
+  if (int st = chol_factor(s, count, w.Gy, f_out, bs, w.linvy, w.xinvy, w.zbuf, w.flags)) return st;
+  zero_upper_kernel<<<grid_o2, 256, 0, s>>>(w.Gy, f_out, bs);
+  KVX_LAUNCH_CHECK();
+  if (int st = chol_forward(s, count, w.G, f_in, bs, w.xinvx, w.zbuf, w.C, f_out)) return st;
+  identity_kernel<<<grid_o2, 256, 0, s>>>(w.E, f_out, bs);
+  KVX_LAUNCH_CHECK();
+  if (int st = chol_forward(s, count, w.Gy, f_out, bs, w.xinvy, w.zbuf, w.E, f_out)) return st;  // E = L_y^-1
+  if (int st = dgemm(s, count, f_in, f_out, f_out, w.C, f_out, 1, w.E, 1, f_out, w.M, f_out, bs, 0, 1)) return st;
+
+  std::vector<int32_t> flags(static_cast<size_t>(count), 0);
+  KVX_HIP_TRY(hipMemcpyAsync(flags.data(), w.flags, sizeof(int32_t) * count, hipMemcpyDeviceToHost, s));
+
+  // 3. S = M^T M, then the polar iteration
+  double *Y = w.ns[0], *Z = w.ns[1], *T = w.ns[2], *N = w.ns[3];
+  if (int st = dgemm(s, count, f_out, f_out, f_in, w.M, 1, f_out, w.M, f_out, 1, Y, f_out, bs, 0, 1)) return st;
+  frob_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(Y, f_out, bs, w.scal);
+  scale_kernel<<<grid_o2, 256, 0, s>>>(Y, fo2, bs, w.scal, -1.0);
+  identity_kernel<<<grid_o2, 256, 0, s>>>(Z, f_out, bs);
+  KVX_LAUNCH_CHECK();
+  std::vector<double> dev(static_cast<size_t>(count) * NS_BLOCKS), prev(static_cast<size_t>(count), 1e300);
+  std::vector<uint8_t> done(static_cast<size_t>(count), 0);
+  int32_t it = 0;
+  for (; it < RC_MAX_ITERS; ++it) {
+    if (int st = dgemm(s, count, f_out, f_out, f_out, Z, f_out, 1, Y, f_out, 1, T, f_out, bs, 0, 1)) return st;
+    ns_mid_kernel<<<dim3(NS_BLOCKS, static_cast<unsigned>(count)), 256, 0, s>>>(T, f_out, bs, w.dev);
+    KVX_LAUNCH_CHECK();
+    if (int st = dgemm(s, count, f_out, f_out, f_out, Y, f_out, 1, T, f_out, 1, N, f_out, bs, 0, 1)) return st;
+    std::swap(Y, N);
+    if (int st = dgemm(s, count, f_out, f_out, f_out, T, f_out, 1, Z, f_out, 1, N, f_out, bs, 0, 1)) return st;
+    std::swap(Z, N);
+    KVX_HIP_TRY(hipMemcpyAsync(dev.data(), w.dev, sizeof(double) * dev.size(), hipMemcpyDeviceToHost, s));
+    KVX_HIP_TRY(hipStreamSynchronize(s));
+    bool all = true;
+    for (int32_t z = 0; z < count; ++z) {
+      if (flags[z] || done[z]) continue;
+      double m = 0.0;
+      for (int b = 0; b < NS_BLOCKS; ++b) {
+        const double d = dev[static_cast<size_t>(z) * NS_BLOCKS + b];
+        m = (d > m || d != d) ? d : m;
+      }
+      // converged, or at the rounding floor (a quadratic step gains far more than 4x)
+      if (m <= RC_TOL || (m <= RC_FLOOR && m >= 0.25 * prev[z]))
+        done[z] = 1;
+      else
+        all = false;
+      prev[z] = m;
+    }
+    if (all) {
+      ++it;
+      break;
+    }
+  }
+  if (iters) *iters = it;
+  frob_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(Z, f_out, bs, w.scal + 1);
+  KVX_LAUNCH_CHECK();
+  std::vector<double> zf(static_cast<size_t>(count));
+  for (int32_t z = 0; z < count; ++z)
+    KVX_HIP_TRY(hipMemcpyAsync(&zf[z], w.scal + z * bs + 1, sizeof(double), hipMemcpyDeviceToHost, s));
+
+  // 4. W = L_x^-T Q L_y^T with Q = M S^-1/2, S^-1/2 = Z / sqrt(c); b = mean_y - mean_x W
+  scale_kernel<<<grid_o2, 256, 0, s>>>(Z, fo2, bs, w.scal, -0.5);
+  KVX_LAUNCH_CHECK();
+  if (int st = dgemm(s, count, f_in, f_out, f_out, w.M, f_out, 1, Z, f_out, 1, w.C, f_out, bs, 0, 1)) return st;
+  if (int st = dgemm(s, count, f_in, f_out, f_out, w.C, f_out, 1, w.Gy, 1, f_out, w.M, f_out, bs, 0, 1)) return st;
+  if (int st = chol_backward(s, count, w.G, f_in, bs, w.xinvx, w.zbuf, w.M, f_out)) return st;
+  for (int32_t z = 0; z < count; ++z) {
+    fit_output_kernel<<<grid_for(static_cast<int64_t>(f_in) * f_out), 256, 0, s>>>(
+        w.M + z * bs, f_in, f_out, w_out[z], b_out[z], w.sx + z * bs, w.sy + z * bs, inv_n);
+    KVX_LAUNCH_CHECK();
+  }
+  KVX_HIP_TRY(hipStreamSynchronize(s));
+  int result = KVX_OK;
+  for (int32_t z = 0; z < count; ++z) {
+    const bool determined = done[z] && zf[z] <= RC_ZMAX;  // false for NaN too
+    const int st = flags[z] ? KVX_ERR_NOT_SPD : (determined ? KVX_OK : KVX_ERR_NOT_CONVERGED);
+    if (status) status[z] = st;
+    if (st != KVX_OK && result == KVX_OK) result = st;
   }
   return result;
 }

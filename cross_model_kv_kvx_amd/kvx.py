@@ -22,14 +22,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvx.so")
 
 F32, BF16 = 0, 1
-OK, ERR_INVALID, ERR_SHAPE, ERR_WORKSPACE, ERR_NOT_SPD, ERR_HIP, ERR_UNSUPPORTED = range(7)
+OK, ERR_INVALID, ERR_SHAPE, ERR_WORKSPACE, ERR_NOT_SPD, ERR_HIP, ERR_UNSUPPORTED, ERR_NOT_CONVERGED = range(8)
 
 EXPORTS = (
     "kvx_status_string", "kvx_align_workspace_size", "kvx_align_tokens", "kvx_align_batched_workspace_size",
     "kvx_align_tokens_batched", "kvx_layer_map", "kvx_translate_workspace_size", "kvx_translate",
     "kvx_translate_timed", "kvx_translate_placed_workspace_size", "kvx_translate_placed", "kvx_gather_features",
     "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fit_ridge_batched_workspace_size",
-    "kvx_fit_ridge_batched", "kvx_fold_lowrank",
+    "kvx_fit_ridge_batched", "kvx_fit_recolor_workspace_size", "kvx_fit_recolor", "kvx_fold_lowrank",
 )
 
 
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
             "kvx_fit_ridge_batched_workspace_size": (sz, [i32, i32, i32]),
             "kvx_fit_ridge_batched": (ctypes.c_int, [i32, vpp, i64, vpp, i64, i32, i64, i32, i32, dbl, dbl, i32,
                                                      vpp, vpp, ip, vp, sz, vp]),
+            "kvx_fit_recolor_workspace_size": (sz, [i32, i32, i32]),
+            "kvx_fit_recolor": (ctypes.c_int, [i32, vpp, i64, vpp, i64, i32, i64, i32, i32, dbl, dbl, vpp, vpp,
+                                               ip, ip, vp, sz, vp]),
             "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -373,6 +376,52 @@ def fit_ridge_batched(xs, ys, *, lambda_abs: float = 0.0, lambda_rel: float = 0.
     else:
         _check(st, "kvx_fit_ridge_batched")
     return w_outs, (b_outs if fit_intercept else [None] * count)
+
+
+def fit_recolor(xs, ys, *, rho_x: float = 0.0, rho_y: float = 0.0, w_outs=None, b_outs=None,
+                workspace: Optional[torch.Tensor] = None, stream=None, status: Optional[list] = None,
+                info: Optional[dict] = None):
+    """kvx_fit_recolor on lists of row-major 2-D x [n][f_in] and y [n][f_out]
+    (one shape, one dtype, one row stride each).  Returns the lists
+    (wt fp32 [f_out][f_in], b fp32 [f_out]).  With a list ``status``, appends
+    each problem's status and raises only for other errors; with a dict
+    ``info``, stores the number of polar iterations under "iters"."""
+    count = len(xs)
+    if count == 0 or len(ys) != count:
+        raise ValueError("xs and ys must be non-empty lists of equal length")
+    x0, y0 = xs[0], ys[0]
+    for x, y in zip(xs, ys):
+        if x.dim() != 2 or y.dim() != 2 or x.shape != x0.shape or y.shape != y0.shape:
+            raise ValueError("every x (and every y) must be 2-D of one shape")
+        if x.stride() != x0.stride() or y.stride() != y0.stride() or x.stride(1) != 1 or y.stride(1) != 1:
+            raise ValueError("rows must be contiguous with one row stride per operand")
+        if x.dtype != x0.dtype or y.dtype != x0.dtype:
+            raise TypeError("x and y must share a dtype")
+    n, f_in = x0.shape
+    f_out = y0.shape[1]
+    dev = x0.device
+    if w_outs is None:
+        w_outs = [torch.empty((f_out, f_in), dtype=torch.float32, device=dev) for _ in range(count)]
+    if b_outs is None:
+        b_outs = [torch.empty(f_out, dtype=torch.float32, device=dev) for _ in range(count)]
+    arr = ctypes.c_void_p * count
+    xp, yp = arr(*[x.data_ptr() for x in xs]), arr(*[y.data_ptr() for y in ys])
+    wp, bp = arr(*[w.data_ptr() for w in w_outs]), arr(*[b.data_ptr() for b in b_outs])
+    st_arr = (ctypes.c_int32 * count)()
+    iters = ctypes.c_int32(0)
+    ws = _workspace(lib().kvx_fit_recolor_workspace_size(count, f_in, f_out), dev, workspace)
+    st = lib().kvx_fit_recolor(count, xp, x0.stride(0), yp, y0.stride(0), _dtype_code(x0), n, f_in, f_out,
+                               float(rho_x), float(rho_y), wp, bp, st_arr, ctypes.byref(iters), _ptr(ws), ws.numel(),
+                               _stream(stream))
+    if info is not None:
+        info["iters"] = int(iters.value)
+    if status is not None:
+        status.extend(int(v) for v in st_arr)
+        if st not in (OK, ERR_NOT_SPD, ERR_NOT_CONVERGED):
+            _check(st, "kvx_fit_recolor")
+    else:
+        _check(st, "kvx_fit_recolor")
+    return w_outs, b_outs
 
 
 def fold_lowrank(wt: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16,

@@ -51,7 +51,9 @@ typedef enum {
   KVX_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
   KVX_ERR_NOT_SPD = 4,     /* regularised Gram matrix not positive definite */
   KVX_ERR_HIP = 5,         /* a HIP runtime call failed */
-  KVX_ERR_UNSUPPORTED = 6  /* a valid combination this build does not implement */
+  KVX_ERR_UNSUPPORTED = 6, /* a valid combination this build does not implement */
+  KVX_ERR_NOT_CONVERGED = 7 /* an iteration did not converge, or its result is not determined
+                               (polar factor of a rank-deficient whitened cross-covariance) */
 } kvx_status;
 
 typedef enum { KVX_F32 = 0, KVX_BF16 = 1 } kvx_dtype;
@@ -324,6 +326,53 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
                           int32_t f_out, double lambda_abs, double lambda_rel,
                           int32_t fit_intercept, float* const* w_out, float* const* b_out,
                           int32_t* status, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Moment-matched ("Recolor") fit of `count` affine maps of one shape
+ * ("Prefill-Free Cross-Family KV Cache Transfer ...", Key Contributions 2 and
+ * Methodology 3: both feature spaces are whitened, aligned by an orthogonal
+ * Procrustes solution, and the receiver's means and covariances are put
+ * back):
+ *   S_xx, S_yy, S_xy = covariances of the centred calibration rows,
+ *   S_xx += rho_x trace(S_xx) / f_in I,  S_yy += rho_y trace(S_yy) / f_out I,
+ *   M = A_x^T S_xy A_y for whitenings with A^T S A = I,
+ *   Q = the polar factor of M (orthonormal columns, Q = U V^T from M's SVD),
+ *   W = A_x Q A_y^-1,  b = mean_y - mean_x W.
+ * W does not depend on the choice of whitening.  The translated calibration
+ * rows x W + b have the receiver's mean and (with rho_x = 0) covariance.
+ *
+ * x, y: HOST arrays of `count` device pointers to [n_rows][f_in] (row stride
+ *   ldx) and [n_rows][f_out] (row stride ldy) matrices of in_dtype; bf16
+ *   rows need f_in, f_out, ldx, ldy multiples of 8 and 16-byte aligned bases.
+ * f_in >= f_out (Q with orthonormal columns); f_in < f_out returns
+ *   KVX_ERR_UNSUPPORTED.
+ * rho_x, rho_y >= 0: relative regularisers (rows that repeat a layer tap make
+ *   S_xx singular; rho_x > 0 is then required).
+ * w_out: HOST array of device fp32 [f_out][f_in] (output-major, the layout
+ *   kvx_translate takes); b_out: HOST array of device fp32 [f_out]; neither
+ *   may be NULL.
+ * status: host int32 [count] or NULL; receives per problem KVX_OK,
+ *   KVX_ERR_NOT_SPD (a regularised covariance is not positive definite) or
+ *   KVX_ERR_NOT_CONVERGED (M numerically rank-deficient, so Q is not
+ *   determined: the iteration did not converge, or ||(M^T M / c)^-1/2||_F >
+ *   1e6 for c = ||M^T M||_F; this happens when the calibration rows hold
+ *   fewer distinct sender rows than f_out).
+ * iters: host int32 or NULL; receives the number of polar iterations run.
+ * workspace: device scratch of kvx_fit_recolor_workspace_size(count, f_in,
+ *   f_out) bytes (the Gram partials, shared, plus about
+ *   8 (f_in^2 + 2 f_in f_out + 7 f_out^2) bytes per problem).
+ * Moments are accumulated as in kvx_fit_ridge (bf16: fp32 on matrix cores,
+ * partials added in fp64); the factorisations, the polar iteration (coupled
+ * Newton-Schulz for (M^T M)^-1/2) and the products run in fp64.  Synchronises
+ * `stream` once per polar iteration.  Returns the first non-OK problem status,
+ * else KVX_OK; argument errors as kvx_fit_ridge.
+ * ---------------------------------------------------------------------- */
+size_t kvx_fit_recolor_workspace_size(int32_t count, int32_t f_in, int32_t f_out);
+int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void* const* y,
+                    int64_t ldy, int32_t in_dtype, int64_t n_rows, int32_t f_in, int32_t f_out,
+                    double rho_x, double rho_y, float* const* w_out, float* const* b_out,
+                    int32_t* status, int32_t* iters, void* workspace, size_t ws_bytes,
+                    void* stream);
 
 /* ------------------------------------------------------------------------
  * Rank-r fold ("Prefill-Free ...", Methodology 3: low-rank corrections folded

@@ -134,6 +134,24 @@ def test_other_entry_points_validate_before_launch():
                            1 << 40, None) == kvx.ERR_INVALID                     # intercept needs b_out
     assert L.kvx_fit_ridge(fake, 64, fake, 64, kvx.BF16, 10, 64, 64, 0.0, 0.0, 0, fake, None, fake,
                            16, None) == kvx.ERR_WORKSPACE
+    arr = ctypes.c_void_p * 1
+    ptrs = arr(0x1000)
+    nul = arr(0)
+
+    def recolor(count=1, ldx=64, f_in=64, f_out=64, dt=kvx.BF16, rx=1e-3, ry=0.0, w=ptrs, b=ptrs, ws=1 << 40):
+        return L.kvx_fit_recolor(count, ptrs, ldx, ptrs, 64, dt, 10, f_in, f_out, rx, ry, w, b, None, None, fake,
+                                 ws, None)
+
+    assert recolor(count=0) == kvx.OK
+    assert recolor(rx=-1.0) == kvx.ERR_INVALID
+    assert recolor(b=nul) == kvx.ERR_INVALID                  # the bias is always written
+    assert recolor(ldx=32) == kvx.ERR_SHAPE
+    assert recolor(f_in=32, ldx=64) == kvx.ERR_UNSUPPORTED     # f_in < f_out
+    assert recolor(f_in=60, f_out=56) == kvx.ERR_UNSUPPORTED   # bf16 rows in 16-byte pieces
+    assert recolor(ws=16) == kvx.ERR_WORKSPACE
+    assert L.kvx_fit_recolor_workspace_size(64, 3072, 1024) > 64 * 8 * (3072 * 3072 + 2 * 3072 * 1024)
+    assert L.kvx_fit_recolor_workspace_size(0, 3072, 1024) == 0
+    assert kvx.status_string(kvx.ERR_NOT_CONVERGED) == "iteration did not converge"
     assert L.kvx_fold_lowrank(fake, fake, fake, 0, 8, 8, 2, fake, kvx.BF16, None) == kvx.OK
     assert L.kvx_fold_lowrank(fake, None, fake, 1, 8, 8, 2, fake, kvx.BF16, None) == kvx.ERR_INVALID
     assert L.kvx_fold_lowrank(fake, fake, fake, 1, 8, 8, 2, fake, 5, None) == kvx.ERR_INVALID

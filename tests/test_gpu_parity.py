@@ -754,3 +754,134 @@ def test_fit_full_size_normal_equations():
         res = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
         say(f"  residual {res:.3e}")
         assert res <= 1e-3
+
+
+# ---------------------------------------------------------------- Recolor fit
+
+
+def _recolor_err(w, b, wo, bo):
+    return O.rel_err(w.cpu().numpy(), wo.T), O.rel_err(b.cpu().numpy(), bo)
+
+
+@pytest.mark.parametrize("n,f_in,f_out", [(512, 64, 64), (700, 128, 64), (1000, 264, 72), (2100, 520, 136)])
+def test_recolor_f32_vs_oracle(n, f_in, f_out):
+    """fp32 calibration rows (moments accumulated in fp64): correlated
+    features, a receiver partly explained by them; sizes spanning several
+    64- and 256-wide solve blocks with ragged tails."""
+    say(f"recolor fp32 n={n} f_in={f_in} f_out={f_out}")
+    rng = np.random.default_rng(n + f_in)
+    x = rng.standard_normal((n, f_in)) @ (rng.standard_normal((f_in, f_in)) / np.sqrt(f_in)) + 0.5
+    y = 0.3 * (x @ rng.standard_normal((f_in, f_out)) / np.sqrt(f_in)) + rng.standard_normal((n, f_out)) - 1.0
+    xt = torch.as_tensor(x, dtype=torch.float32, device=DEV)
+    yt = torch.as_tensor(y, dtype=torch.float32, device=DEV)
+    info = {}
+    (w,), (b,) = kvx.fit_recolor([xt], [yt], info=info)
+    wo, bo = O.recolor_fit(O.as_f64(xt), O.as_f64(yt))
+    ew, eb = _recolor_err(w, b, wo, bo)
+    say(f"  W max|err|/RMS = {ew:.3e}, b {eb:.3e}, {info['iters']} polar iterations")
+    assert ew <= TOL_F32 and eb <= TOL_F32
+    # moments of the translated calibration rows, from the oracle's data
+    t = O.as_f64(xt) @ w.cpu().numpy().astype(np.float64).T + b.cpu().numpy()
+    ym = O.as_f64(yt)
+    assert np.max(np.abs(t.mean(0) - ym.mean(0))) <= 1e-4 * np.sqrt(np.mean(ym * ym))
+    ct = np.cov(t.T, bias=True)
+    cy = np.cov(ym.T, bias=True)
+    assert np.max(np.abs(ct - cy)) <= 1e-4 * np.max(np.abs(cy))
+
+
+def test_recolor_recovers_planted_map():
+    """An exact linear relation y = x A + c is recovered (the whitened
+    cross-covariance is already orthonormal)."""
+    say("recolor planted map")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    n, f_in, f_out = 1500, 192, 64
+    x = torch.randn((n, f_in), generator=g, device=DEV, dtype=torch.float64)
+    a = torch.randn((f_in, f_out), generator=g, device=DEV, dtype=torch.float64) / np.sqrt(f_in)
+    c = torch.randn(f_out, generator=g, device=DEV, dtype=torch.float64)
+    xt, yt = x.float(), (x @ a + c).float()
+    (w,), (b,) = kvx.fit_recolor([xt], [yt])
+    # the relation holds up to the fp32 rounding of y
+    an = a.cpu().numpy()
+    ea = np.max(np.abs(w.cpu().numpy().T - an)) / np.sqrt(np.mean(an * an))
+    ec = np.max(np.abs(b.cpu().numpy() - c.cpu().numpy()))
+    say(f"  |W - A| / RMS(A) = {ea:.3e}, |b - c| = {ec:.3e}")
+    assert ea <= 1e-4 and ec <= 1e-4
+
+
+@pytest.mark.parametrize("layer", [0, 15, 31])
+def test_recolor_bf16_vs_oracle(layer):
+    """Gathered bf16 features of 16384 calibration tokens (about 3600
+    distinct sender rows; duplicated taps at layers 0 and 31 make S_xx
+    singular: rho_x = 1e-3) -> the receiver's keys."""
+    say(f"recolor bf16 layer {layer}, 16384 calibration rows")
+    c = fit_case(16384)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    x = kvx.gather_features(c["k_send"], dev_i32(tmap_o), taps[layer])
+    y = c["recv_k"][layer].reshape(16384, 1024)
+    info = {}
+    (w,), (b,) = kvx.fit_recolor([x], [y], rho_x=1e-3, info=info)
+    wo, bo = O.recolor_fit(O.features(c["k_send"], tmap_o, taps[layer]), O.as_f64(y), rho_x=1e-3)
+    ew, eb = _recolor_err(w, b, wo, bo)
+    say(f"  W max|err|/RMS = {ew:.3e}, b {eb:.3e}, {info['iters']} polar iterations")
+    assert ew <= TOL_BF16 and eb <= TOL_BF16
+
+
+def test_recolor_too_few_distinct_rows():
+    """4096 calibration tokens hold about 900 distinct sender rows, fewer
+    than the 1024 outputs: the whitened cross-covariance has rank < 1024 (its
+    smallest singular values vanish in the oracle's SVD), the Procrustes
+    rotation is not determined, and the fit says so."""
+    say("recolor with fewer distinct rows than outputs")
+    c = fit_case(4096)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    assert np.unique(tmap_o).size < 1024
+    x = kvx.gather_features(c["k_send"], dev_i32(tmap_o), taps[15])
+    y = c["recv_k"][15].reshape(4096, 1024)
+    st = []
+    kvx.fit_recolor([x], [y], rho_x=1e-3, status=st)
+    assert st == [kvx.ERR_NOT_CONVERGED]
+
+
+def test_recolor_batched_statuses():
+    """Two problems in one call: one with a constant receiver column (S_yy
+    singular, rho_y = 0 -> not positive definite) next to a well-posed one,
+    which is still fitted (vs the oracle)."""
+    say("recolor batched, one singular receiver covariance")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    n, f_in, f_out = 900, 128, 64
+    xs = [torch.randn((n, f_in), generator=g, device=DEV).to(torch.bfloat16) for _ in range(2)]
+    ys = [torch.randn((n, f_out), generator=g, device=DEV).to(torch.bfloat16) for _ in range(2)]
+    ys[1][:, 7] = 2.0
+    st = []
+    ws, bs = kvx.fit_recolor(xs, ys, status=st)
+    assert st == [kvx.OK, kvx.ERR_NOT_SPD]
+    wo, bo = O.recolor_fit(O.as_f64(xs[0]), O.as_f64(ys[0]))
+    ew, eb = _recolor_err(ws[0], bs[0], wo, bo)
+    say(f"  W max|err|/RMS = {ew:.3e}, b {eb:.3e}")
+    assert ew <= TOL_F32 and eb <= TOL_F32
+    with pytest.raises(kvx.KvxError) as ei:
+        kvx.fit_recolor(xs, ys)
+    assert ei.value.status == kvx.ERR_NOT_SPD
+
+
+def test_recolor_full_size_vs_oracle():
+    """65536 calibration tokens, one layer (3072 -> 1024), the whole fitted
+    map against the oracle's."""
+    say("recolor 65536 rows, layer 20, vs the oracle")
+    c = fit_case(65536)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    layer = 20
+    x = kvx.gather_features(c["k_send"], dev_i32(tmap_o), taps[layer])
+    y = c["recv_k"][layer].reshape(65536, 1024)
+    info = {}
+    (w,), (b,) = kvx.fit_recolor([x], [y], rho_x=1e-3, info=info)
+    say(f"  {info['iters']} polar iterations; oracle ...")
+    wo, bo = O.recolor_fit(O.features(c["k_send"], tmap_o, taps[layer]), O.as_f64(y), rho_x=1e-3)
+    ew, eb = _recolor_err(w, b, wo, bo)
+    say(f"  W max|err|/RMS = {ew:.3e}, b {eb:.3e}")
+    assert ew <= TOL_BF16 and eb <= TOL_BF16
