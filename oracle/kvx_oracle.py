@@ -372,6 +372,61 @@ def recolor_fit(x, y, rho_x: float = 0.0, rho_y: float = 0.0):
 
 
 # ---------------------------------------------------------------------------
+# FP8 map storage   [LB] "Implementation Guidelines" (weights may be stored
+# quantised, e.g. FP8; the product keeps 16-bit precision)
+
+
+def e4m3_values() -> np.ndarray:
+    """Value of each of the 256 OCP FP8 E4M3 codes: sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals
+    m/8 * 2^-6; S.1111.111 is NaN and there are no infinities."""
+    out = np.empty(256)
+    for c in range(256):
+        sgn = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 15 and m == 7:
+            out[c] = np.nan
+        elif e == 0:
+            out[c] = sgn * (m / 8.0) * 2.0 ** -6
+        else:
+            out[c] = sgn * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each finite value by search over the 127
+    non-negative finite values (codes 0..126, ascending); a tie goes to the
+    even code (even mantissa); magnitudes past 448 saturate to 448; the sign
+    bit follows the sign of x (also for zeros)."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = e4m3_values()[:127]
+    a = np.minimum(np.abs(x), vals[-1])
+    hi = np.clip(np.searchsorted(vals, a), 1, 126)   # vals[hi - 1] < a <= vals[hi] inside the range
+    lo = hi - 1
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a == 0.0, 0, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8(w32):
+    """Per-row FP8 storage of fp32 maps [rows][cols]: scale = amax / 448 and
+    codes of w / scale, both quotients in fp32 (correctly rounded); a row
+    whose scale is 0 gets scale 1.  Returns (codes uint8, scale float32)."""
+    w32 = np.asarray(w32, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = e4m3_encode((w32 / scale[..., None]).astype(np.float64))
+    return q, scale
+
+
+def fp8_dequant(q, scale) -> np.ndarray:
+    """The map a row of codes stands for: scale * value(code), float64."""
+    return e4m3_values()[np.asarray(q)] * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+# ---------------------------------------------------------------------------
 # error metric used by the parity tests
 
 
