@@ -434,6 +434,51 @@ def fit_measure(dev, xs, ys, reps=2):
                          "traffic": None}}
 
 
+def fp8_measure(dev, x, taps, steps=10):
+    """The headline step's translation with the maps stored as fp8 (E4M3
+    codes, one fp32 scale per output; folded in fp32, quantised by the
+    library): same inputs, rotations and outputs."""
+    q, sc = {}, {}
+    for role in ("k", "v"):
+        wt, u, v = x[f"fold_{role}"]
+        q[role], sc[role] = kvx.quantize_fp8(kvx.fold_lowrank(wt, u, v, torch.float32))
+    tmap = kvx.align_tokens(x["send_end"], x["recv_end"])
+    N_R = x["recv_end_h"].size
+    U = int(1 + np.count_nonzero(np.diff(tmap.cpu().numpy())))
+    k_out = torch.empty((32, N_R, 8, 128), dtype=torch.bfloat16, device=dev)
+    v_out = torch.empty_like(k_out)
+    send = kvx.cache_desc(x["k_send"], 5e5)
+    recv = kvx.CacheDesc(32, N_R, 8, 128, kvx.BF16, 1e6)
+    ws = torch.empty(kvx.translate_workspace_size(send, recv, 3, False), dtype=torch.uint8, device=dev)
+
+    def call(stage):
+        kvx.translate_fp8(x["k_send"], x["v_send"], tmap, taps, q["k"], q["v"], sc["k"], sc["v"], x["b_k"], x["b_v"],
+                          send_rope_base=5e5, recv_rope_base=1e6, k_recv=k_out, v_recv=v_out, workspace=ws,
+                          stage_ms=stage)
+
+    for _ in range(2):
+        call([])
+    stages = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st = []
+        call(st)
+        stages.append(st)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gemm_ms = float(np.mean([s_[1] for s_ in stages]))
+    flops = 2.0 * U * 3072 * 1024 * 32 * 2
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    return {"workload": "flattened + RoPE, 32768 receiver tokens, maps stored as fp8 E4M3 with per-output scales "
+                        "(widened exactly to bf16 / fp16 operands)",
+            "distinct_sender_rows": U, "tokens_per_s": N_R / (ms * 1e-3), "translate_ms": ms,
+            "map_bytes": 2 * 32 * 1024 * (3072 + 4),
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "kernel": "flat_gemm_kernel (fp8 maps)",
+                         "launch_ms": gemm_ms, "flops_per_launch": flops, "traffic": None}}
+
+
 def recolor_measure(dev, xs, ys, reps=2):
     """Moment-matched (Recolor) fit of the whole calibration setting in one
     call: 64 problems of 65536 rows, 3072 -> 1024, rho_x = 1e-3."""
@@ -483,6 +528,7 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"))
+    ap.add_argument("--fp8-only", action="store_true", help="measure the fp8-map translation alone")
     ap.add_argument("--fit-only", action="store_true",
                     help="measure the ridge and Recolor fits of the calibration setting alone")
     ap.add_argument("--perhead-only", action="store_true",
@@ -506,6 +552,12 @@ def main():
     if args.calibration_copy:
         log("bench: calibration copy")
         calibration_copy(dev)
+    if args.fp8_only:
+        log("bench: flattened + RoPE, bf16 and fp8 maps")
+        x = flat_inputs(dev)
+        taps = kvx.layer_map(36, 32, 3, 4)
+        print(json.dumps({"also_fp8_maps": fp8_measure(dev, x, taps)}), flush=True)
+        return
     if args.fit_only:
         log("bench: calibration fits")
         xs, ys = fit_inputs(dev)
@@ -585,6 +637,8 @@ def main():
         res["also"] = perhead_measure(dev)
         log("bench: per-head workload, rotated keys")
         res["also_perhead_rope"] = perhead_measure(dev, rope=True)
+        log("bench: flattened + RoPE, fp8 maps")
+        res["also_fp8_maps"] = fp8_measure(dev, x, taps)
         del x, outs, ws
         torch.cuda.empty_cache()
         log("bench: flattened + RoPE + receiver key norm, 32768 tokens")

@@ -59,6 +59,9 @@ static int32_t recv_tab_rows_for(const kvx_cache_desc* recv, int32_t pos_limit) 
   return r > pos_limit ? r : pos_limit;
 }
 
+// map element type of the fp8 entry point (internal; not a kvx_dtype)
+constexpr int32_t W_FP8 = 2;
+
 static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
                                     int32_t per_head, int32_t w_dtype, bool key_role, bool value_role,
                                     int32_t pos_limit, void* base) {
@@ -93,7 +96,7 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
     if (w_dtype == KVX_F32) {
       if (key_role) w.wk16 = c.take<uint16_t>(2 * map_elems);
       if (value_role) w.wv16 = c.take<uint16_t>(2 * map_elems);
-    } else if (srope) {
+    } else if (srope && w_dtype == KVX_BF16) {
       w.wk16 = c.take<uint16_t>(map_elems);
     }
   }
@@ -191,9 +194,15 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
                           const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
                           const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
                           const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
-                          void* stream, hipEvent_t* ev, const kvx_placement* pl) {
+                          void* stream, hipEvent_t* ev, const kvx_placement* pl, const float* s_k = nullptr,
+                          const float* s_v = nullptr) {
   if (!desc_ok(send) || !desc_ok(recv)) return KVX_ERR_INVALID;
-  if (w_dtype != KVX_F32 && w_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  if (w_dtype != KVX_F32 && w_dtype != KVX_BF16 && w_dtype != W_FP8) return KVX_ERR_INVALID;
+  if (w_dtype == W_FP8) {
+    // fp8 maps: flattened matrix-core path, scales of every present role
+    if ((k_recv && !s_k) || (v_recv && !s_v)) return KVX_ERR_INVALID;
+    if (per_head || send->dtype != KVX_BF16) return KVX_ERR_UNSUPPORTED;
+  }
   if (n_taps < 1 || n_taps > MAX_TAPS || !taps) return KVX_ERR_INVALID;
   const bool do_k = k_recv != nullptr, do_v = v_recv != nullptr;
   if (do_k && (!k_send || !wt_k)) return KVX_ERR_INVALID;
@@ -379,7 +388,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
       if (int st = launch_rope_table(w.tab_recv, recv_tab_rows_for(recv, pos_limit), recv->head_dim, recv->rope_base, s))
         return st;
     }
-    if (split) {
+    if (w_dtype == W_FP8) {
+      r.wt = wt_k;
+      r.wscale = s_k;
+    } else if (split) {
       if (int st = launch_prepare_maps(wt_k, w.wk16, map_rows, f_in, r.a_f16 ? 2 : 1, s)) return st;
       r.wt = w.wk16;
     } else if (r.a_f16) {
@@ -400,7 +412,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     r.a_layer_stride = send_layer_elems;
     r.a_compact = 0;
     r.a_f16 = 0;
-    if (split) {
+    if (w_dtype == W_FP8) {
+      r.wt = wt_v;
+      r.wscale = s_v;
+    } else if (split) {
       if (int st = launch_prepare_maps(wt_v, w.wv16, map_rows, f_in, 1, s)) return st;
       r.wt = w.wv16;
     } else {
@@ -428,6 +443,7 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   p.pool_rows = pool_rows;
   p.recv_pos = recv_pos;
   p.pos_limit = pos_limit;
+  p.w8 = w_dtype == W_FP8 ? 1 : 0;
   return main_kernel([&] { return launch_flat(p, roles, n, s); });
 }
 
@@ -458,12 +474,13 @@ int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const v
                         wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, place);
 }
 
-int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
-                        const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
-                        const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
-                        const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
-                        void* stream, float* stage_ms) {
-  if (!stage_ms) return KVX_ERR_INVALID;
+}  // extern "C"
+
+namespace kvx {
+// Runs `call(ev)` with three events (before the preparation kernels, before
+// and after the main kernel) and reports the two phases in stage_ms.
+template <typename F>
+static int timed_call(void* stream, float* stage_ms, F&& call) {
   stage_ms[0] = stage_ms[1] = 0.0f;
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   for (auto& e : ev)
@@ -472,8 +489,7 @@ int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const vo
         if (f) (void)hipEventDestroy(f);
       return KVX_ERR_HIP;
     }
-  int st = translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
+  int st = call(ev);
   if (st == KVX_OK) {
     // events exist only when work was launched (empty problems return early)
     if (hipEventSynchronize(ev[2]) != hipSuccess ||
@@ -485,6 +501,40 @@ int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const vo
   }
   for (auto& e : ev) (void)hipEventDestroy(e);
   return st;
+}
+}  // namespace kvx
+
+extern "C" {
+
+int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                        const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
+                        const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
+                        const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                        void* stream, float* stage_ms) {
+  if (!stage_ms) return KVX_ERR_INVALID;
+  return timed_call(stream, stage_ms, [&](hipEvent_t* ev) {
+    return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
+                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
+  });
+}
+
+int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void* v_send, const kvx_cache_desc* recv,
+                      void* k_recv, void* v_recv, const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                      const uint8_t* wq_k, const uint8_t* wq_v, const float* s_k, const float* s_v, const float* b_k,
+                      const float* b_v, void* workspace, size_t ws_bytes, void* stream, float* stage_ms) {
+  auto call = [&](hipEvent_t* ev) {
+    return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, 0, W_FP8, wq_k,
+                          wq_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr, s_k, s_v);
+  };
+  if (!stage_ms) return call(nullptr);
+  return timed_call(stream, stage_ms, call);
+}
+
+int kvx_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q_out, float* scale_out, void* stream) {
+  if (rows < 0 || cols < 1) return KVX_ERR_INVALID;
+  if (rows == 0) return KVX_OK;
+  if (!w || !q_out || !scale_out) return KVX_ERR_INVALID;
+  return launch_quantize_fp8(w, rows, cols, q_out, scale_out, static_cast<hipStream_t>(stream));
 }
 
 int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t derotate,

@@ -64,13 +64,17 @@ constexpr int FT_ROWS_PER_LD = 8;                     // rows of one direct load
 constexpr int FT_A_LD = FT_M / FT_ROWS_PER_LD / FT_WAVES;  // A loads per wave per step
 constexpr int FT_B_LD = FT_N / FT_ROWS_PER_LD / FT_WAVES;  // B loads per wave per step
 constexpr int FT_EP_FLOATS = 32 * 128;                // staging of one wave (16 KB)
+// fp8 maps: the W part of a step is 256 outputs x 64 bytes (16 KB, in the
+// first half of its ring part); a load covers 16 rows (1 KB)
+constexpr int FT_B8_LD = FT_N * FT_BK / 1024 / FT_WAVES;
 
 struct FlatKArgs {
   const uint16_t* a_src[2];
   int64_t a_layer_stride[2];
   int32_t a_compact[2];
   int32_t a_f16[2];
-  const uint16_t* wt[2];  // [L_R][F_out][K], K = k_dim
+  const void* wt[2];      // [L_R][F_out][K], K = k_dim: 16-bit operands, or fp8 E4M3 codes
+  const float* wscale[2]; // fp8 maps: scale of each output [L_R][F_out]
   const float* bias[2];
   uint16_t* out[2];
   int32_t rotate[2];
@@ -104,6 +108,9 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 // Physical 16-byte chunk of logical chunk c in tile row r.
 __device__ __forceinline__ int ft_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+// fp8 W rows are 64 bytes (four 16-byte chunks), swizzled by (r / 4) mod 4
+// so the 16 rows of one quarter-wave fragment read hit distinct banks.
+__device__ __forceinline__ int ft_chunk8(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 // Per-tile addressing of this thread's direct loads.  A load instruction
 // covers 8 tile rows (1 KB of the stage); lane j lands at row +j/8, physical
@@ -139,13 +146,15 @@ __device__ __forceinline__ void ft_issue_a(const TileAddr& ta, int k, uint16_t* 
   for (int i = 0; i < FT_A_LD; ++i) dma16(a_r, ta.a_off[i], a_soff, part + (wave * FT_A_LD + i) * 512);
 }
 
-// W part of step k into `part`.
+// W part of step k into `part` (fp8 maps: 64 bytes of each of the 256 rows).
+template <bool W8>
 __device__ __forceinline__ void ft_issue_b(const TileAddr& ta, int k, uint16_t* part) {
   const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t w_r = buf_rsrc(ta.w_base, k < ta.nk ? ta.w_bytes : 0u);
-  const uint32_t b_soff = 2u * static_cast<uint32_t>(k * FT_BK);
+  constexpr int n_ld = W8 ? FT_B8_LD : FT_B_LD;
+  const uint32_t b_soff = (W8 ? 1u : 2u) * static_cast<uint32_t>(k * FT_BK);
 #pragma unroll
-  for (int i = 0; i < FT_B_LD; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * FT_B_LD + i) * 512);
+  for (int i = 0; i < n_ld; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * n_ld + i) * 512);
 }
 
 // One K step from an A part and a W part: 4 x (2 A + 4 B fragment reads,
@@ -174,6 +183,63 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
   }
 }
 
+// Eight fp8 E4M3 codes (two dwords, element e in byte e) as eight 16-bit
+// operands of the A operand's type; exact (every E4M3 value is a normal bf16
+// and a normal fp16).  The per-output scale is applied in the epilogue.
+template <bool F16>
+__device__ __forceinline__ u32x4 ft_fp8x8(uint32_t lo, uint32_t hi) {
+  if constexpr (F16)
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
+  else
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+// One K step with fp8 maps.  The order of the 64 k inside a step is
+// permuted (the same for both operands, so the contraction is unchanged):
+// sub-step kk of lane half h takes logical 8-element chunk 4h + kk, so the
+// W bytes a lane needs for sub-steps 2p and 2p+1 are one 16-byte chunk
+// (logical 2h + p of its 64-byte row) and one fragment read serves two
+// sub-steps.
+template <bool F16>
+__device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave & 3, wn = wave >> 2;
+  const char* sa = reinterpret_cast<const char*>(pa);
+  const char* sb = reinterpret_cast<const char*>(pb);
+  const int fr = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    u32x4 braw[4];
+    const int pc8 = ft_chunk8(fr, 2 * h + kp) << 4;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) braw[ni] = *reinterpret_cast<const u32x4*>(sb + (wn * 128 + ni * 32 + fr) * 64 + pc8);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kk = 2 * kp + sub;
+      const int pc = ft_chunk(fr, 4 * h + kk) << 4;
+      u32x4 af[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4*>(sa + (wm * 64 + mi * 32 + fr) * 128 + pc);
+      // each W fragment is converted right before its two products, so one
+      // converted fragment is live at a time
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const u32x4 bfr = sub == 0 ? ft_fp8x8<F16>(braw[ni][0], braw[ni][1]) : ft_fp8x8<F16>(braw[ni][2], braw[ni][3]);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) acc[mi][ni] = mfma32<F16>(af[mi], bfr, acc[mi][ni]);
+      }
+    }
+  }
+}
+
 // Wait until all but the last A part issued by this wave have landed, then
 // one barrier: the parts of the current step are complete and every wave
 // has finished the previous step, whose two parts are now free.
@@ -189,16 +255,21 @@ __device__ __forceinline__ void ft_sync() {
 // step k-1.
 #define FT_STEP(K, PA, PB, NB, NA, LIVE)        \
   ft_sync();                                    \
-  ft_issue_b(ta, (K) + 1, NB);                  \
+  ft_issue_b<W8>(ta, (K) + 1, NB);              \
   ft_issue_a(ta, (K) + 2, NA);                  \
-  if (LIVE) ft_compute<F16>(PA, PB, acc);
+  if (LIVE) {                                   \
+    if constexpr (W8)                           \
+      ft_compute8<F16>(PA, PB, acc);            \
+    else                                        \
+      ft_compute<F16>(PA, PB, acc);             \
+  }
 
 // K loop over nk >= 1 steps with A0, W0 and A1 already issued into parts 0,
 // 1 and 2.  The part pattern repeats every five steps.  Issues are
 // unconditional (steps past the end read an empty buffer range and are not
 // multiplied); the loads still in flight at the end are drained before the
 // parts are reused.
-template <bool F16>
+template <bool F16, bool W8>
 __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
                                          uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
   for (int k = 0; k < nk; k += 5) {
@@ -215,7 +286,7 @@ __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p
 // Both operand types in one launch: the K loop is chosen per tile.  PLACED:
 // output rows from the slot array and rotary positions per token (else row
 // and position i).
-template <bool PLACED>
+template <bool PLACED, bool W8>
 __global__ __attribute__((amdgpu_flat_work_group_size(FT_THREADS, FT_THREADS), amdgpu_waves_per_eu(2, 2))) void
 flat_gemm_kernel(const FlatKArgs args) {
   __shared__ __attribute__((aligned(1024))) uint16_t p0[FT_PART_ELEMS];
@@ -261,8 +332,9 @@ flat_gemm_kernel(const FlatKArgs args) {
     ta.taps1 = args.taps[l][1];
     ta.spt = args.send_row / FT_BK;
     ta.n_taps = args.n_taps;
-    ta.w_base = reinterpret_cast<const char*>(args.wt[role] + (static_cast<int64_t>(l) * args.f_out + n0) * args.k_dim);
-    ta.w_bytes = static_cast<uint32_t>(2 * FT_N * args.k_dim);
+    constexpr int wb = W8 ? 1 : 2;  // bytes per map element
+    ta.w_base = static_cast<const char*>(args.wt[role]) + (static_cast<int64_t>(l) * args.f_out + n0) * args.k_dim * wb;
+    ta.w_bytes = static_cast<uint32_t>(wb * FT_N * args.k_dim);
     ta.nk = nk;
 #pragma unroll
     for (int i = 0; i < FT_A_LD; ++i) {
@@ -272,10 +344,18 @@ flat_gemm_kernel(const FlatKArgs args) {
       const int32_t srow = args.a_compact[role] ? u : args.uniq[u];
       ta.a_off[i] = 2u * static_cast<uint32_t>(srow * args.send_row + ft_chunk(r, lane & 7) * 8);
     }
+    if constexpr (W8) {
 #pragma unroll
-    for (int i = 0; i < FT_B_LD; ++i) {
-      const int r = (wave * FT_B_LD + i) * FT_ROWS_PER_LD + lrow;
-      ta.b_off[i] = 2u * static_cast<uint32_t>(r * args.k_dim + ft_chunk(r, lane & 7) * 8);
+      for (int i = 0; i < FT_B8_LD; ++i) {
+        const int r = (wave * FT_B8_LD + i) * 16 + (lane >> 2);
+        ta.b_off[i] = static_cast<uint32_t>(r * args.k_dim + ft_chunk8(r, lane & 3) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FT_B_LD; ++i) {
+        const int r = (wave * FT_B_LD + i) * FT_ROWS_PER_LD + lrow;
+        ta.b_off[i] = 2u * static_cast<uint32_t>(r * args.k_dim + ft_chunk(r, lane & 7) * 8);
+      }
     }
 
     f32x16 acc[2][4];
@@ -290,12 +370,12 @@ flat_gemm_kernel(const FlatKArgs args) {
     // staging before the final barrier of the previous tile, so they are
     // free.
     ft_issue_a(ta, 0, p0);
-    ft_issue_b(ta, 0, p1);
+    ft_issue_b<W8>(ta, 0, p1);
     ft_issue_a(ta, 1, p2);
     if (args.a_f16[role])
-      ft_kloop<true>(ta, nk, p0, p1, p2, p3, p4, acc);
+      ft_kloop<true, W8>(ta, nk, p0, p1, p2, p3, p4, acc);
     else
-      ft_kloop<false>(ta, nk, p0, p1, p2, p3, p4, acc);
+      ft_kloop<false, W8>(ta, nk, p0, p1, p2, p3, p4, acc);
 
     // ------------------------------------------------------------ epilogue
     // Each wave owns 64 unique rows x one 128-wide head, written in two
@@ -312,9 +392,13 @@ flat_gemm_kernel(const FlatKArgs args) {
     const int col = wn * 128 + 8 * q;  // tile column of the first pair member
     const float* bias = args.bias[role];
     float bcol[4];  // bias of the columns this lane stages (ni * 32 + lane % 32)
+    float wsc[4];   // fp8 maps: scale of those columns
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      bcol[ni] = bias ? bias[static_cast<int64_t>(l) * args.f_out + n0 + wn * 128 + ni * 32 + (lane & 31)] : 0.0f;
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t oc = static_cast<int64_t>(l) * args.f_out + n0 + wn * 128 + ni * 32 + (lane & 31);
+      bcol[ni] = bias ? bias[oc] : 0.0f;
+      wsc[ni] = W8 ? args.wscale[role][oc] : 1.0f;
+    }
     const bool rot = args.rotate[role] != 0;
     // the receiver's key normalisation: weights of this lane's pair members
     // (channels 8q.. and 64 + 8q.., read where used: L1-resident)
@@ -340,7 +424,10 @@ flat_gemm_kernel(const FlatKArgs args) {
         for (int r = 0; r < 16; ++r) {
           const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int cc = (ni * 32 + (lane & 31)) ^ (((row >> 2) & 1) << 5);
-          ep[row * 128 + cc] = acc[ph][ni][r] + bcol[ni];
+          if constexpr (W8)
+            ep[row * 128 + cc] = acc[ph][ni][r] * wsc[ni] + bcol[ni];
+          else
+            ep[row * 128 + cc] = acc[ph][ni][r] + bcol[ni];
         }
       KVX_COMPILER_FENCE();  // LDS operations of one wave execute in order
       __builtin_amdgcn_sched_barrier(0);
@@ -516,6 +603,60 @@ int launch_prepare_maps(const void* in, uint16_t* out, int64_t rows, int32_t f_i
   return KVX_OK;
 }
 
+// ---------------------------------------------------------------- fp8 map storage
+// "Cross-Model KV Cache Transfer in Production" (Implementation Guidelines,
+// precision): weights may be stored quantised (FP8) while the product keeps
+// 16-bit operands.  OCP E4M3 (bias 7, 3 mantissa bits, no infinities, 448
+// the largest finite value): with E = max(exponent(|v|), -6), neighbouring
+// codes at |v| are 2^(E-3) apart, n = rint(|v| 2^(3-E)) in 0..16 (exact
+// power-of-two scaling, then nearest even) and the code is
+// 8 (E + 7) + n - 8, which also covers the subnormals (E = -6, n < 8) and a
+// round-up into the next binade (n = 16).  Codes past 448 saturate there;
+// non-finite inputs saturate too.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a <= 512.0f)) return sign | 0x7eu;
+  int e = static_cast<int>((u >> 23) & 0xffu) - 127;
+  if (e < -6) e = -6;
+  const int n = static_cast<int>(rintf(ldexpf(a, 3 - e)));
+  int code = 8 * (e + 7) + n - 8;
+  if (code > 0x7e) code = 0x7e;
+  return sign | static_cast<uint32_t>(code);
+}
+
+// One workgroup per map row: amax (order-free), scale = amax / 448 (1 when
+// that is zero), codes of w / scale; both divisions correctly rounded.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* __restrict__ w, int32_t cols,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int64_t row = blockIdx.x;
+  const float* x = w + row * cols;
+  __shared__ float red[256];
+  float m = 0.0f;
+  for (int32_t c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(x[c]));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + k]);
+    __syncthreads();
+  }
+  float sc = __fdiv_rn(red[0], 448.0f);
+  if (!(sc > 0.0f)) sc = 1.0f;
+  if (threadIdx.x == 0) scale[row] = sc;
+  for (int32_t c = threadIdx.x; c < cols; c += 256) q[row * cols + c] = static_cast<uint8_t>(e4m3_rne(__fdiv_rn(x[c], sc)));
+}
+
+int launch_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q, float* scale, hipStream_t s) {
+  if (rows <= 0) return KVX_OK;
+  for (int64_t r0 = 0; r0 < rows; r0 += 65535) {
+    const int64_t n = rows - r0 < 65535 ? rows - r0 : 65535;
+    quantize_fp8_kernel<<<static_cast<unsigned>(n), 256, 0, s>>>(w + r0 * cols, cols, q + r0 * cols, scale + r0);
+    KVX_LAUNCH_CHECK();
+  }
+  return KVX_OK;
+}
+
 int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s) {
   if (p.recv_tokens <= 0 || n_roles <= 0) return KVX_OK;
   FlatKArgs a{};
@@ -543,7 +684,8 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
     a.a_layer_stride[j] = roles[j].a_layer_stride;
     a.a_compact[j] = roles[j].a_compact;
     a.a_f16[j] = roles[j].a_f16;
-    a.wt[j] = static_cast<const uint16_t*>(roles[j].wt);
+    a.wt[j] = roles[j].wt;
+    a.wscale[j] = roles[j].wscale;
     a.bias[j] = roles[j].bias;
     a.out[j] = roles[j].out;
     a.rotate[j] = roles[j].rotate;
@@ -554,10 +696,19 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
   a.pool_rows = p.pool_rows;
   a.recv_pos = p.recv_pos;
   a.pos_limit = p.pos_limit;
-  if (p.slot || p.recv_pos || p.pool_rows != p.recv_tokens)
-    flat_gemm_kernel<true><<<G, FT_THREADS, 0, s>>>(a);
-  else
-    flat_gemm_kernel<false><<<G, FT_THREADS, 0, s>>>(a);
+  const bool placed = p.slot || p.recv_pos || p.pool_rows != p.recv_tokens;
+  if (p.w8) {
+    for (int j = 0; j < n_roles; ++j)
+      if (!roles[j].wscale) return KVX_ERR_INVALID;
+    if (placed)
+      flat_gemm_kernel<true, true><<<G, FT_THREADS, 0, s>>>(a);
+    else
+      flat_gemm_kernel<false, true><<<G, FT_THREADS, 0, s>>>(a);
+  } else if (placed) {
+    flat_gemm_kernel<true, false><<<G, FT_THREADS, 0, s>>>(a);
+  } else {
+    flat_gemm_kernel<false, false><<<G, FT_THREADS, 0, s>>>(a);
+  }
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }

@@ -53,7 +53,8 @@ struct FlatRole {
   int64_t a_layer_stride;  // elements between consecutive sender layers of a_src
   int32_t a_compact;       // 1: rows of a_src are run indices u; 0: sender tokens uniq[u]
   int32_t a_f16;           // 1: operands are fp16, 0: bf16
-  const void* wt;          // 16-bit map of the operand type, [L_R][F_out][k_dim]
+  const void* wt;          // 16-bit map of the operand type, [L_R][F_out][k_dim], or fp8 E4M3 codes
+  const float* wscale;     // fp8 maps: [L_R][F_out] scale of each output, else null
   const float* bias;       // [L_R][F_out] or null
   uint16_t* out;           // [L_R][N_R][F_out] bf16
   int32_t rotate;          // rotate outputs at the receiver position
@@ -72,6 +73,7 @@ struct FlatProblem {
   int64_t pool_rows;       // output rows per layer
   const int32_t* recv_pos; // [N_R] rotary position of each receiver token, or null (i)
   int32_t pos_limit;       // positions clamped to [0, pos_limit)
+  int32_t w8;              // maps are fp8 E4M3 codes with per-output scales
 };
 
 int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s);
@@ -80,6 +82,10 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
 // fp32 -> [bf16 hi | bf16 lo]; mode 2 fp32 -> [fp16 hi | fp16 lo] (rows of
 // f_in become rows of 2 f_in).
 int launch_prepare_maps(const void* in, uint16_t* out, int64_t rows, int32_t f_in, int32_t mode, hipStream_t s);
+
+// Per-row fp8 E4M3 quantisation of fp32 maps [rows][cols]: scale = amax / 448
+// (1 for an all-zero row), codes = nearest-even E4M3 of w / scale.
+int launch_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q, float* scale, hipStream_t s);
 
 // ---------------------------------------------------------------- per-head translation (bf16)
 struct HeadProblem {

@@ -30,6 +30,7 @@ EXPORTS = (
     "kvx_translate_timed", "kvx_translate_placed_workspace_size", "kvx_translate_placed", "kvx_gather_features",
     "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fit_ridge_batched_workspace_size",
     "kvx_fit_ridge_batched", "kvx_fit_recolor_workspace_size", "kvx_fit_recolor", "kvx_fold_lowrank",
+    "kvx_quantize_fp8", "kvx_translate_fp8",
 )
 
 
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
             "kvx_fit_recolor": (ctypes.c_int, [i32, vpp, i64, vpp, i64, i32, i64, i32, i32, dbl, dbl, vpp, vpp,
                                                ip, ip, vp, sz, vp]),
             "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
+            "kvx_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+            "kvx_translate_fp8": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                 sz, vp, ctypes.POINTER(ctypes.c_float)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -285,6 +289,68 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
     else:
         ms = (ctypes.c_float * 2)()
         _check(lib().kvx_translate_timed(*args, ms), "kvx_translate_timed")
+        stage_ms.extend([float(ms[0]), float(ms[1])])
+    return (k_recv if k_send is not None else None), (v_recv if v_send is not None else None)
+
+
+def quantize_fp8(w: torch.Tensor, stream=None):
+    """kvx_quantize_fp8 over the last dimension of a fp32 tensor: returns
+    (codes uint8 of w's shape, scales fp32 of w.shape[:-1])."""
+    _need(w, "w", torch.float32)
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _check(lib().kvx_quantize_fp8(_ptr(w), rows, cols, _ptr(q), _ptr(sc), _stream(stream)), "kvx_quantize_fp8")
+    return q, sc
+
+
+def translate_fp8(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], recv_to_send: torch.Tensor,
+                  taps, wq_k: Optional[torch.Tensor], wq_v: Optional[torch.Tensor], s_k: Optional[torch.Tensor],
+                  s_v: Optional[torch.Tensor], b_k: Optional[torch.Tensor] = None,
+                  b_v: Optional[torch.Tensor] = None, *, recv_heads: Optional[int] = None,
+                  recv_head_dim: Optional[int] = None, send_rope_base: float = 0.0, recv_rope_base: float = 0.0,
+                  k_recv: Optional[torch.Tensor] = None, v_recv: Optional[torch.Tensor] = None,
+                  recv_key_norm: Optional[torch.Tensor] = None, key_norm_eps: float = 1e-6,
+                  workspace: Optional[torch.Tensor] = None, stream=None, stage_ms: Optional[list] = None):
+    """kvx_translate_fp8 (flattened maps stored as E4M3 codes wq [L_R][F_out][F_in]
+    uint8 with scales s [L_R][F_out] fp32).  Returns (k_recv, v_recv).  With a
+    list ``stage_ms`` the call is timed (synchronous) and the [preparation,
+    translation kernel] device times in ms are appended."""
+    ref = k_send if k_send is not None else v_send
+    if ref is None:
+        raise ValueError("at least one role is needed")
+    taps = np.ascontiguousarray(taps, dtype=np.int32)
+    L_R, n_taps = taps.shape
+    _need(recv_to_send, "recv_to_send", torch.int32)
+    for name, t, dt in (("k_send", k_send, ref.dtype), ("v_send", v_send, ref.dtype), ("wq_k", wq_k, torch.uint8),
+                        ("wq_v", wq_v, torch.uint8), ("s_k", s_k, torch.float32), ("s_v", s_v, torch.float32),
+                        ("b_k", b_k, torch.float32), ("b_v", b_v, torch.float32)):
+        if t is not None:
+            _need(t, name, dt)
+    H_R = recv_heads if recv_heads is not None else ref.shape[2]
+    d_R = recv_head_dim if recv_head_dim is not None else ref.shape[3]
+    N_R = recv_to_send.numel()
+    send = cache_desc(ref, send_rope_base)
+    recv = CacheDesc(int(L_R), int(N_R), int(H_R), int(d_R), _dtype_code(ref), float(recv_rope_base))
+    if recv_key_norm is not None:
+        _need(recv_key_norm, "recv_key_norm", torch.float32)
+        recv.k_norm = recv_key_norm.data_ptr()
+        recv.k_norm_eps = float(key_norm_eps)
+    if k_send is not None and k_recv is None:
+        k_recv = torch.empty((L_R, N_R, H_R, d_R), dtype=ref.dtype, device=ref.device)
+    if v_send is not None and v_recv is None:
+        v_recv = torch.empty((L_R, N_R, H_R, d_R), dtype=ref.dtype, device=ref.device)
+    ws = _workspace(translate_workspace_size(send, recv, n_taps, False), ref.device, workspace)
+    ms = (ctypes.c_float * 2)() if stage_ms is not None else None
+    st = lib().kvx_translate_fp8(ctypes.byref(send), _ptr(k_send), _ptr(v_send), ctypes.byref(recv),
+                                 _ptr(k_recv) if k_send is not None else None,
+                                 _ptr(v_recv) if v_send is not None else None, _ptr(recv_to_send),
+                                 taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_taps), _ptr(wq_k),
+                                 _ptr(wq_v), _ptr(s_k), _ptr(s_v), _ptr(b_k), _ptr(b_v), _ptr(ws), ws.numel(),
+                                 _stream(stream), ms)
+    _check(st, "kvx_translate_fp8")
+    if ms is not None:
         stage_ms.extend([float(ms[0]), float(ms[1])])
     return (k_recv if k_send is not None else None), (v_recv if v_send is not None else None)
 

@@ -328,6 +328,45 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
                           int32_t* status, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 map storage ("Cross-Model KV Cache Transfer in Production",
+ * Implementation Guidelines: weight matrices may be stored quantised, e.g.
+ * FP8, while the products keep 16-bit operands).
+ *
+ * kvx_quantize_fp8: w: device fp32 [rows][cols] (e.g. every map of one role,
+ * rows = L_R * F_out output rows of F_in weights, output-major); per row,
+ *   scale = amax / 448 (fp32, correctly rounded; 1 when that is 0),
+ *   q = the nearest OCP E4M3 code of w / scale (fp32 quotient, correctly
+ *       rounded; ties to the even code; beyond 448 saturated to +-448),
+ * so row r holds the values scale[r] * e4m3(q[r][c]).  q_out: device uint8
+ * [rows][cols]; scale_out: device fp32 [rows].  Inputs must be finite.
+ * Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+int kvx_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q_out,
+                     float* scale_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvx_translate with fp8 maps: the flattened path (per_head = 0) of
+ * kvx_translate for bf16 caches, the maps given as E4M3 codes and scales as
+ * kvx_quantize_fp8 writes them: wq_k / wq_v device uint8 [L_R][F_out][F_in]
+ * (output-major), s_k / s_v device fp32 [L_R][F_out] (needed for each role
+ * translated).  The map of output o is s[o] * e4m3(wq[o][:]): the codes are
+ * widened exactly to the operand type of the role (bf16, or fp16 for
+ * rotated-back keys), products accumulate in fp32 and the sum is scaled by
+ * s[o] before the bias.  Every other argument, the workspace size
+ * (kvx_translate_workspace_size with per_head = 0) and the error behaviour
+ * are those of kvx_translate; per-head translation and fp32 caches return
+ * KVX_ERR_UNSUPPORTED.
+ * stage_ms: NULL (asynchronous) or host float[2]: as kvx_translate_timed
+ * (synchronises `stream`).
+ * ---------------------------------------------------------------------- */
+int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                      const kvx_cache_desc* recv, void* k_recv, void* v_recv,
+                      const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                      const uint8_t* wq_k, const uint8_t* wq_v, const float* s_k, const float* s_v,
+                      const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                      void* stream, float* stage_ms);
+
+/* ------------------------------------------------------------------------
  * Moment-matched ("Recolor") fit of `count` affine maps of one shape
  * ("Prefill-Free Cross-Family KV Cache Transfer ...", Key Contributions 2 and
  * Methodology 3: both feature spaces are whitened, aligned by an orthogonal

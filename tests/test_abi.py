@@ -102,6 +102,16 @@ def test_translate_validation_before_launch():
     assert call(rd=desc(32, 0, 8, 128)) == kvx.OK                # nothing to translate
     assert call(k_recv=None, v_recv=None) == kvx.OK              # no role requested
 
+    def call8(sd=s, rd=r, sk=fake, sv=fake, ws_bytes=1 << 40):
+        return L.kvx_translate_fp8(ctypes.byref(sd), fake, fake, ctypes.byref(rd), fake, fake, fake, tp, 3, fake,
+                                   fake, sk, sv, None, None, fake, ws_bytes, None, None)
+
+    assert call8(sk=None) == kvx.ERR_INVALID                     # fp8 maps need their scales
+    assert call8(sv=None) == kvx.ERR_INVALID
+    assert call8(sd=desc(36, 100, 8, 128, kvx.F32), rd=desc(32, 120, 8, 128, kvx.F32)) == kvx.ERR_UNSUPPORTED
+    assert call8(ws_bytes=16) == kvx.ERR_WORKSPACE
+    assert call8(rd=desc(32, 0, 8, 128)) == kvx.OK
+
 
 def test_workspace_sizes_are_monotone_and_cover_the_key_rows():
     s, r = desc(36, 25000, 8, 128, rope=5e5), desc(32, 32768, 8, 128, rope=1e6)
@@ -152,6 +162,9 @@ def test_other_entry_points_validate_before_launch():
     assert L.kvx_fit_recolor_workspace_size(64, 3072, 1024) > 64 * 8 * (3072 * 3072 + 2 * 3072 * 1024)
     assert L.kvx_fit_recolor_workspace_size(0, 3072, 1024) == 0
     assert kvx.status_string(kvx.ERR_NOT_CONVERGED) == "iteration did not converge"
+    assert L.kvx_quantize_fp8(fake, 0, 16, fake, fake, None) == kvx.OK
+    assert L.kvx_quantize_fp8(fake, 4, 0, fake, fake, None) == kvx.ERR_INVALID
+    assert L.kvx_quantize_fp8(fake, 4, 16, None, fake, None) == kvx.ERR_INVALID
     assert L.kvx_fold_lowrank(fake, fake, fake, 0, 8, 8, 2, fake, kvx.BF16, None) == kvx.OK
     assert L.kvx_fold_lowrank(fake, None, fake, 1, 8, 8, 2, fake, kvx.BF16, None) == kvx.ERR_INVALID
     assert L.kvx_fold_lowrank(fake, fake, fake, 1, 8, 8, 2, fake, 5, None) == kvx.ERR_INVALID

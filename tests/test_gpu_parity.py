@@ -270,9 +270,10 @@ def flat_maps(k):
     return _MAPS[k]
 
 
-def flat_case(k, n_recv=None, seed=None):
+def flat_case(k, n_recv=None, seed=None, with_maps=True):
     """Inputs of the flattened settings on the device: token ends and caches
-    seeded by ``seed``, maps of setting ``k``."""
+    seeded by ``seed``, maps of setting ``k`` (bf16, unless with_maps is
+    false)."""
     cfg = dict(synth.CONFIGS[k])
     seed = cfg["seed"] if seed is None else seed
     nr = cfg["recv_tokens"] if n_recv is None else n_recv
@@ -280,12 +281,13 @@ def flat_case(k, n_recv=None, seed=None):
     shp = synth.CacheShape(36, len(send_end), 8, 128)
     c = dict(send_end=send_end, recv_end=recv_end, shp=shp, n_recv=nr)
     rope = "send_rope" in cfg
-    maps = flat_maps(k)
+    maps = flat_maps(k) if with_maps else None
     for r, role in enumerate(("k", "v")):
         c[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, DEV, outlier_frac=cfg.get("outlier_frac", 0.0),
                                                outlier_scale=cfg.get("outlier_scale", 1.0),
                                                outlier_pairs=(role == "k" and rope))
-        c[f"wt_{role}"], c[f"b_{role}"], c[f"wt_o_{role}"], c[f"b_o_{role}"] = maps[role]
+        if maps:
+            c[f"wt_{role}"], c[f"b_{role}"], c[f"wt_o_{role}"], c[f"b_o_{role}"] = maps[role]
     c["send_rope"] = cfg.get("send_rope", 0.0)
     c["recv_rope"] = cfg.get("recv_rope", 0.0)
     return c
@@ -885,3 +887,128 @@ def test_recolor_full_size_vs_oracle():
     ew, eb = _recolor_err(w, b, wo, bo)
     say(f"  W max|err|/RMS = {ew:.3e}, b {eb:.3e}")
     assert ew <= TOL_BF16 and eb <= TOL_BF16
+
+
+# ---------------------------------------------------------------- fp8 map storage
+
+
+class Fp8Maps:
+    """Oracle-quantised maps (codes and scales); indexing a layer gives its
+    float64 values."""
+
+    def __init__(self, q, sc):
+        self.q, self.sc = q, sc
+
+    def __len__(self):
+        return len(self.q)
+
+    def __getitem__(self, l):
+        return O.fp8_dequant(self.q[l], self.sc[l])
+
+
+_MAPS8 = {}
+
+
+def fp8_maps(k):
+    """Maps of a flattened setting folded in fp32 and stored as fp8 by the
+    library (device) and by the oracle (host): codes and scales must agree
+    bit for bit."""
+    if k not in _MAPS8:
+        seed = synth.CONFIGS[k]["seed"]
+        out = {}
+        for r, role in enumerate(("k", "v")):
+            say(f"  folding + quantising maps of setting {k} role {role}")
+            wt, u, v, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, DEV, 16)
+            g = kvx.fold_lowrank(wt, u, v, torch.float32)
+            q, sc = kvx.quantize_fp8(g)
+            wh, uh, vh = host(wt).numpy(), host(u).numpy(), host(v).numpy()
+            qo, so = [], []
+            for l in range(32):
+                a, s_ = O.quantize_fp8(O.fold_lowrank(wh[l], uh[l], vh[l])[0])
+                qo.append(a)
+                so.append(s_)
+            qo, so = np.stack(qo), np.stack(so)
+            assert np.array_equal(host(q).numpy(), qo), "fp8 codes differ from the oracle's"
+            assert np.array_equal(host(sc).numpy().view(np.uint32), so.view(np.uint32)), "fp8 scales differ"
+            out[role] = (q, sc, b, Fp8Maps(qo, so), host(b).numpy().astype(np.float64))
+            del wt, u, v, g
+        _MAPS8[k] = out
+    return _MAPS8[k]
+
+
+def check_flat8(c, rows=None):
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
+    tmap_o = O.token_align(c["send_end"], c["recv_end"])
+    m8 = fp8_maps(4)
+    k, v = kvx.translate_fp8(c["k_send"], c["v_send"], tmap, taps, m8["k"][0], m8["v"][0], m8["k"][1], m8["v"][1],
+                             m8["k"][2], m8["v"][2], send_rope_base=c["send_rope"], recv_rope_base=c["recv_rope"])
+    torch.cuda.synchronize()
+    n = tmap_o.size
+    rows = np.arange(n) if rows is None else rows
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(c[f"{role}_send"], tmap_o, taps, m8[role][3], m8[role][4], rows, per_head=False,
+                                recv_heads=8, recv_head_dim=128, send_rope_base=c["send_rope"] if rk else 0.0,
+                                recv_rope_base=c["recv_rope"] if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  fp8 maps n={n} {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+
+
+def test_fp8_quantize_special_rows():
+    """Zero rows, an outlier, tiny magnitudes (subnormal codes), negative
+    zeros and exact ties: codes and scales bit for bit as the oracle's."""
+    say("fp8 quantisation of special rows")
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((9, 3072)).astype(np.float32)
+    w[1] = 0.0
+    w[2, 100] = 1e5
+    w[3] *= np.float32(3e-3)
+    w[4] = -0.0
+    w[4, 7] = 1.0
+    w[5] = np.float32(448.0) * (np.arange(3072) % 253 - 126).astype(np.float32) / np.float32(126.0)
+    w[6, :10] = [448.0, 464.0, 15.5, -15.5, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9, 17.0, 1.0, -0.0]
+    q, sc = kvx.quantize_fp8(torch.as_tensor(w, device=DEV))
+    qo, so = O.quantize_fp8(w)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+def test_fp8_every_code_widens_exactly():
+    """Every finite E4M3 code reaches the products exactly, as bf16 operands
+    (values: one-hot sender rows select one code per output) and as fp16
+    operands (keys rotated back at position 0, an identity rotation)."""
+    say("fp8 maps: every code, bf16 and fp16 operands")
+    val = O.e4m3_values()
+    fin = np.isfinite(val)
+    n = 1024
+    x = torch.zeros((1, n, 8, 128), dtype=torch.bfloat16, device=DEV)
+    x.view(n, 1024)[torch.arange(n), torch.arange(n)] = 1.0
+    q = ((np.arange(256)[:, None] + np.arange(1024)[None, :]) % 256).astype(np.uint8)
+    q[~fin[q]] = 0
+    sc = torch.ones((1, 256), dtype=torch.float32, device=DEV)
+    taps = np.zeros((1, 1), np.int32)
+    _, v = kvx.translate_fp8(None, x, dev_i32(np.arange(n)), taps, None, torch.as_tensor(q[None], device=DEV), None,
+                             sc, recv_heads=2, recv_head_dim=128)
+    assert np.array_equal(O.as_f64(v).reshape(n, 256), val[q.T])
+    kx = torch.randn((1, 4, 8, 128), device=DEV).to(torch.bfloat16)
+    kx[0, 0] = 0
+    kx[0, 0, 0, 5] = 1.0
+    q2 = np.zeros((1, 256, 1024), np.uint8)
+    q2[0, :, 5] = np.where(fin, np.arange(256), 0)
+    k, _ = kvx.translate_fp8(kx, None, dev_i32(np.zeros(64)), taps, torch.as_tensor(q2, device=DEV), None, sc, None,
+                             recv_heads=2, recv_head_dim=128, send_rope_base=1e4)
+    got = O.as_f64(k).reshape(64, 256)
+    assert np.array_equal(got, np.broadcast_to(val[q2[0, :, 5]], (64, 256)))
+
+
+def test_fp8_maps_rope_small_all_elements():
+    say("fp8 maps, flattened + RoPE, 700 receiver tokens")
+    check_flat8(flat_case(4, 700, seed=15, with_maps=False))
+
+
+def test_fp8_maps_rope_full_sampled_rows():
+    say("fp8 maps, flattened + RoPE, 32768 receiver tokens, sampled rows")
+    c = flat_case(4, with_maps=False)
+    check_flat8(c, sample_rows(O.token_align(c["send_end"], c["recv_end"]), 256, 4))
