@@ -157,10 +157,47 @@ __device__ __forceinline__ void ft_issue_b(const TileAddr& ta, int k, uint16_t* 
   for (int i = 0; i < n_ld; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * n_ld + i) * 512);
 }
 
+// The loads one K step issues (W of step k+1 into nb, A of step k+2 into
+// na), spread over its sub-steps so the MFMAs of a wave do not wait behind
+// a burst of load issues after each barrier.  W loads come first, then A
+// loads: the next step's wait leaves exactly the A loads in flight.
+struct StepLoads {
+  __amdgpu_buffer_rsrc_t ar, br;
+  uint32_t asoff, bsoff;
+  uint16_t* na;
+  uint16_t* nb;
+};
+
+template <bool W8>
+__device__ __forceinline__ StepLoads ft_step_loads(const TileAddr& ta, int k, uint16_t* nb, uint16_t* na) {
+  StepLoads sl;
+  const int kb = k + 1, ka = k + 2;
+  sl.br = buf_rsrc(ta.w_base, kb < ta.nk ? ta.w_bytes : 0u);
+  sl.bsoff = (W8 ? 1u : 2u) * static_cast<uint32_t>(kb * FT_BK);
+  sl.ar = buf_rsrc(ta.a_src + static_cast<int64_t>(ft_layer(ta, ka)) * ta.a_ls,
+                   ka < ta.nk ? static_cast<uint32_t>(ta.a_ls) : 0u);
+  sl.asoff = 2u * static_cast<uint32_t>((ka % ta.spt) * FT_BK);
+  sl.na = na;
+  sl.nb = nb;
+  return sl;
+}
+
+// Load i of this wave's share of a step (W loads, then A loads).
+template <bool W8>
+__device__ __forceinline__ void ft_load(const TileAddr& ta, const StepLoads& sl, int i) {
+  constexpr int nbl = W8 ? FT_B8_LD : FT_B_LD;
+  const int wave = wave_id();
+  if (i < nbl)
+    dma16(sl.br, ta.b_off[i], sl.bsoff, sl.nb + (wave * nbl + i) * 512);
+  else
+    dma16(sl.ar, ta.a_off[i - nbl], sl.asoff, sl.na + (wave * FT_A_LD + i - nbl) * 512);
+}
+
 // One K step from an A part and a W part: 4 x (2 A + 4 B fragment reads,
 // 8 MFMAs).
-template <bool F16>
-__device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4]) {
+template <bool F16, bool ISSUE = true>
+__device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4],
+                                           const TileAddr& ta, const StepLoads& sl) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;
@@ -169,6 +206,14 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
   const int fr = lane & 31;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
+    // two of the step's eight loads per sub-step (kept in place: the
+    // scheduler would otherwise sink them to the end of the step)
+    if constexpr (ISSUE) {
+      __builtin_amdgcn_sched_barrier(0);
+      ft_load<false>(ta, sl, 2 * kk);
+      ft_load<false>(ta, sl, 2 * kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int pc = ft_chunk(fr, 2 * kk + (lane >> 5)) << 4;
     u32x4 af[2], bfr[4];
 #pragma unroll
@@ -206,8 +251,9 @@ __device__ __forceinline__ u32x4 ft_fp8x8(uint32_t lo, uint32_t hi) {
 // W bytes a lane needs for sub-steps 2p and 2p+1 are one 16-byte chunk
 // (logical 2h + p of its 64-byte row) and one fragment read serves two
 // sub-steps.
-template <bool F16>
-__device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4]) {
+template <bool F16, bool ISSUE = true>
+__device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4],
+                                            const TileAddr& ta, const StepLoads& sl) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;
@@ -223,6 +269,22 @@ __device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int kk = 2 * kp + sub;
+      // the step's six loads (two W, four A), spread over the sub-steps
+      if constexpr (ISSUE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk == 0) {
+          ft_load<true>(ta, sl, 0);
+          ft_load<true>(ta, sl, 1);
+        } else if (kk == 1) {
+          ft_load<true>(ta, sl, 2);
+        } else if (kk == 2) {
+          ft_load<true>(ta, sl, 3);
+          ft_load<true>(ta, sl, 4);
+        } else {
+          ft_load<true>(ta, sl, 5);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int pc = ft_chunk(fr, 4 * h + kk) << 4;
       u32x4 af[2];
 #pragma unroll
@@ -253,34 +315,58 @@ __device__ __forceinline__ void ft_sync() {
 // One step of the ring: A of step k is in part 2k mod 5, W in part
 // 2k+1 mod 5; the step issues W of k+1 and A of k+2 into the two parts of
 // step k-1.
-#define FT_STEP(K, PA, PB, NB, NA, LIVE)        \
-  ft_sync();                                    \
-  ft_issue_b<W8>(ta, (K) + 1, NB);              \
-  ft_issue_a(ta, (K) + 2, NA);                  \
-  if (LIVE) {                                   \
-    if constexpr (W8)                           \
-      ft_compute8<F16>(PA, PB, acc);            \
-    else                                        \
-      ft_compute<F16>(PA, PB, acc);             \
+// A whole step: loads spread over the sub-steps.
+#define FT_STEP(K, PA, PB, NB, NA)                                    \
+  {                                                                   \
+    ft_sync();                                                        \
+    const StepLoads sl = ft_step_loads<W8>(ta, (K), NB, NA);          \
+    if constexpr (W8)                                                 \
+      ft_compute8<F16>(PA, PB, acc, ta, sl);                          \
+    else                                                              \
+      ft_compute<F16>(PA, PB, acc, ta, sl);                           \
+  }
+// A tail step: every load first, the products only while k < nk.
+#define FT_TAIL(K, PA, PB, NB, NA)                                    \
+  {                                                                   \
+    ft_sync();                                                        \
+    const StepLoads sl = ft_step_loads<W8>(ta, (K), NB, NA);          \
+    for (int i_ = 0; i_ < (W8 ? FT_B8_LD : FT_B_LD) + FT_A_LD; ++i_)   \
+      ft_load<W8>(ta, sl, i_);                                        \
+    if ((K) < nk) {                                                   \
+      if constexpr (W8)                                               \
+        ft_compute8<F16, false>(PA, PB, acc, ta, sl);                 \
+      else                                                            \
+        ft_compute<F16, false>(PA, PB, acc, ta, sl);                  \
+    }                                                                 \
   }
 
 // K loop over nk >= 1 steps with A0, W0 and A1 already issued into parts 0,
-// 1 and 2.  The part pattern repeats every five steps.  Issues are
-// unconditional (steps past the end read an empty buffer range and are not
-// multiplied); the loads still in flight at the end are drained before the
+// 1 and 2.  The part pattern repeats every five steps: whole groups of five
+// run without branches, the remaining 1..4 steps (and the loads past the
+// end, which read an empty buffer range so every wait keeps its count) run
+// as a tail.  The loads still in flight at the end are drained before the
 // parts are reused.
 template <bool F16, bool W8>
 __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
                                          uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
-  for (int k = 0; k < nk; k += 5) {
-    FT_STEP(k, p0, p1, p3, p4, true)
-    FT_STEP(k + 1, p2, p3, p0, p1, k + 1 < nk)
-    FT_STEP(k + 2, p4, p0, p2, p3, k + 2 < nk)
-    FT_STEP(k + 3, p1, p2, p4, p0, k + 3 < nk)
-    FT_STEP(k + 4, p3, p4, p1, p2, k + 4 < nk)
+  int k = 0;
+  for (; k + 5 <= nk; k += 5) {
+    FT_STEP(k, p0, p1, p3, p4)
+    FT_STEP(k + 1, p2, p3, p0, p1)
+    FT_STEP(k + 2, p4, p0, p2, p3)
+    FT_STEP(k + 3, p1, p2, p4, p0)
+    FT_STEP(k + 4, p3, p4, p1, p2)
+  }
+  if (k < nk) {
+    FT_TAIL(k, p0, p1, p3, p4)
+    FT_TAIL(k + 1, p2, p3, p0, p1)
+    FT_TAIL(k + 2, p4, p0, p2, p3)
+    FT_TAIL(k + 3, p1, p2, p4, p0)
+    FT_TAIL(k + 4, p3, p4, p1, p2)
   }
   KVX_WAIT_VM(0);
 }
+#undef FT_TAIL
 #undef FT_STEP
 
 // Both operand types in one launch: the K loop is chosen per tile.  PLACED:
