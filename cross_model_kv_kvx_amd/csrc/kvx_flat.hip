@@ -168,15 +168,34 @@ struct StepLoads {
   uint16_t* nb;
 };
 
+// Position of the A part a step issues (step k + 2) inside the taps: the
+// 64-element piece of the tap's row (a_in < spt) and the tap (a_tap <
+// n_taps), carried from step to step instead of divided out each time.
+struct ATap {
+  int32_t a_in, a_tap;
+};
+
+__device__ __forceinline__ ATap ft_atap_start(const TileAddr& ta) {
+  return ATap{2 % ta.spt, (2 / ta.spt) % ta.n_taps};
+}
+
+__device__ __forceinline__ void ft_atap_next(const TileAddr& ta, ATap& t) {
+  if (++t.a_in == ta.spt) {
+    t.a_in = 0;
+    if (++t.a_tap == ta.n_taps) t.a_tap = 0;
+  }
+}
+
 template <bool W8>
-__device__ __forceinline__ StepLoads ft_step_loads(const TileAddr& ta, int k, uint16_t* nb, uint16_t* na) {
+__device__ __forceinline__ StepLoads ft_step_loads(const TileAddr& ta, int k, const ATap& t, uint16_t* nb,
+                                                   uint16_t* na) {
   StepLoads sl;
   const int kb = k + 1, ka = k + 2;
   sl.br = buf_rsrc(ta.w_base, kb < ta.nk ? ta.w_bytes : 0u);
   sl.bsoff = (W8 ? 1u : 2u) * static_cast<uint32_t>(kb * FT_BK);
-  sl.ar = buf_rsrc(ta.a_src + static_cast<int64_t>(ft_layer(ta, ka)) * ta.a_ls,
-                   ka < ta.nk ? static_cast<uint32_t>(ta.a_ls) : 0u);
-  sl.asoff = 2u * static_cast<uint32_t>((ka % ta.spt) * FT_BK);
+  const uint32_t layer = ((t.a_tap < 4 ? ta.taps0 : ta.taps1) >> (8 * (t.a_tap & 3))) & 0xffu;
+  sl.ar = buf_rsrc(ta.a_src + static_cast<int64_t>(layer) * ta.a_ls, ka < ta.nk ? static_cast<uint32_t>(ta.a_ls) : 0u);
+  sl.asoff = 2u * static_cast<uint32_t>(t.a_in * FT_BK);
   sl.na = na;
   sl.nb = nb;
   return sl;
@@ -319,7 +338,8 @@ __device__ __forceinline__ void ft_sync() {
 #define FT_STEP(K, PA, PB, NB, NA)                                    \
   {                                                                   \
     ft_sync();                                                        \
-    const StepLoads sl = ft_step_loads<W8>(ta, (K), NB, NA);          \
+    const StepLoads sl = ft_step_loads<W8>(ta, (K), at, NB, NA);      \
+    ft_atap_next(ta, at);                                             \
     if constexpr (W8)                                                 \
       ft_compute8<F16>(PA, PB, acc, ta, sl);                          \
     else                                                              \
@@ -329,7 +349,8 @@ __device__ __forceinline__ void ft_sync() {
 #define FT_TAIL(K, PA, PB, NB, NA)                                    \
   {                                                                   \
     ft_sync();                                                        \
-    const StepLoads sl = ft_step_loads<W8>(ta, (K), NB, NA);          \
+    const StepLoads sl = ft_step_loads<W8>(ta, (K), at, NB, NA);      \
+    ft_atap_next(ta, at);                                             \
     for (int i_ = 0; i_ < (W8 ? FT_B8_LD : FT_B_LD) + FT_A_LD; ++i_)   \
       ft_load<W8>(ta, sl, i_);                                        \
     if ((K) < nk) {                                                   \
@@ -350,6 +371,7 @@ template <bool F16, bool W8>
 __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
                                          uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
   int k = 0;
+  ATap at = ft_atap_start(ta);
   for (; k + 5 <= nk; k += 5) {
     FT_STEP(k, p0, p1, p3, p4)
     FT_STEP(k + 1, p2, p3, p0, p1)
@@ -444,6 +466,9 @@ flat_gemm_kernel(const FlatKArgs args) {
       }
     }
 
+    // run starts of this wave's two epilogue phases, read now so they have
+    // arrived when the K loop ends
+
     f32x16 acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -496,6 +521,8 @@ flat_gemm_kernel(const FlatKArgs args) {
     KVX_COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
     KVX_COMPILER_FENCE();
+    // run index of the first 64 receiver rows of each phase, requested
+    // before the staging so the stores need not wait for them
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
       const int32_t u0 = m0 + wm * 64 + 32 * ph;
