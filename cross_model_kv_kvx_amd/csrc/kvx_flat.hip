@@ -633,10 +633,15 @@ flat_gemm_kernel(const FlatKArgs args) {
             if (PLACED && args.slot) orow = args.slot[p0 + off];
             if (orow >= 0 && orow < args.pool_rows) {
               uint16_t* o = outp + orow * args.f_out;
-              *reinterpret_cast<u32x4*>(o) = u32x4{cvt_bf16x2(a[0], a[1]), cvt_bf16x2(a[2], a[3]),
-                                                   cvt_bf16x2(a[4], a[5]), cvt_bf16x2(a[6], a[7])};
-              *reinterpret_cast<u32x4*>(o + 64) = u32x4{cvt_bf16x2(b[0], b[1]), cvt_bf16x2(b[2], b[3]),
-                                                        cvt_bf16x2(b[4], b[5]), cvt_bf16x2(b[6], b[7])};
+              // streaming stores: the translated rows are not read again here,
+              // so they should not evict the maps and sender rows that the
+              // other tiles still read through L2 and the last-level cache
+              __builtin_nontemporal_store(u32x4{cvt_bf16x2(a[0], a[1]), cvt_bf16x2(a[2], a[3]),
+                                                cvt_bf16x2(a[4], a[5]), cvt_bf16x2(a[6], a[7])},
+                                          reinterpret_cast<u32x4*>(o));
+              __builtin_nontemporal_store(u32x4{cvt_bf16x2(b[0], b[1]), cvt_bf16x2(b[2], b[3]),
+                                                cvt_bf16x2(b[4], b[5]), cvt_bf16x2(b[6], b[7])},
+                                          reinterpret_cast<u32x4*>(o + 64));
             }
           }
           if (rot && !rpos) {
