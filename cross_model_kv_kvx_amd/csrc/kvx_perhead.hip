@@ -198,7 +198,8 @@ __device__ __forceinline__ void ph_store(const uint16_t* ys, uint16_t* outb, int
     const u32x4 v = *reinterpret_cast<const u32x4*>(yb + row * 256 + 16 * ph_chunk(row, c));
     if (row < rows) {
       const int64_t orow = slot ? slot[tok0 + row] : static_cast<int64_t>(tok0 + row);
-      if (orow >= 0 && orow < pool_rows) *reinterpret_cast<u32x4*>(outb + orow * row_elems + 8 * c) = v;
+      // streaming store: translated rows are not read again by this kernel
+      if (orow >= 0 && orow < pool_rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outb + orow * row_elems + 8 * c));
     }
   }
 }
