@@ -5,30 +5,47 @@
 // applies the receiver's own rotation at the receiver position; values are
 // never rotated.  The rotation acts on half-split pairs (c, c + d/2) with
 // angle pos * base^(-2j/d) for pair j.  Angles reach tens of thousands of
-// radians at long context, so they are formed and reduced in fp64 here, once
-// per (position, pair), and kept as an fp32 (cos, sin) table.
+// radians at long context, so they are formed in fp64 here (a sincos per run
+// of positions, fp64 angle-addition steps inside the run) and kept as an
+// fp32 (cos, sin) table.
 
 #include "kvx_internal.hpp"
 
 namespace kvx {
 
-__global__ void rope_table_kernel(float2* __restrict__ tab, int32_t n_pos, int32_t half,
-                                  int32_t head_dim, double base) {
-  const int64_t total = static_cast<int64_t>(n_pos) * half;
+// One thread: frequency j (consecutive lanes take consecutive j, so the
+// stores of a position are one contiguous row) for RT_RUN consecutive
+// positions p0 .. p0 + RT_RUN - 1.  theta_j = base^(-2j/head_dim) in fp64;
+// (cos, sin)(p0 theta) from fp64 sincos, then each next position by the fp64
+// angle-addition step (cos, sin)((p+1) theta) = (c cos(theta) - s sin(theta),
+// s cos(theta) + c sin(theta)); over RT_RUN steps the fp64 recurrence drifts
+// by ~1e-14, far below the fp32 rounding of the stored table.
+constexpr int RT_RUN = 32;
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int32_t n_pos, int32_t half,
+                                                         int32_t head_dim, double base) {
+  const int64_t runs = (static_cast<int64_t>(n_pos) + RT_RUN - 1) / RT_RUN;
+  const int64_t total = runs * half;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int32_t p = static_cast<int32_t>(i / half);
     const int32_t j = static_cast<int32_t>(i % half);
+    const int32_t p0 = static_cast<int32_t>(i / half) * RT_RUN;
     const double theta = pow(base, -2.0 * static_cast<double>(j) / static_cast<double>(head_dim));
-    double sn, cs;
-    sincos(static_cast<double>(p) * theta, &sn, &cs);
-    tab[i] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+    double s, c, st, ct;
+    sincos(static_cast<double>(p0) * theta, &s, &c);
+    sincos(theta, &st, &ct);
+    const int32_t n = min(RT_RUN, n_pos - p0);
+    for (int32_t r = 0; r < n; ++r) {
+      tab[static_cast<int64_t>(p0 + r) * half + j] = make_float2(static_cast<float>(c), static_cast<float>(s));
+      const double cn = c * ct - s * st;
+      s = s * ct + c * st;
+      c = cn;
+    }
   }
 }
 
 int launch_rope_table(float2* tab, int32_t n_pos, int32_t head_dim, double base, hipStream_t s) {
   const int32_t half = head_dim / 2;
-  const int64_t total = static_cast<int64_t>(n_pos) * half;
+  const int64_t total = (static_cast<int64_t>(n_pos) + RT_RUN - 1) / RT_RUN * half;
   if (total <= 0) return KVX_OK;
   int64_t blocks = ceil_div(total, 256);
   if (blocks > 8192) blocks = 8192;
