@@ -996,12 +996,15 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
 // in the relative regulariser rho * trace / F added to each diagonal).  The
 // inverse square root of S = M^T M comes from the coupled Newton-Schulz
 // iteration Y <- Y T, Z <- T Z, T = (3 I - Z Y) / 2, started at Y = S / c,
-// Z = I with c = ||S||_F (so every eigenvalue of S / c is in (0, 1]):
+// Z = I with c = min(1.1 lam, ||S||_F), lam a power-iteration estimate of the
+// largest eigenvalue (the iteration converges for eigenvalues of S / c in
+// (0, 3), and the nearer the smallest is to 1 the fewer steps it takes):
 // Z -> (S / c)^-1/2.  All products are fp64 on matrix cores, every problem of
 // the call at once; the host reads max |T - I| per problem after each step.
 
 constexpr int NS_BLOCKS = 64;        // workgroups per problem of the middle step
 constexpr int RC_MAX_ITERS = 100;
+constexpr int RC_POWER = 12;         // power steps for the largest eigenvalue of M^T M
 constexpr double RC_TOL = 1e-10;     // max |T - I| taken as converged
 constexpr double RC_FLOOR = 1e-6;    // below this, a step that gains < 4x is the rounding floor
 // ||(S / c)^-1/2||_F above this: M is numerically rank-deficient (fewer
@@ -1051,6 +1054,45 @@ __global__ __launch_bounds__(256) void scale_kernel(double* __restrict__ p, int6
   const double f = pow(scal[blockIdx.y * bs], power);
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256)
     q[e] *= f;
+}
+
+// Start vector of the power iteration (deterministic, no special direction):
+// v_i = 0.5 + frac(0.6180339887 (i + 1)).
+__global__ __launch_bounds__(256) void power_start_kernel(double* __restrict__ v, int32_t n, int64_t bs) {
+  double* q = v + blockIdx.x * bs;
+  for (int32_t i = threadIdx.x; i < n; i += 256) {
+    const double t = 0.6180339887498949 * static_cast<double>(i + 1);
+    q[i] = 0.5 + (t - floor(t));
+  }
+}
+
+// One workgroup per problem: lam = ||y|| (fixed summation order), v = y / lam.
+__global__ __launch_bounds__(256) void power_norm_kernel(const double* __restrict__ y, double* __restrict__ v,
+                                                         int32_t n, int64_t bs, double* __restrict__ lam) {
+  y += blockIdx.x * bs;
+  v += blockIdx.x * bs;
+  __shared__ double red[256];
+  double a = 0.0;
+  for (int32_t i = threadIdx.x; i < n; i += 256) a += y[i] * y[i];
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double nrm = sqrt(red[0]);
+  const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
+  for (int32_t i = threadIdx.x; i < n; i += 256) v[i] = y[i] * inv;
+  if (threadIdx.x == 0) lam[blockIdx.x * bs] = nrm;
+}
+
+// Scale of the polar iteration: c = min(1.1 lam, ||S||_F) with lam the power
+// iteration's estimate of the largest eigenvalue (never above it for a unit
+// vector, close to it after the steps run); ||S||_F bounds it from above.
+__global__ void polar_scale_kernel(double* __restrict__ scal, int64_t bs) {
+  double* q = scal + blockIdx.x * bs;
+  const double c = 1.1 * q[2];
+  if (threadIdx.x == 0) q[0] = (c > 0.0 && c < q[0]) ? c : q[0];
 }
 
 __device__ __forceinline__ double nan_max(double a, double b) { return (b > a || b != b) ? b : a; }
@@ -1188,6 +1230,17 @@ int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void*
   double *Y = w.ns[0], *Z = w.ns[1], *T = w.ns[2], *N = w.ns[3];
   if (int st = dgemm(s, count, f_out, f_out, f_in, w.M, 1, f_out, w.M, f_out, 1, Y, f_out, bs, 0, 1)) return st;
   frob_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(Y, f_out, bs, w.scal);
+  // largest eigenvalue of S by RC_POWER power steps (v in T, S v in N), so
+  // the iteration starts with the spectrum of S / c close to (0, 1]: each
+  // factor 2.25 of underscaling of the smallest eigenvalue costs one step
+  power_start_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(T, f_out, bs);
+  KVX_LAUNCH_CHECK();
+  for (int it_p = 0; it_p < RC_POWER; ++it_p) {
+    if (int st = dgemm(s, count, f_out, 1, f_out, Y, f_out, 1, T, 1, 1, N, 1, bs, 0, 1)) return st;
+    power_norm_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(N, T, f_out, bs, w.scal + 2);
+    KVX_LAUNCH_CHECK();
+  }
+  polar_scale_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(w.scal, bs);
   scale_kernel<<<grid_o2, 256, 0, s>>>(Y, fo2, bs, w.scal, -1.0);
   identity_kernel<<<grid_o2, 256, 0, s>>>(Z, f_out, bs);
   KVX_LAUNCH_CHECK();

@@ -394,8 +394,9 @@ int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void
  *   KVX_ERR_NOT_SPD (a regularised covariance is not positive definite) or
  *   KVX_ERR_NOT_CONVERGED (M numerically rank-deficient, so Q is not
  *   determined: the iteration did not converge, or ||(M^T M / c)^-1/2||_F >
- *   1e6 for c = ||M^T M||_F; this happens when the calibration rows hold
- *   fewer distinct sender rows than f_out).
+ *   1e6 for the iteration's scale c (about 1.1 times the largest eigenvalue
+ *   of M^T M); this happens when the calibration rows hold fewer distinct
+ *   sender rows than f_out).
  * iters: host int32 or NULL; receives the number of polar iterations run.
  * workspace: device scratch of kvx_fit_recolor_workspace_size(count, f_in,
  *   f_out) bytes (the Gram partials, shared, plus about
