@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 // load, or 1 fp32 column) into partial[r][col]; then each column's
 // CS_CHUNKS partials are added in chunk order.  bf16 callers guarantee
 // cols % 8 == 0, ld % 8 == 0 and a 16-byte aligned base.
-constexpr int CS_CHUNKS = 128;
+constexpr int CS_CHUNKS = 512;
 template <bool F32>
 __global__ __launch_bounds__(256) void colsum_part_kernel(const void* __restrict__ m, int64_t ld, int64_t n_rows,
                                                           int32_t cols, int64_t rows_per_chunk,
@@ -621,24 +621,67 @@ dgemm_kernel(const DgArgs g) {
       }
 }
 
-// w_out[o][f] = W[f][o] (fp32); b_out[o] = mean_y[o] - sum_f mean_x[f] W[f][o].
-__global__ __launch_bounds__(256) void fit_output_kernel(const double* __restrict__ W, int32_t f_in, int32_t f_out,
-                                                         float* __restrict__ w_out, float* __restrict__ b_out,
-                                                         const double* __restrict__ sx, const double* __restrict__ sy,
-                                                         double inv_n) {
-  const int64_t total = static_cast<int64_t>(f_in) * f_out;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int32_t o = static_cast<int32_t>(e / f_in), f = static_cast<int32_t>(e % f_in);
-    w_out[e] = static_cast<float>(W[static_cast<int64_t>(f) * f_out + o]);
+// w_out[o][f] = W[f][o] in fp32, by 64 x 64 tiles through LDS so that both
+// the fp64 reads (rows of W) and the fp32 writes (rows of w_out) are
+// contiguous.
+__global__ __launch_bounds__(256) void fit_transpose_kernel(const double* __restrict__ W, int32_t f_in,
+                                                            int32_t f_out, float* __restrict__ w_out) {
+  __shared__ float tile[64][65];
+  const int32_t f0 = blockIdx.y * 64, o0 = blockIdx.x * 64;
+  const int c = threadIdx.x & 63, r4 = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int r = r4; r < 64; r += 4) {
+    const int32_t f = f0 + r, o = o0 + c;
+    if (f < f_in && o < f_out) tile[r][c] = static_cast<float>(W[static_cast<int64_t>(f) * f_out + o]);
   }
+  __syncthreads();
+#pragma unroll 4
+  for (int r = r4; r < 64; r += 4) {
+    const int32_t o = o0 + r, f = f0 + c;
+    if (f < f_in && o < f_out) w_out[static_cast<int64_t>(o) * f_in + f] = tile[c][r];
+  }
+}
+
+// The bias b[o] = mean_y[o] - sum_f mean_x[f] W[f][o] in two passes with a
+// fixed order: workgroup (g, q) adds rows q*rows_per .. of its 256 columns
+// into partial[q][o]; then the BI_CHUNKS partials are added in chunk order.
+constexpr int BI_CHUNKS = 64;
+__global__ __launch_bounds__(256) void fit_bias_part_kernel(const double* __restrict__ W, int32_t f_in, int32_t f_out,
+                                                            const double* __restrict__ sx, double inv_n,
+                                                            int32_t rows_per, double* __restrict__ partial) {
+  const int32_t o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= f_out) return;
+  const int32_t f1 = min(f_in, static_cast<int32_t>((blockIdx.y + 1) * rows_per));
+  double a = 0.0;
+  for (int32_t f = blockIdx.y * rows_per; f < f1; ++f) a += sx[f] * inv_n * W[static_cast<int64_t>(f) * f_out + o];
+  partial[static_cast<int64_t>(blockIdx.y) * f_out + o] = a;
+}
+
+__global__ __launch_bounds__(256) void fit_bias_final_kernel(const double* __restrict__ partial, int32_t f_out,
+                                                             const double* __restrict__ sy, double inv_n,
+                                                             float* __restrict__ b_out) {
+  const int32_t o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= f_out) return;
+  double a = 0.0;
+  for (int q = 0; q < BI_CHUNKS; ++q) a += partial[static_cast<int64_t>(q) * f_out + o];
+  b_out[o] = static_cast<float>(sy[o] * inv_n - a);
+}
+
+// Outputs of one fitted problem: w_out (output-major fp32) and, when b_out
+// is not null, the bias.  partial: BI_CHUNKS * f_out doubles of scratch.
+static int fit_output(hipStream_t s, const double* W, int32_t f_in, int32_t f_out, float* w_out, float* b_out,
+                      const double* sx, const double* sy, double inv_n, double* partial) {
+  fit_transpose_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 64)), static_cast<unsigned>(ceil_div(f_in, 64))),
+                         256, 0, s>>>(W, f_in, f_out, w_out);
+  KVX_LAUNCH_CHECK();
   if (b_out) {
-    for (int32_t o = blockIdx.x * blockDim.x + threadIdx.x; o < f_out; o += gridDim.x * blockDim.x) {
-      double s = sy[o] * inv_n;
-      for (int32_t f = 0; f < f_in; ++f) s -= sx[f] * inv_n * W[static_cast<int64_t>(f) * f_out + o];
-      b_out[o] = static_cast<float>(s);
-    }
+    const int32_t rows_per = static_cast<int32_t>(ceil_div(f_in, BI_CHUNKS));
+    fit_bias_part_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 256)), BI_CHUNKS), 256, 0, s>>>(
+        W, f_in, f_out, sx, inv_n, rows_per, partial);
+    fit_bias_final_kernel<<<static_cast<unsigned>(ceil_div(f_out, 256)), 256, 0, s>>>(partial, f_out, sy, inv_n, b_out);
+    KVX_LAUNCH_CHECK();
   }
+  return KVX_OK;
 }
 
 // Inverse of each 256-wide diagonal block of the factor (for the block
@@ -963,10 +1006,9 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
 
   // 3. outputs
   for (int32_t z = 0; z < count; ++z) {
-    fit_output_kernel<<<grid_for(static_cast<int64_t>(f_in) * f_out), 256, 0, s>>>(
-        w.C + z * bs, f_in, f_out, w_out[z], fit_intercept ? b_out[z] : nullptr, w.sx + z * bs, w.sy + z * bs,
-        inv_n);
-    KVX_LAUNCH_CHECK();
+    if (int st = fit_output(s, w.C + z * bs, f_in, f_out, w_out[z], fit_intercept ? b_out[z] : nullptr,
+                            w.sx + z * bs, w.sy + z * bs, inv_n, w.csp))
+      return st;
   }
 
   std::vector<int32_t> host_flags(static_cast<size_t>(count), 0);
@@ -1291,9 +1333,9 @@ int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void*
   if (int st = dgemm(s, count, f_in, f_out, f_out, w.C, f_out, 1, w.Gy, 1, f_out, w.M, f_out, bs, 0, 1)) return st;
   if (int st = chol_backward(s, count, w.G, f_in, bs, w.xinvx, w.zbuf, w.M, f_out)) return st;
   for (int32_t z = 0; z < count; ++z) {
-    fit_output_kernel<<<grid_for(static_cast<int64_t>(f_in) * f_out), 256, 0, s>>>(
-        w.M + z * bs, f_in, f_out, w_out[z], b_out[z], w.sx + z * bs, w.sy + z * bs, inv_n);
-    KVX_LAUNCH_CHECK();
+    if (int st = fit_output(s, w.M + z * bs, f_in, f_out, w_out[z], b_out[z], w.sx + z * bs, w.sy + z * bs, inv_n,
+                            w.csp))
+      return st;
   }
   KVX_HIP_TRY(hipStreamSynchronize(s));
   int result = KVX_OK;
