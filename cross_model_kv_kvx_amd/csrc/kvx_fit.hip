@@ -98,8 +98,27 @@ __device__ __forceinline__ void gr_issue(__amdgpu_buffer_rsrc_t r, uint32_t pitc
   for (int i = 0; i < GR_LD; ++i) dma16(rr, base + off[i], 0, part + (wave * GR_LD + i) * 512);
 }
 
-// One step: 4 x (2 P + 4 Q fragments, 8 MFMAs).
-__device__ __forceinline__ void gr_compute(const uint16_t* pp, const uint16_t* pq, f32x16 (&acc)[2][4]) {
+// Load i (0..7) of a step's share of this wave: Q of step kq (loads 0..3),
+// then P of step kp (4..7).  The step spreads them over its sub-steps, two
+// at a time, so its products do not wait behind a burst of load issues.
+__device__ __forceinline__ void gr_load(const GrItem& it, int i, int kq, int kp, uint16_t* nq, uint16_t* np) {
+  const int wave = wave_id();
+  if (i < GR_LD) {
+    const __amdgpu_buffer_rsrc_t rr = kq < it.nk ? it.qr : buf_rsrc(nullptr, 0);
+    dma16(rr, static_cast<uint32_t>(kq) * GR_BK * it.q_pitch + it.q_off[i], 0, nq + (wave * GR_LD + i) * 512);
+  } else {
+    const __amdgpu_buffer_rsrc_t rr = kp < it.nk ? it.pr : buf_rsrc(nullptr, 0);
+    dma16(rr, static_cast<uint32_t>(kp) * GR_BK * it.p_pitch + it.p_off[i - GR_LD], 0,
+          np + (wave * GR_LD + i - GR_LD) * 512);
+  }
+}
+
+// One step: 4 x (2 P + 4 Q fragments, 8 MFMAs); with ISSUE, the loads of Q
+// of step kq and P of step kp are issued two per sub-step.
+template <bool ISSUE = false>
+__device__ __forceinline__ void gr_compute(const uint16_t* pp, const uint16_t* pq, f32x16 (&acc)[2][4],
+                                           const GrItem* it = nullptr, int kq = 0, int kp = 0,
+                                           uint16_t* nq = nullptr, uint16_t* np = nullptr) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;
   // lane of a 16-lane group g: the MFMA operand of lane l covers features
@@ -109,6 +128,12 @@ __device__ __forceinline__ void gr_compute(const uint16_t* pp, const uint16_t* p
   const int f0 = 16 * (g & 1) + 4 * (s & 3);
 #pragma unroll
   for (int kk = 0; kk < GR_BK / 16; ++kk) {
+    if constexpr (ISSUE) {
+      __builtin_amdgcn_sched_barrier(0);
+      gr_load(*it, 2 * kk, kq, kp, nq, np);
+      gr_load(*it, 2 * kk + 1, kq, kp, nq, np);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     u32x4 af[2], bf[4];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) af[mi] = gr_frag(pp, 16 * kk + r0, wm * 64 + mi * 32 + f0);
@@ -137,6 +162,10 @@ __device__ __forceinline__ void gr_sync() {
   gr_issue(it.qr, it.q_pitch, it.q_off, (K) + 1, it.nk, NB); \
   gr_issue(it.pr, it.p_pitch, it.p_off, (K) + 2, it.nk, NA); \
   if (LIVE) gr_compute(PA, PB, acc);
+// A whole step (no tail): loads spread over the sub-steps.
+#define GR_STEP_FULL(K, PA, PB, NB, NA)                    \
+  gr_sync();                                               \
+  gr_compute<true>(PA, PB, acc, &it, (K) + 1, (K) + 2, NB, NA);
 
 __global__ __attribute__((amdgpu_flat_work_group_size(GR_THREADS, GR_THREADS), amdgpu_waves_per_eu(2, 2))) void
 gram_kernel(const GramArgs g) {
@@ -217,7 +246,18 @@ gram_kernel(const GramArgs g) {
       gr_issue(it.pr, it.p_pitch, it.p_off, 0, it.nk, p0);
       gr_issue(it.qr, it.q_pitch, it.q_off, 0, it.nk, p1);
       gr_issue(it.pr, it.p_pitch, it.p_off, 1, it.nk, p2);
-      for (int k = 0; k < it.nk; k += 5) {
+      // whole groups of five steps without branches, then the 1..4
+      // remaining steps (a per-step branch would make the compiler drain
+      // every load before the first fragment read of a step)
+      int k = 0;
+      for (; k + 5 <= it.nk; k += 5) {
+        GR_STEP_FULL(k, p0, p1, p3, p4)
+        GR_STEP_FULL(k + 1, p2, p3, p0, p1)
+        GR_STEP_FULL(k + 2, p4, p0, p2, p3)
+        GR_STEP_FULL(k + 3, p1, p2, p4, p0)
+        GR_STEP_FULL(k + 4, p3, p4, p1, p2)
+      }
+      if (k < it.nk) {
         GR_STEP(k, p0, p1, p3, p4, true)
         GR_STEP(k + 1, p2, p3, p0, p1, k + 1 < it.nk)
         GR_STEP(k + 2, p4, p0, p2, p3, k + 2 < it.nk)
@@ -243,6 +283,7 @@ gram_kernel(const GramArgs g) {
   }
 }
 #undef GR_STEP
+#undef GR_STEP_FULL
 
 // fp32 inputs: G, C and column sums in fp64 by plain loops (small fits).
 __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ x, int64_t ldx,
