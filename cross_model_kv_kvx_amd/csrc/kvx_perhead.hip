@@ -38,9 +38,10 @@ namespace kvx {
 // counter is per wave: compute waves only load and store waves never wait,
 // so no load ever waits for stores to complete.  One barrier per tile orders
 // the stages and staging buffers between the two kinds.  Workgroups are
-// numbered receiver layer innermost and consecutive numbers go to one XCD,
-// so the receiver layers that share a sender layer read its rows through one
-// L2.
+// numbered head innermost, then receiver layer, and consecutive numbers go to
+// one XCD: the heads of a layer, which write the 256-byte pieces of the same
+// receiver rows, run side by side, and the neighbouring receiver layers that
+// share a sender layer read its rows through one L2.
 constexpr int PH_TILE = 64;                      // tokens per tile
 constexpr int PH_SPAN = 4096;                    // tokens per workgroup
 constexpr int PH_TILE_ELEMS = PH_TILE * 128;     // 16-bit elements of a tile (16 KB)
@@ -227,12 +228,12 @@ perhead_kernel(const HeadKArgs a) {
 
   int32_t b = blockIdx.x;
   if (a.xcd_remap) b = (b & 7) * (a.n_blocks >> 3) + (b >> 3);
-  const int32_t l = b % a.recv_layers;
-  int32_t rest = b / a.recv_layers;
+  const int32_t h = b % a.heads;
+  int32_t rest = b / a.heads;
+  const int32_t l = rest % a.recv_layers;
+  rest /= a.recv_layers;
   const int32_t span = rest % a.n_span;
-  rest /= a.n_span;
-  const int32_t h = rest % a.heads;
-  const int role = rest / a.heads;
+  const int role = rest / a.n_span;
   const int32_t s = a.tap[l];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int64_t row_elems = static_cast<int64_t>(a.heads) * 128;
