@@ -1012,3 +1012,41 @@ def test_fp8_maps_rope_full_sampled_rows():
     say("fp8 maps, flattened + RoPE, 32768 receiver tokens, sampled rows")
     c = flat_case(4, with_maps=False)
     check_flat8(c, sample_rows(O.token_align(c["send_end"], c["recv_end"]), 256, 4))
+
+
+def test_fp8_maps_key_norm_all_elements():
+    """fp8 maps with the receiver's key normalisation and both rotations: the
+    per-output scale is applied before the bias and the norm; every element of
+    400 receiver tokens vs the oracle on the oracle's own quantised maps."""
+    say("fp8 maps + receiver key norm + RoPE, 400 receiver tokens")
+    send_end, recv_end = synth.token_ends(400, 83)
+    shp = synth.CacheShape(36, len(send_end), 8, 128)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tmap_o = O.token_align(send_end, recv_end)
+    caches, q8, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, 8400 + r, DEV, outlier_frac=0.01, outlier_scale=20.0,
+                                          outlier_pairs=(role == "k"))
+        wt, u, v, b = synth.flat_maps(32, 3072, 1024, 8500 + r, DEV, 16)
+        q, sc = kvx.quantize_fp8(wt)
+        qo, so = O.quantize_fp8(host(wt).numpy())
+        assert np.array_equal(host(q).numpy(), qo)
+        assert np.array_equal(host(sc).numpy().view(np.uint32), so.view(np.uint32))
+        q8[role] = (q, sc, Fp8Maps(qo, so))
+        bias[role] = b
+        del wt, u, v
+    kn = synth.key_norm_weights(32, 128, 8600, DEV)
+    k, v = kvx.translate_fp8(caches["k"], caches["v"], dev_i32(tmap_o), taps, q8["k"][0], q8["v"][0], q8["k"][1],
+                             q8["v"][1], bias["k"], bias["v"], send_rope_base=5e5, recv_rope_base=1e6,
+                             recv_key_norm=kn, key_norm_eps=1e-6)
+    torch.cuda.synchronize()
+    rows = np.arange(tmap_o.size)
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], tmap_o, taps, q8[role][2], host(bias[role]).numpy().astype(np.float64),
+                                rows, per_head=False, recv_heads=8, recv_head_dim=128,
+                                send_rope_base=5e5 if rk else 0.0, recv_rope_base=1e6 if rk else 0.0,
+                                recv_key_norm=host(kn).numpy() if rk else None, key_norm_eps=1e-6)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  fp8 + key norm {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
