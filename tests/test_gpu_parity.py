@@ -1050,3 +1050,43 @@ def test_fp8_maps_key_norm_all_elements():
         err = O.rel_err(rows_of(out, rows), want)
         say(f"  fp8 + key norm {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
         assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("n_taps,fp32", [(1, False), (2, False), (3, False), (1, True)])
+def test_flat_short_k_all_elements(n_taps, fp32):
+    """Two-head caches give K extents of 4, 8 and 12 steps of 64 (fp32 maps
+    double them): K loops that are only a tail, and whole groups of five
+    steps followed by tails of every length; rotated keys."""
+    L_S, L_R, H = 6, 4, 2
+    send_end, recv_end = synth.token_ends(300, 90 + n_taps)
+    shp = synth.CacheShape(L_S, len(send_end), H, 128)
+    if n_taps == 2:  # any tap list is accepted: the matched layer and the next one
+        m = kvx.layer_map(L_S, L_R, 1, 1)[:, 0]
+        taps = np.stack([m, np.minimum(m + 1, L_S - 1)], axis=1).astype(np.int32)
+    else:
+        taps = kvx.layer_map(L_S, L_R, n_taps, 1)
+    say(f"flattened, {n_taps} taps x {H} heads, fp32 maps {fp32}: K steps {n_taps * H * 128 * (2 if fp32 else 1) // 64}")
+    tmap_o = O.token_align(send_end, recv_end)
+    caches, maps, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, 9100 + r, DEV)
+        wt, u, v, b = synth.flat_maps(L_R, n_taps * H * 128, H * 128, 9200 + r, DEV, 4)
+        if fp32:
+            maps[role] = (wt, F32Maps(host(wt).numpy()))
+        else:
+            wb = host(wt).to(torch.bfloat16)
+            maps[role] = (wb.to(DEV), Bf16Maps(wb.view(torch.int16).numpy().view(np.uint16)))
+        bias[role] = b
+        del u, v
+    k, v = kvx.translate(caches["k"], caches["v"], dev_i32(tmap_o), taps, maps["k"][0], maps["v"][0], bias["k"],
+                         bias["v"], send_rope_base=5e5, recv_rope_base=1e6)
+    torch.cuda.synchronize()
+    rows = np.arange(tmap_o.size)
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], tmap_o, taps, maps[role][1], host(bias[role]).numpy().astype(np.float64),
+                                rows, per_head=False, recv_heads=H, recv_head_dim=128,
+                                send_rope_base=5e5 if rk else 0.0, recv_rope_base=1e6 if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
