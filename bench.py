@@ -228,11 +228,15 @@ def flat_inputs(dev):
     return x
 
 
-def run_step(x, taps, ws, outs, stage_ms=None):
-    tmap = kvx.align_tokens(x["send_end"], x["recv_end"], out=outs["map"], workspace=outs["align_ws"])
+def run_step(x, taps, ws, outs, stage_ms=None, events=None):
+    """One step: alignment + translation.  With ``events`` (three recorded
+    torch.cuda.Event) nothing synchronises: the alignment leaves its validity
+    flag on the device and the translation records the phase events."""
+    inv = outs["invalid"] if events is not None else None
+    tmap = kvx.align_tokens(x["send_end"], x["recv_end"], out=outs["map"], workspace=outs["align_ws"], invalid=inv)
     kvx.translate(x["k_send"], x["v_send"], tmap, taps, x["wt_k"], x["wt_v"], x["b_k"], x["b_v"],
                   send_rope_base=5e5, recv_rope_base=1e6, k_recv=outs["k"], v_recv=outs["v"], workspace=ws,
-                  stage_ms=stage_ms)
+                  stage_ms=stage_ms, events=events)
     return tmap
 
 
@@ -602,20 +606,28 @@ def main():
             "align_ws": torch.empty(kvx.lib().kvx_align_workspace_size(N_R), dtype=torch.uint8, device=dev),
             "k": torch.empty((32, N_R, 8, 128), dtype=torch.bfloat16, device=dev)}
     outs["v"] = torch.empty_like(outs["k"])
+    outs["invalid"] = torch.zeros(1, dtype=torch.int32, device=dev)
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):
         run_step(x, taps, ws, outs)
+    # HIP events of every timed step (before the preparation kernels, before
+    # and after the translation kernel), recorded on the launch stream by the
+    # library; created by one record each before timing
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for trio in evs:
+        for e in trio:
+            e.record()
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps")
-    stages = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        st = []
-        tmap = run_step(x, taps, ws, outs, stage_ms=st)
-        stages.append(st)
+    for i in range(args.steps):
+        tmap = run_step(x, taps, ws, outs, events=evs[i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    if int(outs["invalid"].item()) != 0:
+        raise SystemExit("token alignment reported invalid offsets")
+    stages = [[trio[0].elapsed_time(trio[1]), trio[1].elapsed_time(trio[2])] for trio in evs]
     ms_step = dt * 1e3 / args.steps
     m = tmap.cpu().numpy()
     U = int(1 + np.count_nonzero(np.diff(m)))

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "kvx_fit.hpp"
+#include "kvx_align.hpp"
 
 namespace kvx {
 
@@ -135,6 +136,17 @@ int kvx_align_tokens(const int32_t* send_end, int32_t n_send, const int32_t* rec
   if (!workspace || ws_bytes < kvx_align_workspace_size(n_recv)) return KVX_ERR_WORKSPACE;
   return launch_align(send_end, n_send, recv_end, n_recv, recv_to_send, workspace,
                       static_cast<hipStream_t>(stream));
+}
+
+int kvx_align_tokens_async(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                           int32_t* recv_to_send, int32_t* invalid, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_send < 0 || n_recv < 0) return KVX_ERR_INVALID;
+  if (n_recv == 0) return KVX_OK;
+  if (n_send == 0) return KVX_ERR_SHAPE;
+  if (!send_end || !recv_end || !recv_to_send || !invalid) return KVX_ERR_INVALID;
+  if (!workspace || ws_bytes < kvx_align_workspace_size(n_recv)) return KVX_ERR_WORKSPACE;
+  return launch_align_async(send_end, n_send, recv_end, n_recv, recv_to_send, invalid, workspace,
+                            static_cast<hipStream_t>(stream));
 }
 
 size_t kvx_align_batched_workspace_size(const int32_t* recv_off, int32_t n_seq) {
@@ -516,6 +528,18 @@ int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const vo
     return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
                           wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
   });
+}
+
+int kvx_translate_recorded(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                           const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
+                           const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
+                           const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                           void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2]) return KVX_ERR_INVALID;
+  hipEvent_t ev[3] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1]),
+                      static_cast<hipEvent_t>(events[2])};
+  return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
 }
 
 int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void* v_send, const kvx_cache_desc* recv,

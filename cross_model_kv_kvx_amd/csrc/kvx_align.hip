@@ -21,7 +21,7 @@
 
 #include <vector>
 
-#include "kvx_internal.hpp"
+#include "kvx_align.hpp"
 
 namespace kvx {
 
@@ -184,6 +184,17 @@ int launch_align(const int32_t* send_end, int32_t n_send, const int32_t* recv_en
                  int32_t* out, void* ws, hipStream_t s) {
   const int32_t so[2] = {0, n_send}, ro[2] = {0, n_recv};
   return launch_align_batched(send_end, so, recv_end, ro, 1, out, ws, s);
+}
+
+// One sequence without synchronisation: invalid (device) receives 1 when an
+// offset array is not positive and strictly increasing, else 0.
+int launch_align_async(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                       int32_t* out, int32_t* invalid, void* ws, hipStream_t s) {
+  Carve c(ws);
+  (void)c.take<int32_t>(64);  // same layout as the synchronous call
+  int32_t* agg = c.take<int32_t>(ceil_div(n_recv > 0 ? n_recv : 1, SCAN_TILE));
+  if (int st = launch_fill_i32(invalid, 1, 0, s)) return st;
+  return align_one(send_end, n_send, recv_end, n_recv, out, 0, agg, invalid, s);
 }
 
 size_t align_batched_ws_bytes(const int32_t* recv_off, int32_t n_seq) {

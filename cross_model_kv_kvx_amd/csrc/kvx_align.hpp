@@ -1,0 +1,14 @@
+// Launchers of the token alignment that the C-ABI translation unit uses
+// beyond those of kvx_internal.hpp.
+#pragma once
+
+#include "kvx_internal.hpp"
+
+namespace kvx {
+
+// One sequence without synchronisation: invalid (device int32) receives 1
+// when an offset array is not positive and strictly increasing, else 0.
+int launch_align_async(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                       int32_t* out, int32_t* invalid, void* ws, hipStream_t s);
+
+}  // namespace kvx

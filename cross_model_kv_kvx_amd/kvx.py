@@ -30,7 +30,7 @@ EXPORTS = (
     "kvx_translate_timed", "kvx_translate_placed_workspace_size", "kvx_translate_placed", "kvx_gather_features",
     "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fit_ridge_batched_workspace_size",
     "kvx_fit_ridge_batched", "kvx_fit_recolor_workspace_size", "kvx_fit_recolor", "kvx_fold_lowrank",
-    "kvx_quantize_fp8", "kvx_translate_fp8",
+    "kvx_quantize_fp8", "kvx_translate_fp8", "kvx_align_tokens_async", "kvx_translate_recorded",
 )
 
 
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
                                                ip, ip, vp, sz, vp]),
             "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
             "kvx_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+            "kvx_align_tokens_async": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, vp, sz, vp]),
+            "kvx_translate_recorded": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp,
+                                                      vp, vp, sz, vp, vpp]),
             "kvx_translate_fp8": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, vp, vp, vp, vp, vp, vp, vp,
                                                  sz, vp, ctypes.POINTER(ctypes.c_float)]),
         }
@@ -158,8 +161,11 @@ def cache_desc(cache: torch.Tensor, rope_base: float = 0.0, tokens: Optional[int
 
 
 def align_tokens(send_end: torch.Tensor, recv_end: torch.Tensor, out: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """kvx_align_tokens: receiver->sender token map (device int32)."""
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 invalid: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvx_align_tokens: receiver->sender token map (device int32).  With a
+    device int32 tensor ``invalid`` (one element), kvx_align_tokens_async
+    instead: no synchronisation, the validity flag is left in ``invalid``."""
     _need(send_end, "send_end", torch.int32)
     _need(recv_end, "recv_end", torch.int32)
     n_r = recv_end.numel()
@@ -167,6 +173,12 @@ def align_tokens(send_end: torch.Tensor, recv_end: torch.Tensor, out: Optional[t
         out = torch.empty(n_r, dtype=torch.int32, device=recv_end.device)
     _need(out, "out", torch.int32)
     ws = _workspace(lib().kvx_align_workspace_size(n_r), recv_end.device, workspace)
+    if invalid is not None:
+        _need(invalid, "invalid", torch.int32)
+        st = lib().kvx_align_tokens_async(_ptr(send_end), send_end.numel(), _ptr(recv_end), n_r, _ptr(out),
+                                          _ptr(invalid), _ptr(ws), ws.numel(), _stream(stream))
+        _check(st, "kvx_align_tokens_async")
+        return out
     st = lib().kvx_align_tokens(_ptr(send_end), send_end.numel(), _ptr(recv_end), n_r, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream))
     _check(st, "kvx_align_tokens")
@@ -221,11 +233,13 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
               recv_key_norm: Optional[torch.Tensor] = None, key_norm_eps: float = 1e-6,
               slot: Optional[torch.Tensor] = None, pool_rows: Optional[int] = None,
               recv_pos: Optional[torch.Tensor] = None, send_pos: Optional[torch.Tensor] = None,
-              pos_limit: Optional[int] = None):
+              pos_limit: Optional[int] = None, events=None):
     """kvx_translate.  Returns (k_recv, v_recv) (either None when its role is
     skipped).  ``taps``: host int32 [L_R][n_taps] (numpy).  With a list
     ``stage_ms``, calls kvx_translate_timed instead (synchronous) and appends
-    the [preparation, translation kernel] device times in ms."""
+    the [preparation, translation kernel] device times in ms.  With three
+    recorded torch.cuda.Event objects ``events``, calls
+    kvx_translate_recorded (asynchronous; the events mark the phases)."""
     ref = k_send if k_send is not None else v_send
     if ref is None:
         raise ValueError("at least one role is needed")
@@ -262,7 +276,7 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
     if v_send is not None and v_recv is None:
         v_recv = torch.empty((L_R, rows, H_R, d_R), dtype=ref.dtype, device=ref.device)
     if placed:
-        if stage_ms is not None:
+        if stage_ms is not None or events is not None:
             raise ValueError("stage timing is not available with a placement")
         for name, t, dt in (("slot", slot, torch.int64), ("recv_pos", recv_pos, torch.int32),
                             ("send_pos", send_pos, torch.int32)):
@@ -284,6 +298,11 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
             _ptr(ws), ws.numel(), _stream(stream)]
     if placed:
         _check(lib().kvx_translate_placed(*args, ctypes.byref(place)), "kvx_translate_placed")
+    elif events is not None:
+        if len(events) != 3 or any(not e.cuda_event for e in events):
+            raise ValueError("events must be three torch.cuda.Event objects that have been recorded once")
+        ev = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+        _check(lib().kvx_translate_recorded(*args, ev), "kvx_translate_recorded")
     elif stage_ms is None:
         _check(lib().kvx_translate(*args), "kvx_translate")
     else:

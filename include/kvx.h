@@ -328,6 +328,33 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
                           int32_t* status, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvx_align_tokens without synchronisation, for callers that chain the
+ * alignment and the translation on one stream: the same map, and *invalid
+ * (device int32) is set to 1 when an offset array is not positive and
+ * strictly increasing, else 0, for the caller to read when it synchronises.
+ * The map is unspecified when *invalid is 1.  Host-side argument errors are
+ * returned as by kvx_align_tokens.  Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+int kvx_align_tokens_async(const int32_t* send_end, int32_t n_send, const int32_t* recv_end,
+                           int32_t n_recv, int32_t* recv_to_send, int32_t* invalid,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvx_translate recording three caller-created events (hipEvent_t, passed
+ * as void*) on `stream`: events[0] before the preparation kernels,
+ * events[1] before the translation kernel, events[2] after it; nothing is
+ * synchronised, so a caller can time many calls and read the events once.
+ * Nothing is recorded when the call has no work (empty problem).  Arguments
+ * and errors otherwise as kvx_translate; NULL events return KVX_ERR_INVALID.
+ * ---------------------------------------------------------------------- */
+int kvx_translate_recorded(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                           const kvx_cache_desc* recv, void* k_recv, void* v_recv,
+                           const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                           int32_t per_head, int32_t w_dtype, const void* wt_k, const void* wt_v,
+                           const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                           void* stream, void* const* events);
+
+/* ------------------------------------------------------------------------
  * FP8 map storage ("Cross-Model KV Cache Transfer in Production",
  * Implementation Guidelines: weight matrices may be stored quantised, e.g.
  * FP8, while the products keep 16-bit operands).

@@ -102,6 +102,10 @@ def test_translate_validation_before_launch():
     assert call(rd=desc(32, 0, 8, 128)) == kvx.OK                # nothing to translate
     assert call(k_recv=None, v_recv=None) == kvx.OK              # no role requested
 
+    noev = (ctypes.c_void_p * 3)(0x1000, 0, 0x1000)
+    assert L.kvx_translate_recorded(ctypes.byref(s), fake, fake, ctypes.byref(r), fake, fake, fake, tp, 3, 0,
+                                    kvx.BF16, fake, fake, None, None, fake, 1 << 40, None, noev) == kvx.ERR_INVALID
+
     def call8(sd=s, rd=r, sk=fake, sv=fake, ws_bytes=1 << 40):
         return L.kvx_translate_fp8(ctypes.byref(sd), fake, fake, ctypes.byref(rd), fake, fake, fake, tp, 3, fake,
                                    fake, sk, sv, None, None, fake, ws_bytes, None, None)
@@ -165,6 +169,9 @@ def test_other_entry_points_validate_before_launch():
     assert L.kvx_quantize_fp8(fake, 0, 16, fake, fake, None) == kvx.OK
     assert L.kvx_quantize_fp8(fake, 4, 0, fake, fake, None) == kvx.ERR_INVALID
     assert L.kvx_quantize_fp8(fake, 4, 16, None, fake, None) == kvx.ERR_INVALID
+    assert L.kvx_align_tokens_async(fake, 5, fake, 5, fake, None, fake, 1 << 30, None) == kvx.ERR_INVALID
+    assert L.kvx_align_tokens_async(fake, 5, fake, 5, fake, fake, None, 0, None) == kvx.ERR_WORKSPACE
+    assert L.kvx_align_tokens_async(fake, 5, fake, 0, fake, None, None, 0, None) == kvx.OK   # empty receiver
     assert L.kvx_fold_lowrank(fake, fake, fake, 0, 8, 8, 2, fake, kvx.BF16, None) == kvx.OK
     assert L.kvx_fold_lowrank(fake, None, fake, 1, 8, 8, 2, fake, kvx.BF16, None) == kvx.ERR_INVALID
     assert L.kvx_fold_lowrank(fake, fake, fake, 1, 8, 8, 2, fake, 5, None) == kvx.ERR_INVALID

@@ -1090,3 +1090,36 @@ def test_flat_short_k_all_elements(n_taps, fp32):
         err = O.rel_err(rows_of(out, rows), want)
         say(f"  {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
         assert err <= TOL_BF16
+
+
+
+def test_async_align_and_recorded_translate():
+    """The entries that do not synchronise: the alignment gives the same map
+    and flags invalid offsets on the device; the translation with recorded
+    events writes the same outputs, bit for bit, and the events time it."""
+    say("asynchronous alignment and translation with recorded events")
+    c = flat_case(4, 700, seed=17)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    se, re_ = dev_i32(c["send_end"]), dev_i32(c["recv_end"])
+    inv = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    m_sync = kvx.align_tokens(se, re_)
+    m_async = kvx.align_tokens(se, re_, invalid=inv)
+    torch.cuda.synchronize()
+    assert torch.equal(m_sync, m_async) and int(inv.item()) == 0
+    bad = c["recv_end"].copy()
+    bad[10] = bad[9]                                    # not strictly increasing
+    kvx.align_tokens(se, dev_i32(bad), invalid=inv)
+    torch.cuda.synchronize()
+    assert int(inv.item()) == 1
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in ev:
+        e.record()
+    kw = dict(send_rope_base=c["send_rope"], recv_rope_base=c["recv_rope"])
+    k1, v1 = kvx.translate(c["k_send"], c["v_send"], m_sync, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"], **kw)
+    k2, v2 = kvx.translate(c["k_send"], c["v_send"], m_async, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"],
+                           events=ev, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    prep, main = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    say(f"  recorded phases: preparation {prep:.3f} ms, translation {main:.3f} ms")
+    assert prep >= 0.0 and main > 0.0
