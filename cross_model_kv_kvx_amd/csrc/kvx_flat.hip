@@ -26,7 +26,11 @@
 //     output-major.  64 elements are one whole 128-byte line of each row, so
 //     every L2 request is a full line (half-line requests halve the L2
 //     throughput).  While step k is multiplied, W of step k+1 and A of steps
-//     k+1 and k+2 are in flight;
+//     k+1 and k+2 are in flight.  Waves 0..3 (one per SIMD) issue all of a
+//     step's loads and waves 4..7 none: the other wave of each SIMD never
+//     waits behind a queued load issue, and never waits on the vector-memory
+//     counter, so its epilogue stores drain while it already multiplies the
+//     next tile;
 //   * inside each 128-byte LDS row the 16-byte chunks are XOR-swizzled by
 //     (row / 2) mod 8 so fragment reads of consecutive rows hit distinct
 //     banks;
@@ -61,12 +65,13 @@ constexpr int FT_GM = 8;                              // row tiles per L2 group
 constexpr int FT_PART_ELEMS = FT_M * FT_BK;          // 16-bit elements of one ring part (32 KB)
 static_assert(FT_M == FT_N, "A and W parts share one size");
 constexpr int FT_ROWS_PER_LD = 8;                     // rows of one direct load (8 x 128 B)
-constexpr int FT_A_LD = FT_M / FT_ROWS_PER_LD / FT_WAVES;  // A loads per wave per step
-constexpr int FT_B_LD = FT_N / FT_ROWS_PER_LD / FT_WAVES;  // B loads per wave per step
+constexpr int FT_LOADERS = 4;                         // waves 0..3 issue every direct load
+constexpr int FT_A_LD = FT_M / FT_ROWS_PER_LD / FT_LOADERS;  // A loads per loading wave per step
+constexpr int FT_B_LD = FT_N / FT_ROWS_PER_LD / FT_LOADERS;  // B loads per loading wave per step
 constexpr int FT_EP_FLOATS = 32 * 128;                // staging of one wave (16 KB)
 // fp8 maps: the W part of a step is 256 outputs x 64 bytes (16 KB, in the
 // first half of its ring part); a load covers 16 rows (1 KB)
-constexpr int FT_B8_LD = FT_N * FT_BK / 1024 / FT_WAVES;
+constexpr int FT_B8_LD = FT_N * FT_BK / 1024 / FT_LOADERS;
 
 struct FlatKArgs {
   const uint16_t* a_src[2];
@@ -114,8 +119,8 @@ __device__ __forceinline__ int ft_chunk8(int r, int c) { return c ^ ((r >> 2) & 
 
 // Per-tile addressing of this thread's direct loads.  A load instruction
 // covers 8 tile rows (1 KB of the stage); lane j lands at row +j/8, physical
-// chunk j%8.  Wave w loads row groups FT_A_LD*w .. +FT_A_LD of A and
-// FT_B_LD*w .. +FT_B_LD of B.
+// chunk j%8.  Loading wave w (< FT_LOADERS) loads row groups
+// FT_A_LD*w .. +FT_A_LD of A and FT_B_LD*w .. +FT_B_LD of B.
 struct TileAddr {
   const char* a_src;            // A source, layer 0
   int64_t a_ls;                 // bytes between A source layers (< 2^31)
@@ -228,9 +233,10 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
     // two of the step's eight loads per sub-step (kept in place: the
     // scheduler would otherwise sink them to the end of the step)
     if constexpr (ISSUE) {
+      constexpr int nps = (FT_A_LD + FT_B_LD) / 4;
       __builtin_amdgcn_sched_barrier(0);
-      ft_load<false>(ta, sl, 2 * kk);
-      ft_load<false>(ta, sl, 2 * kk + 1);
+#pragma unroll
+      for (int j = 0; j < nps; ++j) ft_load<false>(ta, sl, nps * kk + j);
       __builtin_amdgcn_sched_barrier(0);
     }
     const int pc = ft_chunk(fr, 2 * kk + (lane >> 5)) << 4;
@@ -290,18 +296,11 @@ __device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* 
       const int kk = 2 * kp + sub;
       // the step's six loads (two W, four A), spread over the sub-steps
       if constexpr (ISSUE) {
+        constexpr int nps = (FT_A_LD + FT_B8_LD) / 4;
+        static_assert(nps * 4 == FT_A_LD + FT_B8_LD, "loads spread evenly over the sub-steps");
         __builtin_amdgcn_sched_barrier(0);
-        if (kk == 0) {
-          ft_load<true>(ta, sl, 0);
-          ft_load<true>(ta, sl, 1);
-        } else if (kk == 1) {
-          ft_load<true>(ta, sl, 2);
-        } else if (kk == 2) {
-          ft_load<true>(ta, sl, 3);
-          ft_load<true>(ta, sl, 4);
-        } else {
-          ft_load<true>(ta, sl, 5);
-        }
+#pragma unroll
+        for (int j = 0; j < nps; ++j) ft_load<true>(ta, sl, nps * kk + j);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int pc = ft_chunk(fr, 4 * h + kk) << 4;
@@ -321,11 +320,13 @@ __device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* 
   }
 }
 
-// Wait until all but the last A part issued by this wave have landed, then
-// one barrier: the parts of the current step are complete and every wave
-// has finished the previous step, whose two parts are now free.
+// A loading wave waits until all but the last A part it issued have landed,
+// then one barrier: the parts of the current step are complete and every
+// wave has finished the previous step, whose two parts are now free.  The
+// other waves issue no loads and only take the barrier.
+template <bool LD>
 __device__ __forceinline__ void ft_sync() {
-  KVX_WAIT_VM(FT_A_LD);
+  if constexpr (LD) KVX_WAIT_VM(FT_A_LD);
   KVX_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
   KVX_COMPILER_FENCE();
@@ -337,22 +338,23 @@ __device__ __forceinline__ void ft_sync() {
 // A whole step: loads spread over the sub-steps.
 #define FT_STEP(K, PA, PB, NB, NA)                                    \
   {                                                                   \
-    ft_sync();                                                        \
+    ft_sync<LD>();                                                    \
     const StepLoads sl = ft_step_loads<W8>(ta, (K), at, NB, NA);      \
     ft_atap_next(ta, at);                                             \
     if constexpr (W8)                                                 \
-      ft_compute8<F16>(PA, PB, acc, ta, sl);                          \
+      ft_compute8<F16, LD>(PA, PB, acc, ta, sl);                      \
     else                                                              \
-      ft_compute<F16>(PA, PB, acc, ta, sl);                           \
+      ft_compute<F16, LD>(PA, PB, acc, ta, sl);                       \
   }
 // A tail step: every load first, the products only while k < nk.
 #define FT_TAIL(K, PA, PB, NB, NA)                                    \
   {                                                                   \
-    ft_sync();                                                        \
+    ft_sync<LD>();                                                    \
     const StepLoads sl = ft_step_loads<W8>(ta, (K), at, NB, NA);      \
     ft_atap_next(ta, at);                                             \
-    for (int i_ = 0; i_ < (W8 ? FT_B8_LD : FT_B_LD) + FT_A_LD; ++i_)   \
-      ft_load<W8>(ta, sl, i_);                                        \
+    if constexpr (LD)                                                 \
+      for (int i_ = 0; i_ < (W8 ? FT_B8_LD : FT_B_LD) + FT_A_LD; ++i_) \
+        ft_load<W8>(ta, sl, i_);                                      \
     if ((K) < nk) {                                                   \
       if constexpr (W8)                                               \
         ft_compute8<F16, false>(PA, PB, acc, ta, sl);                 \
@@ -366,8 +368,8 @@ __device__ __forceinline__ void ft_sync() {
 // run without branches, the remaining 1..4 steps (and the loads past the
 // end, which read an empty buffer range so every wait keeps its count) run
 // as a tail.  The loads still in flight at the end are drained before the
-// parts are reused.
-template <bool F16, bool W8>
+// parts are reused.  LD: this wave issues the loads.
+template <bool F16, bool W8, bool LD>
 __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
                                          uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
   int k = 0;
@@ -386,7 +388,7 @@ __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p
     FT_TAIL(k + 3, p1, p2, p4, p0)
     FT_TAIL(k + 4, p3, p4, p1, p2)
   }
-  KVX_WAIT_VM(0);
+  if constexpr (LD) KVX_WAIT_VM(0);
 }
 #undef FT_TAIL
 #undef FT_STEP
@@ -477,16 +479,23 @@ flat_gemm_kernel(const FlatKArgs args) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // prologue: A0, W0 and A1 in flight.  The parts were last used as
-    // staging before the final barrier of the previous tile, so they are
-    // free.
-    ft_issue_a(ta, 0, p0);
-    ft_issue_b<W8>(ta, 0, p1);
-    ft_issue_a(ta, 1, p2);
-    if (args.a_f16[role])
-      ft_kloop<true, W8>(ta, nk, p0, p1, p2, p3, p4, acc);
-    else
-      ft_kloop<false, W8>(ta, nk, p0, p1, p2, p3, p4, acc);
+    // prologue (loading waves): A0, W0 and A1 in flight.  The parts were
+    // last used as staging before the final barrier of the previous tile, so
+    // they are free.
+    if (wave < FT_LOADERS) {
+      ft_issue_a(ta, 0, p0);
+      ft_issue_b<W8>(ta, 0, p1);
+      ft_issue_a(ta, 1, p2);
+      if (args.a_f16[role])
+        ft_kloop<true, W8, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+      else
+        ft_kloop<false, W8, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+    } else {
+      if (args.a_f16[role])
+        ft_kloop<true, W8, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+      else
+        ft_kloop<false, W8, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+    }
 
     // ------------------------------------------------------------ epilogue
     // Each wave owns 64 unique rows x one 128-wide head, written in two
