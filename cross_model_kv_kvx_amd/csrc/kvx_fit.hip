@@ -913,11 +913,11 @@ static int copy_back(hipStream_t s, int32_t count, const double* src, double* ds
   return KVX_OK;
 }
 
-// L Z = C in place for the factor of chol_factor (C [n][nrhs], row stride
-// nrhs) by 256-row blocks: Z_I = X_II C_I, then the rows below are updated,
+// Right-looking L Z = C (C [n][nrhs], row stride nrhs) by 256-row blocks:
+// Z_I = X_II C_I, then the rows below are updated,
 // so the right-hand sides are read and written n/256 times.  zbuf holds
 // 256 x nrhs doubles.
-static int chol_forward(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+static int chol_forward_right(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
                         double* zbuf, double* C, int32_t nrhs) {
   const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
   for (int32_t I = 0; I < n_outer; ++I) {
@@ -938,8 +938,8 @@ static int chol_forward(hipStream_t s, int32_t count, const double* A, int32_t n
   return KVX_OK;
 }
 
-// L^T W = Z in place (W_I = X_II^T Z_I, then the rows above are updated).
-static int chol_backward(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+// Right-looking L^T W = Z (W_I = X_II^T Z_I, then the rows above are updated).
+static int chol_backward_right(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
                          double* zbuf, double* C, int32_t nrhs) {
   const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
   for (int32_t I = n_outer - 1; I >= 0; --I) {
@@ -959,6 +959,74 @@ static int chol_backward(hipStream_t s, int32_t count, const double* A, int32_t 
 }
 
 // Gram and cross products of one problem into its G and C.
+// Left-looking L Z = C (C [n][nrhs], row stride nrhs) by 256-row blocks: block I is first reduced by every
+// solved block above it in one product (C_I -= L[I, 0:I] Z[0:I], K = the
+// rows solved so far), then Z_I = X_II C_I.  Each block of right-hand sides
+// is read and written twice, and the long-K product keeps the fp64 matrix
+// cores fed.  zbuf holds 256 x nrhs doubles.
+static int chol_forward_left(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+                        double* zbuf, double* C, int32_t nrhs) {
+  const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
+  for (int32_t I = 0; I < n_outer; ++I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, n - k0);
+    const double* X = xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    double* CI = C + static_cast<int64_t>(k0) * nrhs;
+    if (k0 > 0) {
+      const double* Lb = A + static_cast<int64_t>(k0) * n;  // L[k0 .. k0+nb)[0 .. k0)
+      if (int st = dgemm(s, count, nb, nrhs, k0, Lb, n, 1, C, nrhs, 1, CI, nrhs, bs, 0, 0)) return st;
+    }
+    if (int st = dgemm(s, count, nb, nrhs, nb, X, SV_NB, 1, CI, nrhs, 1, zbuf, nrhs, bs, 0, 1)) return st;
+    if (int st = copy_back(s, count, zbuf, CI, static_cast<int64_t>(nb) * nrhs, bs)) return st;
+  }
+  return KVX_OK;
+}
+
+// Left-looking L^T W = Z from the last block: Z_I -= L[below, I]^T
+// W[below] in one product, then W_I = X_II^T Z_I.
+static int chol_backward_left(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+                         double* zbuf, double* C, int32_t nrhs) {
+  const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
+  for (int32_t I = n_outer - 1; I >= 0; --I) {
+    const int32_t k0 = I * SV_NB;
+    const int32_t nb = min(SV_NB, n - k0);
+    const double* X = xinv + static_cast<int64_t>(I) * SV_NB * SV_NB;
+    double* CI = C + static_cast<int64_t>(k0) * nrhs;
+    const int32_t rest = n - k0 - nb;
+    if (rest > 0) {
+      // A[m][k] = L[k0 + nb + k][k0 + m]; B = the solved rows below
+      const double* Lc = A + static_cast<int64_t>(k0 + nb) * n + k0;
+      if (int st = dgemm(s, count, nb, nrhs, rest, Lc, 1, n, C + static_cast<int64_t>(k0 + nb) * nrhs, nrhs, 1, CI,
+                         nrhs, bs, 0, 0))
+        return st;
+    }
+    if (int st = dgemm(s, count, nb, nrhs, nb, X, 1, SV_NB, CI, nrhs, 1, zbuf, nrhs, bs, 0, 1)) return st;
+    if (int st = copy_back(s, count, zbuf, CI, static_cast<int64_t>(nb) * nrhs, bs)) return st;
+  }
+  return KVX_OK;
+}
+
+// The triangular solves for the factor of chol_factor, in place.  The
+// left-looking order reads and writes each block of right-hand sides twice
+// but runs one product of 256 x nrhs per problem and block; it is used when
+// the problems of the call give those products enough tiles to fill the
+// chip, else the right-looking order, whose updates span every row below.
+static bool solve_left(int32_t count, int32_t nrhs) {
+  return static_cast<int64_t>(count) * (SV_NB / 128) * ceil_div(nrhs, 128) >= 512;
+}
+
+static int chol_forward(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+                        double* zbuf, double* C, int32_t nrhs) {
+  return solve_left(count, nrhs) ? chol_forward_left(s, count, A, n, bs, xinv, zbuf, C, nrhs)
+                                 : chol_forward_right(s, count, A, n, bs, xinv, zbuf, C, nrhs);
+}
+
+static int chol_backward(hipStream_t s, int32_t count, const double* A, int32_t n, int64_t bs, const double* xinv,
+                         double* zbuf, double* C, int32_t nrhs) {
+  return solve_left(count, nrhs) ? chol_backward_left(s, count, A, n, bs, xinv, zbuf, C, nrhs)
+                                 : chol_backward_right(s, count, A, n, bs, xinv, zbuf, C, nrhs);
+}
+
 static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32, int64_t n_rows,
                     int32_t f_in, int32_t f_out, float* part, double* G, double* C, hipStream_t s) {
   if (in_f32) {

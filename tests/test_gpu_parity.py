@@ -684,6 +684,35 @@ def test_fit_batched_matches_single_and_oracle():
         assert err <= TOL_BF16
 
 
+def test_fit_batched_many_problems_vs_oracle():
+    """32 problems of 776 features -> 1024 outputs in one call (enough
+    tiles for the left-looking triangular solves; 776 = three 256-row blocks
+    and a ragged block of 8), with an intercept: every problem against the
+    oracle's fit, and against the single-problem call (which solves
+    right-looking, so the two agree to rounding, not bit for bit)."""
+    say("batched ridge fit, 32 problems, 1024 rows, 776 -> 1024, intercept")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    n, f_in, f_out, count = 1024, 776, 1024, 32
+    mix = torch.randn((f_in, f_in), generator=g, device=DEV) / f_in ** 0.5 + torch.eye(f_in, device=DEV)
+    xs = [(torch.randn((n, f_in), generator=g, device=DEV) @ mix + 0.5).to(torch.bfloat16) for _ in range(count)]
+    a = torch.randn((f_in, f_out), generator=g, device=DEV) / f_in ** 0.5
+    ys = [(x.float() @ a + 0.3 * torch.randn((n, f_out), generator=g, device=DEV) - 1.0).to(torch.bfloat16)
+          for x in xs]
+    st = []
+    ws, bs = kvx.fit_ridge_batched(xs, ys, lambda_rel=1e-3, fit_intercept=True, status=st)
+    assert st == [kvx.OK] * count
+    for i in (0, 13, 31):
+        wo, bo, _ = O.ridge_fit(O.as_f64(xs[i]), O.as_f64(ys[i]), lam_rel=1e-3, fit_intercept=True)
+        err_w = O.rel_err(ws[i].cpu().numpy(), wo.T)
+        err_b = O.rel_err(bs[i].cpu().numpy(), bo)
+        w1, b1 = kvx.fit_ridge(xs[i], ys[i], lambda_rel=1e-3, fit_intercept=True)
+        d_w = O.rel_err(ws[i].cpu().numpy(), w1.cpu().numpy().astype(np.float64))
+        say(f"  problem {i}: W {err_w:.3e}  b {err_b:.3e}  vs single call {d_w:.3e}")
+        assert err_w <= TOL_BF16 and err_b <= TOL_BF16
+        assert d_w <= 1e-5
+
+
 def test_fit_batched_flags_each_problem():
     """lambda = 0 with one rank-deficient problem (half its feature columns
     zero: exact zero pivots) next to a well-posed one: the status of each is
