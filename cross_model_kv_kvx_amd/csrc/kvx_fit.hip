@@ -846,13 +846,29 @@ static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, 
 // X[b, 0:b] = -L_bb^-1 (L[b, 0:b] X[0:b, 0:b]).  Entries strictly above the
 // diagonal of A are left with partial updates (only the lower triangle is
 // the factor).  A non-positive pivot sets flags[z].
+// When the call's problems fill the chip with the products (see
+// factor_left), the factorisation runs left-looking instead: each panel is
+// first reduced by all columns left of it in one product (K = p0), and
+// nothing right of the panel is touched, so each column block is read and
+// written once by those products rather than once per panel to its left.
+static bool factor_left(int32_t count, int32_t n) {
+  return static_cast<int64_t>(count) * ceil_div(n, 128) * (SV_NB / 128) >= 384;
+}
+
 static int chol_factor(hipStream_t s, int32_t count, double* A, int32_t n, int64_t bs, double* linv, double* xinv,
                        double* zbuf, int32_t* flags) {
   const int32_t nb_total = static_cast<int32_t>(ceil_div(n, CH_NB));
   const int32_t n_outer = static_cast<int32_t>(ceil_div(n, SV_NB));
+  const bool left = factor_left(count, n);
   for (int32_t I = 0; I < n_outer; ++I) {
     const int32_t p0 = I * SV_NB;
     const int32_t pn = min(SV_NB, n - p0);
+    if (left && p0 > 0) {
+      // A[p0:n][p0:p0+pn] -= A[p0:n][0:p0] A[p0:p0+pn][0:p0]^T (lower part)
+      const double* Lr = A + static_cast<int64_t>(p0) * n;
+      double* Ct = A + static_cast<int64_t>(p0) * n + p0;
+      if (int st = dgemm(s, count, n - p0, pn, p0, Lr, n, 1, Lr, 1, n, Ct, n, bs, 1, 0)) return st;
+    }
     for (int32_t k0 = p0; k0 < p0 + pn; k0 += CH_NB) {
       const int32_t nb = min(CH_NB, n - k0);
       double* li = linv + static_cast<int64_t>(k0 / CH_NB) * CH_NB * CH_NB;
@@ -872,7 +888,7 @@ static int chol_factor(hipStream_t s, int32_t count, double* A, int32_t n, int64
     }
     // trailing lower update right of the panel, K = the panel's width
     const int32_t rest = n - p0 - pn;
-    if (rest > 0) {
+    if (!left && rest > 0) {
       const double* PI = A + static_cast<int64_t>(p0 + pn) * n + p0;
       double* Ct = A + static_cast<int64_t>(p0 + pn) * n + p0 + pn;
       if (int st = dgemm(s, count, rest, rest, pn, PI, n, 1, PI, 1, n, Ct, n, bs, 1, 0)) return st;
