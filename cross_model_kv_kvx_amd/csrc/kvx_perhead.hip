@@ -79,21 +79,33 @@ struct PhTile {
   uint32_t row_bytes;
 };
 
-// Direct loads of tile k (64 rows) into `slot` by compute wave w: rows
-// 16w .. 16w+15 with 4 instructions of 4 rows; lane j of instruction i takes
-// row 16w + 4i + j/16, physical chunk j%16.  Tiles past the end read nothing.
-__device__ __forceinline__ void ph_issue(const PhTile& pt, int k, uint16_t* slot) {
+// Sender rows of this lane's 4 loads of tile k (compute wave w: rows
+// 16w .. 16w+15, lane j of load i takes row 16w + 4i + j/16); tiles past
+// the end read an in-range entry.
+struct PhRows {
+  int32_t sv[4];
+};
+__device__ __forceinline__ PhRows ph_rows(const PhTile& pt, int k) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int32_t r0 = k * PH_TILE + 16 * wave + (lane >> 4);
+  PhRows r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.sv[i] = pt.msm[min(r0 + 4 * i, PH_SPAN - 1)];
+  return r;
+}
+
+// Direct loads of tile k (64 rows) into `slot` by compute wave w from its
+// rows `rr`: 4 instructions of 4 rows, lane j of instruction i at physical
+// chunk j%16.  Tiles past the end read nothing.
+__device__ __forceinline__ void ph_issue(const PhTile& pt, int k, const PhRows& rr, uint16_t* slot) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const bool live = k < pt.n_tiles;
   const __amdgpu_buffer_rsrc_t xr = live ? pt.xr : buf_rsrc(nullptr, 0);
   const int q = lane >> 4;
-  const int32_t r0 = k * PH_TILE + 16 * wave + q;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // tiles past the end (not multiplied) read an in-range entry
-    const int32_t sv = pt.msm[min(r0 + 4 * i, PH_SPAN - 1)];
     const int row = 16 * wave + 4 * i + q;
-    const uint32_t voff = static_cast<uint32_t>(sv) * pt.row_bytes + 16u * ph_chunk(row, lane & 15);
+    const uint32_t voff = static_cast<uint32_t>(rr.sv[i]) * pt.row_bytes + 16u * ph_chunk(row, lane & 15);
     dma16(xr, voff, 0, slot + (4 * wave + i) * 512);
   }
 }
@@ -131,18 +143,30 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
   for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[ti][e] = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    u32x4 xf[2];
+  // the fragments of step ks + 1 are read before the products of step ks
+  // are issued, so their LDS latency runs under those products (one compute
+  // wave per SIMD: nothing else would fill the gap)
+  u32x4 xf[2][2];
+  auto read = [&](int ks, int buf) {
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
       const int row = 32 * ti + (lane & 31);
-      xf[ti] = *reinterpret_cast<const u32x4*>(xb + row * 256 + 16 * ph_chunk(row, 2 * ks + (lane >> 5)));
+      xf[buf][ti] = *reinterpret_cast<const u32x4*>(xb + row * 256 + 16 * ph_chunk(row, 2 * ks + (lane >> 5)));
     }
+  };
+  read(0, 0);
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      acc[ti] = ph_mfma<F16>(wh[ks], xf[ti], acc[ti]);
-      if constexpr (WF32) acc[ti] = ph_mfma<F16>(wl[ks], xf[ti], acc[ti]);
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks < 7) {
+      read(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int b = ks & 1;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) acc[ti] = ph_mfma<F16>(wh[ks], xf[b][ti], acc[ti]);
+    if constexpr (WF32) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) acc[ti] = ph_mfma<F16>(wl[ks], xf[b][ti], acc[ti]);
     }
   }
   // lane: token 32 ti + lane % 32, local rows j = 8 g + 4 (lane / 32) + e
@@ -295,11 +319,13 @@ perhead_kernel(const HeadKArgs a) {
   }
 
   // tiles 0 .. 4 in flight while the map fragments are prepared
-  ph_issue(pt, 0, x0);
-  ph_issue(pt, 1, x1);
-  ph_issue(pt, 2, x2);
-  ph_issue(pt, 3, x3);
-  ph_issue(pt, 4, x4);
+  ph_issue(pt, 0, ph_rows(pt, 0), x0);
+  ph_issue(pt, 1, ph_rows(pt, 1), x1);
+  ph_issue(pt, 2, ph_rows(pt, 2), x2);
+  ph_issue(pt, 3, ph_rows(pt, 3), x3);
+  ph_issue(pt, 4, ph_rows(pt, 4), x4);
+  // rows of the tile the first step issues, read a step ahead from then on
+  PhRows rr = ph_rows(pt, PH_RING - 1);
 
   // A fragments: rows n = ph_out(wave, lane % 32) of W_{l,h} ([n][c], output
   // major), k = 16 ks + 8 (lane / 32) .. +8; halves rounded to nearest even
@@ -361,7 +387,8 @@ perhead_kernel(const HeadKArgs a) {
       KVX_WAIT_LGKM0();                                                        \
       ph_barrier();                                                            \
     }                                                                          \
-    ph_issue(pt, (K) + PH_RING - 1, XNEXT);                                    \
+    ph_issue(pt, (K) + PH_RING - 1, rr, XNEXT);                                \
+    rr = ph_rows(pt, (K) + PH_RING);                                           \
     if ((K) < pt.n_tiles)                                                      \
       ph_compute<WF32, F16>(XS, YS, wh, wl, bn, rot, rs, rpos, a.tab_recv,      \
                             pt.t0 + (K) * PH_TILE, a.recv_tokens, a.pos_limit); \
