@@ -230,8 +230,8 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
   const int fr = lane & 31;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    // two of the step's eight loads per sub-step (kept in place: the
-    // scheduler would otherwise sink them to the end of the step)
+    // a loading wave issues four of its sixteen loads per sub-step (kept in
+    // place: the scheduler would otherwise sink them to the end of the step)
     if constexpr (ISSUE) {
       constexpr int nps = (FT_A_LD + FT_B_LD) / 4;
       __builtin_amdgcn_sched_barrier(0);
@@ -294,7 +294,7 @@ __device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int kk = 2 * kp + sub;
-      // the step's six loads (two W, four A), spread over the sub-steps
+      // a loading wave's twelve loads (four W, eight A), three per sub-step
       if constexpr (ISSUE) {
         constexpr int nps = (FT_A_LD + FT_B8_LD) / 4;
         static_assert(nps * 4 == FT_A_LD + FT_B8_LD, "loads spread evenly over the sub-steps");
