@@ -69,9 +69,9 @@ constexpr int FT_LOADERS = 4;                         // waves 0..3 issue every 
 constexpr int FT_A_LD = FT_M / FT_ROWS_PER_LD / FT_LOADERS;  // A loads per loading wave per step
 constexpr int FT_B_LD = FT_N / FT_ROWS_PER_LD / FT_LOADERS;  // B loads per loading wave per step
 constexpr int FT_EP_FLOATS = 32 * 128;                // staging of one wave (16 KB)
-// fp8 maps: the W part of a step is 256 outputs x 64 bytes (16 KB, in the
-// first half of its ring part); a load covers 16 rows (1 KB)
-constexpr int FT_B8_LD = FT_N * FT_BK / 1024 / FT_LOADERS;
+// fp8 maps: a W part holds 128 k of each of the 256 rows (32 KB, one whole
+// 128-byte line per row) and serves two steps
+constexpr int FT_W8_BK = 128;
 
 struct FlatKArgs {
   const uint16_t* a_src[2];
@@ -111,11 +111,9 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                    0, 0, 0);
 }
 
-// Physical 16-byte chunk of logical chunk c in tile row r.
+// Physical 16-byte chunk of logical chunk c in tile row r (128-byte rows of
+// every part: 64 16-bit elements, or 128 fp8 codes of a W part).
 __device__ __forceinline__ int ft_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
-// fp8 W rows are 64 bytes (four 16-byte chunks), swizzled by (r / 4) mod 4
-// so the 16 rows of one quarter-wave fragment read hit distinct banks.
-__device__ __forceinline__ int ft_chunk8(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 // Per-tile addressing of this thread's direct loads.  A load instruction
 // covers 8 tile rows (1 KB of the stage); lane j lands at row +j/8, physical
@@ -151,15 +149,13 @@ __device__ __forceinline__ void ft_issue_a(const TileAddr& ta, int k, uint16_t* 
   for (int i = 0; i < FT_A_LD; ++i) dma16(a_r, ta.a_off[i], a_soff, part + (wave * FT_A_LD + i) * 512);
 }
 
-// W part of step k into `part` (fp8 maps: 64 bytes of each of the 256 rows).
-template <bool W8>
+// W part of step k into `part` (16-bit maps).
 __device__ __forceinline__ void ft_issue_b(const TileAddr& ta, int k, uint16_t* part) {
   const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t w_r = buf_rsrc(ta.w_base, k < ta.nk ? ta.w_bytes : 0u);
-  constexpr int n_ld = W8 ? FT_B8_LD : FT_B_LD;
-  const uint32_t b_soff = (W8 ? 1u : 2u) * static_cast<uint32_t>(k * FT_BK);
+  const uint32_t b_soff = 2u * static_cast<uint32_t>(k * FT_BK);
 #pragma unroll
-  for (int i = 0; i < n_ld; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * n_ld + i) * 512);
+  for (int i = 0; i < FT_B_LD; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * FT_B_LD + i) * 512);
 }
 
 // The loads one K step issues (W of step k+1 into nb, A of step k+2 into
@@ -191,13 +187,12 @@ __device__ __forceinline__ void ft_atap_next(const TileAddr& ta, ATap& t) {
   }
 }
 
-template <bool W8>
 __device__ __forceinline__ StepLoads ft_step_loads(const TileAddr& ta, int k, const ATap& t, uint16_t* nb,
                                                    uint16_t* na) {
   StepLoads sl;
   const int kb = k + 1, ka = k + 2;
   sl.br = buf_rsrc(ta.w_base, kb < ta.nk ? ta.w_bytes : 0u);
-  sl.bsoff = (W8 ? 1u : 2u) * static_cast<uint32_t>(kb * FT_BK);
+  sl.bsoff = 2u * static_cast<uint32_t>(kb * FT_BK);
   const uint32_t layer = ((t.a_tap < 4 ? ta.taps0 : ta.taps1) >> (8 * (t.a_tap & 3))) & 0xffu;
   sl.ar = buf_rsrc(ta.a_src + static_cast<int64_t>(layer) * ta.a_ls, ka < ta.nk ? static_cast<uint32_t>(ta.a_ls) : 0u);
   sl.asoff = 2u * static_cast<uint32_t>(t.a_in * FT_BK);
@@ -207,14 +202,12 @@ __device__ __forceinline__ StepLoads ft_step_loads(const TileAddr& ta, int k, co
 }
 
 // Load i of this wave's share of a step (W loads, then A loads).
-template <bool W8>
 __device__ __forceinline__ void ft_load(const TileAddr& ta, const StepLoads& sl, int i) {
-  constexpr int nbl = W8 ? FT_B8_LD : FT_B_LD;
   const int wave = wave_id();
-  if (i < nbl)
-    dma16(sl.br, ta.b_off[i], sl.bsoff, sl.nb + (wave * nbl + i) * 512);
+  if (i < FT_B_LD)
+    dma16(sl.br, ta.b_off[i], sl.bsoff, sl.nb + (wave * FT_B_LD + i) * 512);
   else
-    dma16(sl.ar, ta.a_off[i - nbl], sl.asoff, sl.na + (wave * FT_A_LD + i - nbl) * 512);
+    dma16(sl.ar, ta.a_off[i - FT_B_LD], sl.asoff, sl.na + (wave * FT_A_LD + i - FT_B_LD) * 512);
 }
 
 // One K step from an A part and a W part: 4 x (2 A + 4 B fragment reads,
@@ -236,7 +229,7 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
       constexpr int nps = (FT_A_LD + FT_B_LD) / 4;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < nps; ++j) ft_load<false>(ta, sl, nps * kk + j);
+      for (int j = 0; j < nps; ++j) ft_load(ta, sl, nps * kk + j);
       __builtin_amdgcn_sched_barrier(0);
     }
     const int pc = ft_chunk(fr, 2 * kk + (lane >> 5)) << 4;
@@ -250,73 +243,6 @@ __device__ __forceinline__ void ft_compute(const uint16_t* pa, const uint16_t* p
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma32<F16>(af[mi], bfr[ni], acc[mi][ni]);
-  }
-}
-
-// Eight fp8 E4M3 codes (two dwords, element e in byte e) as eight 16-bit
-// operands of the A operand's type; exact (every E4M3 value is a normal bf16
-// and a normal fp16).  The per-output scale is applied in the epilogue.
-template <bool F16>
-__device__ __forceinline__ u32x4 ft_fp8x8(uint32_t lo, uint32_t hi) {
-  if constexpr (F16)
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
-  else
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
-}
-
-// One K step with fp8 maps.  The order of the 64 k inside a step is
-// permuted (the same for both operands, so the contraction is unchanged):
-// sub-step kk of lane half h takes logical 8-element chunk 4h + kk, so the
-// W bytes a lane needs for sub-steps 2p and 2p+1 are one 16-byte chunk
-// (logical 2h + p of its 64-byte row) and one fragment read serves two
-// sub-steps.
-template <bool F16, bool ISSUE = true>
-__device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* pb, f32x16 (&acc)[2][4],
-                                            const TileAddr& ta, const StepLoads& sl) {
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int wm = wave & 3, wn = wave >> 2;
-  const char* sa = reinterpret_cast<const char*>(pa);
-  const char* sb = reinterpret_cast<const char*>(pb);
-  const int fr = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    u32x4 braw[4];
-    const int pc8 = ft_chunk8(fr, 2 * h + kp) << 4;
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) braw[ni] = *reinterpret_cast<const u32x4*>(sb + (wn * 128 + ni * 32 + fr) * 64 + pc8);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kk = 2 * kp + sub;
-      // a loading wave's twelve loads (four W, eight A), three per sub-step
-      if constexpr (ISSUE) {
-        constexpr int nps = (FT_A_LD + FT_B8_LD) / 4;
-        static_assert(nps * 4 == FT_A_LD + FT_B8_LD, "loads spread evenly over the sub-steps");
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < nps; ++j) ft_load<true>(ta, sl, nps * kk + j);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const int pc = ft_chunk(fr, 4 * h + kk) << 4;
-      u32x4 af[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const u32x4*>(sa + (wm * 64 + mi * 32 + fr) * 128 + pc);
-      // each W fragment is converted right before its two products, so one
-      // converted fragment is live at a time
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const u32x4 bfr = sub == 0 ? ft_fp8x8<F16>(braw[ni][0], braw[ni][1]) : ft_fp8x8<F16>(braw[ni][2], braw[ni][3]);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) acc[mi][ni] = mfma32<F16>(af[mi], bfr, acc[mi][ni]);
-      }
-    }
   }
 }
 
@@ -339,28 +265,21 @@ __device__ __forceinline__ void ft_sync() {
 #define FT_STEP(K, PA, PB, NB, NA)                                    \
   {                                                                   \
     ft_sync<LD>();                                                    \
-    const StepLoads sl = ft_step_loads<W8>(ta, (K), at, NB, NA);      \
+    const StepLoads sl = ft_step_loads(ta, (K), at, NB, NA);          \
     ft_atap_next(ta, at);                                             \
-    if constexpr (W8)                                                 \
-      ft_compute8<F16, LD>(PA, PB, acc, ta, sl);                      \
-    else                                                              \
-      ft_compute<F16, LD>(PA, PB, acc, ta, sl);                       \
+    ft_compute<F16, LD>(PA, PB, acc, ta, sl);                         \
   }
 // A tail step: every load first, the products only while k < nk.
 #define FT_TAIL(K, PA, PB, NB, NA)                                    \
   {                                                                   \
     ft_sync<LD>();                                                    \
-    const StepLoads sl = ft_step_loads<W8>(ta, (K), at, NB, NA);      \
+    const StepLoads sl = ft_step_loads(ta, (K), at, NB, NA);          \
     ft_atap_next(ta, at);                                             \
     if constexpr (LD)                                                 \
-      for (int i_ = 0; i_ < (W8 ? FT_B8_LD : FT_B_LD) + FT_A_LD; ++i_) \
-        ft_load<W8>(ta, sl, i_);                                      \
-    if ((K) < nk) {                                                   \
-      if constexpr (W8)                                               \
-        ft_compute8<F16, false>(PA, PB, acc, ta, sl);                 \
-      else                                                            \
-        ft_compute<F16, false>(PA, PB, acc, ta, sl);                  \
-    }                                                                 \
+      for (int i_ = 0; i_ < FT_B_LD + FT_A_LD; ++i_)                  \
+        ft_load(ta, sl, i_);                                          \
+    if ((K) < nk)                                                     \
+      ft_compute<F16, false>(PA, PB, acc, ta, sl);                    \
   }
 
 // K loop over nk >= 1 steps with A0, W0 and A1 already issued into parts 0,
@@ -369,7 +288,7 @@ __device__ __forceinline__ void ft_sync() {
 // end, which read an empty buffer range so every wait keeps its count) run
 // as a tail.  The loads still in flight at the end are drained before the
 // parts are reused.  LD: this wave issues the loads.
-template <bool F16, bool W8, bool LD>
+template <bool F16, bool LD>
 __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
                                          uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
   int k = 0;
@@ -392,6 +311,183 @@ __device__ __forceinline__ void ft_kloop(const TileAddr& ta, int nk, uint16_t* p
 }
 #undef FT_TAIL
 #undef FT_STEP
+
+// ---------------------------------------------------------------- fp8 maps
+// With fp8 maps the ring parts keep fixed roles: the A part of step k sits
+// in part k mod 3 (p0..p2) and W part j, 128 k of each of the 256 rows
+// (32 KB, one whole 128-byte line per row) serving steps 2j and 2j+1, in
+// p3 or p4 (j mod 2).  W part j+1 is issued at step 2j, two steps before
+// its first use; the A parts keep their two-step lead.  A loading wave
+// issues 8 W and 8 A loads at an even step and 8 A loads at an odd one, so
+// its wait leaves 8 loads in flight before an even step and 16 before an
+// odd one.  The pattern repeats every 12 steps.
+
+// W part j into `part`.
+__device__ __forceinline__ void ft_issue_w8(const TileAddr& ta, int j, uint16_t* part) {
+  const int wave = wave_id();
+  const __amdgpu_buffer_rsrc_t w_r = buf_rsrc(ta.w_base, 2 * j < ta.nk ? ta.w_bytes : 0u);
+  const uint32_t b_soff = static_cast<uint32_t>(j * FT_W8_BK);
+#pragma unroll
+  for (int i = 0; i < FT_B_LD; ++i) dma16(w_r, ta.b_off[i], b_soff, part + (wave * FT_B_LD + i) * 512);
+}
+
+// The loads of step k: W part k/2 + 1 into nb (even k) and A of step k + 2
+// into na.
+__device__ __forceinline__ StepLoads ft_step_loads8(const TileAddr& ta, int k, const ATap& t, uint16_t* nb,
+                                                    uint16_t* na) {
+  StepLoads sl;
+  const int jb = (k >> 1) + 1, ka = k + 2;
+  sl.br = buf_rsrc(ta.w_base, 2 * jb < ta.nk ? ta.w_bytes : 0u);
+  sl.bsoff = static_cast<uint32_t>(jb * FT_W8_BK);
+  const uint32_t layer = ((t.a_tap < 4 ? ta.taps0 : ta.taps1) >> (8 * (t.a_tap & 3))) & 0xffu;
+  sl.ar = buf_rsrc(ta.a_src + static_cast<int64_t>(layer) * ta.a_ls, ka < ta.nk ? static_cast<uint32_t>(ta.a_ls) : 0u);
+  sl.asoff = 2u * static_cast<uint32_t>(t.a_in * FT_BK);
+  sl.na = na;
+  sl.nb = nb;
+  return sl;
+}
+
+// Load i of a loading wave's share of a step: at an even step the W loads
+// and then the A loads, at an odd step the A loads only.
+template <bool EVEN>
+__device__ __forceinline__ void ft_load8(const TileAddr& ta, const StepLoads& sl, int i) {
+  const int wave = wave_id();
+  if (EVEN && i < FT_B_LD) {
+    dma16(sl.br, ta.b_off[i], sl.bsoff, sl.nb + (wave * FT_B_LD + i) * 512);
+  } else {
+    const int ia = EVEN ? i - FT_B_LD : i;
+    dma16(sl.ar, ta.a_off[ia], sl.asoff, sl.na + (wave * FT_A_LD + ia) * 512);
+  }
+}
+
+// Eight fp8 E4M3 codes (two dwords, element e in byte e) as eight 16-bit
+// operands of the A operand's type; exact (every E4M3 value is a normal bf16
+// and a normal fp16).  The per-output scale is applied in the epilogue.
+template <bool F16>
+__device__ __forceinline__ u32x4 ft_fp8x8(uint32_t lo, uint32_t hi) {
+  if constexpr (F16)
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
+  else
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+// One K step with fp8 maps, from an A part and half S of a W part.  The
+// order of the 64 k inside a step is permuted (the same for both operands,
+// so the contraction is unchanged): sub-step kk of lane half h takes logical
+// 8-element chunk 4h + kk, so the W bytes a lane needs for sub-steps 2p and
+// 2p+1 are one 16-byte chunk (4S + 2h + p of its 128-byte row) and one
+// fragment read serves two sub-steps.  NPS loads are issued per sub-step.
+template <bool F16, int NPS, int S>
+__device__ __forceinline__ void ft_compute8(const uint16_t* pa, const uint16_t* pw, f32x16 (&acc)[2][4],
+                                            const TileAddr& ta, const StepLoads& sl) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave & 3, wn = wave >> 2;
+  const char* sa = reinterpret_cast<const char*>(pa);
+  const char* sw = reinterpret_cast<const char*>(pw);
+  const int fr = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    u32x4 braw[4];
+    const int pcw = ft_chunk(fr, 4 * S + 2 * h + kp) << 4;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) braw[ni] = *reinterpret_cast<const u32x4*>(sw + (wn * 128 + ni * 32 + fr) * 128 + pcw);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kk = 2 * kp + sub;
+      if constexpr (NPS > 0) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NPS; ++j) ft_load8<NPS == (FT_A_LD + FT_B_LD) / 4>(ta, sl, NPS * kk + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int pc = ft_chunk(fr, 4 * h + kk) << 4;
+      u32x4 af[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4*>(sa + (wm * 64 + mi * 32 + fr) * 128 + pc);
+      // each W fragment is converted right before its two products, so one
+      // converted fragment is live at a time
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const u32x4 bfr = sub == 0 ? ft_fp8x8<F16>(braw[ni][0], braw[ni][1]) : ft_fp8x8<F16>(braw[ni][2], braw[ni][3]);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) acc[mi][ni] = mfma32<F16>(af[mi], bfr, acc[mi][ni]);
+      }
+    }
+  }
+}
+
+// Step k = (k - OFF) + OFF of the fp8 K loop, OFF = k mod 12 (fixes the
+// parts and the wait count).  LIVE: k < nk is known; else the products run
+// only while k < nk and the loads are issued before them.
+template <bool F16, bool LD, int OFF, bool LIVE>
+__device__ __forceinline__ void ft_step8(const TileAddr& ta, int k, int nk, ATap& at, uint16_t* const (&pa)[3],
+                                         uint16_t* const (&pw)[2], f32x16 (&acc)[2][4]) {
+  constexpr bool EVEN = (OFF & 1) == 0;
+  constexpr int NLD = EVEN ? FT_A_LD + FT_B_LD : FT_A_LD;  // loads of a loading wave
+  if constexpr (LD) KVX_WAIT_VM(EVEN ? FT_A_LD : FT_A_LD + FT_B_LD);
+  KVX_COMPILER_FENCE();
+  __builtin_amdgcn_s_barrier();
+  KVX_COMPILER_FENCE();
+  const StepLoads sl = ft_step_loads8(ta, k, at, pw[((OFF >> 1) + 1) & 1], pa[(OFF + 2) % 3]);
+  ft_atap_next(ta, at);
+  if constexpr (LIVE) {
+    ft_compute8<F16, LD ? NLD / 4 : 0, OFF & 1>(pa[OFF % 3], pw[(OFF >> 1) & 1], acc, ta, sl);
+  } else {
+    if constexpr (LD)
+      for (int i = 0; i < NLD; ++i) ft_load8<EVEN>(ta, sl, i);
+    if (k < nk) ft_compute8<F16, 0, OFF & 1>(pa[OFF % 3], pw[(OFF >> 1) & 1], acc, ta, sl);
+  }
+}
+
+// fp8 K loop over nk >= 1 steps with A0 in p0, W part 0 in p3 and A1 in p1
+// already issued; whole groups of 12 steps run without branches, the rest
+// as a 12-step tail (loads past the end read an empty range so every wait
+// keeps its count), then the loads in flight are drained.
+template <bool F16, bool LD>
+__device__ __forceinline__ void ft_kloop8(const TileAddr& ta, int nk, uint16_t* p0, uint16_t* p1, uint16_t* p2,
+                                          uint16_t* p3, uint16_t* p4, f32x16 (&acc)[2][4]) {
+  uint16_t* const pa[3] = {p0, p1, p2};
+  uint16_t* const pw[2] = {p3, p4};
+  int k = 0;
+  ATap at = ft_atap_start(ta);
+  for (; k + 12 <= nk; k += 12) {
+    ft_step8<F16, LD, 0, true>(ta, k, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 1, true>(ta, k + 1, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 2, true>(ta, k + 2, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 3, true>(ta, k + 3, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 4, true>(ta, k + 4, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 5, true>(ta, k + 5, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 6, true>(ta, k + 6, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 7, true>(ta, k + 7, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 8, true>(ta, k + 8, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 9, true>(ta, k + 9, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 10, true>(ta, k + 10, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 11, true>(ta, k + 11, nk, at, pa, pw, acc);
+  }
+  if (k < nk) {
+    ft_step8<F16, LD, 0, false>(ta, k, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 1, false>(ta, k + 1, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 2, false>(ta, k + 2, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 3, false>(ta, k + 3, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 4, false>(ta, k + 4, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 5, false>(ta, k + 5, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 6, false>(ta, k + 6, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 7, false>(ta, k + 7, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 8, false>(ta, k + 8, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 9, false>(ta, k + 9, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 10, false>(ta, k + 10, nk, at, pa, pw, acc);
+    ft_step8<F16, LD, 11, false>(ta, k + 11, nk, at, pa, pw, acc);
+  }
+  if constexpr (LD) KVX_WAIT_VM(0);
+}
 
 // Both operand types in one launch: the K loop is chosen per tile.  PLACED:
 // output rows from the slot array and rotary positions per token (else row
@@ -454,18 +550,11 @@ flat_gemm_kernel(const FlatKArgs args) {
       const int32_t srow = args.a_compact[role] ? u : args.uniq[u];
       ta.a_off[i] = 2u * static_cast<uint32_t>(srow * args.send_row + ft_chunk(r, lane & 7) * 8);
     }
-    if constexpr (W8) {
 #pragma unroll
-      for (int i = 0; i < FT_B8_LD; ++i) {
-        const int r = (wave * FT_B8_LD + i) * 16 + (lane >> 2);
-        ta.b_off[i] = static_cast<uint32_t>(r * args.k_dim + ft_chunk8(r, lane & 3) * 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FT_B_LD; ++i) {
-        const int r = (wave * FT_B_LD + i) * FT_ROWS_PER_LD + lrow;
-        ta.b_off[i] = 2u * static_cast<uint32_t>(r * args.k_dim + ft_chunk(r, lane & 7) * 8);
-      }
+    for (int i = 0; i < FT_B_LD; ++i) {
+      // W row r, 16-byte chunk: 8 elements of a 16-bit map, 16 of an fp8 map
+      const int r = (wave * FT_B_LD + i) * FT_ROWS_PER_LD + lrow;
+      ta.b_off[i] = static_cast<uint32_t>(r * args.k_dim * wb + ft_chunk(r, lane & 7) * 16);
     }
 
     // run starts of this wave's two epilogue phases, read now so they have
@@ -482,19 +571,36 @@ flat_gemm_kernel(const FlatKArgs args) {
     // prologue (loading waves): A0, W0 and A1 in flight.  The parts were
     // last used as staging before the final barrier of the previous tile, so
     // they are free.
-    if (wave < FT_LOADERS) {
-      ft_issue_a(ta, 0, p0);
-      ft_issue_b<W8>(ta, 0, p1);
-      ft_issue_a(ta, 1, p2);
-      if (args.a_f16[role])
-        ft_kloop<true, W8, true>(ta, nk, p0, p1, p2, p3, p4, acc);
-      else
-        ft_kloop<false, W8, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+    if constexpr (W8) {
+      if (wave < FT_LOADERS) {
+        ft_issue_a(ta, 0, p0);
+        ft_issue_w8(ta, 0, p3);
+        ft_issue_a(ta, 1, p1);
+        if (args.a_f16[role])
+          ft_kloop8<true, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+        else
+          ft_kloop8<false, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+      } else {
+        if (args.a_f16[role])
+          ft_kloop8<true, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+        else
+          ft_kloop8<false, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+      }
     } else {
-      if (args.a_f16[role])
-        ft_kloop<true, W8, false>(ta, nk, p0, p1, p2, p3, p4, acc);
-      else
-        ft_kloop<false, W8, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+      if (wave < FT_LOADERS) {
+        ft_issue_a(ta, 0, p0);
+        ft_issue_b(ta, 0, p1);
+        ft_issue_a(ta, 1, p2);
+        if (args.a_f16[role])
+          ft_kloop<true, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+        else
+          ft_kloop<false, true>(ta, nk, p0, p1, p2, p3, p4, acc);
+      } else {
+        if (args.a_f16[role])
+          ft_kloop<true, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+        else
+          ft_kloop<false, false>(ta, nk, p0, p1, p2, p3, p4, acc);
+      }
     }
 
     // ------------------------------------------------------------ epilogue
