@@ -1122,6 +1122,46 @@ def test_flat_short_k_all_elements(n_taps, fp32):
 
 
 
+@pytest.mark.parametrize("n_taps,heads", [(1, 2), (2, 2), (3, 2), (2, 4), (5, 2)])
+def test_fp8_short_k_all_elements(n_taps, heads):
+    """fp8 maps over K extents of 4, 8, 12, 16 and 20 steps of 64: K loops
+    that are only a tail, one whole group of twelve steps, and a group
+    followed by a tail (W parts of 128 k serve two steps; the tail's dead
+    steps load empty ranges); rotated keys, every element vs the oracle on
+    the oracle's own quantised maps."""
+    L_S, L_R = 6, 4
+    send_end, recv_end = synth.token_ends(300, 70 + n_taps + heads)
+    shp = synth.CacheShape(L_S, len(send_end), heads, 128)
+    taps = np.stack([np.minimum(kvx.layer_map(L_S, L_R, 1, 1)[:, 0] + t, L_S - 1) for t in range(n_taps)],
+                    axis=1).astype(np.int32)
+    f_in = n_taps * heads * 128
+    say(f"fp8 maps, {n_taps} taps x {heads} heads: K steps {f_in // 64}")
+    tmap_o = O.token_align(send_end, recv_end)
+    caches, q8, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, 9300 + r, DEV)
+        wt, u, v, b = synth.flat_maps(L_R, f_in, 256, 9400 + r, DEV, 4)
+        q, sc = kvx.quantize_fp8(wt)
+        qo, so = O.quantize_fp8(host(wt).numpy())
+        assert np.array_equal(host(q).numpy(), qo)
+        q8[role] = (q, sc, Fp8Maps(qo, so))
+        bias[role] = b
+        del wt, u, v
+    k, v = kvx.translate_fp8(caches["k"], caches["v"], dev_i32(tmap_o), taps, q8["k"][0], q8["v"][0], q8["k"][1],
+                             q8["v"][1], bias["k"], bias["v"], recv_heads=2, recv_head_dim=128,
+                             send_rope_base=5e5, recv_rope_base=1e6)
+    torch.cuda.synchronize()
+    rows = np.arange(tmap_o.size)
+    for role, out in (("k", k), ("v", v)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], tmap_o, taps, q8[role][2], host(bias[role]).numpy().astype(np.float64),
+                                rows, per_head=False, recv_heads=2, recv_head_dim=128,
+                                send_rope_base=5e5 if rk else 0.0, recv_rope_base=1e6 if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  {role}: max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e})")
+        assert err <= TOL_BF16
+
+
 def test_async_align_and_recorded_translate():
     """The entries that do not synchronise: the alignment gives the same map
     and flags invalid offsets on the device; the translation with recorded
