@@ -318,26 +318,38 @@ perhead_kernel(const HeadKArgs a) {
     }
   }
 
-  // tiles 0 .. 4 in flight while the map fragments are prepared
-  ph_issue(pt, 0, ph_rows(pt, 0), x0);
-  ph_issue(pt, 1, ph_rows(pt, 1), x1);
-  ph_issue(pt, 2, ph_rows(pt, 2), x2);
-  ph_issue(pt, 3, ph_rows(pt, 3), x3);
-  ph_issue(pt, 4, ph_rows(pt, 4), x4);
-  // rows of the tile the first step issues, read a step ahead from then on
-  PhRows rr = ph_rows(pt, PH_RING - 1);
+  float bn[16];
+  const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    bn[r] = bias ? bias[ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
 
   // A fragments: rows n = ph_out(wave, lane % 32) of W_{l,h} ([n][c], output
-  // major), k = 16 ks + 8 (lane / 32) .. +8; halves rounded to nearest even
+  // major), k = 16 ks + 8 (lane / 32) .. +8; halves rounded to nearest even.
+  // All map loads are issued before the tiles' loads and converted after
+  // them: one wait covers the map (the counter completes in order), and the
+  // tiles are in flight meanwhile.
   u32x4 wh[8], wl[8];
   const int n_row = ph_out(wave, lane & 31);
   if constexpr (WF32) {
     const float* wp = static_cast<const float*>(a.wt[role]) +
                       ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
+    float4 wu[8], wv[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const float4 u = *reinterpret_cast<const float4*>(wp + 16 * ks);
-      const float4 v = *reinterpret_cast<const float4*>(wp + 16 * ks + 4);
+      wu[ks] = *reinterpret_cast<const float4*>(wp + 16 * ks);
+      wv[ks] = *reinterpret_cast<const float4*>(wp + 16 * ks + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    ph_issue(pt, 0, ph_rows(pt, 0), x0);
+    ph_issue(pt, 1, ph_rows(pt, 1), x1);
+    ph_issue(pt, 2, ph_rows(pt, 2), x2);
+    ph_issue(pt, 3, ph_rows(pt, 3), x3);
+    ph_issue(pt, 4, ph_rows(pt, 4), x4);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float4 u = wu[ks], v = wv[ks];
       const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -359,21 +371,25 @@ perhead_kernel(const HeadKArgs a) {
     const uint16_t* wp = static_cast<const uint16_t*>(a.wt[role]) +
                          ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
 #pragma unroll
+    for (int ks = 0; ks < 8; ++ks) wh[ks] = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
+    __builtin_amdgcn_sched_barrier(0);
+    ph_issue(pt, 0, ph_rows(pt, 0), x0);
+    ph_issue(pt, 1, ph_rows(pt, 1), x1);
+    ph_issue(pt, 2, ph_rows(pt, 2), x2);
+    ph_issue(pt, 3, ph_rows(pt, 3), x3);
+    ph_issue(pt, 4, ph_rows(pt, 4), x4);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
       if constexpr (F16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = cvt_f16x2(bf16lo(w[e]), bf16hi(w[e]));
+        for (int e = 0; e < 4; ++e) wh[ks][e] = cvt_f16x2(bf16lo(wh[ks][e]), bf16hi(wh[ks][e]));
       }
-      wh[ks] = w;
       wl[ks] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  float bn[16];
-  const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    bn[r] = bias ? bias[ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
+  // rows of the tile the first step issues, read a step ahead from then on
+  PhRows rr = ph_rows(pt, PH_RING - 1);
 
   // Step k (tile k in stage k % 6, staging k % 2): the wait leaves the four
   // younger tiles in flight and completes this wave's staging writes, then
