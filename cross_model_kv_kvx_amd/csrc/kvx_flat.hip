@@ -28,9 +28,8 @@
 //     throughput).  While step k is multiplied, W of step k+1 and A of steps
 //     k+1 and k+2 are in flight.  Waves 0..3 (one per SIMD) issue all of a
 //     step's loads and waves 4..7 none: the other wave of each SIMD never
-//     waits behind a queued load issue, and never waits on the vector-memory
-//     counter, so its epilogue stores drain while it already multiplies the
-//     next tile;
+//     waits behind a queued load issue, and waits on the vector-memory
+//     counter only once per tile;
 //   * inside each 128-byte LDS row the 16-byte chunks are XOR-swizzled by
 //     (row / 2) mod 8 so fragment reads of consecutive rows hit distinct
 //     banks;
