@@ -72,11 +72,12 @@ TRACE_FILES = {
     "perhead_kernel": "perhead_kernel__32to80_4k__trace.md",
 }
 # bench.py arguments of the profiled runs of each kernel: the headline step
-# alone, or the per-head workload alone, so every dispatch of the kernel in
-# the profile belongs to the workload the summary names
+# alone (default step counts), or the per-head workload alone, so every
+# dispatch of the kernel in the profile belongs to the workload the summary
+# names; the last field is the number of leading dispatches that are warm-up
 PROFILE_ARGS = {
-    "flat_gemm_kernel": ("flat", "--steps 5 --warmup 1 --no-cpu-baseline --no-also"),
-    "perhead_kernel": ("ph", "--perhead-only"),
+    "flat_gemm_kernel": ("flat", "--no-cpu-baseline --no-also", 3),
+    "perhead_kernel": ("ph", "--perhead-only", 5),
 }
 
 
@@ -150,7 +151,7 @@ def pmc_summary(fetch_csv, write_csv):
         wb = np.array(w[kernel]) * kw
         n = min(fb.size, wb.size)
         tot = fb[:n] + wb[:n]
-        tag, bargs = PROFILE_ARGS[kernel]
+        tag, bargs, _ = PROFILE_ARGS[kernel]
         out[kernel] = (f"# HBM traffic: {kernel}\n\n"
                        f"source hash: `{source_hash(kernel)}`\n\n"
                        "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths "
@@ -171,40 +172,122 @@ def pmc_summary(fetch_csv, write_csv):
     return out
 
 
-def trace_summary(stats_csv, bench_log):
+def trace_summary(trace_dir, bench_log):
     """Markdown summaries of a rocprofv3 --kernel-trace --stats run of one of
-    the profiled commands: the kernel statistics as rocprofv3 wrote them and
-    the live HIP-event launch time that bench.py printed in the same run."""
-    rows = list(csv.DictReader(open(stats_csv)))
+    the profiled commands: per-dispatch durations of the kernel from the
+    kernel trace (warm-up dispatches excluded: mean, median, min), the
+    statistics file as rocprofv3 wrote it, and the live HIP-event launch time
+    that bench.py printed in the same run."""
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))))
     line = next(l for l in open(bench_log) if l.startswith("{"))
     res = json.loads(line)
     out = {}
     for kernel in ("flat_gemm_kernel", "perhead_kernel"):
-        mine = [r for r in rows if f"kvx::{kernel}" in r["Name"]]
-        if not mine:
+        disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+                      if f"kvx::{kernel}" in r["Kernel_Name"])
+        if not disp:
             continue
-        tag, bargs = PROFILE_ARGS[kernel]
-        calls = sum(int(r["Calls"]) for r in mine)
-        total = sum(float(r["TotalDurationNs"]) for r in mine)
+        tag, bargs, skip = PROFILE_ARGS[kernel]
+        dur = np.array([(e - b) / 1e3 for b, e in disp])  # us
+        timed = dur[skip:] if dur.size > skip else dur
         roof = res["roofline"] if kernel == "flat_gemm_kernel" else res["also"]["roofline"]
+        work = roof.get("flops_per_launch") or roof["algorithmic_bytes_per_launch"]
+        scale = 1e12 if roof["unit"] == "TFLOP/s" else 1e9
+        frac_prof = work / (float(np.median(timed)) * 1e-6) / scale / roof["peak"]
         tab = "\n".join(f"| {r['Name'].removeprefix('void ')[:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} |"
-                        for r in rows[:14])
+                        for r in stats[:14])
         out[kernel] = (f"# Kernel trace: {kernel}\n\n"
                        f"source hash: `{source_hash(kernel)}`\n\n"
                        "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths "
                        "relative to the repository), then this summary:\n\n```\n"
                        f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof/{tag}_trace -o trace --output-format csv "
                        f"-- python3 bench.py {bargs} > gpurun_out/prof/{tag}_trace.log\n"
-                       f"python3 bench.py --trace-summary gpurun_out/prof/{tag}_trace/trace_kernel_stats.csv "
-                       f"gpurun_out/prof/{tag}_trace.log\n```\n\n"
-                       "Kernel statistics of the run (all dispatches, input generation and warm-up included; "
-                       "top 14):\n\n| kernel | calls | avg us | min us | max us | % time |\n|---|---|---|---|---|---|\n"
-                       f"{tab}\n\n"
-                       f"{kernel}: {calls} dispatches, mean {total / calls / 1e3:.1f} us per dispatch.\n\n"
-                       f"Same run, live HIP-event timing in bench.py: {roof['launch_ms'] * 1e3:.1f} us per launch "
-                       f"({roof['achieved']:.1f} {roof['unit']} algorithmic, {100 * roof['frac']:.1f}% of "
-                       f"{roof['peak']:.0f}).\n")
+                       f"python3 bench.py --trace-summary gpurun_out/prof/{tag}_trace gpurun_out/prof/{tag}_trace.log\n"
+                       "```\n\n"
+                       f"{kernel}: {dur.size} dispatches; the first {min(skip, dur.size)} are warm-up.\n\n"
+                       f"| dispatches | mean us | median us | min us | max us |\n|---|---|---|---|---|\n"
+                       f"| all {dur.size} | {dur.mean():.1f} | {np.median(dur):.1f} | {dur.min():.1f} | {dur.max():.1f} |\n"
+                       f"| timed {timed.size} | {timed.mean():.1f} | {np.median(timed):.1f} | {timed.min():.1f} | "
+                       f"{timed.max():.1f} |\n\n"
+                       f"Same run, live HIP-event timing in bench.py: {roof['launch_ms'] * 1e3:.1f} us per launch, "
+                       f"{roof['achieved']:.1f} {roof['unit']} algorithmic, frac {roof['frac']:.4f} of "
+                       f"{roof['peak']:.0f}.\n"
+                       f"From the profile's timed median: frac {frac_prof:.4f} "
+                       f"({100 * (frac_prof / roof['frac'] - 1):+.1f}% against the bench line).\n\n"
+                       "Kernel statistics of the run as rocprofv3 wrote them (all dispatches, input generation "
+                       "and warm-up included; top 14):\n\n| kernel | calls | avg us | min us | max us | % time |\n"
+                       f"|---|---|---|---|---|---|\n{tab}\n")
+    return out
+
+
+UNITS_FILES = {
+    "flat_gemm_kernel": "flat_gemm_kernel__crossfamily_rope_32k__units.md",
+    "perhead_kernel": "perhead_kernel__32to80_4k__units.md",
+}
+UNIT_COUNTERS = ("GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+                 "SQ_WAIT_INST_LDS SQ_VMEM_TA_CMD_FIFO_FULL TA_TA_BUSY TA_ADDR_STALLED_BY_TD_CYCLES TD_TD_BUSY "
+                 "TD_TC_STALL")
+
+
+def units_summary(counter_csv, bench_log):
+    """Markdown summaries of one rocprofv3 --pmc run of the unit-activity
+    counters over a profiled command: per-dispatch means, the average clock
+    (GRBM_GUI_ACTIVE is summed over the 8 XCDs), busy fractions per unit, and
+    the matrix-core ceiling at that clock beside the bench line's fraction of
+    the published peak (which assumes 2.4 GHz)."""
+    rows = list(csv.DictReader(open(counter_csv)))
+    line = next(l for l in open(bench_log) if l.startswith("{"))
+    res = json.loads(line)
+    out = {}
+    for kernel in ("flat_gemm_kernel", "perhead_kernel"):
+        mine = [r for r in rows if kernel in r["Kernel_Name"]]
+        if not mine:
+            continue
+        tag, bargs, skip = PROFILE_ARGS[kernel]
+        per = {}
+        for r in mine:
+            per.setdefault(r["Counter_Name"], {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+            per[r["Counter_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        ids = sorted(per["GRBM_GUI_ACTIVE"])
+        timed = ids[skip:] if len(ids) > skip else ids
+        mean = {c: float(np.mean([v[i] for i in timed if i in v])) for c, v in per.items()}
+        roof = res["roofline"] if kernel == "flat_gemm_kernel" else res["also"]["roofline"]
+        t_s = roof["launch_ms"] * 1e-3
+        cyc = mean["GRBM_GUI_ACTIVE"] / 8.0
+        mhz = cyc / t_s / 1e6
+        lines = [f"| {c} | {v:.4g} |" for c, v in sorted(mean.items())]
+        frac = [f"cycles per XCD (GRBM_GUI_ACTIVE / 8): {cyc:.4g} over the bench's launch time "
+                f"{roof['launch_ms'] * 1e3:.1f} us -> {mhz:.0f} MHz average clock"]
+        for c, units in (("SQ_VALU_MFMA_BUSY_CYCLES", 1024), ("TA_TA_BUSY", 256), ("TD_TD_BUSY", 256),
+                         ("TD_TC_STALL", 256), ("SQ_LDS_IDX_ACTIVE", 256), ("SQ_LDS_BANK_CONFLICT", 256),
+                         ("SQ_VMEM_TA_CMD_FIFO_FULL", 256), ("SQ_BUSY_CU_CYCLES", 256)):
+            if c in mean:
+                frac.append(f"{c} per unit ({units} units): {mean[c] / units:.4g} cycles = "
+                            f"{mean[c] / units / cyc:.3f} of the cycles")
+        if roof["unit"] == "TFLOP/s":
+            ceil = roof["peak"] * mhz / 2400.0
+            frac.append(f"matrix-core ceiling at the measured clock: {roof['peak']:.0f} x {mhz:.0f} / 2400 = "
+                        f"{ceil:.0f} TFLOP/s; the launch reaches {roof['achieved']:.1f} TFLOP/s = "
+                        f"{roof['achieved'] / ceil:.3f} of it (bench frac {roof['frac']:.4f} of the published "
+                        f"{roof['peak']:.0f})")
+        out[kernel] = (f"# Unit activity: {kernel}\n\n"
+                       f"source hash: `{source_hash(kernel)}`\n\n"
+                       "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths "
+                       "relative to the repository), then this summary:\n\n```\n"
+                       f"rocprofv3 --pmc {UNIT_COUNTERS} -d gpurun_out/prof/{tag}_units -o units "
+                       f"--output-format csv -- python3 bench.py {bargs} > gpurun_out/prof/{tag}_units.log\n"
+                       f"python3 bench.py --units-summary gpurun_out/prof/{tag}_units/units_counter_collection.csv "
+                       f"gpurun_out/prof/{tag}_units.log\n```\n\n"
+                       f"Values: each counter summed over its instances per dispatch, mean over the "
+                       f"{len(timed)} timed dispatches (the first {min(skip, len(ids))} are warm-up).  Fractions "
+                       "assume each counter is summed over its units: GRBM_GUI_ACTIVE over 8 XCDs, "
+                       "SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs, the TA, TD and per-CU SQ counters over 256 CUs; "
+                       "each is divided by the cycles per XCD.  Launch times under counter collection are not "
+                       "used; the clock uses the same run's HIP-event launch time.\n\n"
+                       "| counter | mean per dispatch |\n|---|---|\n" + "\n".join(lines) + "\n\n"
+                       + "\n".join(f"- {f}" for f in frac) + "\n")
     return out
 
 
@@ -263,16 +346,24 @@ def cold_measure(dev, x, taps, ws, outs, steps=10):
             "gemm_ms": float(np.median(gemm_ms)), "steps": steps}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, target_s=15.0):
     """The oracle as it stands on a bounded sample: token alignment of the
     whole string plus translation of sampled receiver rows (all layers, K
-    and V), with maps folded by the oracle (untimed setup)."""
+    and V), with maps folded by the oracle (untimed setup).  Timed on one
+    host core: the process is pinned to a single CPU and numpy's BLAS pool
+    limited to one thread for the timed part."""
     from oracle import kvx_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the process CPU count
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_limits
     wo = {}
     for role in ("k", "v"):
         wt, u, v = (t.cpu().numpy() for t in x[f"fold_{role}"])
@@ -282,25 +373,36 @@ def cpu_baseline(x, target_s=15.0):
     taps = O.layer_taps(36, 32, 3, 4)
     n_recv = x["recv_end_h"].size
     rng = np.random.default_rng(0)
-    rows_done, t_total, n = 0, 0.0, 64
-    t0 = time.perf_counter()
-    tmap = O.token_align(x["send_end_h"], x["recv_end_h"])
-    t_align = time.perf_counter() - t0
-    while t_total < target_s and rows_done < n_recv:
-        rows = np.sort(rng.choice(n_recv, size=n, replace=False))
-        t0 = time.perf_counter()
-        for role in ("k", "v"):
-            O.translate_rows(caches[role], tmap, taps, wo[role], bo[role], rows, per_head=False,
-                             recv_heads=8, recv_head_dim=128, send_rope_base=5e5 if role == "k" else 0.0,
-                             recv_rope_base=1e6 if role == "k" else 0.0)
-        t_total += time.perf_counter() - t0
-        rows_done += n
+    rows_done, t_total, n = 0, 0.0, 16
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    torch_threads = torch.get_num_threads()
+    os.sched_setaffinity(0, {core})
+    torch.set_num_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            tmap = O.token_align(x["send_end_h"], x["recv_end_h"])
+            t_align = time.perf_counter() - t0
+            while t_total < target_s and rows_done < n_recv:
+                rows = np.sort(rng.choice(n_recv, size=n, replace=False))
+                t0 = time.perf_counter()
+                for role in ("k", "v"):
+                    O.translate_rows(caches[role], tmap, taps, wo[role], bo[role], rows, per_head=False,
+                                     recv_heads=8, recv_head_dim=128, send_rope_base=5e5 if role == "k" else 0.0,
+                                     recv_rope_base=1e6 if role == "k" else 0.0)
+                t_total += time.perf_counter() - t0
+                rows_done += n
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+        torch.set_num_threads(torch_threads)
     per_row = t_total / rows_done
     step_s = t_align + per_row * n_recv
-    return {"value": n_recv / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": n_recv / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpus_allowed": len(allowed), "cpu_model": cpu_model(), "pinned_core": core,
             "sample": f"token alignment of all {n_recv} receiver tokens ({t_align:.3f} s) + translation of "
                       f"{rows_done} random receiver rows x 32 layers x K,V ({t_total:.1f} s), scaled to "
-                      f"{n_recv} rows"}
+                      f"{n_recv} rows; one core (process pinned, BLAS limited to one thread)"}
 
 
 def perhead_measure(dev, steps=10, rope=False):
@@ -349,12 +451,14 @@ def perhead_measure(dev, steps=10, rope=False):
     # algorithmic bytes: each sender row read once, each receiver row written
     # once, maps (fp32) and bias read once
     bytes_alg = 2 * (32 * 4096 * 1024 * 2 + 80 * 4096 * 1024 * 2 + 80 * 8 * 128 * 128 * 4 + 80 * 1024 * 4)
+    traffic = committed_traffic("perhead_kernel") if not rope else None
     return {"workload": "per-head 32->80 layers, 4096 tokens, 8x128 heads, fp32 maps, bf16 caches"
                         + (", keys rotated (RoPE 5e5 -> 1e6)" if rope else ""),
             "tokens_per_s": 4096 / t_call, "call_ms": t_call * 1e3, "kernel_ms": t * 1e3,
             "prep_ms": float(np.mean(prep)),
             "roofline": {"bound": "hbm", "achieved": bytes_alg / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": bytes_alg / t / 1e9 / PEAK_HBM_GBS, "traffic": committed_traffic("perhead_kernel"),
+                         "frac": bytes_alg / t / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
+                         "traffic_over_algorithmic": None if traffic is None else traffic / bytes_alg,
                          "kernel": "perhead_kernel", "launch_ms": t * 1e3, "algorithmic_bytes_per_launch": bytes_alg}}
 
 
@@ -554,16 +658,21 @@ def main():
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
-    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"))
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
+    ap.add_argument("--units-summary", nargs=2, metavar=("COUNTER_CSV", "BENCH_LOG"))
     ap.add_argument("--fp8-only", action="store_true", help="measure the fp8-map translation alone")
     ap.add_argument("--fit-only", action="store_true",
                     help="measure the ridge and Recolor fits of the calibration setting alone")
     ap.add_argument("--perhead-only", action="store_true",
                     help="measure the per-head workload alone (profiling runs of the per-head kernel)")
     args = ap.parse_args()
-    if args.pmc_summary or args.trace_summary:
-        made = pmc_summary(*args.pmc_summary) if args.pmc_summary else trace_summary(*args.trace_summary)
-        files = TRAFFIC_FILES if args.pmc_summary else TRACE_FILES
+    if args.pmc_summary or args.trace_summary or args.units_summary:
+        if args.pmc_summary:
+            made, files = pmc_summary(*args.pmc_summary), TRAFFIC_FILES
+        elif args.trace_summary:
+            made, files = trace_summary(*args.trace_summary), TRACE_FILES
+        else:
+            made, files = units_summary(*args.units_summary), UNITS_FILES
         for kernel, text in made.items():
             path = os.path.join(PROFILES, files[kernel])
             with open(path, "w") as fh:
@@ -639,9 +748,12 @@ def main():
     launch_ms = gemm_ms / launches
     flops = 2.0 * U * 3072 * 1024 * 32 * 2
     achieved = flops / (launch_ms * 1e-3) / 1e12
-    # algorithmic bytes of a launch: unique sender rows of the 3 taps, maps,
-    # bias, and every receiver row written once, both roles
-    bytes_alg = 2 * 32 * (3 * U * 2048 + 3072 * 1024 * 2 + 1024 * 4 + N_R * 2048)
+    # algorithmic bytes of a launch, both roles: the U distinct sender rows of
+    # every sender layer the taps reference read once, the maps and bias read
+    # once, every receiver row written once
+    used_layers = len(set(int(t) for t in np.asarray(taps).ravel()))
+    bytes_alg = 2 * (used_layers * U * 2048 + 32 * (3072 * 1024 * 2 + 1024 * 4) + 32 * N_R * 2048)
+    traffic = committed_traffic("flat_gemm_kernel")
     res = {
         "metric": "translated KV tokens/sec (all layers, K+V) at 32k ctx; % of MFMA/HBM roofline",
         "value": N_R / (ms_step * 1e-3),
@@ -660,9 +772,13 @@ def main():
                    "recv_tokens": N_R, "send_tokens": int(x["send_end_h"].size), "distinct_sender_rows": U,
                    "global_batch": 1, "seq_len": N_R, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": committed_traffic("flat_gemm_kernel"),
+                     "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "flat_gemm_kernel", "launches_per_step": launches, "launch_ms": launch_ms,
-                     "flops_per_launch": flops, "algorithmic_bytes_per_launch": bytes_alg, "prep_ms": prep_ms},
+                     "launch_ms_median": float(np.median([s[1] for s in stages])),
+                     "launch_ms_min": float(np.min([s[1] for s in stages])),
+                     "flops_per_launch": flops, "algorithmic_bytes_per_launch": bytes_alg,
+                     "traffic_over_algorithmic": None if traffic is None else traffic / bytes_alg,
+                     "prep_ms": prep_ms},
     }
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")

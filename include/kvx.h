@@ -183,6 +183,14 @@ int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps,
  * from a rotated sender are fed as fp16 (the map converted to, or split
  * into, fp16), other bf16 rows as bf16; fp32 caches use fp32 arithmetic.
  * Accumulation is fp32 everywhere.
+ * Range of the fp16 operands (rotated keys only): fp16 holds magnitudes up
+ * to 65504 with 11 significant bits down to 2^-14 (about 6.1e-5).  Rotated-
+ * back key values and key-map entries (bf16 maps converted to fp16, the high
+ * part of a split fp32 map) beyond 65504 become infinities in the result;
+ * nothing checks for them.  Smaller entries are kept as fp16 subnormals with
+ * an absolute error of at most 2^-25 (bf16 maps) or below 2^-25 after the
+ * low part (fp32 maps).  bf16 rows and maps (values, unrotated keys) have
+ * bf16's range.
  * Supported: recv->dtype == send->dtype; bf16 caches need head_dim == 128
  * on both sides; recv->k_norm only on the flattened bf16 path
  * (KVX_ERR_UNSUPPORTED otherwise).
@@ -281,7 +289,9 @@ int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const v
  * Guidelines": lambda in [1e-4, 1e-2]).
  *
  * x: device [n_rows][f_in] with row stride ldx elements; y: device
- *   [n_rows][f_out] with row stride ldy; both of in_dtype.
+ *   [n_rows][f_out] with row stride ldy; both of in_dtype.  bf16 rows are
+ *   read in 16-byte pieces: f_in, f_out, ldx and ldy must be multiples of 8
+ *   and x, y 16-byte aligned (KVX_ERR_UNSUPPORTED otherwise).
  * lambda = lambda_abs + lambda_rel * trace(G) / f_in, where G = X^T X (or the
  *   centred Gram when fit_intercept != 0).
  * fit_intercept != 0: the bias is unpenalised; X and Y are centred by their
@@ -338,6 +348,7 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
 int kvx_align_tokens_async(const int32_t* send_end, int32_t n_send, const int32_t* recv_end,
                            int32_t n_recv, int32_t* recv_to_send, int32_t* invalid,
                            void* workspace, size_t ws_bytes, void* stream);
+
 
 /* ------------------------------------------------------------------------
  * kvx_translate recording three caller-created events (hipEvent_t, passed
