@@ -109,6 +109,8 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
 
 using namespace kvx;
 
+static_assert(KVX_NOALLOC_MAX_RECV == NOALLOC_MAX_RECV, "header and library limits of the no-allocation alignment");
+
 extern "C" {
 
 const char* kvx_status_string(int status) {
@@ -147,6 +149,17 @@ int kvx_align_tokens_async(const int32_t* send_end, int32_t n_send, const int32_
   if (!workspace || ws_bytes < kvx_align_workspace_size(n_recv)) return KVX_ERR_WORKSPACE;
   return launch_align_async(send_end, n_send, recv_end, n_recv, recv_to_send, invalid, workspace,
                             static_cast<hipStream_t>(stream));
+}
+
+int kvx_align_tokens_noalloc(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                             int32_t* recv_to_send, int32_t* invalid, void* stream) {
+  if (n_send < 0 || n_recv < 0) return KVX_ERR_INVALID;
+  if (n_recv > KVX_NOALLOC_MAX_RECV) return KVX_ERR_WORKSPACE;
+  if (n_recv == 0) return KVX_OK;
+  if (n_send == 0) return KVX_ERR_SHAPE;
+  if (!send_end || !recv_end || !recv_to_send || !invalid) return KVX_ERR_INVALID;
+  return launch_align_noalloc(send_end, n_send, recv_end, n_recv, recv_to_send, invalid,
+                              static_cast<hipStream_t>(stream));
 }
 
 size_t kvx_align_batched_workspace_size(const int32_t* recv_off, int32_t n_seq) {

@@ -19,6 +19,7 @@
 // state): uniq[u] = value of run u, run_begin[u] = first receiver row of run
 // u (run_begin[U] = N), recv_to_uniq[i] = run of row i, and U.
 
+#include <mutex>
 #include <vector>
 
 #include "kvx_align.hpp"
@@ -193,6 +194,42 @@ int launch_align_async(const int32_t* send_end, int32_t n_send, const int32_t* r
   Carve c(ws);
   (void)c.take<int32_t>(64);  // same layout as the synchronous call
   int32_t* agg = c.take<int32_t>(ceil_div(n_recv > 0 ? n_recv : 1, SCAN_TILE));
+  if (int st = launch_fill_i32(invalid, 1, 0, s)) return st;
+  return align_one(send_end, n_send, recv_end, n_recv, out, 0, agg, invalid, s);
+}
+
+// ---------------------------------------------------------------- alignment without allocation
+// The scan's tile aggregates of the no-allocation entry live in a file-scope
+// device array.  Each device holds its own copy at its own address, found
+// once per device with hipGetSymbolAddress; host code never passes the
+// array's name itself (a host-side stand-in) to a kernel.  Every call on a
+// device shares that device's copy: calls that overlap on one device race.
+// The aggregates are written in full by the first kernel of each call before
+// they are read, so nothing needs clearing between calls.
+static __device__ __align__(256) int32_t scratch[NOALLOC_MAX_RECV / SCAN_TILE];
+
+static int scratch_ptr(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* ptr[64] = {nullptr};
+  int dev = -1;
+  KVX_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return KVX_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    KVX_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return KVX_ERR_HIP;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptr[dev];
+  return KVX_OK;
+}
+
+int launch_align_noalloc(const int32_t* send_end, int32_t n_send, const int32_t* recv_end, int32_t n_recv,
+                         int32_t* out, int32_t* invalid, hipStream_t s) {
+  if (n_recv > NOALLOC_MAX_RECV) return KVX_ERR_WORKSPACE;
+  int32_t* agg = nullptr;
+  if (int st = scratch_ptr(&agg)) return st;
   if (int st = launch_fill_i32(invalid, 1, 0, s)) return st;
   return align_one(send_end, n_send, recv_end, n_recv, out, 0, agg, invalid, s);
 }

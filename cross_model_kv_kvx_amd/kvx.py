@@ -31,6 +31,7 @@ EXPORTS = (
     "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fit_ridge_batched_workspace_size",
     "kvx_fit_ridge_batched", "kvx_fit_recolor_workspace_size", "kvx_fit_recolor", "kvx_fold_lowrank",
     "kvx_quantize_fp8", "kvx_translate_fp8", "kvx_align_tokens_async", "kvx_translate_recorded",
+    "kvx_align_tokens_noalloc",
 )
 
 
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
             "kvx_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
             "kvx_align_tokens_async": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, vp, sz, vp]),
+            "kvx_align_tokens_noalloc": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, vp]),
             "kvx_translate_recorded": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp,
                                                       vp, vp, sz, vp, vpp]),
             "kvx_translate_fp8": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, vp, vp, vp, vp, vp, vp, vp,
@@ -182,6 +184,23 @@ def align_tokens(send_end: torch.Tensor, recv_end: torch.Tensor, out: Optional[t
     st = lib().kvx_align_tokens(_ptr(send_end), send_end.numel(), _ptr(recv_end), n_r, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream))
     _check(st, "kvx_align_tokens")
+    return out
+
+
+def align_tokens_noalloc(send_end: torch.Tensor, recv_end: torch.Tensor, out: torch.Tensor,
+                         invalid: torch.Tensor, stream=None) -> torch.Tensor:
+    """kvx_align_tokens_noalloc: the asynchronous alignment with the library's
+    static scratch; ``out`` (device int32 [n_recv]) and ``invalid`` (device
+    int32, one element) are the caller's, nothing is allocated."""
+    _need(send_end, "send_end", torch.int32)
+    _need(recv_end, "recv_end", torch.int32)
+    _need(out, "out", torch.int32)
+    _need(invalid, "invalid", torch.int32)
+    if out.numel() != recv_end.numel():
+        raise ValueError("out must have one entry per receiver token")
+    st = lib().kvx_align_tokens_noalloc(_ptr(send_end), send_end.numel(), _ptr(recv_end), recv_end.numel(),
+                                        _ptr(out), _ptr(invalid), _stream(stream))
+    _check(st, "kvx_align_tokens_noalloc")
     return out
 
 

@@ -349,6 +349,25 @@ int kvx_align_tokens_async(const int32_t* send_end, int32_t n_send, const int32_
                            int32_t n_recv, int32_t* recv_to_send, int32_t* invalid,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * kvx_align_tokens_async for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument, and the call allocates nothing.  Its scratch (the
+ * scan's per-tile aggregates) is a static device array of the library,
+ * 64 KiB per device, held until the process ends; its address on each device
+ * is looked up once, on the first call there.
+ *
+ * Arguments, result and the device-side validity flag as
+ * kvx_align_tokens_async.  n_recv > KVX_NOALLOC_MAX_RECV returns
+ * KVX_ERR_WORKSPACE before anything is launched.  All calls on one device
+ * share its scratch: calls that overlap on one device (different streams
+ * without ordering) race and must not be issued; calls in stream order may
+ * follow each other freely (nothing carries over between calls).
+ * Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+#define KVX_NOALLOC_MAX_RECV (1 << 24)
+int kvx_align_tokens_noalloc(const int32_t* send_end, int32_t n_send, const int32_t* recv_end,
+                             int32_t n_recv, int32_t* recv_to_send, int32_t* invalid, void* stream);
 
 /* ------------------------------------------------------------------------
  * kvx_translate recording three caller-created events (hipEvent_t, passed
