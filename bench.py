@@ -300,27 +300,45 @@ def flat_inputs(dev):
     for r, role in enumerate(("k", "v")):
         x[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, dev, outlier_frac=0.01, outlier_scale=20.0,
                                                outlier_pairs=(role == "k"))
-        wt, u, v, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, dev, 16)
-        x[f"fold_{role}"] = (wt, u, v)
-        x[f"wt_{role}"] = kvx.fold_lowrank(wt, u, v, torch.bfloat16)
+        w, a, b_lr, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, dev, 16)
+        x[f"fold_{role}"] = (w, a, b_lr)
+        x[f"w_{role}"] = kvx.fold_lowrank(w, a, b_lr, torch.bfloat16)
         x[f"b_{role}"] = b
     x["send_end"] = torch.as_tensor(send_end, device=dev)
     x["recv_end"] = torch.as_tensor(recv_end, device=dev)
     x["send_end_h"], x["recv_end_h"] = send_end, recv_end
     x["shp"] = shp
+    # the maps put once into the kernel layout (untimed, as a server would
+    # when it loads a model pair): fp16 for the rotated-back keys, bf16 values
+    x["send_desc"] = kvx.cache_desc(x["k_send"], 5e5)
+    x["recv_desc"] = kvx.CacheDesc(32, len(recv_end), 8, 128, kvx.BF16, 1e6)
+    for role in ("k", "v"):
+        x[f"p_{role}"] = kvx.prepare_maps(x[f"w_{role}"], role, x["send_desc"], x["recv_desc"], 3)
+    torch.cuda.synchronize()
     return x
 
 
-def run_step(x, taps, ws, outs, stage_ms=None, events=None):
-    """One step: alignment + translation.  With ``events`` (three recorded
-    torch.cuda.Event) nothing synchronises: the alignment leaves its validity
-    flag on the device and the translation records the phase events."""
-    inv = outs["invalid"] if events is not None else None
-    tmap = kvx.align_tokens(x["send_end"], x["recv_end"], out=outs["map"], workspace=outs["align_ws"], invalid=inv)
-    kvx.translate(x["k_send"], x["v_send"], tmap, taps, x["wt_k"], x["wt_v"], x["b_k"], x["b_v"],
+def run_step(x, taps, ws, outs, events=None):
+    """One step: alignment + translation with the prepared maps.  Nothing
+    synchronises: the alignment leaves its validity flag on the device; with
+    ``events`` (three recorded torch.cuda.Event) the translation records the
+    phase events."""
+    tmap = kvx.align_tokens(x["send_end"], x["recv_end"], out=outs["map"], workspace=outs["align_ws"],
+                            invalid=outs["invalid"])
+    kvx.translate(x["k_send"], x["v_send"], tmap, taps, x["p_k"], x["p_v"], x["b_k"], x["b_v"],
                   send_rope_base=5e5, recv_rope_base=1e6, k_recv=outs["k"], v_recv=outs["v"], workspace=ws,
-                  stage_ms=stage_ms, events=events)
+                  events=events, prepared=True, w_dtype=kvx.BF16)
     return tmap
+
+
+def new_events(n):
+    """n trios of timing events, each recorded once (so they exist)."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for trio in evs:
+        for e in trio:
+            e.record()
+    torch.cuda.synchronize()
+    return evs
 
 
 def cold_measure(dev, x, taps, ws, outs, steps=10):
@@ -329,15 +347,15 @@ def cold_measure(dev, x, taps, ws, outs, steps=10):
     timed alone (median over steps)."""
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     step_ms, gemm_ms = [], []
-    for _ in range(steps):
+    evs = new_events(steps)
+    for i in range(steps):
         scratch.fill_(1)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        st = []
-        run_step(x, taps, ws, outs, stage_ms=st)
+        run_step(x, taps, ws, outs, events=evs[i])
         torch.cuda.synchronize()
         step_ms.append((time.perf_counter() - t0) * 1e3)
-        gemm_ms.append(st[1])
+        gemm_ms.append(evs[i][1].elapsed_time(evs[i][2]))
     del scratch
     n_r = x["recv_end_h"].size
     t = float(np.median(step_ms))
@@ -407,55 +425,52 @@ def cpu_baseline(x, target_s=15.0):
 
 def perhead_measure(dev, steps=10, rope=False):
     """Per-head workload: sender 32 layers, receiver 80, 4096 tokens,
-    8 x 128 heads, fp32 128 x 128 maps, identity token map.  With ``rope``
-    the keys are stored rotated on both sides (bases 5e5 and 1e6): the
-    preparation rotates the sender keys back into fp16 rows first."""
+    8 x 128 heads, fp32 128 x 128 maps (prepared once), identity token map.
+    With ``rope`` the keys are stored rotated on both sides (bases 5e5 and
+    1e6): the preparation rotates the sender keys back into fp16 rows first.
+    Calls run back to back on the stream; each records its phase events."""
     shp = synth.CacheShape(32, 4096, 8, 128)
     x = {}
+    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
+    send = kvx.CacheDesc(32, 4096, 8, 128, kvx.BF16, kw.get("send_rope_base", 0.0))
+    recv = kvx.CacheDesc(80, 4096, 8, 128, kvx.BF16, kw.get("recv_rope_base", 0.0))
     for r, role in enumerate(("k", "v")):
         x[f"{role}_send"] = synth.sender_cache(shp, 200 + r, dev, channel_scale="loguniform")
-        x[f"wt_{role}"], x[f"b_{role}"] = synth.perhead_maps(80, 8, 128, 220 + r, dev)
+        w, x[f"b_{role}"] = synth.perhead_maps(80, 8, 128, 220 + r, dev)
+        x[f"p_{role}"] = kvx.prepare_maps(w, role, send, recv, 1, per_head=True)
+        del w
     taps = kvx.layer_map(32, 80, 1)
     ident = torch.arange(4096, dtype=torch.int32, device=dev)
     k = torch.empty((80, 4096, 8, 128), dtype=torch.bfloat16, device=dev)
     v = torch.empty_like(k)
-    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
-    ws = torch.empty(kvx.translate_workspace_size(kvx.cache_desc(x["k_send"], kw.get("send_rope_base", 0.0)),
-                                                  kvx.CacheDesc(80, 4096, 8, 128, kvx.BF16,
-                                                                kw.get("recv_rope_base", 0.0)), 1, True),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvx.lib().kvx_translate_prepared_workspace_size(send, recv, 1, 1, 0), dtype=torch.uint8,
+                     device=dev)
 
-    def call(st=None):
-        kvx.translate(x["k_send"], x["v_send"], ident, taps, x["wt_k"], x["wt_v"], x["b_k"], x["b_v"],
-                      per_head=True, k_recv=k, v_recv=v, workspace=ws, stage_ms=st, **kw)
+    def call(ev=None):
+        kvx.translate(x["k_send"], x["v_send"], ident, taps, x["p_k"], x["p_v"], x["b_k"], x["b_v"],
+                      per_head=True, k_recv=k, v_recv=v, workspace=ws, events=ev, prepared=True,
+                      w_dtype=kvx.F32, **kw)
 
-    # preparation share from synchronous calls timed by stage, then the
-    # calls back to back on the stream (HIP events around them)
-    prep = []
-    for i in range(3):
-        st = []
-        call(st)
-        if i:
-            prep.append(st[0])
-    for _ in range(2):
+    for _ in range(5):
         call()
+    evs = new_events(steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(steps):
-        call()
+    for i in range(steps):
+        call(evs[i])
     e1.record()
     torch.cuda.synchronize()
     t_call = e0.elapsed_time(e1) / steps * 1e-3
-    t = t_call - float(np.mean(prep)) * 1e-3
+    prep_ms = float(np.mean([t[0].elapsed_time(t[1]) for t in evs]))
+    t = float(np.mean([t[1].elapsed_time(t[2]) for t in evs])) * 1e-3
     # algorithmic bytes: each sender row read once, each receiver row written
     # once, maps (fp32) and bias read once
     bytes_alg = 2 * (32 * 4096 * 1024 * 2 + 80 * 4096 * 1024 * 2 + 80 * 8 * 128 * 128 * 4 + 80 * 1024 * 4)
     traffic = committed_traffic("perhead_kernel") if not rope else None
     return {"workload": "per-head 32->80 layers, 4096 tokens, 8x128 heads, fp32 maps, bf16 caches"
                         + (", keys rotated (RoPE 5e5 -> 1e6)" if rope else ""),
-            "tokens_per_s": 4096 / t_call, "call_ms": t_call * 1e3, "kernel_ms": t * 1e3,
-            "prep_ms": float(np.mean(prep)),
+            "tokens_per_s": 4096 / t_call, "call_ms": t_call * 1e3, "kernel_ms": t * 1e3, "prep_ms": prep_ms,
             "roofline": {"bound": "hbm", "achieved": bytes_alg / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": bytes_alg / t / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
                          "traffic_over_algorithmic": None if traffic is None else traffic / bytes_alg,
@@ -464,38 +479,42 @@ def perhead_measure(dev, steps=10, rope=False):
 
 def flat_setting_measure(dev, n_recv, seed, rope, fp32_maps, steps=8, key_norm=False):
     """A flattened setting other than the headline one: translation of all
-    32 receiver layers, K and V, from 36 sender layers with three taps
-    (with ``key_norm``, the receiver's key normalisation in the epilogue)."""
+    32 receiver layers, K and V, from 36 sender layers with three taps, maps
+    prepared once (with ``key_norm``, the receiver's key normalisation in the
+    epilogue).  Each call is synchronised and timed alone."""
     send_end, recv_end = synth.token_ends(n_recv, seed)
     shp = synth.CacheShape(36, len(send_end), 8, 128)
+    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
+    send = kvx.CacheDesc(36, len(send_end), 8, 128, kvx.BF16, kw.get("send_rope_base", 0.0))
+    recv = kvx.CacheDesc(32, n_recv, 8, 128, kvx.BF16, kw.get("recv_rope_base", 0.0))
     x = {}
     for r, role in enumerate(("k", "v")):
         x[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, dev, outlier_frac=0.01 if rope else 0.0,
                                                outlier_scale=20.0 if rope else 1.0, outlier_pairs=(rope and role == "k"))
-        wt, u, v, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, dev, 16)
-        x[f"wt_{role}"] = wt if fp32_maps else kvx.fold_lowrank(wt, u, v, torch.bfloat16)
+        w, a, b_lr, b = synth.flat_maps(32, 3072, 1024, seed * 100 + 20 + r, dev, 16)
+        w = w if fp32_maps else kvx.fold_lowrank(w, a, b_lr, torch.bfloat16)
+        x[f"p_{role}"] = kvx.prepare_maps(w, role, send, recv, 3)
         x[f"b_{role}"] = b
-        del u, v
+        del w, a, b_lr
     taps = kvx.layer_map(36, 32, 3, 4)
     tmap = kvx.align_tokens(torch.as_tensor(send_end, device=dev), torch.as_tensor(recv_end, device=dev))
     m = tmap.cpu().numpy()
     U = int(1 + np.count_nonzero(np.diff(m)))
-    kw = dict(send_rope_base=5e5, recv_rope_base=1e6) if rope else {}
     if key_norm:
         kw["recv_key_norm"] = synth.key_norm_weights(32, 128, seed * 100 + 30, dev)
     outs = {"k_recv": torch.empty((32, n_recv, 8, 128), dtype=torch.bfloat16, device=dev)}
     outs["v_recv"] = torch.empty_like(outs["k_recv"])
     ms, gm = [], []
+    evs = new_events(steps + 2)
     for i in range(steps + 2):
-        st = []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        kvx.translate(x["k_send"], x["v_send"], tmap, taps, x["wt_k"], x["wt_v"], x["b_k"], x["b_v"], stage_ms=st,
-                      **kw, **outs)
+        kvx.translate(x["k_send"], x["v_send"], tmap, taps, x["p_k"], x["p_v"], x["b_k"], x["b_v"], events=evs[i],
+                      prepared=True, w_dtype=kvx.F32 if fp32_maps else kvx.BF16, **kw, **outs)
         torch.cuda.synchronize()
         if i >= 2:
             ms.append((time.perf_counter() - t0) * 1e3)
-            gm.append(st[1])
+            gm.append(evs[i][1].elapsed_time(evs[i][2]))
     t_gemm = float(np.mean(gm))
     flops = 2.0 * U * 3072 * 1024 * 32 * 2  # algorithmic (fp32 maps execute twice: high and low halves)
     return {"workload": f"flattened{' + RoPE' if rope else ''}{' + receiver key norm' if key_norm else ''}, "
@@ -532,7 +551,7 @@ def fit_measure(dev, xs, ys, reps=2):
     call, lambda = 1e-3 tr(G)/3072; and one problem alone for comparison."""
     n = xs[0].shape[0]
     count = len(xs)
-    w_outs = [torch.empty((1024, 3072), dtype=torch.float32, device=dev) for _ in range(count)]
+    w_outs = [torch.empty((3072, 1024), dtype=torch.float32, device=dev) for _ in range(count)]
 
     def timed(c):
         ws = torch.empty(kvx.lib().kvx_fit_ridge_batched_workspace_size(c, 3072, 1024), dtype=torch.uint8,
@@ -615,7 +634,7 @@ def recolor_measure(dev, xs, ys, reps=2):
     call: 64 problems of 65536 rows, 3072 -> 1024, rho_x = 1e-3."""
     n, count = xs[0].shape[0], len(xs)
     fi, fo = 3072, 1024
-    w_outs = [torch.empty((fo, fi), dtype=torch.float32, device=dev) for _ in range(count)]
+    w_outs = [torch.empty((fi, fo), dtype=torch.float32, device=dev) for _ in range(count)]
     b_outs = [torch.empty(fo, dtype=torch.float32, device=dev) for _ in range(count)]
     ws = torch.empty(kvx.lib().kvx_fit_recolor_workspace_size(count, fi, fo), dtype=torch.uint8, device=dev)
     ms, info, st = [], {}, []
@@ -708,9 +727,8 @@ def main():
     x = flat_inputs(dev)
     taps = kvx.layer_map(36, 32, 3, 4)
     N_R = x["recv_end_h"].size
-    send = kvx.cache_desc(x["k_send"], 5e5)
-    recv = kvx.CacheDesc(32, N_R, 8, 128, kvx.BF16, 1e6)
-    ws = torch.empty(kvx.translate_workspace_size(send, recv, 3, False), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvx.lib().kvx_translate_prepared_workspace_size(x["send_desc"], x["recv_desc"], 3, 0, 0),
+                     dtype=torch.uint8, device=dev)
     outs = {"map": torch.empty(N_R, dtype=torch.int32, device=dev),
             "align_ws": torch.empty(kvx.lib().kvx_align_workspace_size(N_R), dtype=torch.uint8, device=dev),
             "k": torch.empty((32, N_R, 8, 128), dtype=torch.bfloat16, device=dev)}
@@ -722,11 +740,7 @@ def main():
     # HIP events of every timed step (before the preparation kernels, before
     # and after the translation kernel), recorded on the launch stream by the
     # library; created by one record each before timing
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for trio in evs:
-        for e in trio:
-            e.record()
-    torch.cuda.synchronize()
+    evs = new_events(args.steps)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -37,6 +37,48 @@ static bool desc_ok(const kvx_cache_desc* d) {
   return true;
 }
 
+// Kernel layout of one role's maps (what kvx_prepare_maps writes): the
+// caller's row-major [batch][R][C] maps transposed to output-major in the
+// operand type of the path that reads them.
+struct MapFormat {
+  int32_t mode = TM_F32;
+  int64_t batch = 0;
+  int32_t R = 0, C = 0;
+  size_t bytes = 0;
+};
+
+static MapFormat map_format(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
+                            int32_t per_head, bool key_role, int32_t w_dtype) {
+  MapFormat f;
+  const bool wf32 = w_dtype == KVX_F32;
+  if (per_head) {
+    f.batch = static_cast<int64_t>(recv->layers) * recv->kv_heads;
+    f.R = f.C = recv->head_dim;
+  } else {
+    f.batch = recv->layers;
+    f.R = n_taps * send->kv_heads * send->head_dim;
+    f.C = recv->kv_heads * recv->head_dim;
+  }
+  const size_t elems = static_cast<size_t>(f.batch) * f.R * f.C;
+  if (send->dtype == KVX_F32 || per_head) {
+    // fp32 caches and the per-head kernel read the map in its own type
+    f.mode = wf32 ? TM_F32 : TM_BF16;
+    f.bytes = elems * (wf32 ? 4 : 2);
+  } else {
+    // flattened bf16 caches: 16-bit operands of the role's type (fp16 for
+    // keys rotated back from a rotated sender), fp32 maps split in two
+    const bool f16 = key_role && send->rope_base > 0.0;
+    if (wf32) {
+      f.mode = f16 ? TM_SPLIT_F16 : TM_SPLIT_BF16;
+      f.bytes = elems * 4;
+    } else {
+      f.mode = f16 ? TM_F16 : TM_BF16;
+      f.bytes = elems * 2;
+    }
+  }
+  return f;
+}
+
 // Workspace layout of kvx_translate.  Returned sizes and the slices used by
 // the launch come from this single function.
 struct TranslateWs {
@@ -45,8 +87,8 @@ struct TranslateWs {
   float2* tab_send = nullptr;
   float2* tab_recv = nullptr;
   uint16_t* krows = nullptr;   // rotated-back unique key rows (fp16)
-  uint16_t* wk16 = nullptr;    // key map as 16-bit operands (fp16 copy or hi|lo split)
-  uint16_t* wv16 = nullptr;    // value map hi|lo split (fp32 maps only)
+  void* wk = nullptr;          // key maps in the kernel layout (raw calls)
+  void* wv = nullptr;          // value maps in the kernel layout (raw calls)
   int32_t rows_cap = 0;
   size_t bytes = 0;
 };
@@ -63,9 +105,11 @@ static int32_t recv_tab_rows_for(const kvx_cache_desc* recv, int32_t pos_limit) 
 // map element type of the fp8 entry point (internal; not a kvx_dtype)
 constexpr int32_t W_FP8 = 2;
 
+// raw: the maps arrive in the caller's layout and are prepared into the
+// workspace (sized for w_dtype).
 static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
                                     int32_t per_head, int32_t w_dtype, bool key_role, bool value_role,
-                                    int32_t pos_limit, void* base) {
+                                    int32_t pos_limit, bool raw, void* base) {
   TranslateWs w;
   Carve c(base);
   const int32_t nr = recv->tokens;
@@ -91,15 +135,9 @@ static TranslateWs layout_translate(const kvx_cache_desc* send, const kvx_cache_
     w.rows_cap = nr;
     w.krows = c.take<uint16_t>(static_cast<size_t>(send->layers) * w.rows_cap * send->kv_heads * send->head_dim);
   }
-  if (!f32 && !per_head) {
-    const size_t map_elems = static_cast<size_t>(recv->layers) * recv->kv_heads * recv->head_dim *
-                             (static_cast<size_t>(n_taps) * send->kv_heads * send->head_dim);
-    if (w_dtype == KVX_F32) {
-      if (key_role) w.wk16 = c.take<uint16_t>(2 * map_elems);
-      if (value_role) w.wv16 = c.take<uint16_t>(2 * map_elems);
-    } else if (srope && w_dtype == KVX_BF16) {
-      w.wk16 = c.take<uint16_t>(map_elems);
-    }
+  if (raw && w_dtype != W_FP8) {
+    if (key_role) w.wk = c.take<char>(map_format(send, recv, n_taps, per_head, true, w_dtype).bytes);
+    if (value_role) w.wv = c.take<char>(map_format(send, recv, n_taps, per_head, false, w_dtype).bytes);
   }
   w.bytes = c.used + 256;
   return w;
@@ -206,7 +244,33 @@ size_t kvx_translate_workspace_size(const kvx_cache_desc* send, const kvx_cache_
                                     int32_t per_head) {
   if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS) return 0;
   // sized for fp32 maps (the larger case) and both roles
-  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, 0, nullptr).bytes;
+  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, 0, true, nullptr).bytes;
+}
+
+size_t kvx_translate_prepared_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv,
+                                             int32_t n_taps, int32_t per_head, int32_t pos_limit) {
+  if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS || pos_limit < 0) return 0;
+  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, false, nullptr).bytes;
+}
+
+size_t kvx_prepared_maps_size(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
+                              int32_t per_head, int32_t role, int32_t w_dtype) {
+  if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS) return 0;
+  if ((role != 0 && role != 1) || (w_dtype != KVX_F32 && w_dtype != KVX_BF16)) return 0;
+  return map_format(send, recv, per_head ? 1 : n_taps, per_head, role == 0, w_dtype).bytes;
+}
+
+int kvx_prepare_maps(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps, int32_t per_head,
+                     int32_t role, int32_t w_dtype, const void* w, void* prepared, size_t prepared_bytes,
+                     void* stream) {
+  if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS) return KVX_ERR_INVALID;
+  if ((role != 0 && role != 1) || (w_dtype != KVX_F32 && w_dtype != KVX_BF16)) return KVX_ERR_INVALID;
+  if (per_head && (n_taps != 1 || send->kv_heads != recv->kv_heads || send->head_dim != recv->head_dim))
+    return KVX_ERR_SHAPE;
+  if (!w || !prepared) return KVX_ERR_INVALID;
+  const MapFormat f = map_format(send, recv, n_taps, per_head, role == 0, w_dtype);
+  if (prepared_bytes < f.bytes) return KVX_ERR_WORKSPACE;
+  return launch_transpose_maps(w, prepared, f.batch, f.R, f.C, f.mode, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -214,13 +278,16 @@ size_t kvx_translate_workspace_size(const kvx_cache_desc* send, const kvx_cache_
 namespace kvx {
 
 // Records ev[0] before the preparation kernels, ev[1] before the main
-// translation kernel and ev[2] after it, when ev is not null.
+// translation kernel and ev[2] after it, when ev is not null.  raw: the maps
+// wt_k, wt_v are the caller's row-major maps and are put into the kernel
+// layout in the workspace first; otherwise they are already in it (prepared
+// maps, or fp8 codes).
 static int translate_impl(const kvx_cache_desc* send, const void* k_send, const void* v_send,
                           const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
                           const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* wt_k,
                           const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
-                          void* stream, hipEvent_t* ev, const kvx_placement* pl, const float* s_k = nullptr,
-                          const float* s_v = nullptr) {
+                          void* stream, hipEvent_t* ev, const kvx_placement* pl, bool raw,
+                          const float* s_k = nullptr, const float* s_v = nullptr) {
   if (!desc_ok(send) || !desc_ok(recv)) return KVX_ERR_INVALID;
   if (w_dtype != KVX_F32 && w_dtype != KVX_BF16 && w_dtype != W_FP8) return KVX_ERR_INVALID;
   if (w_dtype == W_FP8) {
@@ -259,10 +326,13 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
   if (recv->k_norm && do_k && (per_head || send->dtype != KVX_BF16)) return KVX_ERR_UNSUPPORTED;
   if (recv->tokens == 0 || (!do_k && !do_v)) return KVX_OK;
   if (send->tokens == 0) return KVX_ERR_SHAPE;
-  const TranslateWs need = layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, nullptr);
+  const bool raw_maps = raw && w_dtype != W_FP8;
+  const TranslateWs need =
+      layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, raw_maps, nullptr);
   if (!workspace || ws_bytes < need.bytes) return KVX_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const TranslateWs w = layout_translate(send, recv, n_taps, per_head, w_dtype, do_k, do_v, pos_limit, workspace);
+  const TranslateWs w =
+      layout_translate(send, recv, n_taps, per_head, w_dtype, do_k, do_v, pos_limit, raw_maps, workspace);
   auto mark = [&](int i) -> int {
     if (ev && hipEventRecord(ev[i], s) != hipSuccess) return KVX_ERR_HIP;
     return KVX_OK;
@@ -273,6 +343,19 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     return mark(2);
   };
   if (int st = mark(0)) return st;
+  if (raw_maps) {
+    // the caller's row-major maps into the kernel layout
+    if (do_k) {
+      const MapFormat f = map_format(send, recv, n_taps, per_head, true, w_dtype);
+      if (int st = launch_transpose_maps(wt_k, w.wk, f.batch, f.R, f.C, f.mode, s)) return st;
+      wt_k = w.wk;
+    }
+    if (do_v) {
+      const MapFormat f = map_format(send, recv, n_taps, per_head, false, w_dtype);
+      if (int st = launch_transpose_maps(wt_v, w.wv, f.batch, f.R, f.C, f.mode, s)) return st;
+      wt_v = w.wv;
+    }
+  }
   const int32_t f_in = n_taps * send->kv_heads * send->head_dim;
   const int32_t f_out = recv->kv_heads * recv->head_dim;
 
@@ -386,7 +469,6 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     return KVX_ERR_UNSUPPORTED;
   if (int st = launch_runs(recv_to_send, recv->tokens, send->tokens, w.runs, w.runs_scratch, s)) return st;
   const int64_t send_layer_elems = static_cast<int64_t>(send->tokens) * send_row;
-  const int64_t map_rows = static_cast<int64_t>(recv->layers) * f_out;
   const bool split = w_dtype == KVX_F32;
   FlatRole roles[2];
   int n = 0;
@@ -413,18 +495,10 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
       if (int st = launch_rope_table(w.tab_recv, recv_tab_rows_for(recv, pos_limit), recv->head_dim, recv->rope_base, s))
         return st;
     }
-    if (w_dtype == W_FP8) {
-      r.wt = wt_k;
-      r.wscale = s_k;
-    } else if (split) {
-      if (int st = launch_prepare_maps(wt_k, w.wk16, map_rows, f_in, r.a_f16 ? 2 : 1, s)) return st;
-      r.wt = w.wk16;
-    } else if (r.a_f16) {
-      if (int st = launch_prepare_maps(wt_k, w.wk16, map_rows, f_in, 0, s)) return st;
-      r.wt = w.wk16;
-    } else {
-      r.wt = wt_k;
-    }
+    // maps in the kernel layout: fp16 for rotated-back keys, bf16 otherwise
+    // (fp32 maps as hi|lo halves), or fp8 codes with per-output scales
+    r.wt = wt_k;
+    if (w_dtype == W_FP8) r.wscale = s_k;
     r.bias = b_k;
     r.out = static_cast<uint16_t*>(k_recv);
     r.rotate = w.tab_recv ? 1 : 0;
@@ -437,15 +511,8 @@ static int translate_impl(const kvx_cache_desc* send, const void* k_send, const 
     r.a_layer_stride = send_layer_elems;
     r.a_compact = 0;
     r.a_f16 = 0;
-    if (w_dtype == W_FP8) {
-      r.wt = wt_v;
-      r.wscale = s_v;
-    } else if (split) {
-      if (int st = launch_prepare_maps(wt_v, w.wv16, map_rows, f_in, 1, s)) return st;
-      r.wt = w.wv16;
-    } else {
-      r.wt = wt_v;
-    }
+    r.wt = wt_v;
+    if (w_dtype == W_FP8) r.wscale = s_v;
     r.bias = b_v;
     r.out = static_cast<uint16_t*>(v_recv);
     r.rotate = 0;
@@ -481,13 +548,13 @@ int kvx_translate(const kvx_cache_desc* send, const void* k_send, const void* v_
                   int32_t per_head, int32_t w_dtype, const void* wt_k, const void* wt_v, const float* b_k,
                   const float* b_v, void* workspace, size_t ws_bytes, void* stream) {
   return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, nullptr);
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, nullptr, true);
 }
 
 size_t kvx_translate_placed_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
                                            int32_t per_head, int32_t pos_limit) {
   if (!desc_ok(send) || !desc_ok(recv) || n_taps < 1 || n_taps > MAX_TAPS || pos_limit < 0) return 0;
-  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, nullptr).bytes;
+  return layout_translate(send, recv, n_taps, per_head, KVX_F32, true, true, pos_limit, true, nullptr).bytes;
 }
 
 int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const void* v_send,
@@ -496,7 +563,7 @@ int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const v
                          const void* wt_v, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
                          void* stream, const kvx_placement* place) {
   return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, place);
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, nullptr, place, true);
 }
 
 }  // extern "C"
@@ -539,7 +606,7 @@ int kvx_translate_timed(const kvx_cache_desc* send, const void* k_send, const vo
   if (!stage_ms) return KVX_ERR_INVALID;
   return timed_call(stream, stage_ms, [&](hipEvent_t* ev) {
     return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
+                          wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr, true);
   });
 }
 
@@ -552,7 +619,22 @@ int kvx_translate_recorded(const kvx_cache_desc* send, const void* k_send, const
   hipEvent_t ev[3] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1]),
                       static_cast<hipEvent_t>(events[2])};
   return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
-                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr);
+                        wt_k, wt_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr, true);
+}
+
+int kvx_translate_prepared(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                           const kvx_cache_desc* recv, void* k_recv, void* v_recv, const int32_t* recv_to_send,
+                           const int32_t* taps, int32_t n_taps, int32_t per_head, int32_t w_dtype, const void* pk,
+                           const void* pv, const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                           void* stream, const kvx_placement* place, void* const* events) {
+  if (w_dtype != KVX_F32 && w_dtype != KVX_BF16) return KVX_ERR_INVALID;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  if (events) {
+    if (!events[0] || !events[1] || !events[2]) return KVX_ERR_INVALID;
+    for (int i = 0; i < 3; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, per_head, w_dtype,
+                        pk, pv, b_k, b_v, workspace, ws_bytes, stream, events ? ev : nullptr, place, false);
 }
 
 int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void* v_send, const kvx_cache_desc* recv,
@@ -561,17 +643,19 @@ int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void
                       const float* b_v, void* workspace, size_t ws_bytes, void* stream, float* stage_ms) {
   auto call = [&](hipEvent_t* ev) {
     return translate_impl(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, 0, W_FP8, wq_k,
-                          wq_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr, s_k, s_v);
+                          wq_v, b_k, b_v, workspace, ws_bytes, stream, ev, nullptr, false, s_k, s_v);
   };
   if (!stage_ms) return call(nullptr);
   return timed_call(stream, stage_ms, call);
 }
 
-int kvx_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q_out, float* scale_out, void* stream) {
-  if (rows < 0 || cols < 1) return KVX_ERR_INVALID;
-  if (rows == 0) return KVX_OK;
+int kvx_quantize_fp8(const float* w, int32_t count, int32_t f_in, int32_t f_out, uint8_t* q_out, float* scale_out,
+                     void* stream) {
+  if (count < 0 || f_in < 1 || f_out < 1) return KVX_ERR_INVALID;
+  if (count == 0) return KVX_OK;
+  if (count > 65535) return KVX_ERR_UNSUPPORTED;
   if (!w || !q_out || !scale_out) return KVX_ERR_INVALID;
-  return launch_quantize_fp8(w, rows, cols, q_out, scale_out, static_cast<hipStream_t>(stream));
+  return launch_quantize_fp8(w, count, f_in, f_out, q_out, scale_out, static_cast<hipStream_t>(stream));
 }
 
 int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t derotate,
@@ -661,13 +745,13 @@ int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_
                                fit_intercept, &w_out, &b_out, nullptr, workspace, ws_bytes, stream);
 }
 
-int kvx_fold_lowrank(const float* wt, const float* a, const float* b, int32_t count, int32_t f_in, int32_t f_out,
+int kvx_fold_lowrank(const float* w, const float* a, const float* b, int32_t count, int32_t f_in, int32_t f_out,
                      int32_t rank, void* w_out, int32_t out_dtype, void* stream) {
   if (count < 0 || f_in < 1 || f_out < 1 || rank < 0) return KVX_ERR_INVALID;
   if (out_dtype != KVX_F32 && out_dtype != KVX_BF16) return KVX_ERR_INVALID;
   if (count == 0) return KVX_OK;
-  if (!wt || !w_out || (rank > 0 && (!a || !b))) return KVX_ERR_INVALID;
-  return launch_fold(wt, a, b, count, f_in, f_out, rank, w_out, out_dtype == KVX_BF16,
+  if (!w || !w_out || (rank > 0 && (!a || !b))) return KVX_ERR_INVALID;
+  return launch_fold(w, a, b, count, f_in, f_out, rank, w_out, out_dtype == KVX_BF16,
                      static_cast<hipStream_t>(stream));
 }
 

@@ -662,25 +662,12 @@ dgemm_kernel(const DgArgs g) {
       }
 }
 
-// w_out[o][f] = W[f][o] in fp32, by 64 x 64 tiles through LDS so that both
-// the fp64 reads (rows of W) and the fp32 writes (rows of w_out) are
-// contiguous.
-__global__ __launch_bounds__(256) void fit_transpose_kernel(const double* __restrict__ W, int32_t f_in,
-                                                            int32_t f_out, float* __restrict__ w_out) {
-  __shared__ float tile[64][65];
-  const int32_t f0 = blockIdx.y * 64, o0 = blockIdx.x * 64;
-  const int c = threadIdx.x & 63, r4 = threadIdx.x >> 6;
-#pragma unroll 4
-  for (int r = r4; r < 64; r += 4) {
-    const int32_t f = f0 + r, o = o0 + c;
-    if (f < f_in && o < f_out) tile[r][c] = static_cast<float>(W[static_cast<int64_t>(f) * f_out + o]);
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int r = r4; r < 64; r += 4) {
-    const int32_t o = o0 + r, f = f0 + c;
-    if (f < f_in && o < f_out) w_out[static_cast<int64_t>(o) * f_in + f] = tile[c][r];
-  }
+// w_out[f][o] = W[f][o] rounded to fp32 (both row-major [f_in][f_out]).
+__global__ __launch_bounds__(256) void fit_store_kernel(const double* __restrict__ W, int64_t n,
+                                                        float* __restrict__ w_out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    w_out[i] = static_cast<float>(W[i]);
 }
 
 // The bias b[o] = mean_y[o] - sum_f mean_x[f] W[f][o] in two passes with a
@@ -708,12 +695,13 @@ __global__ __launch_bounds__(256) void fit_bias_final_kernel(const double* __res
   b_out[o] = static_cast<float>(sy[o] * inv_n - a);
 }
 
-// Outputs of one fitted problem: w_out (output-major fp32) and, when b_out
-// is not null, the bias.  partial: BI_CHUNKS * f_out doubles of scratch.
+// Outputs of one fitted problem: w_out (row-major fp32 [f_in][f_out]) and,
+// when b_out is not null, the bias.  partial: BI_CHUNKS * f_out doubles of
+// scratch.
 static int fit_output(hipStream_t s, const double* W, int32_t f_in, int32_t f_out, float* w_out, float* b_out,
                       const double* sx, const double* sy, double inv_n, double* partial) {
-  fit_transpose_kernel<<<dim3(static_cast<unsigned>(ceil_div(f_out, 64)), static_cast<unsigned>(ceil_div(f_in, 64))),
-                         256, 0, s>>>(W, f_in, f_out, w_out);
+  const int64_t n = static_cast<int64_t>(f_in) * f_out;
+  fit_store_kernel<<<static_cast<unsigned>(ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192), 256, 0, s>>>(W, n, w_out);
   KVX_LAUNCH_CHECK();
   if (b_out) {
     const int32_t rows_per = static_cast<int32_t>(ceil_div(f_in, BI_CHUNKS));

@@ -778,59 +778,65 @@ flat_gemm_kernel(const FlatKArgs args) {
 }
 
 // ---------------------------------------------------------------- map preparation
-// mode 0: bf16 -> fp16 (same layout); mode 1: fp32 -> [bf16 hi | bf16 lo];
-// mode 2: fp32 -> [fp16 hi | fp16 lo].  Split maps double the K extent:
-// out[l][o][f] = hi, out[l][o][F_in + f] = lo.  Each thread converts 8
-// (mode 0) or 4 (modes 1, 2) consecutive elements of a row per step with
-// 16-byte loads; every conversion rounds to nearest even.
-__global__ __launch_bounds__(256) void prepare_maps_kernel(const void* __restrict__ in, uint16_t* __restrict__ out,
-                                                           int64_t rows, int32_t f_in, int32_t mode) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (mode == 0) {
-    const int64_t n8 = rows * f_in / 8;
-    const u32x4* src = static_cast<const u32x4*>(in);
-    u32x4* dst = reinterpret_cast<u32x4*>(out);
-    for (int64_t i = t0; i < n8; i += stride) {
-      const u32x4 v = src[i];
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = cvt_f16x2(bf16lo(v[e]), bf16hi(v[e]));
-      dst[i] = o;
+// The caller's maps are row-major [batch][R][C] (R inputs, C outputs,
+// y = x W); the kernels read them output-major, [batch][C][m R], in the
+// operand type of the role (see MapMode).  The split modes write the high
+// half at [o][f] and the low half at [o][R + f]: W = hi + lo to about 2^-16
+// relative (bf16) or better (fp16), and the K loop runs over 2 R.  Every
+// conversion rounds to nearest even.  64 x 64 tiles through LDS: the reads
+// run along C and the writes along R.
+__global__ __launch_bounds__(256) void transpose_maps_kernel(const void* __restrict__ in, void* __restrict__ out,
+                                                             int32_t R, int32_t C, int32_t mode) {
+  __shared__ float tile[64][65];
+  const int64_t b = blockIdx.z;
+  const int32_t r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
+  const bool in_f32 = mode == TM_F32 || mode == TM_SPLIT_BF16 || mode == TM_SPLIT_F16;
+#pragma unroll 4
+  for (int r = tr; r < 64; r += 4) {
+    const int32_t rr = r0 + r, cc = c0 + tc;
+    float v = 0.0f;
+    if (rr < R && cc < C) {
+      const int64_t i = (b * R + rr) * C + cc;
+      v = in_f32 ? static_cast<const float*>(in)[i] : bf16_to_f32(static_cast<const uint16_t*>(in)[i]);
     }
-    return;
+    tile[r][tc] = v;
   }
-  const int32_t q = f_in / 4;  // 4-element groups per row
-  const int64_t n4 = rows * q;
-  for (int64_t i = t0; i < n4; i += stride) {
-    const int64_t r = i / q, f = (i % q) * 4;
-    const float4 x = static_cast<const float4*>(in)[i];
-    const float xs[4] = {x.x, x.y, x.z, x.w};
-    uint32_t hi[2], lo[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      if (mode == 1) {
-        hi[e] = pack_bf16(xs[2 * e], xs[2 * e + 1]);
-        lo[e] = pack_bf16(xs[2 * e] - bf16lo(hi[e]), xs[2 * e + 1] - bf16hi(hi[e]));
-      } else {
-        hi[e] = cvt_f16x2(xs[2 * e], xs[2 * e + 1]);
-        const float h0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] & 0xffffu)));
-        const float h1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] >> 16)));
-        lo[e] = cvt_f16x2(xs[2 * e] - h0, xs[2 * e + 1] - h1);
-      }
+  __syncthreads();
+  const bool split = mode == TM_SPLIT_BF16 || mode == TM_SPLIT_F16;
+  const int64_t row = split ? 2 * static_cast<int64_t>(R) : R;
+#pragma unroll 4
+  for (int c = tr; c < 64; c += 4) {
+    const int32_t cc = c0 + c, rr = r0 + tc;
+    if (rr >= R || cc >= C) continue;
+    const float v = tile[tc][c];
+    const int64_t o = (b * C + cc) * row + rr;
+    if (mode == TM_F32) {
+      static_cast<float*>(out)[o] = v;
+    } else if (mode == TM_BF16) {
+      static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);  // exact: v came from bf16
+    } else if (mode == TM_F16) {
+      static_cast<uint16_t*>(out)[o] = f32_to_f16_bits(v);
+    } else if (mode == TM_SPLIT_BF16) {
+      const uint16_t hi = f32_to_bf16_rne(v);
+      static_cast<uint16_t*>(out)[o] = hi;
+      static_cast<uint16_t*>(out)[o + R] = f32_to_bf16_rne(v - bf16_to_f32(hi));
+    } else {
+      const uint16_t hi = f32_to_f16_bits(v);
+      static_cast<uint16_t*>(out)[o] = hi;
+      static_cast<uint16_t*>(out)[o + R] =
+          f32_to_f16_bits(v - static_cast<float>(__builtin_bit_cast(_Float16, hi)));
     }
-    *reinterpret_cast<u32x2*>(out + r * 2 * f_in + f) = u32x2{hi[0], hi[1]};
-    *reinterpret_cast<u32x2*>(out + r * 2 * f_in + f_in + f) = u32x2{lo[0], lo[1]};
   }
 }
 
-int launch_prepare_maps(const void* in, uint16_t* out, int64_t rows, int32_t f_in, int32_t mode, hipStream_t s) {
-  const int64_t total = rows * f_in;
-  if (total <= 0) return KVX_OK;
-  if (f_in % 8 != 0) return KVX_ERR_UNSUPPORTED;
-  int64_t blocks = ceil_div(total / (mode == 0 ? 8 : 4), 256);
-  if (blocks > 16384) blocks = 16384;
-  prepare_maps_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, rows, f_in, mode);
+int launch_transpose_maps(const void* in, void* out, int64_t batch, int32_t R, int32_t C, int32_t mode,
+                          hipStream_t s) {
+  if (batch <= 0 || R <= 0 || C <= 0) return KVX_OK;
+  if (batch > 65535) return KVX_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(ceil_div(C, 64)), static_cast<unsigned>(ceil_div(R, 64)),
+                  static_cast<unsigned>(batch));
+  transpose_maps_kernel<<<grid, 256, 0, s>>>(in, out, R, C, mode);
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
@@ -858,34 +864,59 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return sign | static_cast<uint32_t>(code);
 }
 
-// One workgroup per map row: amax (order-free), scale = amax / 448 (1 when
-// that is zero), codes of w / scale; both divisions correctly rounded.
-__global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* __restrict__ w, int32_t cols,
+// One workgroup per 16 consecutive outputs o of one map w[f][o] (row-major
+// [f_in][f_out]): amax over f (order-free), scale = amax / 448 (1 when that
+// is zero), codes of w / scale; both divisions correctly rounded.  Codes go
+// out output-major, q[o][f], staged 1024 inputs at a time in LDS so the
+// writes run along f.
+constexpr int QZ_OUT = 16;
+constexpr int QZ_CHUNK = 1024;
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* __restrict__ w, int32_t f_in, int32_t f_out,
                                                            uint8_t* __restrict__ q, float* __restrict__ scale) {
-  const int64_t row = blockIdx.x;
-  const float* x = w + row * cols;
-  __shared__ float red[256];
+  __shared__ float red[16][QZ_OUT + 1];
+  __shared__ float sc_s[QZ_OUT];
+  __shared__ uint8_t codes[QZ_OUT][QZ_CHUNK + 16];
+  const int64_t b = blockIdx.y;
+  const int32_t o0 = blockIdx.x * QZ_OUT;
+  const int oc = threadIdx.x % QZ_OUT, rg = threadIdx.x / QZ_OUT;  // output, row group
+  const int32_t o = o0 + oc;
+  const float* wb = w + b * f_in * static_cast<int64_t>(f_out);
   float m = 0.0f;
-  for (int32_t c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(x[c]));
-  red[threadIdx.x] = m;
+  if (o < f_out)
+    for (int32_t f = rg; f < f_in; f += 16) m = fmaxf(m, fabsf(wb[static_cast<int64_t>(f) * f_out + o]));
+  red[rg][oc] = m;
   __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (threadIdx.x < k) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + k]);
+  if (threadIdx.x < QZ_OUT) {
+    float mm = 0.0f;
+    for (int g = 0; g < 16; ++g) mm = fmaxf(mm, red[g][threadIdx.x]);
+    float sc = __fdiv_rn(mm, 448.0f);
+    if (!(sc > 0.0f)) sc = 1.0f;
+    sc_s[threadIdx.x] = sc;
+    if (o0 + static_cast<int32_t>(threadIdx.x) < f_out) scale[b * f_out + o0 + threadIdx.x] = sc;
+  }
+  __syncthreads();
+  const float sc = sc_s[oc];
+  for (int32_t f0 = 0; f0 < f_in; f0 += QZ_CHUNK) {
+    const int32_t n = min(QZ_CHUNK, f_in - f0);
+    for (int32_t fl = rg; fl < n; fl += 16)
+      codes[oc][fl] = o < f_out ? static_cast<uint8_t>(e4m3_rne(__fdiv_rn(wb[static_cast<int64_t>(f0 + fl) * f_out + o], sc)))
+                                : 0;
+    __syncthreads();
+    for (int32_t i = threadIdx.x; i < QZ_OUT * n; i += 256) {
+      const int32_t r = i / n, fl = i % n;
+      if (o0 + r < f_out) q[(b * f_out + o0 + r) * static_cast<int64_t>(f_in) + f0 + fl] = codes[r][fl];
+    }
     __syncthreads();
   }
-  float sc = __fdiv_rn(red[0], 448.0f);
-  if (!(sc > 0.0f)) sc = 1.0f;
-  if (threadIdx.x == 0) scale[row] = sc;
-  for (int32_t c = threadIdx.x; c < cols; c += 256) q[row * cols + c] = static_cast<uint8_t>(e4m3_rne(__fdiv_rn(x[c], sc)));
 }
 
-int launch_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q, float* scale, hipStream_t s) {
-  if (rows <= 0) return KVX_OK;
-  for (int64_t r0 = 0; r0 < rows; r0 += 65535) {
-    const int64_t n = rows - r0 < 65535 ? rows - r0 : 65535;
-    quantize_fp8_kernel<<<static_cast<unsigned>(n), 256, 0, s>>>(w + r0 * cols, cols, q + r0 * cols, scale + r0);
-    KVX_LAUNCH_CHECK();
-  }
+int launch_quantize_fp8(const float* w, int64_t count, int32_t f_in, int32_t f_out, uint8_t* q, float* scale,
+                        hipStream_t s) {
+  if (count <= 0) return KVX_OK;
+  if (count > 65535) return KVX_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(ceil_div(f_out, QZ_OUT)), static_cast<unsigned>(count));
+  quantize_fp8_kernel<<<grid, 256, 0, s>>>(w, f_in, f_out, q, scale);
+  KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
 

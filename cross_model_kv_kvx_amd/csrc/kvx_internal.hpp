@@ -78,14 +78,24 @@ struct FlatProblem {
 
 int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStream_t s);
 
-// 16-bit operand maps from the caller's maps: mode 0 bf16 -> fp16; mode 1
-// fp32 -> [bf16 hi | bf16 lo]; mode 2 fp32 -> [fp16 hi | fp16 lo] (rows of
-// f_in become rows of 2 f_in).
-int launch_prepare_maps(const void* in, uint16_t* out, int64_t rows, int32_t f_in, int32_t mode, hipStream_t s);
+// Map preparation: row-major [batch][R][C] (y = x W) -> output-major
+// [batch][C][m R] in the kernels' operand type.
+enum MapMode : int32_t {
+  TM_F32 = 0,        // fp32 -> fp32
+  TM_BF16 = 1,       // bf16 -> bf16
+  TM_F16 = 2,        // bf16 -> fp16
+  TM_SPLIT_BF16 = 3, // fp32 -> [bf16 hi | bf16 lo]  (m = 2)
+  TM_SPLIT_F16 = 4,  // fp32 -> [fp16 hi | fp16 lo]  (m = 2)
+};
+int launch_transpose_maps(const void* in, void* out, int64_t batch, int32_t R, int32_t C, int32_t mode,
+                          hipStream_t s);
 
-// Per-row fp8 E4M3 quantisation of fp32 maps [rows][cols]: scale = amax / 448
-// (1 for an all-zero row), codes = nearest-even E4M3 of w / scale.
-int launch_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q, float* scale, hipStream_t s);
+// fp8 E4M3 quantisation of `count` row-major fp32 maps [f_in][f_out], per
+// output o: scale = amax_f |w[f][o]| / 448 (1 for an all-zero output), codes
+// = nearest-even E4M3 of w / scale, written output-major q[count][f_out][f_in],
+// scale[count][f_out].
+int launch_quantize_fp8(const float* w, int64_t count, int32_t f_in, int32_t f_out, uint8_t* q, float* scale,
+                        hipStream_t s);
 
 // ---------------------------------------------------------------- per-head translation (bf16)
 struct HeadProblem {
@@ -132,7 +142,8 @@ struct F32Role {
 int launch_f32(const F32Problem& p, const F32Role* roles, int n_roles, hipStream_t s);
 
 // ---------------------------------------------------------------- fold
-int launch_fold(const float* wt, const float* a, const float* b, int64_t count, int32_t f_in,
+// W [f_in][f_out] + A [f_in][rank] B [rank][f_out], per map, row-major.
+int launch_fold(const float* w, const float* a, const float* b, int64_t count, int32_t f_in,
                 int32_t f_out, int32_t rank, void* out, int32_t out_bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- features / fit

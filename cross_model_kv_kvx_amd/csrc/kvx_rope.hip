@@ -209,10 +209,14 @@ int launch_gather(const void* cache, int32_t cache_f32, int32_t send_tokens, int
 
 // ---------------------------------------------------------------- rank-r fold
 // "Prefill-Free ...", Methodology 3: the rank-16 corrections are folded into
-// one fixed map.  Products rounded to fp32, summed in rank order, added to
-// the dense entry, then stored (bf16: nearest even).  Contraction into fused
-// multiply-adds is switched off so the order of roundings is the stated one.
-__global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ wt,
+// one fixed map, W_eff = W + A B with W [f_in][f_out], A [f_in][rank],
+// B [rank][f_out] (row-major, y = x W).  Products rounded to fp32, summed in
+// rank order, added to the dense entry, then stored (bf16: nearest even).
+// Contraction into fused multiply-adds is switched off so the order of
+// roundings is the stated one.  One thread per entry (f, o); consecutive
+// threads take consecutive o, so the reads of W and B and the writes run
+// along rows.
+__global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ w,
                                                    const float* __restrict__ a,
                                                    const float* __restrict__ b, int64_t count,
                                                    int32_t f_in, int32_t f_out, int32_t rank,
@@ -224,16 +228,16 @@ __global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ wt,
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t m = i / per;
     const int64_t r0 = i % per;
-    const int32_t o = static_cast<int32_t>(r0 / f_in);
-    const int32_t f = static_cast<int32_t>(r0 % f_in);
+    const int32_t f = static_cast<int32_t>(r0 / f_out);
+    const int32_t o = static_cast<int32_t>(r0 % f_out);
     const float* ar = a + (m * f_in + f) * rank;
-    const float* br = b + (m * f_out + o) * rank;
+    const float* bc = b + m * rank * static_cast<int64_t>(f_out) + o;
     float acc = 0.0f;
     for (int32_t r = 0; r < rank; ++r) {
-      const float p = br[r] * ar[r];
+      const float p = ar[r] * bc[static_cast<int64_t>(r) * f_out];
       acc = (r == 0) ? p : acc + p;
     }
-    const float tot = (rank > 0) ? wt[i] + acc : wt[i];
+    const float tot = (rank > 0) ? w[i] + acc : w[i];
     if (out_bf16)
       static_cast<uint16_t*>(out)[i] = f32_to_bf16_rne(tot);
     else
@@ -241,13 +245,13 @@ __global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ wt,
   }
 }
 
-int launch_fold(const float* wt, const float* a, const float* b, int64_t count, int32_t f_in,
+int launch_fold(const float* w, const float* a, const float* b, int64_t count, int32_t f_in,
                 int32_t f_out, int32_t rank, void* out, int32_t out_bf16, hipStream_t s) {
   const int64_t total = count * f_in * static_cast<int64_t>(f_out);
   if (total <= 0) return KVX_OK;
   int64_t blocks = ceil_div(total, 256);
   if (blocks > 65536) blocks = 65536;
-  fold_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(wt, a, b, count, f_in, f_out, rank, out,
+  fold_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(w, a, b, count, f_in, f_out, rank, out,
                                                             out_bf16);
   KVX_LAUNCH_CHECK();
   return KVX_OK;

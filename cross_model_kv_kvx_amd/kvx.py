@@ -31,7 +31,8 @@ EXPORTS = (
     "kvx_fit_ridge_workspace_size", "kvx_fit_ridge", "kvx_fit_ridge_batched_workspace_size",
     "kvx_fit_ridge_batched", "kvx_fit_recolor_workspace_size", "kvx_fit_recolor", "kvx_fold_lowrank",
     "kvx_quantize_fp8", "kvx_translate_fp8", "kvx_align_tokens_async", "kvx_translate_recorded",
-    "kvx_align_tokens_noalloc",
+    "kvx_align_tokens_noalloc", "kvx_prepared_maps_size", "kvx_prepare_maps",
+    "kvx_translate_prepared_workspace_size", "kvx_translate_prepared",
 )
 
 
@@ -92,7 +93,12 @@ def lib() -> ctypes.CDLL:
             "kvx_fit_recolor": (ctypes.c_int, [i32, vpp, i64, vpp, i64, i32, i64, i32, i32, dbl, dbl, vpp, vpp,
                                                ip, ip, vp, sz, vp]),
             "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
-            "kvx_quantize_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+            "kvx_quantize_fp8": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
+            "kvx_prepared_maps_size": (sz, [dp, dp, i32, i32, i32, i32]),
+            "kvx_prepare_maps": (ctypes.c_int, [dp, dp, i32, i32, i32, i32, vp, vp, sz, vp]),
+            "kvx_translate_prepared_workspace_size": (sz, [dp, dp, i32, i32, i32]),
+            "kvx_translate_prepared": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp,
+                                                      vp, vp, sz, vp, ctypes.POINTER(Placement), vpp]),
             "kvx_align_tokens_async": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, vp, sz, vp]),
             "kvx_align_tokens_noalloc": (ctypes.c_int, [vp, i32, vp, i32, vp, vp, vp]),
             "kvx_translate_recorded": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp,
@@ -242,7 +248,7 @@ def translate_workspace_size(send: CacheDesc, recv: CacheDesc, n_taps: int, per_
 
 
 def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], recv_to_send: torch.Tensor,
-              taps, wt_k: Optional[torch.Tensor], wt_v: Optional[torch.Tensor],
+              taps, w_k: Optional[torch.Tensor], w_v: Optional[torch.Tensor],
               b_k: Optional[torch.Tensor] = None, b_v: Optional[torch.Tensor] = None, *,
               recv_layers: Optional[int] = None, recv_heads: Optional[int] = None,
               recv_head_dim: Optional[int] = None, per_head: bool = False,
@@ -252,13 +258,19 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
               recv_key_norm: Optional[torch.Tensor] = None, key_norm_eps: float = 1e-6,
               slot: Optional[torch.Tensor] = None, pool_rows: Optional[int] = None,
               recv_pos: Optional[torch.Tensor] = None, send_pos: Optional[torch.Tensor] = None,
-              pos_limit: Optional[int] = None, events=None):
+              pos_limit: Optional[int] = None, events=None, prepared: bool = False,
+              w_dtype: Optional[int] = None):
     """kvx_translate.  Returns (k_recv, v_recv) (either None when its role is
-    skipped).  ``taps``: host int32 [L_R][n_taps] (numpy).  With a list
-    ``stage_ms``, calls kvx_translate_timed instead (synchronous) and appends
-    the [preparation, translation kernel] device times in ms.  With three
-    recorded torch.cuda.Event objects ``events``, calls
-    kvx_translate_recorded (asynchronous; the events mark the phases)."""
+    skipped).  ``taps``: host int32 [L_R][n_taps] (numpy).  ``w_k``, ``w_v``:
+    row-major maps [L_R][F_in][F_out] (per head [L_R][H][d][d], w[l][h][c][o]),
+    fp32 or bf16.  With a list ``stage_ms``, calls kvx_translate_timed
+    instead (synchronous) and appends the [preparation, translation kernel]
+    device times in ms.  With three recorded torch.cuda.Event objects
+    ``events``, calls kvx_translate_recorded (asynchronous; the events mark
+    the phases).  With ``prepared`` (and ``w_dtype``, F32 or BF16, the type
+    they were prepared from), ``w_k``/``w_v`` are buffers from
+    ``prepare_maps`` and kvx_translate_prepared runs (placement and events
+    allowed, no stage timing)."""
     ref = k_send if k_send is not None else v_send
     if ref is None:
         raise ValueError("at least one role is needed")
@@ -270,7 +282,7 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
     for name, t in (("k_send", k_send), ("v_send", v_send)):
         if t is not None:
             _need(t, name, ref.dtype)
-    w_ref = wt_k if wt_k is not None else wt_v
+    w_ref = w_k if w_k is not None else w_v
     H_R = recv_heads if recv_heads is not None else ref.shape[2]
     d_R = recv_head_dim if recv_head_dim is not None else ref.shape[3]
     N_R = recv_to_send.numel()
@@ -282,9 +294,17 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
             raise ValueError("recv_key_norm must be [recv_layers][head_dim]")
         recv.k_norm = recv_key_norm.data_ptr()
         recv.k_norm_eps = float(key_norm_eps)
-    for name, t in (("wt_k", wt_k), ("wt_v", wt_v)):
+    for name, t in (("w_k", w_k), ("w_v", w_v)):
         if t is not None:
             _need(t, name, w_ref.dtype)
+    if prepared:
+        if w_dtype not in (F32, BF16) or w_ref.dtype != torch.uint8:
+            raise ValueError("prepared maps are uint8 buffers from prepare_maps, with w_dtype F32 or BF16")
+        if stage_ms is not None:
+            raise ValueError("stage timing is not available with prepared maps (use events)")
+        code = int(w_dtype)
+    else:
+        code = _dtype_code(w_ref)
     for name, t in (("b_k", b_k), ("b_v", b_v)):
         if t is not None:
             _need(t, name, torch.float32)
@@ -294,8 +314,9 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
         k_recv = torch.empty((L_R, rows, H_R, d_R), dtype=ref.dtype, device=ref.device)
     if v_send is not None and v_recv is None:
         v_recv = torch.empty((L_R, rows, H_R, d_R), dtype=ref.dtype, device=ref.device)
+    place = None
     if placed:
-        if stage_ms is not None or events is not None:
+        if stage_ms is not None or (events is not None and not prepared):
             raise ValueError("stage timing is not available with a placement")
         for name, t, dt in (("slot", slot, torch.int64), ("recv_pos", recv_pos, torch.int32),
                             ("send_pos", send_pos, torch.int32)):
@@ -305,22 +326,32 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
                           recv_pos.data_ptr() if recv_pos is not None else None,
                           send_pos.data_ptr() if send_pos is not None else None,
                           int(pos_limit) if pos_limit is not None else 0)
-        ws = _workspace(lib().kvx_translate_placed_workspace_size(ctypes.byref(send), ctypes.byref(recv),
-                                                                  int(n_taps), int(bool(per_head)), place.pos_limit),
-                        ref.device, workspace)
+    pl = place.pos_limit if place is not None else 0
+    if prepared:
+        nbytes = lib().kvx_translate_prepared_workspace_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps),
+                                                             int(bool(per_head)), pl)
+    elif placed:
+        nbytes = lib().kvx_translate_placed_workspace_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps),
+                                                           int(bool(per_head)), pl)
     else:
-        ws = _workspace(translate_workspace_size(send, recv, n_taps, per_head), ref.device, workspace)
+        nbytes = translate_workspace_size(send, recv, n_taps, per_head)
+    ws = _workspace(nbytes, ref.device, workspace)
     args = [ctypes.byref(send), _ptr(k_send), _ptr(v_send), ctypes.byref(recv),
             _ptr(k_recv) if k_send is not None else None, _ptr(v_recv) if v_send is not None else None,
             _ptr(recv_to_send), taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_taps),
-            int(bool(per_head)), _dtype_code(w_ref), _ptr(wt_k), _ptr(wt_v), _ptr(b_k), _ptr(b_v),
+            int(bool(per_head)), code, _ptr(w_k), _ptr(w_v), _ptr(b_k), _ptr(b_v),
             _ptr(ws), ws.numel(), _stream(stream)]
-    if placed:
-        _check(lib().kvx_translate_placed(*args, ctypes.byref(place)), "kvx_translate_placed")
-    elif events is not None:
+    ev = None
+    if events is not None:
         if len(events) != 3 or any(not e.cuda_event for e in events):
             raise ValueError("events must be three torch.cuda.Event objects that have been recorded once")
         ev = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+    if prepared:
+        _check(lib().kvx_translate_prepared(*args, ctypes.byref(place) if place is not None else None, ev),
+               "kvx_translate_prepared")
+    elif placed:
+        _check(lib().kvx_translate_placed(*args, ctypes.byref(place)), "kvx_translate_placed")
+    elif ev is not None:
         _check(lib().kvx_translate_recorded(*args, ev), "kvx_translate_recorded")
     elif stage_ms is None:
         _check(lib().kvx_translate(*args), "kvx_translate")
@@ -331,16 +362,40 @@ def translate(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], re
     return (k_recv if k_send is not None else None), (v_recv if v_send is not None else None)
 
 
+def prepare_maps(w: torch.Tensor, role: str, send: CacheDesc, recv: CacheDesc, n_taps: int,
+                 per_head: bool = False, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvx_prepare_maps: the maps of one role ("k" or "v"; row-major as
+    ``translate`` takes them, fp32 or bf16) in the kernel layout for
+    translations with these descriptors; returns the device uint8 buffer to
+    pass to ``translate(..., prepared=True, w_dtype=...)``."""
+    _need(w, "w")
+    r = {"k": 0, "v": 1}[role]
+    code = _dtype_code(w)
+    n = int(lib().kvx_prepared_maps_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps), int(bool(per_head)), r,
+                                         code))
+    if n == 0:
+        raise ValueError("invalid descriptors for prepared maps")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _check(lib().kvx_prepare_maps(ctypes.byref(send), ctypes.byref(recv), int(n_taps), int(bool(per_head)), r, code,
+                                  _ptr(w), _ptr(out), out.numel(), _stream(stream)), "kvx_prepare_maps")
+    return out
+
+
 def quantize_fp8(w: torch.Tensor, stream=None):
-    """kvx_quantize_fp8 over the last dimension of a fp32 tensor: returns
-    (codes uint8 of w's shape, scales fp32 of w.shape[:-1])."""
+    """kvx_quantize_fp8 on row-major fp32 maps [count][f_in][f_out] (a single
+    map may drop the leading dimension): returns (codes uint8
+    [count][f_out][f_in], output-major, and scales fp32 [count][f_out])."""
     _need(w, "w", torch.float32)
-    cols = w.shape[-1]
-    rows = w.numel() // cols
-    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
-    sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
-    _check(lib().kvx_quantize_fp8(_ptr(w), rows, cols, _ptr(q), _ptr(sc), _stream(stream)), "kvx_quantize_fp8")
-    return q, sc
+    squeeze = w.dim() == 2
+    if squeeze:
+        w = w[None]
+    count, f_in, f_out = w.shape
+    q = torch.empty((count, f_out, f_in), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((count, f_out), dtype=torch.float32, device=w.device)
+    _check(lib().kvx_quantize_fp8(_ptr(w), count, f_in, f_out, _ptr(q), _ptr(sc), _stream(stream)),
+           "kvx_quantize_fp8")
+    return (q[0], sc[0]) if squeeze else (q, sc)
 
 
 def translate_fp8(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], recv_to_send: torch.Tensor,
@@ -417,7 +472,7 @@ def fit_ridge(x: torch.Tensor, y: torch.Tensor, *, lambda_abs: float = 0.0, lamb
               fit_intercept: bool = False, w_out: Optional[torch.Tensor] = None,
               b_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
     """kvx_fit_ridge on row-major 2-D x [n][f_in], y [n][f_out].  Returns
-    (wt fp32 [f_out][f_in], b fp32 [f_out] or None)."""
+    (w fp32 [f_in][f_out], y = x w + b; b fp32 [f_out] or None)."""
     if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
         raise ValueError("x and y must be 2-D with equal row counts")
     if x.stride(1) != 1 or y.stride(1) != 1:
@@ -427,7 +482,7 @@ def fit_ridge(x: torch.Tensor, y: torch.Tensor, *, lambda_abs: float = 0.0, lamb
     n, f_in = x.shape
     f_out = y.shape[1]
     if w_out is None:
-        w_out = torch.empty((f_out, f_in), dtype=torch.float32, device=x.device)
+        w_out = torch.empty((f_in, f_out), dtype=torch.float32, device=x.device)
     if fit_intercept and b_out is None:
         b_out = torch.empty(f_out, dtype=torch.float32, device=x.device)
     ws = _workspace(lib().kvx_fit_ridge_workspace_size(f_in, f_out), x.device, workspace)
@@ -443,7 +498,7 @@ def fit_ridge_batched(xs, ys, *, lambda_abs: float = 0.0, lambda_rel: float = 0.
                       status: Optional[list] = None):
     """kvx_fit_ridge_batched on lists of row-major 2-D x [n][f_in] and
     y [n][f_out] (one shape, one dtype, one row stride each).  Returns the
-    lists (wt fp32 [f_out][f_in], b fp32 [f_out] or None).  With a list
+    lists (w fp32 [f_in][f_out], b fp32 [f_out] or None).  With a list
     ``status``, appends each problem's status and raises only for other
     errors."""
     count = len(xs)
@@ -461,7 +516,7 @@ def fit_ridge_batched(xs, ys, *, lambda_abs: float = 0.0, lambda_rel: float = 0.
     f_out = y0.shape[1]
     dev = x0.device
     if w_outs is None:
-        w_outs = [torch.empty((f_out, f_in), dtype=torch.float32, device=dev) for _ in range(count)]
+        w_outs = [torch.empty((f_in, f_out), dtype=torch.float32, device=dev) for _ in range(count)]
     if fit_intercept and b_outs is None:
         b_outs = [torch.empty(f_out, dtype=torch.float32, device=dev) for _ in range(count)]
     arr = ctypes.c_void_p * count
@@ -487,7 +542,7 @@ def fit_recolor(xs, ys, *, rho_x: float = 0.0, rho_y: float = 0.0, w_outs=None, 
                 info: Optional[dict] = None):
     """kvx_fit_recolor on lists of row-major 2-D x [n][f_in] and y [n][f_out]
     (one shape, one dtype, one row stride each).  Returns the lists
-    (wt fp32 [f_out][f_in], b fp32 [f_out]).  With a list ``status``, appends
+    (w fp32 [f_in][f_out], b fp32 [f_out]).  With a list ``status``, appends
     each problem's status and raises only for other errors; with a dict
     ``info``, stores the number of polar iterations under "iters"."""
     count = len(xs)
@@ -505,7 +560,7 @@ def fit_recolor(xs, ys, *, rho_x: float = 0.0, rho_y: float = 0.0, w_outs=None, 
     f_out = y0.shape[1]
     dev = x0.device
     if w_outs is None:
-        w_outs = [torch.empty((f_out, f_in), dtype=torch.float32, device=dev) for _ in range(count)]
+        w_outs = [torch.empty((f_in, f_out), dtype=torch.float32, device=dev) for _ in range(count)]
     if b_outs is None:
         b_outs = [torch.empty(f_out, dtype=torch.float32, device=dev) for _ in range(count)]
     arr = ctypes.c_void_p * count
@@ -528,21 +583,24 @@ def fit_recolor(xs, ys, *, rho_x: float = 0.0, rho_y: float = 0.0, w_outs=None, 
     return w_outs, b_outs
 
 
-def fold_lowrank(wt: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16,
+def fold_lowrank(w: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """kvx_fold_lowrank on [count][f_out][f_in] maps with a [count][f_in][r],
-    b [count][f_out][r] (a single map may drop the leading dimension)."""
-    squeeze = wt.dim() == 2
+    """kvx_fold_lowrank: W + A B on row-major [count][f_in][f_out] maps with
+    a [count][f_in][r], b [count][r][f_out] (a single map may drop the
+    leading dimension)."""
+    squeeze = w.dim() == 2
     if squeeze:
-        wt, a, b = wt[None], a[None], b[None]
-    for name, t in (("wt", wt), ("a", a), ("b", b)):
+        w, a, b = w[None], a[None], b[None]
+    for name, t in (("w", w), ("a", a), ("b", b)):
         _need(t, name, torch.float32)
-    count, f_out, f_in = wt.shape
+    count, f_in, f_out = w.shape
     rank = a.shape[-1]
+    if tuple(a.shape) != (count, f_in, rank) or tuple(b.shape) != (count, rank, f_out):
+        raise ValueError("a must be [count][f_in][rank] and b [count][rank][f_out]")
     if out is None:
-        out = torch.empty((count, f_out, f_in), dtype=out_dtype, device=wt.device)
+        out = torch.empty((count, f_in, f_out), dtype=out_dtype, device=w.device)
     code = BF16 if out.dtype == torch.bfloat16 else F32
-    st = lib().kvx_fold_lowrank(_ptr(wt), _ptr(a), _ptr(b), count, f_in, f_out, rank, _ptr(out), code,
+    st = lib().kvx_fold_lowrank(_ptr(w), _ptr(a), _ptr(b), count, f_in, f_out, rank, _ptr(out), code,
                                 _stream(stream))
     _check(st, "kvx_fold_lowrank")
     return out[0] if squeeze else out

@@ -171,31 +171,32 @@ def receiver_cache(shape: CacheShape, seed: int, device="cpu", dtype=torch.bfloa
 
 def flat_maps(recv_layers: int, f_in: int, f_out: int, seed: int, device="cpu",
               rank: int = 16):
-    """Flattened affine maps for one role, stored output-major.
+    """Flattened affine maps for one role, row-major (y = x W).
 
-    Returns ``wt`` fp32 ``[L][f_out][f_in]`` (wt[o][f] multiplies feature f
-    into output o), rank factors ``u`` fp32 ``[L][f_in][rank]`` and
-    ``v`` fp32 ``[L][f_out][rank]`` (the correction to wt[o][f] is
-    sum_r v[o][r] u[f][r]), and bias fp32 ``[L][f_out]``.
-    wt, u ~ N(0,1)/sqrt(f_in); v ~ 0.1 N(0,1)/sqrt(rank); bias ~ N(0, 0.1^2).
+    Returns ``w`` fp32 ``[L][f_in][f_out]`` (w[f][o] multiplies feature f
+    into output o), rank factors ``a`` fp32 ``[L][f_in][rank]`` and ``b_lr``
+    fp32 ``[L][rank][f_out]`` (the correction is A B), and bias fp32
+    ``[L][f_out]``.  w, a ~ N(0,1)/sqrt(f_in); b_lr ~ 0.1 N(0,1)/sqrt(rank);
+    bias ~ N(0, 0.1^2).
     """
     g = _gen(device, seed)
-    wt = torch.randn((recv_layers, f_out, f_in), generator=g, device=device) / math.sqrt(f_in)
-    u = torch.randn((recv_layers, f_in, rank), generator=g, device=device) / math.sqrt(f_in)
-    v = torch.randn((recv_layers, f_out, rank), generator=g, device=device) * (0.1 / math.sqrt(rank))
+    w = torch.randn((recv_layers, f_in, f_out), generator=g, device=device) / math.sqrt(f_in)
+    a = torch.randn((recv_layers, f_in, rank), generator=g, device=device) / math.sqrt(f_in)
+    b_lr = torch.randn((recv_layers, rank, f_out), generator=g, device=device) * (0.1 / math.sqrt(rank))
     b = torch.randn((recv_layers, f_out), generator=g, device=device) * 0.1
-    return wt.contiguous(), u.contiguous(), v.contiguous(), b.contiguous()
+    return w.contiguous(), a.contiguous(), b_lr.contiguous(), b.contiguous()
 
 
 def perhead_maps(recv_layers: int, heads: int, head_dim: int, seed: int, device="cpu",
                  std=None, bias_std: float = 0.1):
-    """Per-head maps for one role: ``wt`` fp32 ``[L][H][d_out][d_in]``
-    with N(0,1)/sqrt(d) entries (or ``std``), bias fp32 ``[L][H*d]``."""
+    """Per-head maps for one role: ``w`` fp32 ``[L][H][d_in][d_out]``
+    (w[l][h][c][o]: input channel c to output channel o of head h) with
+    N(0,1)/sqrt(d) entries (or ``std``), bias fp32 ``[L][H*d]``."""
     g = _gen(device, seed)
     s = (1.0 / math.sqrt(head_dim)) if std is None else std
-    wt = torch.randn((recv_layers, heads, head_dim, head_dim), generator=g, device=device) * s
+    w = torch.randn((recv_layers, heads, head_dim, head_dim), generator=g, device=device) * s
     b = torch.randn((recv_layers, heads * head_dim), generator=g, device=device) * bias_std
-    return wt.contiguous(), b.contiguous()
+    return w.contiguous(), b.contiguous()
 
 
 def key_norm_weights(recv_layers: int, head_dim: int, seed: int, device="cpu"):
@@ -222,9 +223,9 @@ def config(k: int, device="cpu", small: bool = False):
         for r, role in enumerate(("k", "v")):
             out[f"x_cal_{role}"] = sender_cache(cal, seed * 100 + r, device, torch.float32)
             out[f"x_{role}"] = sender_cache(shp, seed * 100 + 10 + r, device, torch.float32)
-            wt, b = perhead_maps(1, c["heads"], c["head_dim"], seed * 100 + 20 + r, device,
-                                 std=1.0 / math.sqrt(c["head_dim"]))
-            out[f"w_true_{role}"], out[f"b_true_{role}"] = wt, b
+            w, b = perhead_maps(1, c["heads"], c["head_dim"], seed * 100 + 20 + r, device,
+                                std=1.0 / math.sqrt(c["head_dim"]))
+            out[f"w_true_{role}"], out[f"b_true_{role}"] = w, b
             out[f"noise_cal_{role}"] = gaussian(cal.shape(), seed * 100 + 30 + r, device, 0.01)
             out[f"noise_{role}"] = gaussian(shp.shape(), seed * 100 + 40 + r, device, 0.01)
         return out
@@ -238,8 +239,8 @@ def config(k: int, device="cpu", small: bool = False):
         for r, role in enumerate(("k", "v")):
             out[f"{role}_send"] = sender_cache(shp, seed * 100 + r, device,
                                                channel_scale="loguniform")
-            wt, b = perhead_maps(lr, c["heads"], c["head_dim"], seed * 100 + 20 + r, device)
-            out[f"wt_{role}"], out[f"b_{role}"] = wt, b
+            w, b = perhead_maps(lr, c["heads"], c["head_dim"], seed * 100 + 20 + r, device)
+            out[f"w_{role}"], out[f"b_{role}"] = w, b
         return out
     if k in (3, 4, 5):
         nr = c["cal_tokens"] if k == 5 else c["recv_tokens"]
@@ -261,8 +262,8 @@ def config(k: int, device="cpu", small: bool = False):
             if k == 5:
                 out[f"{role}_recv_native"] = receiver_cache(out["recv_shape"], seed * 100 + 50 + r, device)
             else:
-                wt, u, v, b = flat_maps(lr, f_in, f_out, seed * 100 + 20 + r, device, c["rank"])
-                out[f"wt_{role}"], out[f"u_{role}"], out[f"v_{role}"], out[f"b_{role}"] = wt, u, v, b
+                w, a, b_lr, b = flat_maps(lr, f_in, f_out, seed * 100 + 20 + r, device, c["rank"])
+                out[f"w_{role}"], out[f"a_{role}"], out[f"blr_{role}"], out[f"b_{role}"] = w, a, b_lr, b
         if k == 5:
             fs = c["fresh_seed"]
             nf = 256 if small else c["recv_tokens"]

@@ -169,10 +169,15 @@ int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps,
  *   out of bounds).
  * taps: host int32 [recv->layers][n_taps], values in [0, send->layers).
  * w_dtype: element type of the maps (KVX_F32 or KVX_BF16).
- * wt_k, wt_v: device maps stored output-major:
- *   flattened: [L_R][H_R*d_R][n_taps*H_S*d_S], wt[l][o][f] multiplies
+ * wt_k, wt_v: device maps, row-major with y = x W:
+ *   flattened: [L_R][n_taps*H_S*d_S][H_R*d_R], w[l][f][o] multiplies
  *              feature f into output o;
- *   per_head:  [L_R][H][d][d], wt[l][h][o][c].
+ *   per_head:  [L_R][H][d][d], w[l][h][c][o] multiplies channel c of head h
+ *              into output channel o of head h.
+ *   Each call first puts them into the kernels' layout inside the workspace
+ *   (a transposition, and the conversions of kvx_prepare_maps); callers that
+ *   translate repeatedly with the same maps prepare them once with
+ *   kvx_prepare_maps and call kvx_translate_prepared.
  * b_k, b_v: device fp32 bias [L_R][H_R*d_R], or NULL for none.  The bias is
  *   added before the receiver rotation.
  * workspace: device scratch of kvx_translate_workspace_size(...) bytes.
@@ -192,8 +197,10 @@ int kvx_layer_map(int32_t send_layers, int32_t recv_layers, int32_t n_taps,
  * low part (fp32 maps).  bf16 rows and maps (values, unrotated keys) have
  * bf16's range.
  * Supported: recv->dtype == send->dtype; bf16 caches need head_dim == 128
- * on both sides; recv->k_norm only on the flattened bf16 path
- * (KVX_ERR_UNSUPPORTED otherwise).
+ * on both sides, and flattened bf16 translation needs H_R*d_R a multiple of
+ * 256 (the kernel's output tile); fp32 caches take any head count and size
+ * up to 8192 features on either side; recv->k_norm only on the flattened
+ * bf16 path (KVX_ERR_UNSUPPORTED otherwise).
  * ---------------------------------------------------------------------- */
 size_t kvx_translate_workspace_size(const kvx_cache_desc* send,
                                     const kvx_cache_desc* recv,
@@ -296,9 +303,9 @@ int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const v
  *   centred Gram when fit_intercept != 0).
  * fit_intercept != 0: the bias is unpenalised; X and Y are centred by their
  *   column means, W solves the centred system and b = mean_y - mean_x W.
- * w_out: device fp32 [f_out][f_in] (output-major, the layout kvx_translate
- *   takes); b_out: device fp32 [f_out] (written only with fit_intercept; may
- *   be NULL otherwise).
+ * w_out: device fp32 [f_in][f_out], row-major (y = x W: the layout
+ *   kvx_translate and kvx_prepare_maps take); b_out: device fp32 [f_out]
+ *   (written only with fit_intercept; may be NULL otherwise).
  * workspace: device scratch of kvx_fit_ridge_workspace_size(f_in, f_out).
  * G and X^T Y are accumulated in fp32 on matrix cores; the solve (Cholesky
  * factorisation and two triangular solves) runs in fp64.
@@ -385,20 +392,67 @@ int kvx_translate_recorded(const kvx_cache_desc* send, const void* k_send, const
                            void* stream, void* const* events);
 
 /* ------------------------------------------------------------------------
+ * Prepared maps: the maps of one role put once into the layout the
+ * translation kernels read, so repeated translations with the same maps do
+ * no per-call conversion ("Cross-Model KV Cache Transfer in Production",
+ * stages 2 and 4: the projections are fixed once fitted and applied to every
+ * new cache).
+ *
+ * kvx_prepare_maps: w: device maps of `role` (0 = K, 1 = V) in the layout
+ *   kvx_translate takes (row-major [L_R][F_in][F_out], or [L_R][H][d][d] per
+ *   head), element type w_dtype (KVX_F32 or KVX_BF16).  prepared: device
+ *   buffer of kvx_prepared_maps_size(...) bytes that receives the kernel
+ *   layout: the maps transposed to output-major, and for flattened bf16
+ *   caches converted to the role's operand type: bf16, or fp16 for keys of a
+ *   rotated sender (send->rope_base > 0); fp32 maps split into a 16-bit high
+ *   and low part (each rounded to nearest even; the range limits of fp16
+ *   operands under kvx_translate apply).  The layout depends on send->dtype,
+ *   send->rope_base, per_head, role and w_dtype: a prepared buffer is valid
+ *   only for translations with the same values (and shapes).
+ *   Asynchronous on `stream`.  KVX_ERR_WORKSPACE when prepared_bytes is too
+ *   small.
+ *
+ * kvx_translate_prepared: kvx_translate with prepared maps pk, pv (either
+ *   NULL with its role skipped) of the given w_dtype, and optionally a
+ *   placement (`place`, as kvx_translate_placed; NULL = none) and three
+ *   events (`events`, as kvx_translate_recorded; NULL = none).  workspace:
+ *   kvx_translate_prepared_workspace_size(send, recv, n_taps, per_head,
+ *   pos_limit) bytes (pos_limit 0 without per-token positions), which holds
+ *   no maps.  Results are bit-identical to kvx_translate with the maps the
+ *   buffers were prepared from.  Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+size_t kvx_prepared_maps_size(const kvx_cache_desc* send, const kvx_cache_desc* recv,
+                              int32_t n_taps, int32_t per_head, int32_t role, int32_t w_dtype);
+int kvx_prepare_maps(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps,
+                     int32_t per_head, int32_t role, int32_t w_dtype, const void* w,
+                     void* prepared, size_t prepared_bytes, void* stream);
+size_t kvx_translate_prepared_workspace_size(const kvx_cache_desc* send,
+                                             const kvx_cache_desc* recv, int32_t n_taps,
+                                             int32_t per_head, int32_t pos_limit);
+int kvx_translate_prepared(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                           const kvx_cache_desc* recv, void* k_recv, void* v_recv,
+                           const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                           int32_t per_head, int32_t w_dtype, const void* pk, const void* pv,
+                           const float* b_k, const float* b_v, void* workspace, size_t ws_bytes,
+                           void* stream, const kvx_placement* place, void* const* events);
+
+/* ------------------------------------------------------------------------
  * FP8 map storage ("Cross-Model KV Cache Transfer in Production",
  * Implementation Guidelines: weight matrices may be stored quantised, e.g.
  * FP8, while the products keep 16-bit operands).
  *
- * kvx_quantize_fp8: w: device fp32 [rows][cols] (e.g. every map of one role,
- * rows = L_R * F_out output rows of F_in weights, output-major); per row,
- *   scale = amax / 448 (fp32, correctly rounded; 1 when that is 0),
- *   q = the nearest OCP E4M3 code of w / scale (fp32 quotient, correctly
+ * kvx_quantize_fp8: w: device fp32 [count][f_in][f_out], row-major maps
+ * (y = x W; e.g. every layer's map of one role, count = L_R).  Per map and
+ * output o:
+ *   scale = amax_f |w[f][o]| / 448 (fp32, correctly rounded; 1 when that is 0),
+ *   q = the nearest OCP E4M3 code of w[f][o] / scale (fp32 quotient, correctly
  *       rounded; ties to the even code; beyond 448 saturated to +-448),
- * so row r holds the values scale[r] * e4m3(q[r][c]).  q_out: device uint8
- * [rows][cols]; scale_out: device fp32 [rows].  Inputs must be finite.
- * Asynchronous on `stream`.
+ * so w[f][o] is stored as scale[o] * e4m3(q[o][f]).  q_out: device uint8
+ * [count][f_out][f_in] (output-major: the layout kvx_translate_fp8 reads);
+ * scale_out: device fp32 [count][f_out].  Inputs must be finite.  count up
+ * to 65535.  Asynchronous on `stream`.
  * ---------------------------------------------------------------------- */
-int kvx_quantize_fp8(const float* w, int64_t rows, int32_t cols, uint8_t* q_out,
+int kvx_quantize_fp8(const float* w, int32_t count, int32_t f_in, int32_t f_out, uint8_t* q_out,
                      float* scale_out, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -444,9 +498,9 @@ int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void
  *   KVX_ERR_UNSUPPORTED.
  * rho_x, rho_y >= 0: relative regularisers (rows that repeat a layer tap make
  *   S_xx singular; rho_x > 0 is then required).
- * w_out: HOST array of device fp32 [f_out][f_in] (output-major, the layout
- *   kvx_translate takes); b_out: HOST array of device fp32 [f_out]; neither
- *   may be NULL.
+ * w_out: HOST array of device fp32 [f_in][f_out] (row-major, y = x W + b,
+ *   the layout kvx_translate takes); b_out: HOST array of device fp32
+ *   [f_out]; neither may be NULL.
  * status: host int32 [count] or NULL; receives per problem KVX_OK,
  *   KVX_ERR_NOT_SPD (a regularised covariance is not positive definite) or
  *   KVX_ERR_NOT_CONVERGED (M numerically rank-deficient, so Q is not
@@ -475,16 +529,18 @@ int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void
  * Rank-r fold ("Prefill-Free ...", Methodology 3: low-rank corrections folded
  * into one fixed affine map per layer and role).
  *
- * For each of `count` maps: wt: device fp32 [f_out][f_in] (output-major);
- * a: device fp32 [f_in][rank]; b: device fp32 [f_out][rank];
- * w_out[o][f] = wt[o][f] + sum_r b[o][r] * a[f][r], each product rounded to
+ * For each of `count` maps, all row-major (y = x W): w: device fp32
+ * [f_in][f_out]; a: device fp32 [f_in][rank]; b: device fp32 [rank][f_out];
+ * W_eff = W + A B:
+ * w_out[f][o] = w[f][o] + sum_r a[f][r] * b[r][o], each product rounded to
  * fp32, the products summed in rank order r = 0, 1, ... in fp32 and the sum
- * added to wt[o][f] in fp32 (no fused multiply-add anywhere), then stored as
+ * added to w[f][o] in fp32 (no fused multiply-add anywhere), then stored as
  * out_dtype (bf16: nearest even).  The maps are consecutive in memory.
- * w_out: device, count*f_out*f_in elements; must not overlap the inputs.
- * Asynchronous on `stream`.
+ * w_out: device, count*f_in*f_out elements; must not overlap the inputs.
+ * The fold runs on the device (one pass over the maps), asynchronous on
+ * `stream`.
  * ---------------------------------------------------------------------- */
-int kvx_fold_lowrank(const float* wt, const float* a, const float* b, int32_t count,
+int kvx_fold_lowrank(const float* w, const float* a, const float* b, int32_t count,
                      int32_t f_in, int32_t f_out, int32_t rank, void* w_out,
                      int32_t out_dtype, void* stream);
 

@@ -194,9 +194,10 @@ def features(cache, src_rows, taps_of_layer, derotate_base: float = 0.0) -> np.n
 # A5/A7 affine maps and A6 re-rotation   [LB] stages 2 and 4; [HF] step 2
 
 
-def affine(x, wt, b=None) -> np.ndarray:
-    """y = x W + b with W stored output-major: wt[o][f] = W[f][o]."""
-    y = np.asarray(x, dtype=np.float64) @ np.asarray(wt, dtype=np.float64).T
+def affine(x, w, b=None) -> np.ndarray:
+    """y = x W + b, W row-major [F_in][F_out] (a row vector of features times
+    the map, as the blog writes K_content W_K)."""
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
     if b is not None:
         y = y + np.asarray(b, dtype=np.float64)[None, :]
     return y
@@ -215,7 +216,7 @@ def key_norm(y, weight, eps: float) -> np.ndarray:
     return y / np.sqrt(ms + eps) * w
 
 
-def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: bool,
+def translate_rows(send_cache, token_map, taps, w, bias, rows, *, per_head: bool,
                    recv_heads: int, recv_head_dim: int,
                    send_rope_base: float = 0.0, recv_rope_base: float = 0.0,
                    recv_key_norm=None, key_norm_eps: float = 1e-6) -> np.ndarray:
@@ -224,8 +225,9 @@ def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: boo
     ``rows``: receiver token indices to produce.  Returns float64
     [L_R][len(rows)][H_R*d_R], unrounded.
 
-    Flattened: y = features(...) W_l + b_l.  Per head (single tap, H and d
-    equal on both sides): y_h = x_h W_{l,h} + b_{l,h}, wt [L_R][H][d][d].
+    Flattened: y = features(...) W_l + b_l, w [L_R][F_in][F_out].  Per head
+    (single tap, H and d equal on both sides): y_h = x_h W_{l,h} + b_{l,h},
+    w [L_R][H][d][d] with w[l][h][c][o] taking input channel c to output o.
     Keys: with ``send_rope_base`` the sender keys are de-rotated at the sender
     position; with ``recv_rope_base`` the mapped key of receiver row i is
     rotated at position i (bias added before the rotation; values are never
@@ -242,13 +244,13 @@ def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: boo
         bl = None if bias is None else as_f64(bias[l])
         if per_head:
             d = recv_head_dim
-            w = as_f64(wt[l])
+            wl = as_f64(w[l])
             y = np.zeros((rows.size, recv_heads * d))
             for h in range(recv_heads):
-                y[:, h * d:(h + 1) * d] = affine(x[:, h * d:(h + 1) * d], w[h],
+                y[:, h * d:(h + 1) * d] = affine(x[:, h * d:(h + 1) * d], wl[h],
                                                  None if bl is None else bl[h * d:(h + 1) * d])
         else:
-            y = affine(x, as_f64(wt[l]), bl)
+            y = affine(x, as_f64(w[l]), bl)
         if recv_key_norm is not None:
             y = key_norm(y.reshape(rows.size, recv_heads, recv_head_dim), as_f64(recv_key_norm[l]),
                          key_norm_eps).reshape(rows.size, -1)
@@ -263,28 +265,29 @@ def translate_rows(send_cache, token_map, taps, wt, bias, rows, *, per_head: boo
 # A8  rank-16 fold   [HF] "Key Contributions" 3, "Methodology" step 3
 
 
-def fold_lowrank(wt, u, v):
+def fold_lowrank(w, a, b):
     """Fold a low-rank correction into a fixed map, in float32, then bf16.
 
-    W_eff = W + U V^T; stored output-major: wt_eff[o][f] = wt[o][f] +
-    sum_r v[o][r] u[f][r].  Reading of "fp32 then cast to bf16": each product
-    rounded to fp32, summed in rank order from r = 0 in fp32 (no fused
-    multiply-add), added to wt in fp32, then rounded to bf16 (nearest even).
-    Returns (fp32 sum, bf16 bits)."""
-    wt = np.asarray(wt, dtype=np.float32)
-    u = np.asarray(u, dtype=np.float32)
-    v = np.asarray(v, dtype=np.float32)
+    W_eff = W + A B with W [F_in][F_out], A [F_in][r], B [r][F_out]
+    (row-major, y = x W): w_eff[f][o] = w[f][o] + sum_r a[f][r] b[r][o].
+    Reading of "fp32 then cast to bf16": each product rounded to fp32, summed
+    in rank order from r = 0 in fp32 (no fused multiply-add), added to w in
+    fp32, then rounded to bf16 (nearest even).  Returns (fp32 sum, bf16
+    bits)."""
+    w = np.asarray(w, dtype=np.float32)
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
     acc = None
-    for r in range(u.shape[1]):
-        p = (v[:, r][:, None] * u[:, r][None, :]).astype(np.float32)
+    for r in range(a.shape[1]):
+        p = (a[:, r][:, None] * b[r, :][None, :]).astype(np.float32)
         acc = p if acc is None else (acc + p).astype(np.float32)
-    tot = wt if acc is None else (wt + acc).astype(np.float32)
+    tot = w if acc is None else (w + acc).astype(np.float32)
     return tot, f32_to_bf16_bits(tot)
 
 
-def fold_lowrank_f64(wt, u, v) -> np.ndarray:
+def fold_lowrank_f64(w, a, b) -> np.ndarray:
     """The same fold in float64, unrounded (for checking the fp32 order)."""
-    return np.asarray(wt, np.float64) + np.asarray(v, np.float64) @ np.asarray(u, np.float64).T
+    return np.asarray(w, np.float64) + np.asarray(a, np.float64) @ np.asarray(b, np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -410,9 +413,11 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def quantize_fp8(w32):
-    """Per-row FP8 storage of fp32 maps [rows][cols]: scale = amax / 448 and
-    codes of w / scale, both quotients in fp32 (correctly rounded); a row
-    whose scale is 0 gets scale 1.  Returns (codes uint8, scale float32)."""
+    """Per-row FP8 storage of fp32 values [rows][cols]: scale = amax / 448
+    and codes of w / scale, both quotients in fp32 (correctly rounded); a
+    row whose scale is 0 gets scale 1.  Returns (codes uint8, scale float32).
+    For a map W [F_in][F_out] the rows are its output channels: quantise W^T
+    (one scale per output), so W = fp8_dequant(codes, scale)^T."""
     w32 = np.asarray(w32, dtype=np.float32)
     amax = np.max(np.abs(w32), axis=-1)
     scale = (amax / np.float32(448.0)).astype(np.float32)

@@ -166,9 +166,10 @@ def test_other_entry_points_validate_before_launch():
     assert L.kvx_fit_recolor_workspace_size(64, 3072, 1024) > 64 * 8 * (3072 * 3072 + 2 * 3072 * 1024)
     assert L.kvx_fit_recolor_workspace_size(0, 3072, 1024) == 0
     assert kvx.status_string(kvx.ERR_NOT_CONVERGED) == "iteration did not converge"
-    assert L.kvx_quantize_fp8(fake, 0, 16, fake, fake, None) == kvx.OK
-    assert L.kvx_quantize_fp8(fake, 4, 0, fake, fake, None) == kvx.ERR_INVALID
-    assert L.kvx_quantize_fp8(fake, 4, 16, None, fake, None) == kvx.ERR_INVALID
+    assert L.kvx_quantize_fp8(fake, 0, 16, 16, fake, fake, None) == kvx.OK
+    assert L.kvx_quantize_fp8(fake, 4, 0, 16, fake, fake, None) == kvx.ERR_INVALID
+    assert L.kvx_quantize_fp8(fake, 4, 16, 0, fake, fake, None) == kvx.ERR_INVALID
+    assert L.kvx_quantize_fp8(fake, 4, 16, 16, None, fake, None) == kvx.ERR_INVALID
     assert L.kvx_align_tokens_async(fake, 5, fake, 5, fake, None, fake, 1 << 30, None) == kvx.ERR_INVALID
     assert L.kvx_align_tokens_async(fake, 5, fake, 5, fake, fake, None, 0, None) == kvx.ERR_WORKSPACE
     assert L.kvx_align_tokens_async(fake, 5, fake, 0, fake, None, None, 0, None) == kvx.OK   # empty receiver
@@ -181,3 +182,41 @@ def test_other_entry_points_validate_before_launch():
     bad = np.array([0, 4], np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     assert L.kvx_gather_features(ctypes.byref(s), fake, 0, fake, 3, bad, 2, fake, None) == kvx.ERR_INVALID
     assert L.kvx_gather_features(ctypes.byref(s), fake, 0, fake, 0, tp, 2, fake, None) == kvx.OK
+
+
+def test_prepared_maps_sizes_and_validation():
+    """Sizes of the kernel layout of prepared maps (16-bit operands for the
+    flattened bf16 path, hi|lo halves for fp32 maps, the map's own type per
+    head and for fp32 caches) and argument checks before anything runs."""
+    L = kvx.lib()
+    fake = ctypes.c_void_p(0x1000)
+    s, r = desc(36, 25000, 8, 128, rope=5e5), desc(32, 32768, 8, 128, rope=1e6)
+    n = 32 * 3072 * 1024
+    size = lambda *a: L.kvx_prepared_maps_size(ctypes.byref(a[0]), ctypes.byref(a[1]), *a[2:])
+    assert size(s, r, 3, 0, 0, kvx.BF16) == 2 * n          # fp16 keys
+    assert size(s, r, 3, 0, 1, kvx.BF16) == 2 * n          # bf16 values
+    assert size(s, r, 3, 0, 0, kvx.F32) == 4 * n           # hi|lo halves
+    ps, pr = desc(32, 4096, 8, 128), desc(80, 4096, 8, 128)
+    assert size(ps, pr, 1, 1, 0, kvx.F32) == 80 * 8 * 128 * 128 * 4
+    assert size(ps, pr, 1, 1, 1, kvx.BF16) == 80 * 8 * 128 * 128 * 2
+    fs, fr = desc(5, 100, 2, 64, kvx.F32), desc(3, 90, 2, 64, kvx.F32)
+    assert size(fs, fr, 3, 0, 0, kvx.F32) == 3 * 384 * 128 * 4
+    assert size(s, r, 3, 0, 2, kvx.BF16) == 0              # no such role
+    assert size(s, r, 3, 0, 0, 5) == 0
+    prep = lambda *a, **k: L.kvx_prepare_maps(ctypes.byref(a[0]), ctypes.byref(a[1]), *a[2:])
+    assert prep(s, r, 3, 0, 0, kvx.BF16, fake, fake, 16, None) == kvx.ERR_WORKSPACE
+    assert prep(s, r, 3, 0, 0, kvx.BF16, None, fake, 1 << 40, None) == kvx.ERR_INVALID
+    assert prep(s, r, 3, 1, 0, kvx.BF16, fake, fake, 1 << 40, None) == kvx.ERR_SHAPE   # per head: one tap
+    assert prep(s, r, 3, 0, 3, kvx.BF16, fake, fake, 1 << 40, None) == kvx.ERR_INVALID
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tp = taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    ws_prep = L.kvx_translate_prepared_workspace_size(ctypes.byref(s), ctypes.byref(r), 3, 0, 0)
+    assert 0 < ws_prep < kvx.translate_workspace_size(s, r, 3, False)   # no maps in it
+
+    def tpp(w_dtype=kvx.BF16, ws_bytes=1 << 40, events=None):
+        return L.kvx_translate_prepared(ctypes.byref(s), fake, fake, ctypes.byref(r), fake, fake, fake, tp, 3, 0,
+                                        w_dtype, fake, fake, None, None, fake, ws_bytes, None, None, events)
+
+    assert tpp(w_dtype=2) == kvx.ERR_INVALID
+    assert tpp(ws_bytes=16) == kvx.ERR_WORKSPACE
+    assert tpp(events=(ctypes.c_void_p * 3)(0x1000, 0, 0x1000)) == kvx.ERR_INVALID

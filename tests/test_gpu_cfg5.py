@@ -112,7 +112,7 @@ def test_cfg5_fit_vs_oracle(cal):
             wo, _, lam = O.ridge_fit(x, y, lam_rel=LAM_REL)
             cal["oracle_w"][(role, l)] = wo
             del x, y
-            w = cal["ws"][problem(role, l)].cpu().numpy().astype(np.float64).T
+            w = cal["ws"][problem(role, l)].cpu().numpy().astype(np.float64)
             err = O.rel_err(w, wo)
             say(f"  {role} layer {l}: W max|err|/RMS = {err:.3e} (lambda {lam:.5g})")
             assert err <= TOL_BF16
@@ -128,7 +128,7 @@ def test_cfg5_fit_normal_equations_all_problems(cal):
         xd = cal["xs"][p].double()
         yd = cal["ys"][p].double()
         lam = LAM_REL * float((xd * xd).sum()) / 3072
-        w = cal["ws"][p].double().T.contiguous()  # [3072][1024], y = x W
+        w = cal["ws"][p].double()  # [3072][1024], y = x W
         for _ in range(3):
             r = torch.as_tensor(rng.standard_normal(1024), device=DEV)
             wr = w @ r
@@ -163,7 +163,7 @@ def test_cfg5_translate_fresh_cache_with_fitted_maps(cal):
     rows = sample_rows(tmap_o, 256, 6)
     sel = np.asarray(CHECK_LAYERS)
     for role, out in (("k", k), ("v", v)):
-        wo = [cal["oracle_w"][(role, l)].T for l in CHECK_LAYERS]  # output-major, as translate_rows takes
+        wo = [cal["oracle_w"][(role, l)] for l in CHECK_LAYERS]
         want = O.translate_rows(caches[role], tmap_o, taps[sel], wo, None, rows, per_head=False, recv_heads=8,
                                 recv_head_dim=128)
         got = rows_of(out, rows)[sel]

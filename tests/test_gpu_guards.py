@@ -20,7 +20,7 @@ import torch
 
 from cross_model_kv_kvx_amd import kvx, synth
 from oracle import kvx_oracle as O
-from tests.kvx_cases import TOL_BF16, TOL_F32, rows_of
+from tests.kvx_cases import TOL_BF16, TOL_F32, bf16_floor, rows_of
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -112,8 +112,9 @@ def flat_setting(map_kind, n_recv=300, seed=120, clamp=False, L_S=10, L_R=8):
             maps[role] = (wt, Maps(wt.cpu()))
         else:
             q, sc = kvx.quantize_fp8(wt)
-            qo, so = O.quantize_fp8(wt.cpu().numpy())
-            maps[role] = ((q, sc), [O.fp8_dequant(qo[l], so[l]) for l in range(L_R)])
+            wh = wt.cpu().numpy()
+            qs = [O.quantize_fp8(np.ascontiguousarray(wh[l].T)) for l in range(L_R)]  # one scale per output
+            maps[role] = ((q, sc), [O.fp8_dequant(qo, so).T for qo, so in qs])
         bias[role] = b
     pad_o = 64 * 1024
     outs = {role: guarded((L_R, n_recv, 8, 128), torch.bfloat16, pad_o) for role in ("k", "v")}
@@ -243,9 +244,16 @@ def test_flat_rotated_keys_large_values_small_maps(map_kind):
     """The fp16 operand path of rotated-back keys at the edges of its range:
     outlier channels of about 1e3 (fp16 holds up to 65504 with 11 significant
     bits) and map entries of about 1e-5 (below fp16's smallest normal,
-    6.1e-5: the bf16 map converted to fp16, or the fp32 map split into fp16
-    high and low parts, keeps an absolute error of at most 2^-25 per entry).
-    Every element of 300 receiver tokens vs the oracle."""
+    6.1e-5).  Every element of 300 receiver tokens is checked against a bound
+    derived from the operand types: the map entries reach the products with
+    an absolute error of at most 2^-25 (bf16 -> fp16; fp32 maps also lose
+    2^-22 relative in the high/low split), the rotated keys with a relative
+    error of 2^-11, the fp32 sums add at most 2^-16 of sum |x w|, the
+    receiver rotation mixes the two members of a pair (bounds added), and
+    the output is rounded to bf16 (half an ulp of the result).  max|err|/RMS
+    is printed beside the bf16 floor: with outliers this large the rounding
+    of the outputs alone reaches the 2e-2 of the bf16 bar, so the bar itself
+    is not the check here."""
     say(f"rotated keys with outliers ~1e3, {map_kind} maps with entries ~1e-5")
     L_S, L_R, n_recv, seed = 10, 8, 300, 150
     send_end, recv_end = synth.token_ends(n_recv, seed)
@@ -253,18 +261,31 @@ def test_flat_rotated_keys_large_values_small_maps(map_kind):
     taps = kvx.layer_map(L_S, L_R, 3, 2)
     tmap_o = O.token_align(send_end, recv_end)
     k = synth.sender_cache(shp, seed * 10, DEV, outlier_frac=0.01, outlier_scale=1000.0, outlier_pairs=True)
-    wt, _, _, b = synth.flat_maps(L_R, 3072, 1024, seed * 10 + 5, DEV, 4)
-    wt = wt * 5e-4  # N(0,1)/sqrt(3072) * 5e-4: entries of about 1e-5
+    w32, _, _, b = synth.flat_maps(L_R, 3072, 1024, seed * 10 + 5, DEV, 4)
+    w32 = w32 * 5e-4  # N(0,1)/sqrt(3072) * 5e-4: entries of about 1e-5
     b = b * 1e-2
-    w = wt.to(torch.bfloat16) if map_kind == "bf16" else wt
+    w = w32.to(torch.bfloat16) if map_kind == "bf16" else w32
     out, _ = kvx.translate(k, None, dev_i32(tmap_o), taps, w, None, b, None, send_rope_base=5e5,
                            recv_rope_base=1e6)
     torch.cuda.synchronize()
     rows = np.arange(n_recv)
-    want = O.translate_rows(k, tmap_o, taps, Maps(w.cpu()), O.as_f64(b), rows, per_head=False, recv_heads=8,
+    wm = Maps(w.cpu())
+    want = O.translate_rows(k, tmap_o, taps, wm, O.as_f64(b), rows, per_head=False, recv_heads=8,
                             recv_head_dim=128, send_rope_base=5e5, recv_rope_base=1e6)
     got = rows_of(out, rows)
     assert np.all(np.isfinite(got))
+    c_rel = 2.0 ** -11 + 2.0 ** -16 + (2.0 ** -22 if map_kind == "f32" else 0.0)
+    worst = 0.0
+    for l in range(L_R):
+        x = O.features(k, tmap_o[rows], taps[l], 5e5)
+        bound = 2.0 ** -25 * np.abs(x).sum(axis=1)[:, None] + c_rel * (np.abs(x) @ np.abs(wm[l]))
+        bh = bound.reshape(n_recv, 8, 2, 64)
+        pair = (bh[:, :, 0] + bh[:, :, 1])[:, :, None, :]          # the rotation mixes c and c + 64
+        bound = np.broadcast_to(pair, bh.shape).reshape(n_recv, 1024)
+        g = got[l]
+        half_ulp = np.where(g != 0, 2.0 ** (np.floor(np.log2(np.abs(np.where(g != 0, g, 1.0)))) - 8), 0.0)
+        excess = np.abs(g - want[l]) - (bound + half_ulp)
+        worst = max(worst, float(np.max(np.abs(g - want[l]) / (bound + half_ulp))))
+        assert np.all(excess <= 0), f"layer {l}: error above the operand bound"
     err = O.rel_err(got, want)
-    say(f"  max|err|/RMS = {err:.4e}")
-    assert err <= TOL_BF16
+    say(f"  max|err|/RMS = {err:.4e} (bf16 floor {bf16_floor(want):.4e}); worst error / bound = {worst:.3f}")

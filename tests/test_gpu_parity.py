@@ -90,11 +90,11 @@ def test_fold_bit_exact():
 # ---------------------------------------------------------------- cfg1: fp32 per-head fit + translate
 
 
-def cfg1_receiver(x, wt, b, noise):
+def cfg1_receiver(x, w, b, noise):
     """The matched receiver of the fp32 single-layer setting, built on the
-    host: y_h = x_h W_true,h^T + b_h + noise (W stored output-major)."""
+    host: y_h = x_h W_true,h + b_h + noise (w[0][h][c][o], row-major)."""
     xs = x.double()
-    y = torch.einsum("lnhc,hoc->lnho", xs, wt[0].double()) + b.double().reshape(1, 1, wt.shape[1], -1)
+    y = torch.einsum("lnhc,hco->lnho", xs, w[0].double()) + b.double().reshape(1, 1, w.shape[1], -1)
     return (y + noise.double()).float()
 
 
@@ -115,11 +115,11 @@ def test_cfg1_fit_and_translate_fp32():
             w, b = kvx.fit_ridge(xg[0, :, h, :], yg[0, :, h, :], lambda_abs=1e-2, fit_intercept=True)
             wo, bo_h, lam = O.ridge_fit(O.as_f64(c[f"x_cal_{role}"][0, :, h, :]), O.as_f64(y_cal[0, :, h, :]),
                                         lam_abs=1e-2, fit_intercept=True)
-            assert O.rel_err(w.cpu().numpy(), wo.T) <= TOL_F32
+            assert O.rel_err(w.cpu().numpy(), wo) <= TOL_F32
             assert O.rel_err(b.cpu().numpy(), bo_h) <= TOL_F32
             wts.append(w)
             bs.append(b)
-            wto.append(wo.T)
+            wto.append(wo)
             bo.append(bo_h)
         maps_g[role] = (torch.stack(wts)[None].contiguous(), torch.cat(bs)[None].contiguous())
         maps_o[role] = (np.stack(wto)[None], np.concatenate(bo)[None])
@@ -146,17 +146,17 @@ def run_cfg2(n_tokens, rows=None, seed=2):
         c["send_end"], c["recv_end"] = synth.identical_ends(n_tokens, seed)
         for r, role in enumerate(("k", "v")):
             c[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, DEV, channel_scale="loguniform")
-            c[f"wt_{role}"], c[f"b_{role}"] = synth.perhead_maps(80, 8, 128, seed * 100 + 20 + r, DEV)
+            c[f"w_{role}"], c[f"b_{role}"] = synth.perhead_maps(80, 8, 128, seed * 100 + 20 + r, DEV)
     taps = kvx.layer_map(32, 80, 1)
     tmap = kvx.align_tokens(dev_i32(c["send_end"]), dev_i32(c["recv_end"]))
     tmap_o = O.token_align(c["send_end"], c["recv_end"])
     assert np.array_equal(tmap.cpu().numpy(), tmap_o)
-    k, v = kvx.translate(c["k_send"], c["v_send"], tmap, taps, c["wt_k"], c["wt_v"], c["b_k"], c["b_v"],
+    k, v = kvx.translate(c["k_send"], c["v_send"], tmap, taps, c["w_k"], c["w_v"], c["b_k"], c["b_v"],
                          per_head=True)
     n = tmap_o.size
     rows = np.arange(n) if rows is None else rows
     for role, out in (("k", k), ("v", v)):
-        want = O.translate_rows(c[f"{role}_send"], tmap_o, taps, host(c[f"wt_{role}"]), host(c[f"b_{role}"]), rows,
+        want = O.translate_rows(c[f"{role}_send"], tmap_o, taps, host(c[f"w_{role}"]), host(c[f"b_{role}"]), rows,
                                 per_head=True, recv_heads=8, recv_head_dim=128)
         got = rows_of(out, rows)
         err = O.rel_err(got, want)
@@ -352,7 +352,7 @@ def test_cfg4_flat_rope_full_sampled_rows():
 
 
 class F32Maps:
-    """fp32 maps [L][F_out][F_in] (host), handed to the oracle one layer at a
+    """fp32 maps [L][F_in][F_out] (host), handed to the oracle one layer at a
     time as fp64."""
 
     def __init__(self, a):
@@ -561,8 +561,8 @@ def test_translate_deterministic_and_identity_maps():
     # flattened [0; I; 0] selects the centre tap exactly (bf16 in, bf16 out)
     L, N, F = 6, 300, 1024
     x = synth.sender_cache(synth.CacheShape(L, N, 8, 128), 77, DEV)
-    sel = torch.zeros((L, F, 3 * F), dtype=torch.bfloat16, device=DEV)
-    sel[:, :, F:2 * F] = torch.eye(F, dtype=torch.bfloat16, device=DEV)
+    sel = torch.zeros((L, 3 * F, F), dtype=torch.bfloat16, device=DEV)
+    sel[:, F:2 * F, :] = torch.eye(F, dtype=torch.bfloat16, device=DEV)
     ident = dev_i32(np.arange(N))
     taps6 = kvx.layer_map(L, L, 3, 1)
     ky, _ = kvx.translate(x, None, ident, taps6, sel, None)
@@ -632,7 +632,7 @@ def test_fit_ridge_vs_oracle(layer):
     xo = O.features(c["k_send"], tmap_o, taps[layer])
     yo = O.as_f64(c["recv_k"][layer]).reshape(4096, 1024)
     wo, _, lam = O.ridge_fit(xo, yo, lam_rel=1e-3)
-    err = O.rel_err(w.cpu().numpy(), wo.T)
+    err = O.rel_err(w.cpu().numpy(), wo)
     say(f"  W max|err|/RMS = {err:.3e} (lambda {lam:.4g})")
     assert err <= TOL_BF16
     if layer in (0, 31):
@@ -642,7 +642,7 @@ def test_fit_ridge_vs_oracle(layer):
         t = taps[layer]
         a, b = [(i, j) for i in range(3) for j in range(i + 1, 3) if t[i] == t[j]][0]
         wn = w.cpu().numpy().astype(np.float64)
-        gap = np.max(np.abs(wn[:, a * 1024:(a + 1) * 1024] - wn[:, b * 1024:(b + 1) * 1024]))
+        gap = np.max(np.abs(wn[a * 1024:(a + 1) * 1024] - wn[b * 1024:(b + 1) * 1024]))
         say(f"  duplicated-block gap / RMS = {gap / np.sqrt(np.mean(wn * wn)):.3e}")
         assert gap <= 1e-6 * np.sqrt(np.mean(wn * wn))
 
@@ -679,7 +679,7 @@ def test_fit_batched_matches_single_and_oracle():
         assert torch.equal(w, w1), f"layer {l}: batched and single fits differ"
         wo, _, _ = O.ridge_fit(O.features(c["k_send"], tmap_o, taps[l]),
                                O.as_f64(c["recv_k"][l]).reshape(4096, 1024), lam_rel=1e-3)
-        err = O.rel_err(w.cpu().numpy(), wo.T)
+        err = O.rel_err(w.cpu().numpy(), wo)
         say(f"  layer {l}: W max|err|/RMS = {err:.3e}")
         assert err <= TOL_BF16
 
@@ -704,7 +704,7 @@ def test_fit_batched_many_problems_vs_oracle():
     assert st == [kvx.OK] * count
     for i in (0, 13, 31):
         wo, bo, _ = O.ridge_fit(O.as_f64(xs[i]), O.as_f64(ys[i]), lam_rel=1e-3, fit_intercept=True)
-        err_w = O.rel_err(ws[i].cpu().numpy(), wo.T)
+        err_w = O.rel_err(ws[i].cpu().numpy(), wo)
         err_b = O.rel_err(bs[i].cpu().numpy(), bo)
         w1, b1 = kvx.fit_ridge(xs[i], ys[i], lambda_rel=1e-3, fit_intercept=True)
         d_w = O.rel_err(ws[i].cpu().numpy(), w1.cpu().numpy().astype(np.float64))
@@ -732,7 +732,7 @@ def test_fit_batched_flags_each_problem():
     w1, b1 = kvx.fit_ridge(x0, ys[0], fit_intercept=True)
     assert torch.equal(ws[0], w1) and torch.equal(bs[0], b1)
     wo, bo, _ = O.ridge_fit(O.as_f64(x0), O.as_f64(ys[0]), fit_intercept=True)
-    err_w = O.rel_err(ws[0].cpu().numpy(), wo.T)
+    err_w = O.rel_err(ws[0].cpu().numpy(), wo)
     err_b = O.rel_err(bs[0].cpu().numpy(), bo)
     say(f"  W max|err|/RMS = {err_w:.3e}, b {err_b:.3e}")
     assert err_w <= TOL_F32 and err_b <= TOL_F32
@@ -754,7 +754,7 @@ def test_fit_ragged_shapes(n, f_in, ld_pad, f_out):
     y = torch.randn((n, f_out), generator=g, device=DEV).to(torch.bfloat16)
     w, _ = kvx.fit_ridge(x, y, lambda_rel=1e-3)
     wo, _, _ = O.ridge_fit(O.as_f64(x), O.as_f64(y), lam_rel=1e-3)
-    err = O.rel_err(w.cpu().numpy(), wo.T)
+    err = O.rel_err(w.cpu().numpy(), wo)
     say(f"  W max|err|/RMS = {err:.3e}")
     assert err <= TOL_F32
 
@@ -774,7 +774,7 @@ def test_fit_full_size_normal_equations():
     tmap_o = O.token_align(c["send_end"], c["recv_end"])
     X = O.features(c["k_send"], tmap_o, taps[layer])
     Y = O.as_f64(c["recv_k"][layer]).reshape(65536, 1024)
-    W = w.cpu().numpy().astype(np.float64).T
+    W = w.cpu().numpy().astype(np.float64)
     lam = 1e-3 * float(np.einsum("ij,ij->", X, X)) / 3072
     rng = np.random.default_rng(0)
     for _ in range(3):
@@ -791,7 +791,7 @@ def test_fit_full_size_normal_equations():
 
 
 def _recolor_err(w, b, wo, bo):
-    return O.rel_err(w.cpu().numpy(), wo.T), O.rel_err(b.cpu().numpy(), bo)
+    return O.rel_err(w.cpu().numpy(), wo), O.rel_err(b.cpu().numpy(), bo)
 
 
 @pytest.mark.parametrize("n,f_in,f_out", [(512, 64, 64), (700, 128, 64), (1000, 264, 72), (2100, 520, 136)])
@@ -812,7 +812,7 @@ def test_recolor_f32_vs_oracle(n, f_in, f_out):
     say(f"  W max|err|/RMS = {ew:.3e}, b {eb:.3e}, {info['iters']} polar iterations")
     assert ew <= TOL_F32 and eb <= TOL_F32
     # moments of the translated calibration rows, from the oracle's data
-    t = O.as_f64(xt) @ w.cpu().numpy().astype(np.float64).T + b.cpu().numpy()
+    t = O.as_f64(xt) @ w.cpu().numpy().astype(np.float64) + b.cpu().numpy()
     ym = O.as_f64(yt)
     assert np.max(np.abs(t.mean(0) - ym.mean(0))) <= 1e-4 * np.sqrt(np.mean(ym * ym))
     ct = np.cov(t.T, bias=True)
@@ -834,7 +834,7 @@ def test_recolor_recovers_planted_map():
     (w,), (b,) = kvx.fit_recolor([xt], [yt])
     # the relation holds up to the fp32 rounding of y
     an = a.cpu().numpy()
-    ea = np.max(np.abs(w.cpu().numpy().T - an)) / np.sqrt(np.mean(an * an))
+    ea = np.max(np.abs(w.cpu().numpy() - an)) / np.sqrt(np.mean(an * an))
     ec = np.max(np.abs(b.cpu().numpy() - c.cpu().numpy()))
     say(f"  |W - A| / RMS(A) = {ea:.3e}, |b - c| = {ec:.3e}")
     assert ea <= 1e-4 and ec <= 1e-4
@@ -922,8 +922,9 @@ def test_recolor_full_size_vs_oracle():
 
 
 class Fp8Maps:
-    """Oracle-quantised maps (codes and scales); indexing a layer gives its
-    float64 values."""
+    """Oracle-quantised maps (codes [L][F_out][F_in] and scales [L][F_out]:
+    one scale per output); indexing a layer gives its float64 map, row-major
+    [F_in][F_out]."""
 
     def __init__(self, q, sc):
         self.q, self.sc = q, sc
@@ -932,7 +933,15 @@ class Fp8Maps:
         return len(self.q)
 
     def __getitem__(self, l):
-        return O.fp8_dequant(self.q[l], self.sc[l])
+        return O.fp8_dequant(self.q[l], self.sc[l]).T
+
+
+def oracle_fp8(w):
+    """The oracle's fp8 storage of row-major maps w [L][F_in][F_out] (host
+    array): each layer's output channels quantised (O.quantize_fp8 of W^T).
+    Returns (codes [L][F_out][F_in], scales [L][F_out])."""
+    qs = [O.quantize_fp8(np.ascontiguousarray(w[l].T)) for l in range(w.shape[0])]
+    return np.stack([q for q, _ in qs]), np.stack([s_ for _, s_ in qs])
 
 
 _MAPS8 = {}
@@ -951,12 +960,7 @@ def fp8_maps(k):
             g = kvx.fold_lowrank(wt, u, v, torch.float32)
             q, sc = kvx.quantize_fp8(g)
             wh, uh, vh = host(wt).numpy(), host(u).numpy(), host(v).numpy()
-            qo, so = [], []
-            for l in range(32):
-                a, s_ = O.quantize_fp8(O.fold_lowrank(wh[l], uh[l], vh[l])[0])
-                qo.append(a)
-                so.append(s_)
-            qo, so = np.stack(qo), np.stack(so)
+            qo, so = oracle_fp8(np.stack([O.fold_lowrank(wh[l], uh[l], vh[l])[0] for l in range(32)]))
             assert np.array_equal(host(q).numpy(), qo), "fp8 codes differ from the oracle's"
             assert np.array_equal(host(sc).numpy().view(np.uint32), so.view(np.uint32)), "fp8 scales differ"
             out[role] = (q, sc, b, Fp8Maps(qo, so), host(b).numpy().astype(np.float64))
@@ -998,7 +1002,8 @@ def test_fp8_quantize_special_rows():
     w[4, 7] = 1.0
     w[5] = np.float32(448.0) * (np.arange(3072) % 253 - 126).astype(np.float32) / np.float32(126.0)
     w[6, :10] = [448.0, 464.0, 15.5, -15.5, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9, 17.0, 1.0, -0.0]
-    q, sc = kvx.quantize_fp8(torch.as_tensor(w, device=DEV))
+    # the rows are the output channels of one map W = w^T [3072][9]
+    q, sc = kvx.quantize_fp8(torch.as_tensor(np.ascontiguousarray(w.T), device=DEV))
     qo, so = O.quantize_fp8(w)
     assert np.array_equal(q.cpu().numpy(), qo)
     assert np.array_equal(sc.cpu().numpy().view(np.uint32), so.view(np.uint32))
@@ -1058,7 +1063,7 @@ def test_fp8_maps_key_norm_all_elements():
                                           outlier_pairs=(role == "k"))
         wt, u, v, b = synth.flat_maps(32, 3072, 1024, 8500 + r, DEV, 16)
         q, sc = kvx.quantize_fp8(wt)
-        qo, so = O.quantize_fp8(host(wt).numpy())
+        qo, so = oracle_fp8(host(wt).numpy())
         assert np.array_equal(host(q).numpy(), qo)
         assert np.array_equal(host(sc).numpy().view(np.uint32), so.view(np.uint32))
         q8[role] = (q, sc, Fp8Maps(qo, so))
@@ -1142,7 +1147,7 @@ def test_fp8_short_k_all_elements(n_taps, heads):
         caches[role] = synth.sender_cache(shp, 9300 + r, DEV)
         wt, u, v, b = synth.flat_maps(L_R, f_in, 256, 9400 + r, DEV, 4)
         q, sc = kvx.quantize_fp8(wt)
-        qo, so = O.quantize_fp8(host(wt).numpy())
+        qo, so = oracle_fp8(host(wt).numpy())
         assert np.array_equal(host(q).numpy(), qo)
         q8[role] = (q, sc, Fp8Maps(qo, so))
         bias[role] = b
@@ -1192,3 +1197,79 @@ def test_async_align_and_recorded_translate():
     prep, main = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
     say(f"  recorded phases: preparation {prep:.3f} ms, translation {main:.3f} ms")
     assert prep >= 0.0 and main > 0.0
+
+
+@pytest.mark.parametrize("case", ["flat_bf16_rope", "flat_f32_rope", "flat_bf16_plain", "perhead_f32_rope",
+                                  "perhead_bf16", "f32_caches"])
+def test_prepared_maps_equal_raw_maps(case):
+    """kvx_prepare_maps + kvx_translate_prepared give the outputs of
+    kvx_translate with the same row-major maps, bit for bit (the raw call
+    prepares the same layout in its workspace), and the prepared call with a
+    placement and events equals the raw placed call."""
+    say(f"prepared maps vs raw maps: {case}")
+    per_head = case.startswith("perhead")
+    f32c = case == "f32_caches"
+    rope = "rope" in case or f32c
+    n_recv = 300
+    send_end, recv_end = synth.token_ends(n_recv, 160)
+    tm = dev_i32(O.token_align(send_end, recv_end))
+    if f32c:
+        L_S, L_R, H, d, n_taps = 5, 3, 2, 64, 3
+    elif per_head:
+        L_S, L_R, H, d, n_taps = 6, 14, 8, 128, 1
+    else:
+        L_S, L_R, H, d, n_taps = 10, 8, 8, 128, 3
+    shp = synth.CacheShape(L_S, len(send_end), H, d)
+    taps = kvx.layer_map(L_S, L_R, n_taps, 2)
+    dt = torch.float32 if f32c else torch.bfloat16
+    caches, maps, bias = {}, {}, {}
+    for r, role in enumerate(("k", "v")):
+        caches[role] = synth.sender_cache(shp, 1600 + r, DEV, dt)
+        if per_head:
+            w, b = synth.perhead_maps(L_R, H, d, 1610 + r, DEV)
+        else:
+            w, _, _, b = synth.flat_maps(L_R, n_taps * H * d, H * d, 1610 + r, DEV, 2)
+        maps[role] = w.to(torch.bfloat16) if "bf16" in case else w
+        bias[role] = b
+    sb, rb = (1e4, 1e4) if f32c else ((5e5, 1e6) if rope else (0.0, 0.0))
+    send = kvx.cache_desc(caches["k"], sb)
+    recv = kvx.CacheDesc(L_R, n_recv, H, d, kvx.F32 if f32c else kvx.BF16, rb)
+    w_dtype = kvx.BF16 if "bf16" in case else kvx.F32
+    pk = kvx.prepare_maps(maps["k"], "k", send, recv, n_taps, per_head)
+    pv = kvx.prepare_maps(maps["v"], "v", send, recv, n_taps, per_head)
+    kw = dict(per_head=per_head, send_rope_base=sb, recv_rope_base=rb)
+    k1, v1 = kvx.translate(caches["k"], caches["v"], tm, taps, maps["k"], maps["v"], bias["k"], bias["v"], **kw)
+    k2, v2 = kvx.translate(caches["k"], caches["v"], tm, taps, pk, pv, bias["k"], bias["v"], prepared=True,
+                           w_dtype=w_dtype, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    # the oracle on the same row-major maps
+    rows = np.arange(n_recv)
+    tol = TOL_F32 if f32c else TOL_BF16
+    for role, out in (("k", k2), ("v", v2)):
+        rk = role == "k"
+        want = O.translate_rows(caches[role], O.token_align(send_end, recv_end), taps, O.as_f64(maps[role]),
+                                O.as_f64(bias[role]), rows, per_head=per_head, recv_heads=H, recv_head_dim=d,
+                                send_rope_base=sb if rk else 0.0, recv_rope_base=rb if rk else 0.0)
+        err = O.rel_err(rows_of(out, rows), want)
+        say(f"  {role}: max|err|/RMS = {err:.4e}")
+        assert err <= tol
+    if f32c:
+        return
+    # placement and events on the prepared path vs the raw placed call
+    pool = n_recv + 40
+    slot = torch.as_tensor(np.random.default_rng(3).permutation(pool)[:n_recv], device=DEV)
+    outs = {}
+    for name, prep in (("raw", False), ("prepared", True)):
+        o = {role: torch.full((L_R, pool, H, d), 3.0, dtype=torch.bfloat16, device=DEV) for role in "kv"}
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if prep else None
+        if ev:
+            for e in ev:
+                e.record()
+        kvx.translate(caches["k"], caches["v"], tm, taps, pk if prep else maps["k"], pv if prep else maps["v"],
+                      bias["k"], bias["v"], k_recv=o["k"], v_recv=o["v"], slot=slot, pool_rows=pool,
+                      prepared=prep, w_dtype=w_dtype if prep else None, events=ev, **kw)
+        outs[name] = o
+    torch.cuda.synchronize()
+    for role in "kv":
+        assert torch.equal(outs["raw"][role], outs["prepared"][role])

@@ -71,7 +71,7 @@ def test_rope_identities():
 
 # ---------------------------------------------------------------- features / affine / translate
 
-def brute_translate(cache, tmap, taps, wt, b, rows, H, d, per_head, sb, rb):
+def brute_translate(cache, tmap, taps, w, b, rows, H, d, per_head, sb, rb):
     """Element-by-element loops over a tiny problem (no numpy matmul)."""
     L_R = len(taps)
     out = np.zeros((L_R, len(rows), H * d))
@@ -94,9 +94,9 @@ def brute_translate(cache, tmap, taps, wt, b, rows, H, d, per_head, sb, rb):
             for o in range(H * d):
                 if per_head:
                     h, c = divmod(o, d)
-                    s = sum(feat[h * d + f] * wt[li][h][c][f] for f in range(d))
+                    s = sum(feat[h * d + f] * w[li][h][f][c] for f in range(d))
                 else:
-                    s = sum(feat[f] * wt[li][o][f] for f in range(len(feat)))
+                    s = sum(feat[f] * w[li][f][o] for f in range(len(feat)))
                 y.append(s + (b[li][o] if b is not None else 0.0))
             if rb:
                 for h in range(H):
@@ -122,14 +122,14 @@ def test_translate_rows_vs_brute_force(per_head, sb, rb):
     taps = O.layer_taps(L_S, L_R, n_taps, 2)
     tmap = np.array([0, 0, 1, 3, 3, 3, 4, 8])
     if per_head:
-        wt = rng.standard_normal((L_R, H, d, d))
+        w = rng.standard_normal((L_R, H, d, d))
     else:
-        wt = rng.standard_normal((L_R, H * d, n_taps * H * d))
+        w = rng.standard_normal((L_R, n_taps * H * d, H * d))
     b = rng.standard_normal((L_R, H * d))
     rows = np.arange(len(tmap))
-    got = O.translate_rows(cache, tmap, taps, wt, b, rows, per_head=per_head, recv_heads=H,
+    got = O.translate_rows(cache, tmap, taps, w, b, rows, per_head=per_head, recv_heads=H,
                            recv_head_dim=d, send_rope_base=sb, recv_rope_base=rb)
-    want = brute_translate(cache, tmap, taps, wt, b, rows, H, d, per_head, sb, rb)
+    want = brute_translate(cache, tmap, taps, w, b, rows, H, d, per_head, sb, rb)
     assert np.max(np.abs(got - want)) < 1e-12
 
 
@@ -138,7 +138,7 @@ def test_one_row_by_hand():
     # y = (1*1 + 2*3, 1*2 + 2*4) + b = (7.5, 9)
     cache = np.array([[[[1.0, 2.0]]]])
     W = np.array([[1.0, 2.0], [3.0, 4.0]])
-    y = O.translate_rows(cache, [0], [[0]], [W.T], [[0.5, -1.0]], [0], per_head=False,
+    y = O.translate_rows(cache, [0], [[0]], [W], [[0.5, -1.0]], [0], per_head=False,
                          recv_heads=1, recv_head_dim=2)
     assert np.array_equal(y, [[[7.5, 9.0]]])
 
@@ -153,8 +153,8 @@ def test_identity_maps_reproduce_input_exactly():
     assert np.array_equal(y, cache.reshape(L, N, H * d).astype(np.float64))
     # flattened [0; I; 0] selects the centre tap exactly
     F = H * d
-    sel = np.zeros((L, F, 3 * F))
-    sel[:, :, F:2 * F] = np.eye(F)
+    sel = np.zeros((L, 3 * F, F))
+    sel[:, F:2 * F, :] = np.eye(F)
     taps = O.layer_taps(L, L, 3, 1)
     y3 = O.translate_rows(cache, np.arange(N), taps, sel, None, np.arange(N), per_head=False,
                           recv_heads=H, recv_head_dim=d)
@@ -200,7 +200,7 @@ def test_translate_rows_with_key_norm():
     L_S, N_S, H, d = 4, 10, 2, 8
     cache = rng.standard_normal((L_S, N_S, H, d))
     taps = O.layer_taps(L_S, 3, 3, 1)
-    wt = rng.standard_normal((3, H * d, 3 * H * d))
+    wt = rng.standard_normal((3, 3 * H * d, H * d))
     b = rng.standard_normal((3, H * d))
     tmap = np.array([0, 1, 1, 4, 7, 9])
     rows = np.arange(tmap.size)
@@ -235,26 +235,29 @@ def test_features_layout_and_derotation():
 def test_fold_fp32_order_and_bounds():
     rng = np.random.default_rng(6)
     fo, fi, R = 64, 96, 16
-    wt = (rng.standard_normal((fo, fi)) / np.sqrt(fi)).astype(np.float32)
+    wt = (rng.standard_normal((fi, fo)) / np.sqrt(fi)).astype(np.float32)
     u = (rng.standard_normal((fi, R)) / np.sqrt(fi)).astype(np.float32)
-    v = (rng.standard_normal((fo, R)) * 0.1 / 4).astype(np.float32)
+    v = (rng.standard_normal((R, fo)) * 0.1 / 4).astype(np.float32)
     tot, bits = O.fold_lowrank(wt, u, v)
     exact = O.fold_lowrank_f64(wt, u, v)
     # fp32 running sum of R products then one add: error <= (R+1) u_32 sum|terms|
-    bound = (R + 1) * 2.0 ** -24 * (np.abs(wt) + np.abs(v.astype(np.float64)) @ np.abs(u.astype(np.float64)).T)
+    bound = (R + 1) * 2.0 ** -24 * (np.abs(wt) + np.abs(u.astype(np.float64)) @ np.abs(v.astype(np.float64)))
     assert np.all(np.abs(tot.astype(np.float64) - exact) <= bound)
     # bf16 of the fp32 fold is within one bf16 ulp of the exact fold
     got = O.bf16_bits_to_f64(bits)
     ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - 7)
     assert np.all(np.abs(got - exact) <= ulp)
     # rank 0 keeps W; small integers fold exactly
-    t0, b0 = O.fold_lowrank(wt, u[:, :0], v[:, :0])
+    t0, b0 = O.fold_lowrank(wt, u[:, :0], v[:0, :])
     assert np.array_equal(t0, wt) and np.array_equal(b0, O.f32_to_bf16_bits(wt))
-    wi = rng.integers(-8, 8, (fo, fi)).astype(np.float32)
+    wi = rng.integers(-8, 8, (fi, fo)).astype(np.float32)
     ui = rng.integers(-3, 4, (fi, R)).astype(np.float32)
-    vi = rng.integers(-3, 4, (fo, R)).astype(np.float32)
+    vi = rng.integers(-3, 4, (R, fo)).astype(np.float32)
     ti, _ = O.fold_lowrank(wi, ui, vi)
-    assert np.array_equal(ti.astype(np.float64), wi + vi.astype(np.float64) @ ui.T.astype(np.float64))
+    assert np.array_equal(ti.astype(np.float64), wi + ui.astype(np.float64) @ vi.astype(np.float64))
+    # one entry by hand: w = 0.5, a = (1, 2), b = (3, -1) -> 0.5 + 3 - 2 = 1.5
+    th, _ = O.fold_lowrank(np.array([[0.5]]), np.array([[1.0, 2.0]]), np.array([[3.0], [-1.0]]))
+    assert th[0, 0] == np.float32(1.5)
 
 
 # ---------------------------------------------------------------- ridge

@@ -36,9 +36,9 @@ def test_cache_shapes_and_outlier_pairs():
 
 def test_configs_small():
     c = synth.config(3, small=True)
-    assert c["k_send"].shape[0] == 36 and c["wt_k"].shape == (32, 1024, 3072)
+    assert c["k_send"].shape[0] == 36 and c["w_k"].shape == (32, 3072, 1024)
     c2 = synth.config(2, small=True)
-    assert c2["wt_v"].shape == (80, 8, 128, 128)
+    assert c2["w_v"].shape == (80, 8, 128, 128)
     c1 = synth.config(1)
     assert c1["x_cal_k"].shape == (1, 512, 2, 64) and c1["x_k"].dtype == torch.float32
 
