@@ -60,13 +60,14 @@ static MapFormat map_format(const kvx_cache_desc* send, const kvx_cache_desc* re
     f.C = recv->kv_heads * recv->head_dim;
   }
   const size_t elems = static_cast<size_t>(f.batch) * f.R * f.C;
-  if (send->dtype == KVX_F32 || per_head) {
-    // fp32 caches and the per-head kernel read the map in its own type
+  if (send->dtype == KVX_F32) {
+    // fp32 caches: the map in its own type
     f.mode = wf32 ? TM_F32 : TM_BF16;
     f.bytes = elems * (wf32 ? 4 : 2);
   } else {
-    // flattened bf16 caches: 16-bit operands of the role's type (fp16 for
-    // keys rotated back from a rotated sender), fp32 maps split in two
+    // bf16 caches (flattened and per head): 16-bit operands of the role's
+    // type (fp16 for keys rotated back from a rotated sender), fp32 maps
+    // split in two
     const bool f16 = key_role && send->rope_base > 0.0;
     if (wf32) {
       f.mode = f16 ? TM_SPLIT_F16 : TM_SPLIT_BF16;
@@ -743,6 +744,24 @@ int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_
                   float* w_out, float* b_out, void* workspace, size_t ws_bytes, void* stream) {
   return kvx_fit_ridge_batched(1, &x, ldx, &y, ldy, in_dtype, n_rows, f_in, f_out, lambda_abs, lambda_rel,
                                fit_intercept, &w_out, &b_out, nullptr, workspace, ws_bytes, stream);
+}
+
+int kvx_probe_hbm(int32_t mode, void* a, void* b, int64_t bytes, int32_t iters, float* ms_per_launch, void* stream) {
+  if (mode < 0 || mode > 2 || bytes < 16 || (bytes % 16) != 0 || iters < 1 || !a || !ms_per_launch)
+    return KVX_ERR_INVALID;
+  if (mode != 2 && !b) return KVX_ERR_INVALID;
+  return run_probe_hbm(mode, a, b, bytes, iters, ms_per_launch, static_cast<hipStream_t>(stream));
+}
+
+int kvx_probe_mfma(float* out, int32_t reps, int32_t iters, float* ms_per_launch, double* flops_per_launch,
+                   void* stream) {
+  if (!out || reps < 1 || iters < 1 || !ms_per_launch || !flops_per_launch) return KVX_ERR_INVALID;
+  return run_probe_mfma(out, reps, iters, ms_per_launch, flops_per_launch, static_cast<hipStream_t>(stream));
+}
+
+int32_t kvx_probe_scratch_words(void) {
+  const int a = probe_mfma_out_floats(), b = probe_read_sink_words();
+  return a > b ? a : b;
 }
 
 int kvx_fold_lowrank(const float* w, const float* a, const float* b, int32_t count, int32_t f_in, int32_t f_out,

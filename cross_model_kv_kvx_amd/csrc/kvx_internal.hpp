@@ -116,7 +116,7 @@ struct HeadRole {
   const int32_t* row_of;   // [N_R] row of x for each receiver token (the token map, or the run index)
   int32_t x_f16;           // x holds fp16 rows rotated back at the sender position
   int32_t rotate;          // rotate outputs at the receiver position
-  const void* wt;          // [L_R][H][128][128]
+  const void* wt;          // prepared maps [L_R][H][128 outputs][128 (16-bit) or 2 x 128 (fp32: hi | lo)]
   const float* bias;       // [L_R][H*128] or null
   uint16_t* out;           // [L_R][N_R][H][128]
 };
@@ -162,5 +162,13 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
 
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();
+
+// ---------------------------------------------------------------- measurement probes
+// mode 0: copy a -> b; 1: read a (b: sink of probe_read_sink_words() words);
+// 2: fill a.  Mean ms per launch over `iters` launches.
+int run_probe_hbm(int32_t mode, void* a, void* b, int64_t bytes, int32_t iters, float* ms, hipStream_t s);
+int run_probe_mfma(float* out, int32_t reps, int32_t iters, float* ms, double* flops, hipStream_t s);
+int probe_mfma_out_floats();
+int probe_read_sink_words();
 
 }  // namespace kvx

@@ -15,26 +15,31 @@ namespace kvx {
 // ---------------------------------------------------------------- bf16 caches, d = 128
 // One workgroup per (role, receiver layer l, head h, span of up to 4096
 // receiver tokens) with two kinds of waves:
-//   * compute waves 0..3.  Wave w owns the 32 outputs 16w .. 16w+15 and
-//     64+16w .. 64+16w+15 of the head, so the two members (c, c+64) of every
-//     rotary pair sit in one lane (accumulator elements r and r+8).  The
-//     wave's 32 rows of W_{l,h} stay in registers for the whole span as MFMA
-//     A fragments (fp32 maps split once into a high and a low 16-bit half:
-//     y = x W_hi + x W_lo keeps fp32-level accuracy of the map while the
-//     16-bit inputs stay exact).  Sender rows of 64-token tiles stream
-//     through a ring of six 16 KB LDS stages by direct global->LDS 16-byte
-//     loads (whole 256-byte rows, 16-byte chunks XOR-swizzled by row so
-//     fragment reads of 16 consecutive rows hit distinct banks); the span's
-//     row indices are copied to LDS once.  Keys of a rotated receiver are
-//     rotated at the receiver position before rounding, with a recurrence
-//     that steps each lane's (cos, sin) by 64 positions per tile from table
-//     values read once.  Each tile's 64 x 128 bf16 outputs are staged in one
-//     of two 16 KB LDS buffers;
-//   * store waves 4..7 write the staged tile one step later, 16 bytes per
+//   * compute waves 0..7, two per SIMD.  Wave w owns the 32 outputs
+//     16s .. 16s+15 and 64+16s .. 64+16s+15 of the head (s = w mod 4), so the
+//     two members (c, c+64) of every rotary pair sit in one lane
+//     (accumulator elements r and r+8), and tokens 32 (w / 4) .. +31 of each
+//     64-token tile: the two waves of a SIMD hold the same map rows and
+//     split the tile, so one's fragment reads, epilogue and barrier wait run
+//     under the other's products.  The wave's 32 rows of W_{l,h} stay in
+//     registers for the whole span as MFMA A fragments (fp32 maps prepared
+//     as a high and a low 16-bit half: y = x W_hi + x W_lo keeps fp32-level
+//     accuracy of the map while the 16-bit inputs stay exact).
+//     Sender rows of 64-token tiles stream through a ring of six 16 KB LDS
+//     stages by direct global->LDS 16-byte loads that waves 0..3 issue
+//     (whole 256-byte rows, 16-byte chunks XOR-swizzled by row so fragment
+//     reads of 16 consecutive rows hit distinct banks); waves 4..7 issue no
+//     loads and never wait on the memory counter.  The span's row indices
+//     are copied to LDS once.  Keys of a rotated receiver are rotated at the
+//     receiver position before rounding, with a recurrence that steps each
+//     lane's (cos, sin) by 64 positions per tile from table values read
+//     once.  Each tile's 64 x 128 bf16 outputs are staged in one of two
+//     16 KB LDS buffers;
+//   * store waves 8..11 write the staged tile one step later, 16 bytes per
 //     lane and four whole 256-byte rows per instruction.
 // Sender rows are bf16 cache rows (token map as row index), or, for keys
 // stored rotated, fp16 rows rotated back at the sender position (run index
-// as row index; the map is then split into fp16 halves).  The vector-memory
+// as row index; the map is then prepared in fp16).  The vector-memory
 // counter is per wave: compute waves only load and store waves never wait,
 // so no load ever waits for stores to complete.  One barrier per tile orders
 // the stages and staging buffers between the two kinds.  Workgroups are
@@ -46,7 +51,17 @@ constexpr int PH_TILE = 64;                      // tokens per tile
 constexpr int PH_SPAN = 4096;                    // tokens per workgroup
 constexpr int PH_TILE_ELEMS = PH_TILE * 128;     // 16-bit elements of a tile (16 KB)
 constexpr int PH_RING = 6;                       // LDS stages of sender tiles
-constexpr int PH_THREADS = 512;                  // 4 compute + 4 store waves
+constexpr int PH_LOADERS = 4;                    // compute waves 0..3 issue the tile loads
+// NTB = 64-token tile halves (32-token blocks) per compute wave: 1 with eight
+// compute waves (two per SIMD), 2 with four (one per SIMD, each taking the
+// whole tile: rotating roles with fp32 maps, whose rotation state and map
+// halves do not fit in the registers of three waves per SIMD); plus 4 store
+// waves.
+template <int NTB>
+struct PhShape {
+  static constexpr int compute = 8 / NTB;
+  static constexpr int threads = 64 * (compute + 4);
+};
 
 struct HeadKArgs {
   const uint16_t* x[2];
@@ -120,38 +135,41 @@ __device__ __forceinline__ f32x16 ph_mfma(const u32x4& w, const u32x4& x, const 
                                                    0, 0);
 }
 
-// Rotation state of a lane: (cos, sin) at its two tokens of the current tile
+// Rotation state of a lane: (cos, sin) at its token(s) of the current tile
 // for its 8 pairs, and the step (cos, sin)(64 t) per tile.
+template <int NTB>
 struct PhRot {
-  float cs[2][8], sn[2][8], c64[8], s64[8];
+  float cs[NTB][8], sn[NTB][8], c64[8], s64[8];
 };
 
-// Fragments of one tile, MFMA D[n][tok] += W[n][k] X[tok][k]; add the bias,
-// rotate pairs when `rot`, stage (bf16 nearest even) into `ys` as [tok][n]
-// with swizzled chunks.
-// With per-token positions (`rpos`), the (cos, sin) of the lane's tokens
-// (tile tokens from `tok0`) are read from the table instead of stepped.
-template <bool WF32, bool F16>
+// Fragments of this wave's token blocks of one tile (block ti = wave / 4
+// with eight compute waves, both blocks with four), MFMA D[n][tok] +=
+// W[n][k] X[tok][k]; add the bias, rotate pairs when ROT, stage (bf16 nearest
+// even) into `ys` as [tok][n] with swizzled chunks.  With per-token positions
+// (`rpos`), the (cos, sin) of the lane's tokens (tile tokens from `tok0`) are
+// read from the table instead of stepped.
+template <bool WF32, bool F16, bool ROT, int NTB>
 __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, const u32x4 (&wh)[8],
-                                           const u32x4 (&wl)[8], const float (&bn)[16], bool rot, PhRot& rs,
+                                           const u32x4 (&wl)[8], const float (&bn)[16], PhRot<NTB>& rs,
                                            const int32_t* rpos, const float2* tab, int32_t tok0, int32_t n_tok_all,
                                            int32_t pos_limit) {
   const int lane = threadIdx.x & 63, wave = wave_id();
+  const int sw = wave & 3;
+  const int tb0 = NTB == 2 ? 0 : (wave >> 2);  // first token block of this wave
   const char* xb = reinterpret_cast<const char*>(xs);
-  f32x16 acc[2];
+  f32x16 acc[NTB];
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
+  for (int j = 0; j < NTB; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[ti][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
   // the fragments of step ks + 1 are read before the products of step ks
-  // are issued, so their LDS latency runs under those products (one compute
-  // wave per SIMD: nothing else would fill the gap)
-  u32x4 xf[2][2];
+  // are issued, so their LDS latency runs under those products
+  u32x4 xf[2][NTB];
   auto read = [&](int ks, int buf) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int row = 32 * ti + (lane & 31);
-      xf[buf][ti] = *reinterpret_cast<const u32x4*>(xb + row * 256 + 16 * ph_chunk(row, 2 * ks + (lane >> 5)));
+    for (int j = 0; j < NTB; ++j) {
+      const int row = 32 * (tb0 + j) + (lane & 31);
+      xf[buf][j] = *reinterpret_cast<const u32x4*>(xb + row * 256 + 16 * ph_chunk(row, 2 * ks + (lane >> 5)));
     }
   };
   read(0, 0);
@@ -163,44 +181,47 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
     }
     const int b = ks & 1;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) acc[ti] = ph_mfma<F16>(wh[ks], xf[b][ti], acc[ti]);
+    for (int j = 0; j < NTB; ++j) acc[j] = ph_mfma<F16>(wh[ks], xf[b][j], acc[j]);
     if constexpr (WF32) {
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti) acc[ti] = ph_mfma<F16>(wl[ks], xf[b][ti], acc[ti]);
+      for (int j = 0; j < NTB; ++j) acc[j] = ph_mfma<F16>(wl[ks], xf[b][j], acc[j]);
     }
   }
   // lane: token 32 ti + lane % 32, local rows j = 8 g + 4 (lane / 32) + e
   char* yb = reinterpret_cast<char*>(ys);
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
+  for (int j = 0; j < NTB; ++j) {
+    const int ti = tb0 + j;
     float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = acc[ti][r] + bn[r];
-    if (rot && rpos) {
-      int32_t pp = rpos[min(tok0 + 32 * ti + (lane & 31), n_tok_all - 1)];
-      pp = pp < 0 ? 0 : (pp >= pos_limit ? pos_limit - 1 : pp);
+    for (int r = 0; r < 16; ++r) v[r] = acc[j][r] + bn[r];
+    if constexpr (ROT) {
+      if (rpos) {
+        int32_t pp = rpos[min(tok0 + 32 * ti + (lane & 31), n_tok_all - 1)];
+        pp = pp < 0 ? 0 : (pp >= pos_limit ? pos_limit - 1 : pp);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float2 t = tab[static_cast<int64_t>(pp) * 64 + ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))];
-        const float a = v[r], b = v[r + 8];
-        v[r] = a * t.x - b * t.y;
-        v[r + 8] = a * t.y + b * t.x;
-      }
-    } else if (rot) {
+        for (int r = 0; r < 8; ++r) {
+          const float2 t = tab[static_cast<int64_t>(pp) * 64 + ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))];
+          const float a = v[r], b = v[r + 8];
+          v[r] = a * t.x - b * t.y;
+          v[r + 8] = a * t.y + b * t.x;
+        }
+      } else {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float a = v[r], b = v[r + 8];
-        v[r] = a * rs.cs[ti][r] - b * rs.sn[ti][r];
-        v[r + 8] = a * rs.sn[ti][r] + b * rs.cs[ti][r];
-        const float cn = rs.cs[ti][r] * rs.c64[r] - rs.sn[ti][r] * rs.s64[r];
-        rs.sn[ti][r] = rs.sn[ti][r] * rs.c64[r] + rs.cs[ti][r] * rs.s64[r];
-        rs.cs[ti][r] = cn;
+        for (int r = 0; r < 8; ++r) {
+          const float a = v[r], b = v[r + 8];
+          v[r] = a * rs.cs[j][r] - b * rs.sn[j][r];
+          v[r + 8] = a * rs.sn[j][r] + b * rs.cs[j][r];
+          const float cn = rs.cs[j][r] * rs.c64[r] - rs.sn[j][r] * rs.s64[r];
+          rs.sn[j][r] = rs.sn[j][r] * rs.c64[r] + rs.cs[j][r] * rs.s64[r];
+          rs.cs[j][r] = cn;
+        }
       }
     }
     const int tok = 32 * ti + (lane & 31);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int c = ph_out(wave, 8 * g) >> 3;  // 16-byte chunk of outputs ph_out(w, 8g) .. +7
+      const int c = ph_out(sw, 8 * g) >> 3;  // 16-byte chunk of outputs ph_out(s, 8g) .. +7
       const u32x2 o = u32x2{cvt_bf16x2(v[4 * g], v[4 * g + 1]), cvt_bf16x2(v[4 * g + 2], v[4 * g + 3])};
       *reinterpret_cast<u32x2*>(yb + tok * 256 + 16 * ph_chunk(tok, c) + 8 * (lane >> 5)) = o;
     }
@@ -212,9 +233,10 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
 // skipped).
 // outb: row 0 of the layer and head in the output pool; tok0: the tile's
 // first receiver token; slot: output row of each token (null: the token).
+template <int NC>
 __device__ __forceinline__ void ph_store(const uint16_t* ys, uint16_t* outb, int32_t tok0, int32_t rows,
                                          int64_t row_elems, const int64_t* slot, int64_t pool_rows) {
-  const int t = threadIdx.x - 256;
+  const int t = threadIdx.x - 64 * NC;
   const char* yb = reinterpret_cast<const char*>(ys);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -235,11 +257,15 @@ __device__ __forceinline__ void ph_barrier() {
   KVX_COMPILER_FENCE();
 }
 
-// WF32: fp32 maps (split in two halves); F16: fp16 sender rows (rotated back)
-// and fp16 map halves, else bf16.
-template <bool WF32, bool F16>
-__global__ __attribute__((amdgpu_flat_work_group_size(PH_THREADS, PH_THREADS), amdgpu_waves_per_eu(2, 2))) void
+// WF32: fp32 maps (prepared as two 16-bit halves); F16: fp16 sender rows
+// (rotated back) and fp16 maps, else bf16; ROT: outputs rotated at the
+// receiver position; NTB: token blocks per compute wave (see PhShape).
+template <bool WF32, bool F16, bool ROT, int NTB>
+__global__ __attribute__((amdgpu_flat_work_group_size(PhShape<NTB>::threads, PhShape<NTB>::threads),
+                          amdgpu_waves_per_eu(3 - NTB / 2, 3 - NTB / 2))) void
 perhead_kernel(const HeadKArgs a) {
+  constexpr int NC = PhShape<NTB>::compute;
+  constexpr int NT = PhShape<NTB>::threads;
   __shared__ __attribute__((aligned(1024))) uint16_t x0[PH_TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t x1[PH_TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t x2[PH_TILE_ELEMS];
@@ -276,7 +302,7 @@ perhead_kernel(const HeadKArgs a) {
   // the span's sender rows, clamped to valid rows (entries past the span
   // repeat its last token)
   const int32_t* row_of = a.row_of[role];
-  for (int i = threadIdx.x; i < PH_SPAN; i += PH_THREADS) {
+  for (int i = threadIdx.x; i < PH_SPAN; i += NT) {
     int32_t v = row_of[pt.t0 + min(i, pt.n_tok - 1)];
     msm[i] = v < 0 ? 0 : (v >= x_rows ? x_rows - 1 : v);
   }
@@ -284,32 +310,34 @@ perhead_kernel(const HeadKArgs a) {
 
   // Every wave passes the barriers B_0 .. B_n (n = n_tiles) once each: at
   // B_k tile k is in LDS and the staged tile k-1 is complete.
-  if (wave >= 4) {
+  if (wave >= NC) {
     ph_barrier();  // B_0
     for (int32_t k = 1; k <= pt.n_tiles; ++k) {
       ph_barrier();  // B_k: store tile k-1
-      ph_store(((k - 1) & 1) ? y1 : y0, outb, pt.t0 + (k - 1) * PH_TILE, pt.n_tok - (k - 1) * PH_TILE, row_elems,
+      ph_store<NC>(((k - 1) & 1) ? y1 : y0, outb, pt.t0 + (k - 1) * PH_TILE, pt.n_tok - (k - 1) * PH_TILE, row_elems,
                a.slot, a.pool_rows);
     }
     return;
   }
 
   // compute waves.  Rotation state first (its loads precede the tile loads,
-  // so waiting for them never waits for a tile): the lane's tokens of tile 0
+  // so waiting for them never waits for a tile): the lane's token of tile 0
   // and the step by one tile.
-  const bool rot = a.rotate[role] != 0;
-  const int32_t* rpos = rot ? a.recv_pos : nullptr;
-  PhRot rs;
-  if (rot && !rpos) {
+  const int sw = wave & 3;  // output block of this wave
+  const bool loader = wave < PH_LOADERS;
+  const int32_t* rpos = ROT ? a.recv_pos : nullptr;
+  PhRot<NTB> rs;
+  if (ROT && !rpos) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int pr = ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));  // pair index (< 64)
+      const int pr = ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));  // pair index (< 64)
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
+      for (int j = 0; j < NTB; ++j) {
+        const int ti = (NTB == 2 ? 0 : (wave >> 2)) + j;
         const int32_t tok = min(pt.t0 + 32 * ti + (lane & 31), a.recv_tokens - 1);
         const float2 t = a.tab_recv[static_cast<int64_t>(tok) * 64 + pr];
-        rs.cs[ti][r] = t.x;
-        rs.sn[ti][r] = t.y;
+        rs.cs[j][r] = t.x;
+        rs.sn[j][r] = t.y;
       }
       // the table holds position 64 whenever a span has more than one tile
       const float2 t64 = pt.n_tiles > 1 ? a.tab_recv[64 * 64 + pr] : float2{1.0f, 0.0f};
@@ -322,91 +350,58 @@ perhead_kernel(const HeadKArgs a) {
   const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
-    bn[r] = bias ? bias[ph_out(wave, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
+    bn[r] = bias ? bias[ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
 
-  // A fragments: rows n = ph_out(wave, lane % 32) of W_{l,h} ([n][c], output
-  // major), k = 16 ks + 8 (lane / 32) .. +8; halves rounded to nearest even.
-  // All map loads are issued before the tiles' loads and converted after
-  // them: one wait covers the map (the counter completes in order), and the
-  // tiles are in flight meanwhile.
+  // A fragments: rows n = ph_out(s, lane % 32) of W_{l,h}, prepared
+  // output-major in the operand type: [n][c] (16-bit maps) or [n][hi c | lo c]
+  // (fp32 maps split into halves), k = 16 ks + 8 (lane / 32) .. +8.  The map
+  // loads are issued before the tiles' loads: one wait covers them (the
+  // counter completes in order), and the tiles are in flight meanwhile.
   u32x4 wh[8], wl[8];
-  const int n_row = ph_out(wave, lane & 31);
-  if constexpr (WF32) {
-    const float* wp = static_cast<const float*>(a.wt[role]) +
-                      ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
-    float4 wu[8], wv[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      wu[ks] = *reinterpret_cast<const float4*>(wp + 16 * ks);
-      wv[ks] = *reinterpret_cast<const float4*>(wp + 16 * ks + 4);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    ph_issue(pt, 0, ph_rows(pt, 0), x0);
-    ph_issue(pt, 1, ph_rows(pt, 1), x1);
-    ph_issue(pt, 2, ph_rows(pt, 2), x2);
-    ph_issue(pt, 3, ph_rows(pt, 3), x3);
-    ph_issue(pt, 4, ph_rows(pt, 4), x4);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const float4 u = wu[ks], v = wv[ks];
-      const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (F16) {
-          hi[e] = cvt_f16x2(f[2 * e], f[2 * e + 1]);
-          const float h0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] & 0xffffu)));
-          const float h1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi[e] >> 16)));
-          lo[e] = cvt_f16x2(f[2 * e] - h0, f[2 * e + 1] - h1);
-        } else {
-          hi[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
-          lo[e] = pack_bf16(f[2 * e] - bf16lo(hi[e]), f[2 * e + 1] - bf16hi(hi[e]));
-        }
-      }
-      wh[ks] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      wl[ks] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    }
-  } else {
+  {
+    constexpr int KW = WF32 ? 256 : 128;  // 16-bit elements per map row
+    const int n_row = ph_out(sw, lane & 31);
     const uint16_t* wp = static_cast<const uint16_t*>(a.wt[role]) +
-                         ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * 128 + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) wh[ks] = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
-    __builtin_amdgcn_sched_barrier(0);
-    ph_issue(pt, 0, ph_rows(pt, 0), x0);
-    ph_issue(pt, 1, ph_rows(pt, 1), x1);
-    ph_issue(pt, 2, ph_rows(pt, 2), x2);
-    ph_issue(pt, 3, ph_rows(pt, 3), x3);
-    ph_issue(pt, 4, ph_rows(pt, 4), x4);
-    __builtin_amdgcn_sched_barrier(0);
+                         ((static_cast<int64_t>(l) * a.heads + h) * 128 + n_row) * KW + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if constexpr (F16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wh[ks][e] = cvt_f16x2(bf16lo(wh[ks][e]), bf16hi(wh[ks][e]));
-      }
-      wl[ks] = u32x4{0u, 0u, 0u, 0u};
+      wh[ks] = *reinterpret_cast<const u32x4*>(wp + 16 * ks);
+      wl[ks] = WF32 ? *reinterpret_cast<const u32x4*>(wp + 128 + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  if (loader) {
+    ph_issue(pt, 0, ph_rows(pt, 0), x0);
+    ph_issue(pt, 1, ph_rows(pt, 1), x1);
+    ph_issue(pt, 2, ph_rows(pt, 2), x2);
+    ph_issue(pt, 3, ph_rows(pt, 3), x3);
+    ph_issue(pt, 4, ph_rows(pt, 4), x4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // rows of the tile the first step issues, read a step ahead from then on
-  PhRows rr = ph_rows(pt, PH_RING - 1);
+  // (loading waves only)
+  PhRows rr{};
+  if (loader) rr = ph_rows(pt, PH_RING - 1);
 
-  // Step k (tile k in stage k % 6, staging k % 2): the wait leaves the four
-  // younger tiles in flight and completes this wave's staging writes, then
-  // B_k; tile k+5 is issued into the stage of tile k-1 and tile k is
-  // multiplied into its staging buffer.  Steps past n_tiles (the unrolled
-  // loop runs a multiple of 6) pass no barrier.
+  // Step k (tile k in stage k % 6, staging k % 2): a loading wave's wait
+  // leaves the four younger tiles in flight, every wave's LDS wait completes
+  // its staging writes, then B_k; a loading wave issues tile k+5 into the
+  // stage of tile k-1, and tile k is multiplied into its staging buffer.
+  // Steps past n_tiles (the unrolled loop runs a multiple of 6) pass no
+  // barrier.
 #define PH_STEP(K, XS, YS, XNEXT)                                              \
   {                                                                            \
     if ((K) <= pt.n_tiles) {                                                   \
-      KVX_WAIT_VM(4 * (PH_RING - 2));                                          \
+      if (loader) KVX_WAIT_VM(4 * (PH_RING - 2));                              \
       KVX_WAIT_LGKM0();                                                        \
       ph_barrier();                                                            \
     }                                                                          \
-    ph_issue(pt, (K) + PH_RING - 1, rr, XNEXT);                                \
-    rr = ph_rows(pt, (K) + PH_RING);                                           \
+    if (loader) {                                                              \
+      ph_issue(pt, (K) + PH_RING - 1, rr, XNEXT);                              \
+      rr = ph_rows(pt, (K) + PH_RING);                                         \
+    }                                                                          \
     if ((K) < pt.n_tiles)                                                      \
-      ph_compute<WF32, F16>(XS, YS, wh, wl, bn, rot, rs, rpos, a.tab_recv,      \
+      ph_compute<WF32, F16, ROT, NTB>(XS, YS, wh, wl, bn, rs, rpos, a.tab_recv, \
                             pt.t0 + (K) * PH_TILE, a.recv_tokens, a.pos_limit); \
   }
   for (int32_t k = 0; k < pt.n_tiles; k += 6) {
@@ -427,14 +422,26 @@ perhead_kernel(const HeadKArgs a) {
   KVX_WAIT_VM(0);
 }
 
+template <bool WF32, bool F16, bool ROT>
+static void ph_launch(unsigned g, const HeadKArgs& a, hipStream_t s) {
+  // eight compute waves (two per SIMD, each a 32-token half of every tile),
+  // except for rotating roles with fp32 maps: their rotation state and both
+  // map halves do not fit in the registers of three waves per SIMD, so four
+  // compute waves hold both halves
+  constexpr int NTB = (ROT && WF32) ? 2 : 1;
+  perhead_kernel<WF32, F16, ROT, NTB><<<g, PhShape<NTB>::threads, 0, s>>>(a);
+}
+
 int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hipStream_t s) {
   if (p.recv_tokens <= 0 || n_roles <= 0) return KVX_OK;
   // one launch per operand type (fp16 rotated-back key rows, bf16 otherwise)
-  for (int f16 = 1; f16 >= 0; --f16) {
+  // and rotation of the outputs
+  for (int kind = 3; kind >= 0; --kind) {
+    const int f16 = kind >> 1, rot = kind & 1;
     HeadKArgs a{};
     int n = 0;
     for (int i = 0; i < n_roles; ++i) {
-      if (roles[i].x_f16 != f16) continue;
+      if (roles[i].x_f16 != f16 || (roles[i].rotate != 0) != (rot != 0)) continue;
       // sender rows of one layer are addressed with 32-bit byte offsets
       if (static_cast<int64_t>(roles[i].x_rows) * p.heads * 256 >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
       a.x[n] = roles[i].x;
@@ -465,14 +472,14 @@ int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hip
     const unsigned g = static_cast<unsigned>(nb);
     if (p.w_f32) {
       if (f16)
-        perhead_kernel<true, true><<<g, PH_THREADS, 0, s>>>(a);
+        rot ? ph_launch<true, true, true>(g, a, s) : ph_launch<true, true, false>(g, a, s);
       else
-        perhead_kernel<true, false><<<g, PH_THREADS, 0, s>>>(a);
+        rot ? ph_launch<true, false, true>(g, a, s) : ph_launch<true, false, false>(g, a, s);
     } else {
       if (f16)
-        perhead_kernel<false, true><<<g, PH_THREADS, 0, s>>>(a);
+        rot ? ph_launch<false, true, true>(g, a, s) : ph_launch<false, true, false>(g, a, s);
       else
-        perhead_kernel<false, false><<<g, PH_THREADS, 0, s>>>(a);
+        rot ? ph_launch<false, false, true>(g, a, s) : ph_launch<false, false, false>(g, a, s);
     }
     KVX_LAUNCH_CHECK();
   }

@@ -32,7 +32,8 @@ EXPORTS = (
     "kvx_fit_ridge_batched", "kvx_fit_recolor_workspace_size", "kvx_fit_recolor", "kvx_fold_lowrank",
     "kvx_quantize_fp8", "kvx_translate_fp8", "kvx_align_tokens_async", "kvx_translate_recorded",
     "kvx_align_tokens_noalloc", "kvx_prepared_maps_size", "kvx_prepare_maps",
-    "kvx_translate_prepared_workspace_size", "kvx_translate_prepared",
+    "kvx_translate_prepared_workspace_size", "kvx_translate_prepared", "kvx_probe_hbm", "kvx_probe_mfma",
+    "kvx_probe_scratch_words",
 )
 
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
             "kvx_fold_lowrank": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp]),
             "kvx_quantize_fp8": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
             "kvx_prepared_maps_size": (sz, [dp, dp, i32, i32, i32, i32]),
+            "kvx_probe_hbm": (ctypes.c_int, [i32, vp, vp, i64, i32, ctypes.POINTER(ctypes.c_float), vp]),
+            "kvx_probe_mfma": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(ctypes.c_float),
+                                              ctypes.POINTER(ctypes.c_double), vp]),
+            "kvx_probe_scratch_words": (i32, []),
             "kvx_prepare_maps": (ctypes.c_int, [dp, dp, i32, i32, i32, i32, vp, vp, sz, vp]),
             "kvx_translate_prepared_workspace_size": (sz, [dp, dp, i32, i32, i32]),
             "kvx_translate_prepared": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, i32, i32, vp, vp, vp,
@@ -604,3 +609,27 @@ def fold_lowrank(w: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out_dtype=to
                                 _stream(stream))
     _check(st, "kvx_fold_lowrank")
     return out[0] if squeeze else out
+
+
+def probe_hbm(mode: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, iters: int = 10,
+              stream=None) -> float:
+    """kvx_probe_hbm: "copy" (a -> b), "read" (a; b a sink the binding
+    allocates) or "fill" (a).  Returns the mean ms per launch."""
+    m = {"copy": 0, "read": 1, "fill": 2}[mode]
+    _need(a, "a")
+    nbytes = a.numel() * a.element_size()
+    if m == 1 and b is None:
+        b = torch.empty(int(lib().kvx_probe_scratch_words()), dtype=torch.int32, device=a.device)
+    ms = ctypes.c_float(0.0)
+    _check(lib().kvx_probe_hbm(m, _ptr(a), _ptr(b), nbytes, int(iters), ctypes.byref(ms), _stream(stream)),
+           "kvx_probe_hbm")
+    return float(ms.value)
+
+
+def probe_mfma(reps: int = 100000, iters: int = 8, device="cuda", stream=None):
+    """kvx_probe_mfma: returns (ms per launch, flops per launch)."""
+    out = torch.empty(int(lib().kvx_probe_scratch_words()), dtype=torch.float32, device=device)
+    ms, fl = ctypes.c_float(0.0), ctypes.c_double(0.0)
+    _check(lib().kvx_probe_mfma(_ptr(out), int(reps), int(iters), ctypes.byref(ms), ctypes.byref(fl),
+                                _stream(stream)), "kvx_probe_mfma")
+    return float(ms.value), float(fl.value)

@@ -544,6 +544,32 @@ int kvx_fold_lowrank(const float* w, const float* a, const float* b, int32_t cou
                      int32_t f_in, int32_t f_out, int32_t rank, void* w_out,
                      int32_t out_dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement probes (not part of the translation): the rates this chip
+ * sustains, the denominators of "fraction of achievable peak" beside the
+ * published peaks.
+ *
+ * kvx_probe_hbm: mode 0 copies `bytes` from device buffer a to device buffer
+ *   b (each byte read once and written once), mode 1 reads a (b: device
+ *   uint32 sink of kvx_probe_scratch_words() words), mode 2 fills a.  bytes:
+ *   a positive multiple of 16, far above the 256 MB last-level cache for an
+ *   HBM figure.  16-byte vector accesses, streaming stores.  One untimed
+ *   launch, then `iters` launches between two events on `stream`;
+ *   *ms_per_launch = their mean.  Synchronises `stream`.
+ * kvx_probe_mfma: every wave of 8 per compute unit issues `reps` x 4
+ *   independent v_mfma_f32_32x32x16_bf16 (bf16 dense products, fp32
+ *   accumulation); out: device float scratch of kvx_probe_scratch_words()
+ *   entries (receives the accumulator sums).  Timed like kvx_probe_hbm;
+ *   *flops_per_launch = the products' flops (2 m n k each).
+ * kvx_probe_scratch_words: scratch words either probe needs on the current
+ *   device.
+ * ---------------------------------------------------------------------- */
+int kvx_probe_hbm(int32_t mode, void* a, void* b, int64_t bytes, int32_t iters, float* ms_per_launch,
+                  void* stream);
+int kvx_probe_mfma(float* out, int32_t reps, int32_t iters, float* ms_per_launch,
+                   double* flops_per_launch, void* stream);
+int32_t kvx_probe_scratch_words(void);
+
 #ifdef __cplusplus
 }
 #endif
