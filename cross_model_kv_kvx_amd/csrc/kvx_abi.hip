@@ -30,6 +30,7 @@ int device_cu_count() {
 static bool desc_ok(const kvx_cache_desc* d) {
   if (!d) return false;
   if (d->layers < 1 || d->layers > MAX_LAYERS || d->tokens < 0 || d->kv_heads < 1 || d->head_dim < 1) return false;
+  if (static_cast<int64_t>(d->kv_heads) * d->head_dim > KVX_MAX_ROW) return false;
   if (d->dtype != KVX_F32 && d->dtype != KVX_BF16) return false;
   if (!(d->rope_base >= 0.0)) return false;
   if (d->rope_base > 0.0 && (d->head_dim % 2) != 0) return false;
@@ -202,7 +203,9 @@ int kvx_align_tokens_noalloc(const int32_t* send_end, int32_t n_send, const int3
 }
 
 size_t kvx_align_batched_workspace_size(const int32_t* recv_off, int32_t n_seq) {
-  if (!recv_off || n_seq < 1) return 0;
+  if (!recv_off || n_seq < 1 || recv_off[0] != 0) return 0;
+  for (int32_t q = 0; q < n_seq; ++q)
+    if (recv_off[q + 1] < recv_off[q]) return 0;
   return align_batched_ws_bytes(recv_off, n_seq) + 256;
 }
 
@@ -679,8 +682,12 @@ int kvx_gather_features(const kvx_cache_desc* send, const void* kv_send, int32_t
 
 size_t kvx_fit_ridge_workspace_size(int32_t f_in, int32_t f_out) { return kvx_fit_ridge_batched_workspace_size(1, f_in, f_out); }
 
+static bool fit_size_ok(int32_t count, int32_t f_in, int32_t f_out) {
+  return count <= KVX_MAX_PROBLEMS && f_in <= KVX_MAX_FIT_FEATURES && f_out <= KVX_MAX_FIT_FEATURES;
+}
+
 size_t kvx_fit_ridge_batched_workspace_size(int32_t count, int32_t f_in, int32_t f_out) {
-  if (count < 1 || f_in < 1 || f_out < 1) return 0;
+  if (count < 1 || f_in < 1 || f_out < 1 || !fit_size_ok(count, f_in, f_out)) return 0;
   return fit_ws_bytes(count, f_in, f_out);
 }
 
@@ -690,6 +697,7 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
                           int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
   if (count < 0 || f_in < 1 || f_out < 1 || n_rows < 0) return KVX_ERR_INVALID;
   if (count == 0) return KVX_OK;
+  if (!fit_size_ok(count, f_in, f_out)) return KVX_ERR_UNSUPPORTED;
   if (in_dtype != KVX_F32 && in_dtype != KVX_BF16) return KVX_ERR_INVALID;
   if (!(lambda_abs >= 0.0) || !(lambda_rel >= 0.0)) return KVX_ERR_INVALID;
   if (!x || !y || !w_out || (fit_intercept && !b_out)) return KVX_ERR_INVALID;
@@ -710,7 +718,7 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
 }
 
 size_t kvx_fit_recolor_workspace_size(int32_t count, int32_t f_in, int32_t f_out) {
-  if (count < 1 || f_in < 1 || f_out < 1) return 0;
+  if (count < 1 || f_in < 1 || f_out < 1 || !fit_size_ok(count, f_in, f_out)) return 0;
   return recolor_ws_bytes(count, f_in, f_out);
 }
 
@@ -720,6 +728,7 @@ int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void
                     size_t ws_bytes, void* stream) {
   if (count < 0 || f_in < 1 || f_out < 1 || n_rows < 0) return KVX_ERR_INVALID;
   if (count == 0) return KVX_OK;
+  if (!fit_size_ok(count, f_in, f_out)) return KVX_ERR_UNSUPPORTED;
   if (in_dtype != KVX_F32 && in_dtype != KVX_BF16) return KVX_ERR_INVALID;
   if (!(rho_x >= 0.0) || !(rho_y >= 0.0)) return KVX_ERR_INVALID;
   if (!x || !y || !w_out || !b_out) return KVX_ERR_INVALID;

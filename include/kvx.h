@@ -58,11 +58,19 @@ typedef enum {
 
 typedef enum { KVX_F32 = 0, KVX_BF16 = 1 } kvx_dtype;
 
+/* Size limits checked by every entry point (larger values are refused with
+ * KVX_ERR_INVALID or, for the fits, KVX_ERR_UNSUPPORTED; size queries return
+ * 0): features of one cache row (kv_heads * head_dim), problems of one fit
+ * call, and features on either side of a fitted map. */
+#define KVX_MAX_ROW 65536
+#define KVX_MAX_PROBLEMS 65535
+#define KVX_MAX_FIT_FEATURES 65536
+
 /* Shape of one role (K or V) of one model's cache. */
 typedef struct {
   int32_t layers;     /* >= 1, <= 255 */
   int32_t tokens;     /* >= 0 */
-  int32_t kv_heads;   /* >= 1 */
+  int32_t kv_heads;   /* >= 1; kv_heads * head_dim <= KVX_MAX_ROW */
   int32_t head_dim;   /* >= 1; even when rope_base > 0 */
   int32_t dtype;      /* kvx_dtype of the cache elements */
   double rope_base;   /* > 0: keys are stored rotated (RoPE, half-split pairs
@@ -307,6 +315,7 @@ int kvx_translate_placed(const kvx_cache_desc* send, const void* k_send, const v
  *   kvx_translate and kvx_prepare_maps take); b_out: device fp32 [f_out]
  *   (written only with fit_intercept; may be NULL otherwise).
  * workspace: device scratch of kvx_fit_ridge_workspace_size(f_in, f_out).
+ * f_in, f_out <= KVX_MAX_FIT_FEATURES (KVX_ERR_UNSUPPORTED beyond).
  * G and X^T Y are accumulated in fp32 on matrix cores; the solve (Cholesky
  * factorisation and two triangular solves) runs in fp64.
  * Synchronises `stream` once to read the factorisation flag:
@@ -329,7 +338,7 @@ int kvx_fit_ridge(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_
  * x, y, w_out, b_out: HOST arrays of `count` device pointers, each as in
  *   kvx_fit_ridge (b_out may be NULL without fit_intercept).
  * status: host int32 [count] or NULL; receives KVX_OK or KVX_ERR_NOT_SPD
- *   per problem.
+ *   per problem.  count <= KVX_MAX_PROBLEMS (KVX_ERR_UNSUPPORTED beyond).
  * workspace: device scratch of kvx_fit_ridge_batched_workspace_size(count,
  *   f_in, f_out) bytes (the Gram partials, shared, plus about
  *   8 (f_in + 1)(f_in + f_out) bytes per problem).
@@ -495,7 +504,8 @@ int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void
  *   ldx) and [n_rows][f_out] (row stride ldy) matrices of in_dtype; bf16
  *   rows need f_in, f_out, ldx, ldy multiples of 8 and 16-byte aligned bases.
  * f_in >= f_out (Q with orthonormal columns); f_in < f_out returns
- *   KVX_ERR_UNSUPPORTED.
+ *   KVX_ERR_UNSUPPORTED, as do count > KVX_MAX_PROBLEMS and f_in >
+ *   KVX_MAX_FIT_FEATURES.
  * rho_x, rho_y >= 0: relative regularisers (rows that repeat a layer tap make
  *   S_xx singular; rho_x > 0 is then required).
  * w_out: HOST array of device fp32 [f_in][f_out] (row-major, y = x W + b,
