@@ -23,6 +23,7 @@
 // at once, so the chain's latency is paid once per call.  A non-positive
 // pivot sets the problem's device flag; the host reads the flags once.
 
+#include <algorithm>
 #include <vector>
 
 #include "kvx_fit.hpp"
@@ -84,16 +85,18 @@ struct GrItem {
   uint32_t p_pitch, q_pitch;      // row pitch (bytes)
   uint32_t p_off[GR_LD], q_off[GR_LD];  // this lane's row * pitch + chunk * 16 inside a step
   int32_t nk;                     // steps of the split
+  int32_t p_wrap;                 // P step k reads P rows of step k - p_wrap from step p_wrap on (k < 2 p_wrap)
 };
+constexpr int32_t GR_NO_WRAP = 1 << 30;
 
 // Part of step k (64 rows) into `part`: load i of wave w covers part rows
 // 2 (4w + i) and +1, lane j -> row + j/32, physical chunk j mod 32.  Steps
 // past the end read nothing.
 __device__ __forceinline__ void gr_issue(__amdgpu_buffer_rsrc_t r, uint32_t pitch, const uint32_t (&off)[GR_LD], int k,
-                                         int nk, uint16_t* part) {
+                                         int nk, uint16_t* part, int32_t wrap = GR_NO_WRAP) {
   const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t rr = k < nk ? r : buf_rsrc(nullptr, 0);
-  const uint32_t base = static_cast<uint32_t>(k) * GR_BK * pitch;
+  const uint32_t base = static_cast<uint32_t>(k >= wrap ? k - wrap : k) * GR_BK * pitch;
 #pragma unroll
   for (int i = 0; i < GR_LD; ++i) dma16(rr, base + off[i], 0, part + (wave * GR_LD + i) * 512);
 }
@@ -108,7 +111,8 @@ __device__ __forceinline__ void gr_load(const GrItem& it, int i, int kq, int kp,
     dma16(rr, static_cast<uint32_t>(kq) * GR_BK * it.q_pitch + it.q_off[i], 0, nq + (wave * GR_LD + i) * 512);
   } else {
     const __amdgpu_buffer_rsrc_t rr = kp < it.nk ? it.pr : buf_rsrc(nullptr, 0);
-    dma16(rr, static_cast<uint32_t>(kp) * GR_BK * it.p_pitch + it.p_off[i - GR_LD], 0,
+    const int kw = kp >= it.p_wrap ? kp - it.p_wrap : kp;
+    dma16(rr, static_cast<uint32_t>(kw) * GR_BK * it.p_pitch + it.p_off[i - GR_LD], 0,
           np + (wave * GR_LD + i - GR_LD) * 512);
   }
 }
@@ -160,7 +164,7 @@ __device__ __forceinline__ void gr_sync() {
 #define GR_STEP(K, PA, PB, NB, NA, LIVE)                   \
   gr_sync();                                               \
   gr_issue(it.qr, it.q_pitch, it.q_off, (K) + 1, it.nk, NB); \
-  gr_issue(it.pr, it.p_pitch, it.p_off, (K) + 2, it.nk, NA); \
+  gr_issue(it.pr, it.p_pitch, it.p_off, (K) + 2, it.nk, NA, it.p_wrap); \
   if (LIVE) gr_compute(PA, PB, acc);
 // A whole step (no tail): loads spread over the sub-steps.
 #define GR_STEP_FULL(K, PA, PB, NB, NA)                    \
@@ -226,6 +230,7 @@ gram_kernel(const GramArgs g) {
       it.qr = buf_rsrc(nullptr, 0);
     }
     it.nk = static_cast<int32_t>((rows + GR_BK - 1) / GR_BK);
+    it.p_wrap = GR_NO_WRAP;
 #pragma unroll
     for (int i = 0; i < GR_LD; ++i) {
       const int row = 2 * (wave * GR_LD + i) + (lane >> 5);
@@ -282,6 +287,269 @@ gram_kernel(const GramArgs g) {
     __syncthreads();
   }
 }
+
+// ---------------------------------------------------------------- Gram from runs of the alignment
+//
+// The features of a calibration row are the sender rows of its aligned
+// sender token, so within a run u of receiver tokens that share one sender
+// token (length c_u) every feature row is the same row x_u.  Then
+//   X^T X = sum_u c_u x_u x_u^T = sum_j 2^j sum_{u : bit j of c_u} x_u x_u^T
+// (runs of 2^15 or more tokens add their c_u >> 15 to group 15), and with the
+// groups taken from the largest j down, each group's sum accumulated on top
+// of the accumulator doubled 2^(j_prev - j) times (exact) leaves
+// sum_j 2^j G_j after the last group and a final scaling by 2^(j_last).  The
+// products are the exact bf16 products of the plain Gram, summed in fp32.
+// X^T Y = sum_u x_u s_u^T with s_u the run's target sum, taken as a high and
+// a low bf16 part: the distinct rows x_u are read twice, once against the
+// high parts and once against the low parts.
+// A launch covers every problem (receiver layer) of one role: items are
+// (problem, tile) with the full row range each, so no split partials are
+// kept; each item writes its fp64 tile of C or of G's lower triangle (tiles
+// on and below the diagonal; the Cholesky factorisation, the solves and the
+// trace read nothing else, so the upper triangle off the diagonal tiles is
+// left unwritten).
+constexpr int GRR_BLOCK = 5;                    // steps per unrolled block of the K loop
+constexpr int GRR_PAD = GRR_BLOCK * GR_BK;      // rows of each bit group padded to whole blocks
+constexpr int GRR_MAX_GROUPS = 16;
+
+struct GramRunsArgs {
+  const uint16_t* xg;       // [L_S][xg_rows][row]: the bit-group rows of every sender layer
+  const uint16_t* xu;       // [L_S][u_pad][row]: the distinct rows x_u
+  const uint16_t* qp;       // [problems][2 u_pad][f_out]: run sums of the targets, high then low parts
+  int64_t xg_layer, xu_layer, qp_layer;  // element strides between layers (problems for qp)
+  const int32_t* taps;      // device [problems][n_taps]: sender layer of each tap
+  double* G;                // problem p's G (f_in x f_in) and C (f_in x f_out) at p * bs
+  double* C;
+  int64_t bs;
+  int32_t row, xg_rows, u_pad, n_taps, n_problems;
+  int32_t f_in, f_out, nbi, nbc, n_g, n_c;
+  int32_t n_groups;
+  int32_t grp_end[GRR_MAX_GROUPS];  // block (of GRR_BLOCK steps) after which group g ends
+  int32_t grp_exp[GRR_MAX_GROUPS];  // its bit j
+};
+
+// arr[idx] of a kernel-argument array with constant indices only (stays in
+// scalar registers, no memory access inside the K loop)
+__device__ __forceinline__ int32_t grr_pick(const int32_t (&arr)[GRR_MAX_GROUPS], int32_t idx) {
+  int32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < GRR_MAX_GROUPS; ++i) v = (i == idx) ? arr[i] : v;
+  return v;
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(GR_THREADS, GR_THREADS), amdgpu_waves_per_eu(2, 2))) void
+gram_runs_kernel(const GramRunsArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint16_t p0[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p1[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p2[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p3[GR_PART];
+  __shared__ __attribute__((aligned(1024))) uint16_t p4[GR_PART];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave & 3, wn = wave >> 2;
+  const int32_t per = g.n_g + g.n_c;
+  const int64_t T = static_cast<int64_t>(g.n_problems) * per;
+  const int32_t NG = gridDim.x;
+  const int32_t slot = (NG % 8 == 0) ? (blockIdx.x & 7) * (NG >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const uint32_t xpitch = static_cast<uint32_t>(2 * g.row);
+
+  for (int64_t t = slot; t < T; t += NG) {
+    const int32_t prob = static_cast<int32_t>(t / per);
+    int32_t tt = static_cast<int32_t>(t % per);
+    int32_t bi, bj;
+    bool is_c;
+    if (tt < g.n_g) {
+      is_c = false;
+      bi = 0;
+      int32_t rowlen = g.nbi;
+      while (tt >= rowlen) {
+        tt -= rowlen;
+        ++bi;
+        --rowlen;
+      }
+      bj = bi + tt;
+      // the lower tile (bj, bi): every reader of G takes the lower triangle
+      // (and whole diagonal tiles), so each tile is stored once, in rows
+      const int32_t sw = bi;
+      bi = bj;
+      bj = sw;
+    } else {
+      is_c = true;
+      tt -= g.n_g;
+      bi = tt / g.nbc;
+      bj = tt % g.nbc;
+    }
+    const int32_t i0 = bi * GR_T, j0 = bj * GR_T;
+    // feature tile bi lies inside one tap's row (row is a multiple of 256)
+    const int32_t tap_i = g.taps[static_cast<int64_t>(prob) * g.n_taps + i0 / g.row];
+    const int32_t off_i = i0 % g.row;
+
+    GrItem it;
+    it.p_pitch = xpitch;
+    if (is_c) {
+      const uint16_t* pb = g.xu + tap_i * g.xu_layer + off_i;
+      const uint16_t* qb = g.qp + prob * g.qp_layer + j0;
+      it.pr = buf_rsrc(pb, static_cast<uint32_t>(static_cast<int64_t>(g.u_pad) * xpitch - 2 * off_i));
+      it.q_pitch = static_cast<uint32_t>(2 * g.f_out);
+      it.qr = buf_rsrc(qb, static_cast<uint32_t>(2LL * g.u_pad * it.q_pitch - 2 * j0));
+      it.p_wrap = g.u_pad / GR_BK;
+      it.nk = 2 * it.p_wrap;
+    } else {
+      const int32_t tap_j = g.taps[static_cast<int64_t>(prob) * g.n_taps + j0 / g.row];
+      const int32_t off_j = j0 % g.row;
+      const uint16_t* pb = g.xg + tap_i * g.xg_layer + off_i;
+      const uint16_t* qb = g.xg + tap_j * g.xg_layer + off_j;
+      it.pr = buf_rsrc(pb, static_cast<uint32_t>(static_cast<int64_t>(g.xg_rows) * xpitch - 2 * off_i));
+      it.q_pitch = xpitch;
+      it.qr = buf_rsrc(qb, static_cast<uint32_t>(static_cast<int64_t>(g.xg_rows) * xpitch - 2 * off_j));
+      it.p_wrap = GR_NO_WRAP;
+      it.nk = g.xg_rows / GR_BK;  // whole blocks: each bit group ends on a block boundary
+    }
+    if (it.nk == 0) {
+      it.pr = buf_rsrc(nullptr, 0);
+      it.qr = buf_rsrc(nullptr, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < GR_LD; ++i) {
+      const int r = 2 * (wave * GR_LD + i) + (lane >> 5);
+      const int pc = gr_chunk(r, lane & 31);
+      it.p_off[i] = static_cast<uint32_t>(r) * it.p_pitch + 16u * pc;
+      it.q_off[i] = static_cast<uint32_t>(r) * it.q_pitch + 16u * pc;
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    if (it.nk > 0) {
+      gr_issue(it.pr, it.p_pitch, it.p_off, 0, it.nk, p0, it.p_wrap);
+      gr_issue(it.qr, it.q_pitch, it.q_off, 0, it.nk, p1);
+      gr_issue(it.pr, it.p_pitch, it.p_off, 1, it.nk, p2, it.p_wrap);
+      int32_t grp = 0;                                   // current bit group (G items)
+      int32_t grp_end = is_c ? -1 : grr_pick(g.grp_end, 0);
+      int k = 0;
+      for (; k + GRR_BLOCK <= it.nk; k += GRR_BLOCK) {
+        GR_STEP_FULL(k, p0, p1, p3, p4)
+        GR_STEP_FULL(k + 1, p2, p3, p0, p1)
+        GR_STEP_FULL(k + 2, p4, p0, p2, p3)
+        GR_STEP_FULL(k + 3, p1, p2, p4, p0)
+        GR_STEP_FULL(k + 4, p3, p4, p1, p2)
+        if ((k + GRR_BLOCK) / GRR_BLOCK == grp_end) {
+          // end of bit group grp: double the sums (j_grp - j_next) times,
+          // j_next = 0 after the last group
+          const int32_t e_now = grr_pick(g.grp_exp, grp);
+          const int32_t e_next = grp + 1 < g.n_groups ? grr_pick(g.grp_exp, grp + 1) : 0;
+          const float f = __uint_as_float(static_cast<uint32_t>(127 + e_now - e_next) << 23);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[i][j][e] *= f;
+          ++grp;
+          grp_end = grp < g.n_groups ? grr_pick(g.grp_end, grp) : -1;
+        }
+      }
+      if (k < it.nk) {  // C items only: the 1..4 remaining steps
+        GR_STEP(k, p0, p1, p3, p4, true)
+        GR_STEP(k + 1, p2, p3, p0, p1, k + 1 < it.nk)
+        GR_STEP(k + 2, p4, p0, p2, p3, k + 2 < it.nk)
+        GR_STEP(k + 3, p1, p2, p4, p0, k + 3 < it.nk)
+        GR_STEP(k + 4, p3, p4, p1, p2, k + 4 < it.nk)
+      }
+      KVX_WAIT_VM(0);
+    }
+
+    double* G = g.G + prob * g.bs;
+    double* C = g.C + prob * g.bs;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t i = i0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int32_t j = j0 + wn * 128 + ni * 32 + (lane & 31);
+          const double v = static_cast<double>(acc[mi][ni][r]);
+          if (is_c) {
+            if (i < g.f_in && j < g.f_out) C[static_cast<int64_t>(i) * g.f_out + j] = v;
+          } else if (i < g.f_in && j < g.f_in) {
+            G[static_cast<int64_t>(i) * g.f_in + j] = v;
+          }
+        }
+    __syncthreads();
+  }
+}
+
+// out[s][r][:] = the sender row of run list[r] (list null: run r < n_valid) of
+// sender layer s, or zeros (padding), 16 bytes per thread.
+__global__ __launch_bounds__(256) void fitc_gather_kernel(const uint16_t* __restrict__ send, int64_t send_layer,
+                                                          int32_t row, const int32_t* __restrict__ uniq,
+                                                          const int32_t* __restrict__ list, int32_t n_valid,
+                                                          int32_t rows_out, uint16_t* __restrict__ out,
+                                                          int64_t out_layer) {
+  const int64_t sl = blockIdx.y;
+  const int32_t cpr = row / 8;
+  const int64_t total = static_cast<int64_t>(rows_out) * cpr;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * 256) {
+    const int32_t r = static_cast<int32_t>(t / cpr), c = static_cast<int32_t>(t % cpr);
+    const int32_t u = list ? list[r] : (r < n_valid ? r : -1);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (u >= 0) {
+      const int64_t tok = uniq[u];
+      v = *reinterpret_cast<const u32x4*>(send + sl * send_layer + tok * row + 8 * c);
+    }
+    *reinterpret_cast<u32x4*>(out + sl * out_layer + static_cast<int64_t>(r) * row + 8 * c) = v;
+  }
+}
+
+// Run sums of the targets of problem l: s_u = sum over the run's tokens i
+// (in token order, fp32) of y[l][i][:]; qp[l][u] = bf16(s_u) (nearest even)
+// and qp[l][u_pad + u] = bf16(s_u - that), zeros for u >= U.  8 outputs per
+// thread.  y_layer: elements between the problems' target layers.
+__global__ __launch_bounds__(256) void fitc_target_sums_kernel(const uint16_t* __restrict__ y, int64_t y_layer,
+                                                               int32_t f_out, const int32_t* __restrict__ run_begin,
+                                                               int32_t n_runs, int32_t u_pad,
+                                                               uint16_t* __restrict__ qp, int64_t qp_layer) {
+  const int64_t l = blockIdx.y;
+  const int32_t cpr = f_out / 8;
+  const int64_t total = static_cast<int64_t>(u_pad) * cpr;
+  const uint16_t* yl = y + l * y_layer;
+  uint16_t* ql = qp + l * qp_layer;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * 256) {
+    const int32_t u = static_cast<int32_t>(t / cpr), c = static_cast<int32_t>(t % cpr);
+    float sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
+    if (u < n_runs) {
+      for (int32_t i = run_begin[u]; i < run_begin[u + 1]; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(yl + static_cast<int64_t>(i) * f_out + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[2 * e] += bf16lo(v[e]);
+          sum[2 * e + 1] += bf16hi(v[e]);
+        }
+      }
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t h0 = f32_to_bf16_rne(sum[2 * e]), h1 = f32_to_bf16_rne(sum[2 * e + 1]);
+      const uint16_t l0 = f32_to_bf16_rne(sum[2 * e] - bf16_to_f32(h0));
+      const uint16_t l1 = f32_to_bf16_rne(sum[2 * e + 1] - bf16_to_f32(h1));
+      hi[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+      lo[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+    }
+    *reinterpret_cast<u32x4*>(ql + static_cast<int64_t>(u) * f_out + 8 * c) = hi;
+    *reinterpret_cast<u32x4*>(ql + (static_cast<int64_t>(u_pad) + u) * f_out + 8 * c) = lo;
+  }
+}
+
 #undef GR_STEP
 #undef GR_STEP_FULL
 
@@ -533,9 +801,10 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
 // z start bsa, bsb, bsc elements after those of problem z-1), with
 // A(m,k) = A[m*sam + k*sak] and B(k,n) = B[k*sbk + n*sbn].  Block tiles of
 // 2 WT x 2 WT; four waves of WT x WT, each from MFMA 16x16x4 fp64 blocks; K in
-// chunks of 16 through LDS as [k][m] and [k][n] (global elements are read
-// along the operand's unit-stride index; rows padded so the 16-lane row
-// pieces of a fragment read fall in distinct banks); the next chunk is read
+// chunks of 16 through LDS (global elements are read along the operand's
+// unit-stride index and kept in that order: [k][m] / [k][n], or [m][k] /
+// [n][k] for an operand read along k; rows padded against bank conflicts of
+// the stores and of the fragment reads); the next chunk is read
 // into registers while the current one is multiplied.  A workgroup reads all
 // of its A rows and B columns before it writes its tile, so C may alias A when
 // N <= 2 WT or B when M <= 2 WT.  lower_only skips tiles strictly above the
@@ -556,17 +825,22 @@ constexpr int DG_BK = 16;
 // before the K loop; WT = 64: 128 x 128 block tiles (large products, long K).
 // AK / BK: A / B read along k (unit stride in k), else along m / n.
 template <int WT, bool AK, bool BK>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WT == 32 ? 4 : 2, 8))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WT == 32 ? 3 : 2, 8))) void
 dgemm_kernel(const DgArgs g) {
   constexpr int BT = 2 * WT;           // block tile
-  constexpr int LD = BT + 16;          // LDS row (doubles): 16-lane row pieces in distinct banks
+  constexpr int LD = BT + 16;          // [k][m] rows (doubles): 16-lane row pieces in distinct banks
+  // an operand read along k is kept [m][k] with an odd row stride: a thread's
+  // store is then contiguous with its neighbours' and the 16 rows of a
+  // fragment read start in distinct bank pairs (kept [k][m], its transposing
+  // stores put 8 lanes on one bank pair)
+  constexpr int LDK = DG_BK + 1;
   constexpr int NQ = BT * DG_BK / 256; // elements of A (and of B) per thread and chunk
   constexpr int NF = WT / 16;          // MFMA blocks per wave and dimension
   constexpr bool PRE_C = WT == 32;
   const int32_t bm = blockIdx.y, bn = blockIdx.x;
   if (g.lower_only && bm < bn) return;
-  __shared__ double As[DG_BK][LD];
-  __shared__ double Bs[DG_BK][LD];
+  __shared__ double As[AK ? BT : DG_BK][AK ? LDK : LD];
+  __shared__ double Bs[BK ? BT : DG_BK][BK ? LDK : LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int32_t m0 = bm * BT, n0 = bn * BT;
@@ -624,8 +898,14 @@ dgemm_kernel(const DgArgs g) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
-      As[a_k ? (e & 15) : (e / BT)][a_k ? (e >> 4) : (e % BT)] = av[q];
-      Bs[b_k ? (e & 15) : (e / BT)][b_k ? (e >> 4) : (e % BT)] = bv[q];
+      if constexpr (AK)
+        As[e >> 4][e & 15] = av[q];
+      else
+        As[e / BT][e % BT] = av[q];
+      if constexpr (BK)
+        Bs[e >> 4][e & 15] = bv[q];
+      else
+        Bs[e / BT][e % BT] = bv[q];
     }
     __syncthreads();
     if (k0 + DG_BK < g.K) load(k0 + DG_BK);
@@ -635,9 +915,21 @@ dgemm_kernel(const DgArgs g) {
       const int kr = k4 + (lane >> 4);
       double a[NF], b[NF];
 #pragma unroll
-      for (int i = 0; i < NF; ++i) a[i] = As[kr][wm * WT + i * 16 + (lane & 15)];
+      for (int i = 0; i < NF; ++i) {
+        const int m = wm * WT + i * 16 + (lane & 15);
+        if constexpr (AK)
+          a[i] = As[m][kr];
+        else
+          a[i] = As[kr][m];
+      }
 #pragma unroll
-      for (int j = 0; j < NF; ++j) b[j] = Bs[kr][wn * WT + j * 16 + (lane & 15)];
+      for (int j = 0; j < NF; ++j) {
+        const int nn = wn * WT + j * 16 + (lane & 15);
+        if constexpr (BK)
+          b[j] = Bs[nn][kr];
+        else
+          b[j] = Bs[kr][nn];
+      }
 #pragma unroll
       for (int i = 0; i < NF; ++i)
 #pragma unroll
@@ -755,10 +1047,13 @@ struct FitWs {
   size_t bytes;
 };
 
-static FitWs fit_layout(int32_t count, int32_t f_in, int32_t f_out, void* base) {
+// with_part = false: no Gram split partials (the Gram from runs writes G and
+// C directly).
+static FitWs fit_layout(int32_t count, int32_t f_in, int32_t f_out, void* base, bool with_part = true) {
   FitWs w{};
   Carve c(base);
-  w.part = c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out));
+  w.part = with_part ? c.take<float>(static_cast<size_t>(GR_MAX_SPLIT) * f_in * (static_cast<size_t>(f_in) + f_out))
+                     : nullptr;
   w.csp = c.take<double>(static_cast<size_t>(CS_CHUNKS) * (f_in > f_out ? f_in : f_out));
   const int64_t nb_total = ceil_div(f_in, CH_NB);
   auto up = [](int64_t v) { return (v + 31) / 32 * 32; };  // 256-byte sub-areas
@@ -1129,6 +1424,200 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
   KVX_HIP_TRY(hipStreamSynchronize(s));
   int result = KVX_OK;
   for (int32_t z = 0; z < count; ++z) {
+    if (status) status[z] = host_flags[z] ? KVX_ERR_NOT_SPD : KVX_OK;
+    if (host_flags[z]) result = KVX_ERR_NOT_SPD;
+  }
+  return result;
+}
+
+// ---------------------------------------------------------------- fit from the caches
+//
+// Every receiver layer and role of a model pair from the calibration caches
+// (see gram_runs_kernel for the Gram from the alignment's runs).  Problems are
+// ordered role by role (K, then V), receiver layer within; the fp64 solve is
+// the one of launch_fit, all problems at once.
+
+__global__ __launch_bounds__(256) void lambda_batched_kernel(double* __restrict__ G, int64_t bs, int32_t f_in,
+                                                             double lam_abs, double lam_rel,
+                                                             double* __restrict__ lam_out) {
+  // problem blockIdx.x: the same fixed summation order as lambda_kernel
+  G += blockIdx.x * bs;
+  __shared__ double red[256];
+  double sum = 0.0;
+  for (int32_t i = threadIdx.x; i < f_in; i += 256) sum += G[static_cast<int64_t>(i) * f_in + i];
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double lam = lam_abs + lam_rel * red[0] / static_cast<double>(f_in);
+  for (int32_t i = threadIdx.x; i < f_in; i += 256) G[static_cast<int64_t>(i) * f_in + i] += lam;
+  if (threadIdx.x == 0) lam_out[blockIdx.x * bs] = lam;
+}
+
+struct FitcWs {
+  FitWs fit;
+  Runs runs;
+  void* runs_scratch;
+  int32_t* glist;
+  int32_t* taps;
+  uint16_t* xu;
+  uint16_t* xg;
+  uint16_t* qp;
+  int64_t u_cap, g_cap;  // row capacities of xu (and half of qp) and xg
+  size_t bytes;
+};
+
+// Sized for the worst case of n_recv runs of one token: U <= n_recv, and the
+// bit-group rows sum_u popcount(c_u) <= sum_u c_u = n_recv, plus padding.
+static FitcWs fitc_layout(const FitcShape& sh, void* base) {
+  FitcWs w{};
+  w.fit = fit_layout(sh.count, sh.f_in, sh.f_out, base, false);
+  Carve c(base);
+  c.used = w.fit.bytes;
+  const int32_t n = sh.n_recv;
+  w.runs.uniq = c.take<int32_t>(n);
+  w.runs.run_begin = c.take<int32_t>(static_cast<size_t>(n) + 1);
+  w.runs.recv_to_uniq = c.take<int32_t>(n);
+  w.runs.n_uniq = c.take<int32_t>(64);
+  w.runs_scratch = c.take<char>(runs_ws_bytes(n));
+  w.u_cap = ceil_div(n, GR_BK) * GR_BK;
+  w.g_cap = ceil_div(static_cast<int64_t>(n) + static_cast<int64_t>(GRR_MAX_GROUPS) * GRR_PAD, GRR_PAD) * GRR_PAD;
+  w.glist = c.take<int32_t>(static_cast<size_t>(w.g_cap));
+  w.taps = c.take<int32_t>(static_cast<size_t>(sh.recv_layers) * sh.n_taps);
+  w.xu = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.u_cap * sh.row);
+  w.xg = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.g_cap * sh.row);
+  w.qp = c.take<uint16_t>(static_cast<size_t>(sh.recv_layers) * 2 * w.u_cap * sh.f_out);
+  w.bytes = c.used + 256;
+  return w;
+}
+
+size_t fitc_ws_bytes(const FitcShape& sh) { return fitc_layout(sh, nullptr).bytes; }
+
+int64_t fitc_max_rows(const FitcShape& sh) {
+  const FitcWs w = fitc_layout(sh, nullptr);
+  return w.g_cap > 2 * w.u_cap ? w.g_cap : 2 * w.u_cap;
+}
+
+// The bit groups of the run lengths c_u (from run_begin, host), largest bit
+// first: group j holds the runs with bit j of c_u set (j < 15), group 15 the
+// runs with c_u >= 2^15, each c_u >> 15 times; each group padded with -1 to
+// whole GRR_PAD rows.
+static void fitc_groups(const std::vector<int32_t>& rb, int32_t n_runs, std::vector<int32_t>& list,
+                        GramRunsArgs& g) {
+  list.clear();
+  g.n_groups = 0;
+  for (int j = GRR_MAX_GROUPS - 1; j >= 0; --j) {
+    const size_t start = list.size();
+    for (int32_t u = 0; u < n_runs; ++u) {
+      const int32_t cu = rb[static_cast<size_t>(u) + 1] - rb[static_cast<size_t>(u)];
+      const int32_t reps = j == GRR_MAX_GROUPS - 1 ? (cu >> (GRR_MAX_GROUPS - 1)) : ((cu >> j) & 1);
+      for (int32_t q = 0; q < reps; ++q) list.push_back(u);
+    }
+    if (list.size() == start) continue;
+    while (list.size() % GRR_PAD) list.push_back(-1);
+    g.grp_exp[g.n_groups] = j;
+    g.grp_end[g.n_groups] = static_cast<int32_t>(list.size() / GRR_PAD);
+    ++g.n_groups;
+  }
+}
+
+int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
+                      const int32_t* map, const int32_t* taps_host, double lam_abs, double lam_rel,
+                      float* const* w_role, int32_t* status, void* ws, hipStream_t s) {
+  const FitcWs w = fitc_layout(sh, ws);
+  const int64_t bs = w.fit.bs;
+  if (int st = launch_fill_i32(w.fit.flags, sh.count, 0, s)) return st;
+
+  // 1. runs of the alignment; their lengths on the host for the bit groups
+  if (int st = launch_runs(map, sh.n_recv, sh.n_send, w.runs, w.runs_scratch, s)) return st;
+  int32_t n_runs = 0;
+  KVX_HIP_TRY(hipMemcpyAsync(&n_runs, w.runs.n_uniq, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  KVX_HIP_TRY(hipStreamSynchronize(s));
+  if (n_runs < 1 || n_runs > sh.n_recv) return KVX_ERR_HIP;
+  std::vector<int32_t> rb(static_cast<size_t>(n_runs) + 1);
+  KVX_HIP_TRY(hipMemcpyAsync(rb.data(), w.runs.run_begin, sizeof(int32_t) * rb.size(), hipMemcpyDeviceToHost, s));
+  KVX_HIP_TRY(hipStreamSynchronize(s));
+  GramRunsArgs g{};
+  std::vector<int32_t> list;
+  fitc_groups(rb, n_runs, list, g);
+  if (static_cast<int64_t>(list.size()) > w.g_cap) return KVX_ERR_HIP;
+  const int32_t u_pad = static_cast<int32_t>(ceil_div(n_runs, GR_BK) * GR_BK);
+  KVX_HIP_TRY(hipMemcpyAsync(w.glist, list.data(), sizeof(int32_t) * list.size(), hipMemcpyHostToDevice, s));
+
+  g.row = sh.row;
+  g.xg_rows = static_cast<int32_t>(list.size());
+  g.u_pad = u_pad;
+  g.xg_layer = static_cast<int64_t>(g.xg_rows) * sh.row;
+  g.xu_layer = static_cast<int64_t>(u_pad) * sh.row;
+  g.qp_layer = 2LL * u_pad * sh.f_out;
+  g.xg = w.xg;
+  g.xu = w.xu;
+  g.qp = w.qp;
+  g.taps = w.taps;
+  g.n_taps = sh.n_taps;
+  g.n_problems = sh.recv_layers;
+  g.f_in = sh.f_in;
+  g.f_out = sh.f_out;
+  g.nbi = static_cast<int32_t>(ceil_div(sh.f_in, GR_T));
+  g.nbc = static_cast<int32_t>(ceil_div(sh.f_out, GR_T));
+  g.n_g = g.nbi * (g.nbi + 1) / 2;
+  g.n_c = g.nbi * g.nbc;
+  g.bs = bs;
+  KVX_HIP_TRY(hipMemcpyAsync(w.taps, taps_host, sizeof(int32_t) * sh.recv_layers * sh.n_taps, hipMemcpyHostToDevice,
+                             s));
+
+  // 2. per role: the distinct rows and the bit-group rows of every sender
+  // layer, the run sums of the targets, then the Gram of all its problems
+  const int cus = device_cu_count();
+  for (int32_t r = 0; r < sh.n_roles; ++r) {
+    const uint16_t* xs = static_cast<const uint16_t*>(send_role[r]);
+    const uint16_t* ys = static_cast<const uint16_t*>(recv_role[r]);
+    const int64_t send_layer = static_cast<int64_t>(sh.n_send) * sh.row;
+    const unsigned gx_u = static_cast<unsigned>(std::min<int64_t>(ceil_div(g.xu_layer / 8, 256), 4096));
+    fitc_gather_kernel<<<dim3(gx_u, static_cast<unsigned>(sh.send_layers)), 256, 0, s>>>(
+        xs, send_layer, sh.row, w.runs.uniq, nullptr, n_runs, u_pad, w.xu, g.xu_layer);
+    KVX_LAUNCH_CHECK();
+    const unsigned gx_g = static_cast<unsigned>(std::min<int64_t>(ceil_div(g.xg_layer / 8, 256), 4096));
+    fitc_gather_kernel<<<dim3(gx_g, static_cast<unsigned>(sh.send_layers)), 256, 0, s>>>(
+        xs, send_layer, sh.row, w.runs.uniq, w.glist, 0, g.xg_rows, w.xg, g.xg_layer);
+    KVX_LAUNCH_CHECK();
+    const unsigned gx_q =
+        static_cast<unsigned>(std::min<int64_t>(ceil_div(static_cast<int64_t>(u_pad) * sh.f_out / 8, 256), 4096));
+    fitc_target_sums_kernel<<<dim3(gx_q, static_cast<unsigned>(sh.recv_layers)), 256, 0, s>>>(
+        ys, static_cast<int64_t>(sh.n_recv) * sh.f_out, sh.f_out, w.runs.run_begin, n_runs, u_pad, w.qp, g.qp_layer);
+    KVX_LAUNCH_CHECK();
+    GramRunsArgs gr = g;
+    gr.G = w.fit.G + static_cast<int64_t>(r) * sh.recv_layers * bs;
+    gr.C = w.fit.C + static_cast<int64_t>(r) * sh.recv_layers * bs;
+    const int64_t items = static_cast<int64_t>(sh.recv_layers) * (g.n_g + g.n_c);
+    gram_runs_kernel<<<static_cast<unsigned>(items < cus ? items : cus), GR_THREADS, 0, s>>>(gr);
+    KVX_LAUNCH_CHECK();
+  }
+  lambda_batched_kernel<<<static_cast<unsigned>(sh.count), 256, 0, s>>>(w.fit.G, bs, sh.f_in, lam_abs, lam_rel,
+                                                                        w.fit.lam);
+  KVX_LAUNCH_CHECK();
+
+  // 3. Cholesky and the two block triangular solves of all problems at once
+  if (int st = chol_factor(s, sh.count, w.fit.G, sh.f_in, bs, w.fit.linv, w.fit.xinv, w.fit.zbuf, w.fit.flags))
+    return st;
+  if (int st = chol_forward(s, sh.count, w.fit.G, sh.f_in, bs, w.fit.xinv, w.fit.zbuf, w.fit.C, sh.f_out)) return st;
+  if (int st = chol_backward(s, sh.count, w.fit.G, sh.f_in, bs, w.fit.xinv, w.fit.zbuf, w.fit.C, sh.f_out)) return st;
+
+  // 4. outputs [f_in][f_out] per problem
+  const int64_t nw = static_cast<int64_t>(sh.f_in) * sh.f_out;
+  for (int32_t z = 0; z < sh.count; ++z) {
+    float* out = w_role[z / sh.recv_layers] + static_cast<int64_t>(z % sh.recv_layers) * nw;
+    fit_store_kernel<<<grid_for(nw), 256, 0, s>>>(w.fit.C + z * bs, nw, out);
+    KVX_LAUNCH_CHECK();
+  }
+
+  std::vector<int32_t> host_flags(static_cast<size_t>(sh.count), 0);
+  KVX_HIP_TRY(hipMemcpyAsync(host_flags.data(), w.fit.flags, sizeof(int32_t) * sh.count, hipMemcpyDeviceToHost, s));
+  KVX_HIP_TRY(hipStreamSynchronize(s));
+  int result = KVX_OK;
+  for (int32_t z = 0; z < sh.count; ++z) {
     if (status) status[z] = host_flags[z] ? KVX_ERR_NOT_SPD : KVX_OK;
     if (host_flags[z]) result = KVX_ERR_NOT_SPD;
   }

@@ -16,4 +16,20 @@ int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void*
                    float* const* w_out, float* const* b_out, int32_t* status, int32_t* iters, void* ws,
                    hipStream_t s);
 
+// Ridge fits of every receiver layer of n_roles roles from the calibration
+// caches (kvx_fit_ridge_caches): shapes, host arrays of the roles' cache
+// pointers and outputs; problems role by role, receiver layer within.
+struct FitcShape {
+  int32_t send_layers, n_send, row;        // sender: layers, tokens, H_S d_S (a multiple of 256)
+  int32_t recv_layers, n_recv, f_out;      // receiver: layers, tokens, H_R d_R
+  int32_t n_taps, f_in, n_roles, count;    // f_in = n_taps row, count = n_roles recv_layers
+};
+size_t fitc_ws_bytes(const FitcShape& sh);
+// the most rows a per-layer operand of the Gram can have (for the 32-bit
+// offset limit of its loads)
+int64_t fitc_max_rows(const FitcShape& sh);
+int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
+                      const int32_t* map, const int32_t* taps_host, double lam_abs, double lam_rel,
+                      float* const* w_role, int32_t* status, void* ws, hipStream_t s);
+
 }  // namespace kvx

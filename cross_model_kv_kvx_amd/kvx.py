@@ -33,7 +33,7 @@ EXPORTS = (
     "kvx_quantize_fp8", "kvx_translate_fp8", "kvx_align_tokens_async", "kvx_translate_recorded",
     "kvx_align_tokens_noalloc", "kvx_prepared_maps_size", "kvx_prepare_maps",
     "kvx_translate_prepared_workspace_size", "kvx_translate_prepared", "kvx_probe_hbm", "kvx_probe_mfma",
-    "kvx_probe_scratch_words",
+    "kvx_probe_scratch_words", "kvx_fit_ridge_caches_workspace_size", "kvx_fit_ridge_caches",
 )
 
 
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
             "kvx_fit_ridge": (ctypes.c_int, [vp, i64, vp, i64, i32, i64, i32, i32, dbl, dbl, i32, vp, vp, vp, sz,
                                              vp]),
             "kvx_fit_ridge_batched_workspace_size": (sz, [i32, i32, i32]),
+            "kvx_fit_ridge_caches_workspace_size": (sz, [dp, dp, i32]),
+            "kvx_fit_ridge_caches": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, dbl, dbl, vp, vp, ip, vp,
+                                                    sz, vp]),
             "kvx_fit_ridge_batched": (ctypes.c_int, [i32, vpp, i64, vpp, i64, i32, i64, i32, i32, dbl, dbl, i32,
                                                      vpp, vpp, ip, vp, sz, vp]),
             "kvx_fit_recolor_workspace_size": (sz, [i32, i32, i32]),
@@ -540,6 +543,61 @@ def fit_ridge_batched(xs, ys, *, lambda_abs: float = 0.0, lambda_rel: float = 0.
     else:
         _check(st, "kvx_fit_ridge_batched")
     return w_outs, (b_outs if fit_intercept else [None] * count)
+
+
+def fit_ridge_caches_workspace_size(send: CacheDesc, recv: CacheDesc, n_taps: int) -> int:
+    return int(lib().kvx_fit_ridge_caches_workspace_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps)))
+
+
+def fit_ridge_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], k_recv: Optional[torch.Tensor],
+                     v_recv: Optional[torch.Tensor], recv_to_send: torch.Tensor, taps, *, lambda_abs: float = 0.0,
+                     lambda_rel: float = 0.0, w_k: Optional[torch.Tensor] = None, w_v: Optional[torch.Tensor] = None,
+                     roles=("k", "v"), workspace: Optional[torch.Tensor] = None, stream=None,
+                     status: Optional[list] = None):
+    """kvx_fit_ridge_caches: the ridge maps of every receiver layer of the
+    requested ``roles`` from the calibration caches (bf16 [L][N][H][d]; the
+    sender's N_S tokens, the receiver's N), the alignment ``recv_to_send``
+    (device int32 [N]) and ``taps`` (host int32 [L_R][n_taps]).  Returns
+    (w_k, w_v), fp32 [L_R][F_in][F_out] (None for a role not requested).
+    With a list ``status``, appends the [2][L_R] per-problem statuses and
+    raises only for other errors."""
+    taps = np.ascontiguousarray(taps, dtype=np.int32)
+    L_R, n_taps = taps.shape
+    ref_send = k_send if "k" in roles else v_send
+    ref_recv = k_recv if "k" in roles else v_recv
+    send, recv = cache_desc(ref_send), cache_desc(ref_recv)
+    if recv.layers != L_R:
+        raise ValueError("taps rows must equal the receiver's layers")
+    for t in (k_send, v_send, k_recv, v_recv):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("caches must be contiguous")
+    f_in = n_taps * send.kv_heads * send.head_dim
+    f_out = recv.kv_heads * recv.head_dim
+    dev = ref_send.device
+    if "k" in roles and w_k is None:
+        w_k = torch.empty((L_R, f_in, f_out), dtype=torch.float32, device=dev)
+    if "v" in roles and w_v is None:
+        w_v = torch.empty((L_R, f_in, f_out), dtype=torch.float32, device=dev)
+    if "k" not in roles:
+        w_k = None
+    if "v" not in roles:
+        w_v = None
+    ws = _workspace(fit_ridge_caches_workspace_size(send, recv, n_taps), dev, workspace)
+    st_arr = (ctypes.c_int32 * (2 * L_R))()
+    st = lib().kvx_fit_ridge_caches(ctypes.byref(send), _ptr(k_send if w_k is not None else None),
+                                    _ptr(v_send if w_v is not None else None), ctypes.byref(recv),
+                                    _ptr(k_recv if w_k is not None else None),
+                                    _ptr(v_recv if w_v is not None else None), _ptr(recv_to_send),
+                                    taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_taps),
+                                    float(lambda_abs), float(lambda_rel), _ptr(w_k), _ptr(w_v), st_arr, _ptr(ws),
+                                    ws.numel(), _stream(stream))
+    if status is not None:
+        status.extend(int(v) for v in st_arr)
+        if st not in (OK, ERR_NOT_SPD):
+            _check(st, "kvx_fit_ridge_caches")
+    else:
+        _check(st, "kvx_fit_ridge_caches")
+    return w_k, w_v
 
 
 def fit_recolor(xs, ys, *, rho_x: float = 0.0, rho_y: float = 0.0, w_outs=None, b_outs=None,

@@ -354,6 +354,60 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
                           int32_t* status, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The ridge fits of every receiver layer and role of one model pair,
+ * straight from the calibration caches ("Cross-Model KV Cache Transfer in
+ * Production", stage 2: W = (X^T X + lambda I)^-1 X^T Y per layer pair, with
+ * X the sender features of the matched layers (stage 3's layer map and the
+ * taps) at each receiver token's aligned sender token, and Y the receiver's
+ * own cache rows).  The result equals kvx_fit_ridge_batched on the features
+ * kvx_gather_features builds (no rotation, no intercept), up to the rounding
+ * of the sums, without materialising those features:
+ *   - a receiver token's feature row is the row of its aligned sender token,
+ *     so X^T X = sum over runs u of equal map values of c_u x_u x_u^T (c_u =
+ *     the run's length): formed from the distinct rows, each run's count
+ *     written in binary, the rows with bit j set accumulated as one group and
+ *     the groups combined by exact doublings (every product stays exact in
+ *     the fp32 sums, as in kvx_fit_ridge_batched);
+ *   - X^T Y = sum over runs of x_u (sum of the run's target rows)^T, each
+ *     run's target sum formed in fp32 in token order and taken to 16
+ *     significant bits as a high and a low bf16 part (the error this adds is
+ *     at most 2^-16 of the sum, below the fp32 accumulation error of the
+ *     products).
+ *
+ * send, k_send, v_send: the sender's calibration caches [L_S][N_S][H_S][d_S]
+ *   (bf16, rope_base 0: features are the rows as stored), 16-byte aligned.
+ * recv, k_recv, v_recv: the receiver's calibration caches [L_R][N][H_R][d_R]
+ *   (bf16, rope_base 0, 16-byte aligned), the targets of each receiver
+ *   layer; N = recv->tokens.
+ * recv_to_send: device int32 [N], the calibration alignment (values clamped
+ *   into [0, N_S) as in kvx_translate).
+ * taps: host int32 [L_R][n_taps] from kvx_layer_map; the features of
+ *   receiver layer l are taps[l][0..n_taps) x H_S d_S (F_in = n_taps H_S d_S,
+ *   F_out = H_R d_R).  H_S d_S must be a multiple of 256; F_out a multiple
+ *   of 8; F_in, F_out <= KVX_MAX_FIT_FEATURES.
+ * lambda = lambda_abs + lambda_rel * trace(X^T X) / F_in per problem.
+ * w_k, w_v: device fp32 [L_R][F_in][F_out] (row-major, y = x W, the layout
+ *   kvx_translate takes), or NULL to skip that role (at least one given).
+ *   No intercept is fitted (use kvx_fit_ridge_batched for one).
+ * status: host int32 [2][L_R] or NULL: per role and layer KVX_OK or
+ *   KVX_ERR_NOT_SPD (a skipped role's entries are KVX_OK).
+ * workspace: kvx_fit_ridge_caches_workspace_size(send, recv, n_taps) bytes
+ *   (sized for the worst case of N runs of one token: the fp64 systems of
+ *   2 L_R problems plus, for one role at a time, the distinct sender rows of
+ *   every sender layer, twice, and the receiver's run sums).
+ * Synchronises `stream` twice (the run lengths, the factorisation flags).
+ * KVX_ERR_UNSUPPORTED for other dtypes, rotated caches or shapes; otherwise
+ * errors as kvx_fit_ridge_batched.
+ * ---------------------------------------------------------------------- */
+size_t kvx_fit_ridge_caches_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv,
+                                           int32_t n_taps);
+int kvx_fit_ridge_caches(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                         const kvx_cache_desc* recv, const void* k_recv, const void* v_recv,
+                         const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                         double lambda_abs, double lambda_rel, float* w_k, float* w_v,
+                         int32_t* status, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * kvx_align_tokens without synchronisation, for callers that chain the
  * alignment and the translation on one stream: the same map, and *invalid
  * (device int32) is set to 1 when an offset array is not positive and

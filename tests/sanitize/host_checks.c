@@ -491,6 +491,40 @@ static void check_fits(void) {
   free(status);
 }
 
+static void check_fit_from_caches(const int32_t* taps36) {
+  const size_t huge_ws = (size_t)1 << 40;
+  kvx_cache_desc s = desc(36, 50000, 8, 128, KVX_BF16, 0.0), r = desc(32, 65536, 8, 128, KVX_BF16, 0.0);
+  EXPECT(kvx_fit_ridge_caches_workspace_size(&s, &r, 3) > (size_t)64 * 8 * (3072 * 3072 + 3072 * 1024));
+  kvx_cache_desc rmax = desc(255, INT32_MAX, 8, 128, KVX_BF16, 0.0), smax = desc(255, INT32_MAX, 8, 128, KVX_BF16, 0.0);
+  EXPECT(kvx_fit_ridge_caches_workspace_size(&smax, &rmax, 7) > 0);
+  kvx_cache_desc r0 = desc(32, 0, 8, 128, KVX_BF16, 0.0);
+  EXPECT_EQ(kvx_fit_ridge_caches_workspace_size(&s, &r0, 3), 0);
+  float* w = (float*)FAKE;
+#define FC(sd, rd, ks, kr, map, taps, nt, lam, wk, wv, wsb) \
+  kvx_fit_ridge_caches(sd, ks, FAKE, rd, kr, FAKE, map, taps, nt, 0.0, lam, wk, wv, NULL, FAKE, wsb, NULL)
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, taps36, 3, 1e-3, NULL, NULL, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, taps36, 3, NAN, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(FC(&s, &r, NULL, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, NULL, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, NULL, 3, 1e-3, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, taps36, 0, 1e-3, w, w, huge_ws), KVX_ERR_INVALID);
+  int32_t* bad = exact_i32(taps36, 96);
+  bad[95] = 36;
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, bad, 3, 1e-3, w, w, huge_ws), KVX_ERR_INVALID);
+  free(bad);
+  kvx_cache_desc srot = desc(36, 50000, 8, 128, KVX_BF16, 1e4);
+  EXPECT_EQ(FC(&srot, &r, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+  kvx_cache_desc snarrow = desc(36, 50000, 3, 64, KVX_BF16, 0.0);
+  EXPECT_EQ(FC(&snarrow, &r, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+  EXPECT_EQ(FC(&s, &r, (void*)(uintptr_t)0x1008, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+  EXPECT_EQ(FC(&s, &r0, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_SHAPE);
+  EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, 16), KVX_ERR_WORKSPACE);
+  /* the Gram's 32-bit offsets: too many calibration tokens for one call */
+  kvx_cache_desc rbig = desc(32, 1 << 26, 8, 128, KVX_BF16, 0.0);
+  EXPECT_EQ(FC(&s, &rbig, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+#undef FC
+}
+
 static void check_maps_and_probes(void) {
   const float* w = (const float*)FAKE;
   EXPECT_EQ(kvx_quantize_fp8(w, 0, 16, 16, (uint8_t*)FAKE, (float*)FAKE, NULL), KVX_OK);
@@ -525,6 +559,7 @@ int main(void) {
   check_translate(taps36);
   check_gather();
   check_fits();
+  check_fit_from_caches(taps36);
   check_maps_and_probes();
   free(taps36);
   if (failures) {

@@ -220,3 +220,38 @@ def test_prepared_maps_sizes_and_validation():
     assert tpp(w_dtype=2) == kvx.ERR_INVALID
     assert tpp(ws_bytes=16) == kvx.ERR_WORKSPACE
     assert tpp(events=(ctypes.c_void_p * 3)(0x1000, 0, 0x1000)) == kvx.ERR_INVALID
+
+
+def test_fit_from_caches_validation():
+    """kvx_fit_ridge_caches: sizes and argument checks before anything runs."""
+    L = kvx.lib()
+    fake = ctypes.c_void_p(0x1000)
+    s, r = desc(36, 50000, 8, 128), desc(32, 65536, 8, 128)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tp = taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    size = kvx.fit_ridge_caches_workspace_size(s, r, 3)
+    # the fp64 systems of 64 problems at least
+    assert size > 64 * 8 * (3072 * 3072 + 3072 * 1024)
+    assert kvx.fit_ridge_caches_workspace_size(s, desc(32, 0, 8, 128), 3) == 0
+    assert kvx.fit_ridge_caches_workspace_size(s, r, 0) == 0
+
+    def call(sd=s, rd=r, taps_p=tp, n_taps=3, lam=1e-3, wk=fake, wv=fake, ws=1 << 40, ks=fake, kr=fake,
+             m=fake):
+        return L.kvx_fit_ridge_caches(ctypes.byref(sd), ks, fake, ctypes.byref(rd), kr, fake, m, taps_p, n_taps,
+                                      0.0, lam, wk, wv, None, fake, ws, None)
+
+    assert call(wk=None, wv=None) == kvx.ERR_INVALID             # no role
+    assert call(lam=-1.0) == kvx.ERR_INVALID
+    assert call(ks=None) == kvx.ERR_INVALID                      # K output without K caches
+    assert call(kr=None) == kvx.ERR_INVALID
+    assert call(m=None) == kvx.ERR_INVALID
+    assert call(taps_p=None) == kvx.ERR_INVALID
+    bad = taps.copy()
+    bad[5, 2] = 36
+    assert call(taps_p=bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == kvx.ERR_INVALID
+    assert call(sd=desc(36, 50000, 8, 128, rope=1e4)) == kvx.ERR_UNSUPPORTED   # rotated keys
+    assert call(sd=desc(36, 50000, 8, 128, kvx.F32), rd=desc(32, 65536, 8, 128, kvx.F32)) == kvx.ERR_UNSUPPORTED
+    assert call(sd=desc(36, 50000, 3, 64)) == kvx.ERR_UNSUPPORTED    # sender rows not a multiple of 256
+    assert call(ks=ctypes.c_void_p(0x1008)) == kvx.ERR_UNSUPPORTED  # 16-byte pieces
+    assert call(rd=desc(32, 0, 8, 128)) == kvx.ERR_SHAPE
+    assert call(ws=16) == kvx.ERR_WORKSPACE

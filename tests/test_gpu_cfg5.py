@@ -77,7 +77,7 @@ def cal():
     tmap = kvx.align_tokens(dev_i32(send_end), dev_i32(recv_end))
     tmap_o = O.token_align(send_end, recv_end)
     assert np.array_equal(tmap.cpu().numpy(), tmap_o)
-    d = dict(send_end=send_end, recv_end=recv_end, taps=taps, tmap_o=tmap_o)
+    d = dict(send_end=send_end, recv_end=recv_end, taps=taps, tmap_o=tmap_o, tmap=tmap)
     xs, ys = [], []
     for r, role in enumerate(("k", "v")):
         d[f"{role}_send"] = synth.sender_cache(shp, seed * 100 + r, DEV)
@@ -139,6 +139,48 @@ def test_cfg5_fit_normal_equations_all_problems(cal):
             assert res <= FREIVALDS_TOL, f"problem {p}: residual {res:.3e}"
         del xd, yd
     say(f"  worst normal-equation residual over 64 problems: {worst:.3e}")
+
+
+def test_cfg5_fit_from_caches(cal):
+    """The same 64 fits by kvx_fit_ridge_caches straight from the caches (the
+    Gram from the alignment's runs): layers 0 / 15 / 31 of both roles vs the
+    oracle's fits, and every fit against its normal equations formed exactly
+    from the gathered bf16 features, as for the batched call."""
+    st = []
+    wk, wv = kvx.fit_ridge_caches(cal["k_send"], cal["v_send"], cal["k_recv"], cal["v_recv"], cal["tmap"],
+                                  cal["taps"], lambda_rel=LAM_REL, status=st)
+    torch.cuda.synchronize()
+    assert st == [kvx.OK] * 64
+    for role, w in (("k", wk), ("v", wv)):
+        for l in CHECK_LAYERS:
+            wo = cal["oracle_w"].get((role, l))
+            if wo is None:
+                x = O.features(cal[f"{role}_send"], cal["tmap_o"], cal["taps"][l])
+                y = O.as_f64(cal[f"{role}_recv"][l]).reshape(N_CAL, 1024)
+                wo = O.ridge_fit(x, y, lam_rel=LAM_REL)[0]
+                cal["oracle_w"][(role, l)] = wo
+                del x, y
+            err = O.rel_err(w[l].cpu().numpy().astype(np.float64), wo)
+            say(f"  from caches, {role} layer {l}: W max|err|/RMS = {err:.3e}")
+            assert err <= TOL_BF16
+    rng = np.random.default_rng(56)
+    worst = 0.0
+    for p in range(64):
+        xd = cal["xs"][p].double()
+        yd = cal["ys"][p].double()
+        lam = LAM_REL * float((xd * xd).sum()) / 3072
+        w = (wk if p < 32 else wv)[p % 32].double()
+        for _ in range(3):
+            r = torch.as_tensor(rng.standard_normal(1024), device=DEV)
+            wr = w @ r
+            res = float(torch.linalg.norm(xd.T @ (xd @ wr) + lam * wr - xd.T @ (yd @ r)) /
+                        torch.linalg.norm(xd.T @ (yd @ r)))
+            worst = max(worst, res)
+            assert res <= FREIVALDS_TOL, f"problem {p}: residual {res:.3e}"
+        del xd, yd
+    say(f"  from caches: worst normal-equation residual over 64 problems: {worst:.3e}")
+    del wk, wv
+    torch.cuda.empty_cache()
 
 
 def test_cfg5_translate_fresh_cache_with_fitted_maps(cal):

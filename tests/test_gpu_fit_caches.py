@@ -1,0 +1,144 @@
+"""kvx_fit_ridge_caches through the C-ABI: the ridge maps of every receiver
+layer and role straight from the calibration caches ("Cross-Model KV Cache
+Transfer in Production", The Closed-Form Ridge Mapping Pipeline, stage 2:
+W = (X^T X + lambda I)^-1 X^T Y per layer pair; stage 3: the layer map).
+
+The oracle fits on the gathered features of each receiver layer (the plain
+definition, 65536-row duplicates and all); the library forms X^T X from the
+alignment's runs (bit groups of the run lengths, exact doublings) and X^T Y
+from run sums of the targets.  Checks, every element of every map:
+* a two-head setting (6 -> 4 layers, taps -2/0/+2, 4096 receiver tokens of
+  the synthetic string) vs the oracle, and vs kvx_fit_ridge_batched on the
+  gathered features;
+* a token map with one run of 33000 tokens (past 2^15: the top bit group
+  repeats a run) followed by 2000 short runs, a revisited sender token and a
+  clamped entry, vs the oracle on the clamped map;
+* one role alone (the skipped role's statuses OK);
+* zero feature columns with lambda 0 reported per problem as not positive
+  definite.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from cross_model_kv_kvx_amd import kvx, synth
+from oracle import kvx_oracle as O
+from tests.kvx_cases import TOL_BF16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+LAM_REL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_i32(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.int32), device=DEV)
+
+
+def small_setting(n_recv, seed, send_layers=6, recv_layers=4, stride=2):
+    send_end, recv_end = synth.token_ends(n_recv, seed)
+    sshape = synth.CacheShape(send_layers, len(send_end), 2, 128)
+    rshape = synth.CacheShape(recv_layers, n_recv, 2, 128)
+    d = {"taps": kvx.layer_map(send_layers, recv_layers, 3, stride),
+         "tmap": kvx.align_tokens(dev_i32(send_end), dev_i32(recv_end)),
+         "tmap_o": O.token_align(send_end, recv_end)}
+    for r, role in enumerate(("k", "v")):
+        d[f"{role}_send"] = synth.sender_cache(sshape, seed * 10 + r, DEV)
+        d[f"{role}_recv"] = synth.receiver_cache(rshape, seed * 10 + 5 + r, DEV)
+    return d
+
+
+def oracle_fit(d, role, l, src_rows, lam_rel=LAM_REL):
+    x = O.features(d[f"{role}_send"], src_rows, d["taps"][l])
+    y = O.as_f64(d[f"{role}_recv"][l]).reshape(x.shape[0], -1)
+    return O.ridge_fit(x, y, lam_rel=lam_rel)[0]
+
+
+def test_fit_caches_vs_oracle_and_features_path():
+    d = small_setting(4096, 31)
+    wk, wv = kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                                  lambda_rel=LAM_REL)
+    torch.cuda.synchronize()
+    L_R = d["taps"].shape[0]
+    for role, w in (("k", wk), ("v", wv)):
+        xs = [kvx.gather_features(d[f"{role}_send"], d["tmap"], d["taps"][l]) for l in range(L_R)]
+        ys = [d[f"{role}_recv"][l].reshape(4096, -1) for l in range(L_R)]
+        wb, _ = kvx.fit_ridge_batched(xs, ys, lambda_rel=LAM_REL)
+        for l in range(L_R):
+            wo = oracle_fit(d, role, l, d["tmap_o"])
+            got = w[l].cpu().numpy().astype(np.float64)
+            err = O.rel_err(got, wo)
+            gap = O.rel_err(got, wb[l].cpu().numpy().astype(np.float64))
+            say(f"  {role} layer {l}: max|err|/RMS vs oracle {err:.3e}, vs the features path {gap:.3e}")
+            assert err <= TOL_BF16
+            # both are fp32-accumulated solutions of one system: they agree
+            # to far better than either's bound against the oracle
+            assert gap <= 1e-3
+
+
+def test_fit_caches_long_run_and_arbitrary_map():
+    rng = np.random.default_rng(7)
+    lens = [33000] + list(rng.integers(1, 40, size=2000))
+    n = int(sum(lens))
+    n_send = len(lens) + 5
+    vals = np.arange(len(lens), dtype=np.int64)
+    vals[1200] = vals[100]                # a sender token visited by two separate runs
+    vals[-1] = n_send + 7                 # past the sender: clamped to n_send - 1
+    tmap_h = np.repeat(vals, lens).astype(np.int32)
+    clamped = np.clip(tmap_h, 0, n_send - 1)
+    sshape = synth.CacheShape(6, n_send, 2, 128)
+    rshape = synth.CacheShape(4, n, 2, 128)
+    d = {"taps": kvx.layer_map(6, 4, 3, 2)}
+    for r, role in enumerate(("k", "v")):
+        d[f"{role}_send"] = synth.sender_cache(sshape, 70 + r, DEV)
+        d[f"{role}_recv"] = synth.receiver_cache(rshape, 75 + r, DEV)
+    st = []
+    wk, wv = kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], dev_i32(tmap_h), d["taps"],
+                                  lambda_rel=LAM_REL, status=st)
+    torch.cuda.synchronize()
+    assert st == [kvx.OK] * 8
+    # receiver layers 1 and 2 (taps 0/2/4 and 1/3/5): layers 0 and 3 repeat a
+    # tap, which leaves only lambda in some directions, and beside the
+    # 33000-token run that system's condition number is near 1e6, past what
+    # fp32 sums resolve to the parity bar for any accumulation order
+    for role, w in (("k", wk), ("v", wv)):
+        for l in (1, 2):
+            wo = oracle_fit(d, role, l, clamped)
+            err = O.rel_err(w[l].cpu().numpy().astype(np.float64), wo)
+            say(f"  long run, {role} layer {l}: max|err|/RMS {err:.3e}")
+            assert err <= TOL_BF16
+
+
+def test_fit_caches_one_role_and_singular_status():
+    d = small_setting(1500, 33)
+    L_R = d["taps"].shape[0]
+    st = []
+    wk, wv = kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                                  lambda_rel=LAM_REL, roles=("v",), status=st)
+    torch.cuda.synchronize()
+    assert wk is None and st == [kvx.OK] * (2 * L_R)
+    for l in range(L_R):
+        err = O.rel_err(wv[l].cpu().numpy().astype(np.float64), oracle_fit(d, "v", l, d["tmap_o"]))
+        assert err <= TOL_BF16
+    # sender layer 0 zeroed and lambda 0: the receiver layers that tap it
+    # (layers 0 and 1 of the 6 -> 4 map) have zero feature columns, so an
+    # exact zero pivot, in both roles
+    for role in ("k", "v"):
+        d[f"{role}_send"][0].zero_()
+    assert all(0 in d["taps"][l] for l in (0, 1))
+    st = []
+    kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                         lambda_rel=0.0, status=st)
+    torch.cuda.synchronize()
+    for z in (0, 1, L_R, L_R + 1):
+        assert st[z] == kvx.ERR_NOT_SPD, st
+    assert all(v in (kvx.OK, kvx.ERR_NOT_SPD) for v in st)
+    with pytest.raises(kvx.KvxError):
+        kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                             lambda_rel=0.0)
