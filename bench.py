@@ -62,7 +62,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "flat_gemm_kernel": ["kvx_flat.hip", "kvx_common.hpp", "kvx_internal.hpp"],
     "perhead_kernel": ["kvx_perhead.hip", "kvx_common.hpp", "kvx_internal.hpp"],
+    "fit_from_caches": ["kvx_fit.hip", "kvx_fit.hpp", "kvx_align.hip", "kvx_common.hpp", "kvx_internal.hpp"],
 }
+FIT_TRACE_FILE = "fit_from_caches__calibration_64x65536__trace.md"
 TRAFFIC_FILES = {
     "flat_gemm_kernel": "flat_gemm_kernel__crossfamily_rope_32k__traffic.md",
     "perhead_kernel": "perhead_kernel__32to80_4k__traffic.md",
@@ -222,6 +224,57 @@ def trace_summary(trace_dir, bench_log):
     return out
 
 
+def fit_trace_summary(trace_dir, bench_log):
+    """Markdown summary of a rocprofv3 --kernel-trace run of ``bench.py
+    --fit-only``: the kernels of the last kvx_fit_ridge_caches call (from its
+    run compaction to its last output store), per kernel and per phase, beside
+    the same run's fit_ms."""
+    trace = sorted(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    res = json.loads(next(l for l in open(bench_log) if l.startswith("{")))
+    starts = [i for i, r in enumerate(trace) if "kvx::runs_flags_scan" in r["Kernel_Name"]]
+    seg = trace[starts[-1]:]
+    last_store = max(i for i, r in enumerate(seg) if "kvx::fit_store_kernel" in r["Kernel_Name"])
+    seg = seg[:last_store + 1]
+    span = (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e6
+    per = {}
+    for r in seg:
+        name = r["Kernel_Name"].split("(")[0].removeprefix("void ")
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        c, t = per.get(name, (0, 0.0))
+        per[name] = (c + 1, t + d)
+
+    def phase(name):
+        if any(k in name for k in ("gram_runs", "fitc_gather", "fitc_target", "runs_")):
+            return "Gram from the runs (gathers, run sums, Gram)"
+        if any(k in name for k in ("dgemm", "potrf", "copy_f64", "fill_f64", "place_linv", "lambda")):
+            return "fp64 solve (lambda, Cholesky, two triangular solves)"
+        return "other (outputs, flags)"
+
+    phases = {}
+    for name, (c, t) in per.items():
+        phases[phase(name)] = phases.get(phase(name), 0.0) + t
+    busy = sum(t for _, t in per.values())
+    rows = "\n".join(f"| {n[:60]} | {c} | {t:.2f} | {1e3 * t / c:.1f} |"
+                     for n, (c, t) in sorted(per.items(), key=lambda kv: -kv[1][1]))
+    prow = "\n".join(f"| {k} | {v:.2f} |" for k, v in sorted(phases.items(), key=lambda kv: -kv[1]))
+    fit = res["also_fit"]
+    return (f"# Kernel trace: fit from the calibration caches (kvx_fit_ridge_caches)\n\n"
+            f"source hash: `{source_hash('fit_from_caches')}`\n\n"
+            "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths relative to the "
+            "repository), then this summary:\n\n```\n"
+            "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/fit_trace -o trace --output-format csv "
+            "-- python3 bench.py --fit-only > gpurun_out/prof/fit_trace.log\n"
+            "python3 bench.py --fit-trace-summary gpurun_out/prof/fit_trace gpurun_out/prof/fit_trace.log\n"
+            "```\n\n"
+            f"Workload: {fit['workload']}.\n\n"
+            f"Last timed call: {len(seg)} dispatches, {span:.2f} ms from its first to its last kernel, "
+            f"{busy:.2f} ms of kernel time.  Same run, bench.py's host clock around the call: "
+            f"{fit['fit_ms']:.2f} ms (mean of the timed calls).\n\n"
+            "| phase | ms |\n|---|---|\n" + prow + "\n\n"
+            "| kernel | calls | total ms | mean us |\n|---|---|---|---|\n" + rows + "\n")
+
+
 UNITS_FILES = {
     "flat_gemm_kernel": "flat_gemm_kernel__crossfamily_rope_32k__units.md",
     "perhead_kernel": "perhead_kernel__32to80_4k__units.md",
@@ -316,6 +369,53 @@ def measured_peaks(dev):
             "hbm_fill_GBs": gib4 / (ms_f * 1e-3) / 1e9, "mfma_bf16_TFLOPs": fl / (ms_m * 1e-3) / 1e12,
             "note": "copy = 2 GiB read + 2 GiB written per launch; read and fill over 4 GiB; matrix cores: "
                     "4 independent 32x32x16 bf16 chains per wave, 8 waves per compute unit, ~100 ms"}
+
+
+def library_gemm(dev, rows):
+    """What the vendor library's dense bf16 products reach on this machine, as
+    torch.matmul runs them (hipBLASLt): one 8192 x 8192 x 8192 product, and
+    the headline's 64 products without its gather, epilogue or rotation (rows
+    x 3072 by 3072 x 1024, one map each, 1024 outputs per row instead of the
+    translation's expansion to every receiver row), timed with events on the
+    current stream.  A reference for an achievable GEMM rate here; nothing of
+    the translation runs through it."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+
+    def timed(fn, iters):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    a = torch.randn((8192, 8192), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    ms_sq = timed(lambda: torch.matmul(a, b, out=c), 10)
+    del a, b, c
+    x = torch.randn((rows, 3072), generator=g, device=dev).to(torch.bfloat16)
+    ws = [torch.randn((3072, 1024), generator=g, device=dev).to(torch.bfloat16).contiguous() for _ in range(64)]
+    y = torch.empty((rows, 1024), dtype=torch.bfloat16, device=dev)
+
+    def shapes():
+        for w in ws:
+            torch.matmul(x, w, out=y)
+
+    ms_sh = timed(shapes, 5)
+    del x, ws, y
+    torch.cuda.empty_cache()
+    return {"library_gemm_8192_TFLOPs": 2.0 * 8192 ** 3 / (ms_sq * 1e-3) / 1e12,
+            "headline_shapes_library_ms": ms_sh,
+            "headline_shapes_library_TFLOPs": 64 * 2.0 * rows * 3072 * 1024 / (ms_sh * 1e-3) / 1e12,
+            "library_note": "torch.matmul (hipBLASLt) on contiguous bf16 operands: 8192^3, and 64 products of "
+                            f"{rows} x 3072 by 3072 x 1024 (the headline's distinct rows and maps, no gather, no "
+                            "epilogue) timed back to back"}
 
 
 def flat_inputs(dev):
@@ -734,12 +834,19 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
     ap.add_argument("--units-summary", nargs=2, metavar=("COUNTER_CSV", "BENCH_LOG"))
+    ap.add_argument("--fit-trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
     ap.add_argument("--fp8-only", action="store_true", help="measure the fp8-map translation alone")
     ap.add_argument("--fit-only", action="store_true",
                     help="measure the ridge and Recolor fits of the calibration setting alone")
     ap.add_argument("--perhead-only", action="store_true",
                     help="measure the per-head workload alone (profiling runs of the per-head kernel)")
     args = ap.parse_args()
+    if args.fit_trace_summary:
+        path = os.path.join(PROFILES, FIT_TRACE_FILE)
+        with open(path, "w") as fh:
+            fh.write(fit_trace_summary(*args.fit_trace_summary))
+        print(f"wrote {path}")
+        return
     if args.pmc_summary or args.trace_summary or args.units_summary:
         if args.pmc_summary:
             made, files = pmc_summary(*args.pmc_summary), TRAFFIC_FILES
@@ -852,8 +959,12 @@ def main():
                      "traffic_over_algorithmic": None if traffic is None else traffic / bytes_alg,
                      "prep_ms": prep_ms},
     }
+    log("bench: library GEMM reference")
+    peaks.update(library_gemm(dev, U))
     res["measured_peaks"] = peaks
     res["roofline"]["frac_of_measured_peak"] = achieved / peaks["mfma_bf16_TFLOPs"]
+    res["roofline"]["frac_of_library_gemm_8192"] = achieved / peaks["library_gemm_8192_TFLOPs"]
+    res["roofline"]["library_same_shapes_ms"] = peaks["headline_shapes_library_ms"]
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(x)
