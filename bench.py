@@ -227,13 +227,16 @@ def trace_summary(trace_dir, bench_log):
 def fit_trace_summary(trace_dir, bench_log):
     """Markdown summary of a rocprofv3 --kernel-trace run of ``bench.py
     --fit-only``: the kernels of the last kvx_fit_ridge_caches call (from its
-    run compaction to its last output store), per kernel and per phase, beside
-    the same run's fit_ms."""
+    run compaction to its last output store, before the Recolor fit's first
+    Gram), per kernel and per phase, beside the same run's fit_ms."""
     trace = sorted(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))),
                    key=lambda r: int(r["Start_Timestamp"]))
     res = json.loads(next(l for l in open(bench_log) if l.startswith("{")))
     starts = [i for i, r in enumerate(trace) if "kvx::runs_flags_scan" in r["Kernel_Name"]]
     seg = trace[starts[-1]:]
+    # the call ends before the next fit's Gram (Recolor follows in this run)
+    nxt = [i for i, r in enumerate(seg) if "kvx::gram_kernel" in r["Kernel_Name"]]
+    seg = seg[:nxt[0]] if nxt else seg
     last_store = max(i for i, r in enumerate(seg) if "kvx::fit_store_kernel" in r["Kernel_Name"])
     seg = seg[:last_store + 1]
     span = (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e6
