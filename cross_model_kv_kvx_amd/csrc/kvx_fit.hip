@@ -24,6 +24,8 @@
 // pivot sets the problem's device flag; the host reads the flags once.
 
 #include <algorithm>
+#include <array>
+#include <map>
 #include <vector>
 
 #include "kvx_fit.hpp"
@@ -302,15 +304,31 @@ gram_kernel(const GramArgs g) {
 // X^T Y = sum_u x_u s_u^T with s_u the run's target sum, taken as a high and
 // a low bf16 part: the distinct rows x_u are read twice, once against the
 // high parts and once against the low parts.
-// A launch covers every problem (receiver layer) of one role: items are
-// (problem, tile) with the full row range each, so no split partials are
-// kept; each item writes its fp64 tile of C or of G's lower triangle (tiles
-// on and below the diagonal; the Cholesky factorisation, the solves and the
-// trace read nothing else, so the upper triangle off the diagonal tiles is
-// left unwritten).
+// A launch covers every problem (receiver layer) of one role, with the full
+// row range per item, so no split partials are kept.  Items are the distinct
+// lower tiles of G over all problems (receiver layers whose taps pair the
+// same sender layers at the same offsets share a tile: formed once, written
+// to each) and the (problem, tile) items of C.  G is written on and below
+// the diagonal tiles only: the Cholesky factorisation, the solves and the
+// trace read nothing else.
 constexpr int GRR_BLOCK = 5;                    // steps per unrolled block of the K loop
 constexpr int GRR_PAD = GRR_BLOCK * GR_BK;      // rows of each bit group padded to whole blocks
 constexpr int GRR_MAX_GROUPS = 16;
+
+// One distinct lower tile of G: sender layer and row offset of its row side
+// (a) and column side (b), and its consumers dests[first .. first + count).
+// Receiver layers whose taps pair the same sender layers at the same offsets
+// share the tile: it is formed once and written to each of them.
+struct GrrKey {
+  int32_t la, oa, lb, ob, first, count, pad0, pad1;
+};
+// A consumer: problem, tile position (bi, bj) in its G, and whether it takes
+// the tile transposed (its row side is the key's b side).
+struct GrrDest {
+  int32_t prob, bi, bj, trans;
+};
+typedef const __attribute__((address_space(4))) GrrKey* grr_key_ptr;
+typedef const __attribute__((address_space(4))) GrrDest* grr_dest_ptr;
 
 struct GramRunsArgs {
   const uint16_t* xg;       // [L_S][xg_rows][row]: the bit-group rows of every sender layer
@@ -321,6 +339,9 @@ struct GramRunsArgs {
   double* G;                // problem p's G (f_in x f_in) and C (f_in x f_out) at p * bs
   double* C;
   int64_t bs;
+  const GrrKey* keys;       // [n_keys] distinct G tiles (read as uniform scalar loads)
+  const GrrDest* dests;     // their consumers
+  int32_t n_keys;
   int32_t row, xg_rows, u_pad, n_taps, n_problems;
   int32_t f_in, f_out, nbi, nbc, n_g, n_c;
   int32_t n_groups;
@@ -346,42 +367,31 @@ gram_runs_kernel(const GramRunsArgs g) {
   __shared__ __attribute__((aligned(1024))) uint16_t p4[GR_PART];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;
-  const int32_t per = g.n_g + g.n_c;
-  const int64_t T = static_cast<int64_t>(g.n_problems) * per;
+  // items: the distinct G tiles, then (problem, C tile)
+  const int64_t T = g.n_keys + static_cast<int64_t>(g.n_problems) * g.n_c;
   const int32_t NG = gridDim.x;
   const int32_t slot = (NG % 8 == 0) ? (blockIdx.x & 7) * (NG >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   const uint32_t xpitch = static_cast<uint32_t>(2 * g.row);
+  const grr_key_ptr keys = (grr_key_ptr)(g.keys);  // constant address space: scalar loads
+  const grr_dest_ptr dests = (grr_dest_ptr)(g.dests);
 
   for (int64_t t = slot; t < T; t += NG) {
-    const int32_t prob = static_cast<int32_t>(t / per);
-    int32_t tt = static_cast<int32_t>(t % per);
-    int32_t bi, bj;
-    bool is_c;
-    if (tt < g.n_g) {
-      is_c = false;
-      bi = 0;
-      int32_t rowlen = g.nbi;
-      while (tt >= rowlen) {
-        tt -= rowlen;
-        ++bi;
-        --rowlen;
-      }
-      bj = bi + tt;
-      // the lower tile (bj, bi): every reader of G takes the lower triangle
-      // (and whole diagonal tiles), so each tile is stored once, in rows
-      const int32_t sw = bi;
-      bi = bj;
-      bj = sw;
+    const bool is_c = t >= g.n_keys;
+    int32_t prob = 0, bi = 0, bj = 0, tap_i, off_i, key = 0;
+    if (is_c) {
+      const int32_t tt = static_cast<int32_t>(t - g.n_keys);
+      prob = tt / g.n_c;
+      bi = (tt % g.n_c) / g.nbc;
+      bj = (tt % g.n_c) % g.nbc;
+      // feature tile bi lies inside one tap's row (row is a multiple of 256)
+      tap_i = g.taps[static_cast<int64_t>(prob) * g.n_taps + bi * GR_T / g.row];
+      off_i = bi * GR_T % g.row;
     } else {
-      is_c = true;
-      tt -= g.n_g;
-      bi = tt / g.nbc;
-      bj = tt % g.nbc;
+      key = static_cast<int32_t>(t);
+      tap_i = keys[key].la;
+      off_i = keys[key].oa;
     }
-    const int32_t i0 = bi * GR_T, j0 = bj * GR_T;
-    // feature tile bi lies inside one tap's row (row is a multiple of 256)
-    const int32_t tap_i = g.taps[static_cast<int64_t>(prob) * g.n_taps + i0 / g.row];
-    const int32_t off_i = i0 % g.row;
+    const int32_t j0 = bj * GR_T;
 
     GrItem it;
     it.p_pitch = xpitch;
@@ -394,8 +404,8 @@ gram_runs_kernel(const GramRunsArgs g) {
       it.p_wrap = g.u_pad / GR_BK;
       it.nk = 2 * it.p_wrap;
     } else {
-      const int32_t tap_j = g.taps[static_cast<int64_t>(prob) * g.n_taps + j0 / g.row];
-      const int32_t off_j = j0 % g.row;
+      const int32_t tap_j = keys[key].lb;
+      const int32_t off_j = keys[key].ob;
       const uint16_t* pb = g.xg + tap_i * g.xg_layer + off_i;
       const uint16_t* qb = g.xg + tap_j * g.xg_layer + off_j;
       it.pr = buf_rsrc(pb, static_cast<uint32_t>(static_cast<int64_t>(g.xg_rows) * xpitch - 2 * off_i));
@@ -463,23 +473,44 @@ gram_runs_kernel(const GramRunsArgs g) {
       KVX_WAIT_VM(0);
     }
 
-    double* G = g.G + prob * g.bs;
-    double* C = g.C + prob * g.bs;
+    // tile-local row (P side) and column (Q side) of accumulator element
+    // (mi, ni, r) of this lane
+    auto lrow = [&](int mi, int r) { return wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
+    auto lcol = [&](int ni) { return wn * 128 + ni * 32 + (lane & 31); };
+    if (is_c) {
+      double* C = g.C + prob * g.bs;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t i = i0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int32_t j = j0 + wn * 128 + ni * 32 + (lane & 31);
-          const double v = static_cast<double>(acc[mi][ni][r]);
-          if (is_c) {
-            if (i < g.f_in && j < g.f_out) C[static_cast<int64_t>(i) * g.f_out + j] = v;
-          } else if (i < g.f_in && j < g.f_in) {
-            G[static_cast<int64_t>(i) * g.f_in + j] = v;
+          for (int r = 0; r < 16; ++r) {
+            const int32_t i = bi * GR_T + lrow(mi, r), j = j0 + lcol(ni);
+            if (i < g.f_in && j < g.f_out) C[static_cast<int64_t>(i) * g.f_out + j] = static_cast<double>(acc[mi][ni][r]);
           }
-        }
+    } else {
+      const int32_t first = keys[key].first, count = keys[key].count;
+      for (int32_t d = 0; d < count; ++d) {
+        const int32_t dp = dests[first + d].prob, dbi = dests[first + d].bi, dbj = dests[first + d].bj;
+        const bool tr = dests[first + d].trans != 0;
+        double* G = g.G + dp * g.bs;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              // not transposed: the tile's rows are the consumer's rows
+              const int32_t i = dbi * GR_T + (tr ? lcol(ni) : lrow(mi, r));
+              const int32_t j = dbj * GR_T + (tr ? lrow(mi, r) : lcol(ni));
+              // converted per store: hoisted out of the consumer loop, the
+              // 128 fp64 values would not fit the registers
+              float a = acc[mi][ni][r];
+              asm volatile("" : "+v"(a));
+              G[static_cast<int64_t>(i) * g.f_in + j] = static_cast<double>(a);
+            }
+      }
+    }
     __syncthreads();
   }
 }
@@ -1462,6 +1493,8 @@ struct FitcWs {
   void* runs_scratch;
   int32_t* glist;
   int32_t* taps;
+  GrrKey* keys;        // distinct lower G tiles (at most one per problem and tile)
+  GrrDest* dests;      // their consumers (one per problem and tile)
   uint16_t* xu;
   uint16_t* xg;
   uint16_t* qp;
@@ -1486,6 +1519,9 @@ static FitcWs fitc_layout(const FitcShape& sh, void* base) {
   w.g_cap = ceil_div(static_cast<int64_t>(n) + static_cast<int64_t>(GRR_MAX_GROUPS) * GRR_PAD, GRR_PAD) * GRR_PAD;
   w.glist = c.take<int32_t>(static_cast<size_t>(w.g_cap));
   w.taps = c.take<int32_t>(static_cast<size_t>(sh.recv_layers) * sh.n_taps);
+  const int64_t nb = ceil_div(sh.f_in, GR_T);
+  w.keys = c.take<GrrKey>(static_cast<size_t>(sh.recv_layers) * (nb * (nb + 1) / 2));
+  w.dests = c.take<GrrDest>(static_cast<size_t>(sh.recv_layers) * (nb * (nb + 1) / 2));
   w.xu = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.u_cap * sh.row);
   w.xg = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.g_cap * sh.row);
   w.qp = c.take<uint16_t>(static_cast<size_t>(sh.recv_layers) * 2 * w.u_cap * sh.f_out);
@@ -1520,6 +1556,34 @@ static void fitc_groups(const std::vector<int32_t>& rb, int32_t n_runs, std::vec
     g.grp_exp[g.n_groups] = j;
     g.grp_end[g.n_groups] = static_cast<int32_t>(list.size() / GRR_PAD);
     ++g.n_groups;
+  }
+}
+
+// The distinct lower tiles of G over all problems of a role: tile (bi, bj),
+// bi >= bj, of receiver layer l pairs sender layer taps[l][bi 256 / row] at
+// row offset bi 256 mod row with the same for bj; keys ordered by (layers,
+// offsets) with the larger (layer, offset) on the row side, so consecutive
+// items share their row panel.
+static void fitc_keys(const FitcShape& sh, const int32_t* taps, std::vector<GrrKey>& keys,
+                      std::vector<GrrDest>& dests) {
+  const int32_t nb = static_cast<int32_t>(ceil_div(sh.f_in, GR_T));
+  std::map<std::array<int32_t, 4>, std::vector<GrrDest>> m;
+  for (int32_t l = 0; l < sh.recv_layers; ++l)
+    for (int32_t bi = 0; bi < nb; ++bi)
+      for (int32_t bj = 0; bj <= bi; ++bj) {
+        const std::array<int32_t, 2> a{taps[l * sh.n_taps + bi * GR_T / sh.row], bi * GR_T % sh.row};
+        const std::array<int32_t, 2> b{taps[l * sh.n_taps + bj * GR_T / sh.row], bj * GR_T % sh.row};
+        if (a >= b)
+          m[{a[0], a[1], b[0], b[1]}].push_back(GrrDest{l, bi, bj, 0});
+        else
+          m[{b[0], b[1], a[0], a[1]}].push_back(GrrDest{l, bi, bj, 1});
+      }
+  keys.clear();
+  dests.clear();
+  for (const auto& kv : m) {
+    keys.push_back(GrrKey{kv.first[0], kv.first[1], kv.first[2], kv.first[3], static_cast<int32_t>(dests.size()),
+                          static_cast<int32_t>(kv.second.size()), 0, 0});
+    dests.insert(dests.end(), kv.second.begin(), kv.second.end());
   }
 }
 
@@ -1567,6 +1631,14 @@ int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const v
   g.bs = bs;
   KVX_HIP_TRY(hipMemcpyAsync(w.taps, taps_host, sizeof(int32_t) * sh.recv_layers * sh.n_taps, hipMemcpyHostToDevice,
                              s));
+  std::vector<GrrKey> keys;
+  std::vector<GrrDest> dests;
+  fitc_keys(sh, taps_host, keys, dests);
+  KVX_HIP_TRY(hipMemcpyAsync(w.keys, keys.data(), sizeof(GrrKey) * keys.size(), hipMemcpyHostToDevice, s));
+  KVX_HIP_TRY(hipMemcpyAsync(w.dests, dests.data(), sizeof(GrrDest) * dests.size(), hipMemcpyHostToDevice, s));
+  g.keys = w.keys;
+  g.dests = w.dests;
+  g.n_keys = static_cast<int32_t>(keys.size());
 
   // 2. per role: the distinct rows and the bit-group rows of every sender
   // layer, the run sums of the targets, then the Gram of all its problems
@@ -1591,7 +1663,7 @@ int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const v
     GramRunsArgs gr = g;
     gr.G = w.fit.G + static_cast<int64_t>(r) * sh.recv_layers * bs;
     gr.C = w.fit.C + static_cast<int64_t>(r) * sh.recv_layers * bs;
-    const int64_t items = static_cast<int64_t>(sh.recv_layers) * (g.n_g + g.n_c);
+    const int64_t items = g.n_keys + static_cast<int64_t>(sh.recv_layers) * g.n_c;
     gram_runs_kernel<<<static_cast<unsigned>(items < cus ? items : cus), GR_THREADS, 0, s>>>(gr);
     KVX_LAUNCH_CHECK();
   }
