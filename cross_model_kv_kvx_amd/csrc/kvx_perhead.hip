@@ -14,7 +14,8 @@ namespace kvx {
 
 // ---------------------------------------------------------------- bf16 caches, d = 128
 // One workgroup per (role, receiver layer l, head h, span of up to 4096
-// receiver tokens) with two kinds of waves:
+// receiver tokens; shorter spans where that fills the last round of
+// workgroups) with two kinds of waves:
 //   * compute waves 0..7, two per SIMD.  Wave w owns the 32 outputs
 //     16s .. 16s+15 and 64+16s .. 64+16s+15 of the head (s = w mod 4), so the
 //     two members (c, c+64) of every rotary pair sit in one lane
@@ -48,15 +49,14 @@ namespace kvx {
 // receiver rows, run side by side, and the neighbouring receiver layers that
 // share a sender layer read its rows through one L2.
 constexpr int PH_TILE = 64;                      // tokens per tile
-constexpr int PH_SPAN = 4096;                    // tokens per workgroup
+constexpr int PH_SPAN = 4096;                    // tokens per workgroup at most
+constexpr int PH_MIN_SPAN = 1024;                // shortest span chosen to fill a round of workgroups
 constexpr int PH_TILE_ELEMS = PH_TILE * 128;     // 16-bit elements of a tile (16 KB)
 constexpr int PH_RING = 6;                       // LDS stages of sender tiles
 constexpr int PH_LOADERS = 4;                    // compute waves 0..3 issue the tile loads
-// NTB = 64-token tile halves (32-token blocks) per compute wave: 1 with eight
-// compute waves (two per SIMD), 2 with four (one per SIMD, each taking the
-// whole tile: rotating roles with fp32 maps, whose rotation state and map
-// halves do not fit in the registers of three waves per SIMD); plus 4 store
-// waves.
+// NTB = 64-token tile halves (32-token blocks) per compute wave: with NTB = 1
+// (every launch) eight compute waves, two per SIMD, each take one half; NTB =
+// 2 would give four compute waves, each the whole tile.  Plus 4 store waves.
 template <int NTB>
 struct PhShape {
   static constexpr int compute = 8 / NTB;
@@ -77,7 +77,7 @@ struct HeadKArgs {
   int64_t pool_rows;        // output rows per layer
   const int32_t* recv_pos;  // rotary position of each receiver token, or null (i)
   int32_t pos_limit;
-  int32_t recv_layers, recv_tokens, heads, n_span, n_blocks, xcd_remap;
+  int32_t recv_layers, recv_tokens, heads, n_span, span_len, n_blocks, xcd_remap;
   uint8_t tap[MAX_LAYERS];  // sender layer of each receiver layer
 };
 
@@ -139,7 +139,8 @@ __device__ __forceinline__ f32x16 ph_mfma(const u32x4& w, const u32x4& x, const 
 // for its 8 pairs, and the step (cos, sin)(64 t) per tile.
 template <int NTB>
 struct PhRot {
-  float cs[NTB][8], sn[NTB][8], c64[8], s64[8];
+  float cs[NTB][8], sn[NTB][8];
+  const float* step;  // LDS [2][64]: cos and sin of one tile's 64 positions for each pair
 };
 
 // Fragments of this wave's token blocks of one tile (block ti = wave / 4
@@ -148,9 +149,12 @@ struct PhRot {
 // even) into `ys` as [tok][n] with swizzled chunks.  With per-token positions
 // (`rpos`), the (cos, sin) of the lane's tokens (tile tokens from `tok0`) are
 // read from the table instead of stepped.
+// The bias comes from registers (bn) or, where registers are short (rotating
+// roles with fp32 maps), from the workgroup's 128 values in LDS (bl).
 template <bool WF32, bool F16, bool ROT, int NTB>
 __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, const u32x4 (&wh)[8],
-                                           const u32x4 (&wl)[8], const float (&bn)[16], PhRot<NTB>& rs,
+                                           const u32x4 (&wl)[8], const float (&bn)[16], const float* bl,
+                                           PhRot<NTB>& rs,
                                            const int32_t* rpos, const float2* tab, int32_t tok0, int32_t n_tok_all,
                                            int32_t pos_limit) {
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -194,7 +198,8 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
     const int ti = tb0 + j;
     float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = acc[j][r] + bn[r];
+    for (int r = 0; r < 16; ++r)
+      v[r] = acc[j][r] + (ROT && WF32 ? bl[ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : bn[r]);
     if constexpr (ROT) {
       if (rpos) {
         int32_t pp = rpos[min(tok0 + 32 * ti + (lane & 31), n_tok_all - 1)];
@@ -212,8 +217,10 @@ __device__ __forceinline__ void ph_compute(const uint16_t* xs, uint16_t* ys, con
           const float a = v[r], b = v[r + 8];
           v[r] = a * rs.cs[j][r] - b * rs.sn[j][r];
           v[r + 8] = a * rs.sn[j][r] + b * rs.cs[j][r];
-          const float cn = rs.cs[j][r] * rs.c64[r] - rs.sn[j][r] * rs.s64[r];
-          rs.sn[j][r] = rs.sn[j][r] * rs.c64[r] + rs.cs[j][r] * rs.s64[r];
+          const int pr = ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));
+          const float c64 = rs.step[pr], s64 = rs.step[64 + pr];
+          const float cn = rs.cs[j][r] * c64 - rs.sn[j][r] * s64;
+          rs.sn[j][r] = rs.sn[j][r] * c64 + rs.cs[j][r] * s64;
           rs.cs[j][r] = cn;
         }
       }
@@ -275,6 +282,8 @@ perhead_kernel(const HeadKArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t y0[PH_TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t y1[PH_TILE_ELEMS];
   __shared__ int32_t msm[PH_SPAN];
+  __shared__ float rot_step[2][64];
+  __shared__ float bias_l[128];
 
   int32_t b = blockIdx.x;
   if (a.xcd_remap) b = (b & 7) * (a.n_blocks >> 3) + (b >> 3);
@@ -290,8 +299,8 @@ perhead_kernel(const HeadKArgs a) {
   const int32_t x_rows = a.x_rows[role];
 
   PhTile pt;
-  pt.t0 = span * PH_SPAN;
-  pt.n_tok = min(PH_SPAN, a.recv_tokens - pt.t0);
+  pt.t0 = span * a.span_len;
+  pt.n_tok = min(a.span_len, a.recv_tokens - pt.t0);
   pt.n_tiles = (pt.n_tok + PH_TILE - 1) / PH_TILE;
   pt.msm = msm;
   pt.row_bytes = static_cast<uint32_t>(2 * row_elems);
@@ -305,6 +314,17 @@ perhead_kernel(const HeadKArgs a) {
   for (int i = threadIdx.x; i < PH_SPAN; i += NT) {
     int32_t v = row_of[pt.t0 + min(i, pt.n_tok - 1)];
     msm[i] = v < 0 ? 0 : (v >= x_rows ? x_rows - 1 : v);
+  }
+  if (ROT && WF32 && threadIdx.x < 128) {
+    const float* bias = a.bias[role];
+    bias_l[threadIdx.x] = bias ? bias[static_cast<int64_t>(l) * row_elems + h * 128 + threadIdx.x] : 0.0f;
+  }
+  // the rotation's step by one tile (64 positions) of each pair; the table
+  // holds position 64 whenever a span has more than one tile
+  if (ROT && !a.recv_pos && threadIdx.x < 64) {
+    const float2 t64 = pt.n_tiles > 1 ? a.tab_recv[64 * 64 + threadIdx.x] : float2{1.0f, 0.0f};
+    rot_step[0][threadIdx.x] = t64.x;
+    rot_step[1][threadIdx.x] = t64.y;
   }
   __syncthreads();
 
@@ -339,18 +359,20 @@ perhead_kernel(const HeadKArgs a) {
         rs.cs[j][r] = t.x;
         rs.sn[j][r] = t.y;
       }
-      // the table holds position 64 whenever a span has more than one tile
-      const float2 t64 = pt.n_tiles > 1 ? a.tab_recv[64 * 64 + pr] : float2{1.0f, 0.0f};
-      rs.c64[r] = t64.x;
-      rs.s64[r] = t64.y;
     }
   }
+  rs.step = &rot_step[0][0];
 
   float bn[16];
   const float* bias = a.bias[role] ? a.bias[role] + static_cast<int64_t>(l) * row_elems + h * 128 : nullptr;
+  if constexpr (ROT && WF32) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    bn[r] = bias ? bias[ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
+    for (int r = 0; r < 16; ++r) bn[r] = 0.0f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      bn[r] = bias ? bias[ph_out(sw, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3))] : 0.0f;
+  }
 
   // A fragments: rows n = ph_out(s, lane % 32) of W_{l,h}, prepared
   // output-major in the operand type: [n][c] (16-bit maps) or [n][hi c | lo c]
@@ -401,7 +423,7 @@ perhead_kernel(const HeadKArgs a) {
       rr = ph_rows(pt, (K) + PH_RING);                                         \
     }                                                                          \
     if ((K) < pt.n_tiles)                                                      \
-      ph_compute<WF32, F16, ROT, NTB>(XS, YS, wh, wl, bn, rs, rpos, a.tab_recv, \
+      ph_compute<WF32, F16, ROT, NTB>(XS, YS, wh, wl, bn, bias_l, rs, rpos, a.tab_recv, \
                             pt.t0 + (K) * PH_TILE, a.recv_tokens, a.pos_limit); \
   }
   for (int32_t k = 0; k < pt.n_tiles; k += 6) {
@@ -424,11 +446,10 @@ perhead_kernel(const HeadKArgs a) {
 
 template <bool WF32, bool F16, bool ROT>
 static void ph_launch(unsigned g, const HeadKArgs& a, hipStream_t s) {
-  // eight compute waves (two per SIMD, each a 32-token half of every tile),
-  // except for rotating roles with fp32 maps: their rotation state and both
-  // map halves do not fit in the registers of three waves per SIMD, so four
-  // compute waves hold both halves
-  constexpr int NTB = (ROT && WF32) ? 2 : 1;
+  // eight compute waves (two per SIMD, each a 32-token half of every tile);
+  // rotating roles with fp32 maps read their bias and the rotation's step
+  // from LDS so they fit the registers of three waves per SIMD
+  constexpr int NTB = 1;
   perhead_kernel<WF32, F16, ROT, NTB><<<g, PhShape<NTB>::threads, 0, s>>>(a);
 }
 
@@ -463,9 +484,29 @@ int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hip
     a.recv_layers = p.recv_layers;
     a.recv_tokens = p.recv_tokens;
     a.heads = p.heads;
-    a.n_span = static_cast<int32_t>(ceil_div(p.recv_tokens, PH_SPAN));
+    // spans of up to PH_SPAN tokens; more (shorter, at least PH_MIN_SPAN)
+    // spans when that fills the last round of workgroups clearly better (one
+    // role per launch leaves half a round idle where two roles fill it)
+    const int64_t per_span = static_cast<int64_t>(n) * p.heads * p.recv_layers;
+    const int cus = device_cu_count();
+    auto fill = [&](int64_t items) {
+      return static_cast<double>(items) / static_cast<double>(ceil_div(items, cus) * cus);
+    };
+    int32_t span_len = PH_SPAN;
+    double best = fill(per_span * ceil_div(p.recv_tokens, PH_SPAN));
+    for (int64_t ns = ceil_div(p.recv_tokens, PH_SPAN) + 1;; ++ns) {
+      const int32_t len = static_cast<int32_t>(ceil_div(ceil_div(p.recv_tokens, ns), PH_TILE) * PH_TILE);
+      if (len < PH_MIN_SPAN) break;
+      const double f = fill(per_span * ceil_div(p.recv_tokens, len));
+      if (f > best + 0.05) {
+        best = f;
+        span_len = len;
+      }
+    }
+    a.span_len = span_len;
+    a.n_span = static_cast<int32_t>(ceil_div(p.recv_tokens, span_len));
     for (int l = 0; l < p.recv_layers; ++l) a.tap[l] = static_cast<uint8_t>(p.taps[l]);
-    const int64_t nb = static_cast<int64_t>(n) * p.heads * a.n_span * p.recv_layers;
+    const int64_t nb = per_span * a.n_span;
     if (nb >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
     a.n_blocks = static_cast<int32_t>(nb);
     a.xcd_remap = (nb % 8 == 0) ? 1 : 0;
