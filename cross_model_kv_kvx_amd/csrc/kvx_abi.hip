@@ -766,6 +766,31 @@ static bool fitc_shape(const kvx_cache_desc* send, const kvx_cache_desc* recv, i
   return true;
 }
 
+// Arguments shared by the two fits from the caches: KVX_OK when they describe
+// one (the caller checks its own outputs), else the status to return.
+static int fitc_check(const kvx_cache_desc* send, const void* k_send, const void* v_send, const kvx_cache_desc* recv,
+                      const void* k_recv, const void* v_recv, const int32_t* recv_to_send, const int32_t* taps,
+                      int32_t n_taps, bool do_k, bool do_v, FitcShape* sh) {
+  const int32_t n_roles = (do_k ? 1 : 0) + (do_v ? 1 : 0);
+  if (n_roles == 0 || !fitc_shape(send, recv, n_taps, n_roles, sh)) return KVX_ERR_INVALID;
+  if ((do_k && (!k_send || !k_recv)) || (do_v && (!v_send || !v_recv))) return KVX_ERR_INVALID;
+  if (!taps || (recv->tokens > 0 && !recv_to_send)) return KVX_ERR_INVALID;
+  for (int32_t i = 0; i < recv->layers * n_taps; ++i)
+    if (taps[i] < 0 || taps[i] >= send->layers) return KVX_ERR_INVALID;
+  if (send->dtype != KVX_BF16 || recv->dtype != KVX_BF16 || send->rope_base != 0.0 || recv->rope_base != 0.0)
+    return KVX_ERR_UNSUPPORTED;
+  if ((sh->row % 256) != 0 || (sh->f_out % 8) != 0) return KVX_ERR_UNSUPPORTED;
+  // rows are read in 16-byte pieces
+  for (const void* p : {k_send, v_send, k_recv, v_recv})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return KVX_ERR_UNSUPPORTED;
+  if (sh->f_in > KVX_MAX_FIT_FEATURES || sh->f_out > KVX_MAX_FIT_FEATURES) return KVX_ERR_UNSUPPORTED;
+  if (sh->n_recv < 1 || sh->n_send < 1) return KVX_ERR_SHAPE;
+  // the Gram's per-layer operands are addressed with 32-bit byte offsets
+  const int64_t widest = sh->row > sh->f_out ? sh->row : sh->f_out;
+  if (fitc_max_rows(*sh) * widest * 2 >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
+  return KVX_OK;
+}
+
 size_t kvx_fit_ridge_caches_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv, int32_t n_taps) {
   FitcShape sh{};
   if (!fitc_shape(send, recv, n_taps, 2, &sh) || sh.n_recv < 1) return 0;
@@ -779,24 +804,10 @@ int kvx_fit_ridge_caches(const kvx_cache_desc* send, const void* k_send, const v
                          double lambda_rel, float* w_k, float* w_v, int32_t* status, void* workspace,
                          size_t ws_bytes, void* stream) {
   FitcShape sh{};
-  const int32_t n_roles = (w_k ? 1 : 0) + (w_v ? 1 : 0);
-  if (n_roles == 0 || !fitc_shape(send, recv, n_taps, n_roles, &sh)) return KVX_ERR_INVALID;
+  if (int st = fitc_check(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, w_k != nullptr,
+                          w_v != nullptr, &sh))
+    return st;
   if (!(lambda_abs >= 0.0) || !(lambda_rel >= 0.0)) return KVX_ERR_INVALID;
-  if ((w_k && (!k_send || !k_recv)) || (w_v && (!v_send || !v_recv))) return KVX_ERR_INVALID;
-  if (!taps || (recv->tokens > 0 && !recv_to_send)) return KVX_ERR_INVALID;
-  for (int32_t i = 0; i < recv->layers * n_taps; ++i)
-    if (taps[i] < 0 || taps[i] >= send->layers) return KVX_ERR_INVALID;
-  if (send->dtype != KVX_BF16 || recv->dtype != KVX_BF16 || send->rope_base != 0.0 || recv->rope_base != 0.0)
-    return KVX_ERR_UNSUPPORTED;
-  if ((sh.row % 256) != 0 || (sh.f_out % 8) != 0) return KVX_ERR_UNSUPPORTED;
-  // rows are read in 16-byte pieces
-  for (const void* p : {k_send, v_send, k_recv, v_recv})
-    if (reinterpret_cast<uintptr_t>(p) % 16) return KVX_ERR_UNSUPPORTED;
-  if (sh.f_in > KVX_MAX_FIT_FEATURES || sh.f_out > KVX_MAX_FIT_FEATURES) return KVX_ERR_UNSUPPORTED;
-  if (sh.n_recv < 1 || sh.n_send < 1) return KVX_ERR_SHAPE;
-  // the Gram's per-layer operands are addressed with 32-bit byte offsets
-  const int64_t widest = sh.row > sh.f_out ? sh.row : sh.f_out;
-  if (fitc_max_rows(sh) * widest * 2 >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < fitc_ws_bytes(sh)) return KVX_ERR_WORKSPACE;
   const void* sends[2];
   const void* recvs[2];
@@ -817,6 +828,57 @@ int kvx_fit_ridge_caches(const kvx_cache_desc* send, const void* k_send, const v
                                    workspace, static_cast<hipStream_t>(stream));
   if (status && (st == KVX_OK || st == KVX_ERR_NOT_SPD)) {
     // [2][L_R]: a skipped role's entries are KVX_OK
+    int32_t z = 0;
+    for (int32_t role = 0; role < 2; ++role) {
+      const bool present = role == 0 ? w_k != nullptr : w_v != nullptr;
+      for (int32_t l = 0; l < recv->layers; ++l) status[role * recv->layers + l] = present ? st_roles[z++] : KVX_OK;
+    }
+  }
+  return st;
+}
+
+size_t kvx_fit_recolor_caches_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv,
+                                             int32_t n_taps) {
+  FitcShape sh{};
+  if (!fitc_shape(send, recv, n_taps, 2, &sh) || sh.n_recv < 1) return 0;
+  if (sh.f_in > KVX_MAX_FIT_FEATURES || sh.f_out > KVX_MAX_FIT_FEATURES) return 0;
+  return recolor_caches_ws_bytes(sh);
+}
+
+int kvx_fit_recolor_caches(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                           const kvx_cache_desc* recv, const void* k_recv, const void* v_recv,
+                           const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps, double rho_x,
+                           double rho_y, float* w_k, float* w_v, float* b_k, float* b_v, int32_t* status,
+                           int32_t* iters, void* workspace, size_t ws_bytes, void* stream) {
+  FitcShape sh{};
+  if (int st = fitc_check(send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps, w_k != nullptr,
+                          w_v != nullptr, &sh))
+    return st;
+  if (!(rho_x >= 0.0) || !(rho_y >= 0.0)) return KVX_ERR_INVALID;
+  if ((w_k && !b_k) || (w_v && !b_v)) return KVX_ERR_INVALID;  // the bias is always written
+  if (sh.f_in < sh.f_out) return KVX_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < recolor_caches_ws_bytes(sh)) return KVX_ERR_WORKSPACE;
+  const void* sends[2];
+  const void* recvs[2];
+  float* ws_[2];
+  float* bs_[2];
+  int32_t r = 0;
+  if (w_k) {
+    sends[r] = k_send;
+    recvs[r] = k_recv;
+    ws_[r] = w_k;
+    bs_[r++] = b_k;
+  }
+  if (w_v) {
+    sends[r] = v_send;
+    recvs[r] = v_recv;
+    ws_[r] = w_v;
+    bs_[r++] = b_v;
+  }
+  int32_t st_roles[2 * MAX_LAYERS];
+  const int st = launch_recolor_caches(sh, sends, recvs, recv_to_send, taps, rho_x, rho_y, ws_, bs_, st_roles, iters,
+                                       workspace, static_cast<hipStream_t>(stream));
+  if (status && (st == KVX_OK || st == KVX_ERR_NOT_SPD || st == KVX_ERR_NOT_CONVERGED)) {
     int32_t z = 0;
     for (int32_t role = 0; role < 2; ++role) {
       const bool present = role == 0 ? w_k != nullptr : w_v != nullptr;

@@ -1487,8 +1487,8 @@ __global__ __launch_bounds__(256) void lambda_batched_kernel(double* __restrict_
   if (threadIdx.x == 0) lam_out[blockIdx.x * bs] = lam;
 }
 
-struct FitcWs {
-  FitWs fit;
+// The Gram-from-runs part of a workspace (both fits from the caches).
+struct RunsWs {
   Runs runs;
   void* runs_scratch;
   int32_t* glist;
@@ -1498,17 +1498,14 @@ struct FitcWs {
   uint16_t* xu;
   uint16_t* xg;
   uint16_t* qp;
+  double* sigma;       // [L_S][row]: sum_u c_u x_u of every sender layer (one role)
   int64_t u_cap, g_cap;  // row capacities of xu (and half of qp) and xg
-  size_t bytes;
 };
 
 // Sized for the worst case of n_recv runs of one token: U <= n_recv, and the
 // bit-group rows sum_u popcount(c_u) <= sum_u c_u = n_recv, plus padding.
-static FitcWs fitc_layout(const FitcShape& sh, void* base) {
-  FitcWs w{};
-  w.fit = fit_layout(sh.count, sh.f_in, sh.f_out, base, false);
-  Carve c(base);
-  c.used = w.fit.bytes;
+static RunsWs runs_layout(const FitcShape& sh, Carve& c) {
+  RunsWs w{};
   const int32_t n = sh.n_recv;
   w.runs.uniq = c.take<int32_t>(n);
   w.runs.run_begin = c.take<int32_t>(static_cast<size_t>(n) + 1);
@@ -1525,6 +1522,22 @@ static FitcWs fitc_layout(const FitcShape& sh, void* base) {
   w.xu = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.u_cap * sh.row);
   w.xg = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.g_cap * sh.row);
   w.qp = c.take<uint16_t>(static_cast<size_t>(sh.recv_layers) * 2 * w.u_cap * sh.f_out);
+  w.sigma = c.take<double>(static_cast<size_t>(sh.send_layers) * sh.row);
+  return w;
+}
+
+struct FitcWs {
+  FitWs fit;
+  RunsWs r;
+  size_t bytes;
+};
+
+static FitcWs fitc_layout(const FitcShape& sh, void* base) {
+  FitcWs w{};
+  w.fit = fit_layout(sh.count, sh.f_in, sh.f_out, base, false);
+  Carve c(base);
+  c.used = w.fit.bytes;
+  w.r = runs_layout(sh, c);
   w.bytes = c.used + 256;
   return w;
 }
@@ -1533,7 +1546,7 @@ size_t fitc_ws_bytes(const FitcShape& sh) { return fitc_layout(sh, nullptr).byte
 
 int64_t fitc_max_rows(const FitcShape& sh) {
   const FitcWs w = fitc_layout(sh, nullptr);
-  return w.g_cap > 2 * w.u_cap ? w.g_cap : 2 * w.u_cap;
+  return w.r.g_cap > 2 * w.r.u_cap ? w.r.g_cap : 2 * w.r.u_cap;
 }
 
 // The bit groups of the run lengths c_u (from run_begin, host), largest bit
@@ -1587,13 +1600,41 @@ static void fitc_keys(const FitcShape& sh, const int32_t* taps, std::vector<GrrK
   }
 }
 
-int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
-                      const int32_t* map, const int32_t* taps_host, double lam_abs, double lam_rel,
-                      float* const* w_role, int32_t* status, void* ws, hipStream_t s) {
-  const FitcWs w = fitc_layout(sh, ws);
-  const int64_t bs = w.fit.bs;
-  if (int st = launch_fill_i32(w.fit.flags, sh.count, 0, s)) return st;
+// sigma[s][f] = sum over runs u of c_u x_u[s][f] for every sender layer s
+// (the column sums of the features, n times their means), fp64, four
+// partial sums over u mod 4 added in a fixed order.
+__global__ __launch_bounds__(256) void fitc_sigma_kernel(const uint16_t* __restrict__ xu, int64_t xu_layer,
+                                                         int32_t row, const int32_t* __restrict__ run_begin,
+                                                         int32_t n_runs, double* __restrict__ sigma) {
+  const int64_t sl = blockIdx.y;
+  const int32_t f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= row) return;
+  const uint16_t* col = xu + sl * xu_layer + f;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int32_t u = 0; u < n_runs; ++u)
+    acc[u & 3] += static_cast<double>(run_begin[u + 1] - run_begin[u]) *
+                  static_cast<double>(bf16_to_f32(col[static_cast<int64_t>(u) * row]));
+  sigma[sl * row + f] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
 
+// sx of problem z (receiver layer z - z0): tap t's row of sigma.
+__global__ __launch_bounds__(256) void fitc_sx_kernel(const double* __restrict__ sigma, int32_t row,
+                                                      const int32_t* __restrict__ taps, int32_t n_taps,
+                                                      double* __restrict__ sx, int64_t bs) {
+  const int32_t l = blockIdx.y;
+  const int32_t f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= n_taps * row) return;
+  sx[l * bs + f] = sigma[static_cast<int64_t>(taps[l * n_taps + f / row]) * row + f % row];
+}
+
+// The moments from the runs for every role (problems role by role, receiver
+// layer within; problem z's G and C at z * bs): the runs, their bit groups and
+// the shared tiles once, then per role the distinct and bit-group rows of
+// every sender layer, the run sums of the targets and one Gram launch.  With
+// sx non-null also each problem's feature column sums (n times the means).
+static int gram_from_runs(const FitcShape& sh, const RunsWs& w, const void* const* send_role,
+                          const void* const* recv_role, const int32_t* map, const int32_t* taps_host, double* G,
+                          double* C, double* sx, int64_t bs, hipStream_t s) {
   // 1. runs of the alignment; their lengths on the host for the bit groups
   if (int st = launch_runs(map, sh.n_recv, sh.n_send, w.runs, w.runs_scratch, s)) return st;
   int32_t n_runs = 0;
@@ -1661,12 +1702,32 @@ int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const v
         ys, static_cast<int64_t>(sh.n_recv) * sh.f_out, sh.f_out, w.runs.run_begin, n_runs, u_pad, w.qp, g.qp_layer);
     KVX_LAUNCH_CHECK();
     GramRunsArgs gr = g;
-    gr.G = w.fit.G + static_cast<int64_t>(r) * sh.recv_layers * bs;
-    gr.C = w.fit.C + static_cast<int64_t>(r) * sh.recv_layers * bs;
+    const int64_t z0 = static_cast<int64_t>(r) * sh.recv_layers;
+    gr.G = G + z0 * bs;
+    gr.C = C + z0 * bs;
     const int64_t items = g.n_keys + static_cast<int64_t>(sh.recv_layers) * g.n_c;
     gram_runs_kernel<<<static_cast<unsigned>(items < cus ? items : cus), GR_THREADS, 0, s>>>(gr);
     KVX_LAUNCH_CHECK();
+    if (sx) {
+      fitc_sigma_kernel<<<dim3(static_cast<unsigned>(ceil_div(sh.row, 256)), static_cast<unsigned>(sh.send_layers)),
+                          256, 0, s>>>(w.xu, g.xu_layer, sh.row, w.runs.run_begin, n_runs, w.sigma);
+      KVX_LAUNCH_CHECK();
+      fitc_sx_kernel<<<dim3(static_cast<unsigned>(ceil_div(sh.f_in, 256)), static_cast<unsigned>(sh.recv_layers)),
+                       256, 0, s>>>(w.sigma, sh.row, w.taps, sh.n_taps, sx + z0 * bs, bs);
+      KVX_LAUNCH_CHECK();
+    }
   }
+  return KVX_OK;
+}
+
+int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
+                      const int32_t* map, const int32_t* taps_host, double lam_abs, double lam_rel,
+                      float* const* w_role, int32_t* status, void* ws, hipStream_t s) {
+  const FitcWs w = fitc_layout(sh, ws);
+  const int64_t bs = w.fit.bs;
+  if (int st = launch_fill_i32(w.fit.flags, sh.count, 0, s)) return st;
+  if (int st = gram_from_runs(sh, w.r, send_role, recv_role, map, taps_host, w.fit.G, w.fit.C, nullptr, bs, s))
+    return st;
   lambda_batched_kernel<<<static_cast<unsigned>(sh.count), 256, 0, s>>>(w.fit.G, bs, sh.f_in, lam_abs, lam_rel,
                                                                         w.fit.lam);
   KVX_LAUNCH_CHECK();
@@ -1897,6 +1958,9 @@ size_t recolor_ws_bytes(int32_t count, int32_t f_in, int32_t f_out) {
   return recolor_layout(count, f_in, f_out, nullptr).bytes;
 }
 
+static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, double inv_n, float* const* w_out,
+                         float* const* b_out, int32_t* status, int32_t* iters, hipStream_t s);
+
 int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy,
                    int32_t in_f32, int64_t n_rows, int32_t f_in, int32_t f_out, double rho_x, double rho_y,
                    float* const* w_out, float* const* b_out, int32_t* status, int32_t* iters, void* ws,
@@ -1927,6 +1991,17 @@ int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void*
     lambda_kernel<<<1, 256, 0, s>>>(Gy, f_out, 0.0, rho_y, w.lam + z * bs + 1);
     KVX_LAUNCH_CHECK();
   }
+  return recolor_solve(w, count, f_in, f_out, inv_n, w_out, b_out, status, iters, s);
+}
+
+// Steps 2-4 of the Recolor fit from the regularised moments in w (G, C, Gy,
+// and the column sums sx, sy, n times the covariances; only G's lower
+// triangle and diagonal tiles are read): every problem of the call at once.
+static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, double inv_n, float* const* w_out,
+                         float* const* b_out, int32_t* status, int32_t* iters, hipStream_t s) {
+  const int64_t bs = w.bs;
+  const int64_t fo2 = static_cast<int64_t>(f_out) * f_out;
+  const dim3 grid_o2(grid_for(fo2 / 8 + 1), static_cast<unsigned>(count));
 
   // 2. factors and the whitened cross-covariance M = L_x^-1 C L_y^-T
   if (int st = chol_factor(s, count, w.G, f_in, bs, w.linvx, w.xinvx, w.zbuf, w.flags)) return st;
@@ -2020,6 +2095,66 @@ int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void*
     if (st != KVX_OK && result == KVX_OK) result = st;
   }
   return result;
+}
+
+// Recolor fits of every receiver layer of n_roles roles from the
+// calibration caches: the moments X^T X, X^T Y and the feature column sums
+// from the alignment's runs (gram_from_runs), Y^T Y and the target column
+// sums from each receiver layer's rows, then the solve of launch_recolor.
+struct RccWs {
+  RcWs rc;
+  RunsWs r;
+  size_t bytes;
+};
+
+static RccWs recolor_caches_layout(const FitcShape& sh, void* base) {
+  RccWs w{};
+  w.rc = recolor_layout(sh.count, sh.f_in, sh.f_out, base);
+  Carve c(base);
+  c.used = w.rc.bytes;
+  w.r = runs_layout(sh, c);
+  w.bytes = c.used + 256;
+  return w;
+}
+
+size_t recolor_caches_ws_bytes(const FitcShape& sh) { return recolor_caches_layout(sh, nullptr).bytes; }
+
+int launch_recolor_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
+                          const int32_t* map, const int32_t* taps_host, double rho_x, double rho_y,
+                          float* const* w_role, float* const* b_role, int32_t* status, int32_t* iters, void* ws,
+                          hipStream_t s) {
+  RccWs w = recolor_caches_layout(sh, ws);
+  RcWs& rc = w.rc;
+  const int64_t bs = rc.bs;
+  if (int st = launch_fill_i32(rc.flags, sh.count, 0, s)) return st;
+  if (int st = gram_from_runs(sh, w.r, send_role, recv_role, map, taps_host, rc.G, rc.C, rc.sx, bs, s)) return st;
+  const double inv_n = 1.0 / static_cast<double>(sh.n_recv);
+  const int64_t fo2 = static_cast<int64_t>(sh.f_out) * sh.f_out;
+  for (int32_t z = 0; z < sh.count; ++z) {
+    const uint16_t* y = static_cast<const uint16_t*>(recv_role[z / sh.recv_layers]) +
+                        static_cast<int64_t>(z % sh.recv_layers) * sh.n_recv * sh.f_out;
+    double* G = rc.G + z * bs;
+    double* C = rc.C + z * bs;
+    double* Gy = rc.Gy + z * bs;
+    double* sx = rc.sx + z * bs;
+    double* sy = rc.sy + z * bs;
+    if (int st = gram_one(y, sh.f_out, y, sh.f_out, 0, sh.n_recv, sh.f_out, 0, rc.part, Gy, nullptr, s)) return st;
+    if (int st = colsum(y, sh.f_out, sh.n_recv, sh.f_out, 0, rc.csp, sy, s)) return st;
+    center_kernel<<<grid_for(static_cast<int64_t>(sh.f_in) * (sh.f_in + sh.f_out)), 256, 0, s>>>(
+        G, C, sx, sy, sh.f_in, sh.f_out, inv_n);
+    center_kernel<<<grid_for(fo2), 256, 0, s>>>(Gy, nullptr, sy, sy, sh.f_out, 0, inv_n);
+    KVX_LAUNCH_CHECK();
+    lambda_kernel<<<1, 256, 0, s>>>(G, sh.f_in, 0.0, rho_x, rc.lam + z * bs);
+    lambda_kernel<<<1, 256, 0, s>>>(Gy, sh.f_out, 0.0, rho_y, rc.lam + z * bs + 1);
+    KVX_LAUNCH_CHECK();
+  }
+  std::vector<float*> w_out(static_cast<size_t>(sh.count)), b_out(static_cast<size_t>(sh.count));
+  const int64_t nw = static_cast<int64_t>(sh.f_in) * sh.f_out;
+  for (int32_t z = 0; z < sh.count; ++z) {
+    w_out[z] = w_role[z / sh.recv_layers] + static_cast<int64_t>(z % sh.recv_layers) * nw;
+    b_out[z] = b_role[z / sh.recv_layers] + static_cast<int64_t>(z % sh.recv_layers) * sh.f_out;
+  }
+  return recolor_solve(rc, sh.count, sh.f_in, sh.f_out, inv_n, w_out.data(), b_out.data(), status, iters, s);
 }
 
 }  // namespace kvx

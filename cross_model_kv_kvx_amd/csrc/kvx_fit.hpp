@@ -31,5 +31,12 @@ int64_t fitc_max_rows(const FitcShape& sh);
 int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
                       const int32_t* map, const int32_t* taps_host, double lam_abs, double lam_rel,
                       float* const* w_role, int32_t* status, void* ws, hipStream_t s);
+// Recolor fits of every receiver layer of n_roles roles from the calibration
+// caches (kvx_fit_recolor_caches); status and iters as for launch_recolor.
+size_t recolor_caches_ws_bytes(const FitcShape& sh);
+int launch_recolor_caches(const FitcShape& sh, const void* const* send_role, const void* const* recv_role,
+                          const int32_t* map, const int32_t* taps_host, double rho_x, double rho_y,
+                          float* const* w_role, float* const* b_role, int32_t* status, int32_t* iters, void* ws,
+                          hipStream_t s);
 
 }  // namespace kvx

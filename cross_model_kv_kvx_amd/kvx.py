@@ -34,6 +34,7 @@ EXPORTS = (
     "kvx_align_tokens_noalloc", "kvx_prepared_maps_size", "kvx_prepare_maps",
     "kvx_translate_prepared_workspace_size", "kvx_translate_prepared", "kvx_probe_hbm", "kvx_probe_mfma",
     "kvx_probe_scratch_words", "kvx_fit_ridge_caches_workspace_size", "kvx_fit_ridge_caches",
+    "kvx_fit_recolor_caches_workspace_size", "kvx_fit_recolor_caches",
 )
 
 
@@ -91,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "kvx_fit_ridge_caches_workspace_size": (sz, [dp, dp, i32]),
             "kvx_fit_ridge_caches": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, dbl, dbl, vp, vp, ip, vp,
                                                     sz, vp]),
+            "kvx_fit_recolor_caches_workspace_size": (sz, [dp, dp, i32]),
+            "kvx_fit_recolor_caches": (ctypes.c_int, [dp, vp, vp, dp, vp, vp, vp, ip, i32, dbl, dbl, vp, vp, vp, vp,
+                                                      ip, ip, vp, sz, vp]),
             "kvx_fit_ridge_batched": (ctypes.c_int, [i32, vpp, i64, vpp, i64, i32, i64, i32, i32, dbl, dbl, i32,
                                                      vpp, vpp, ip, vp, sz, vp]),
             "kvx_fit_recolor_workspace_size": (sz, [i32, i32, i32]),
@@ -549,6 +553,42 @@ def fit_ridge_caches_workspace_size(send: CacheDesc, recv: CacheDesc, n_taps: in
     return int(lib().kvx_fit_ridge_caches_workspace_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps)))
 
 
+class _CacheFit:
+    """Arguments shared by the fits from the caches: the descriptors, the
+    per-role pointers (null for a role not requested) and the shapes."""
+
+    def __init__(self, k_send, v_send, k_recv, v_recv, taps, roles):
+        taps = np.ascontiguousarray(taps, dtype=np.int32)
+        if taps.ndim != 2:
+            raise ValueError("taps must be [L_R][n_taps]")
+        self.taps = taps
+        self.L_R, self.n_taps = taps.shape
+        self.do_k, self.do_v = "k" in roles, "v" in roles
+        if not (self.do_k or self.do_v):
+            raise ValueError("roles must name k, v or both")
+        ref_send = k_send if self.do_k else v_send
+        ref_recv = k_recv if self.do_k else v_recv
+        self.send, self.recv = cache_desc(ref_send), cache_desc(ref_recv)
+        if self.recv.layers != self.L_R:
+            raise ValueError("taps rows must equal the receiver's layers")
+        for t in (k_send, v_send, k_recv, v_recv):
+            if t is not None and not t.is_contiguous():
+                raise ValueError("caches must be contiguous")
+        self.f_in = self.n_taps * self.send.kv_heads * self.send.head_dim
+        self.f_out = self.recv.kv_heads * self.recv.head_dim
+        self.dev = ref_send.device
+        self.ptrs = (_ptr(k_send if self.do_k else None), _ptr(v_send if self.do_v else None),
+                     _ptr(k_recv if self.do_k else None), _ptr(v_recv if self.do_v else None))
+
+    def out(self, given, present, shape):
+        if not present:
+            return None
+        return given if given is not None else torch.empty(shape, dtype=torch.float32, device=self.dev)
+
+    def taps_ptr(self):
+        return self.taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
 def fit_ridge_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], k_recv: Optional[torch.Tensor],
                      v_recv: Optional[torch.Tensor], recv_to_send: torch.Tensor, taps, *, lambda_abs: float = 0.0,
                      lambda_rel: float = 0.0, w_k: Optional[torch.Tensor] = None, w_v: Optional[torch.Tensor] = None,
@@ -561,36 +601,15 @@ def fit_ridge_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tens
     (w_k, w_v), fp32 [L_R][F_in][F_out] (None for a role not requested).
     With a list ``status``, appends the [2][L_R] per-problem statuses and
     raises only for other errors."""
-    taps = np.ascontiguousarray(taps, dtype=np.int32)
-    L_R, n_taps = taps.shape
-    ref_send = k_send if "k" in roles else v_send
-    ref_recv = k_recv if "k" in roles else v_recv
-    send, recv = cache_desc(ref_send), cache_desc(ref_recv)
-    if recv.layers != L_R:
-        raise ValueError("taps rows must equal the receiver's layers")
-    for t in (k_send, v_send, k_recv, v_recv):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("caches must be contiguous")
-    f_in = n_taps * send.kv_heads * send.head_dim
-    f_out = recv.kv_heads * recv.head_dim
-    dev = ref_send.device
-    if "k" in roles and w_k is None:
-        w_k = torch.empty((L_R, f_in, f_out), dtype=torch.float32, device=dev)
-    if "v" in roles and w_v is None:
-        w_v = torch.empty((L_R, f_in, f_out), dtype=torch.float32, device=dev)
-    if "k" not in roles:
-        w_k = None
-    if "v" not in roles:
-        w_v = None
-    ws = _workspace(fit_ridge_caches_workspace_size(send, recv, n_taps), dev, workspace)
-    st_arr = (ctypes.c_int32 * (2 * L_R))()
-    st = lib().kvx_fit_ridge_caches(ctypes.byref(send), _ptr(k_send if w_k is not None else None),
-                                    _ptr(v_send if w_v is not None else None), ctypes.byref(recv),
-                                    _ptr(k_recv if w_k is not None else None),
-                                    _ptr(v_recv if w_v is not None else None), _ptr(recv_to_send),
-                                    taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_taps),
-                                    float(lambda_abs), float(lambda_rel), _ptr(w_k), _ptr(w_v), st_arr, _ptr(ws),
-                                    ws.numel(), _stream(stream))
+    a = _CacheFit(k_send, v_send, k_recv, v_recv, taps, roles)
+    w_k = a.out(w_k, a.do_k, (a.L_R, a.f_in, a.f_out))
+    w_v = a.out(w_v, a.do_v, (a.L_R, a.f_in, a.f_out))
+    ws = _workspace(fit_ridge_caches_workspace_size(a.send, a.recv, a.n_taps), a.dev, workspace)
+    st_arr = (ctypes.c_int32 * (2 * a.L_R))()
+    ks, vs, kr, vr = a.ptrs
+    st = lib().kvx_fit_ridge_caches(ctypes.byref(a.send), ks, vs, ctypes.byref(a.recv), kr, vr, _ptr(recv_to_send),
+                                    a.taps_ptr(), int(a.n_taps), float(lambda_abs), float(lambda_rel), _ptr(w_k),
+                                    _ptr(w_v), st_arr, _ptr(ws), ws.numel(), _stream(stream))
     if status is not None:
         status.extend(int(v) for v in st_arr)
         if st not in (OK, ERR_NOT_SPD):
@@ -598,6 +617,48 @@ def fit_ridge_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tens
     else:
         _check(st, "kvx_fit_ridge_caches")
     return w_k, w_v
+
+
+def fit_recolor_caches_workspace_size(send: CacheDesc, recv: CacheDesc, n_taps: int) -> int:
+    return int(lib().kvx_fit_recolor_caches_workspace_size(ctypes.byref(send), ctypes.byref(recv), int(n_taps)))
+
+
+def fit_recolor_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor],
+                       k_recv: Optional[torch.Tensor], v_recv: Optional[torch.Tensor], recv_to_send: torch.Tensor,
+                       taps, *, rho_x: float = 0.0, rho_y: float = 0.0, w_k: Optional[torch.Tensor] = None,
+                       w_v: Optional[torch.Tensor] = None, b_k: Optional[torch.Tensor] = None,
+                       b_v: Optional[torch.Tensor] = None, roles=("k", "v"),
+                       workspace: Optional[torch.Tensor] = None, stream=None, status: Optional[list] = None,
+                       info: Optional[dict] = None):
+    """kvx_fit_recolor_caches: the Recolor maps of every receiver layer of
+    the requested ``roles`` from the calibration caches, arguments as for
+    fit_ridge_caches.  Returns (w_k, w_v, b_k, b_v): fp32 [L_R][F_in][F_out]
+    and [L_R][F_out] (None for a role not requested).  With a list
+    ``status``, appends the [2][L_R] per-problem statuses and raises only for
+    other errors; with a dict ``info``, stores the polar iterations under
+    "iters"."""
+    a = _CacheFit(k_send, v_send, k_recv, v_recv, taps, roles)
+    w_k = a.out(w_k, a.do_k, (a.L_R, a.f_in, a.f_out))
+    w_v = a.out(w_v, a.do_v, (a.L_R, a.f_in, a.f_out))
+    b_k = a.out(b_k, a.do_k, (a.L_R, a.f_out))
+    b_v = a.out(b_v, a.do_v, (a.L_R, a.f_out))
+    ws = _workspace(fit_recolor_caches_workspace_size(a.send, a.recv, a.n_taps), a.dev, workspace)
+    st_arr = (ctypes.c_int32 * (2 * a.L_R))()
+    iters = ctypes.c_int32(0)
+    ks, vs, kr, vr = a.ptrs
+    st = lib().kvx_fit_recolor_caches(ctypes.byref(a.send), ks, vs, ctypes.byref(a.recv), kr, vr,
+                                      _ptr(recv_to_send), a.taps_ptr(), int(a.n_taps), float(rho_x), float(rho_y),
+                                      _ptr(w_k), _ptr(w_v), _ptr(b_k), _ptr(b_v), st_arr, ctypes.byref(iters),
+                                      _ptr(ws), ws.numel(), _stream(stream))
+    if info is not None:
+        info["iters"] = int(iters.value)
+    if status is not None:
+        status.extend(int(v) for v in st_arr)
+        if st not in (OK, ERR_NOT_SPD, ERR_NOT_CONVERGED):
+            _check(st, "kvx_fit_recolor_caches")
+    else:
+        _check(st, "kvx_fit_recolor_caches")
+    return w_k, w_v, b_k, b_v
 
 
 def fit_recolor(xs, ys, *, rho_x: float = 0.0, rho_y: float = 0.0, w_outs=None, b_outs=None,

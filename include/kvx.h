@@ -590,6 +590,47 @@ int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void
                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * The Recolor fits of every receiver layer and role of one model pair,
+ * straight from the calibration caches: kvx_fit_recolor on the features
+ * kvx_gather_features builds and each receiver layer's own rows, without
+ * materialising the features (the moment-matched fit of "Prefill-Free
+ * Cross-Family KV Cache Transfer ...", Methodology 3, on the calibration
+ * alignment and stage 3's layer map of "Cross-Model KV Cache Transfer in
+ * Production").  The feature moments come from the alignment's runs as in
+ * kvx_fit_ridge_caches (X^T X, X^T Y); the feature column sums are the
+ * distinct sender rows weighted by their run lengths, summed in fp64; Y^T Y
+ * and the target column sums come from the receiver rows as in
+ * kvx_fit_recolor.  The solve (whitening, polar factor, W, b) is
+ * kvx_fit_recolor's, for all 2 L_R problems at once.
+ *
+ * send, k_send, v_send, recv, k_recv, v_recv, recv_to_send, taps, n_taps:
+ *   as for kvx_fit_ridge_caches (same shape limits); F_in >= F_out besides
+ *   (else KVX_ERR_UNSUPPORTED).
+ * rho_x, rho_y >= 0: as for kvx_fit_recolor.
+ * w_k, w_v: device fp32 [L_R][F_in][F_out], or NULL to skip that role (at
+ *   least one given); b_k, b_v: device fp32 [L_R][F_out], required for each
+ *   role fitted (the intercept is part of the map).
+ * status: host int32 [2][L_R] or NULL: per role and layer KVX_OK,
+ *   KVX_ERR_NOT_SPD or KVX_ERR_NOT_CONVERGED as in kvx_fit_recolor (a
+ *   skipped role's entries are KVX_OK).  iters: host int32 or NULL: the
+ *   polar iterations run.
+ * workspace: kvx_fit_recolor_caches_workspace_size(send, recv, n_taps)
+ *   bytes (worst case, as for kvx_fit_ridge_caches, plus the Recolor solve's
+ *   per-problem matrices).
+ * Synchronises `stream` once for the run lengths and once per polar
+ * iteration.  Returns the first non-OK problem status, else KVX_OK; argument
+ * errors as kvx_fit_ridge_caches.
+ * ---------------------------------------------------------------------- */
+size_t kvx_fit_recolor_caches_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv,
+                                             int32_t n_taps);
+int kvx_fit_recolor_caches(const kvx_cache_desc* send, const void* k_send, const void* v_send,
+                           const kvx_cache_desc* recv, const void* k_recv, const void* v_recv,
+                           const int32_t* recv_to_send, const int32_t* taps, int32_t n_taps,
+                           double rho_x, double rho_y, float* w_k, float* w_v, float* b_k,
+                           float* b_v, int32_t* status, int32_t* iters, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Rank-r fold ("Prefill-Free ...", Methodology 3: low-rank corrections folded
  * into one fixed affine map per layer and role).
  *

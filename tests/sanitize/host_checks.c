@@ -525,6 +525,43 @@ static void check_fit_from_caches(const int32_t* taps36) {
 #undef FC
 }
 
+static void check_recolor_from_caches(const int32_t* taps36) {
+  const size_t huge_ws = (size_t)1 << 40;
+  kvx_cache_desc s = desc(36, 50000, 8, 128, KVX_BF16, 0.0), r = desc(32, 65536, 8, 128, KVX_BF16, 0.0);
+  EXPECT(kvx_fit_recolor_caches_workspace_size(&s, &r, 3) > kvx_fit_ridge_caches_workspace_size(&s, &r, 3));
+  kvx_cache_desc rmax = desc(255, INT32_MAX, 8, 128, KVX_BF16, 0.0), smax = desc(255, INT32_MAX, 8, 128, KVX_BF16, 0.0);
+  EXPECT(kvx_fit_recolor_caches_workspace_size(&smax, &rmax, 7) > 0);
+  kvx_cache_desc r0 = desc(32, 0, 8, 128, KVX_BF16, 0.0);
+  EXPECT_EQ(kvx_fit_recolor_caches_workspace_size(&s, &r0, 3), 0);
+  float* w = (float*)FAKE;
+  int32_t status[64], iters = 0;
+#define RC(sd, rd, ks, map, taps, nt, rho, wk, wv, bk, bv, wsb)                                              \
+  kvx_fit_recolor_caches(sd, ks, FAKE, rd, FAKE, FAKE, map, taps, nt, rho, 0.0, wk, wv, bk, bv, status, &iters, \
+                         FAKE, wsb, NULL)
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, taps36, 3, 1e-3, NULL, NULL, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, taps36, 3, NAN, w, w, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, taps36, 3, 1e-3, w, w, NULL, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, taps36, 3, 1e-3, w, w, w, NULL, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(RC(&s, &r, NULL, FAKE, taps36, 3, 1e-3, w, w, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(RC(&s, &r, FAKE, NULL, taps36, 3, 1e-3, w, w, w, w, huge_ws), KVX_ERR_INVALID);
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, NULL, 3, 1e-3, w, w, w, w, huge_ws), KVX_ERR_INVALID);
+  int32_t* bad = exact_i32(taps36, 96);
+  bad[0] = -1;
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, bad, 3, 1e-3, w, w, w, w, huge_ws), KVX_ERR_INVALID);
+  free(bad);
+  /* F_in < F_out: one tap of a 2 x 128 sender row, 8 x 128 targets */
+  kvx_cache_desc s2 = desc(36, 50000, 2, 128, KVX_BF16, 0.0);
+  int32_t* one = exact_i32(taps36, 32);
+  for (int i = 0; i < 32; ++i) one[i] = i;
+  EXPECT_EQ(RC(&s2, &r, FAKE, FAKE, one, 1, 1e-3, w, w, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+  free(one);
+  EXPECT_EQ(RC(&s, &r0, FAKE, FAKE, taps36, 3, 1e-3, w, w, w, w, huge_ws), KVX_ERR_SHAPE);
+  EXPECT_EQ(RC(&s, &r, FAKE, FAKE, taps36, 3, 1e-3, w, w, w, w, 16), KVX_ERR_WORKSPACE);
+  kvx_cache_desc rbig = desc(32, 1 << 26, 8, 128, KVX_BF16, 0.0);
+  EXPECT_EQ(RC(&s, &rbig, FAKE, FAKE, taps36, 3, 1e-3, w, w, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+#undef RC
+}
+
 static void check_maps_and_probes(void) {
   const float* w = (const float*)FAKE;
   EXPECT_EQ(kvx_quantize_fp8(w, 0, 16, 16, (uint8_t*)FAKE, (float*)FAKE, NULL), KVX_OK);
@@ -560,6 +597,7 @@ int main(void) {
   check_gather();
   check_fits();
   check_fit_from_caches(taps36);
+  check_recolor_from_caches(taps36);
   check_maps_and_probes();
   free(taps36);
   if (failures) {

@@ -255,3 +255,40 @@ def test_fit_from_caches_validation():
     assert call(ks=ctypes.c_void_p(0x1008)) == kvx.ERR_UNSUPPORTED  # 16-byte pieces
     assert call(rd=desc(32, 0, 8, 128)) == kvx.ERR_SHAPE
     assert call(ws=16) == kvx.ERR_WORKSPACE
+
+
+def test_recolor_from_caches_validation():
+    """kvx_fit_recolor_caches: sizes and argument checks before anything runs."""
+    L = kvx.lib()
+    fake = ctypes.c_void_p(0x1000)
+    s, r = desc(36, 50000, 8, 128), desc(32, 65536, 8, 128)
+    taps = kvx.layer_map(36, 32, 3, 4)
+    tp = taps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    size = kvx.fit_recolor_caches_workspace_size(s, r, 3)
+    # more than the ridge fit's: the solve keeps Y^T Y, its factor and the
+    # polar iterates per problem besides
+    assert size > kvx.fit_ridge_caches_workspace_size(s, r, 3)
+    assert size > 64 * 8 * (3072 * 3072 + 3072 * 1024 + 5 * 1024 * 1024)
+    assert kvx.fit_recolor_caches_workspace_size(s, desc(32, 0, 8, 128), 3) == 0
+    assert kvx.fit_recolor_caches_workspace_size(s, r, 0) == 0
+
+    def call(sd=s, rd=r, taps_p=tp, n_taps=3, rho=1e-3, wk=fake, wv=fake, bk=fake, bv=fake, ws=1 << 40, ks=fake,
+             m=fake):
+        return L.kvx_fit_recolor_caches(ctypes.byref(sd), ks, fake, ctypes.byref(rd), fake, fake, m, taps_p,
+                                        n_taps, rho, 0.0, wk, wv, bk, bv, None, None, fake, ws, None)
+
+    assert call(wk=None, wv=None) == kvx.ERR_INVALID             # no role
+    assert call(rho=-1.0) == kvx.ERR_INVALID
+    assert call(rho=float("nan")) == kvx.ERR_INVALID
+    assert call(bk=None) == kvx.ERR_INVALID                      # a fitted role needs its bias
+    assert call(ks=None) == kvx.ERR_INVALID
+    assert call(m=None) == kvx.ERR_INVALID
+    assert call(taps_p=None) == kvx.ERR_INVALID
+    assert call(sd=desc(36, 50000, 8, 128, rope=1e4)) == kvx.ERR_UNSUPPORTED
+    assert call(sd=desc(36, 50000, 3, 64)) == kvx.ERR_UNSUPPORTED
+    # F_in < F_out: one tap of a 2 x 128 sender row against 8 x 128 targets
+    one = np.zeros((32, 1), dtype=np.int32)
+    assert call(sd=desc(36, 50000, 2, 128), taps_p=one.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                n_taps=1) == kvx.ERR_UNSUPPORTED
+    assert call(rd=desc(32, 0, 8, 128)) == kvx.ERR_SHAPE
+    assert call(ws=16) == kvx.ERR_WORKSPACE

@@ -183,6 +183,40 @@ def test_cfg5_fit_from_caches(cal):
     torch.cuda.empty_cache()
 
 
+def test_cfg5_recolor_from_caches(cal):
+    """The 64 Recolor fits of the workload by kvx_fit_recolor_caches (rho_x =
+    1e-3: layers 0 and 31 repeat a tap): K layer 15 and V layer 31 vs the
+    oracle's Recolor fit on its own features, and all 64 (W and b) vs
+    kvx_fit_recolor on the gathered features."""
+    st, info = [], {}
+    wk, wv, bk, bv = kvx.fit_recolor_caches(cal["k_send"], cal["v_send"], cal["k_recv"], cal["v_recv"],
+                                            cal["tmap"], cal["taps"], rho_x=1e-3, status=st, info=info)
+    torch.cuda.synchronize()
+    assert st == [kvx.OK] * 64
+    say(f"  recolor from caches: {info['iters']} polar iterations")
+    for role, l in (("k", 15), ("v", 31)):
+        x = O.features(cal[f"{role}_send"], cal["tmap_o"], cal["taps"][l])
+        y = O.as_f64(cal[f"{role}_recv"][l]).reshape(N_CAL, 1024)
+        wo, bo = O.recolor_fit(x, y, rho_x=1e-3)
+        del x, y
+        w, b = (wk, bk) if role == "k" else (wv, bv)
+        ew = O.rel_err(w[l].cpu().numpy().astype(np.float64), wo)
+        eb = O.rel_err(b[l].cpu().numpy().astype(np.float64), bo)
+        say(f"  recolor from caches, {role} layer {l}: W {ew:.3e}, b {eb:.3e} vs the oracle")
+        assert ew <= TOL_BF16 and eb <= TOL_BF16
+    wf, bf = kvx.fit_recolor(cal["xs"], cal["ys"], rho_x=1e-3)
+    worst = 0.0
+    for p in range(64):
+        w, b = (wk, bk) if p < 32 else (wv, bv)
+        gw = O.rel_err(w[p % 32].cpu().numpy().astype(np.float64), wf[p].cpu().numpy().astype(np.float64))
+        gb = O.rel_err(b[p % 32].cpu().numpy().astype(np.float64), bf[p].cpu().numpy().astype(np.float64))
+        worst = max(worst, gw, gb)
+        assert gw <= 5e-3 and gb <= 5e-3, f"problem {p}: W {gw:.3e}, b {gb:.3e}"
+    say(f"  recolor from caches vs the features path, worst over 64 problems: {worst:.3e}")
+    del wk, wv, bk, bv, wf, bf
+    torch.cuda.empty_cache()
+
+
 def test_cfg5_translate_fresh_cache_with_fitted_maps(cal):
     """A fresh 16384-token cache (its own string and sender caches) aligned
     and translated with the fitted fp32 maps (high and low 16-bit halves in

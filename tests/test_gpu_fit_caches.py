@@ -16,6 +16,18 @@ from run sums of the targets.  Checks, every element of every map:
 * one role alone (the skipped role's statuses OK);
 * zero feature columns with lambda 0 reported per problem as not positive
   definite.
+
+kvx_fit_recolor_caches through the C-ABI: the moment-matched maps ("Prefill-
+Free Cross-Family KV Cache Transfer ...", Methodology 3) of every receiver
+layer and role from the same caches (feature moments from the runs, the
+feature column sums weighted by run length).  Checks, every element of
+every W and b:
+* the two-head setting vs the oracle's Recolor fit on the gathered
+  features, and vs kvx_fit_recolor on the gathered features;
+* the long-run map (both roles, layers 1 and 2) vs the oracle;
+* one role alone, a constant receiver column with rho_y 0 (not positive
+  definite for that problem only) and, on a map with fewer distinct sender
+  rows than outputs, every problem reported not converged.
 """
 import sys
 
@@ -30,6 +42,7 @@ from tests.kvx_cases import TOL_BF16
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 LAM_REL = 1e-3
+RHO_X = 1e-3      # duplicated taps (receiver layers 0 and 3 of 6 -> 4) make S_xx singular
 
 
 def say(*a):
@@ -142,3 +155,100 @@ def test_fit_caches_one_role_and_singular_status():
     with pytest.raises(kvx.KvxError):
         kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
                              lambda_rel=0.0)
+
+
+def oracle_recolor(d, role, l, src_rows, rho_x=RHO_X):
+    x = O.features(d[f"{role}_send"], src_rows, d["taps"][l])
+    y = O.as_f64(d[f"{role}_recv"][l]).reshape(x.shape[0], -1)
+    return O.recolor_fit(x, y, rho_x=rho_x)
+
+
+def recolor_err(w, b, wo, bo):
+    return (O.rel_err(w.cpu().numpy().astype(np.float64), wo),
+            O.rel_err(b.cpu().numpy().astype(np.float64), bo))
+
+
+def test_recolor_caches_vs_oracle_and_features_path():
+    d = small_setting(4096, 31)
+    st, info = [], {}
+    wk, wv, bk, bv = kvx.fit_recolor_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"],
+                                            d["taps"], rho_x=RHO_X, status=st, info=info)
+    torch.cuda.synchronize()
+    L_R = d["taps"].shape[0]
+    assert st == [kvx.OK] * (2 * L_R)
+    say(f"  recolor from caches: {info['iters']} polar iterations")
+    for role, w, b in (("k", wk, bk), ("v", wv, bv)):
+        xs = [kvx.gather_features(d[f"{role}_send"], d["tmap"], d["taps"][l]) for l in range(L_R)]
+        ys = [d[f"{role}_recv"][l].reshape(4096, -1) for l in range(L_R)]
+        wf, bf = kvx.fit_recolor(xs, ys, rho_x=RHO_X)
+        for l in range(L_R):
+            wo, bo = oracle_recolor(d, role, l, d["tmap_o"])
+            ew, eb = recolor_err(w[l], b[l], wo, bo)
+            gw, gb = recolor_err(w[l], b[l], wf[l].cpu().numpy().astype(np.float64),
+                                 bf[l].cpu().numpy().astype(np.float64))
+            say(f"  {role} layer {l}: W {ew:.3e}, b {eb:.3e} vs the oracle; W {gw:.3e}, b {gb:.3e} vs the "
+                f"features path")
+            assert ew <= TOL_BF16 and eb <= TOL_BF16
+            # both solve one fp64 problem from fp32-accumulated moments that
+            # differ only in summation order
+            assert gw <= 5e-3 and gb <= 5e-3
+
+
+def test_recolor_caches_long_run():
+    rng = np.random.default_rng(7)
+    lens = [33000] + list(rng.integers(1, 40, size=2000))
+    n = int(sum(lens))
+    n_send = len(lens) + 5
+    vals = np.arange(len(lens), dtype=np.int64)
+    vals[1200] = vals[100]
+    vals[-1] = n_send + 7
+    tmap_h = np.repeat(vals, lens).astype(np.int32)
+    clamped = np.clip(tmap_h, 0, n_send - 1)
+    sshape = synth.CacheShape(6, n_send, 2, 128)
+    rshape = synth.CacheShape(4, n, 2, 128)
+    d = {"taps": kvx.layer_map(6, 4, 3, 2)}
+    for r, role in enumerate(("k", "v")):
+        d[f"{role}_send"] = synth.sender_cache(sshape, 80 + r, DEV)
+        d[f"{role}_recv"] = synth.receiver_cache(rshape, 85 + r, DEV)
+    st = []
+    wk, wv, bk, bv = kvx.fit_recolor_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], dev_i32(tmap_h),
+                                            d["taps"], rho_x=RHO_X, status=st)
+    torch.cuda.synchronize()
+    for role, w, b in (("k", wk, bk), ("v", wv, bv)):
+        for l in (1, 2):
+            assert st[(0 if role == "k" else 4) + l] == kvx.OK
+            wo, bo = oracle_recolor(d, role, l, clamped)
+            ew, eb = recolor_err(w[l], b[l], wo, bo)
+            say(f"  long run, {role} layer {l}: W {ew:.3e}, b {eb:.3e}")
+            assert ew <= TOL_BF16 and eb <= TOL_BF16
+
+
+def test_recolor_caches_one_role_and_statuses():
+    d = small_setting(4096, 34)
+    L_R = d["taps"].shape[0]
+    # a constant target column of V layer 2: S_yy singular with rho_y = 0
+    d["v_recv"][2][:, 1, 5] = 2.0
+    st = []
+    wk, wv, bk, bv = kvx.fit_recolor_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"],
+                                            d["taps"], rho_x=RHO_X, roles=("v",), status=st)
+    torch.cuda.synchronize()
+    assert wk is None and bk is None
+    assert st == [kvx.OK] * L_R + [kvx.OK, kvx.OK, kvx.ERR_NOT_SPD, kvx.OK], st
+    for l in (0, 1, 3):
+        wo, bo = oracle_recolor(d, "v", l, d["tmap_o"])
+        ew, eb = recolor_err(wv[l], bv[l], wo, bo)
+        assert ew <= TOL_BF16 and eb <= TOL_BF16
+    with pytest.raises(kvx.KvxError) as ei:
+        kvx.fit_recolor_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                               rho_x=RHO_X, roles=("v",))
+    assert ei.value.status == kvx.ERR_NOT_SPD
+    # 100 distinct sender rows for 256 outputs: the whitened cross-covariance
+    # has rank below 256, so the Procrustes factor is not determined
+    tmap_h = np.repeat(np.arange(100, dtype=np.int32), 15)
+    sshape = synth.CacheShape(6, 120, 2, 128)
+    rshape = synth.CacheShape(4, tmap_h.size, 2, 128)
+    ks, kr = synth.sender_cache(sshape, 90, DEV), synth.receiver_cache(rshape, 91, DEV)
+    st = []
+    kvx.fit_recolor_caches(ks, None, kr, None, dev_i32(tmap_h), d["taps"], rho_x=RHO_X, roles=("k",), status=st)
+    torch.cuda.synchronize()
+    assert st == [kvx.ERR_NOT_CONVERGED] * L_R + [kvx.OK] * L_R, st

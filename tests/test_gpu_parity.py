@@ -220,15 +220,14 @@ def test_perhead_rope_all_elements(send_rope, recv_rope, map_dtype):
     perhead_rope_case(300, 71, send_rope, recv_rope, map_dtype)
 
 
-def test_perhead_rope_long_span_sampled_rows():
-    """Two spans of receiver tokens (4096 + a ragged rest): the rotation
-    recurrence runs over 64 tiles; rows sampled at the start and end of each
-    span and in between."""
-    say("per-head + RoPE, 4500 receiver tokens, sampled rows")
-    n = 4500
-    rows = np.unique(np.concatenate([np.arange(0, 70), np.arange(4030, 4160), np.arange(n - 70, n),
-                                     sample_rows(np.arange(n), 64, 3)]))
-    perhead_rope_case(n, 72, 5e5, 1e6, torch.float32, rows=rows, L_S=4, L_R=6)
+def test_perhead_rope_long_span_all_rows():
+    """Several spans of receiver tokens with a ragged last one: with 6
+    receiver layers one role's launch is 48 workgroups per span, so the
+    launcher splits the 4500 tokens into spans shorter than 4096 to fill its
+    rounds, and each span restarts the rotation recurrence at its own first
+    token.  Every row is checked, so every span start and end is."""
+    say("per-head + RoPE, 4500 receiver tokens, all rows")
+    perhead_rope_case(4500, 72, 5e5, 1e6, torch.float32, L_S=4, L_R=6)
 
 
 # ---------------------------------------------------------------- cfg3/4: flattened maps
@@ -396,12 +395,13 @@ def test_flat_fp32_maps_all_elements():
 
 def test_perhead_rope_full_size_sampled_rows():
     """The per-head setting with rotated keys at the size the bench times
-    (32 -> 80 layers, 4096 tokens, fp32 maps), sampled rows."""
+    (32 -> 80 layers, 4096 tokens, fp32 maps), sampled rows, among them the
+    rows around token 2048 (one role per launch: two spans of 2048)."""
     say("per-head + RoPE 32 -> 80 layers, 4096 tokens, sampled rows")
     shp = synth.CacheShape(32, 4096, 8, 128)
     taps = kvx.layer_map(32, 80, 1)
     ident = np.arange(4096)
-    rows = sample_rows(ident, 96, 5)
+    rows = np.unique(np.concatenate([sample_rows(ident, 96, 5), np.arange(2040, 2057)]))
     for r, role in enumerate(("k", "v")):
         x = synth.sender_cache(shp, 200 + r, DEV, channel_scale="loguniform")
         wt, b = synth.perhead_maps(80, 8, 128, 220 + r, DEV)
