@@ -224,58 +224,91 @@ def trace_summary(trace_dir, bench_log):
     return out
 
 
-def fit_trace_summary(trace_dir, bench_log):
-    """Markdown summary of a rocprofv3 --kernel-trace run of ``bench.py
-    --fit-only``: the kernels of the last kvx_fit_ridge_caches call (from its
-    run compaction to its last output store, before the Recolor fit's first
-    Gram), per kernel and per phase, beside the same run's fit_ms."""
-    trace = sorted(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))),
-                   key=lambda r: int(r["Start_Timestamp"]))
-    res = json.loads(next(l for l in open(bench_log) if l.startswith("{")))
-    starts = [i for i, r in enumerate(trace) if "kvx::runs_flags_scan" in r["Kernel_Name"]]
-    seg = trace[starts[-1]:]
-    # the call ends before the next fit's Gram (Recolor follows in this run)
-    nxt = [i for i, r in enumerate(seg) if "kvx::gram_kernel" in r["Kernel_Name"]]
-    seg = seg[:nxt[0]] if nxt else seg
-    last_store = max(i for i, r in enumerate(seg) if "kvx::fit_store_kernel" in r["Kernel_Name"])
-    seg = seg[:last_store + 1]
-    span = (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e6
+def _kernel_table(seg):
     per = {}
     for r in seg:
         name = r["Kernel_Name"].split("(")[0].removeprefix("void ")
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
         c, t = per.get(name, (0, 0.0))
         per[name] = (c + 1, t + d)
-
-    def phase(name):
-        if any(k in name for k in ("gram_runs", "fitc_gather", "fitc_target", "runs_")):
-            return "Gram from the runs (gathers, run sums, Gram)"
-        if any(k in name for k in ("dgemm", "potrf", "copy_f64", "fill_f64", "place_linv", "lambda")):
-            return "fp64 solve (lambda, Cholesky, two triangular solves)"
-        return "other (outputs, flags)"
-
-    phases = {}
-    for name, (c, t) in per.items():
-        phases[phase(name)] = phases.get(phase(name), 0.0) + t
+    span = (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e6
     busy = sum(t for _, t in per.values())
     rows = "\n".join(f"| {n[:60]} | {c} | {t:.2f} | {1e3 * t / c:.1f} |"
                      for n, (c, t) in sorted(per.items(), key=lambda kv: -kv[1][1]))
-    prow = "\n".join(f"| {k} | {v:.2f} |" for k, v in sorted(phases.items(), key=lambda kv: -kv[1]))
+    return span, busy, "| kernel | calls | total ms | mean us |\n|---|---|---|---|\n" + rows + "\n"
+
+
+def _phase_table(seg, cuts):
+    """Kernel time per phase: ``cuts`` are (phase name, index of its first
+    dispatch in seg), in order."""
+    out = []
+    for k, (name, i0) in enumerate(cuts):
+        i1 = cuts[k + 1][1] if k + 1 < len(cuts) else len(seg)
+        t = sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in seg[i0:i1])
+        out.append(f"| {name} | {i1 - i0} | {t:.2f} |")
+    return "| phase | dispatches | ms |\n|---|---|---|\n" + "\n".join(out) + "\n"
+
+
+def fit_trace_summary(trace_dir, bench_log):
+    """Markdown summary of a rocprofv3 --kernel-trace run of ``bench.py
+    --fit-only``: the kernels of the last kvx_fit_ridge_caches call and of
+    the last kvx_fit_recolor_caches call, per kernel and per phase, beside
+    the same run's fit_ms of each.  A call from the caches starts with the
+    alignment's run compaction; the ridge call ends with its last output
+    store, the Recolor call (the only one that forms weighted feature sums)
+    with its last bias kernel."""
+    trace = sorted(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    res = json.loads(next(l for l in open(bench_log) if l.startswith("{")))
+
+    def has(seg, key):
+        return any(key in r["Kernel_Name"] for r in seg)
+
+    def first(seg, key):
+        return next(i for i, r in enumerate(seg) if key in r["Kernel_Name"])
+
+    def last(seg, key):
+        return max(i for i, r in enumerate(seg) if key in r["Kernel_Name"])
+
+    starts = [i for i, r in enumerate(trace) if "kvx::runs_flags_scan" in r["Kernel_Name"]]
+    segs = [trace[a:(starts[k + 1] if k + 1 < len(starts) else len(trace))] for k, a in enumerate(starts)]
+    ridge = [g for g in segs if not has(g, "kvx::fitc_sx_kernel") and has(g, "kvx::fit_store_kernel")][-1]
+    # a ridge call ends before the next call's first Gram
+    ridge = ridge[:first(ridge, "kvx::gram_kernel")] if has(ridge, "kvx::gram_kernel") else ridge
+    ridge = ridge[:last(ridge, "kvx::fit_store_kernel") + 1]
+    rc = [g for g in segs if has(g, "kvx::fitc_sx_kernel")][-1]
+    rc = rc[:last(rc, "kvx::fit_bias_final_kernel") + 1]
+
+    out = (f"# Kernel trace: the fits from the calibration caches\n\n"
+           f"source hash: `{source_hash('fit_from_caches')}`\n\n"
+           "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths relative to the "
+           "repository), then this summary:\n\n```\n"
+           "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/fit_trace -o trace --output-format csv "
+           "-- python3 bench.py --fit-only > gpurun_out/prof/fit_trace.log\n"
+           "python3 bench.py --fit-trace-summary gpurun_out/prof/fit_trace gpurun_out/prof/fit_trace.log\n"
+           "```\n\n")
     fit = res["also_fit"]
-    return (f"# Kernel trace: fit from the calibration caches (kvx_fit_ridge_caches)\n\n"
-            f"source hash: `{source_hash('fit_from_caches')}`\n\n"
-            "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first, paths relative to the "
-            "repository), then this summary:\n\n```\n"
-            "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/fit_trace -o trace --output-format csv "
-            "-- python3 bench.py --fit-only > gpurun_out/prof/fit_trace.log\n"
-            "python3 bench.py --fit-trace-summary gpurun_out/prof/fit_trace gpurun_out/prof/fit_trace.log\n"
-            "```\n\n"
-            f"Workload: {fit['workload']}.\n\n"
-            f"Last timed call: {len(seg)} dispatches, {span:.2f} ms from its first to its last kernel, "
+    span, busy, table = _kernel_table(ridge)
+    cuts = [("Gram from the runs (run compaction, gathers, run sums, Gram)", 0),
+            ("fp64 solve (lambda, Cholesky, two triangular solves)", first(ridge, "kvx::lambda_batched_kernel")),
+            ("outputs", first(ridge, "kvx::fit_store_kernel"))]
+    out += (f"## Ridge (kvx_fit_ridge_caches)\n\nWorkload: {fit['workload']}.\n\n"
+            f"Last timed call: {len(ridge)} dispatches, {span:.2f} ms from its first to its last kernel, "
             f"{busy:.2f} ms of kernel time.  Same run, bench.py's host clock around the call: "
-            f"{fit['fit_ms']:.2f} ms (mean of the timed calls).\n\n"
-            "| phase | ms |\n|---|---|\n" + prow + "\n\n"
-            "| kernel | calls | total ms | mean us |\n|---|---|---|---|\n" + rows + "\n")
+            f"{fit['fit_ms']:.2f} ms (mean of the timed calls).\n\n" + _phase_table(ridge, cuts) + "\n" + table)
+    rec = res["also_recolor"]
+    span, busy, table = _kernel_table(rc)
+    cuts = [("moments (Gram from the runs, feature sums, Y^T Y, target sums, centring)", 0),
+            ("factors and whitened cross-covariance (Cholesky of both, solves, M)", first(rc, "kvx::potrf_diag")),
+            # S = M^T M is the product just before the first mirroring
+            ("polar iteration (S = M^T M, scale, Newton-Schulz steps)", first(rc, "kvx::sym_from_lower") - 1),
+            ("map and bias (Q, back-substitution, outputs)", last(rc, "kvx::frob_final") + 1)]
+    out += (f"\n## Recolor (kvx_fit_recolor_caches)\n\nWorkload: {rec['workload']}.\n\n"
+            f"Last timed call: {len(rc)} dispatches, {span:.2f} ms from its first to its last kernel, "
+            f"{busy:.2f} ms of kernel time, {rec['polar_iterations']} polar iterations.  Same run, bench.py's "
+            f"host clock around the call: {rec['fit_ms']:.2f} ms (mean of the timed calls).\n\n"
+            + _phase_table(rc, cuts) + "\n" + table)
+    return out
 
 
 UNITS_FILES = {

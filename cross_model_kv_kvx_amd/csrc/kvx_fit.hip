@@ -838,8 +838,8 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
 // the stores and of the fragment reads); the next chunk is read
 // into registers while the current one is multiplied.  A workgroup reads all
 // of its A rows and B columns before it writes its tile, so C may alias A when
-// N <= 2 WT or B when M <= 2 WT.  lower_only skips tiles strictly above the
-// diagonal.
+// N <= 2 WT or B when M <= 2 WT.  lower_only forms only the tiles on and
+// below the diagonal (the grid holds just those).
 struct DgArgs {
   int32_t M, N, K;
   const double* A;
@@ -868,8 +868,22 @@ dgemm_kernel(const DgArgs g) {
   constexpr int NQ = BT * DG_BK / 256; // elements of A (and of B) per thread and chunk
   constexpr int NF = WT / 16;          // MFMA blocks per wave and dimension
   constexpr bool PRE_C = WT == 32;
-  const int32_t bm = blockIdx.y, bn = blockIdx.x;
-  if (g.lower_only && bm < bn) return;
+  int32_t bm = blockIdx.y, bn = blockIdx.x;
+  if (g.lower_only) {
+    // blockIdx.x enumerates only the tiles on and below the diagonal, row by
+    // row (row bm holds min(bm + 1, column tiles) of them), so consecutive
+    // workgroups, which go to different XCDs, share the work evenly
+    const int32_t nbn = (g.N + BT - 1) / BT;
+    int32_t t = blockIdx.x;
+    bm = 0;
+    for (;;) {
+      const int32_t w = bm + 1 < nbn ? bm + 1 : nbn;
+      if (t < w) break;
+      t -= w;
+      ++bm;
+    }
+    bn = t;
+  }
   __shared__ double As[AK ? BT : DG_BK][AK ? LDK : LD];
   __shared__ double Bs[BK ? BT : DG_BK][BK ? LDK : LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1132,8 +1146,12 @@ static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, 
   const bool ak = sak == 1 && sam != 1, bk = sbk == 1 && sbn != 1;
   const bool big = M >= 128 && N >= 128 && K >= 128;
   const int bt = big ? 128 : 64;
-  const dim3 grid(static_cast<unsigned>(ceil_div(N, bt)), static_cast<unsigned>(ceil_div(M, bt)),
-                  static_cast<unsigned>(count));
+  const int64_t nbm = ceil_div(M, bt), nbn = ceil_div(N, bt);
+  int64_t n_lower = 0;  // tiles on and below the diagonal
+  for (int64_t bm = 0; bm < nbm; ++bm) n_lower += bm + 1 < nbn ? bm + 1 : nbn;
+  const dim3 grid = lower_only ? dim3(static_cast<unsigned>(n_lower), 1, static_cast<unsigned>(count))
+                               : dim3(static_cast<unsigned>(nbn), static_cast<unsigned>(nbm),
+                                      static_cast<unsigned>(count));
 #define KVX_DG(WT, A_, B_) dgemm_kernel<WT, A_, B_><<<grid, 256, 0, s>>>(g)
   if (big) {
     if (ak) { if (bk) KVX_DG(64, true, true); else KVX_DG(64, true, false); }
@@ -1488,6 +1506,7 @@ __global__ __launch_bounds__(256) void lambda_batched_kernel(double* __restrict_
 }
 
 // The Gram-from-runs part of a workspace (both fits from the caches).
+constexpr int SG_CHUNKS = 64;  // run chunks of the weighted feature sums
 struct RunsWs {
   Runs runs;
   void* runs_scratch;
@@ -1499,6 +1518,7 @@ struct RunsWs {
   uint16_t* xg;
   uint16_t* qp;
   double* sigma;       // [L_S][row]: sum_u c_u x_u of every sender layer (one role)
+  double* sigma_part;  // [L_S][SG_CHUNKS][row]: its per-chunk partials
   int64_t u_cap, g_cap;  // row capacities of xu (and half of qp) and xg
 };
 
@@ -1523,6 +1543,7 @@ static RunsWs runs_layout(const FitcShape& sh, Carve& c) {
   w.xg = c.take<uint16_t>(static_cast<size_t>(sh.send_layers) * w.g_cap * sh.row);
   w.qp = c.take<uint16_t>(static_cast<size_t>(sh.recv_layers) * 2 * w.u_cap * sh.f_out);
   w.sigma = c.take<double>(static_cast<size_t>(sh.send_layers) * sh.row);
+  w.sigma_part = c.take<double>(static_cast<size_t>(sh.send_layers) * SG_CHUNKS * sh.row);
   return w;
 }
 
@@ -1600,21 +1621,46 @@ static void fitc_keys(const FitcShape& sh, const int32_t* taps, std::vector<GrrK
   }
 }
 
-// sigma[s][f] = sum over runs u of c_u x_u[s][f] for every sender layer s
-// (the column sums of the features, n times their means), fp64, four
-// partial sums over u mod 4 added in a fixed order.
-__global__ __launch_bounds__(256) void fitc_sigma_kernel(const uint16_t* __restrict__ xu, int64_t xu_layer,
-                                                         int32_t row, const int32_t* __restrict__ run_begin,
-                                                         int32_t n_runs, double* __restrict__ sigma) {
+// Run-length-weighted column sums of the distinct rows of every sender layer
+// (sum_u c_u x_u, n times the feature means of that layer's taps), in two
+// passes: each one-wave workgroup sums SG_CHUNKS-th of the runs for 512
+// columns (8 per lane, 16-byte loads), fp64 partials written per chunk; then
+// the chunks are added in order.
+__global__ __launch_bounds__(64) void fitc_sigma_part_kernel(const uint16_t* __restrict__ xu, int64_t xu_layer,
+                                                             int32_t row, const int32_t* __restrict__ run_begin,
+                                                             int32_t n_runs, double* __restrict__ part) {
+  const int32_t c0 = (blockIdx.x * 64 + threadIdx.x) * 8;
+  const int64_t sl = blockIdx.z;
+  const int32_t per = (n_runs + SG_CHUNKS - 1) / SG_CHUNKS;
+  const int32_t u0 = blockIdx.y * per;
+  const int32_t u1 = min(n_runs, u0 + per);
+  if (c0 >= row) return;
+  const uint16_t* col = xu + sl * xu_layer + c0;
+  double acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = 0.0;
+  for (int32_t u = u0; u < u1; ++u) {
+    const double c = static_cast<double>(run_begin[u + 1] - run_begin[u]);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(col + static_cast<int64_t>(u) * row);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += c * static_cast<double>(bf16lo(q[e]));
+      acc[2 * e + 1] += c * static_cast<double>(bf16hi(q[e]));
+    }
+  }
+  double* out = part + (sl * SG_CHUNKS + blockIdx.y) * row + c0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) out[v] = acc[v];
+}
+
+__global__ __launch_bounds__(256) void fitc_sigma_final_kernel(const double* __restrict__ part, int32_t row,
+                                                               double* __restrict__ sigma) {
   const int64_t sl = blockIdx.y;
   const int32_t f = blockIdx.x * 256 + threadIdx.x;
   if (f >= row) return;
-  const uint16_t* col = xu + sl * xu_layer + f;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int32_t u = 0; u < n_runs; ++u)
-    acc[u & 3] += static_cast<double>(run_begin[u + 1] - run_begin[u]) *
-                  static_cast<double>(bf16_to_f32(col[static_cast<int64_t>(u) * row]));
-  sigma[sl * row + f] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  double a = 0.0;
+  for (int q = 0; q < SG_CHUNKS; ++q) a += part[(sl * SG_CHUNKS + q) * row + f];
+  sigma[sl * row + f] = a;
 }
 
 // sx of problem z (receiver layer z - z0): tap t's row of sigma.
@@ -1709,8 +1755,13 @@ static int gram_from_runs(const FitcShape& sh, const RunsWs& w, const void* cons
     gram_runs_kernel<<<static_cast<unsigned>(items < cus ? items : cus), GR_THREADS, 0, s>>>(gr);
     KVX_LAUNCH_CHECK();
     if (sx) {
-      fitc_sigma_kernel<<<dim3(static_cast<unsigned>(ceil_div(sh.row, 256)), static_cast<unsigned>(sh.send_layers)),
-                          256, 0, s>>>(w.xu, g.xu_layer, sh.row, w.runs.run_begin, n_runs, w.sigma);
+      // rows are whole 16-byte pieces: row is a multiple of 256
+      fitc_sigma_part_kernel<<<dim3(static_cast<unsigned>(ceil_div(sh.row, 512)), SG_CHUNKS,
+                                    static_cast<unsigned>(sh.send_layers)),
+                               64, 0, s>>>(w.xu, g.xu_layer, sh.row, w.runs.run_begin, n_runs, w.sigma_part);
+      fitc_sigma_final_kernel<<<dim3(static_cast<unsigned>(ceil_div(sh.row, 256)),
+                                     static_cast<unsigned>(sh.send_layers)),
+                                256, 0, s>>>(w.sigma_part, sh.row, w.sigma);
       KVX_LAUNCH_CHECK();
       fitc_sx_kernel<<<dim3(static_cast<unsigned>(ceil_div(sh.f_in, 256)), static_cast<unsigned>(sh.recv_layers)),
                        256, 0, s>>>(w.sigma, sh.row, w.taps, sh.n_taps, sx + z0 * bs, bs);
@@ -1807,21 +1858,77 @@ __global__ __launch_bounds__(256) void zero_upper_kernel(double* __restrict__ p,
     if (e % n > e / n) q[e] = 0.0;
 }
 
-// ||S||_F of each problem (one workgroup per problem, fixed summation order).
-__global__ __launch_bounds__(256) void frob_kernel(const double* __restrict__ S, int32_t n, int64_t bs,
-                                                   double* __restrict__ out) {
-  S += blockIdx.x * bs;
+// ||S||_F of each problem in a fixed summation order: NS_BLOCKS workgroups
+// per problem sum the squares of interleaved elements, then the partials are
+// added in block order.
+__global__ __launch_bounds__(256) void frob_part_kernel(const double* __restrict__ S, int32_t n, int64_t bs,
+                                                        double* __restrict__ part) {
+  const double* q = S + blockIdx.y * bs;
   __shared__ double red[256];
   const int64_t total = static_cast<int64_t>(n) * n;
   double a = 0.0;
-  for (int64_t e = threadIdx.x; e < total; e += 256) a += S[e] * S[e];
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total; e += NS_BLOCKS * 256)
+    a += q[e] * q[e];
   red[threadIdx.x] = a;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[blockIdx.x * bs] = sqrt(red[0]);
+  if (threadIdx.x == 0) part[blockIdx.y * NS_BLOCKS + blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(64) void frob_final_kernel(const double* __restrict__ part, int64_t bs,
+                                                        double* __restrict__ out) {
+  if (threadIdx.x != 0) return;
+  double a = 0.0;
+  for (int b = 0; b < NS_BLOCKS; ++b) a += part[blockIdx.x * NS_BLOCKS + b];
+  out[blockIdx.x * bs] = sqrt(a);
+}
+
+// out[z * bs] = ||S_z||_F; part holds count * NS_BLOCKS doubles
+static int frob(hipStream_t s, int32_t count, const double* S, int32_t n, int64_t bs, double* part, double* out) {
+  frob_part_kernel<<<dim3(NS_BLOCKS, static_cast<unsigned>(count)), 256, 0, s>>>(S, n, bs, part);
+  frob_final_kernel<<<static_cast<unsigned>(count), 64, 0, s>>>(part, bs, out);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
+}
+
+// Symmetric from its lower triangle: every entry above the diagonal of each
+// problem's n x n matrix is set to its mirror below.  One workgroup per 64 x
+// 64 block on or above the diagonal reads the mirror block row by row into
+// LDS and writes the block row by row (a diagonal block only above its
+// diagonal); the blocks it reads are never written.
+__global__ __launch_bounds__(256) void sym_from_lower_kernel(double* __restrict__ P, int32_t n, int64_t bs) {
+  __shared__ double tile[RD_T][RD_T + 1];
+  double* q = P + blockIdx.y * bs;
+  const int32_t nb = (n + RD_T - 1) / RD_T;
+  int32_t t = blockIdx.x, bi = 0, rowlen = nb;
+  while (t >= rowlen) {
+    t -= rowlen;
+    ++bi;
+    --rowlen;
+  }
+  const int32_t bj = bi + t;  // target block (bi, bj), bi <= bj; source (bj, bi)
+  for (int e = threadIdx.x; e < RD_T * RD_T; e += 256) {
+    const int r = e / RD_T, c = e % RD_T;
+    const int32_t m = bj * RD_T + r, k = bi * RD_T + c;
+    tile[r][c] = (m < n && k < n) ? q[static_cast<int64_t>(m) * n + k] : 0.0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < RD_T * RD_T; e += 256) {
+    const int r = e / RD_T, c = e % RD_T;
+    const int32_t i = bi * RD_T + r, j = bj * RD_T + c;
+    if (i < n && j < n && j > i) q[static_cast<int64_t>(i) * n + j] = tile[c][r];
+  }
+}
+
+static int sym_from_lower(hipStream_t s, int32_t count, double* P, int32_t n, int64_t bs) {
+  const int32_t nb = static_cast<int32_t>(ceil_div(n, RD_T));
+  sym_from_lower_kernel<<<dim3(static_cast<unsigned>(nb * (nb + 1) / 2), static_cast<unsigned>(count)), 256, 0, s>>>(
+      P, n, bs);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
 }
 
 // p *= c^power with c = scal of the problem.
@@ -2019,8 +2126,15 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
 
   // 3. S = M^T M, then the polar iteration
   double *Y = w.ns[0], *Z = w.ns[1], *T = w.ns[2], *N = w.ns[3];
-  if (int st = dgemm(s, count, f_out, f_out, f_in, w.M, 1, f_out, w.M, f_out, 1, Y, f_out, bs, 0, 1)) return st;
-  frob_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(Y, f_out, bs, w.scal);
+  // S and each step's T are symmetric (the iterates are polynomials in S):
+  // only their tiles on and below the diagonal are formed, then mirrored.
+  // Y and Z are updated by the full products with the one symmetric T, from
+  // opposite sides: mirroring them as well breaks the pairing of their
+  // rounding errors that keeps the coupled iteration stable (it then
+  // diverges once Z grows large), so they stay as computed.
+  if (int st = dgemm(s, count, f_out, f_out, f_in, w.M, 1, f_out, w.M, f_out, 1, Y, f_out, bs, 1, 1)) return st;
+  if (int st = sym_from_lower(s, count, Y, f_out, bs)) return st;
+  if (int st = frob(s, count, Y, f_out, bs, w.dev, w.scal)) return st;
   // largest eigenvalue of S by RC_POWER power steps (v in T, S v in N), so
   // the iteration starts with the spectrum of S / c close to (0, 1]: each
   // factor 2.25 of underscaling of the smallest eigenvalue costs one step
@@ -2039,7 +2153,8 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
   std::vector<uint8_t> done(static_cast<size_t>(count), 0);
   int32_t it = 0;
   for (; it < RC_MAX_ITERS; ++it) {
-    if (int st = dgemm(s, count, f_out, f_out, f_out, Z, f_out, 1, Y, f_out, 1, T, f_out, bs, 0, 1)) return st;
+    if (int st = dgemm(s, count, f_out, f_out, f_out, Z, f_out, 1, Y, f_out, 1, T, f_out, bs, 1, 1)) return st;
+    if (int st = sym_from_lower(s, count, T, f_out, bs)) return st;
     ns_mid_kernel<<<dim3(NS_BLOCKS, static_cast<unsigned>(count)), 256, 0, s>>>(T, f_out, bs, w.dev);
     KVX_LAUNCH_CHECK();
     if (int st = dgemm(s, count, f_out, f_out, f_out, Y, f_out, 1, T, f_out, 1, N, f_out, bs, 0, 1)) return st;
@@ -2069,8 +2184,7 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
     }
   }
   if (iters) *iters = it;
-  frob_kernel<<<static_cast<unsigned>(count), 256, 0, s>>>(Z, f_out, bs, w.scal + 1);
-  KVX_LAUNCH_CHECK();
+  if (int st = frob(s, count, Z, f_out, bs, w.dev, w.scal + 1)) return st;
   std::vector<double> zf(static_cast<size_t>(count));
   for (int32_t z = 0; z < count; ++z)
     KVX_HIP_TRY(hipMemcpyAsync(&zf[z], w.scal + z * bs + 1, sizeof(double), hipMemcpyDeviceToHost, s));
