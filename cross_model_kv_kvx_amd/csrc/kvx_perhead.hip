@@ -44,10 +44,11 @@ namespace kvx {
 // counter is per wave: compute waves only load and store waves never wait,
 // so no load ever waits for stores to complete.  One barrier per tile orders
 // the stages and staging buffers between the two kinds.  Workgroups are
-// numbered head innermost, then receiver layer, and consecutive numbers go to
-// one XCD: the heads of a layer, which write the 256-byte pieces of the same
-// receiver rows, run side by side, and the neighbouring receiver layers that
-// share a sender layer read its rows through one L2.
+// numbered by group of receiver layers that share a sender layer, then head,
+// then layer within the group, and consecutive numbers go to one XCD: the
+// 2-3 workgroups that read one sender head start together and read its rows
+// through one L2, and a group's heads, which write the 256-byte pieces of the
+// same receiver rows, run side by side.
 constexpr int PH_TILE = 64;                      // tokens per tile
 constexpr int PH_SPAN = 4096;                    // tokens per workgroup at most
 constexpr int PH_MIN_SPAN = 1024;                // shortest span chosen to fill a round of workgroups
@@ -79,6 +80,10 @@ struct HeadKArgs {
   int32_t pos_limit;
   int32_t recv_layers, recv_tokens, heads, n_span, span_len, n_blocks, xcd_remap;
   uint8_t tap[MAX_LAYERS];  // sender layer of each receiver layer
+  // receiver layers form groups: maximal runs of consecutive layers with one
+  // sender layer; first layer and size of each layer's group
+  uint8_t gstart[MAX_LAYERS];
+  uint8_t gsize[MAX_LAYERS];
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r.
@@ -287,12 +292,16 @@ perhead_kernel(const HeadKArgs a) {
 
   int32_t b = blockIdx.x;
   if (a.xcd_remap) b = (b & 7) * (a.n_blocks >> 3) + (b >> 3);
-  const int32_t h = b % a.heads;
-  int32_t rest = b / a.heads;
-  const int32_t l = rest % a.recv_layers;
-  rest /= a.recv_layers;
-  const int32_t span = rest % a.n_span;
-  const int role = rest / a.n_span;
+  // within a (role, span): group by group, head by head, the group's layers
+  // innermost, so the 2-3 workgroups that read one sender head are adjacent
+  const int32_t per = a.heads * a.recv_layers;
+  const int32_t o = b % per;
+  const int32_t span = (b / per) % a.n_span;
+  const int role = (b / per) / a.n_span;
+  const int32_t gs = a.gstart[o / a.heads], gz = a.gsize[o / a.heads];
+  const int32_t loc = o - gs * a.heads;
+  const int32_t h = loc / gz;
+  const int32_t l = gs + loc % gz;
   const int32_t s = a.tap[l];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int64_t row_elems = static_cast<int64_t>(a.heads) * 128;
@@ -506,6 +515,15 @@ int launch_perhead(const HeadProblem& p, const HeadRole* roles, int n_roles, hip
     a.span_len = span_len;
     a.n_span = static_cast<int32_t>(ceil_div(p.recv_tokens, span_len));
     for (int l = 0; l < p.recv_layers; ++l) a.tap[l] = static_cast<uint8_t>(p.taps[l]);
+    for (int l = 0; l < p.recv_layers;) {
+      int e = l + 1;
+      while (e < p.recv_layers && p.taps[e] == p.taps[l]) ++e;
+      for (int i = l; i < e; ++i) {
+        a.gstart[i] = static_cast<uint8_t>(l);
+        a.gsize[i] = static_cast<uint8_t>(e - l);
+      }
+      l = e;
+    }
     const int64_t nb = per_span * a.n_span;
     if (nb >= (1LL << 31)) return KVX_ERR_UNSUPPORTED;
     a.n_blocks = static_cast<int32_t>(nb);
