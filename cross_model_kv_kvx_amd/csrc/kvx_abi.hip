@@ -763,6 +763,11 @@ static bool fitc_shape(const kvx_cache_desc* send, const kvx_cache_desc* recv, i
   sh->f_in = n_taps * sh->row;
   sh->n_roles = n_roles;
   sh->count = n_roles * recv->layers;
+  sh->send_rope = send->rope_base;
+  sh->recv_rope = recv->rope_base;
+  sh->send_hd = send->head_dim;
+  sh->recv_hd = recv->head_dim;
+  sh->key_role = -1;
   return true;
 }
 
@@ -777,8 +782,11 @@ static int fitc_check(const kvx_cache_desc* send, const void* k_send, const void
   if (!taps || (recv->tokens > 0 && !recv_to_send)) return KVX_ERR_INVALID;
   for (int32_t i = 0; i < recv->layers * n_taps; ++i)
     if (taps[i] < 0 || taps[i] >= send->layers) return KVX_ERR_INVALID;
-  if (send->dtype != KVX_BF16 || recv->dtype != KVX_BF16 || send->rope_base != 0.0 || recv->rope_base != 0.0)
+  if (send->dtype != KVX_BF16 || recv->dtype != KVX_BF16) return KVX_ERR_UNSUPPORTED;
+  // rotated keys are turned back in pieces of 8 pairs (c .. c+7, c+d/2 .. c+d/2+7)
+  if ((send->rope_base > 0.0 && send->head_dim % 16) || (recv->rope_base > 0.0 && recv->head_dim % 16))
     return KVX_ERR_UNSUPPORTED;
+  sh->key_role = do_k ? 0 : -1;
   if ((sh->row % 256) != 0 || (sh->f_out % 8) != 0) return KVX_ERR_UNSUPPORTED;
   // rows are read in 16-byte pieces
   for (const void* p : {k_send, v_send, k_recv, v_recv})

@@ -515,69 +515,128 @@ gram_runs_kernel(const GramRunsArgs g) {
   }
 }
 
-// out[s][r][:] = the sender row of run list[r] (list null: run r < n_valid) of
-// sender layer s, or zeros (padding), 16 bytes per thread.
+// One 16-byte piece of a row, or with ROT (keys stored rotated) the pieces
+// of 8 pairs (c .. c+7 and c+d/2 .. c+d/2+7 of a head of d) rotated back
+// at the row's position (its token index) from the fp32 (cos, sin) table,
+// rounded to bf16.  Row r takes token uniq[u] of u = list[r] (or u = r below
+// n_valid, zero past it); without uniq the token is u itself.
+template <bool ROT>
 __global__ __launch_bounds__(256) void fitc_gather_kernel(const uint16_t* __restrict__ send, int64_t send_layer,
                                                           int32_t row, const int32_t* __restrict__ uniq,
                                                           const int32_t* __restrict__ list, int32_t n_valid,
                                                           int32_t rows_out, uint16_t* __restrict__ out,
-                                                          int64_t out_layer) {
+                                                          int64_t out_layer, const float2* __restrict__ tab,
+                                                          int32_t hd) {
   const int64_t sl = blockIdx.y;
-  const int32_t cpr = row / 8;
+  const int32_t cpr = ROT ? row / 16 : row / 8;
   const int64_t total = static_cast<int64_t>(rows_out) * cpr;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < total;
        t += static_cast<int64_t>(gridDim.x) * 256) {
     const int32_t r = static_cast<int32_t>(t / cpr), c = static_cast<int32_t>(t % cpr);
     const int32_t u = list ? list[r] : (r < n_valid ? r : -1);
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (u >= 0) {
-      const int64_t tok = uniq[u];
-      v = *reinterpret_cast<const u32x4*>(send + sl * send_layer + tok * row + 8 * c);
+    const int64_t tok = u < 0 ? 0 : (uniq ? uniq[u] : u);
+    const uint16_t* src = send + sl * send_layer + tok * row;
+    uint16_t* dst = out + sl * out_layer + static_cast<int64_t>(r) * row;
+    if constexpr (!ROT) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (u >= 0) v = *reinterpret_cast<const u32x4*>(src + 8 * c);
+      *reinterpret_cast<u32x4*>(dst + 8 * c) = v;
+    } else {
+      const int32_t qh = hd / 16;  // pieces per half head
+      const int32_t ca = (c / qh) * hd + 8 * (c % qh), cb = ca + hd / 2;
+      u32x4 va = u32x4{0u, 0u, 0u, 0u}, vb = va;
+      if (u >= 0) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(src + ca);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(src + cb);
+        const float2* cs = tab + tok * (hd / 2) + 8 * (c % qh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 c0 = cs[2 * e], c1 = cs[2 * e + 1];
+          const float a0 = bf16lo(a[e]), a1 = bf16hi(a[e]), b0 = bf16lo(b[e]), b1 = bf16hi(b[e]);
+          // rotation by -angle: (a, b) -> (a cos + b sin, b cos - a sin)
+          va[e] = pack_bf16(a0 * c0.x + b0 * c0.y, a1 * c1.x + b1 * c1.y);
+          vb[e] = pack_bf16(b0 * c0.x - a0 * c0.y, b1 * c1.x - a1 * c1.y);
+        }
+      }
+      *reinterpret_cast<u32x4*>(dst + ca) = va;
+      *reinterpret_cast<u32x4*>(dst + cb) = vb;
     }
-    *reinterpret_cast<u32x4*>(out + sl * out_layer + static_cast<int64_t>(r) * row + 8 * c) = v;
   }
 }
 
-// Run sums of the targets of problem l: s_u = sum over the run's tokens i
-// (in token order, fp32) of y[l][i][:]; qp[l][u] = bf16(s_u) (nearest even)
-// and qp[l][u_pad + u] = bf16(s_u - that), zeros for u >= U.  8 outputs per
-// thread.  y_layer: elements between the problems' target layers.
+// Run sums of the targets: for run u of every receiver layer, the sum over its
+// receiver rows in token order, fp32, stored as a high bf16 part (rows
+// 0 .. u_pad) and the bf16 rounding of the remainder (rows u_pad .. 2 u_pad);
+// padding runs get zeros.  One thread: one 16-byte piece, or with ROT (target
+// keys stored rotated) the two pieces of 8 pairs, each row rotated back at
+// its position (its token index) before it is added.
+template <bool ROT>
 __global__ __launch_bounds__(256) void fitc_target_sums_kernel(const uint16_t* __restrict__ y, int64_t y_layer,
                                                                int32_t f_out, const int32_t* __restrict__ run_begin,
                                                                int32_t n_runs, int32_t u_pad,
-                                                               uint16_t* __restrict__ qp, int64_t qp_layer) {
+                                                               uint16_t* __restrict__ qp, int64_t qp_layer,
+                                                               const float2* __restrict__ tab, int32_t hd) {
+  constexpr int NP = ROT ? 2 : 1;  // pieces per thread
   const int64_t l = blockIdx.y;
-  const int32_t cpr = f_out / 8;
+  const int32_t cpr = f_out / (8 * NP);
   const int64_t total = static_cast<int64_t>(u_pad) * cpr;
   const uint16_t* yl = y + l * y_layer;
   uint16_t* ql = qp + l * qp_layer;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < total;
        t += static_cast<int64_t>(gridDim.x) * 256) {
     const int32_t u = static_cast<int32_t>(t / cpr), c = static_cast<int32_t>(t % cpr);
-    float sum[8];
+    int32_t col[NP];
+    if constexpr (ROT) {
+      const int32_t qh = hd / 16;
+      col[0] = (c / qh) * hd + 8 * (c % qh);
+      col[NP - 1] = col[0] + hd / 2;
+    } else {
+      col[0] = 8 * c;
+    }
+    float sum[NP][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[p][e] = 0.0f;
     if (u < n_runs) {
       for (int32_t i = run_begin[u]; i < run_begin[u + 1]; ++i) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(yl + static_cast<int64_t>(i) * f_out + 8 * c);
+        const uint16_t* yr = yl + static_cast<int64_t>(i) * f_out;
+        if constexpr (ROT) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(yr + col[0]);
+          const u32x4 b = *reinterpret_cast<const u32x4*>(yr + col[NP - 1]);
+          const float2* cs = tab + static_cast<int64_t>(i) * (hd / 2) + 8 * (c % (hd / 16));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sum[2 * e] += bf16lo(v[e]);
-          sum[2 * e + 1] += bf16hi(v[e]);
+          for (int e = 0; e < 8; ++e) {
+            const float2 q = cs[e];
+            const float av = (e & 1) ? bf16hi(a[e >> 1]) : bf16lo(a[e >> 1]);
+            const float bv = (e & 1) ? bf16hi(b[e >> 1]) : bf16lo(b[e >> 1]);
+            sum[0][e] += av * q.x + bv * q.y;
+            sum[NP - 1][e] += bv * q.x - av * q.y;
+          }
+        } else {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(yr + col[0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sum[0][2 * e] += bf16lo(v[e]);
+            sum[0][2 * e + 1] += bf16hi(v[e]);
+          }
         }
       }
     }
-    u32x4 hi, lo;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t h0 = f32_to_bf16_rne(sum[2 * e]), h1 = f32_to_bf16_rne(sum[2 * e + 1]);
-      const uint16_t l0 = f32_to_bf16_rne(sum[2 * e] - bf16_to_f32(h0));
-      const uint16_t l1 = f32_to_bf16_rne(sum[2 * e + 1] - bf16_to_f32(h1));
-      hi[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-      lo[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+    for (int p = 0; p < NP; ++p) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h0 = f32_to_bf16_rne(sum[p][2 * e]), h1 = f32_to_bf16_rne(sum[p][2 * e + 1]);
+        const uint16_t l0 = f32_to_bf16_rne(sum[p][2 * e] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16_rne(sum[p][2 * e + 1] - bf16_to_f32(h1));
+        hi[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lo[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+      }
+      *reinterpret_cast<u32x4*>(ql + static_cast<int64_t>(u) * f_out + col[p]) = hi;
+      *reinterpret_cast<u32x4*>(ql + (static_cast<int64_t>(u_pad) + u) * f_out + col[p]) = lo;
     }
-    *reinterpret_cast<u32x4*>(ql + static_cast<int64_t>(u) * f_out + 8 * c) = hi;
-    *reinterpret_cast<u32x4*>(ql + (static_cast<int64_t>(u_pad) + u) * f_out + 8 * c) = lo;
   }
 }
 
@@ -1519,6 +1578,8 @@ struct RunsWs {
   uint16_t* qp;
   double* sigma;       // [L_S][row]: sum_u c_u x_u of every sender layer (one role)
   double* sigma_part;  // [L_S][SG_CHUNKS][row]: its per-chunk partials
+  float2* tab_send;    // (cos, sin) per sender position and pair, when the sender keys are rotated
+  float2* tab_recv;    // the same for the receiver's (target) keys
   int64_t u_cap, g_cap;  // row capacities of xu (and half of qp) and xg
 };
 
@@ -1544,6 +1605,8 @@ static RunsWs runs_layout(const FitcShape& sh, Carve& c) {
   w.qp = c.take<uint16_t>(static_cast<size_t>(sh.recv_layers) * 2 * w.u_cap * sh.f_out);
   w.sigma = c.take<double>(static_cast<size_t>(sh.send_layers) * sh.row);
   w.sigma_part = c.take<double>(static_cast<size_t>(sh.send_layers) * SG_CHUNKS * sh.row);
+  if (sh.send_rope > 0.0) w.tab_send = c.take<float2>(static_cast<size_t>(sh.n_send) * (sh.send_hd / 2));
+  if (sh.recv_rope > 0.0) w.tab_recv = c.take<float2>(static_cast<size_t>(sh.n_recv) * (sh.recv_hd / 2));
   return w;
 }
 
@@ -1726,26 +1789,47 @@ static int gram_from_runs(const FitcShape& sh, const RunsWs& w, const void* cons
   g.keys = w.keys;
   g.dests = w.dests;
   g.n_keys = static_cast<int32_t>(keys.size());
+  if (sh.key_role >= 0 && sh.send_rope > 0.0)
+    if (int st = launch_rope_table(w.tab_send, sh.n_send, sh.send_hd, sh.send_rope, s)) return st;
+  if (sh.key_role >= 0 && sh.recv_rope > 0.0)
+    if (int st = launch_rope_table(w.tab_recv, sh.n_recv, sh.recv_hd, sh.recv_rope, s)) return st;
 
   // 2. per role: the distinct rows and the bit-group rows of every sender
   // layer, the run sums of the targets, then the Gram of all its problems
+  // (keys stored rotated are turned back on the way: the sender's at the
+  // sender position, the targets at the receiver position)
   const int cus = device_cu_count();
   for (int32_t r = 0; r < sh.n_roles; ++r) {
     const uint16_t* xs = static_cast<const uint16_t*>(send_role[r]);
     const uint16_t* ys = static_cast<const uint16_t*>(recv_role[r]);
+    const bool rot_x = r == sh.key_role && sh.send_rope > 0.0;
+    const bool rot_y = r == sh.key_role && sh.recv_rope > 0.0;
     const int64_t send_layer = static_cast<int64_t>(sh.n_send) * sh.row;
     const unsigned gx_u = static_cast<unsigned>(std::min<int64_t>(ceil_div(g.xu_layer / 8, 256), 4096));
-    fitc_gather_kernel<<<dim3(gx_u, static_cast<unsigned>(sh.send_layers)), 256, 0, s>>>(
-        xs, send_layer, sh.row, w.runs.uniq, nullptr, n_runs, u_pad, w.xu, g.xu_layer);
-    KVX_LAUNCH_CHECK();
     const unsigned gx_g = static_cast<unsigned>(std::min<int64_t>(ceil_div(g.xg_layer / 8, 256), 4096));
-    fitc_gather_kernel<<<dim3(gx_g, static_cast<unsigned>(sh.send_layers)), 256, 0, s>>>(
-        xs, send_layer, sh.row, w.runs.uniq, w.glist, 0, g.xg_rows, w.xg, g.xg_layer);
+    const dim3 grid_u(gx_u, static_cast<unsigned>(sh.send_layers)), grid_g(gx_g, static_cast<unsigned>(sh.send_layers));
+    if (rot_x) {
+      fitc_gather_kernel<true><<<grid_u, 256, 0, s>>>(xs, send_layer, sh.row, w.runs.uniq, nullptr, n_runs, u_pad,
+                                                      w.xu, g.xu_layer, w.tab_send, sh.send_hd);
+      fitc_gather_kernel<true><<<grid_g, 256, 0, s>>>(xs, send_layer, sh.row, w.runs.uniq, w.glist, 0, g.xg_rows,
+                                                      w.xg, g.xg_layer, w.tab_send, sh.send_hd);
+    } else {
+      fitc_gather_kernel<false><<<grid_u, 256, 0, s>>>(xs, send_layer, sh.row, w.runs.uniq, nullptr, n_runs, u_pad,
+                                                       w.xu, g.xu_layer, nullptr, 0);
+      fitc_gather_kernel<false><<<grid_g, 256, 0, s>>>(xs, send_layer, sh.row, w.runs.uniq, w.glist, 0, g.xg_rows,
+                                                       w.xg, g.xg_layer, nullptr, 0);
+    }
     KVX_LAUNCH_CHECK();
-    const unsigned gx_q =
-        static_cast<unsigned>(std::min<int64_t>(ceil_div(static_cast<int64_t>(u_pad) * sh.f_out / 8, 256), 4096));
-    fitc_target_sums_kernel<<<dim3(gx_q, static_cast<unsigned>(sh.recv_layers)), 256, 0, s>>>(
-        ys, static_cast<int64_t>(sh.n_recv) * sh.f_out, sh.f_out, w.runs.run_begin, n_runs, u_pad, w.qp, g.qp_layer);
+    const dim3 grid_q(
+        static_cast<unsigned>(std::min<int64_t>(ceil_div(static_cast<int64_t>(u_pad) * sh.f_out / 8, 256), 4096)),
+        static_cast<unsigned>(sh.recv_layers));
+    const int64_t y_layer = static_cast<int64_t>(sh.n_recv) * sh.f_out;
+    if (rot_y)
+      fitc_target_sums_kernel<true><<<grid_q, 256, 0, s>>>(ys, y_layer, sh.f_out, w.runs.run_begin, n_runs, u_pad,
+                                                           w.qp, g.qp_layer, w.tab_recv, sh.recv_hd);
+    else
+      fitc_target_sums_kernel<false><<<grid_q, 256, 0, s>>>(ys, y_layer, sh.f_out, w.runs.run_begin, n_runs, u_pad,
+                                                            w.qp, g.qp_layer, nullptr, 0);
     KVX_LAUNCH_CHECK();
     GramRunsArgs gr = g;
     const int64_t z0 = static_cast<int64_t>(r) * sh.recv_layers;
@@ -2218,6 +2302,7 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
 struct RccWs {
   RcWs rc;
   RunsWs r;
+  uint16_t* ybuf;  // a receiver layer's keys rotated back, when they are stored rotated
   size_t bytes;
 };
 
@@ -2227,6 +2312,7 @@ static RccWs recolor_caches_layout(const FitcShape& sh, void* base) {
   Carve c(base);
   c.used = w.rc.bytes;
   w.r = runs_layout(sh, c);
+  if (sh.recv_rope > 0.0) w.ybuf = c.take<uint16_t>(static_cast<size_t>(sh.n_recv) * sh.f_out);
   w.bytes = c.used + 256;
   return w;
 }
@@ -2247,6 +2333,16 @@ int launch_recolor_caches(const FitcShape& sh, const void* const* send_role, con
   for (int32_t z = 0; z < sh.count; ++z) {
     const uint16_t* y = static_cast<const uint16_t*>(recv_role[z / sh.recv_layers]) +
                         static_cast<int64_t>(z % sh.recv_layers) * sh.n_recv * sh.f_out;
+    if (z / sh.recv_layers == sh.key_role && sh.recv_rope > 0.0) {
+      // the targets' moments from the rows rotated back (the table was built
+      // for the run sums)
+      const unsigned gx = static_cast<unsigned>(
+          std::min<int64_t>(ceil_div(static_cast<int64_t>(sh.n_recv) * sh.f_out / 16, 256), 4096));
+      fitc_gather_kernel<true><<<dim3(gx, 1), 256, 0, s>>>(y, 0, sh.f_out, nullptr, nullptr, sh.n_recv, sh.n_recv,
+                                                           w.ybuf, 0, w.r.tab_recv, sh.recv_hd);
+      KVX_LAUNCH_CHECK();
+      y = w.ybuf;
+    }
     double* G = rc.G + z * bs;
     double* C = rc.C + z * bs;
     double* Gy = rc.Gy + z * bs;

@@ -23,6 +23,12 @@ struct FitcShape {
   int32_t send_layers, n_send, row;        // sender: layers, tokens, H_S d_S (a multiple of 256)
   int32_t recv_layers, n_recv, f_out;      // receiver: layers, tokens, H_R d_R
   int32_t n_taps, f_in, n_roles, count;    // f_in = n_taps row, count = n_roles recv_layers
+  // keys stored rotated (base > 0): the sender's rotated back at the sender
+  // position, the receiver's (the targets) at the receiver position; head
+  // dims for the pairs (c, c + d/2); key_role = index of the key role among
+  // the roles fitted, or -1
+  double send_rope, recv_rope;
+  int32_t send_hd, recv_hd, key_role;
 };
 size_t fitc_ws_bytes(const FitcShape& sh);
 // the most rows a per-layer operand of the Gram can have (for the 32-bit

@@ -557,7 +557,7 @@ class _CacheFit:
     """Arguments shared by the fits from the caches: the descriptors, the
     per-role pointers (null for a role not requested) and the shapes."""
 
-    def __init__(self, k_send, v_send, k_recv, v_recv, taps, roles):
+    def __init__(self, k_send, v_send, k_recv, v_recv, taps, roles, send_rope=0.0, recv_rope=0.0):
         taps = np.ascontiguousarray(taps, dtype=np.int32)
         if taps.ndim != 2:
             raise ValueError("taps must be [L_R][n_taps]")
@@ -568,7 +568,7 @@ class _CacheFit:
             raise ValueError("roles must name k, v or both")
         ref_send = k_send if self.do_k else v_send
         ref_recv = k_recv if self.do_k else v_recv
-        self.send, self.recv = cache_desc(ref_send), cache_desc(ref_recv)
+        self.send, self.recv = cache_desc(ref_send, send_rope), cache_desc(ref_recv, recv_rope)
         if self.recv.layers != self.L_R:
             raise ValueError("taps rows must equal the receiver's layers")
         for t in (k_send, v_send, k_recv, v_recv):
@@ -592,16 +592,18 @@ class _CacheFit:
 def fit_ridge_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Tensor], k_recv: Optional[torch.Tensor],
                      v_recv: Optional[torch.Tensor], recv_to_send: torch.Tensor, taps, *, lambda_abs: float = 0.0,
                      lambda_rel: float = 0.0, w_k: Optional[torch.Tensor] = None, w_v: Optional[torch.Tensor] = None,
-                     roles=("k", "v"), workspace: Optional[torch.Tensor] = None, stream=None,
-                     status: Optional[list] = None):
+                     roles=("k", "v"), send_rope: float = 0.0, recv_rope: float = 0.0,
+                     workspace: Optional[torch.Tensor] = None, stream=None, status: Optional[list] = None):
     """kvx_fit_ridge_caches: the ridge maps of every receiver layer of the
     requested ``roles`` from the calibration caches (bf16 [L][N][H][d]; the
     sender's N_S tokens, the receiver's N), the alignment ``recv_to_send``
     (device int32 [N]) and ``taps`` (host int32 [L_R][n_taps]).  Returns
     (w_k, w_v), fp32 [L_R][F_in][F_out] (None for a role not requested).
+    ``send_rope`` / ``recv_rope`` > 0: the keys are stored rotated with that
+    base (turned back at the sender / receiver position before the fit).
     With a list ``status``, appends the [2][L_R] per-problem statuses and
     raises only for other errors."""
-    a = _CacheFit(k_send, v_send, k_recv, v_recv, taps, roles)
+    a = _CacheFit(k_send, v_send, k_recv, v_recv, taps, roles, send_rope, recv_rope)
     w_k = a.out(w_k, a.do_k, (a.L_R, a.f_in, a.f_out))
     w_v = a.out(w_v, a.do_v, (a.L_R, a.f_in, a.f_out))
     ws = _workspace(fit_ridge_caches_workspace_size(a.send, a.recv, a.n_taps), a.dev, workspace)
@@ -627,9 +629,9 @@ def fit_recolor_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Te
                        k_recv: Optional[torch.Tensor], v_recv: Optional[torch.Tensor], recv_to_send: torch.Tensor,
                        taps, *, rho_x: float = 0.0, rho_y: float = 0.0, w_k: Optional[torch.Tensor] = None,
                        w_v: Optional[torch.Tensor] = None, b_k: Optional[torch.Tensor] = None,
-                       b_v: Optional[torch.Tensor] = None, roles=("k", "v"),
-                       workspace: Optional[torch.Tensor] = None, stream=None, status: Optional[list] = None,
-                       info: Optional[dict] = None):
+                       b_v: Optional[torch.Tensor] = None, roles=("k", "v"), send_rope: float = 0.0,
+                       recv_rope: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None,
+                       status: Optional[list] = None, info: Optional[dict] = None):
     """kvx_fit_recolor_caches: the Recolor maps of every receiver layer of
     the requested ``roles`` from the calibration caches, arguments as for
     fit_ridge_caches.  Returns (w_k, w_v, b_k, b_v): fp32 [L_R][F_in][F_out]
@@ -637,7 +639,7 @@ def fit_recolor_caches(k_send: Optional[torch.Tensor], v_send: Optional[torch.Te
     ``status``, appends the [2][L_R] per-problem statuses and raises only for
     other errors; with a dict ``info``, stores the polar iterations under
     "iters"."""
-    a = _CacheFit(k_send, v_send, k_recv, v_recv, taps, roles)
+    a = _CacheFit(k_send, v_send, k_recv, v_recv, taps, roles, send_rope, recv_rope)
     w_k = a.out(w_k, a.do_k, (a.L_R, a.f_in, a.f_out))
     w_v = a.out(w_v, a.do_v, (a.L_R, a.f_in, a.f_out))
     b_k = a.out(b_k, a.do_k, (a.L_R, a.f_out))

@@ -375,10 +375,18 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
  *     products).
  *
  * send, k_send, v_send: the sender's calibration caches [L_S][N_S][H_S][d_S]
- *   (bf16, rope_base 0: features are the rows as stored), 16-byte aligned.
+ *   (bf16, 16-byte aligned).  With send->rope_base > 0 the keys are stored
+ *   rotated: each key row is rotated back at its sender position (its token
+ *   index; pairs (c, c + d/2), fp32 from an fp64-derived table) and rounded
+ *   to bf16, as kvx_gather_features does (the fit then equals the fit on
+ *   those rounded features; the rounding is a 2^-9 relative perturbation of
+ *   the inputs that an ill-conditioned system amplifies); d_S must then be a
+ *   multiple of 16.  Values are never rotated.
  * recv, k_recv, v_recv: the receiver's calibration caches [L_R][N][H_R][d_R]
- *   (bf16, rope_base 0, 16-byte aligned), the targets of each receiver
- *   layer; N = recv->tokens.
+ *   (bf16, 16-byte aligned), the targets of each receiver layer;
+ *   N = recv->tokens.  With recv->rope_base > 0 the target keys are rotated
+ *   back at the receiver position before they are summed (fp32); d_R must
+ *   then be a multiple of 16.
  * recv_to_send: device int32 [N], the calibration alignment (values clamped
  *   into [0, N_S) as in kvx_translate).
  * taps: host int32 [L_R][n_taps] from kvx_layer_map; the features of
@@ -394,10 +402,11 @@ int kvx_fit_ridge_batched(int32_t count, const void* const* x, int64_t ldx, cons
  * workspace: kvx_fit_ridge_caches_workspace_size(send, recv, n_taps) bytes
  *   (sized for the worst case of N runs of one token: the fp64 systems of
  *   2 L_R problems plus, for one role at a time, the distinct sender rows of
- *   every sender layer, twice, and the receiver's run sums).
+ *   every sender layer, twice, and the receiver's run sums; with rotated
+ *   keys also the (cos, sin) tables of the positions).
  * Synchronises `stream` twice (the run lengths, the factorisation flags).
- * KVX_ERR_UNSUPPORTED for other dtypes, rotated caches or shapes; otherwise
- * errors as kvx_fit_ridge_batched.
+ * KVX_ERR_UNSUPPORTED for other dtypes or shapes; otherwise errors as
+ * kvx_fit_ridge_batched.
  * ---------------------------------------------------------------------- */
 size_t kvx_fit_ridge_caches_workspace_size(const kvx_cache_desc* send, const kvx_cache_desc* recv,
                                            int32_t n_taps);
@@ -616,7 +625,8 @@ int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void
  *   polar iterations run.
  * workspace: kvx_fit_recolor_caches_workspace_size(send, recv, n_taps)
  *   bytes (worst case, as for kvx_fit_ridge_caches, plus the Recolor solve's
- *   per-problem matrices).
+ *   per-problem matrices and, with rotated receiver keys, one layer of them
+ *   rotated back for Y^T Y).
  * Synchronises `stream` once for the run lengths and once per polar
  * iteration.  Returns the first non-OK problem status, else KVX_OK; argument
  * errors as kvx_fit_ridge_caches.

@@ -512,8 +512,14 @@ static void check_fit_from_caches(const int32_t* taps36) {
   bad[95] = 36;
   EXPECT_EQ(FC(&s, &r, FAKE, FAKE, FAKE, bad, 3, 1e-3, w, w, huge_ws), KVX_ERR_INVALID);
   free(bad);
-  kvx_cache_desc srot = desc(36, 50000, 8, 128, KVX_BF16, 1e4);
+  /* rotated keys are turned back 8 pairs at a time: head_dim a multiple of 16 */
+  kvx_cache_desc srot = desc(36, 50000, 32, 8, KVX_BF16, 1e4), rrot = desc(32, 65536, 32, 8, KVX_BF16, 1e6);
   EXPECT_EQ(FC(&srot, &r, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+  EXPECT_EQ(FC(&s, &rrot, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
+  /* workspace sizes grow by the (cos, sin) tables of rotated keys */
+  kvx_cache_desc s_rope = desc(36, 50000, 8, 128, KVX_BF16, 1e4);
+  EXPECT(kvx_fit_ridge_caches_workspace_size(&s_rope, &r, 3) >= kvx_fit_ridge_caches_workspace_size(&s, &r, 3) +
+                                                                    (size_t)50000 * 64 * 8);
   kvx_cache_desc snarrow = desc(36, 50000, 3, 64, KVX_BF16, 0.0);
   EXPECT_EQ(FC(&snarrow, &r, FAKE, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);
   EXPECT_EQ(FC(&s, &r, (void*)(uintptr_t)0x1008, FAKE, FAKE, taps36, 3, 1e-3, w, w, huge_ws), KVX_ERR_UNSUPPORTED);

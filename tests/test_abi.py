@@ -249,7 +249,9 @@ def test_fit_from_caches_validation():
     bad = taps.copy()
     bad[5, 2] = 36
     assert call(taps_p=bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == kvx.ERR_INVALID
-    assert call(sd=desc(36, 50000, 8, 128, rope=1e4)) == kvx.ERR_UNSUPPORTED   # rotated keys
+    # rotated keys are turned back 8 pairs at a time: head_dim a multiple of 16
+    assert call(sd=desc(36, 50000, 32, 8, rope=1e4)) == kvx.ERR_UNSUPPORTED
+    assert call(rd=desc(32, 65536, 32, 8, rope=1e6)) == kvx.ERR_UNSUPPORTED
     assert call(sd=desc(36, 50000, 8, 128, kvx.F32), rd=desc(32, 65536, 8, 128, kvx.F32)) == kvx.ERR_UNSUPPORTED
     assert call(sd=desc(36, 50000, 3, 64)) == kvx.ERR_UNSUPPORTED    # sender rows not a multiple of 256
     assert call(ks=ctypes.c_void_p(0x1008)) == kvx.ERR_UNSUPPORTED  # 16-byte pieces
@@ -284,7 +286,7 @@ def test_recolor_from_caches_validation():
     assert call(ks=None) == kvx.ERR_INVALID
     assert call(m=None) == kvx.ERR_INVALID
     assert call(taps_p=None) == kvx.ERR_INVALID
-    assert call(sd=desc(36, 50000, 8, 128, rope=1e4)) == kvx.ERR_UNSUPPORTED
+    assert call(sd=desc(36, 50000, 32, 8, rope=1e4)) == kvx.ERR_UNSUPPORTED
     assert call(sd=desc(36, 50000, 3, 64)) == kvx.ERR_UNSUPPORTED
     # F_in < F_out: one tap of a 2 x 128 sender row against 8 x 128 targets
     one = np.zeros((32, 1), dtype=np.int32)

@@ -28,6 +28,10 @@ every W and b:
 * one role alone, a constant receiver column with rho_y 0 (not positive
   definite for that problem only) and, on a map with fewer distinct sender
   rows than outputs, every problem reported not converged.
+
+Both fits: receiver rows of 3 heads x 64 (a partial output tile), and keys
+stored rotated (rotated back at the sender and receiver positions) against
+the oracle and the features path.
 """
 import sys
 
@@ -252,3 +256,75 @@ def test_recolor_caches_one_role_and_statuses():
     kvx.fit_recolor_caches(ks, None, kr, None, dev_i32(tmap_h), d["taps"], rho_x=RHO_X, roles=("k",), status=st)
     torch.cuda.synchronize()
     assert st == [kvx.ERR_NOT_CONVERGED] * L_R + [kvx.OK] * L_R, st
+
+
+def test_fit_caches_ragged_output_width():
+    """Receiver rows of 3 heads x 64 (F_out = 192: a partial 256-wide output
+    tile) from sender rows of 2 x 128 at taps -2/0/+2 (F_in = 768): both fits
+    from the caches vs the oracle, every element."""
+    n = 3000
+    send_end, recv_end = synth.token_ends(n, 41)
+    d = {"taps": kvx.layer_map(6, 4, 3, 2), "tmap": kvx.align_tokens(dev_i32(send_end), dev_i32(recv_end)),
+         "tmap_o": O.token_align(send_end, recv_end)}
+    for r, role in enumerate(("k", "v")):
+        d[f"{role}_send"] = synth.sender_cache(synth.CacheShape(6, len(send_end), 2, 128), 410 + r, DEV)
+        d[f"{role}_recv"] = synth.receiver_cache(synth.CacheShape(4, n, 3, 64), 415 + r, DEV)
+    wk, wv = kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                                  lambda_rel=LAM_REL)
+    st = []
+    rk, rv, bk, bv = kvx.fit_recolor_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"],
+                                            d["taps"], rho_x=RHO_X, status=st)
+    torch.cuda.synchronize()
+    assert wk.shape == (4, 768, 192) and bk.shape == (4, 192)
+    assert st == [kvx.OK] * 8, st
+    for role, w, rw, rb in (("k", wk, rk, bk), ("v", wv, rv, bv)):
+        for l in range(4):
+            err = O.rel_err(w[l].cpu().numpy().astype(np.float64), oracle_fit(d, role, l, d["tmap_o"]))
+            ew, eb = recolor_err(rw[l], rb[l], *oracle_recolor(d, role, l, d["tmap_o"]))
+            say(f"  F_out 192, {role} layer {l}: ridge {err:.3e}, Recolor W {ew:.3e} b {eb:.3e}")
+            assert err <= TOL_BF16 and ew <= TOL_BF16 and eb <= TOL_BF16
+
+
+def test_fits_from_rotated_caches():
+    """Keys stored rotated (sender base 1e4, receiver base 1e6) in the
+    two-head setting at 8192 tokens (about 1860 distinct sender rows for 768
+    features): the key rows are rotated back at the sender positions and,
+    like the features kvx_gather_features writes, rounded to bf16 for the
+    matrix cores; the target keys are rotated back at the receiver positions
+    and summed in fp32.  So both fits are checked, every element, against
+    the oracle fitted on the features rotated back in fp64 and rounded
+    fp64 -> fp32 -> bf16 (a rounding taken in a different precision than the
+    kernel's only where the fp32 rotation lands within 2^-24 of a bf16
+    rounding boundary: a few elements in 10^5, each one bf16 step) and the
+    targets rotated back in fp64; the value maps (never rotated) as without
+    rotation; and the key maps against the features path fed the rows
+    kvx_gather_features rotates back (which also rounds the targets)."""
+    n = 8192
+    sb, rb = 1e4, 1e6
+    d = small_setting(n, 43)
+    L_R = d["taps"].shape[0]
+    wk, wv = kvx.fit_ridge_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"], d["taps"],
+                                  lambda_rel=LAM_REL, send_rope=sb, recv_rope=rb)
+    st = []
+    rk, rv, bk, bv = kvx.fit_recolor_caches(d["k_send"], d["v_send"], d["k_recv"], d["v_recv"], d["tmap"],
+                                            d["taps"], rho_x=RHO_X, send_rope=sb, recv_rope=rb, status=st)
+    torch.cuda.synchronize()
+    assert st == [kvx.OK] * (2 * L_R), st
+    ident = dev_i32(np.arange(n))
+    xs = [kvx.gather_features(d["k_send"], d["tmap"], d["taps"][l], derotate=True, rope_base=sb) for l in range(L_R)]
+    ys = [kvx.gather_features(d["k_recv"], ident, [l], derotate=True, rope_base=rb) for l in range(L_R)]
+    wf, _ = kvx.fit_ridge_batched(xs, ys, lambda_rel=LAM_REL)
+    for l in range(L_R):
+        x = O.features(d["k_send"], d["tmap_o"], d["taps"][l], derotate_base=sb)
+        x = O.bf16_bits_to_f64(O.f32_to_bf16_bits(x.astype(np.float32)))
+        y = O.rope_rotate(O.as_f64(d["k_recv"][l]), np.arange(n), rb, -1).reshape(n, -1)
+        err = O.rel_err(wk[l].cpu().numpy().astype(np.float64), O.ridge_fit(x, y, lam_rel=LAM_REL)[0])
+        gap = O.rel_err(wk[l].cpu().numpy().astype(np.float64), wf[l].cpu().numpy().astype(np.float64))
+        ew, eb = recolor_err(rk[l], bk[l], *O.recolor_fit(x, y, rho_x=RHO_X))
+        ev = O.rel_err(wv[l].cpu().numpy().astype(np.float64), oracle_fit(d, "v", l, d["tmap_o"]))
+        evr, ebr = recolor_err(rv[l], bv[l], *oracle_recolor(d, "v", l, d["tmap_o"]))
+        say(f"  rotated keys, layer {l}: ridge K {err:.3e} (features path {gap:.3e}), Recolor K W {ew:.3e} "
+            f"b {eb:.3e}; V ridge {ev:.3e}, Recolor {evr:.3e} / {ebr:.3e}")
+        assert max(err, ew, eb, ev, evr, ebr) <= TOL_BF16
+        # the features path also rounds the rotated-back targets to bf16
+        assert gap <= TOL_BF16
