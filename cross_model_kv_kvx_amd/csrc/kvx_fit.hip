@@ -45,7 +45,10 @@ struct GramArgs {
   const uint16_t* y;
   int64_t ldx, ldy, n_rows, rows_per_split;
   int32_t f_in, f_out, nbi, nbc, n_g, n_c, split;
-  float* part;  // [split][f_in][f_in + f_out]
+  float* part;  // [batch][split][f_in][f_in + f_out]
+  // problems of one launch: x, y and part of problem b at b times these
+  int32_t batch;
+  int64_t x_batch, y_batch;
 };
 
 // G = X^T X (tiles on and above the diagonal) and C = X^T Y over row splits,
@@ -183,7 +186,8 @@ gram_kernel(const GramArgs g) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;
   const int32_t per = g.n_g + g.n_c;
-  const int64_t T = static_cast<int64_t>(g.split) * per;
+  const int64_t per_prob = static_cast<int64_t>(g.split) * per;
+  const int64_t T = g.batch * per_prob;
   const int32_t G = gridDim.x;
   // consecutive items go to the workgroups of one XCD (dispatch is round
   // robin over the 8 XCDs)
@@ -191,8 +195,11 @@ gram_kernel(const GramArgs g) {
   const int64_t ldp = static_cast<int64_t>(g.f_in) + g.f_out;
 
   for (int64_t t = slot; t < T; t += G) {
-    const int32_t sidx = static_cast<int32_t>(t / per);
-    int32_t tt = static_cast<int32_t>(t % per);
+    const int64_t prob = t / per_prob;
+    const int32_t sidx = static_cast<int32_t>((t % per_prob) / per);
+    int32_t tt = static_cast<int32_t>((t % per_prob) % per);
+    const uint16_t* gx = g.x + prob * g.x_batch;
+    const uint16_t* gy = g.y + prob * g.y_batch;
     int32_t bi, bj;
     bool is_c;
     if (tt < g.n_g) {  // upper-triangle tile index -> (bi, bj), bi <= bj
@@ -216,7 +223,7 @@ gram_kernel(const GramArgs g) {
     if (rows > g.rows_per_split) rows = g.rows_per_split;
     if (rows < 0) rows = 0;
     const int32_t i0 = bi * GR_T, j0 = bj * GR_T;
-    const uint16_t* q = is_c ? g.y : g.x;
+    const uint16_t* q = is_c ? gy : gx;
     const int64_t ldq = is_c ? g.ldy : g.ldx;
     const int32_t fq = is_c ? g.f_out : g.f_in;
 
@@ -225,7 +232,7 @@ gram_kernel(const GramArgs g) {
     it.q_pitch = static_cast<uint32_t>(2 * ldq);
     // the range ends with the split's last row (features past the row's end
     // come from the next row and only reach outputs that are not written)
-    it.pr = buf_rsrc(g.x + k_begin * g.ldx + i0, static_cast<uint32_t>(rows * 2 * g.ldx - 2 * i0));
+    it.pr = buf_rsrc(gx + k_begin * g.ldx + i0, static_cast<uint32_t>(rows * 2 * g.ldx - 2 * i0));
     it.qr = buf_rsrc(q + k_begin * ldq + j0, static_cast<uint32_t>(rows * 2 * ldq - 2 * j0));
     if (rows == 0) {
       it.pr = buf_rsrc(nullptr, 0);
@@ -274,7 +281,7 @@ gram_kernel(const GramArgs g) {
       KVX_WAIT_VM(0);
     }
 
-    float* part = g.part + static_cast<int64_t>(sidx) * g.f_in * ldp + (is_c ? g.f_in : 0);
+    float* part = g.part + (prob * g.split + sidx) * g.f_in * ldp + (is_c ? g.f_in : 0);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -731,8 +738,13 @@ static int colsum(const void* m, int64_t ld, int64_t n_rows, int32_t cols, int32
 constexpr int RD_T = 64;
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int32_t split,
                                                           int32_t f_in, int32_t f_out, double* __restrict__ G,
-                                                          double* __restrict__ C) {
+                                                          double* __restrict__ C, int64_t bs) {
   __shared__ double tr[RD_T][RD_T + 1];
+  // problem blockIdx.y: its split partials follow the previous problem's,
+  // its G and C sit bs doubles after the previous problem's
+  part += static_cast<int64_t>(blockIdx.y) * split * f_in * (static_cast<int64_t>(f_in) + f_out);
+  G += static_cast<int64_t>(blockIdx.y) * bs;
+  if (C) C += static_cast<int64_t>(blockIdx.y) * bs;
   const int32_t nbi = (f_in + RD_T - 1) / RD_T;
   const int32_t nbc = (f_out + RD_T - 1) / RD_T;
   const int32_t n_g = nbi * (nbi + 1) / 2;
@@ -785,10 +797,16 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
   }
 }
 
-// Centring: G -= sx sx^T / n, C -= sx sy^T / n.
+// Centring: G -= sx sx^T / n, C -= sx sy^T / n; problem blockIdx.y has its
+// G, C, sx and sy bs doubles after the previous problem's.
 __global__ __launch_bounds__(256) void center_kernel(double* __restrict__ G, double* __restrict__ C,
                                                      const double* __restrict__ sx, const double* __restrict__ sy,
-                                                     int32_t f_in, int32_t f_out, double inv_n) {
+                                                     int32_t f_in, int32_t f_out, double inv_n, int64_t bs) {
+  const int64_t z = static_cast<int64_t>(blockIdx.y) * bs;
+  G += z;
+  sx += z;
+  sy += z;
+  if (C) C += z;
   const int64_t ld = static_cast<int64_t>(f_in) + f_out;
   const int64_t total = static_cast<int64_t>(f_in) * ld;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
@@ -1434,17 +1452,28 @@ static int chol_backward(hipStream_t s, int32_t count, const double* A, int32_t 
                                  : chol_backward_right(s, count, A, n, bs, xinv, zbuf, C, nrhs);
 }
 
-static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32, int64_t n_rows,
-                    int32_t f_in, int32_t f_out, float* part, double* G, double* C, hipStream_t s) {
-  if (in_f32) {
-    gram_f32_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(
-        static_cast<const float*>(x), ldx, static_cast<const float*>(y), ldy, n_rows, f_in, f_out, G, C);
-    KVX_LAUNCH_CHECK();
+// The Grams of `batch` problems of one shape from bf16 rows, in as few
+// launches as the partials' room allows: problem b reads x + b x_batch and
+// y + b y_batch (f_out = 0: X^T X only) and writes its G and C b bs doubles
+// after problem 0's; `part` has room for part_cap floats of split partials.
+static int gram_batch(const uint16_t* x, int64_t ldx, int64_t x_batch, const uint16_t* y, int64_t ldy,
+                      int64_t y_batch, int64_t n_rows, int32_t f_in, int32_t f_out, int32_t batch, float* part,
+                      int64_t part_cap, double* G, double* C, int64_t bs, hipStream_t s) {
+  const int64_t per_split = static_cast<int64_t>(f_in) * (static_cast<int64_t>(f_in) + f_out);
+  const int64_t fit = part_cap / per_split;  // problems whose single-split partials fit at once
+  if (fit < 1) return KVX_ERR_WORKSPACE;
+  if (batch > fit) {
+    for (int32_t b0 = 0; b0 < batch; b0 += static_cast<int32_t>(fit)) {
+      const int32_t nb = static_cast<int32_t>(std::min<int64_t>(fit, batch - b0));
+      if (int st = gram_batch(x + b0 * x_batch, ldx, x_batch, y ? y + b0 * y_batch : nullptr, ldy, y_batch, n_rows,
+                              f_in, f_out, nb, part, part_cap, G + b0 * bs, C ? C + b0 * bs : nullptr, bs, s))
+        return st;
+    }
     return KVX_OK;
   }
   GramArgs g{};
-  g.x = static_cast<const uint16_t*>(x);
-  g.y = static_cast<const uint16_t*>(y);
+  g.x = x;
+  g.y = y;
   g.ldx = ldx;
   g.ldy = ldy;
   g.n_rows = n_rows;
@@ -1454,13 +1483,18 @@ static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int3
   g.nbc = static_cast<int32_t>(ceil_div(f_out, GR_T));
   g.n_g = g.nbi * (g.nbi + 1) / 2;
   g.n_c = g.nbi * g.nbc;
+  g.batch = batch;
+  g.x_batch = x_batch;
+  g.y_batch = y_batch;
   // row splits: the fewest that fill the persistent grid best (fewer
-  // partials to add up, longer K loops), each at least one step long
+  // partials to add up, longer K loops), each at least one step long, as
+  // many as the partials' room holds
   const int cus = device_cu_count();
-  const int64_t tiles = g.n_g + g.n_c;
+  const int64_t tiles = static_cast<int64_t>(batch) * (g.n_g + g.n_c);
+  const int64_t cap_split = std::min<int64_t>(GR_MAX_SPLIT, part_cap / (per_split * batch));
   int64_t split = 1;
   double best = 0.0;
-  for (int64_t sp = 1; sp <= GR_MAX_SPLIT; ++sp) {
+  for (int64_t sp = 1; sp <= cap_split; ++sp) {
     const int64_t items = sp * tiles;
     const double eff = static_cast<double>(items) / static_cast<double>(ceil_div(items, cus) * cus);
     if (eff > best + 1e-9) {
@@ -1480,13 +1514,24 @@ static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int3
   const unsigned grid = static_cast<unsigned>(items < cus ? items : cus);
   gram_kernel<<<grid, GR_THREADS, 0, s>>>(g);
   KVX_LAUNCH_CHECK();
-  {
-    const int64_t nbi = ceil_div(f_in, RD_T), nbc = ceil_div(f_out, RD_T);
-    gram_reduce_kernel<<<static_cast<unsigned>(nbi * (nbi + 1) / 2 + nbi * nbc), 256, 0, s>>>(part, g.split, f_in,
-                                                                                               f_out, G, C);
-  }
+  const int64_t nbi = ceil_div(f_in, RD_T), nbc = ceil_div(f_out, RD_T);
+  gram_reduce_kernel<<<dim3(static_cast<unsigned>(nbi * (nbi + 1) / 2 + nbi * nbc), static_cast<unsigned>(batch)),
+                       256, 0, s>>>(part, g.split, f_in, f_out, G, C, bs);
   KVX_LAUNCH_CHECK();
   return KVX_OK;
+}
+
+static int gram_one(const void* x, int64_t ldx, const void* y, int64_t ldy, int32_t in_f32, int64_t n_rows,
+                    int32_t f_in, int32_t f_out, float* part, double* G, double* C, hipStream_t s) {
+  if (in_f32) {
+    gram_f32_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(
+        static_cast<const float*>(x), ldx, static_cast<const float*>(y), ldy, n_rows, f_in, f_out, G, C);
+    KVX_LAUNCH_CHECK();
+    return KVX_OK;
+  }
+  return gram_batch(static_cast<const uint16_t*>(x), ldx, 0, static_cast<const uint16_t*>(y), ldy, 0, n_rows, f_in,
+                    f_out, 1, part, static_cast<int64_t>(GR_MAX_SPLIT) * f_in * (static_cast<int64_t>(f_in) + f_out),
+                    G, C, 0, s);
 }
 
 int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* const* y, int64_t ldy, int32_t in_f32,
@@ -1508,7 +1553,7 @@ int launch_fit(int32_t count, const void* const* x, int64_t ldx, const void* con
       if (int st = colsum(x[z], ldx, n_rows, f_in, in_f32, w.csp, sx, s)) return st;
       if (int st = colsum(y[z], ldy, n_rows, f_out, in_f32, w.csp, sy, s)) return st;
       center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
-                                                                                          inv_n);
+                                                                                          inv_n, 0);
       KVX_LAUNCH_CHECK();
     }
     lambda_kernel<<<1, 256, 0, s>>>(G, f_in, lam_abs, lam_rel, w.lam + z * bs);
@@ -2175,8 +2220,8 @@ int launch_recolor(int32_t count, const void* const* x, int64_t ldx, const void*
     if (int st = colsum(x[z], ldx, n_rows, f_in, in_f32, w.csp, sx, s)) return st;
     if (int st = colsum(y[z], ldy, n_rows, f_out, in_f32, w.csp, sy, s)) return st;
     center_kernel<<<grid_for(static_cast<int64_t>(f_in) * (f_in + f_out)), 256, 0, s>>>(G, C, sx, sy, f_in, f_out,
-                                                                                        inv_n);
-    center_kernel<<<grid_for(fo2), 256, 0, s>>>(Gy, nullptr, sy, sy, f_out, 0, inv_n);
+                                                                                        inv_n, 0);
+    center_kernel<<<grid_for(fo2), 256, 0, s>>>(Gy, nullptr, sy, sy, f_out, 0, inv_n, 0);
     KVX_LAUNCH_CHECK();
     lambda_kernel<<<1, 256, 0, s>>>(G, f_in, 0.0, rho_x, w.lam + z * bs);
     lambda_kernel<<<1, 256, 0, s>>>(Gy, f_out, 0.0, rho_y, w.lam + z * bs + 1);
@@ -2330,34 +2375,47 @@ int launch_recolor_caches(const FitcShape& sh, const void* const* send_role, con
   if (int st = gram_from_runs(sh, w.r, send_role, recv_role, map, taps_host, rc.G, rc.C, rc.sx, bs, s)) return st;
   const double inv_n = 1.0 / static_cast<double>(sh.n_recv);
   const int64_t fo2 = static_cast<int64_t>(sh.f_out) * sh.f_out;
-  for (int32_t z = 0; z < sh.count; ++z) {
-    const uint16_t* y = static_cast<const uint16_t*>(recv_role[z / sh.recv_layers]) +
-                        static_cast<int64_t>(z % sh.recv_layers) * sh.n_recv * sh.f_out;
-    if (z / sh.recv_layers == sh.key_role && sh.recv_rope > 0.0) {
-      // the targets' moments from the rows rotated back (the table was built
-      // for the run sums)
-      const unsigned gx = static_cast<unsigned>(
-          std::min<int64_t>(ceil_div(static_cast<int64_t>(sh.n_recv) * sh.f_out / 16, 256), 4096));
-      fitc_gather_kernel<true><<<dim3(gx, 1), 256, 0, s>>>(y, 0, sh.f_out, nullptr, nullptr, sh.n_recv, sh.n_recv,
-                                                           w.ybuf, 0, w.r.tab_recv, sh.recv_hd);
-      KVX_LAUNCH_CHECK();
-      y = w.ybuf;
+  // the targets' moments: Y^T Y of a role's layers in batched Gram launches,
+  // the column sums per layer; target keys stored rotated are rotated back
+  // one layer at a time first (the table was built for the run sums)
+  const int64_t part_cap = static_cast<int64_t>(GR_MAX_SPLIT) * sh.f_in * (static_cast<int64_t>(sh.f_in) + sh.f_out);
+  const int64_t y_layer = static_cast<int64_t>(sh.n_recv) * sh.f_out;
+  for (int32_t r = 0; r < sh.n_roles; ++r) {
+    const uint16_t* yr = static_cast<const uint16_t*>(recv_role[r]);
+    const int64_t z0 = static_cast<int64_t>(r) * sh.recv_layers;
+    const bool rot = r == sh.key_role && sh.recv_rope > 0.0;
+    if (!rot) {
+      if (int st = gram_batch(yr, sh.f_out, y_layer, yr, sh.f_out, y_layer, sh.n_recv, sh.f_out, 0, sh.recv_layers,
+                              rc.part, part_cap, rc.Gy + z0 * bs, nullptr, bs, s))
+        return st;
     }
-    double* G = rc.G + z * bs;
-    double* C = rc.C + z * bs;
-    double* Gy = rc.Gy + z * bs;
-    double* sx = rc.sx + z * bs;
-    double* sy = rc.sy + z * bs;
-    if (int st = gram_one(y, sh.f_out, y, sh.f_out, 0, sh.n_recv, sh.f_out, 0, rc.part, Gy, nullptr, s)) return st;
-    if (int st = colsum(y, sh.f_out, sh.n_recv, sh.f_out, 0, rc.csp, sy, s)) return st;
-    center_kernel<<<grid_for(static_cast<int64_t>(sh.f_in) * (sh.f_in + sh.f_out)), 256, 0, s>>>(
-        G, C, sx, sy, sh.f_in, sh.f_out, inv_n);
-    center_kernel<<<grid_for(fo2), 256, 0, s>>>(Gy, nullptr, sy, sy, sh.f_out, 0, inv_n);
-    KVX_LAUNCH_CHECK();
-    lambda_kernel<<<1, 256, 0, s>>>(G, sh.f_in, 0.0, rho_x, rc.lam + z * bs);
-    lambda_kernel<<<1, 256, 0, s>>>(Gy, sh.f_out, 0.0, rho_y, rc.lam + z * bs + 1);
-    KVX_LAUNCH_CHECK();
+    for (int32_t l = 0; l < sh.recv_layers; ++l) {
+      const uint16_t* y = yr + l * y_layer;
+      const int64_t z = z0 + l;
+      if (rot) {
+        const unsigned gx =
+            static_cast<unsigned>(std::min<int64_t>(ceil_div(y_layer / 16, 256), 4096));
+        fitc_gather_kernel<true><<<dim3(gx, 1), 256, 0, s>>>(y, 0, sh.f_out, nullptr, nullptr, sh.n_recv, sh.n_recv,
+                                                             w.ybuf, 0, w.r.tab_recv, sh.recv_hd);
+        KVX_LAUNCH_CHECK();
+        y = w.ybuf;
+        if (int st = gram_one(y, sh.f_out, y, sh.f_out, 0, sh.n_recv, sh.f_out, 0, rc.part, rc.Gy + z * bs, nullptr,
+                              s))
+          return st;
+      }
+      if (int st = colsum(y, sh.f_out, sh.n_recv, sh.f_out, 0, rc.csp, rc.sy + z * bs, s)) return st;
+    }
   }
+  // centring and the regularisers of every problem at once
+  center_kernel<<<dim3(grid_for(static_cast<int64_t>(sh.f_in) * (sh.f_in + sh.f_out)),
+                       static_cast<unsigned>(sh.count)),
+                  256, 0, s>>>(rc.G, rc.C, rc.sx, rc.sy, sh.f_in, sh.f_out, inv_n, bs);
+  center_kernel<<<dim3(grid_for(fo2), static_cast<unsigned>(sh.count)), 256, 0, s>>>(rc.Gy, nullptr, rc.sy, rc.sy,
+                                                                                    sh.f_out, 0, inv_n, bs);
+  KVX_LAUNCH_CHECK();
+  lambda_batched_kernel<<<static_cast<unsigned>(sh.count), 256, 0, s>>>(rc.G, bs, sh.f_in, 0.0, rho_x, rc.lam);
+  lambda_batched_kernel<<<static_cast<unsigned>(sh.count), 256, 0, s>>>(rc.Gy, bs, sh.f_out, 0.0, rho_y, rc.lam + 1);
+  KVX_LAUNCH_CHECK();
   std::vector<float*> w_out(static_cast<size_t>(sh.count)), b_out(static_cast<size_t>(sh.count));
   const int64_t nw = static_cast<int64_t>(sh.f_in) * sh.f_out;
   for (int32_t z = 0; z < sh.count; ++z) {
