@@ -682,10 +682,17 @@ constexpr int CS_CHUNKS = 512;
 template <bool F32>
 __global__ __launch_bounds__(256) void colsum_part_kernel(const void* __restrict__ m, int64_t ld, int64_t n_rows,
                                                           int32_t cols, int64_t rows_per_chunk,
-                                                          double* __restrict__ partial) {
+                                                          double* __restrict__ partial, int64_t m_batch) {
+  // problem blockIdx.z: its rows m_batch elements after the previous
+  // problem's, its partials gridDim.y chunks after them
   constexpr int V = F32 ? 1 : 8;
   const int32_t c0 = (blockIdx.x * 256 + threadIdx.x) * V;
   if (c0 >= cols) return;
+  if constexpr (F32)
+    m = static_cast<const float*>(m) + blockIdx.z * m_batch;
+  else
+    m = static_cast<const uint16_t*>(m) + blockIdx.z * m_batch;
+  partial += static_cast<int64_t>(blockIdx.z) * gridDim.y * cols;
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_chunk;
   const int64_t r1 = min(n_rows, r0 + rows_per_chunk);
   double acc[V];
@@ -708,12 +715,15 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(const void* __restrict
 }
 
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(const double* __restrict__ partial, int32_t cols,
-                                                            double* __restrict__ out) {
+                                                            int32_t chunks, double* __restrict__ out,
+                                                            int64_t out_batch) {
+  // problem blockIdx.y: chunks partials of cols each, added in chunk order
   const int32_t c = blockIdx.x * 256 + threadIdx.x;
   if (c >= cols) return;
+  partial += static_cast<int64_t>(blockIdx.y) * chunks * cols;
   double s = 0.0;
-  for (int q = 0; q < CS_CHUNKS; ++q) s += partial[static_cast<int64_t>(q) * cols + c];
-  out[c] = s;
+  for (int q = 0; q < chunks; ++q) s += partial[static_cast<int64_t>(q) * cols + c];
+  out[static_cast<int64_t>(blockIdx.y) * out_batch + c] = s;
 }
 
 static int colsum(const void* m, int64_t ld, int64_t n_rows, int32_t cols, int32_t f32, double* partial, double* out,
@@ -722,10 +732,32 @@ static int colsum(const void* m, int64_t ld, int64_t n_rows, int32_t cols, int32
   const int v = f32 ? 1 : 8;
   const dim3 grid(static_cast<unsigned>(ceil_div(cols, 256 * v)), CS_CHUNKS);
   if (f32)
-    colsum_part_kernel<true><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial);
+    colsum_part_kernel<true><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial, 0);
   else
-    colsum_part_kernel<false><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial);
-  colsum_reduce_kernel<<<static_cast<unsigned>(ceil_div(cols, 256)), 256, 0, s>>>(partial, cols, out);
+    colsum_part_kernel<false><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial, 0);
+  colsum_reduce_kernel<<<static_cast<unsigned>(ceil_div(cols, 256)), 256, 0, s>>>(partial, cols, CS_CHUNKS, out, 0);
+  KVX_LAUNCH_CHECK();
+  return KVX_OK;
+}
+
+// Column sums of `batch` bf16 matrices of one shape in one pass: problem b's
+// rows m_batch elements after problem a's, its sums at out + b out_batch;
+// `partial` has room for cap doubles (as many row chunks as fit, at most
+// CS_CHUNKS; one problem at a time when not even one chunk per problem fits).
+static int colsum_batch(const uint16_t* m, int64_t ld, int64_t m_batch, int64_t n_rows, int32_t cols, int32_t batch,
+                        double* partial, int64_t cap, double* out, int64_t out_batch, hipStream_t s) {
+  const int64_t chunks = std::min<int64_t>(CS_CHUNKS, cap / (static_cast<int64_t>(cols) * batch));
+  if (chunks < 1) {
+    for (int32_t b = 0; b < batch; ++b)
+      if (int st = colsum(m + b * m_batch, ld, n_rows, cols, 0, partial, out + b * out_batch, s)) return st;
+    return KVX_OK;
+  }
+  const int64_t rpc = ceil_div(n_rows, chunks);
+  const dim3 grid(static_cast<unsigned>(ceil_div(cols, 256 * 8)), static_cast<unsigned>(chunks),
+                  static_cast<unsigned>(batch));
+  colsum_part_kernel<false><<<grid, 256, 0, s>>>(m, ld, n_rows, cols, rpc, partial, m_batch);
+  colsum_reduce_kernel<<<dim3(static_cast<unsigned>(ceil_div(cols, 256)), static_cast<unsigned>(batch)), 256, 0,
+                         s>>>(partial, cols, static_cast<int32_t>(chunks), out, out_batch);
   KVX_LAUNCH_CHECK();
   return KVX_OK;
 }
@@ -2388,6 +2420,11 @@ int launch_recolor_caches(const FitcShape& sh, const void* const* send_role, con
       if (int st = gram_batch(yr, sh.f_out, y_layer, yr, sh.f_out, y_layer, sh.n_recv, sh.f_out, 0, sh.recv_layers,
                               rc.part, part_cap, rc.Gy + z0 * bs, nullptr, bs, s))
         return st;
+      // the Gram's partials are added up: their room holds the sums' chunks
+      if (int st = colsum_batch(yr, sh.f_out, y_layer, sh.n_recv, sh.f_out, sh.recv_layers,
+                                reinterpret_cast<double*>(rc.part), part_cap / 2, rc.sy + z0 * bs, bs, s))
+        return st;
+      continue;
     }
     for (int32_t l = 0; l < sh.recv_layers; ++l) {
       const uint16_t* y = yr + l * y_layer;
