@@ -2271,7 +2271,8 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
   const int64_t fo2 = static_cast<int64_t>(f_out) * f_out;
   const dim3 grid_o2(grid_for(fo2 / 8 + 1), static_cast<unsigned>(count));
 
-  // 2. factors and the whitened cross-covariance M = L_x^-1 C L_y^-T
+  // 2. factors, Z0 = L_x^-1 C and E = L_y^-1 (the whitened cross-covariance
+  // is M = Z0 E^T)
   if (int st = chol_factor(s, count, w.G, f_in, bs, w.linvx, w.xinvx, w.zbuf, w.flags)) return st;
   if (int st = chol_factor(s, count, w.Gy, f_out, bs, w.linvy, w.xinvy, w.zbuf, w.flags)) return st;
   zero_upper_kernel<<<grid_o2, 256, 0, s>>>(w.Gy, f_out, bs);
@@ -2280,20 +2281,24 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
   identity_kernel<<<grid_o2, 256, 0, s>>>(w.E, f_out, bs);
   KVX_LAUNCH_CHECK();
   if (int st = chol_forward(s, count, w.Gy, f_out, bs, w.xinvy, w.zbuf, w.E, f_out)) return st;  // E = L_y^-1
-  if (int st = dgemm(s, count, f_in, f_out, f_out, w.C, f_out, 1, w.E, 1, f_out, w.M, f_out, bs, 0, 1)) return st;
 
   std::vector<int32_t> flags(static_cast<size_t>(count), 0);
   KVX_HIP_TRY(hipMemcpyAsync(flags.data(), w.flags, sizeof(int32_t) * count, hipMemcpyDeviceToHost, s));
 
-  // 3. S = M^T M, then the polar iteration
+  // 3. S = M^T M with M = Z0 E^T (Z0 = L_x^-1 S_xy, in C) formed as
+  // E (Z0^T Z0) E^T, so the f_in x f_out matrix M is never formed (K in T,
+  // E K in N, S in Y); then the polar iteration
   double *Y = w.ns[0], *Z = w.ns[1], *T = w.ns[2], *N = w.ns[3];
-  // S and each step's T are symmetric (the iterates are polynomials in S):
-  // only their tiles on and below the diagonal are formed, then mirrored.
+  // K, S and each step's T are symmetric (the iterates are polynomials in
+  // S): only their tiles on and below the diagonal are formed, then mirrored.
   // Y and Z are updated by the full products with the one symmetric T, from
   // opposite sides: mirroring them as well breaks the pairing of their
   // rounding errors that keeps the coupled iteration stable (it then
   // diverges once Z grows large), so they stay as computed.
-  if (int st = dgemm(s, count, f_out, f_out, f_in, w.M, 1, f_out, w.M, f_out, 1, Y, f_out, bs, 1, 1)) return st;
+  if (int st = dgemm(s, count, f_out, f_out, f_in, w.C, 1, f_out, w.C, f_out, 1, T, f_out, bs, 1, 1)) return st;
+  if (int st = sym_from_lower(s, count, T, f_out, bs)) return st;
+  if (int st = dgemm(s, count, f_out, f_out, f_out, w.E, f_out, 1, T, f_out, 1, N, f_out, bs, 0, 1)) return st;
+  if (int st = dgemm(s, count, f_out, f_out, f_out, N, f_out, 1, w.E, 1, f_out, Y, f_out, bs, 1, 1)) return st;
   if (int st = sym_from_lower(s, count, Y, f_out, bs)) return st;
   if (int st = frob(s, count, Y, f_out, bs, w.dev, w.scal)) return st;
   // largest eigenvalue of S by RC_POWER power steps (v in T, S v in N), so
@@ -2350,11 +2355,14 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
   for (int32_t z = 0; z < count; ++z)
     KVX_HIP_TRY(hipMemcpyAsync(&zf[z], w.scal + z * bs + 1, sizeof(double), hipMemcpyDeviceToHost, s));
 
-  // 4. W = L_x^-T Q L_y^T with Q = M S^-1/2, S^-1/2 = Z / sqrt(c); b = mean_y - mean_x W
+  // 4. W = L_x^-T Q L_y^T with Q = M S^-1/2 = Z0 E^T S^-1/2, S^-1/2 = Z / sqrt(c):
+  // R = (E^T S^-1/2) L_y^T in the f_out x f_out products (Y, then T), then
+  // W = L_x^-T (Z0 R); b = mean_y - mean_x W
   scale_kernel<<<grid_o2, 256, 0, s>>>(Z, fo2, bs, w.scal, -0.5);
   KVX_LAUNCH_CHECK();
-  if (int st = dgemm(s, count, f_in, f_out, f_out, w.M, f_out, 1, Z, f_out, 1, w.C, f_out, bs, 0, 1)) return st;
-  if (int st = dgemm(s, count, f_in, f_out, f_out, w.C, f_out, 1, w.Gy, 1, f_out, w.M, f_out, bs, 0, 1)) return st;
+  if (int st = dgemm(s, count, f_out, f_out, f_out, w.E, 1, f_out, Z, f_out, 1, Y, f_out, bs, 0, 1)) return st;
+  if (int st = dgemm(s, count, f_out, f_out, f_out, Y, f_out, 1, w.Gy, 1, f_out, T, f_out, bs, 0, 1)) return st;
+  if (int st = dgemm(s, count, f_in, f_out, f_out, w.C, f_out, 1, T, f_out, 1, w.M, f_out, bs, 0, 1)) return st;
   if (int st = chol_backward(s, count, w.G, f_in, bs, w.xinvx, w.zbuf, w.M, f_out)) return st;
   for (int32_t z = 0; z < count; ++z) {
     if (int st = fit_output(s, w.M + z * bs, f_in, f_out, w_out[z], b_out[z], w.sx + z * bs, w.sy + z * bs, inv_n,
