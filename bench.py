@@ -862,10 +862,11 @@ def recolor_measure(dev, cal, reps=2):
     torch.cuda.empty_cache()
     it = info["iters"]
     gram = count * 2.0 * n * (fi * (fi + 1) / 2 + fi * fo + fo * (fo + 1) / 2)   # S_xx, S_xy, S_yy on bf16 MFMA
-    fp64 = count * (fi ** 3 / 3 + fo ** 3 / 3 + fi ** 2 * fo + fo ** 3 / 3       # factors, L_x^-1 S_xy, L_y^-1
-                    + 2 * fi * fo ** 2 + fi * fo ** 2                             # M = Z L_y^-T, S = M^T M
-                    + it * 6 * fo ** 3                                            # polar iterations
-                    + 2 * fi * fo ** 2 + fi * fo ** 2 + fi ** 2 * fo)              # Q, Q L_y^T, L_x^-T
+    # the fp64 FLOPs the solve executes (symmetric results counted once)
+    fp64 = count * (fi ** 3 / 3 + fo ** 3 / 3 + fi ** 2 * fo + fo ** 3 / 3       # factors, Z0 = L_x^-1 S_xy, L_y^-1
+                    + fi * fo ** 2 + 2 * fo ** 3 + fo ** 3                        # S = E (Z0^T Z0) E^T
+                    + it * 6 * fo ** 3                                            # steps: P, P^2 halves, Y T, T Z
+                    + 4 * fo ** 3 + 2 * fi * fo ** 2 + fi ** 2 * fo)               # R = E^T Z L_y^T, Z0 R, L_x^-T
     t_roof = gram / (PEAK_MFMA_BF16_TFLOPS * 1e12) + fp64 / (PEAK_FP64_TFLOPS * 1e12)
     return {"workload": f"Recolor fit of all {count} maps (32 layers x K,V) in one call from the calibration caches: "
                         "65536 receiver tokens, 3072 bf16 sender features -> 1024 receiver outputs each, "
@@ -879,8 +880,8 @@ def recolor_measure(dev, cal, reps=2):
             "roofline": {"bound": "fp64", "achieved": fp64 / (t * 1e-3) / 1e12, "peak": PEAK_FP64_TFLOPS,
                          "unit": "TFLOP/s", "frac": t_roof / (t * 1e-3),
                          "note": "frac = (moment FLOPs of the plain definition over all 65536 rows at the bf16 "
-                                 "peak + fp64 FLOPs at the fp64 peak) / measured time; achieved = fp64 FLOPs "
-                                 "over the whole fit time",
+                                 "peak + the fp64 FLOPs the solve executes at the fp64 peak) / measured time; "
+                                 "achieved = those fp64 FLOPs over the whole fit time",
                          "traffic": None}}
 
 

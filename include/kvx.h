@@ -587,9 +587,9 @@ int kvx_translate_fp8(const kvx_cache_desc* send, const void* k_send, const void
  *   8 (f_in^2 + 2 f_in f_out + 7 f_out^2) bytes per problem).
  * Moments are accumulated as in kvx_fit_ridge (bf16: fp32 on matrix cores,
  * partials added in fp64); the factorisations, the polar iteration (coupled
- * Newton-Schulz for (M^T M)^-1/2) and the products run in fp64.  Synchronises
- * `stream` once per polar iteration.  Returns the first non-OK problem status,
- * else KVX_OK; argument errors as kvx_fit_ridge.
+ * third-order Newton-Schulz for (M^T M)^-1/2) and the products run in fp64.
+ * Synchronises `stream` once per polar iteration.  Returns the first non-OK
+ * problem status, else KVX_OK; argument errors as kvx_fit_ridge.
  * ---------------------------------------------------------------------- */
 size_t kvx_fit_recolor_workspace_size(int32_t count, int32_t f_in, int32_t f_out);
 int kvx_fit_recolor(int32_t count, const void* const* x, int64_t ldx, const void* const* y,
