@@ -299,10 +299,12 @@ def fit_trace_summary(trace_dir, bench_log):
     rec = res["also_recolor"]
     span, busy, table = _kernel_table(rc)
     cuts = [("moments (Gram from the runs, feature sums, Y^T Y, target sums, centring)", 0),
-            ("factors and whitened cross-covariance (Cholesky of both, solves, M)", first(rc, "kvx::potrf_diag")),
-            # S = M^T M is the product just before the first mirroring
-            ("polar iteration (S = M^T M, scale, Newton-Schulz steps)", first(rc, "kvx::sym_from_lower") - 1),
-            ("map and bias (Q, back-substitution, outputs)", last(rc, "kvx::frob_final") + 1)]
+            ("factors (Cholesky of both, Z0 = L_x^-1 S_xy, E = L_y^-1)", first(rc, "kvx::potrf_diag")),
+            # Z0^T Z0 is the product just before the first mirroring
+            ("polar iteration (S = E Z0^T Z0 E^T, scale, Newton-Schulz steps)",
+             first(rc, "kvx::sym_from_lower") - 1),
+            ("map and bias (R = E^T S^-1/2 L_y^T, Z0 R, back-substitution, outputs)",
+             last(rc, "kvx::frob_final") + 1)]
     out += (f"\n## Recolor (kvx_fit_recolor_caches)\n\nWorkload: {rec['workload']}.\n\n"
             f"Last timed call: {len(rc)} dispatches, {span:.2f} ms from its first to its last kernel, "
             f"{busy:.2f} ms of kernel time, {rec['polar_iterations']} polar iterations.  Same run, bench.py's "
