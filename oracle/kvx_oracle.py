@@ -155,7 +155,8 @@ def rope_rotate(x, pos, base: float, sign: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# A3  runs of equal map values (restructuring of "reuse the sender state")
+# A3  runs of equal map values (an exact restructuring of the reuse of one sender
+#     token's state by every receiver token aligned to it)
 
 
 def runs(token_map) -> tuple[np.ndarray, np.ndarray]:
@@ -270,7 +271,7 @@ def fold_lowrank(w, a, b):
 
     W_eff = W + A B with W [F_in][F_out], A [F_in][r], B [r][F_out]
     (row-major, y = x W): w_eff[f][o] = w[f][o] + sum_r a[f][r] b[r][o].
-    Reading of "fp32 then cast to bf16": each product rounded to fp32, summed
+    Reading of a fold done in fp32 and cast to bf16: each product rounded to fp32, summed
     in rank order from r = 0 in fp32 (no fused multiply-add), added to w in
     fp32, then rounded to bf16 (nearest even).  Returns (fp32 sum, bf16
     bits)."""
