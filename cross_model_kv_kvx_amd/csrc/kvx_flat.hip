@@ -541,13 +541,21 @@ flat_gemm_kernel(const FlatKArgs args) {
     ta.w_base = static_cast<const char*>(args.wt[role]) + (static_cast<int64_t>(l) * args.f_out + n0) * args.k_dim * wb;
     ta.w_bytes = static_cast<uint32_t>(wb * FT_N * args.k_dim);
     ta.nk = nk;
+    // the sender rows of this tile's A part: only the loading waves read
+    // them, so the other waves issue no load at the tile start and nothing
+    // makes them wait there for the previous tile's epilogue stores
+    if (wave < FT_LOADERS) {
 #pragma unroll
-    for (int i = 0; i < FT_A_LD; ++i) {
-      const int r = (wave * FT_A_LD + i) * FT_ROWS_PER_LD + lrow;
-      int32_t u = m0 + r;
-      u = u < U ? u : U - 1;
-      const int32_t srow = args.a_compact[role] ? u : args.uniq[u];
-      ta.a_off[i] = 2u * static_cast<uint32_t>(srow * args.send_row + ft_chunk(r, lane & 7) * 8);
+      for (int i = 0; i < FT_A_LD; ++i) {
+        const int r = (wave * FT_A_LD + i) * FT_ROWS_PER_LD + lrow;
+        int32_t u = m0 + r;
+        u = u < U ? u : U - 1;
+        const int32_t srow = args.a_compact[role] ? u : args.uniq[u];
+        ta.a_off[i] = 2u * static_cast<uint32_t>(srow * args.send_row + ft_chunk(r, lane & 7) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FT_A_LD; ++i) ta.a_off[i] = 0u;
     }
 #pragma unroll
     for (int i = 0; i < FT_B_LD; ++i) {
