@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <array>
+#include <cmath>
 #include <map>
 #include <vector>
 
@@ -870,17 +871,32 @@ __global__ __launch_bounds__(256) void lambda_kernel(double* __restrict__ G, int
 
 // ---------------------------------------------------------------- fp64 Cholesky pieces
 
+// A double of lane l (l uniform), as two 32-bit lane reads.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), l));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), l));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
 // Factor the diagonal block [k0, k0+nb) (lower) of one problem of a batch
 // (one workgroup per problem), flag non-positive pivots,
 // and write the inverse of the factor (lower, nb x nb, zero above the
 // diagonal, row stride CH_NB) to `linv`: the panel and the block triangular
-// solves then become products with it.  One wave, no barrier: lane i keeps
-// row i in registers; at column j every lane takes the pivot from lane j
-// (the square root is recomputed per lane), lane i scales its entry and
-// publishes it in LDS, and each lane updates its row with the published
-// column (LDS operations of one wave execute in order).  Rows past nb are
-// the identity.  The inverse is formed one column per lane by forward
-// substitution against the factor in LDS.
+// solves then become products with it.  One wave.  The block's lower
+// triangle is read a row at a time (lane = column, whole rows per load) and
+// turned through LDS so that lane i holds row i in registers.  At column j
+// every lane publishes its entry of the column in LDS and reads the whole
+// column back, two entries per read that every lane shares (one wave: its
+// LDS operations execute in order); the square root and its reciprocal are
+// recomputed per lane, each lane scales its own entry and updates the rest
+// of its row with the column scaled by the reciprocal (folded into the
+// lane's multiplier).  Entries above the diagonal take updates too and are
+// never read.  Rows past nb are the identity.  The factor goes back through
+// LDS (lane = column on the way out), and the inverse is formed one column
+// per lane by forward substitution against it, each factor entry one LDS
+// read that every lane shares, the division by the pivot a product with the
+// reciprocal held by the pivot's lane.
 __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, int64_t bsa, int32_t n, int32_t k0,
                                                         int32_t nb, int32_t* __restrict__ flag,
                                                         double* __restrict__ linv, int64_t bsl) {
@@ -889,51 +905,66 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
   flag += blockIdx.x;
   linv += blockIdx.x * bsl;
   __shared__ double L[CH_NB][CH_NB + 1];
-  __shared__ double col[CH_NB];
+  __shared__ __align__(16) double col[CH_NB];
   const int i = threadIdx.x;
+  {
+    // every row's load in flight at once (the block was just updated, often by another XCD)
+    double in[CH_NB];
+#pragma unroll
+    for (int r = 0; r < CH_NB; ++r)
+      in[r] = (r < nb && i < nb) ? (i <= r ? A[static_cast<int64_t>(k0 + r) * n + k0 + i] : 0.0) : (r == i ? 1.0 : 0.0);
+#pragma unroll
+    for (int r = 0; r < CH_NB; ++r) L[r][i] = in[r];
+  }
+  __syncthreads();
   double row[CH_NB];
 #pragma unroll
-  for (int c = 0; c < CH_NB; ++c)
-    row[c] = (i < nb && c < nb) ? A[static_cast<int64_t>(k0 + i) * n + k0 + c] : (i == c ? 1.0 : 0.0);
+  for (int c = 0; c < CH_NB; ++c) row[c] = L[i][c];
   int bad = 0;
+  double rp_own = 1.0;  // lane j: 1 / pivot j
 #pragma unroll
   for (int j = 0; j < CH_NB; ++j) {
-    // pivot of column j, from lane j
-    const double d = __shfl(row[j], j, 64);
+    col[i] = row[j];
+    KVX_COMPILER_FENCE();
+    double cj[CH_NB];  // column j as published (entries j..63 read)
+#pragma unroll
+    for (int c = j & ~1; c < CH_NB; c += 2) {
+      const double2 v = *reinterpret_cast<const double2*>(&col[c]);
+      cj[c] = v.x;
+      cj[c + 1] = v.y;
+    }
+    KVX_COMPILER_FENCE();
+    const double d = cj[j];
     const bool ok = d > 0.0;
     if (j < nb && !ok) bad = 1;
     const double piv = sqrt(ok ? d : 1.0);
     const double rp = 1.0 / piv;
-    if (i == j) row[j] = piv;
-    if (i > j) row[j] *= rp;
-    col[i] = row[j];
-    KVX_COMPILER_FENCE();
+    rp_own = i == j ? rp : rp_own;
+    row[j] = i == j ? piv : (i > j ? row[j] * rp : row[j]);
+    // L[c][j] = cj[c] * rp: the reciprocal joins this lane's multiplier
+    const double t = row[j] * rp;
 #pragma unroll
-    for (int c = j + 1; c < CH_NB; ++c) {
-      const double lc = col[c];
-      if (i >= c) row[c] -= row[j] * lc;
-    }
-    KVX_COMPILER_FENCE();
+    for (int c = j + 1; c < CH_NB; ++c) row[c] = fma(-t, cj[c], row[c]);
   }
   if (bad && i == 0) *flag = 1;
+  __syncthreads();  // every lane has read its row of the input
 #pragma unroll
   for (int c = 0; c < CH_NB; ++c) L[i][c] = (c <= i) ? row[c] : 0.0;
-  KVX_COMPILER_FENCE();
-  // inverse: lane c forms column c
-  double x[CH_NB];
-  const int c = i;
+  __syncthreads();
 #pragma unroll
-  for (int r = 0; r < CH_NB; ++r) {
-    double v = (r == c) ? 1.0 : 0.0;
-#pragma unroll
-    for (int q = 0; q < r; ++q) v -= L[r][q] * x[q];
-    x[r] = (r >= c) ? v / L[r][r] : 0.0;
-  }
-#pragma unroll
-  for (int r = 0; r < CH_NB; ++r) {
+  for (int r = 0; r < CH_NB; ++r)
     if (i < nb && r < nb && r >= i) A[static_cast<int64_t>(k0 + r) * n + k0 + i] = L[r][i];
-    linv[r * CH_NB + c] = (r < nb && c < nb) ? x[r] : 0.0;
+  // inverse: lane c forms column c (entries above the diagonal come out 0)
+  double x[CH_NB];
+#pragma unroll
+  for (int r = 0; r < CH_NB; ++r) {
+    double v = (r == i) ? 1.0 : 0.0;
+#pragma unroll
+    for (int q = 0; q < r; ++q) v = fma(-L[r][q], x[q], v);
+    x[r] = v * readlane_f64(rp_own, r);
   }
+#pragma unroll
+  for (int r = 0; r < CH_NB; ++r) linv[r * CH_NB + i] = (r < nb && i < nb) ? x[r] : 0.0;
 }
 
 // C[M x N] -= A * B (overwrite = 0) or C = A * B (overwrite = 1) in fp64 on
@@ -1992,13 +2023,20 @@ int launch_fit_caches(const FitcShape& sh, const void* const* send_role, const v
 // x <- x p(x)^2 converges to 1 for x in (0, 2.3), and each step multiplies a
 // small eigenvalue of S / c by (15/8)^2): Z -> (S / c)^-1/2.  All products
 // are fp64 on matrix cores, every problem of the call at once; the host
-// reads max |T - I| per problem after each step.
+// reads ||T - I||_F per problem after each step.  T - I = -(P - I)/2 to first
+// order and the step takes an error e of P to about e^3, so once
+// ||T - I||_F <= RC_TOL (spectral error of P at most about 2e-4) the step
+// being applied brings P to within about 1e-11 of I, far below the fp32
+// rounding of the maps, and the iteration ends with it, with no further step
+// to confirm it.
 
 constexpr int NS_BLOCKS = 64;        // workgroups per problem of the middle step
 constexpr int RC_MAX_ITERS = 100;
 constexpr int RC_POWER = 12;         // power steps for the largest eigenvalue of M^T M
-constexpr double RC_TOL = 1e-10;     // max |T - I| taken as converged
-constexpr double RC_FLOOR = 1e-6;    // below this, a step that gains < 4x is the rounding floor
+constexpr double RC_TOL = 1e-4;      // ||T - I||_F after which this step's update is the last
+// below this, a step that gains < 4x is the rounding floor (a step from
+// ||T - I||_F <= 1e-3 that still converges gains far more)
+constexpr double RC_FLOOR = 1e-3;
 // ||(S / c)^-1/2||_F above this: M is numerically rank-deficient (fewer
 // distinct calibration rows than outputs, or outputs unrelated to the
 // features in some direction), so the polar factor is not determined
@@ -2143,11 +2181,9 @@ __global__ void polar_scale_kernel(double* __restrict__ scal, int64_t bs) {
   if (threadIdx.x == 0) q[0] = (c > 0.0 && c < q[0]) ? c : q[0];
 }
 
-__device__ __forceinline__ double nan_max(double a, double b) { return (b > a || b != b) ? b : a; }
-
 // Middle of a third-order Newton-Schulz step: from P = Z Y and Q = P^2,
 // T = (15 I - 10 P + 3 Q) / 8 in place of P (x^-1/2 to second order about
-// x = 1, at x = P); each workgroup writes the largest |T - I| of its share
+// x = 1, at x = P); each workgroup writes the sum of (T - I)^2 over its share
 // (NaN propagates) to dev[problem][workgroup].
 __global__ __launch_bounds__(256) void ns_mid_kernel(double* __restrict__ P, const double* __restrict__ Q,
                                                       int32_t n, int64_t bs, double* __restrict__ dev) {
@@ -2160,12 +2196,12 @@ __global__ __launch_bounds__(256) void ns_mid_kernel(double* __restrict__ P, con
     const double id = (e / n == e % n) ? 1.0 : 0.0;
     const double t = (15.0 * id - 10.0 * p[e] + 3.0 * q[e]) * 0.125;
     p[e] = t;
-    m = nan_max(m, fabs(t - id));
+    m += (t - id) * (t - id);
   }
   red[threadIdx.x] = m;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] = nan_max(red[threadIdx.x], red[threadIdx.x + w]);
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
   if (threadIdx.x == 0) dev[blockIdx.y * NS_BLOCKS + blockIdx.x] = red[0];
@@ -2341,12 +2377,11 @@ static int recolor_solve(RcWs& w, int32_t count, int32_t f_in, int32_t f_out, do
     for (int32_t z = 0; z < count; ++z) {
       if (flags[z] || done[z]) continue;
       double m = 0.0;
-      for (int b = 0; b < NS_BLOCKS; ++b) {
-        const double d = dev[static_cast<size_t>(z) * NS_BLOCKS + b];
-        m = (d > m || d != d) ? d : m;
-      }
-      // converged, or at the rounding floor (a quadratic step gains far more than 4x)
-      if (m <= RC_TOL || (m <= RC_FLOOR && m >= 0.25 * prev[z]))
+      for (int b = 0; b < NS_BLOCKS; ++b) m += dev[static_cast<size_t>(z) * NS_BLOCKS + b];
+      m = std::sqrt(m);
+      // converged with this step, at the rounding floor, or NaN (then Z is
+      // NaN too and the problem reports that it did not converge)
+      if (m <= RC_TOL || (m <= RC_FLOOR && m >= 0.25 * prev[z]) || m != m)
         done[z] = 1;
       else
         all = false;
