@@ -958,10 +958,12 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
   double x[CH_NB];
 #pragma unroll
   for (int r = 0; r < CH_NB; ++r) {
-    double v = (r == i) ? 1.0 : 0.0;
+    // the sum taken positive and subtracted once (written as repeated
+    // fma(-l, x, v), this loop takes the compiler minutes)
+    double a = 0.0;
 #pragma unroll
-    for (int q = 0; q < r; ++q) v = fma(-L[r][q], x[q], v);
-    x[r] = v * readlane_f64(rp_own, r);
+    for (int q = 0; q < r; ++q) a = fma(L[r][q], x[q], a);
+    x[r] = (((r == i) ? 1.0 : 0.0) - a) * readlane_f64(rp_own, r);
   }
 #pragma unroll
   for (int r = 0; r < CH_NB; ++r) linv[r * CH_NB + i] = (r < nb && i < nb) ? x[r] : 0.0;
@@ -971,14 +973,14 @@ __global__ __launch_bounds__(64) void potrf_diag_kernel(double* __restrict__ A, 
 // matrix cores, for a batch of problems (blockIdx.z; the operands of problem
 // z start bsa, bsb, bsc elements after those of problem z-1), with
 // A(m,k) = A[m*sam + k*sak] and B(k,n) = B[k*sbk + n*sbn].  Block tiles of
-// 2 WT x 2 WT; four waves of WT x WT, each from MFMA 16x16x4 fp64 blocks; K in
+// BT x BT; 2 x NWN waves, each from MFMA 16x16x4 fp64 blocks; K in
 // chunks of 16 through LDS (global elements are read along the operand's
 // unit-stride index and kept in that order: [k][m] / [k][n], or [m][k] /
 // [n][k] for an operand read along k; rows padded against bank conflicts of
 // the stores and of the fragment reads); the next chunk is read
 // into registers while the current one is multiplied.  A workgroup reads all
 // of its A rows and B columns before it writes its tile, so C may alias A when
-// N <= 2 WT or B when M <= 2 WT.  lower_only forms only the tiles on and
+// N <= BT or B when M <= BT.  lower_only forms only the tiles on and
 // below the diagonal (the grid holds just those).
 struct DgArgs {
   int32_t M, N, K;
@@ -992,22 +994,32 @@ struct DgArgs {
 };
 constexpr int DG_BK = 16;
 
-// WT = 32: 64 x 64 block tiles (small products), the updated C tile read
-// before the K loop; WT = 64: 128 x 128 block tiles (large products, long K).
+// BT = 64: 64 x 64 block tiles (small products), the updated C tile read
+// before the K loop; BT = 128: 128 x 128 block tiles (large products, long
+// K).  2 x NWN waves, each a (BT / 2) x (BT / NWN) wave tile.
 // AK / BK: A / B read along k (unit stride in k), else along m / n.
-template <int WT, bool AK, bool BK>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WT == 32 ? 3 : 2, 8))) void
+#ifndef KVX_DG_BIG_NWN
+#define KVX_DG_BIG_NWN 4
+#endif
+template <int BT, int NWN>
+constexpr int dg_min_waves() {
+  return BT == 64 ? 3 : (NWN == 4 ? 4 : 2);
+}
+template <int BT, int NWN, bool AK, bool BK>
+__global__ __attribute__((amdgpu_flat_work_group_size(128 * NWN, 128 * NWN),
+                          amdgpu_waves_per_eu(dg_min_waves<BT, NWN>(), 8))) void
 dgemm_kernel(const DgArgs g) {
-  constexpr int BT = 2 * WT;           // block tile
+  constexpr int NT = 128 * NWN;        // threads
   constexpr int LD = BT + 16;          // [k][m] rows (doubles): 16-lane row pieces in distinct banks
   // an operand read along k is kept [m][k] with an odd row stride: a thread's
   // store is then contiguous with its neighbours' and the 16 rows of a
   // fragment read start in distinct bank pairs (kept [k][m], its transposing
   // stores put 8 lanes on one bank pair)
   constexpr int LDK = DG_BK + 1;
-  constexpr int NQ = BT * DG_BK / 256; // elements of A (and of B) per thread and chunk
-  constexpr int NF = WT / 16;          // MFMA blocks per wave and dimension
-  constexpr bool PRE_C = WT == 32;
+  constexpr int NQ = BT * DG_BK / NT;  // elements of A (and of B) per thread and chunk
+  constexpr int WTM = BT / 2, WTN = BT / NWN;
+  constexpr int NFM = WTM / 16, NFN = WTN / 16;  // MFMA blocks per wave along m and n
+  constexpr bool PRE_C = BT == 64;
   int32_t bm = blockIdx.y, bn = blockIdx.x;
   if (g.lower_only) {
     // blockIdx.x enumerates only the tiles on and below the diagonal, row by
@@ -1033,45 +1045,56 @@ dgemm_kernel(const DgArgs g) {
   const double* B = g.B + blockIdx.z * g.bsb;
   double* C = g.C + blockIdx.z * g.bsc;
   constexpr bool a_k = AK, b_k = BK;
-  // this thread's elements of a chunk: fixed row / column, k offset 0..15;
-  // offsets inside one problem's operands are below 2^31 elements
-  int32_t oa[NQ], ob[NQ];
+  // this thread's elements of a chunk: fixed row / column, k offset 0..15,
+  // as byte offsets from the chunk's first k (one 32-bit register each, the
+  // chunk's base a uniform pointer); every operand of one problem holds at
+  // most KVX_MAX_FIT_FEATURES^2 = 2^28 elements, so they fit
+  uint32_t oa[NQ], ob[NQ];
   uint32_t va = 0, vb = 0;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int e = tid + 256 * q;
+    const int e = tid + NT * q;
     const int ma = a_k ? (e >> 4) : (e % BT), ka = a_k ? (e & 15) : (e / BT);
     if (m0 + ma < g.M) va |= 1u << q;
-    oa[q] = static_cast<int32_t>((m0 + ma) * g.sam + ka * g.sak);
+    oa[q] = static_cast<uint32_t>(((m0 + ma) * g.sam + ka * g.sak) * 8);
     const int nb_ = b_k ? (e >> 4) : (e % BT), kb = b_k ? (e & 15) : (e / BT);
     if (n0 + nb_ < g.N) vb |= 1u << q;
-    ob[q] = static_cast<int32_t>((n0 + nb_) * g.sbn + kb * g.sbk);
+    ob[q] = static_cast<uint32_t>(((n0 + nb_) * g.sbn + kb * g.sbk) * 8);
   }
   double av[NQ], bv[NQ];
+  // buffer loads: the per-lane offset above plus the chunk's uniform offset;
+  // an element outside the operand takes an offset past the resource's end,
+  // which reads zero without a memory access
+  constexpr uint32_t OOB = 0x7ffffff8u;
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A, OOB), rb = buf_rsrc(B, OOB);
   auto load = [&](int32_t k0) {
+    const uint32_t sa = static_cast<uint32_t>(static_cast<int64_t>(k0) * g.sak * 8);
+    const uint32_t sb = static_cast<uint32_t>(static_cast<int64_t>(k0) * g.sbk * 8);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int ka = a_k ? (e & 15) : (e / BT), kb = b_k ? (e & 15) : (e / BT);
-      av[q] = ((va >> q) & 1u) && k0 + ka < g.K ? A[oa[q] + static_cast<int64_t>(k0) * g.sak] : 0.0;
-      bv[q] = ((vb >> q) & 1u) && k0 + kb < g.K ? B[ob[q] + static_cast<int64_t>(k0) * g.sbk] : 0.0;
+      const uint32_t pa = ((va >> q) & 1u) && k0 + ka < g.K ? oa[q] : OOB;
+      const uint32_t pb = ((vb >> q) & 1u) && k0 + kb < g.K ? ob[q] : OOB;
+      av[q] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(ra, pa, sa, 0));
+      bv[q] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rb, pb, sb, 0));
     }
   };
   // element r of lane l: row l/16 + 4r, column l%16 of its 16 x 16 block
-  auto row_of = [&](int i, int r) { return m0 + wm * WT + i * 16 + (lane >> 4) + 4 * r; };
-  auto col_of = [&](int j) { return n0 + wn * WT + j * 16 + (lane & 15); };
+  auto row_of = [&](int i, int r) { return m0 + wm * WTM + i * 16 + (lane >> 4) + 4 * r; };
+  auto col_of = [&](int j) { return n0 + wn * WTN + j * 16 + (lane & 15); };
 
-  f64x4 acc[NF][NF], cv[PRE_C ? NF : 1][PRE_C ? NF : 1];
+  f64x4 acc[NFM][NFN], cv[PRE_C ? NFM : 1][PRE_C ? NFN : 1];
 #pragma unroll
-  for (int i = 0; i < NF; ++i)
+  for (int i = 0; i < NFM; ++i)
 #pragma unroll
-    for (int j = 0; j < NF; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < NFN; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
   load(0);
   if constexpr (PRE_C) {
 #pragma unroll
-    for (int i = 0; i < NF; ++i)
+    for (int i = 0; i < NFM; ++i)
 #pragma unroll
-      for (int j = 0; j < NF; ++j)
+      for (int j = 0; j < NFN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t m = row_of(i, r), n = col_of(j);
@@ -1082,7 +1105,7 @@ dgemm_kernel(const DgArgs g) {
     __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       if constexpr (AK)
         As[e >> 4][e & 15] = av[q];
       else
@@ -1098,33 +1121,33 @@ dgemm_kernel(const DgArgs g) {
     for (int k4 = 0; k4 < DG_BK; k4 += 4) {
       // operands of MFMA 16x16x4: lane l holds A[l%16][l/16] and B[l/16][l%16]
       const int kr = k4 + (lane >> 4);
-      double a[NF], b[NF];
+      double a[NFM], b[NFN];
 #pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        const int m = wm * WT + i * 16 + (lane & 15);
+      for (int i = 0; i < NFM; ++i) {
+        const int m = wm * WTM + i * 16 + (lane & 15);
         if constexpr (AK)
           a[i] = As[m][kr];
         else
           a[i] = As[kr][m];
       }
 #pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        const int nn = wn * WT + j * 16 + (lane & 15);
+      for (int j = 0; j < NFN; ++j) {
+        const int nn = wn * WTN + j * 16 + (lane & 15);
         if constexpr (BK)
           b[j] = Bs[nn][kr];
         else
           b[j] = Bs[kr][nn];
       }
 #pragma unroll
-      for (int i = 0; i < NF; ++i)
+      for (int i = 0; i < NFM; ++i)
 #pragma unroll
-        for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NFN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int i = 0; i < NF; ++i)
+  for (int i = 0; i < NFM; ++i)
 #pragma unroll
-    for (int j = 0; j < NF; ++j)
+    for (int j = 0; j < NFN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int32_t m = row_of(i, r), n = col_of(j);
@@ -1292,13 +1315,14 @@ static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, 
   const dim3 grid = lower_only ? dim3(static_cast<unsigned>(n_lower), 1, static_cast<unsigned>(count))
                                : dim3(static_cast<unsigned>(nbn), static_cast<unsigned>(nbm),
                                       static_cast<unsigned>(count));
-#define KVX_DG(WT, A_, B_) dgemm_kernel<WT, A_, B_><<<grid, 256, 0, s>>>(g)
+#define KVX_DG(BT_, NWN_, A_, B_) dgemm_kernel<BT_, NWN_, A_, B_><<<grid, 128 * NWN_, 0, s>>>(g)
   if (big) {
-    if (ak) { if (bk) KVX_DG(64, true, true); else KVX_DG(64, true, false); }
-    else { if (bk) KVX_DG(64, false, true); else KVX_DG(64, false, false); }
+    constexpr int W = KVX_DG_BIG_NWN;
+    if (ak) { if (bk) KVX_DG(128, W, true, true); else KVX_DG(128, W, true, false); }
+    else { if (bk) KVX_DG(128, W, false, true); else KVX_DG(128, W, false, false); }
   } else {
-    if (ak) { if (bk) KVX_DG(32, true, true); else KVX_DG(32, true, false); }
-    else { if (bk) KVX_DG(32, false, true); else KVX_DG(32, false, false); }
+    if (ak) { if (bk) KVX_DG(64, 2, true, true); else KVX_DG(64, 2, true, false); }
+    else { if (bk) KVX_DG(64, 2, false, true); else KVX_DG(64, 2, false, false); }
   }
 #undef KVX_DG
   KVX_LAUNCH_CHECK();

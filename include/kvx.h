@@ -61,10 +61,12 @@ typedef enum { KVX_F32 = 0, KVX_BF16 = 1 } kvx_dtype;
 /* Size limits checked by every entry point (larger values are refused with
  * KVX_ERR_INVALID or, for the fits, KVX_ERR_UNSUPPORTED; size queries return
  * 0): features of one cache row (kv_heads * head_dim), problems of one fit
- * call, and features on either side of a fitted map. */
+ * call, and features on either side of a fitted map (a fit's fp64 matrices
+ * of one problem then hold at most 2^28 elements, 2 GiB, which the fp64
+ * products address with 32-bit byte offsets). */
 #define KVX_MAX_ROW 65536
 #define KVX_MAX_PROBLEMS 65535
-#define KVX_MAX_FIT_FEATURES 65536
+#define KVX_MAX_FIT_FEATURES 16384
 
 /* Shape of one role (K or V) of one model's cache. */
 typedef struct {

@@ -239,7 +239,8 @@ static void check_sizes(void) {
   EXPECT(kvx_fit_ridge_workspace_size(3072, 1024) > (size_t)3072 * 3072 * 8);
   EXPECT_EQ(kvx_fit_ridge_workspace_size(0, 1024), 0);
   EXPECT(kvx_fit_ridge_batched_workspace_size(65535, 3072, 1024) > kvx_fit_ridge_batched_workspace_size(64, 3072, 1024));
-  EXPECT(kvx_fit_ridge_batched_workspace_size(1, 1 << 16, 1 << 16) > 0);
+  EXPECT(kvx_fit_ridge_batched_workspace_size(1, KVX_MAX_FIT_FEATURES, KVX_MAX_FIT_FEATURES) > 0);
+  EXPECT_EQ(kvx_fit_ridge_batched_workspace_size(1, 1 << 16, 1 << 16), 0);
   EXPECT(kvx_fit_ridge_batched_workspace_size(KVX_MAX_PROBLEMS, KVX_MAX_FIT_FEATURES, KVX_MAX_FIT_FEATURES) >
          (size_t)KVX_MAX_PROBLEMS * KVX_MAX_FIT_FEATURES * KVX_MAX_FIT_FEATURES * 8);
   EXPECT_EQ(kvx_fit_ridge_batched_workspace_size(KVX_MAX_PROBLEMS + 1, 64, 64), 0);
