@@ -51,7 +51,7 @@ typedef enum {
   KVX_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
   KVX_ERR_NOT_SPD = 4,     /* regularised Gram matrix not positive definite */
   KVX_ERR_HIP = 5,         /* a HIP runtime call failed */
-  KVX_ERR_UNSUPPORTED = 6, /* a valid combination this build does not implement */
+  KVX_ERR_UNSUPPORTED = 6, /* a valid combination the library does not implement */
   KVX_ERR_NOT_CONVERGED = 7 /* an iteration did not converge, or its result is not determined
                                (polar factor of a rank-deficient whitened cross-covariance) */
 } kvx_status;
