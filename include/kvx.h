@@ -670,7 +670,8 @@ int kvx_fold_lowrank(const float* w, const float* a, const float* b, int32_t cou
  *   b (each byte read once and written once), mode 1 reads a (b: device
  *   uint32 sink of kvx_probe_scratch_words() words), mode 2 fills a.  bytes:
  *   a positive multiple of 16, far above the 256 MB last-level cache for an
- *   HBM figure.  16-byte vector accesses, streaming stores.  One untimed
+ *   HBM figure.  16-byte vector accesses, eight per thread and pass with the
+ *   loads issued before the stores.  One untimed
  *   launch, then `iters` launches between two events on `stream`;
  *   *ms_per_launch = their mean.  Synchronises `stream`.
  * kvx_probe_mfma: every wave of 8 per compute unit issues `reps` x 4

@@ -25,6 +25,17 @@ def test_hbm_probes():
     torch.cuda.synchronize()
     assert ms_r > 0 and ms_f > 0
     assert bool(torch.all(b.view(torch.int16) == 0x3c00))
+    # a length that ends inside the last pass of the grid (every thread moves
+    # eight 16-byte pieces per pass): the tail is copied and filled, nothing past it
+    m = 4 * 300007
+    c = torch.arange(m + 64, dtype=torch.int32, device=DEV)
+    d = torch.full((m + 64,), -1, dtype=torch.int32, device=DEV)
+    kvx.probe_hbm("copy", c[:m], d[:m], iters=1)
+    torch.cuda.synchronize()
+    assert torch.equal(d[:m], c[:m]) and bool(torch.all(d[m:] == -1))
+    kvx.probe_hbm("fill", d[:m], iters=1)
+    torch.cuda.synchronize()
+    assert bool(torch.all(d[:m].view(torch.int16) == 0x3c00)) and bool(torch.all(d[m:] == -1))
 
 
 def test_mfma_probe():
