@@ -998,9 +998,6 @@ constexpr int DG_BK = 16;
 // before the K loop; BT = 128: 128 x 128 block tiles (large products, long
 // K).  2 x NWN waves, each a (BT / 2) x (BT / NWN) wave tile.
 // AK / BK: A / B read along k (unit stride in k), else along m / n.
-#ifndef KVX_DG_BIG_NWN
-#define KVX_DG_BIG_NWN 4
-#endif
 template <int BT, int NWN>
 constexpr int dg_min_waves() {
   return BT == 64 ? 3 : (NWN == 4 ? 4 : 2);
@@ -1317,7 +1314,7 @@ static int dgemm(hipStream_t s, int32_t count, int32_t M, int32_t N, int32_t K, 
                                       static_cast<unsigned>(count));
 #define KVX_DG(BT_, NWN_, A_, B_) dgemm_kernel<BT_, NWN_, A_, B_><<<grid, 128 * NWN_, 0, s>>>(g)
   if (big) {
-    constexpr int W = KVX_DG_BIG_NWN;
+    constexpr int W = 4;  // 8 waves of 64 x 32 (4 waves of 64 x 64 ran 3-4% slower)
     if (ak) { if (bk) KVX_DG(128, W, true, true); else KVX_DG(128, W, true, false); }
     else { if (bk) KVX_DG(128, W, false, true); else KVX_DG(128, W, false, false); }
   } else {
