@@ -109,6 +109,21 @@ def committed_traffic(kernel):
     return float(m_b.group(1))
 
 
+def committed_clock_mhz(kernel):
+    """Average clock under the kernel (GRBM_GUI_ACTIVE per XCD over the
+    dispatches' duration) from the committed unit-counter summary, or None
+    when the summary is missing or the kernel sources changed since."""
+    path = os.path.join(PROFILES, UNITS_FILES[kernel])
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"source hash: `([0-9a-f]+)`", text)
+    m_c = re.search(r"-> ([0-9.]+) MHz average clock", text)
+    if not m_h or not m_c or m_h.group(1) != source_hash(kernel):
+        return None
+    return float(m_c.group(1))
+
+
 def calibration_copy(dev):
     """A plain device copy of known size: CALIB_BYTES read, CALIB_BYTES written
     per dispatch (an elementwise multiply by one, run twice)."""
@@ -1027,6 +1042,12 @@ def main():
     res["roofline"]["frac_of_measured_peak"] = achieved / peaks["mfma_bf16_TFLOPs"]
     res["roofline"]["frac_of_library_gemm_8192"] = achieved / peaks["library_gemm_8192_TFLOPs"]
     res["roofline"]["library_same_shapes_ms"] = peaks["headline_shapes_library_ms"]
+    # the matrix cores' ceiling at the clock they hold under this kernel (the
+    # published peak assumes 2.4 GHz), from the committed unit-counter run
+    mhz = committed_clock_mhz("flat_gemm_kernel")
+    res["roofline"]["clock_mhz_under_load"] = mhz
+    res["roofline"]["frac_of_clock_limited_peak"] = (
+        None if mhz is None else achieved / (PEAK_MFMA_BF16_TFLOPS * mhz / 2400.0))
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(x)
