@@ -95,6 +95,10 @@ struct FlatKArgs {
   const int32_t* run_begin;
   const int32_t* r2u;
   const int32_t* n_uniq;
+  // receiver layer of the i-th problem of a role: layers whose taps share
+  // sender layers follow one another, so their sender rows are read again
+  // while still in the last-level cache
+  uint8_t layer_order[MAX_LAYERS];
   // taps of layer l: bytes of taps[l][0] (taps 0..3) and taps[l][1] (4..6);
   // dword-packed so they are read with scalar loads
   uint32_t taps[MAX_LAYERS][2];
@@ -528,7 +532,7 @@ flat_gemm_kernel(const FlatKArgs args) {
     const int32_t p = static_cast<int32_t>(mrow / mt);
     const int32_t m0 = static_cast<int32_t>(mrow % mt) * FT_M;
     const int role = p / args.recv_layers;
-    const int l = p % args.recv_layers;
+    const int l = args.layer_order[p % args.recv_layers];
 
     TileAddr ta;
     ta.a_src = reinterpret_cast<const char*>(args.a_src[role]);
@@ -948,6 +952,42 @@ int launch_flat(const FlatProblem& p, const FlatRole* roles, int n_roles, hipStr
   for (int l = 0; l < p.recv_layers; ++l)
     for (int t = 0; t < p.n_taps; ++t)
       a.taps[l][t / 4] |= static_cast<uint32_t>(p.taps[l * p.n_taps + t] & 0xff) << (8 * (t % 4));
+  // problem order inside a role: from layer 0, each next layer is the
+  // unvisited one sharing the most sender layers with the current one (the
+  // nearest on ties)
+  {
+    bool used[MAX_LAYERS] = {false};
+    int cur = 0;
+    used[0] = true;
+    a.layer_order[0] = 0;
+    for (int i = 1; i < p.recv_layers; ++i) {
+      int best = -1, best_shared = -1, best_dist = 0;
+      for (int c = 0; c < p.recv_layers; ++c) {
+        if (used[c]) continue;
+        int shared = 0;
+        for (int t = 0; t < p.n_taps; ++t) {
+          const int32_t sl = p.taps[c * p.n_taps + t];
+          bool seen = false;  // count each sender layer of c once
+          for (int u = 0; u < t; ++u) seen = seen || p.taps[c * p.n_taps + u] == sl;
+          if (seen) continue;
+          for (int u = 0; u < p.n_taps; ++u)
+            if (p.taps[cur * p.n_taps + u] == sl) {
+              ++shared;
+              break;
+            }
+        }
+        const int dist = c > cur ? c - cur : cur - c;
+        if (shared > best_shared || (shared == best_shared && dist < best_dist)) {
+          best = c;
+          best_shared = shared;
+          best_dist = dist;
+        }
+      }
+      used[best] = true;
+      a.layer_order[i] = static_cast<uint8_t>(best);
+      cur = best;
+    }
+  }
   int G = device_cu_count();
   G = G >= 8 ? (G / 8) * 8 : 8;
   for (int j = 0; j < n_roles; ++j) {
